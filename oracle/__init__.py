@@ -1,0 +1,195 @@
+"""fp64 CPU oracle for the truly sparse COO layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library (``coo_spmm_amd``)
+never imports, links or calls it, and the two share no code: the oracle is the
+plain C file ``snack_oracle.c`` (loops in double) plus this ctypes wrapper.
+
+What each function computes, and the passage it follows, is documented in
+``snack_oracle.c``.  In short (W is [M, K], X is [B, K], dY is [B, M]):
+
+* ``canonicalize``  -- sort by (row, col), row pointer, transposed index
+  ("Padded-CSR" post, sections 3.2 and 7.2; SNACK paper, Table 7).
+* ``forward``       -- Y = X W^T  (SNACK paper, Figure 1; Padded-CSR 6.1).
+* ``backward_dx``   -- dX = dY W  (Padded-CSR 7.1).
+* ``backward_dw``   -- dW on the support (Padded-CSR 7.1; SNACK Figure 1).
+* ``prune_regrow``  -- SET-style drop of the smallest |w|, uniform regrow
+  (Padded-CSR 4.3; SNACK Figure 1).  The candidate stream is SplitMix64:
+  parity of the stream itself is pinned only to SplitMix64's published output
+  and a uniformity test, since the pages name no generator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "snack_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, INVALID, RANGE, DUPLICATE, NOMEM = 0, 1, 2, 3, 4
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+        lib.oracle_canonicalize.argtypes = [i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_canonicalize.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [i32, i32, i64, P, P, P, i32, P, P, P]
+        lib.oracle_forward.restype = None
+        lib.oracle_backward_dx.argtypes = [i32, i32, i64, P, P, P, i32, P, P, P]
+        lib.oracle_backward_dx.restype = None
+        lib.oracle_backward_dw.argtypes = [i32, i32, i64, P, P, i32, P, P, P, P]
+        lib.oracle_backward_dw.restype = None
+        lib.oracle_mse_grad.argtypes = [i64, P, P, P]
+        lib.oracle_gelu_fwd.argtypes = [i64, P, P]
+        lib.oracle_gelu_bwd.argtypes = [i64, P, P, P]
+        lib.oracle_sgd.argtypes = [i64, P, P, f64, P]
+        lib.oracle_splitmix64_mix.argtypes = [u64]
+        lib.oracle_splitmix64_mix.restype = u64
+        lib.oracle_regrow_candidate.argtypes = [u64, u64, u64, u64]
+        lib.oracle_regrow_candidate.restype = u64
+        lib.oracle_prune_regrow.argtypes = [i32, i32, i64, P, P, P, i64, u64, u64, P, P, P, P]
+        lib.oracle_prune_regrow.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        super().__init__({1: "invalid argument", 2: "index out of range", 3: "duplicate position",
+                          4: "out of memory"}.get(code, str(code)))
+        self.code = code
+
+
+def canonicalize(M, K, rows, cols, vals):
+    """Returns dict(rows, cols, vals, row_ptr, perm, rows_t, col_ptr); raises OracleError."""
+    rows, cols, vals = _i32(rows), _i32(cols), _f32(vals)
+    nnz = rows.shape[0]
+    out = dict(rows=np.empty(nnz, np.int32), cols=np.empty(nnz, np.int32), vals=np.empty(nnz, np.float32),
+               row_ptr=np.empty(M + 1, np.int32), perm=np.empty(nnz, np.int32),
+               rows_t=np.empty(nnz, np.int32), col_ptr=np.empty(K + 1, np.int32))
+    rc = _load().oracle_canonicalize(M, K, nnz, _p(rows), _p(cols), _p(vals), _p(out["rows"]), _p(out["cols"]),
+                                     _p(out["vals"]), _p(out["row_ptr"]), _p(out["perm"]), _p(out["rows_t"]),
+                                     _p(out["col_ptr"]))
+    if rc != OK:
+        raise OracleError(rc)
+    return out
+
+
+def forward(M, K, rows, cols, vals, X):
+    """Y[b, i] = sum_k v_k X[b, c_k] over r_k = i, in fp64; returns (Y, abs_sum)."""
+    rows, cols, vals, X = _i32(rows), _i32(cols), _f32(vals), _f32(X)
+    B = X.shape[0]
+    assert X.shape == (B, K)
+    Y = np.empty((B, M), np.float64)
+    A = np.empty((B, M), np.float64)
+    _load().oracle_forward(M, K, rows.shape[0], _p(rows), _p(cols), _p(vals), B, _p(X), _p(Y), _p(A))
+    return Y, A
+
+
+def backward_dx(M, K, rows, cols, vals, dY):
+    rows, cols, vals, dY = _i32(rows), _i32(cols), _f32(vals), _f32(dY)
+    B = dY.shape[0]
+    assert dY.shape == (B, M)
+    dX = np.empty((B, K), np.float64)
+    A = np.empty((B, K), np.float64)
+    _load().oracle_backward_dx(M, K, rows.shape[0], _p(rows), _p(cols), _p(vals), B, _p(dY), _p(dX), _p(A))
+    return dX, A
+
+
+def backward_dw(M, K, rows, cols, X, dY):
+    rows, cols, X, dY = _i32(rows), _i32(cols), _f32(X), _f32(dY)
+    B = X.shape[0]
+    assert X.shape == (B, K) and dY.shape == (B, M)
+    nnz = rows.shape[0]
+    dW = np.empty(nnz, np.float64)
+    A = np.empty(nnz, np.float64)
+    _load().oracle_backward_dw(M, K, nnz, _p(rows), _p(cols), B, _p(X), _p(dY), _p(dW), _p(A))
+    return dW, A
+
+
+def mse_grad(Y, T):
+    Y, T = _f32(Y), _f32(T)
+    out = np.empty(Y.shape, np.float64)
+    _load().oracle_mse_grad(Y.size, _p(Y), _p(T), _p(out))
+    return out
+
+
+def gelu_fwd(X):
+    X = _f32(X)
+    out = np.empty(X.shape, np.float64)
+    _load().oracle_gelu_fwd(X.size, _p(X), _p(out))
+    return out
+
+
+def gelu_bwd(X, dY):
+    X, dY = _f32(X), _f32(dY)
+    out = np.empty(X.shape, np.float64)
+    _load().oracle_gelu_bwd(X.size, _p(X), _p(dY), _p(out))
+    return out
+
+
+def sgd(v, g, lr):
+    v, g = _f32(v), _f32(g)
+    out = np.empty(v.shape, np.float64)
+    _load().oracle_sgd(v.size, _p(v), _p(g), float(lr), _p(out))
+    return out
+
+
+def splitmix64_mix(z):
+    return int(_load().oracle_splitmix64_mix(ctypes.c_uint64(z & (2**64 - 1))))
+
+
+def regrow_candidate(seed, epoch, t, N):
+    return int(_load().oracle_regrow_candidate(seed & (2**64 - 1), epoch, t, N))
+
+
+def prune_regrow(M, K, rows, cols, vals, n_drop, seed, epoch):
+    """Canonical triple in, canonical triple out (nnz unchanged).  Returns (rows, cols, vals, candidates_used)."""
+    rows, cols, vals = _i32(rows), _i32(cols), _f32(vals)
+    nnz = rows.shape[0]
+    o_r, o_c, o_v = np.empty(nnz, np.int32), np.empty(nnz, np.int32), np.empty(nnz, np.float32)
+    used = ctypes.c_uint64(0)
+    rc = _load().oracle_prune_regrow(M, K, nnz, _p(rows), _p(cols), _p(vals), int(n_drop), seed & (2**64 - 1),
+                                     int(epoch), _p(o_r), _p(o_c), _p(o_v), ctypes.byref(used))
+    if rc != OK:
+        raise OracleError(rc)
+    return o_r, o_c, o_v, int(used.value)
+
+
+def tolerance_ok(got, ref, abs_sum, rel=1e-5, atol=1e-6):
+    """Per-element acceptance |got - ref| <= rel * sum|terms| + atol."""
+    got = np.asarray(got, np.float64)
+    return np.abs(got - ref) <= rel * abs_sum + atol
