@@ -1,0 +1,124 @@
+// aux.hip -- feature-major activation copies and the elementwise training
+// helpers (SGD, MSE gradient, exact GELU).  None of these is the sparse
+// method; they keep the training loop on the device.
+#include "internal.h"
+
+#include <math.h>
+
+namespace snack {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;
+
+inline unsigned grid_for(int64_t n)
+{
+    int64_t g = (n + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    if (g > 65535LL * 8) g = 65535LL * 8;
+    return (unsigned)g;
+}
+
+// dst[c * bp + b] = (b < B) ? src[b * n + c] : 0 ; one 64 x 64 tile per block via LDS.
+__global__ void __launch_bounds__(kThreads) transpose_pad_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                                 int B, int n, int bp)
+{
+    __shared__ float tile[kTile][kTile + 1];
+    const int c0 = blockIdx.x * kTile;
+    const int b0 = blockIdx.y * kTile;
+    const int tx = threadIdx.x & (kTile - 1);
+    const int ty = threadIdx.x / kTile;   // 0..3
+    for (int bb = ty; bb < kTile; bb += kThreads / kTile) {
+        const int b = b0 + bb, c = c0 + tx;
+        float v = 0.0f;
+        if (b < B && c < n) v = src[(int64_t)b * n + c];
+        tile[bb][tx] = v;
+    }
+    __syncthreads();
+    for (int cc = ty; cc < kTile; cc += kThreads / kTile) {
+        const int c = c0 + cc, b = b0 + tx;
+        if (c < n && b < bp) dst[(int64_t)c * bp + b] = tile[tx][cc];
+    }
+}
+
+__global__ void sgd_kernel(float* __restrict__ v, const float* __restrict__ g, float lr, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        v[i] = v[i] - lr * g[i];
+}
+
+__global__ void mse_grad_kernel(const float* __restrict__ Y, const float* __restrict__ T, float* __restrict__ dY,
+                                int64_t n, float scale)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dY[i] = scale * (Y[i] - T[i]);
+}
+
+__global__ void gelu_fwd_kernel(const float* __restrict__ X, float* __restrict__ Y, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const float x = X[i];
+        Y[i] = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    }
+}
+
+__global__ void gelu_bwd_kernel(const float* __restrict__ X, const float* __restrict__ dY, float* __restrict__ dX,
+                                int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const float x = X[i];
+        const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+        const float pdf = 0.39894228040143268f * expf(-0.5f * x * x);
+        dX[i] = dY[i] * (cdf + x * pdf);
+    }
+}
+
+}  // namespace
+
+snack_status transpose_pad(const float* src, float* dst, int B, int n, int bp, int kclass, hipStream_t s)
+{
+    ProfScope prof(kclass, s);
+    dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((bp + kTile - 1) / kTile));
+    hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(kThreads), 0, s, src, dst, B, n, bp);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+snack_status sgd_update(snack_layer* L, const float* dW, float lr, hipStream_t s)
+{
+    if (L->nnz == 0) return SNACK_OK;
+    ProfScope prof(KC_SGD, s);
+    hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->vals, dW, lr, L->nnz);
+    SNACK_HIP(hipGetLastError());
+    L->vals_t_stale = true;
+    return SNACK_OK;
+}
+
+snack_status mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale, hipStream_t s)
+{
+    if (n == 0) return SNACK_OK;
+    ProfScope prof(KC_ELEMENTWISE, s);
+    hipLaunchKernelGGL(mse_grad_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, Y, T, dY, n, scale);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s)
+{
+    if (n == 0) return SNACK_OK;
+    ProfScope prof(KC_ELEMENTWISE, s);
+    hipLaunchKernelGGL(gelu_fwd_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, X, Y, n);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hipStream_t s)
+{
+    if (n == 0) return SNACK_OK;
+    ProfScope prof(KC_ELEMENTWISE, s);
+    hipLaunchKernelGGL(gelu_bwd_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, X, dY, dX, n);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+}  // namespace snack

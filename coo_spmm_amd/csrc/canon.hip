@@ -1,0 +1,234 @@
+// canon.hip -- canonical order, validation and index structures of the layer.
+//
+// Canonical order: stored positions sorted by linear position row*K + col,
+// i.e. by row then column -- the sorted COO with a row pointer of the
+// "Padded-CSR" post, section 3.2.  The transposed view lists the same slots
+// sorted by (column, row) together with the permutation map of section 7.2
+// (transposed slot -> canonical slot) and the column pointer (the CSC of the
+// SNACK paper's Table 7).  Both views carry a key-aligned work partition:
+// chunk c owns keys [chunk_key[c], chunk_key[c+1]), cut so that each chunk
+// holds about kChunkWork units of (entries + keys); a row is never split, so
+// the SpMM needs no cross-chunk fix-up and writes every output row once.
+#include "internal.h"
+
+namespace snack {
+namespace {
+
+constexpr int kThreads = 256;
+
+inline unsigned grid_for(int64_t n, int per_block = kThreads)
+{
+    int64_t g = (n + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > 65535LL * 16) g = 65535LL * 16;
+    return (unsigned)g;
+}
+
+inline int bits_for(uint64_t maxval)
+{
+    int b = 1;
+    while (b < 64 && (maxval >> b) != 0) ++b;
+    return b;
+}
+
+// Linear position keys with range validation.  flag |= 1 on a bad index.
+template <typename KeyT>
+__global__ void make_keys_kernel(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, int64_t nnz,
+                                 int32_t M, int32_t K, KeyT* __restrict__ keys, uint32_t* __restrict__ slots,
+                                 int32_t* __restrict__ flag)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t r = rows[k], c = cols[k];
+        KeyT key = 0;
+        if (r < 0 || r >= M || c < 0 || c >= K) {
+            atomicOr(flag, 1);
+        } else {
+            key = (KeyT)r * (KeyT)K + (KeyT)c;
+        }
+        keys[k] = key;
+        slots[k] = (uint32_t)k;
+    }
+}
+
+// Canonical arrays from the sorted keys; flag |= 2 on a repeated position.
+template <typename KeyT>
+__global__ void gather_canonical_kernel(const KeyT* __restrict__ keys, const uint32_t* __restrict__ slots,
+                                        int64_t nnz, int32_t K, const float* __restrict__ vin,
+                                        int32_t* __restrict__ rows, int32_t* __restrict__ cols,
+                                        float* __restrict__ vals, int32_t* __restrict__ flag)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x) {
+        const KeyT key = keys[k];
+        if (k > 0 && keys[k - 1] == key) atomicOr(flag, 2);
+        rows[k] = (int32_t)(key / (KeyT)K);
+        cols[k] = (int32_t)(key % (KeyT)K);
+        vals[k] = vin ? vin[slots[k]] : 0.0f;
+    }
+}
+
+// ptr[r] = first slot whose key >= r, for r in [0, nkeys]; keys sorted.
+__global__ void build_ptr_kernel(const int32_t* __restrict__ keys, int64_t nnz, int32_t nkeys,
+                                 int32_t* __restrict__ ptr)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k <= nnz;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t prev = (k == 0) ? -1 : keys[k - 1];
+        const int32_t cur = (k == nnz) ? nkeys : keys[k];
+        for (int32_t r = prev + 1; r <= cur; ++r) ptr[r] = (int32_t)k;
+    }
+}
+
+// chunk_key[c] = smallest key r with ptr[r] + r >= c * work, chunk_key[nchunks] = nkeys.
+__global__ void build_chunks_kernel(const int32_t* __restrict__ ptr, int32_t nkeys, int32_t nchunks, int32_t work,
+                                    int32_t* __restrict__ chunk_key)
+{
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c <= nchunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        if (c == nchunks) {
+            chunk_key[c] = nkeys;
+            continue;
+        }
+        const int64_t target = c * (int64_t)work;
+        int32_t lo = 0, hi = nkeys;
+        while (lo < hi) {
+            const int32_t mid = lo + ((hi - lo) >> 1);
+            if ((int64_t)ptr[mid] + mid >= target) hi = mid;
+            else lo = mid + 1;
+        }
+        chunk_key[c] = lo;
+    }
+}
+
+__global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, uint32_t* __restrict__ keys,
+                                 uint32_t* __restrict__ slots)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x) {
+        keys[k] = (uint32_t)cols[k];
+        slots[k] = (uint32_t)k;
+    }
+}
+
+__global__ void build_transposed_kernel(const uint32_t* __restrict__ tkeys, const uint32_t* __restrict__ tslots,
+                                        int64_t nnz, const int32_t* __restrict__ rows, const float* __restrict__ vals,
+                                        int32_t* __restrict__ perm, int32_t* __restrict__ rows_t,
+                                        int32_t* __restrict__ cols_t, float* __restrict__ vals_t)
+{
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t k = (int32_t)tslots[j];
+        perm[j] = k;
+        cols_t[j] = (int32_t)tkeys[j];
+        rows_t[j] = rows[k];
+        vals_t[j] = vals[k];
+    }
+}
+
+__global__ void refresh_vals_t_kernel(const int32_t* __restrict__ perm, const float* __restrict__ vals, int64_t nnz,
+                                      float* __restrict__ vals_t)
+{
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * blockDim.x)
+        vals_t[j] = vals[perm[j]];
+}
+
+snack_status build_view_partition(View& v, int64_t nnz, hipStream_t s)
+{
+    hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)v.nchunks + 1)), dim3(kThreads), 0, s, v.ptr,
+                       v.nkeys, v.nchunks, kChunkWork, v.chunk_key);
+    SNACK_HIP(hipGetLastError());
+    (void)nnz;
+    return SNACK_OK;
+}
+
+}  // namespace
+
+size_t canon_scratch_bytes(const snack_layer* L, int64_t nnz)
+{
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    const int kb = bits_for(N > 0 ? N - 1 : 0);
+    const size_t kw = kb > 32 ? 8 : 4;
+    size_t b = 0;
+    b += ((size_t)nnz * kw + 255) & ~(size_t)255;     // keys
+    b += ((size_t)nnz * 4 + 255) & ~(size_t)255;      // slots
+    b += radix_sort_scratch_bytes(nnz, kb);
+    return b + 256;
+}
+
+snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t* cols, const float* vals,
+                              hipStream_t s)
+{
+    ProfScope prof(KC_CANON, s);
+    const int64_t nnz = L->nnz;
+    if (nnz == 0) return SNACK_OK;
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    const int kb = bits_for(N - 1);
+    char* p = (char*)L->scratch;
+    if (kb > 32) {
+        uint64_t* keys = (uint64_t*)p;
+        p += ((size_t)nnz * 8 + 255) & ~(size_t)255;
+        uint32_t* slots = (uint32_t*)p;
+        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+        hipLaunchKernelGGL(make_keys_kernel<uint64_t>, dim3(grid_for(nnz)), dim3(kThreads), 0, s, rows, cols, nnz,
+                           L->M, L->K, keys, slots, L->flag);
+        SNACK_HIP(hipGetLastError());
+        SNACK_CHECK(radix_sort_u64(keys, slots, nnz, kb, p, s));
+        hipLaunchKernelGGL(gather_canonical_kernel<uint64_t>, dim3(grid_for(nnz)), dim3(kThreads), 0, s, keys, slots,
+                           nnz, L->K, vals, L->rows, L->cols, L->vals, L->flag);
+        SNACK_HIP(hipGetLastError());
+    } else {
+        uint32_t* keys = (uint32_t*)p;
+        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+        uint32_t* slots = (uint32_t*)p;
+        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+        hipLaunchKernelGGL(make_keys_kernel<uint32_t>, dim3(grid_for(nnz)), dim3(kThreads), 0, s, rows, cols, nnz,
+                           L->M, L->K, keys, slots, L->flag);
+        SNACK_HIP(hipGetLastError());
+        SNACK_CHECK(radix_sort_u32(keys, slots, nnz, kb, p, s));
+        hipLaunchKernelGGL(gather_canonical_kernel<uint32_t>, dim3(grid_for(nnz)), dim3(kThreads), 0, s, keys, slots,
+                           nnz, L->K, vals, L->rows, L->cols, L->vals, L->flag);
+        SNACK_HIP(hipGetLastError());
+    }
+    return SNACK_OK;
+}
+
+snack_status canon_build_index(snack_layer* L, hipStream_t s)
+{
+    ProfScope prof(KC_CANON, s);
+    const int64_t nnz = L->nnz;
+    hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->rows, nnz, L->M,
+                       L->row_ptr);
+    SNACK_HIP(hipGetLastError());
+    if (nnz > 0) {
+        char* p = (char*)L->scratch;
+        uint32_t* tkeys = (uint32_t*)p;
+        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+        uint32_t* tslots = (uint32_t*)p;
+        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+        hipLaunchKernelGGL(iota_cols_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->cols, nnz, tkeys, tslots);
+        SNACK_HIP(hipGetLastError());
+        // canonical order is (row, col), so a stable sort by column yields (col, row)
+        SNACK_CHECK(radix_sort_u32(tkeys, tslots, nnz, bits_for((uint64_t)(L->K - 1)), p, s));
+        hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tkeys, tslots, nnz,
+                           L->rows, L->vals, L->perm, L->rows_t, L->cols_t, L->vals_t);
+        SNACK_HIP(hipGetLastError());
+    }
+    hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->cols_t, nnz, L->K,
+                       L->col_ptr);
+    SNACK_HIP(hipGetLastError());
+    L->vals_t_stale = false;
+    SNACK_CHECK(build_view_partition(L->fwd, nnz, s));
+    SNACK_CHECK(build_view_partition(L->tr, nnz, s));
+    return SNACK_OK;
+}
+
+snack_status refresh_vals_t(snack_layer* L, hipStream_t s)
+{
+    if (L->nnz > 0) {
+        ProfScope prof(KC_VALS_T_REFRESH, s);
+        hipLaunchKernelGGL(refresh_vals_t_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->perm, L->vals,
+                           L->nnz, L->vals_t);
+        SNACK_HIP(hipGetLastError());
+    }
+    L->vals_t_stale = false;
+    return SNACK_OK;
+}
+
+}  // namespace snack

@@ -1,0 +1,188 @@
+// internal.h -- shared declarations of the HIP implementation of snack.h.
+// Host code only sees launchers; every __global__ kernel lives in the .hip file
+// that launches it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <vector>
+
+#include "../../include/snack.h"
+
+namespace snack {
+
+constexpr int kWave = 64;              // CDNA wavefront width
+constexpr int kChunkWork = 1024;       // target work (nnz + rows) per SpMM chunk
+constexpr int kPad = 1024;             // slack elements after every nnz-sized array
+
+// Kernel classes for the profiling hooks (order = snack_profile_name ids).
+enum KernelClass : int {
+    KC_SPMM_FWD = 0,
+    KC_SPMM_DX,
+    KC_SDDMM_DW,
+    KC_TRANSPOSE,
+    KC_VALS_T_REFRESH,
+    KC_SGD,
+    KC_ELEMENTWISE,
+    KC_SORT,
+    KC_CANON,
+    KC_PRUNE,
+    KC_COUNT
+};
+
+// One sorted view of the triple: keys ascending (rows for the canonical view,
+// cols for the transposed one), the gathered index, the values, the key
+// pointer [nkeys+1] and the work partition into key-aligned chunks.
+struct View {
+    int32_t nkeys = 0;      // M (canonical) or K (transposed)
+    int32_t nidx = 0;       // K (canonical) or M (transposed)
+    int32_t* keys = nullptr;
+    int32_t* idx = nullptr;
+    float* vals = nullptr;
+    int32_t* ptr = nullptr;         // [nkeys + 1]
+    int32_t nchunks = 0;
+    int32_t* chunk_key = nullptr;   // [nchunks + 1], first key of each chunk
+};
+
+struct Scratch {
+    size_t bytes = 0;
+    void* base = nullptr;
+};
+
+}  // namespace snack
+
+struct snack_layer {
+    int device = 0;
+    int32_t M = 0, K = 0;
+    int64_t nnz = 0;
+    int64_t cap = 0;          // element capacity of each nnz-sized array (>= nnz + kPad)
+    uint64_t seed = 0;
+    uint64_t epoch = 0;
+
+    // canonical (row-sorted) triple
+    int32_t* rows = nullptr;
+    int32_t* cols = nullptr;
+    float* vals = nullptr;
+    int32_t* row_ptr = nullptr;   // [M+1]
+    // transposed (column-sorted) index
+    int32_t* perm = nullptr;      // transposed slot -> canonical slot
+    int32_t* rows_t = nullptr;
+    int32_t* cols_t = nullptr;    // sorted column keys
+    float* vals_t = nullptr;      // values in transposed order
+    int32_t* col_ptr = nullptr;   // [K+1]
+    bool vals_t_stale = true;
+
+    snack::View fwd;   // keys = rows, idx = cols
+    snack::View tr;    // keys = cols_t, idx = rows_t
+
+    // per-batch workspace: feature-major copies of X and dY
+    float* ws = nullptr;
+    size_t ws_bytes = 0;
+
+    // scratch for sorting / prune_regrow (reserved at create)
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    int32_t* flag = nullptr;      // device error / count word(s)
+
+    size_t device_bytes = 0;
+    std::vector<void*> allocations;
+};
+
+namespace snack {
+
+// ---- error handling ------------------------------------------------------
+#define SNACK_HIP(call)                                   \
+    do {                                                  \
+        hipError_t _e = (call);                           \
+        if (_e != hipSuccess) return SNACK_ERR_HIP;       \
+    } while (0)
+
+#define SNACK_CHECK(call)                                 \
+    do {                                                  \
+        snack_status _s = (call);                         \
+        if (_s != SNACK_OK) return _s;                    \
+    } while (0)
+
+// ---- profiling hooks (prof.hip) ------------------------------------------
+bool prof_on();
+void prof_begin(int kclass, hipStream_t s);
+void prof_end(int kclass, hipStream_t s);
+
+struct ProfScope {
+    int k;
+    hipStream_t s;
+    bool on;
+    ProfScope(int kc, hipStream_t st) : k(kc), s(st), on(prof_on()) {
+        if (on) prof_begin(k, s);
+    }
+    ~ProfScope() {
+        if (on) prof_end(k, s);
+    }
+};
+
+// ---- allocation helpers (layer.hip) ---------------------------------------
+snack_status layer_alloc(snack_layer* L, void** p, size_t bytes);
+
+// ---- sort / scan primitives (sort.hip) --------------------------------------
+// Bytes of scratch needed to sort n (key, value) pairs with the given key width.
+size_t radix_sort_scratch_bytes(int64_t n, int key_bits);
+// Stable LSD radix sort of (keys, vals) by the low `key_bits` bits of keys.
+// keys/vals are sorted in place; scratch must hold radix_sort_scratch_bytes.
+snack_status radix_sort_u32(uint32_t* keys, uint32_t* vals, int64_t n, int key_bits, void* scratch,
+                            hipStream_t s);
+snack_status radix_sort_u64(uint64_t* keys, uint32_t* vals, int64_t n, int key_bits, void* scratch,
+                            hipStream_t s);
+// Exclusive prefix sum of int32 flags/counts (n elements), total written to *total_dev
+// if non-null.  Scratch: scan_scratch_bytes(n).
+size_t scan_scratch_bytes(int64_t n);
+snack_status exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total_dev, void* scratch,
+                                hipStream_t s);
+
+// ---- canonicalisation (canon.hip) -----------------------------------------
+// Bytes of scratch canonicalise needs for nnz entries.
+size_t canon_scratch_bytes(const snack_layer* L, int64_t nnz);
+// Sort an arbitrary-order triple (device) into the layer's canonical arrays and
+// validate it.  Writes error code into L->flag (0 ok).
+snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t* cols, const float* vals,
+                              hipStream_t s);
+// Given canonical rows/cols/vals, build row_ptr, the transposed view, vals_t,
+// and both work partitions.
+snack_status canon_build_index(snack_layer* L, hipStream_t s);
+// vals_t[j] = vals[perm[j]]
+snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
+
+// ---- kernels ---------------------------------------------------------------
+// Batch tiling for a batch of B columns: B_tile columns per kernel pass, padded
+// batch Bp (multiple of B_tile) used as the row stride of feature-major copies.
+struct BatchPlan {
+    int bt;      // lanes per group
+    int nb;      // batch values per lane
+    int u;       // run of entries per group per wave step
+    int btile;   // bt * nb
+    int bp;      // padded batch
+    int ntiles;  // bp / btile
+};
+BatchPlan plan_batch(int B);
+
+// dst[c * bp + b] = src[b * n + c] for b < B, 0 for B <= b < bp  (src [B, n])
+snack_status transpose_pad(const float* src, float* dst, int B, int n, int bp, int kclass, hipStream_t s);
+
+// out[b, key] = sum over the view's entries of that key of v * feat[idx, b]
+snack_status spmm_view(const snack::View& v, const float* feat_t, const BatchPlan& p, int B, float* out,
+                       int kclass, hipStream_t s);
+
+// dW[k] = sum_b dYt[r_k, b] * Xt[c_k, b] in canonical order
+snack_status sddmm_dw(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
+                      float* dW, hipStream_t s);
+
+snack_status sgd_update(snack_layer* L, const float* dW, float lr, hipStream_t s);
+snack_status mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale, hipStream_t s);
+snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s);
+snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hipStream_t s);
+
+// ---- prune / regrow (prune.hip) ---------------------------------------------
+size_t prune_scratch_bytes(const snack_layer* L);
+snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s);
+
+}  // namespace snack

@@ -1,0 +1,348 @@
+// layer.hip -- the C ABI of snack.h: layer lifetime, queries and the
+// forward / backward / drop-regrow entry points.  Host code only: it checks
+// arguments, owns the device buffers and launches the kernels of the other
+// translation units on the caller's stream.
+#include "internal.h"
+
+#include <limits.h>
+#include <string.h>
+
+using namespace snack;
+
+namespace snack {
+
+snack_status layer_alloc(snack_layer* L, void** p, size_t bytes)
+{
+    *p = nullptr;
+    if (bytes == 0) bytes = 256;
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return SNACK_ERR_ALLOC;
+    }
+    L->allocations.push_back(*p);
+    L->device_bytes += bytes;
+    return SNACK_OK;
+}
+
+}  // namespace snack
+
+namespace {
+
+void free_layer(snack_layer* L)
+{
+    if (!L) return;
+    (void)hipDeviceSynchronize();
+    for (void* p : L->allocations) (void)hipFree(p);
+    if (L->ws) (void)hipFree(L->ws);
+    delete L;
+}
+
+inline hipStream_t as_stream(snack_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t ws_need(const snack_layer* L, const BatchPlan& p)
+{
+    const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
+    const size_t b = (((size_t)L->M * p.bp * 4) + 255) & ~(size_t)255;
+    return a + b;
+}
+
+snack_status ensure_ws(snack_layer* L, const BatchPlan& p)
+{
+    const size_t need = ws_need(L, p);
+    if (need <= L->ws_bytes) return SNACK_OK;
+    if (L->ws) {
+        SNACK_HIP(hipDeviceSynchronize());
+        (void)hipFree(L->ws);
+        L->device_bytes -= L->ws_bytes;
+        L->ws = nullptr;
+        L->ws_bytes = 0;
+    }
+    void* p2 = nullptr;
+    if (hipMalloc(&p2, need) != hipSuccess) {
+        (void)hipGetLastError();
+        return SNACK_ERR_ALLOC;
+    }
+    L->ws = (float*)p2;
+    L->ws_bytes = need;
+    L->device_bytes += need;
+    return SNACK_OK;
+}
+
+float* ws_x(snack_layer* L) { return L->ws; }
+float* ws_dy(snack_layer* L, const BatchPlan& p)
+{
+    const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
+    return (float*)((char*)L->ws + a);
+}
+
+}  // namespace
+
+extern "C" const char* snack_status_string(snack_status s)
+{
+    switch (s) {
+    case SNACK_OK: return "ok";
+    case SNACK_ERR_INVALID_ARG: return "invalid argument";
+    case SNACK_ERR_INDEX_RANGE: return "index out of range";
+    case SNACK_ERR_DUPLICATE: return "duplicate position";
+    case SNACK_ERR_ALLOC: return "device allocation failed";
+    case SNACK_ERR_HIP: return "HIP runtime error";
+    case SNACK_ERR_UNSUPPORTED: return "unsupported size";
+    }
+    return "unknown status";
+}
+
+extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, const int32_t* rows,
+                                           const int32_t* cols, const float* vals, uint64_t seed,
+                                           snack_stream stream, snack_layer** out)
+{
+    if (!out) return SNACK_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (M < 1 || K < 1 || nnz < 0) return SNACK_ERR_INVALID_ARG;
+    if ((uint64_t)nnz > (uint64_t)M * (uint64_t)K) return SNACK_ERR_INVALID_ARG;
+    if (nnz > (int64_t)INT_MAX - 4 * kPad) return SNACK_ERR_UNSUPPORTED;
+    if (M > INT_MAX - 2 || K > INT_MAX - 2) return SNACK_ERR_UNSUPPORTED;
+    if (nnz > 0 && (!rows || !cols)) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+
+    snack_layer* L = new snack_layer();
+    if (hipGetDevice(&L->device) != hipSuccess) {
+        delete L;
+        return SNACK_ERR_HIP;
+    }
+    L->M = M;
+    L->K = K;
+    L->nnz = nnz;
+    L->seed = seed;
+    L->epoch = 0;
+    L->cap = ((nnz + 255) / 256) * 256 + kPad;
+
+    auto fail = [&](snack_status st) {
+        free_layer(L);
+        return st;
+    };
+    const size_t nb4 = (size_t)L->cap * 4;
+    void* p = nullptr;
+#define ALLOC(field, type, bytes)                                     \
+    do {                                                              \
+        snack_status _s = layer_alloc(L, &p, (bytes));                \
+        if (_s != SNACK_OK) return fail(_s);                          \
+        L->field = (type)p;                                           \
+        if (hipMemsetAsync(p, 0, (bytes), s) != hipSuccess) return fail(SNACK_ERR_HIP); \
+    } while (0)
+    ALLOC(rows, int32_t*, nb4);
+    ALLOC(cols, int32_t*, nb4);
+    ALLOC(vals, float*, nb4);
+    ALLOC(perm, int32_t*, nb4);
+    ALLOC(rows_t, int32_t*, nb4);
+    ALLOC(cols_t, int32_t*, nb4);
+    ALLOC(vals_t, float*, nb4);
+    ALLOC(row_ptr, int32_t*, ((size_t)M + 1) * 4);
+    ALLOC(col_ptr, int32_t*, ((size_t)K + 1) * 4);
+    ALLOC(flag, int32_t*, 64);
+
+    const int64_t nchf = (nnz + M + kChunkWork - 1) / kChunkWork;
+    const int64_t ncht = (nnz + K + kChunkWork - 1) / kChunkWork;
+    if (nchf > INT_MAX / 2 || ncht > INT_MAX / 2) return fail(SNACK_ERR_UNSUPPORTED);
+    L->fwd.nkeys = M;
+    L->fwd.nidx = K;
+    L->fwd.keys = L->rows;
+    L->fwd.idx = L->cols;
+    L->fwd.vals = L->vals;
+    L->fwd.ptr = L->row_ptr;
+    L->fwd.nchunks = (int32_t)(nchf < 1 ? 1 : nchf);
+    ALLOC(fwd.chunk_key, int32_t*, ((size_t)L->fwd.nchunks + 1) * 4);
+    L->tr.nkeys = K;
+    L->tr.nidx = M;
+    L->tr.keys = L->cols_t;
+    L->tr.idx = L->rows_t;
+    L->tr.vals = L->vals_t;
+    L->tr.ptr = L->col_ptr;
+    L->tr.nchunks = (int32_t)(ncht < 1 ? 1 : ncht);
+    ALLOC(tr.chunk_key, int32_t*, ((size_t)L->tr.nchunks + 1) * 4);
+
+    size_t scr = canon_scratch_bytes(L, nnz);
+    const size_t pscr = prune_scratch_bytes(L);
+    if (pscr > scr) scr = pscr;
+    {
+        snack_status _s = layer_alloc(L, &L->scratch, scr);
+        if (_s != SNACK_OK) return fail(_s);
+        L->scratch_bytes = scr;
+    }
+#undef ALLOC
+
+    snack_status st = canon_sort_input(L, rows, cols, vals, s);
+    if (st != SNACK_OK) return fail(st);
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, L->flag, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return fail(SNACK_ERR_HIP);
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(SNACK_ERR_HIP);
+    if (flag & 1) return fail(SNACK_ERR_INDEX_RANGE);
+    if (flag & 2) return fail(SNACK_ERR_DUPLICATE);
+    st = canon_build_index(L, s);
+    if (st != SNACK_OK) return fail(st);
+    *out = L;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_destroy(snack_layer* layer)
+{
+    free_layer(layer);
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_reserve(snack_layer* L, int32_t max_batch)
+{
+    if (!L || max_batch < 1) return SNACK_ERR_INVALID_ARG;
+    return ensure_ws(L, plan_batch(max_batch));
+}
+
+extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, int32_t B, snack_stream stream)
+{
+    if (!L || !X || !Y || B < 1) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const BatchPlan p = plan_batch(B);
+    const float* feat = X;
+    if (p.bp > 1) {
+        SNACK_CHECK(ensure_ws(L, p));
+        SNACK_CHECK(transpose_pad(X, ws_x(L), B, L->K, p.bp, KC_TRANSPOSE, s));
+        feat = ws_x(L);
+    }
+    return spmm_view(L->fwd, feat, p, B, Y, KC_SPMM_FWD, s);
+}
+
+extern "C" snack_status snack_backward(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
+                                       int32_t B, snack_stream stream)
+{
+    if (!L || !dY || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (dW && !X) return SNACK_ERR_INVALID_ARG;
+    if (!dX && !dW) return SNACK_OK;
+    hipStream_t s = as_stream(stream);
+    const BatchPlan p = plan_batch(B);
+    const float* dyt = dY;
+    const float* xt = X;
+    if (p.bp > 1) {
+        SNACK_CHECK(ensure_ws(L, p));
+        SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), B, L->M, p.bp, KC_TRANSPOSE, s));
+        dyt = ws_dy(L, p);
+        if (dW) {
+            SNACK_CHECK(transpose_pad(X, ws_x(L), B, L->K, p.bp, KC_TRANSPOSE, s));
+            xt = ws_x(L);
+        }
+    }
+    if (dX) {
+        if (L->vals_t_stale) SNACK_CHECK(refresh_vals_t(L, s));
+        SNACK_CHECK(spmm_view(L->tr, dyt, p, B, dX, KC_SPMM_DX, s));
+    }
+    if (dW) SNACK_CHECK(sddmm_dw(L, xt, dyt, p, B, dW, s));
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack_stream stream)
+{
+    if (!L || n_drop < 0 || n_drop > L->nnz) return SNACK_ERR_INVALID_ARG;
+    return snack::prune_regrow(L, n_drop, as_stream(stream));
+}
+
+extern "C" snack_status snack_layer_shape(const snack_layer* L, int32_t* M, int32_t* K)
+{
+    if (!L || !M || !K) return SNACK_ERR_INVALID_ARG;
+    *M = L->M;
+    *K = L->K;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_nnz(const snack_layer* L, int64_t* nnz)
+{
+    if (!L || !nnz) return SNACK_ERR_INVALID_ARG;
+    *nnz = L->nnz;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_device_bytes(const snack_layer* L, int64_t* bytes)
+{
+    if (!L || !bytes) return SNACK_ERR_INVALID_ARG;
+    *bytes = (int64_t)L->device_bytes;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_values(snack_layer* L, float** dev_values)
+{
+    if (!L || !dev_values) return SNACK_ERR_INVALID_ARG;
+    *dev_values = L->vals;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_values_updated(snack_layer* L)
+{
+    if (!L) return SNACK_ERR_INVALID_ARG;
+    L->vals_t_stale = true;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_export(const snack_layer* L, int32_t* rows, int32_t* cols, float* vals,
+                                           snack_stream stream)
+{
+    if (!L) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const size_t n4 = (size_t)L->nnz * 4;
+    if (n4 == 0) return SNACK_OK;
+    if (rows) SNACK_HIP(hipMemcpyAsync(rows, L->rows, n4, hipMemcpyDeviceToDevice, s));
+    if (cols) SNACK_HIP(hipMemcpyAsync(cols, L->cols, n4, hipMemcpyDeviceToDevice, s));
+    if (vals) SNACK_HIP(hipMemcpyAsync(vals, L->vals, n4, hipMemcpyDeviceToDevice, s));
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_export_index(const snack_layer* L, int32_t* row_ptr, int32_t* perm,
+                                                 int32_t* rows_t, int32_t* col_ptr, snack_stream stream)
+{
+    if (!L) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const size_t n4 = (size_t)L->nnz * 4;
+    if (row_ptr) SNACK_HIP(hipMemcpyAsync(row_ptr, L->row_ptr, ((size_t)L->M + 1) * 4, hipMemcpyDeviceToDevice, s));
+    if (col_ptr) SNACK_HIP(hipMemcpyAsync(col_ptr, L->col_ptr, ((size_t)L->K + 1) * 4, hipMemcpyDeviceToDevice, s));
+    if (n4) {
+        if (perm) SNACK_HIP(hipMemcpyAsync(perm, L->perm, n4, hipMemcpyDeviceToDevice, s));
+        if (rows_t) SNACK_HIP(hipMemcpyAsync(rows_t, L->rows_t, n4, hipMemcpyDeviceToDevice, s));
+    }
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_get_epoch(const snack_layer* L, uint64_t* epoch)
+{
+    if (!L || !epoch) return SNACK_ERR_INVALID_ARG;
+    *epoch = L->epoch;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_layer_set_epoch(snack_layer* L, uint64_t epoch)
+{
+    if (!L) return SNACK_ERR_INVALID_ARG;
+    L->epoch = epoch;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_sgd_step(snack_layer* L, const float* dW, float lr, snack_stream stream)
+{
+    if (!L || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
+    return sgd_update(L, dW, lr, as_stream(stream));
+}
+
+extern "C" snack_status snack_mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale,
+                                       snack_stream stream)
+{
+    if (n < 0 || (n > 0 && (!Y || !T || !dY))) return SNACK_ERR_INVALID_ARG;
+    return mse_grad(Y, T, dY, n, scale, as_stream(stream));
+}
+
+extern "C" snack_status snack_gelu_fwd(const float* X, float* Y, int64_t n, snack_stream stream)
+{
+    if (n < 0 || (n > 0 && (!X || !Y))) return SNACK_ERR_INVALID_ARG;
+    return gelu_fwd(X, Y, n, as_stream(stream));
+}
+
+extern "C" snack_status snack_gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, snack_stream stream)
+{
+    if (n < 0 || (n > 0 && (!X || !dY || !dX))) return SNACK_ERR_INVALID_ARG;
+    return gelu_bwd(X, dY, dX, n, as_stream(stream));
+}

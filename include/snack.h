@@ -1,0 +1,184 @@
+/*
+ * snack.h -- C ABI of the MI355X (gfx950) truly sparse COO layer.
+ *
+ * The layer stores its weight W [M x K] (out_features x in_features) only as
+ * the COO triple of its stored positions -- values, row indices, column
+ * indices -- and never materialises W.  This follows the SNACK paper ("Beyond
+ * Masked Sparsity: SNACK Enables Truly Sparse Neural Networks on GPU"),
+ * Figure 1: the block is a drop-in nn.Linear, the forward runs directly on the
+ * triple, the backward is a sparse outer product over supp(W), and DST adds or
+ * drops connections in place.  The transposed index used by the input gradient
+ * is the cached transpose with a permutation map of the "Padded-CSR" post
+ * (section 7.2) and the CSC column of the SNACK paper's Table 7.
+ *
+ * Conventions shared by every entry point:
+ *  - Activations are fp32, contiguous, row-major in the nn.Linear layout:
+ *    X [B, K], Y and dY [B, M], dX [B, K].  No bias.
+ *  - Pointers marked "device" must be device memory on the layer's device,
+ *    "host" host memory.  Device memory passed in stays owned by the caller.
+ *  - `stream` is a hipStream_t (NULL selects the null stream).  Compute entry
+ *    points are asynchronous on that stream; calls on one layer are ordered by
+ *    the stream they are issued on.  A layer is not thread-safe.
+ *  - Every call returns a snack_status.  Host-side argument checks are
+ *    synchronous and leave the layer unchanged.  A HIP launch or runtime error
+ *    is returned as SNACK_ERR_HIP; asynchronous device faults surface at the
+ *    next synchronising call.  No C++ exception crosses this interface.
+ *  - Index type is int32: nnz, M and K must each be below 2^31.
+ *  - Canonical slot order: stored positions sorted by linear position
+ *    row*K + col (row-major: by row, then column), as the sorted COO with a row
+ *    pointer of the "Padded-CSR" post, section 3.2.  Values and dW are always
+ *    in this order.
+ */
+#ifndef SNACK_H
+#define SNACK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum snack_status {
+    SNACK_OK = 0,
+    SNACK_ERR_INVALID_ARG = 1,   /* null pointer, negative size, shape mismatch, bad count */
+    SNACK_ERR_INDEX_RANGE = 2,   /* a row or column index outside the matrix */
+    SNACK_ERR_DUPLICATE = 3,     /* two entries name the same position */
+    SNACK_ERR_ALLOC = 4,         /* device allocation failed */
+    SNACK_ERR_HIP = 5,           /* a HIP runtime or launch error */
+    SNACK_ERR_UNSUPPORTED = 6    /* sizes beyond the int32 index range */
+} snack_status;
+
+typedef struct snack_layer snack_layer;
+typedef void* snack_stream;     /* hipStream_t */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* snack_status_string(snack_status s);
+
+/*
+ * Create a layer from an arbitrary-order COO triple.  SNACK paper, Figure 1
+ * (the weight is the triple over the non-zeros) and "Padded-CSR" section 3.2
+ * (sorted COO + row pointer).
+ *   M, K        out_features, in_features (>= 1).
+ *   nnz         number of stored positions (>= 0, <= M*K).
+ *   rows, cols  device int32[nnz]; 0 <= rows < M, 0 <= cols < K; positions
+ *               distinct (the support is a set).
+ *   vals        device float[nnz], or NULL for all-zero values.
+ *   seed        keys the regrow candidate stream; the epoch starts at 0.
+ * The layer copies the triple (the caller may free its buffers on return),
+ * sorts it into canonical order, builds the row pointer, the transposed index
+ * and its work partition, and synchronises `stream` once to report
+ * SNACK_ERR_INDEX_RANGE / SNACK_ERR_DUPLICATE.  On error *out is set to NULL.
+ */
+snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz,
+                                const int32_t* rows, const int32_t* cols, const float* vals,
+                                uint64_t seed, snack_stream stream, snack_layer** out);
+
+/* Free every buffer of the layer (synchronises the device first).  NULL is a no-op. */
+snack_status snack_layer_destroy(snack_layer* layer);
+
+/*
+ * Pre-size the per-batch workspace (feature-major copies of X and dY) for
+ * batches up to max_batch, so that later forward/backward calls with B <=
+ * max_batch allocate nothing.  A larger B grows the workspace on first use.
+ */
+snack_status snack_layer_reserve(snack_layer* layer, int32_t max_batch);
+
+/*
+ * Forward Y = X W^T.  SNACK paper, Figure 1 (forward on the triple, drop-in
+ * nn.Linear); "Padded-CSR" section 6.1 (each live entry scales one input value
+ * into its output row).
+ *   X  device float[B, K];  Y device float[B, M], overwritten (rows of W with no
+ *   stored position give 0).  1 <= B.  X and Y must not overlap.
+ */
+snack_status snack_forward(snack_layer* layer, const float* X, float* Y, int32_t B, snack_stream stream);
+
+/*
+ * Backward.  "Padded-CSR" section 7.1: dX = dY W (the SpMM with the transpose,
+ * run over the cached transposed index of section 7.2) and dW restricted to the
+ * stored positions, dW[k] = sum_b dY[b, r_k] X[b, c_k]; the SNACK paper's
+ * Figure 1 calls the latter the sparse outer product over supp(W).
+ *   X   device float[B, K] (the forward's input), dY device float[B, M].
+ *   dX  device float[B, K] or NULL (skipped); overwritten.
+ *   dW  device float[nnz] in canonical slot order, or NULL; overwritten (the
+ *       caller accumulates if it wants to).  Stored zeros get a gradient.
+ */
+snack_status snack_backward(snack_layer* layer, const float* X, const float* dY,
+                            float* dX, float* dW, int32_t B, snack_stream stream);
+
+/*
+ * In-place drop / regrow with nnz fixed ("Padded-CSR" section 4.3: drop some
+ * live entries, grow the same number elsewhere; SNACK paper Figure 1: in place
+ * on the triple).  Drops the n_drop entries of smallest |value| -- order key
+ * (IEEE bits of |v|, canonical slot), so -0 ties +0 and NaN is dropped last --
+ * then grows n_drop positions uniformly at random among the positions empty
+ * after the drop, with value +0.0: candidate t of epoch e is SplitMix64 output
+ * number e*2^40 + t of the generator seeded with the layer's seed, mapped onto
+ * [0, M*K) by the high word of the 64x64-bit product; a candidate is accepted
+ * if its position is neither kept nor accepted earlier in the stream.  The
+ * triple is re-canonicalised and the epoch incremented.  0 <= n_drop <= nnz.
+ * May synchronise `stream` (once per candidate batch, normally once).
+ */
+snack_status snack_prune_regrow(snack_layer* layer, int64_t n_drop, snack_stream stream);
+
+/* Shape and size queries (host outputs). */
+snack_status snack_layer_shape(const snack_layer* layer, int32_t* M, int32_t* K);
+snack_status snack_layer_nnz(const snack_layer* layer, int64_t* nnz);
+/* Total bytes the layer holds in device memory (its own allocations). */
+snack_status snack_layer_device_bytes(const snack_layer* layer, int64_t* bytes);
+
+/*
+ * Layer-owned device pointer to the canonical values (float[nnz]).  Valid until
+ * destroy; prune_regrow rewrites its contents in place.  The caller may update
+ * the values through it (an optimiser step) and must then call
+ * snack_layer_values_updated before the next backward.
+ */
+snack_status snack_layer_values(snack_layer* layer, float** dev_values);
+snack_status snack_layer_values_updated(snack_layer* layer);
+
+/* Copy the canonical triple into caller device buffers (checkpointing, parity). */
+snack_status snack_layer_export(const snack_layer* layer, int32_t* rows, int32_t* cols, float* vals,
+                                snack_stream stream);
+
+/*
+ * Copy the index structures into caller device buffers ("Padded-CSR" 3.2 and
+ * 7.2; SNACK Table 7): row_ptr int32[M+1], perm int32[nnz] (transposed slot ->
+ * canonical slot), rows_t int32[nnz] (row of each transposed slot), col_ptr
+ * int32[K+1].  Any pointer may be NULL.
+ */
+snack_status snack_layer_export_index(const snack_layer* layer, int32_t* row_ptr, int32_t* perm,
+                                      int32_t* rows_t, int32_t* col_ptr, snack_stream stream);
+
+/* Epoch = number of prune_regrow calls so far (resume: create + set_epoch). */
+snack_status snack_layer_get_epoch(const snack_layer* layer, uint64_t* epoch);
+snack_status snack_layer_set_epoch(snack_layer* layer, uint64_t epoch);
+
+/*
+ * Training-loop helpers (elementwise fp32; not part of the sparse method).
+ *   snack_sgd_step:  values[k] -= lr * dW[k]   (dW device float[nnz], canonical order)
+ *   snack_mse_grad:  dY[i] = scale * (Y[i] - T[i]), i < n   (MSE mean: scale = 2/n)
+ *   snack_gelu_fwd:  Y = 0.5 X (1 + erf(X / sqrt 2))
+ *   snack_gelu_bwd:  dX = dY * (Phi(X) + X phi(X))
+ */
+snack_status snack_sgd_step(snack_layer* layer, const float* dW, float lr, snack_stream stream);
+snack_status snack_mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale,
+                            snack_stream stream);
+snack_status snack_gelu_fwd(const float* X, float* Y, int64_t n, snack_stream stream);
+snack_status snack_gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, snack_stream stream);
+
+/*
+ * Kernel timing.  While enabled, the library brackets each of its kernel
+ * launches with HIP events recorded on the launch stream; snack_profile_read
+ * synchronises those events and returns, for one kernel class, the launch count
+ * and the summed duration in milliseconds.  Classes are numbered from 0;
+ * snack_profile_name returns NULL past the last one.
+ */
+snack_status snack_profile_enable(int on);
+snack_status snack_profile_reset(void);
+const char* snack_profile_name(int kernel_class);
+snack_status snack_profile_read(int kernel_class, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNACK_H */

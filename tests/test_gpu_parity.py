@@ -1,0 +1,158 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Floating outputs: |gpu - oracle| <= 1e-5 * sum|terms| + 1e-6 per element.
+Integer work (canonical order, row pointer, transposed index): bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from snack_inputs import random_layer, normal, weight_std
+from tests.gpu_util import say, lib, dev, host, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _make(M, K, nnz, key, std=None):
+    rows, cols, vals = random_layer(M, K, nnz, key, std)
+    return rows, cols, vals
+
+
+def _check_layer_vs_oracle(M, K, nnz, batches, key, std=None, check_index=True):
+    import torch
+    L = lib()
+    rows, cols, vals = _make(M, K, nnz, key, std)
+    ref = oracle.canonicalize(M, K, rows, cols, vals)
+    say("create", key, M, K, nnz)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    try:
+        if check_index:
+            r, c, v = layer.export()
+            assert np.array_equal(host(r), ref["rows"])
+            assert np.array_equal(host(c), ref["cols"])
+            assert np.array_equal(host(v).view(np.uint32), ref["vals"].view(np.uint32))
+            rp, pm, rt, cp = layer.export_index()
+            assert np.array_equal(host(rp), ref["row_ptr"])
+            assert np.array_equal(host(cp), ref["col_ptr"])
+            if nnz:
+                assert np.array_equal(host(pm), ref["perm"])
+                assert np.array_equal(host(rt), ref["rows_t"])
+        for B in batches:
+            X = normal((B, K), f"{key}/X/{B}")
+            dY = normal((B, M), f"{key}/dY/{B}")
+            say("forward/backward", key, "B", B)
+            Xd, dYd = dev(X), dev(dY)
+            Y = layer.forward(Xd)
+            dX, dW = layer.backward(Xd, dYd)
+            Yr, Ya = oracle.forward(M, K, ref["rows"], ref["cols"], ref["vals"], X)
+            assert_close(f"Y B={B}", host(Y), Yr, Ya)
+            dXr, dXa = oracle.backward_dx(M, K, ref["rows"], ref["cols"], ref["vals"], dY)
+            assert_close(f"dX B={B}", host(dX), dXr, dXa)
+            dWr, dWa = oracle.backward_dw(M, K, ref["rows"], ref["cols"], X, dY)
+            assert_close(f"dW B={B}", host(dW), dWr, dWa)
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(1, 1, 1), (1, 300, 17), (300, 1, 29), (7, 9, 0), (37, 53, 400),
+                                     (130, 70, 2000), (64, 4096, 20000)])
+def test_small_shapes_all_batch_plans(M, K, nnz):
+    _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 13, 16, 17, 32, 33, 64, 65, 130), f"gpu/small/{M}x{K}")
+
+
+def test_long_rows_and_columns_span_many_chunks():
+    # a row longer than a chunk, a dense column, and many empty rows/columns
+    M, K = 50, 6000
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([np.full(5000, 3), np.arange(50), rng.integers(10, 20, 300)])
+    cols = np.concatenate([np.arange(5000), np.full(50, 5500), rng.integers(5001, 5499, 300)])
+    pos = np.unique(rows.astype(np.int64) * K + cols)
+    rng.shuffle(pos)
+    r, c = (pos // K).astype(np.int32), (pos % K).astype(np.int32)
+    v = rng.standard_normal(pos.shape[0]).astype(np.float32)
+    import torch
+    L = lib()
+    ref = oracle.canonicalize(M, K, r, c, v)
+    say("create long rows", M, K, pos.shape[0])
+    layer = L.SnackLayer(M, K, dev(r), dev(c), dev(v))
+    try:
+        for B in (1, 4, 33):
+            X = normal((B, K), f"long/X/{B}"); dY = normal((B, M), f"long/dY/{B}")
+            say("long rows B", B)
+            Y = layer.forward(dev(X)); dX, dW = layer.backward(dev(X), dev(dY))
+            Yr, Ya = oracle.forward(M, K, ref["rows"], ref["cols"], ref["vals"], X)
+            assert_close("Y", host(Y), Yr, Ya)
+            dXr, dXa = oracle.backward_dx(M, K, ref["rows"], ref["cols"], ref["vals"], dY)
+            assert_close("dX", host(dX), dXr, dXa)
+            dWr, dWa = oracle.backward_dw(M, K, ref["rows"], ref["cols"], X, dY)
+            assert_close("dW", host(dW), dWr, dWa)
+    finally:
+        layer.close()
+
+
+def test_worked_example_exact():
+    # "Padded-CSR" section 6.1, nn.Linear layout: Y^T = [[23, 5, 23], [28, 10, 28]]
+    import torch
+    L = lib()
+    rows = np.array([2, 0, 1, 2, 0], np.int32); cols = np.array([2, 1, 0, 1, 3], np.int32)
+    vals = np.array([4, 3, 5, 1, 2], np.float32)
+    say("worked example")
+    layer = L.SnackLayer(3, 4, dev(rows), dev(cols), dev(vals))
+    X = dev(np.array([[1, 3, 5, 7], [2, 4, 6, 8]], np.float32))
+    Y = host(layer.forward(X))
+    assert Y.tolist() == [[23, 5, 23], [28, 10, 28]]
+    layer.close()
+
+
+def test_integer_data_bit_exact():
+    import torch
+    L = lib()
+    M, K, nnz = 200, 300, 6000
+    rows, cols, _ = random_layer(M, K, nnz, "gpu/int")
+    rng = np.random.default_rng(11)
+    vals = rng.integers(-8, 9, nnz).astype(np.float32)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    ref = oracle.canonicalize(M, K, rows, cols, vals)
+    for B in (1, 3, 64):
+        X = rng.integers(-8, 9, (B, K)).astype(np.float32)
+        dY = rng.integers(-8, 9, (B, M)).astype(np.float32)
+        say("integer exact B", B)
+        Y = layer.forward(dev(X)); dX, dW = layer.backward(dev(X), dev(dY))
+        Yr, _ = oracle.forward(M, K, ref["rows"], ref["cols"], ref["vals"], X)
+        dXr, _ = oracle.backward_dx(M, K, ref["rows"], ref["cols"], ref["vals"], dY)
+        dWr, _ = oracle.backward_dw(M, K, ref["rows"], ref["cols"], X, dY)
+        assert np.array_equal(host(Y).astype(np.float64), Yr)
+        assert np.array_equal(host(dX).astype(np.float64), dXr)
+        assert np.array_equal(host(dW).astype(np.float64), dWr)
+    layer.close()
+
+
+def test_repeat_runs_bit_identical():
+    import torch
+    L = lib()
+    M, K, nnz = 3000, 2000, 300000
+    rows, cols, vals = random_layer(M, K, nnz, "gpu/det")
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    for B in (1, 16, 64):
+        X = dev(normal((B, K), "det/X")); dY = dev(normal((B, M), "det/dY"))
+        say("determinism B", B)
+        a = [host(t) for t in (layer.forward(X),) + layer.backward(X, dY)]
+        for _ in range(3):
+            b = [host(t) for t in (layer.forward(X),) + layer.backward(X, dY)]
+            for x, y in zip(a, b):
+                assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    layer.close()
+
+
+def test_create_errors_leave_no_layer():
+    L = lib()
+    say("create errors")
+    with pytest.raises(L.SnackError) as e:
+        L.SnackLayer(4, 4, dev(np.array([0, 4], np.int32)), dev(np.array([0, 0], np.int32)))
+    assert e.value.code == L.ERR_INDEX_RANGE
+    with pytest.raises(L.SnackError) as e:
+        L.SnackLayer(4, 4, dev(np.array([1, 2, 1], np.int32)), dev(np.array([3, 3, 3], np.int32)))
+    assert e.value.code == L.ERR_DUPLICATE
+    with pytest.raises(L.SnackError) as e:
+        L.SnackLayer(4, 4, dev(np.array([1, -1], np.int32)), dev(np.array([3, 3], np.int32)))
+    assert e.value.code == L.ERR_INDEX_RANGE

@@ -1,0 +1,59 @@
+"""Drop / regrow on the GPU vs the oracle: bit-exact triples and index."""
+import numpy as np
+import pytest
+
+import oracle
+from snack_inputs import random_layer
+from tests.gpu_util import say, lib, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(M, K, nnz, fracs, key, seed=12345, vals=None, rounds=1):
+    L = lib()
+    rows, cols, v = random_layer(M, K, nnz, key)
+    if vals is not None:
+        v = vals
+    ref = oracle.canonicalize(M, K, rows, cols, v)
+    say("prune create", key, M, K, nnz)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(v), seed=seed)
+    cur = (ref["rows"], ref["cols"], ref["vals"])
+    try:
+        epoch = 0
+        for _ in range(rounds):
+            for frac in fracs:
+                n_drop = int(nnz * frac)
+                say("prune", key, "n_drop", n_drop, "epoch", epoch)
+                layer.prune_regrow(n_drop)
+                o = oracle.prune_regrow(M, K, cur[0], cur[1], cur[2], n_drop, seed, epoch)
+                epoch += 1
+                r, c, vv = (host(t) for t in layer.export())
+                assert np.array_equal(r, o[0]) and np.array_equal(c, o[1])
+                assert np.array_equal(vv.view(np.uint32), o[2].view(np.uint32))
+                assert layer.epoch == epoch
+                cur = o[:3]
+                ci = oracle.canonicalize(M, K, *cur)
+                rp, pm, rt, cp = (host(t) for t in layer.export_index())
+                assert np.array_equal(rp, ci["row_ptr"]) and np.array_equal(cp, ci["col_ptr"])
+                if nnz:
+                    assert np.array_equal(pm, ci["perm"]) and np.array_equal(rt, ci["rows_t"])
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(6, 5, 14), (40, 30, 300), (500, 500, 12500), (64, 64, 4096),
+                                     (3000, 700, 105000)])
+def test_prune_regrow_matches_oracle(M, K, nnz):
+    _run(M, K, nnz, (0.3, 0.0, 0.5, 1.0), f"gpu/prune/{M}x{K}")
+
+
+def test_prune_ties_signed_zero_nan():
+    M, K, nnz = 30, 40, 600
+    rng = np.random.default_rng(3)
+    vals = rng.choice(np.array([0.0, -0.0, 0.25, -0.25, 1.0, np.nan, 2.0], np.float32), nnz)
+    _run(M, K, nnz, (0.1, 0.3, 0.6), "gpu/prune/ties", vals=vals)
+
+
+def test_prune_full_scale_10000_square():
+    # 10000 x 10000 at 95 %: drop 30 % of 5,000,000 twice (two epochs)
+    _run(10000, 10000, 5_000_000, (0.3,), "gpu/prune/c4", rounds=2)
