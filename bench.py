@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse COO layer's hot path on one MI355X.
+
+Workload: one 10000 x 10000 layer at 95 % unstructured sparsity (nnz =
+5,000,000 uniform random positions), fp32 values, int32 indices, trained with
+the batch sweep B in {1, 2, 4, 8, 16, 32, 64}.  One *step* is one training
+iteration at every batch size of the sweep, each iteration being forward
+Y = X W^T, MSE gradient, backward (dX and dW on the support) and an SGD update
+(lr 0.01) of the values; after every 10th iteration the layer drops the 30 %
+smallest-|w| entries and regrows as many at random empty positions (SET-style,
+nnz fixed).  Inputs are synthetic (seeded N(0,1) activations and targets) and
+resident in device memory before the timed region starts.
+
+Printed: one JSON line.  `value` is the achieved algorithmic bandwidth over
+the timed region -- the bytes the method must move for forward + backward
+(28 nnz + 4 B (3K + 2M)), the MSE gradient (12 B M) and SGD (12 nnz), per
+iteration, divided by the wall time of the whole timed region, which also
+contains the drop/regrow calls (they add time but no credited bytes).
+`per_batch` gives forward+backward microseconds per iteration from HIP events
+(fwd, dX, dW and their activation transposes), `roofline` the dominant kernel
+against the 8 TB/s HBM peak, and `cpu_baseline` the fp64 oracle timed on one
+host core on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SpMM fwd+bwd µs/iter + achieved GB/s, 10000² at 95% sparse, batch 1–64"
+HBM_PEAK_GBPS = 8000.0
+
+
+def fwd_bwd_bytes(nnz, M, K, B):
+    return 28 * nnz + 4 * B * (3 * K + 2 * M)
+
+
+def kernel_bytes(kind, nnz, M, K, B):
+    # per launch, algorithmic: the triple (12 B / entry) plus the dense operands once
+    if kind == "spmm_forward":
+        return 12 * nnz + 4 * B * (K + M)
+    if kind == "spmm_dx":
+        return 12 * nnz + 4 * B * (M + K)
+    if kind == "sddmm_dw":
+        return 12 * nnz + 4 * B * (M + K)
+    raise KeyError(kind)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batches", default="1,2,4,8,16,32,64")
+    ap.add_argument("--prune-every", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="time without per-kernel HIP events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import coo_spmm_amd as L
+    from snack_inputs import normal, random_layer, weight_std
+
+    torch.cuda.set_device(0)
+    M = K = 10000
+    sparsity = 95
+    nnz = M * K * (100 - sparsity) // 100
+    batches = [int(b) for b in args.batches.split(",")]
+    n_drop = nnz * 3 // 10
+    lr = 0.01
+
+    rows, cols, vals = random_layer(M, K, nnz, "c4/s95", weight_std(K, sparsity))
+    layer = L.SnackLayer(M, K, torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda(),
+                         torch.from_numpy(vals).cuda(), seed=2024)
+    layer.reserve(max(batches))
+    bufs = {}
+    for B in batches:
+        X = torch.from_numpy(normal((B, K), f"c4/X/{B}")).cuda()
+        T = torch.from_numpy(normal((B, M), f"c4/T/{B}")).cuda()
+        bufs[B] = dict(X=X, T=T, Y=torch.empty(B, M, device="cuda"), dY=torch.empty(B, M, device="cuda"),
+                       dX=torch.empty(B, K, device="cuda"), dW=torch.empty(nnz, device="cuda"))
+    stream = torch.cuda.current_stream()
+
+    it_counter = [0]
+
+    def iteration(B):
+        b = bufs[B]
+        L.snack_forward(layer.h, b["X"], b["Y"], stream)
+        L.snack_mse_grad(b["Y"], b["T"], b["dY"], 2.0 / (B * M), stream)
+        L.snack_backward(layer.h, b["X"], b["dY"], b["dX"], b["dW"], stream)
+        L.snack_sgd_step(layer.h, b["dW"], lr, stream)
+        it_counter[0] += 1
+        if args.prune_every > 0 and it_counter[0] % args.prune_every == 0:
+            L.snack_profile_set_tag(-1)
+            L.snack_prune_regrow(layer.h, n_drop, stream)
+
+    def step():
+        for B in batches:
+            L.snack_profile_set_tag(B)
+            iteration(B)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    cls = L.profile_class_ids()
+    L.snack_profile_reset()
+    L.snack_profile_enable(not args.no_profile)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.snack_profile_enable(False)
+    wall = t1 - t0
+
+    iters_per_b = args.steps
+    credited = sum((fwd_bwd_bytes(nnz, M, K, B) + 12 * B * M + 12 * nnz) * iters_per_b for B in batches)
+    value_gbps = credited / wall / 1e9
+
+    per_batch = {}
+    dominant = None
+    for B in batches:
+        d = {}
+        tot_us = 0.0
+        for name in ("spmm_forward", "spmm_dx", "sddmm_dw", "transpose", "vals_t_refresh", "sgd", "elementwise"):
+            n, ms = L.snack_profile_read_tag(cls[name], B)
+            d[name + "_us"] = round(ms * 1e3 / max(iters_per_b, 1), 3)
+            if name in ("spmm_forward", "spmm_dx", "sddmm_dw", "transpose", "vals_t_refresh"):
+                tot_us += ms * 1e3 / max(iters_per_b, 1)
+            if name in ("spmm_forward", "spmm_dx", "sddmm_dw") and n > 0:
+                if dominant is None or ms > dominant[3]:
+                    dominant = (name, B, n, ms)
+        d["fwd_bwd_us"] = round(tot_us, 3)
+        if tot_us > 0:
+            gbps = fwd_bwd_bytes(nnz, M, K, B) / (tot_us * 1e-6) / 1e9
+            d["fwd_bwd_GBps"] = round(gbps, 1)
+            d["fwd_bwd_frac_of_hbm"] = round(gbps / HBM_PEAK_GBPS, 4)
+        per_batch[str(B)] = d
+    n_pr, ms_pr = L.snack_profile_read_tag(cls["prune_regrow"], -1)
+
+    roofline = None
+    if dominant is not None:
+        name, B, n, ms = dominant
+        per_launch = kernel_bytes(name, nnz, M, K, B)
+        achieved = per_launch * n / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": f"{name} (B={B})", "avg_launch_us": round(ms * 1e3 / n, 3),
+                    "bytes_per_launch": per_launch}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": ("10000x10000 COO layer, 95% sparse (nnz 5,000,000), batch sweep "
+                                f"{'/'.join(map(str, batches))}; fwd + MSE grad + bwd(dX, dW) + SGD per batch; "
+                                f"drop/regrow 30% every {args.prune_every} iterations"),
+                   "M": M, "K": K, "nnz": nnz, "batches": batches, "n_drop": n_drop, "lr": lr,
+                   "parallelism": "single GPU"},
+        "per_batch": per_batch,
+        "prune_regrow_us_per_call": round(ms_pr * 1e3 / n_pr, 1) if n_pr else None,
+        "prune_regrow_calls": n_pr,
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layer, M, K, nnz, batches, lr)
+
+    layer.close()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layer, M, K, nnz, batches, lr, min_seconds=10.0, max_steps=20):
+    """The fp64 oracle as it stands, one host core, on a bounded sample of the
+    workload: whole sweep steps (forward, MSE gradient, dX, dW and SGD for every
+    batch size, no drop/regrow) repeated until about ten seconds have passed."""
+    import numpy as np
+
+    import oracle
+    from snack_inputs import normal
+
+    r, c, v = (t.cpu().numpy() for t in layer.export())
+    inputs = [(B, normal((B, K), f"c4/X/{B}"), normal((B, M), f"c4/T/{B}")) for B in batches]
+    credited = 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for B, X, T in inputs:
+            Y, _ = oracle.forward(M, K, r, c, v, X)
+            dY = oracle.mse_grad(Y.astype(np.float32), T).astype(np.float32)
+            oracle.backward_dx(M, K, r, c, v, dY)
+            dW, _ = oracle.backward_dw(M, K, r, c, X, dY)
+            v = oracle.sgd(v, dW.astype(np.float32), lr).astype(np.float32)
+            credited += fwd_bwd_bytes(nnz, M, K, B) + 12 * B * M + 12 * nnz
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or steps >= max_steps:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": round(credited / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d sweep step(s) (fwd, MSE grad, dX, dW, SGD for B = %s) without drop/regrow; "
+                      "single-threaded fp64 C oracle; %.1f s; host has %s usable cores"
+                      % (steps, "/".join(map(str, batches)), dt, cores),
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

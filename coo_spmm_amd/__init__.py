@@ -52,6 +52,8 @@ _SIGS = {
     "snack_profile_reset": ([], ST),
     "snack_profile_name": ([ctypes.c_int], ctypes.c_char_p),
     "snack_profile_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(f64)], ST),
+    "snack_profile_set_tag": ([i64], ST),
+    "snack_profile_read_tag": ([ctypes.c_int, i64, ctypes.POINTER(i64), ctypes.POINTER(f64)], ST),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -225,6 +227,27 @@ def snack_profile_read(k):
     n, ms = i64(), f64()
     _check(_lib.snack_profile_read(k, ctypes.byref(n), ctypes.byref(ms)), "snack_profile_read")
     return n.value, ms.value
+
+
+def snack_profile_set_tag(tag):
+    _check(_lib.snack_profile_set_tag(int(tag)), "snack_profile_set_tag")
+
+
+def snack_profile_read_tag(k, tag):
+    n, ms = i64(), f64()
+    _check(_lib.snack_profile_read_tag(k, int(tag), ctypes.byref(n), ctypes.byref(ms)), "snack_profile_read_tag")
+    return n.value, ms.value
+
+
+def profile_class_ids():
+    """{kernel class name: id}."""
+    out, k = {}, 0
+    while True:
+        name = snack_profile_name(k)
+        if name is None:
+            return out
+        out[name] = k
+        k += 1
 
 
 def profile_snapshot():

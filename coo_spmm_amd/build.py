@@ -1,6 +1,7 @@
 """Build libsnack.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m coo_spmm_amd.build   (always recompiles)
+Usage: python coo_spmm_amd/build.py   (always recompiles; run by path so that a
+stale library is never imported first)
 """
 from __future__ import annotations
 

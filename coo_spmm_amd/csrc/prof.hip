@@ -2,13 +2,16 @@
 // launch stream around each library launch.
 #include "internal.h"
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 namespace snack {
 namespace {
 
 struct Rec {
     int k;
+    int64_t tag;
     hipEvent_t a, b;
 };
 
@@ -19,6 +22,8 @@ std::vector<Rec> g_done;          // ended, not yet read
 std::vector<hipEvent_t> g_pool;   // reusable events
 int64_t g_count[KC_COUNT];
 double g_ms[KC_COUNT];
+int64_t g_tag = 0;
+std::map<std::pair<int, int64_t>, std::pair<int64_t, double>> g_tagged;
 
 const char* const g_names[KC_COUNT] = {"spmm_forward", "spmm_dx", "sddmm_dw", "transpose", "vals_t_refresh",
                                        "sgd", "elementwise", "radix_sort", "canonicalise", "prune_regrow"};
@@ -43,6 +48,12 @@ void drain_locked()
             if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
                 g_ms[r.k] += ms;
                 g_count[r.k] += 1;
+                auto key = std::make_pair(r.k, r.tag);
+                if (g_tagged.count(key) || g_tagged.size() < 1024 * KC_COUNT) {
+                    auto& t = g_tagged[key];
+                    t.first += 1;
+                    t.second += ms;
+                }
             }
         }
         if (r.a) g_pool.push_back(r.a);
@@ -58,7 +69,7 @@ bool prof_on() { return g_on; }
 void prof_begin(int kclass, hipStream_t s)
 {
     std::lock_guard<std::mutex> lk(g_mu);
-    Rec r{kclass, get_event(), nullptr};
+    Rec r{kclass, g_tag, get_event(), nullptr};
     if (r.a) hipEventRecord(r.a, s);
     g_open.push_back(r);
 }
@@ -99,6 +110,7 @@ extern "C" snack_status snack_profile_reset(void)
         g_count[i] = 0;
         g_ms[i] = 0.0;
     }
+    g_tagged.clear();
     return SNACK_OK;
 }
 
@@ -115,5 +127,23 @@ extern "C" snack_status snack_profile_read(int kernel_class, int64_t* launches, 
     drain_locked();
     *launches = g_count[kernel_class];
     *total_ms = g_ms[kernel_class];
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_profile_set_tag(int64_t tag)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_tag = tag;
+    return SNACK_OK;
+}
+
+extern "C" snack_status snack_profile_read_tag(int kernel_class, int64_t tag, int64_t* launches, double* total_ms)
+{
+    if (kernel_class < 0 || kernel_class >= KC_COUNT || !launches || !total_ms) return SNACK_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    drain_locked();
+    auto it = g_tagged.find(std::make_pair(kernel_class, tag));
+    *launches = it == g_tagged.end() ? 0 : it->second.first;
+    *total_ms = it == g_tagged.end() ? 0.0 : it->second.second;
     return SNACK_OK;
 }

@@ -176,6 +176,14 @@ snack_status snack_profile_enable(int on);
 snack_status snack_profile_reset(void);
 const char* snack_profile_name(int kernel_class);
 snack_status snack_profile_read(int kernel_class, int64_t* launches, double* total_ms);
+/*
+ * Tagged timing: launches made after snack_profile_set_tag(t) are also counted
+ * under (kernel_class, t); snack_profile_read_tag returns those totals.  Tags
+ * are caller-chosen integers (for example the batch size); at most 1024
+ * distinct tags are kept.
+ */
+snack_status snack_profile_set_tag(int64_t tag);
+snack_status snack_profile_read_tag(int kernel_class, int64_t tag, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

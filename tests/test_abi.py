@@ -18,8 +18,8 @@ def _declared():
 
 def _ensure_built():
     if not os.path.exists(LIB):
-        from coo_spmm_amd.build import build
-        build()
+        import __graft_entry__
+        __graft_entry__._builder().build()
 
 
 def test_header_declares_the_core_entry_points():
