@@ -41,7 +41,7 @@ _SIGS = {
     "snack_layer_values": ([P, ctypes.POINTER(P)], ST),
     "snack_layer_values_updated": ([P], ST),
     "snack_layer_export": ([P, P, P, P, P], ST),
-    "snack_layer_export_index": ([P, P, P, P, P, P], ST),
+    "snack_layer_export_index": ([P, P, P, P, P, P, P], ST),
     "snack_layer_get_epoch": ([P, ctypes.POINTER(u64)], ST),
     "snack_layer_set_epoch": ([P, u64], ST),
     "snack_sgd_step": ([P, P, f32, P], ST),
@@ -178,8 +178,8 @@ def snack_layer_export(h, rows, cols, vals, stream=None):
     _check(_lib.snack_layer_export(h, _ptr(rows), _ptr(cols), _ptr(vals), _stream(stream)), "snack_layer_export")
 
 
-def snack_layer_export_index(h, row_ptr, perm, rows_t, col_ptr, stream=None):
-    _check(_lib.snack_layer_export_index(h, _ptr(row_ptr), _ptr(perm), _ptr(rows_t), _ptr(col_ptr),
+def snack_layer_export_index(h, row_ptr, perm, rows_t, col_ptr, vals_t=None, stream=None):
+    _check(_lib.snack_layer_export_index(h, _ptr(row_ptr), _ptr(perm), _ptr(rows_t), _ptr(col_ptr), _ptr(vals_t),
                                          _stream(stream)), "snack_layer_export_index")
 
 
@@ -314,13 +314,18 @@ class SnackLayer:
         snack_layer_export(self.h, r, c, v, stream)
         return r, c, v
 
-    def export_index(self, device="cuda", stream=None):
+    def export_index(self, device="cuda", stream=None, with_values=False):
         import torch
         rp = torch.empty(self.M + 1, dtype=torch.int32, device=device)
         pm = torch.empty(self.nnz, dtype=torch.int32, device=device)
         rt = torch.empty(self.nnz, dtype=torch.int32, device=device)
         cp = torch.empty(self.K + 1, dtype=torch.int32, device=device)
-        snack_layer_export_index(self.h, rp, pm if self.nnz else None, rt if self.nnz else None, cp, stream)
+        vt = torch.empty(self.nnz, dtype=torch.float32, device=device)
+        ok = self.nnz > 0
+        snack_layer_export_index(self.h, rp, pm if ok else None, rt if ok else None, cp,
+                                 vt if (ok and with_values) else None, stream)
+        if with_values:
+            return rp, pm, rt, cp, vt
         return rp, pm, rt, cp
 
     def values_ptr(self):

@@ -20,11 +20,19 @@ inline unsigned grid_for(int64_t n)
 }
 
 // dst[c * bp + b] = (b < B) ? src[b * n + c] : 0 ; one 64 x 64 tile per block via LDS.
-__global__ void __launch_bounds__(kThreads) transpose_pad_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                                 int B, int n, int bp)
+// Blocks [0, nx1) handle (src, dst, n), the rest (src2, dst2, n2).
+__global__ void __launch_bounds__(kThreads) transpose_pad_kernel(const float* __restrict__ src1,
+                                                                 float* __restrict__ dst1, int n1,
+                                                                 const float* __restrict__ src2,
+                                                                 float* __restrict__ dst2, int n2, int nx1, int B,
+                                                                 int bp)
 {
     __shared__ float tile[kTile][kTile + 1];
-    const int c0 = blockIdx.x * kTile;
+    const bool first = (int)blockIdx.x < nx1;
+    const float* __restrict__ src = first ? src1 : src2;
+    float* __restrict__ dst = first ? dst1 : dst2;
+    const int n = first ? n1 : n2;
+    const int c0 = (first ? (int)blockIdx.x : (int)blockIdx.x - nx1) * kTile;
     const int b0 = blockIdx.y * kTile;
     const int tx = threadIdx.x & (kTile - 1);
     const int ty = threadIdx.x / kTile;   // 0..3
@@ -41,10 +49,38 @@ __global__ void __launch_bounds__(kThreads) transpose_pad_kernel(const float* __
     }
 }
 
-__global__ void sgd_kernel(float* __restrict__ v, const float* __restrict__ g, float lr, int64_t n)
+__global__ void sgd_kernel(float* __restrict__ v, const float* __restrict__ g, float lr, int64_t n, int vec)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    const int64_t n4 = vec ? n / 4 : 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 a = reinterpret_cast<float4*>(v)[i];
+        const float4 d = reinterpret_cast<const float4*>(g)[i];
+        a.x = a.x - lr * d.x; a.y = a.y - lr * d.y; a.z = a.z - lr * d.z; a.w = a.w - lr * d.w;
+        reinterpret_cast<float4*>(v)[i] = a;
+    }
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         v[i] = v[i] - lr * g[i];
+}
+
+// both value copies in one launch: (v, g) and (v2, g2), each n long
+__global__ void sgd2_kernel(float* __restrict__ v, const float* __restrict__ g, float* __restrict__ v2,
+                            const float* __restrict__ g2, float lr, int64_t n)
+{
+    const int64_t n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const bool second = i >= n4;
+        const int64_t j = second ? i - n4 : i;
+        float4* __restrict__ pv = reinterpret_cast<float4*>(second ? v2 : v);
+        const float4* __restrict__ pg = reinterpret_cast<const float4*>(second ? g2 : g);
+        float4 a = pv[j];
+        const float4 d = pg[j];
+        a.x = a.x - lr * d.x; a.y = a.y - lr * d.y; a.z = a.z - lr * d.z; a.w = a.w - lr * d.w;
+        pv[j] = a;
+    }
+    for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        v[i] = v[i] - lr * g[i];
+        v2[i] = v2[i] - lr * g2[i];
+    }
 }
 
 __global__ void mse_grad_kernel(const float* __restrict__ Y, const float* __restrict__ T, float* __restrict__ dY,
@@ -75,22 +111,37 @@ __global__ void gelu_bwd_kernel(const float* __restrict__ X, const float* __rest
 
 }  // namespace
 
-snack_status transpose_pad(const float* src, float* dst, int B, int n, int bp, int kclass, hipStream_t s)
+snack_status transpose_pad(const float* src, float* dst, int n, const float* src2, float* dst2, int n2, int B,
+                           int bp, hipStream_t s)
 {
-    ProfScope prof(kclass, s);
-    dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((bp + kTile - 1) / kTile));
-    hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(kThreads), 0, s, src, dst, B, n, bp);
+    ProfScope prof(KC_TRANSPOSE, s);
+    const int nx1 = (n + kTile - 1) / kTile;
+    const int nx2 = src2 ? (n2 + kTile - 1) / kTile : 0;
+    dim3 grid((unsigned)(nx1 + nx2), (unsigned)((bp + kTile - 1) / kTile));
+    hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(kThreads), 0, s, src, dst, n, src2, dst2, n2, nx1, B, bp);
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }
 
-snack_status sgd_update(snack_layer* L, const float* dW, float lr, hipStream_t s)
+snack_status sgd_update(snack_layer* L, const float* dW, const float* dW_t, float lr, hipStream_t s)
 {
     if (L->nnz == 0) return SNACK_OK;
     ProfScope prof(KC_SGD, s);
-    hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->vals, dW, lr, L->nnz);
+    const bool aligned = (((uintptr_t)dW | (uintptr_t)dW_t) & 15) == 0;
+    if (dW_t && aligned) {
+        unsigned g = grid_for(L->nnz / 2 + 1);
+        hipLaunchKernelGGL(sgd2_kernel, dim3(g), dim3(kThreads), 0, s, L->vals, dW, L->vals_t, dW_t, lr, L->nnz);
+    } else {
+        hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(L->nnz / 4 + 1)), dim3(kThreads), 0, s, L->vals, dW, lr,
+                           L->nnz, aligned ? 1 : 0);
+        if (dW_t) {
+            hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(L->nnz / 4 + 1)), dim3(kThreads), 0, s, L->vals_t, dW_t, lr,
+                               L->nnz, 1);
+        } else {
+            L->vals_t_stale = true;
+        }
+    }
     SNACK_HIP(hipGetLastError());
-    L->vals_t_stale = true;
     return SNACK_OK;
 }
 

@@ -6,9 +6,10 @@
 // sorted by (column, row) together with the permutation map of section 7.2
 // (transposed slot -> canonical slot) and the column pointer (the CSC of the
 // SNACK paper's Table 7).  Both views carry a key-aligned work partition:
-// chunk c owns keys [chunk_key[c], chunk_key[c+1]), cut so that each chunk
-// holds about kChunkWork units of (entries + keys); a row is never split, so
-// the SpMM needs no cross-chunk fix-up and writes every output row once.
+// desc[c] = (first key, first entry) of chunk c, cut so that each chunk holds
+// about kChunkWork units of (entries + keys); a key is never split, so the
+// SpMM needs no cross-chunk fix-up and writes every output row once.  Each view
+// also lists its keys without entries, whose outputs are zero.
 #include "internal.h"
 
 namespace snack {
@@ -78,25 +79,39 @@ __global__ void build_ptr_kernel(const int32_t* __restrict__ keys, int64_t nnz, 
     }
 }
 
-// chunk_key[c] = smallest key r with ptr[r] + r >= c * work, chunk_key[nchunks] = nkeys.
+// desc[c] = (r, ptr[r]) with r the smallest key such that ptr[r] + r >= c * work;
+// desc[nchunks] = (nkeys, nnz).
 __global__ void build_chunks_kernel(const int32_t* __restrict__ ptr, int32_t nkeys, int32_t nchunks, int32_t work,
-                                    int32_t* __restrict__ chunk_key)
+                                    int2* __restrict__ desc)
 {
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c <= nchunks;
          c += (int64_t)gridDim.x * blockDim.x) {
-        if (c == nchunks) {
-            chunk_key[c] = nkeys;
-            continue;
+        int32_t key = nkeys;
+        if (c < nchunks) {
+            const int64_t target = c * (int64_t)work;
+            int32_t lo = 0, hi = nkeys;
+            while (lo < hi) {
+                const int32_t mid = lo + ((hi - lo) >> 1);
+                if ((int64_t)ptr[mid] + mid >= target) hi = mid;
+                else lo = mid + 1;
+            }
+            key = lo;
         }
-        const int64_t target = c * (int64_t)work;
-        int32_t lo = 0, hi = nkeys;
-        while (lo < hi) {
-            const int32_t mid = lo + ((hi - lo) >> 1);
-            if ((int64_t)ptr[mid] + mid >= target) hi = mid;
-            else lo = mid + 1;
-        }
-        chunk_key[c] = lo;
+        desc[c] = make_int2(key, ptr[key]);
     }
+}
+
+__global__ void empty_flags_kernel(const int32_t* __restrict__ ptr, int32_t nkeys, int32_t* __restrict__ flags)
+{
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nkeys; r += (int64_t)gridDim.x * blockDim.x)
+        flags[r] = ptr[r] == ptr[r + 1] ? 1 : 0;
+}
+
+__global__ void empty_compact_kernel(const int32_t* __restrict__ flags, const int32_t* __restrict__ pos,
+                                     int32_t nkeys, int32_t* __restrict__ out)
+{
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nkeys; r += (int64_t)gridDim.x * blockDim.x)
+        if (flags[r]) out[pos[r]] = (int32_t)r;
 }
 
 __global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, uint32_t* __restrict__ keys,
@@ -129,12 +144,18 @@ __global__ void refresh_vals_t_kernel(const int32_t* __restrict__ perm, const fl
         vals_t[j] = vals[perm[j]];
 }
 
-snack_status build_view_partition(View& v, int64_t nnz, hipStream_t s)
+snack_status build_view_partition(View& v, void* scratch, hipStream_t s)
 {
     hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)v.nchunks + 1)), dim3(kThreads), 0, s, v.ptr,
-                       v.nkeys, v.nchunks, kChunkWork, v.chunk_key);
+                       v.nkeys, v.nchunks, kChunkWork, v.desc);
+    int32_t* flags = (int32_t*)scratch;
+    int32_t* pos = flags + (((size_t)v.nkeys + 63) & ~(size_t)63);
+    void* scan_scr = pos + (((size_t)v.nkeys + 63) & ~(size_t)63);
+    hipLaunchKernelGGL(empty_flags_kernel, dim3(grid_for(v.nkeys)), dim3(kThreads), 0, s, v.ptr, v.nkeys, flags);
+    SNACK_CHECK(exclusive_scan_i32(flags, pos, v.nkeys, v.n_empty, scan_scr, s));
+    hipLaunchKernelGGL(empty_compact_kernel, dim3(grid_for(v.nkeys)), dim3(kThreads), 0, s, flags, pos, v.nkeys,
+                       v.empty_keys);
     SNACK_HIP(hipGetLastError());
-    (void)nnz;
     return SNACK_OK;
 }
 
@@ -149,7 +170,10 @@ size_t canon_scratch_bytes(const snack_layer* L, int64_t nnz)
     b += ((size_t)nnz * kw + 255) & ~(size_t)255;     // keys
     b += ((size_t)nnz * 4 + 255) & ~(size_t)255;      // slots
     b += radix_sort_scratch_bytes(nnz, kb);
-    return b + 256;
+    // empty-key lists of the two views
+    const int64_t nk = L->M > L->K ? L->M : L->K;
+    const size_t e = 2 * (((size_t)nk + 63) & ~(size_t)63) * 4 + scan_scratch_bytes(nk) + 256;
+    return (b > e ? b : e) + 256;
 }
 
 snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t* cols, const float* vals,
@@ -214,8 +238,8 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
                        L->col_ptr);
     SNACK_HIP(hipGetLastError());
     L->vals_t_stale = false;
-    SNACK_CHECK(build_view_partition(L->fwd, nnz, s));
-    SNACK_CHECK(build_view_partition(L->tr, nnz, s));
+    SNACK_CHECK(build_view_partition(L->fwd, L->scratch, s));
+    SNACK_CHECK(build_view_partition(L->tr, L->scratch, s));
     return SNACK_OK;
 }
 

@@ -13,8 +13,8 @@
 namespace snack {
 
 constexpr int kWave = 64;              // CDNA wavefront width
-constexpr int kChunkWork = 1024;       // target work (nnz + rows) per SpMM chunk
-constexpr int kPad = 1024;             // slack elements after every nnz-sized array
+constexpr int kChunkWork = 512;        // target work (entries + keys) per SpMM chunk
+constexpr int kPad = 2048;             // slack elements after every nnz-sized array
 
 // Kernel classes for the profiling hooks (order = snack_profile_name ids).
 enum KernelClass : int {
@@ -42,7 +42,9 @@ struct View {
     float* vals = nullptr;
     int32_t* ptr = nullptr;         // [nkeys + 1]
     int32_t nchunks = 0;
-    int32_t* chunk_key = nullptr;   // [nchunks + 1], first key of each chunk
+    int2* desc = nullptr;           // [nchunks + 1]: (first key, first entry) of each chunk
+    int32_t* empty_keys = nullptr;  // [nkeys]: keys with no entry, ascending
+    int32_t* n_empty = nullptr;     // device count of empty_keys
 };
 
 struct Scratch {
@@ -72,6 +74,11 @@ struct snack_layer {
     float* vals_t = nullptr;      // values in transposed order
     int32_t* col_ptr = nullptr;   // [K+1]
     bool vals_t_stale = true;
+    // dW in transposed order from the last backward (bit-identical to the
+    // canonical dW it was produced with); lets SGD update both value copies
+    float* dwt = nullptr;
+    const float* dwt_for = nullptr;
+    bool dwt_valid = false;
 
     snack::View fwd;   // keys = rows, idx = cols
     snack::View tr;    // keys = cols_t, idx = rows_t
@@ -165,18 +172,27 @@ struct BatchPlan {
 };
 BatchPlan plan_batch(int B);
 
-// dst[c * bp + b] = src[b * n + c] for b < B, 0 for B <= b < bp  (src [B, n])
-snack_status transpose_pad(const float* src, float* dst, int B, int n, int bp, int kclass, hipStream_t s);
+// dst[c * bp + b] = src[b * n + c] for b < B, 0 for B <= b < bp  (src [B, n]); the
+// second pair (src2 may be null) is transposed by the same launch
+snack_status transpose_pad(const float* src, float* dst, int n, const float* src2, float* dst2, int n2, int B,
+                           int bp, hipStream_t s);
 
-// out[b, key] = sum over the view's entries of that key of v * feat[idx, b]
-snack_status spmm_view(const snack::View& v, const float* feat_t, const BatchPlan& p, int B, float* out,
-                       int kclass, hipStream_t s);
+// Y[b, key] = sum over the canonical view's entries of v * Xt[idx, b]
+snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
+                          hipStream_t s);
 
-// dW[k] = sum_b dYt[r_k, b] * Xt[c_k, b] in canonical order
-snack_status sddmm_dw(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
-                      float* dW, hipStream_t s);
+// one launch: dX over the transposed view (plus dW in transposed order when
+// dW_t is non-null) and dW over the canonical view; either output may be null.
+// Requires a single batch tile when dW or dW_t is requested.
+snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
+                                 float* dX, float* dW, float* dW_t, hipStream_t s);
 
-snack_status sgd_update(snack_layer* L, const float* dW, float lr, hipStream_t s);
+// dW for batches wider than one tile (loops over the tiles)
+snack_status sddmm_dw_tiles(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,
+                            hipStream_t s);
+
+// values -= lr * dW; also vals_t -= lr * dW_t when dW_t is non-null
+snack_status sgd_update(snack_layer* L, const float* dW, const float* dW_t, float lr, hipStream_t s);
 snack_status mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale, hipStream_t s);
 snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s);
 snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hipStream_t s);

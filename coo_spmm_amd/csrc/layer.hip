@@ -138,6 +138,7 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(rows_t, int32_t*, nb4);
     ALLOC(cols_t, int32_t*, nb4);
     ALLOC(vals_t, float*, nb4);
+    ALLOC(dwt, float*, nb4);
     ALLOC(row_ptr, int32_t*, ((size_t)M + 1) * 4);
     ALLOC(col_ptr, int32_t*, ((size_t)K + 1) * 4);
     ALLOC(flag, int32_t*, 64);
@@ -152,7 +153,9 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     L->fwd.vals = L->vals;
     L->fwd.ptr = L->row_ptr;
     L->fwd.nchunks = (int32_t)(nchf < 1 ? 1 : nchf);
-    ALLOC(fwd.chunk_key, int32_t*, ((size_t)L->fwd.nchunks + 1) * 4);
+    ALLOC(fwd.desc, int2*, ((size_t)L->fwd.nchunks + 1) * 8);
+    ALLOC(fwd.empty_keys, int32_t*, (size_t)M * 4);
+    ALLOC(fwd.n_empty, int32_t*, 4);
     L->tr.nkeys = K;
     L->tr.nidx = M;
     L->tr.keys = L->cols_t;
@@ -160,7 +163,9 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     L->tr.vals = L->vals_t;
     L->tr.ptr = L->col_ptr;
     L->tr.nchunks = (int32_t)(ncht < 1 ? 1 : ncht);
-    ALLOC(tr.chunk_key, int32_t*, ((size_t)L->tr.nchunks + 1) * 4);
+    ALLOC(tr.desc, int2*, ((size_t)L->tr.nchunks + 1) * 8);
+    ALLOC(tr.empty_keys, int32_t*, (size_t)K * 4);
+    ALLOC(tr.n_empty, int32_t*, 4);
 
     size_t scr = canon_scratch_bytes(L, nnz);
     const size_t pscr = prune_scratch_bytes(L);
@@ -205,10 +210,10 @@ extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, 
     const float* feat = X;
     if (p.bp > 1) {
         SNACK_CHECK(ensure_ws(L, p));
-        SNACK_CHECK(transpose_pad(X, ws_x(L), B, L->K, p.bp, KC_TRANSPOSE, s));
+        SNACK_CHECK(transpose_pad(X, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
         feat = ws_x(L);
     }
-    return spmm_view(L->fwd, feat, p, B, Y, KC_SPMM_FWD, s);
+    return spmm_forward(L, feat, p, B, Y, s);
 }
 
 extern "C" snack_status snack_backward(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
@@ -216,6 +221,7 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
 {
     if (!L || !dY || B < 1) return SNACK_ERR_INVALID_ARG;
     if (dW && !X) return SNACK_ERR_INVALID_ARG;
+    if (dW && ((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;   // 16-byte vector stores
     if (!dX && !dW) return SNACK_OK;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
@@ -223,24 +229,31 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
     const float* xt = X;
     if (p.bp > 1) {
         SNACK_CHECK(ensure_ws(L, p));
-        SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), B, L->M, p.bp, KC_TRANSPOSE, s));
+        SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), L->M, dW ? X : nullptr, ws_x(L), L->K, B, p.bp, s));
         dyt = ws_dy(L, p);
-        if (dW) {
-            SNACK_CHECK(transpose_pad(X, ws_x(L), B, L->K, p.bp, KC_TRANSPOSE, s));
-            xt = ws_x(L);
+        xt = ws_x(L);
+    }
+    if (dX && L->vals_t_stale) SNACK_CHECK(refresh_vals_t(L, s));
+    L->dwt_valid = false;
+    if (p.ntiles == 1) {
+        // one launch: dX (+ dW in transposed order) over the column view, dW over the row view
+        float* dwt = (dX && dW) ? L->dwt : nullptr;
+        SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, dW, dwt, s));
+        if (dwt) {
+            L->dwt_for = dW;
+            L->dwt_valid = true;
         }
+    } else {
+        if (dX) SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, nullptr, nullptr, s));
+        if (dW) SNACK_CHECK(sddmm_dw_tiles(L, xt, dyt, p, dW, s));
     }
-    if (dX) {
-        if (L->vals_t_stale) SNACK_CHECK(refresh_vals_t(L, s));
-        SNACK_CHECK(spmm_view(L->tr, dyt, p, B, dX, KC_SPMM_DX, s));
-    }
-    if (dW) SNACK_CHECK(sddmm_dw(L, xt, dyt, p, B, dW, s));
     return SNACK_OK;
 }
 
 extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack_stream stream)
 {
     if (!L || n_drop < 0 || n_drop > L->nnz) return SNACK_ERR_INVALID_ARG;
+    L->dwt_valid = false;
     return snack::prune_regrow(L, n_drop, as_stream(stream));
 }
 
@@ -277,6 +290,7 @@ extern "C" snack_status snack_layer_values_updated(snack_layer* L)
 {
     if (!L) return SNACK_ERR_INVALID_ARG;
     L->vals_t_stale = true;
+    L->dwt_valid = false;
     return SNACK_OK;
 }
 
@@ -293,8 +307,9 @@ extern "C" snack_status snack_layer_export(const snack_layer* L, int32_t* rows, 
     return SNACK_OK;
 }
 
-extern "C" snack_status snack_layer_export_index(const snack_layer* L, int32_t* row_ptr, int32_t* perm,
-                                                 int32_t* rows_t, int32_t* col_ptr, snack_stream stream)
+extern "C" snack_status snack_layer_export_index(snack_layer* L, int32_t* row_ptr, int32_t* perm,
+                                                 int32_t* rows_t, int32_t* col_ptr, float* vals_t,
+                                                 snack_stream stream)
 {
     if (!L) return SNACK_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
@@ -304,6 +319,10 @@ extern "C" snack_status snack_layer_export_index(const snack_layer* L, int32_t* 
     if (n4) {
         if (perm) SNACK_HIP(hipMemcpyAsync(perm, L->perm, n4, hipMemcpyDeviceToDevice, s));
         if (rows_t) SNACK_HIP(hipMemcpyAsync(rows_t, L->rows_t, n4, hipMemcpyDeviceToDevice, s));
+        if (vals_t) {
+            if (L->vals_t_stale) SNACK_CHECK(refresh_vals_t(L, s));
+            SNACK_HIP(hipMemcpyAsync(vals_t, L->vals_t, n4, hipMemcpyDeviceToDevice, s));
+        }
     }
     return SNACK_OK;
 }
@@ -325,7 +344,9 @@ extern "C" snack_status snack_layer_set_epoch(snack_layer* L, uint64_t epoch)
 extern "C" snack_status snack_sgd_step(snack_layer* L, const float* dW, float lr, snack_stream stream)
 {
     if (!L || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
-    return sgd_update(L, dW, lr, as_stream(stream));
+    const float* dwt = (L->dwt_valid && dW == L->dwt_for) ? L->dwt : nullptr;
+    L->dwt_valid = false;
+    return sgd_update(L, dW, dwt, lr, as_stream(stream));
 }
 
 extern "C" snack_status snack_mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale,

@@ -1,27 +1,36 @@
-// spmm.hip -- segmented SpMM over a sorted view of the COO triple, and the
-// sampled dense-dense product for dW.
+// spmm.hip -- segmented SpMM over a sorted view of the COO triple, fused with
+// the sampled dense-dense product for dW.
 //
 // Forward (SNACK paper, Figure 1; "Padded-CSR" section 6.1) and the input
 // gradient ("Padded-CSR" section 7.1, run over the transposed view of section
-// 7.2) are one kernel: out[b, key] = sum of v * feat[idx, b] over the entries
-// of each key, for a view sorted by key.
+// 7.2) are one kernel: out[b, key] = sum over the view's entries of that key of
+// v * G[idx, b], for a view sorted by key.  The same pass can produce the
+// weight gradient on the support ("Padded-CSR" 7.1; SNACK Figure 1's sparse
+// outer product): dw[j] = sum_b G[idx_j, b] * H[key_j, b].
 //
-// Mapping (one wavefront per key-aligned chunk):
-//  * a wave is G = 64/BT lane groups of BT lanes; each lane owns NB
-//    consecutive batch columns, so a group covers a batch tile of BT*NB
-//    columns and every (key, idx, value) load is shared by the whole tile;
-//  * per wave step, group g takes a run of U consecutive entries, loaded as
-//    16-byte vectors, so the G runs of a step stream one contiguous span of
-//    the index and value arrays;
-//  * the activations are feature-major (feat[idx * bp + b]) so the NB values
-//    a lane gathers per entry are one vector load;
-//  * a lane sums its run sequentially per key, then the groups combine run
-//    tails with a segmented Hillis-Steele scan over wavefront shuffles; a key
-//    still open at the end of a step is carried into the next step.  Every
-//    output row is written exactly once, by plain stores: no atomics, so the
-//    result is bit-reproducible.
+// Mapping -- one wavefront per key-aligned chunk of the view:
+//  * a wave step covers a block of E = 256*P consecutive entries; every lane
+//    loads 4P of them with 16-byte loads (the block is read once, coalesced);
+//  * the wave is G = 64/BT lane groups; each lane owns NB consecutive batch
+//    columns, so a group covers a batch tile of BT*NB columns; the block is
+//    split into G contiguous runs, one per group; with BT > 1 the runs reach the
+//    group's lanes through LDS, so no index byte is fetched twice from memory;
+//  * activations are feature-major (G[idx * bp + b]): the NB values a lane
+//    needs per entry are one or two 16-byte loads;
+//  * a lane sums its run sequentially per key (head / middle keys / tail);
+//    the groups then combine run tails with a segmented Hillis-Steele scan over
+//    wavefront shuffles; a key still open at the end of a step is carried into
+//    the next.  Every output row is written once, by plain stores: no atomics,
+//    so results are bit-reproducible;
+//  * the next block is prefetched into registers while the current one is
+//    processed.
 // Chunks never split a key, so no cross-wave fix-up exists.  Workgroups are
-// remapped so that each XCD streams one contiguous range of chunks.
+// remapped so each XCD streams one contiguous range of chunks.
+//
+// dW partial sums are reduced over a group's lanes by one routine
+// (reduce4_group) whatever the view, so dW computed over the column view and
+// over the row view are bit-identical -- the layer relies on this to update
+// its two value copies with streaming SGD.
 #include "internal.h"
 
 #include <limits.h>
@@ -33,46 +42,144 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcd = 8;
 
+struct RoleArgs {
+    const int32_t* idx;
+    const float* vals;
+    const int32_t* ptr;
+    const int2* desc;
+    const int32_t* empty_keys;
+    const int32_t* n_empty;
+    const float* G;      // gathered by idx: [nidx, bp]
+    const float* H;      // indexed by key: [nkeys, bp] (dW only)
+    float* out;          // [B, nkeys] or null
+    float* dwo;          // dW in this view's slot order, or null
+    int64_t cap;         // padded length of idx / vals
+    int32_t nchunks;
+    int32_t nkeys;
+    int32_t nidx;
+    int32_t nblocks;
+    int32_t per_xcd;
+};
+
 template <int NB>
 __device__ inline void load_nb(const float* __restrict__ p, float (&x)[NB])
 {
-    if constexpr (NB == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    if constexpr (NB == 8) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else if constexpr (NB == 4) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     } else if constexpr (NB == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(p);
-        x[0] = v.x; x[1] = v.y;
+        const float2 a = *reinterpret_cast<const float2*>(p);
+        x[0] = a.x; x[1] = a.y;
     } else {
         x[0] = *p;
     }
 }
 
-template <int BT, int NB, int U>
-__global__ void __launch_bounds__(kBlock) spmm_seg_kernel(
-    const int32_t* __restrict__ keys, const int32_t* __restrict__ idx, const float* __restrict__ vals,
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ chunk_key, int32_t nchunks,
-    const float* __restrict__ feat, int bp, int B, int32_t nkeys, float* __restrict__ out, int per_xcd,
-    int nblocks)
+__device__ inline int comp(const int4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
+__device__ inline float compf(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
+
+// Reduce four per-lane values over the BT lanes of a group (a butterfly whose
+// upper levels exchange half of the remaining values).  On return lane bl
+// holds the full group sum of value (bl / (BT/4)) & 3 for BT >= 4, of values
+// {2*bl, 2*bl+1} for BT == 2 (in d[0], d[1]), and all four for BT == 1.
+template <int BT>
+__device__ inline void reduce4_group(float (&d)[4], int bl)
 {
-    static_assert(U % 4 == 0, "runs are loaded as 16-byte vectors");
+    if constexpr (BT >= 2) {
+        {
+            constexpr int m = BT / 2;
+            const bool hi = (bl & m) != 0;
+            const float s0 = hi ? d[0] : d[2];
+            const float s1 = hi ? d[1] : d[3];
+            const float r0 = __shfl_xor(s0, m, kWave);
+            const float r1 = __shfl_xor(s1, m, kWave);
+            const float k0 = hi ? d[2] : d[0];
+            const float k1 = hi ? d[3] : d[1];
+            d[0] = k0 + r0;
+            d[1] = k1 + r1;
+        }
+        if constexpr (BT >= 4) {
+            constexpr int m = BT / 4;
+            const bool hi = (bl & m) != 0;
+            const float s = hi ? d[0] : d[1];
+            const float r = __shfl_xor(s, m, kWave);
+            d[0] = (hi ? d[1] : d[0]) + r;
+#pragma unroll
+            for (int mm = BT / 8; mm >= 1; mm >>= 1) d[0] += __shfl_xor(d[0], mm, kWave);
+        }
+    }
+}
+
+// Keys of a run of ascending entries, derived from the chunk's key pointer
+// slice held in LDS: entry k belongs to key r0 + j with slice[j] <= k <
+// slice[j+1].  Entries outside [s, e) get -1 (before) or INT_MAX (after).
+struct KeyWalk {
+    const int32_t* slice;
+    int32_t r0;
+    int32_t nr;
+    int64_t s, e;
+    int j;
+    int32_t nb;
+
+    __device__ inline void start(int64_t k0, int64_t len)
+    {
+        const int64_t lo_k = k0 > s ? k0 : s;
+        const int64_t hi_k = (k0 + len < e) ? k0 + len : e;
+        j = 0;
+        nb = 0;
+        if (lo_k < hi_k) {
+            int lo = 0, hi = nr;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (slice[mid] <= lo_k) lo = mid;
+                else hi = mid;
+            }
+            j = lo;
+            nb = slice[j + 1];
+        }
+    }
+    __device__ inline int32_t key(int64_t k)
+    {
+        if (k < s) return -1;
+        if (k >= e) return INT_MAX;
+        while (k >= nb) {
+            ++j;
+            nb = slice[j + 1];
+        }
+        return r0 + j;
+    }
+};
+
+// Per-wave work on one chunk.  SPMM: accumulate out[b, key]; DW: produce dw
+// per entry.  Both are compile-time so no load sits under a runtime branch
+// (a conditional load makes the compiler wait for every outstanding load).
+template <int BT, int NB, int P, bool DW, bool SPMM>
+__device__ __forceinline__ void seg_body(const RoleArgs& A, int c, int wv, int lane, int bp, int B,
+                                         int32_t* __restrict__ slice, int4* __restrict__ blk_i,
+                                         int4* __restrict__ blk_v, const float* __restrict__ Gm)
+{
     constexpr int G = kWave / BT;
-    constexpr int STEP = G * U;
-    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int E = 256 * P;          // entries per wave step
+    constexpr int RUN = E / G;          // entries per group per step
+    constexpr int NSB = RUN / 4;        // sub-batches of four entries
+    static_assert(RUN % 4 == 0, "runs are read four entries at a time");
+    static_assert(BT == 1 || P == 1, "wide batch tiles stage one block at a time");
+    static_assert(SPMM || DW, "nothing to do");
+
     const int g = lane / BT;
     const int bl = lane - g * BT;
-
-    const int bid = (int)blockIdx.x;
-    const int vb = (bid % kXcd) * per_xcd + bid / kXcd;
-    if (vb >= nblocks) return;
-    const int c = vb * kWavesPerBlock + (int)(threadIdx.x / kWave);
-    if (c >= nchunks) return;
-    const int32_t r0 = chunk_key[c];
-    const int32_t r1 = chunk_key[c + 1];
-    if (r0 >= r1) return;
-
+    const int2 d0 = A.desc[c];
+    const int2 d1 = A.desc[c + 1];
+    const int32_t r0 = d0.x, r1 = d1.x;
     const int tile0 = (int)blockIdx.y * (BT * NB);
     const int bcol = tile0 + bl * NB;
-    const float* __restrict__ fb = feat + bcol;
+    const int nkeys = A.nkeys;
+    float* __restrict__ out = A.out;
 
     auto write_row = [&](int32_t key, const float (&a)[NB]) {
         if (key >= r0 && key < r1) {
@@ -84,80 +191,145 @@ __global__ void __launch_bounds__(kBlock) spmm_seg_kernel(
         }
     };
 
-    // keys of this chunk with no entry produce zeros
-    for (int32_t r = r0 + lane; r < r1; r += kWave) {
-        if (ptr[r] == ptr[r + 1]) {
-            for (int q = 0; q < BT * NB; ++q) {
-                const int b = tile0 + q;
-                if (b < B) out[(int64_t)b * nkeys + r] = 0.0f;
+    if constexpr (SPMM) {
+        if (g == 0) {
+            // keys with no entry produce zeros; the role's waves share the list
+            const int32_t ne = *A.n_empty;
+            for (int i = c; i < ne; i += A.nchunks) {
+                const int32_t key = A.empty_keys[i];
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    const int b = bcol + n;
+                    if (b < B) out[(int64_t)b * nkeys + key] = 0.0f;
+                }
             }
         }
     }
 
-    const int64_t s = ptr[r0];
-    const int64_t e = ptr[r1];
+    const int64_t s = d0.y;
+    const int64_t e = d1.y;
+    if (s >= e) return;
+    const int64_t base0 = s & ~(int64_t)3;
+    const int64_t lim = A.cap - E;      // last block start that stays inside the padded arrays
+    const int32_t* __restrict__ idx = A.idx;
+    const float* __restrict__ vals = A.vals;
+    const float* __restrict__ Hm = A.H;
+
+    // the chunk's key pointer slice: nr + 1 <= kChunkWork + 1 values
+    const int nr = r1 - r0;
+    for (int i = lane; i <= nr; i += kWave) slice[i] = A.ptr[r0 + i];
+    __builtin_amdgcn_wave_barrier();
+    KeyWalk walk{slice, r0, nr, s, e, 0, 0};
+
     int32_t carry_key = -1;
     float carry[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) carry[n] = 0.0f;
 
-    for (int64_t base = s & ~(int64_t)3; base < e; base += STEP) {
-        const int64_t my = base + (int64_t)g * U;
-        int32_t key[U], ix[U];
-        float v[U];
+    // ---- per-run state and the work on one sub-batch of four entries ----
+    int32_t first_key = -1, cur = -1;
+    bool multi = false;
+    float acc[NB], head[NB];
+    int32_t hkey = -2;
+    float hreg[NB];
 #pragma unroll
-        for (int q = 0; q < U / 4; ++q) {
-            const int4 kk = *reinterpret_cast<const int4*>(keys + my + 4 * q);
-            const int4 ii = *reinterpret_cast<const int4*>(idx + my + 4 * q);
-            const float4 vv = *reinterpret_cast<const float4*>(vals + my + 4 * q);
-            key[4 * q + 0] = kk.x; key[4 * q + 1] = kk.y; key[4 * q + 2] = kk.z; key[4 * q + 3] = kk.w;
-            ix[4 * q + 0] = ii.x; ix[4 * q + 1] = ii.y; ix[4 * q + 2] = ii.z; ix[4 * q + 3] = ii.w;
-            v[4 * q + 0] = vv.x; v[4 * q + 1] = vv.y; v[4 * q + 2] = vv.z; v[4 * q + 3] = vv.w;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = my + u;
-            if (k < s || k >= e) {
-                key[u] = (k < s) ? -1 : INT_MAX;
-                ix[u] = 0;
-                v[u] = 0.0f;
-            }
-        }
-        float x[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_nb<NB>(fb + (int64_t)ix[u] * bp, x[u]);
+    for (int n = 0; n < NB; ++n) hreg[n] = 0.0f;
 
-        // sequential per-key sums along the run
-        float head[NB], acc[NB];
-        bool multi = false;
+    auto run_begin = [&]() {
+        first_key = -1;
+        cur = -1;
+        multi = false;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-            acc[n] = v[0] * x[0][n];
+            acc[n] = 0.0f;
             head[n] = 0.0f;
         }
+    };
+
+    auto sub_batch = [&](int64_t k0, bool first, const float (&vv)[4], const float (&y)[4][NB]) {
+        int32_t kk[4];
 #pragma unroll
-        for (int u = 1; u < U; ++u) {
-            if (key[u] != key[u - 1]) {
-                if (multi) {
-                    write_row(key[u - 1], acc);   // a key wholly inside this run
-                } else {
+        for (int t = 0; t < 4; ++t) kk[t] = walk.key(k0 + t);
+        if (first) {
+            first_key = kk[0];
+            cur = kk[0];
+        }
+        if constexpr (SPMM) {
+            float v[4];
 #pragma unroll
-                    for (int n = 0; n < NB; ++n) head[n] = acc[n];
-                    multi = true;
-                }
+            for (int t = 0; t < 4; ++t) v[t] = (k0 + t >= s && k0 + t < e) ? vv[t] : 0.0f;
+            if (kk[0] == cur && kk[3] == cur) {
 #pragma unroll
-                for (int n = 0; n < NB; ++n) acc[n] = v[u] * x[u][n];
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(v[t], y[t][n], acc[n]);
             } else {
 #pragma unroll
-                for (int n = 0; n < NB; ++n) acc[n] = fmaf(v[u], x[u][n], acc[n]);
+                for (int t = 0; t < 4; ++t) {
+                    if (kk[t] != cur) {
+                        if (multi) {
+                            write_row(cur, acc);   // a key wholly inside this run
+                        } else {
+#pragma unroll
+                            for (int n = 0; n < NB; ++n) head[n] = acc[n];
+                            multi = true;
+                        }
+                        cur = kk[t];
+#pragma unroll
+                        for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+                    }
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(v[t], y[t][n], acc[n]);
+                }
             }
         }
-        const int32_t head_key = key[0];
-        const int32_t tail_key = key[U - 1];
+        if constexpr (DW) {
+            float d[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool inr = kk[t] >= 0 && kk[t] < nkeys;
+                if (inr && kk[t] != hkey) {
+                    load_nb<NB>(Hm + (int64_t)kk[t] * bp + bcol, hreg);
+                    hkey = kk[t];
+                }
+                float a = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NB; ++n) a = fmaf(y[t][n], inr ? hreg[n] : 0.0f, a);
+                d[t] = a;
+            }
+            reduce4_group<BT>(d, bl);
+            float* __restrict__ dwo = A.dwo;
+            if constexpr (BT == 1) {
+                if (k0 >= s && k0 + 3 < e) {
+                    *reinterpret_cast<float4*>(dwo + k0) = make_float4(d[0], d[1], d[2], d[3]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (k0 + t >= s && k0 + t < e) dwo[k0 + t] = d[t];
+                }
+            } else if constexpr (BT == 2) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int64_t k = k0 + 2 * bl + t;
+                    if (k >= s && k < e) dwo[k] = d[t];
+                }
+            } else {
+                constexpr int STRIDE = BT / 4;
+                if ((bl % STRIDE) == 0) {
+                    const int64_t k = k0 + bl / STRIDE;
+                    if (k >= s && k < e) dwo[k] = d[0];
+                }
+            }
+        }
+    };
 
-        // the open key carried from the previous step is complete unless this step continues it
-        const int32_t first_key = __shfl(head_key, 0, kWave);
-        if (g == 0 && carry_key != first_key) write_row(carry_key, carry);
+    // ---- the groups combine their run tails; the open key is carried ----
+    auto finish_step = [&]() {
+        const int32_t head_key = first_key;
+        const int32_t tail_key = cur;
+        // the key carried from the previous step is complete unless this step continues it
+        const int32_t step_first = __shfl(head_key, 0, kWave);
+        if (g == 0 && carry_key != step_first) write_row(carry_key, carry);
 
         int32_t ptail = __shfl_up(tail_key, BT, kWave);
         if (g == 0) ptail = carry_key;
@@ -166,12 +338,12 @@ __global__ void __launch_bounds__(kBlock) spmm_seg_kernel(
 #pragma unroll
         for (int n = 0; n < NB; ++n) S[n] = acc[n];
 #pragma unroll
-        for (int d = 1; d < G; d <<= 1) {
+        for (int dd = 1; dd < G; dd <<= 1) {
             float So[NB];
 #pragma unroll
-            for (int n = 0; n < NB; ++n) So[n] = __shfl_up(S[n], d * BT, kWave);
-            const int fo = __shfl_up(f, d * BT, kWave);
-            if (g >= d) {
+            for (int n = 0; n < NB; ++n) So[n] = __shfl_up(S[n], dd * BT, kWave);
+            const int fo = __shfl_up(f, dd * BT, kWave);
+            if (g >= dd) {
                 if (!f) {
 #pragma unroll
                     for (int n = 0; n < NB; ++n) S[n] += So[n];
@@ -187,7 +359,6 @@ __global__ void __launch_bounds__(kBlock) spmm_seg_kernel(
 #pragma unroll
         for (int n = 0; n < NB; ++n) Sp[n] = __shfl_up(S[n], BT, kWave);
         const int32_t next_head = __shfl_down(head_key, BT, kWave);
-
         if (multi) {
             const bool take = (ptail == head_key);
             float h[NB];
@@ -196,22 +367,174 @@ __global__ void __launch_bounds__(kBlock) spmm_seg_kernel(
             write_row(head_key, h);
         }
         if (g < G - 1 && next_head != tail_key) write_row(tail_key, S);
-
 #pragma unroll
         for (int n = 0; n < NB; ++n) carry[n] = __shfl(S[n], (G - 1) * BT + bl, kWave);
         carry_key = __shfl(tail_key, kWave - 1, kWave);
+    };
+
+    // Blocks of E entries are loaded into rotating register buffers whose
+    // prefetch address is clamped into the padding (never under a branch), so
+    // a block's index/value loads stay in flight across the previous step.
+    struct Buf {
+        int4 i[P];
+        float4 v[P];
+    };
+    auto load_buf = [&](int64_t base, Buf& b) {
+        const int64_t o0 = (base < lim ? base : lim) + (BT == 1 ? (int64_t)RUN * lane : (int64_t)4 * lane);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            b.i[q] = *reinterpret_cast<const int4*>(idx + o0 + 4 * q);
+            if constexpr (SPMM) b.v[q] = *reinterpret_cast<const float4*>(vals + o0 + 4 * q);
+        }
+    };
+
+    if constexpr (BT == 1) {
+        // Each lane's run is its own 4P entries.  Step i issues the gathers of
+        // block i, then the loads of block i+2, then reduces block i.
+        auto step = [&](int64_t base, const Buf& cb, Buf& pre) {
+            float y[RUN][NB];
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                load_nb<NB>(Gm + (int64_t)cb.i[q].x * bp + bcol, y[4 * q + 0]);
+                load_nb<NB>(Gm + (int64_t)cb.i[q].y * bp + bcol, y[4 * q + 1]);
+                load_nb<NB>(Gm + (int64_t)cb.i[q].z * bp + bcol, y[4 * q + 2]);
+                load_nb<NB>(Gm + (int64_t)cb.i[q].w * bp + bcol, y[4 * q + 3]);
+            }
+            load_buf(base + 2 * E, pre);
+            const int64_t k0 = base + (int64_t)RUN * lane;
+            walk.start(k0, RUN);
+            run_begin();
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                float vq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (SPMM) {
+                    vq[0] = cb.v[q].x; vq[1] = cb.v[q].y; vq[2] = cb.v[q].z; vq[3] = cb.v[q].w;
+                }
+                float yq[4][NB];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) yq[t][n] = y[4 * q + t][n];
+                sub_batch(k0 + 4 * q, q == 0, vq, yq);
+            }
+            if constexpr (SPMM) finish_step();
+        };
+        Buf b0, b1, b2;
+        load_buf(base0, b0);
+        load_buf(base0 + E, b1);
+        for (int64_t base = base0;;) {
+            step(base, b0, b2);
+            base += E;
+            if (base >= e) break;
+            step(base, b1, b0);
+            base += E;
+            if (base >= e) break;
+            step(base, b2, b1);
+            base += E;
+            if (base >= e) break;
+        }
+    } else {
+        // Wide batch tiles: the block is staged in LDS and each group reads its
+        // run from there (one memory fetch per entry for the whole tile).  The
+        // next block is loaded into the same registers once they are in LDS,
+        // after this step's gathers are issued.
+        int4 ni;
+        float4 nv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        {
+            const int64_t o = (base0 < lim ? base0 : lim) + 4 * lane;
+            ni = *reinterpret_cast<const int4*>(idx + o);
+            if constexpr (SPMM) nv = *reinterpret_cast<const float4*>(vals + o);
+        }
+        for (int64_t base = base0; base < e; base += E) {
+            blk_i[lane] = ni;
+            if constexpr (SPMM) blk_v[lane] = *reinterpret_cast<const int4*>(&nv);
+            __builtin_amdgcn_wave_barrier();
+            const int64_t run0 = base + (int64_t)g * RUN;
+            walk.start(run0, RUN);
+            run_begin();
+#pragma unroll 2
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int4 i4 = blk_i[g * NSB + sb];
+                float vq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (SPMM) {
+                    const int4 t4 = blk_v[g * NSB + sb];
+                    const float4 v4 = *reinterpret_cast<const float4*>(&t4);
+                    vq[0] = v4.x; vq[1] = v4.y; vq[2] = v4.z; vq[3] = v4.w;
+                }
+                float yq[4][NB];
+                load_nb<NB>(Gm + (int64_t)i4.x * bp + bcol, yq[0]);
+                load_nb<NB>(Gm + (int64_t)i4.y * bp + bcol, yq[1]);
+                load_nb<NB>(Gm + (int64_t)i4.z * bp + bcol, yq[2]);
+                load_nb<NB>(Gm + (int64_t)i4.w * bp + bcol, yq[3]);
+                sub_batch(run0 + 4 * sb, sb == 0, vq, yq);
+            }
+            {
+                const int64_t nb = base + E;
+                const int64_t o = (nb < lim ? nb : lim) + 4 * lane;
+                ni = *reinterpret_cast<const int4*>(idx + o);
+                if constexpr (SPMM) nv = *reinterpret_cast<const float4*>(vals + o);
+            }
+            if constexpr (SPMM) finish_step();
+            __builtin_amdgcn_wave_barrier();
+        }
     }
-    if (g == 0) write_row(carry_key, carry);
+    if constexpr (SPMM) {
+        if (g == 0) write_row(carry_key, carry);
+    }
 }
 
-// dW[k] = sum_b dyt[r_k, b] * xt[c_k, b]; group g of a wave step takes U
-// consecutive slots, its BT lanes split the batch and are reduced by a
-// butterfly within the group.
+template <int BT, int NB, int P, bool DW, int WPB, bool XLDS>
+__global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs rb, int grid_a, int bp, int B)
+{
+    constexpr int E = 256 * P;
+    constexpr int LDS_Q = (BT > 1) ? E / 4 : 1;   // int4 per array per wave
+    __shared__ int32_t slice_s[WPB][kChunkWork + 2];
+    __shared__ int4 blk_s[WPB][2][LDS_Q];
+    extern __shared__ float xs_dyn[];   // the gathered operand, when staged in LDS
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = (int)(threadIdx.x / kWave);
+    int bid = (int)blockIdx.x;
+    const bool role_a = bid < grid_a;
+    if (!role_a) bid -= grid_a;
+    const RoleArgs& A = role_a ? ra : rb;
+    const int vb = (bid % kXcd) * A.per_xcd + bid / kXcd;
+    if (vb >= A.nblocks) return;
+    if constexpr (XLDS) {
+        // stage the whole gathered operand [nidx, bp] in LDS once per workgroup
+        const int64_t n = (int64_t)A.nidx * bp;
+        const int64_t n4 = n / 4;
+        for (int64_t i = threadIdx.x; i < n4; i += WPB * kWave)
+            reinterpret_cast<float4*>(xs_dyn)[i] = reinterpret_cast<const float4*>(A.G)[i];
+        for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += WPB * kWave) xs_dyn[i] = A.G[i];
+        __syncthreads();
+    }
+    const int c = vb * WPB + wv;
+    if (c >= A.nchunks) return;
+    const float* Gm = XLDS ? xs_dyn : A.G;
+    // dW is produced only where a dW output exists (a dX-only pass has none)
+    const bool want_dw = DW && A.dwo != nullptr && A.H != nullptr;
+    if (role_a && A.out != nullptr) {
+        if (want_dw) {
+            seg_body<BT, NB, P, DW, true>(A, c, wv, lane, bp, B, slice_s[wv], blk_s[wv][0], blk_s[wv][1], Gm);
+        } else {
+            seg_body<BT, NB, P, false, true>(A, c, wv, lane, bp, B, slice_s[wv], blk_s[wv][0], blk_s[wv][1], Gm);
+        }
+    } else if constexpr (DW) {
+        if (want_dw && blockIdx.y == 0)
+            seg_body<BT, NB, P, true, false>(A, c, wv, lane, bp, B, slice_s[wv], blk_s[wv][0], blk_s[wv][1], Gm);
+    }
+}
+
+// dW[k] = sum_b dyt[r_k, b] * xt[c_k, b] over several batch tiles (batches
+// wider than one tile); group g of a wave step takes U consecutive slots and
+// its BT lanes are reduced by a butterfly.
 template <int BT, int NB, int U>
-__global__ void __launch_bounds__(kBlock) sddmm_kernel(const int32_t* __restrict__ rows,
-                                                       const int32_t* __restrict__ cols, int64_t nnz,
-                                                       const float* __restrict__ xt, const float* __restrict__ dyt,
-                                                       int bp, int ntiles, float* __restrict__ dW, int64_t nsteps)
+__global__ void __launch_bounds__(kBlock) sddmm_tiles_kernel(const int32_t* __restrict__ rows,
+                                                             const int32_t* __restrict__ cols, int64_t nnz,
+                                                             const float* __restrict__ xt,
+                                                             const float* __restrict__ dyt, int bp, int ntiles,
+                                                             float* __restrict__ dW, int64_t nsteps)
 {
     constexpr int G = kWave / BT;
     constexpr int STEP = G * U;
@@ -219,10 +542,7 @@ __global__ void __launch_bounds__(kBlock) sddmm_kernel(const int32_t* __restrict
     const int g = lane / BT;
     const int bl = lane - g * BT;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    const int bid = (int)blockIdx.x;
-    const int per_xcd = (int)((gridDim.x + kXcd - 1) / kXcd);
-    const int64_t vb = (int64_t)(bid % kXcd) * per_xcd + bid / kXcd;
-    for (int64_t st = vb * kWavesPerBlock + threadIdx.x / kWave; st < nsteps; st += nwaves) {
+    for (int64_t st = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; st < nsteps; st += nwaves) {
         const int64_t my = st * STEP + (int64_t)g * U;
         int32_t r[U], c[U];
 #pragma unroll
@@ -255,51 +575,86 @@ __global__ void __launch_bounds__(kBlock) sddmm_kernel(const int32_t* __restrict
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m, kWave);
         }
-        if constexpr (BT == 1) {
-            if (my + U <= nnz) {
 #pragma unroll
-                for (int q = 0; q < U / 4; ++q)
-                    *reinterpret_cast<float4*>(dW + my + 4 * q) =
-                        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (my + u < nnz) dW[my + u] = acc[u];
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if ((u % BT) == bl && my + u < nnz) dW[my + u] = acc[u];
-        }
+        for (int u = 0; u < U; ++u)
+            if ((u % BT) == bl && my + u < nnz) dW[my + u] = acc[u];
     }
 }
 
-template <int BT, int NB, int U>
-snack_status launch_spmm(const View& v, const float* feat, const BatchPlan& p, int B, float* out, hipStream_t s)
+RoleArgs role_for(const View& v, const float* G, const float* H, float* out, float* dwo, int wpb, int64_t cap)
 {
-    const int nblocks = (v.nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int per_xcd = (nblocks + kXcd - 1) / kXcd;
-    dim3 grid((unsigned)(per_xcd * kXcd), (unsigned)p.ntiles);
-    hipLaunchKernelGGL((spmm_seg_kernel<BT, NB, U>), grid, dim3(kBlock), 0, s, v.keys, v.idx, v.vals, v.ptr,
-                       v.chunk_key, v.nchunks, feat, p.bp, B, v.nkeys, out, per_xcd, nblocks);
+    RoleArgs a;
+    a.cap = cap;
+    a.idx = v.idx;
+    a.vals = v.vals;
+    a.ptr = v.ptr;
+    a.desc = v.desc;
+    a.empty_keys = v.empty_keys;
+    a.n_empty = v.n_empty;
+    a.G = G;
+    a.H = H;
+    a.out = out;
+    a.dwo = dwo;
+    a.nchunks = v.nchunks;
+    a.nkeys = v.nkeys;
+    a.nidx = v.nidx;
+    a.nblocks = (v.nchunks + wpb - 1) / wpb;
+    a.per_xcd = (a.nblocks + kXcd - 1) / kXcd;
+    return a;
+}
+
+constexpr int kXldsBytes = 64 * 1024;   // largest operand staged in LDS
+constexpr int kXldsWaves = 8;
+
+template <int BT, int NB, int P, bool DW, int WPB, bool XLDS>
+snack_status launch_seg(const RoleArgs& a, const RoleArgs* b, int ntiles, int bp, int B, hipStream_t s)
+{
+    const int grid_a = a.per_xcd * kXcd;
+    const int grid_b = b ? b->per_xcd * kXcd : 0;
+    RoleArgs bb = b ? *b : a;
+    dim3 grid((unsigned)(grid_a + grid_b), (unsigned)ntiles);
+    size_t dyn = 0;
+    if (XLDS) {
+        const size_t na = (size_t)a.nidx * bp * 4, nb = b ? (size_t)b->nidx * bp * 4 : 0;
+        dyn = na > nb ? na : nb;
+    }
+    hipLaunchKernelGGL((seg_kernel<BT, NB, P, DW, WPB, XLDS>), grid, dim3(WPB * kWave), dyn, s, a, bb, grid_a, bp, B);
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }
 
-template <int BT, int NB, int U>
-snack_status launch_sddmm(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,
-                          hipStream_t s)
+// operands small enough for LDS are staged there (B = 1 at up to 16K features)
+inline bool use_xlds(const BatchPlan& p, int nidx_max)
 {
-    constexpr int STEP = (kWave / BT) * U;
-    const int64_t nsteps = (L->nnz + STEP - 1) / STEP;
-    int64_t nb = (nsteps + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = 256 * 8 * 4;   // enough resident blocks for the whole chip
-    if (nb > cap) nb = cap;
-    nb = ((nb + kXcd - 1) / kXcd) * kXcd;
-    hipLaunchKernelGGL((sddmm_kernel<BT, NB, U>), dim3((unsigned)nb), dim3(kBlock), 0, s, L->rows, L->cols, L->nnz,
-                       xt, dyt, p.bp, p.ntiles, dW, nsteps);
-    SNACK_HIP(hipGetLastError());
-    return SNACK_OK;
+    return p.btile == 1 && (size_t)nidx_max * p.bp * 4 <= (size_t)kXldsBytes;
+}
+
+template <bool DW>
+snack_status dispatch_seg(const BatchPlan& p, int64_t cap, const View& va, const float* Ga, const float* Ha,
+                          float* outa, float* dwa, const View* vbv, const float* Gb, const float* Hb, float* dwb,
+                          int B, hipStream_t s)
+{
+    const int nmax = vbv && vbv->nidx > va.nidx ? vbv->nidx : va.nidx;
+    if (use_xlds(p, nmax)) {
+        const RoleArgs a = role_for(va, Ga, Ha, outa, dwa, kXldsWaves, cap);
+        RoleArgs b;
+        if (vbv) b = role_for(*vbv, Gb, Hb, nullptr, dwb, kXldsWaves, cap);
+        return launch_seg<1, 1, 2, DW, kXldsWaves, true>(a, vbv ? &b : nullptr, p.ntiles, p.bp, B, s);
+    }
+    const RoleArgs a = role_for(va, Ga, Ha, outa, dwa, kWavesPerBlock, cap);
+    RoleArgs b;
+    if (vbv) b = role_for(*vbv, Gb, Hb, nullptr, dwb, kWavesPerBlock, cap);
+    const RoleArgs* pb = vbv ? &b : nullptr;
+    switch (p.btile) {
+    case 1: return launch_seg<1, 1, 2, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 2: return launch_seg<1, 2, 2, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 4: return launch_seg<1, 4, 2, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 8: return launch_seg<1, 8, 1, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 16: return launch_seg<2, 8, 1, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 32: return launch_seg<4, 8, 1, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    case 64: return launch_seg<8, 8, 1, DW, kWavesPerBlock, false>(a, pb, p.ntiles, p.bp, B, s);
+    default: return SNACK_ERR_INVALID_ARG;
+    }
 }
 
 }  // namespace
@@ -307,51 +662,55 @@ snack_status launch_sddmm(const snack_layer* L, const float* xt, const float* dy
 BatchPlan plan_batch(int B)
 {
     BatchPlan p;
-    if (B <= 1) { p.bt = 1; p.nb = 1; p.u = 4; }
-    else if (B == 2) { p.bt = 1; p.nb = 2; p.u = 4; }
-    else if (B <= 4) { p.bt = 1; p.nb = 4; p.u = 4; }
-    else if (B <= 8) { p.bt = 2; p.nb = 4; p.u = 4; }
-    else if (B <= 16) { p.bt = 4; p.nb = 4; p.u = 8; }
-    else if (B <= 32) { p.bt = 8; p.nb = 4; p.u = 8; }
-    else { p.bt = 16; p.nb = 4; p.u = 16; }
+    if (B <= 1) { p.bt = 1; p.nb = 1; }
+    else if (B == 2) { p.bt = 1; p.nb = 2; }
+    else if (B <= 4) { p.bt = 1; p.nb = 4; }
+    else if (B <= 8) { p.bt = 1; p.nb = 8; }
+    else if (B <= 16) { p.bt = 2; p.nb = 8; }
+    else if (B <= 32) { p.bt = 4; p.nb = 8; }
+    else { p.bt = 8; p.nb = 8; }
+    p.u = 4;
     p.btile = p.bt * p.nb;
     p.ntiles = (B + p.btile - 1) / p.btile;
     p.bp = p.ntiles * p.btile;
     return p;
 }
 
-snack_status spmm_view(const View& v, const float* feat_t, const BatchPlan& p, int B, float* out, int kclass,
-                       hipStream_t s)
+snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
+                          hipStream_t s)
 {
-    ProfScope prof(kclass, s);
-    switch (p.btile) {
-    case 1: return launch_spmm<1, 1, 4>(v, feat_t, p, B, out, s);
-    case 2: return launch_spmm<1, 2, 4>(v, feat_t, p, B, out, s);
-    case 4: return launch_spmm<1, 4, 4>(v, feat_t, p, B, out, s);
-    case 8: return launch_spmm<2, 4, 4>(v, feat_t, p, B, out, s);
-    case 16: return launch_spmm<4, 4, 8>(v, feat_t, p, B, out, s);
-    case 32: return launch_spmm<8, 4, 8>(v, feat_t, p, B, out, s);
-    case 64: return launch_spmm<16, 4, 16>(v, feat_t, p, B, out, s);
-    default: return SNACK_ERR_INVALID_ARG;
-    }
+    ProfScope prof(KC_SPMM_FWD, s);
+    return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               B, s);
 }
 
-snack_status sddmm_dw(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B, float* dW,
-                      hipStream_t s)
+snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
+                                 float* dX, float* dW, float* dW_t, hipStream_t s)
 {
-    (void)B;
+    ProfScope prof(KC_SPMM_DX, s);
+    // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view
+    if (dW && !dX)
+        return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
+    if (dW)
+        return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
+    return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
+}
+
+snack_status sddmm_dw_tiles(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,
+                            hipStream_t s)
+{
     if (L->nnz == 0) return SNACK_OK;
     ProfScope prof(KC_SDDMM_DW, s);
-    switch (p.btile) {
-    case 1: return launch_sddmm<1, 1, 4>(L, xt, dyt, p, dW, s);
-    case 2: return launch_sddmm<1, 2, 4>(L, xt, dyt, p, dW, s);
-    case 4: return launch_sddmm<1, 4, 4>(L, xt, dyt, p, dW, s);
-    case 8: return launch_sddmm<2, 4, 4>(L, xt, dyt, p, dW, s);
-    case 16: return launch_sddmm<4, 4, 8>(L, xt, dyt, p, dW, s);
-    case 32: return launch_sddmm<8, 4, 8>(L, xt, dyt, p, dW, s);
-    case 64: return launch_sddmm<16, 4, 16>(L, xt, dyt, p, dW, s);
-    default: return SNACK_ERR_INVALID_ARG;
-    }
+    constexpr int BT = 8, NB = 8, U = 4;
+    if (p.bt != BT || p.nb != NB) return SNACK_ERR_INVALID_ARG;
+    constexpr int STEP = (kWave / BT) * U;
+    const int64_t nsteps = (L->nnz + STEP - 1) / STEP;
+    int64_t nb = (nsteps + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (nb > 256 * 16) nb = 256 * 16;
+    hipLaunchKernelGGL((sddmm_tiles_kernel<BT, NB, U>), dim3((unsigned)nb), dim3(kBlock), 0, s, L->rows, L->cols,
+                       L->nnz, xt, dyt, p.bp, p.ntiles, dW, nsteps);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
 }
 
 }  // namespace snack

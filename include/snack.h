@@ -99,8 +99,12 @@ snack_status snack_forward(snack_layer* layer, const float* X, float* Y, int32_t
  * Figure 1 calls the latter the sparse outer product over supp(W).
  *   X   device float[B, K] (the forward's input), dY device float[B, M].
  *   dX  device float[B, K] or NULL (skipped); overwritten.
- *   dW  device float[nnz] in canonical slot order, or NULL; overwritten (the
- *       caller accumulates if it wants to).  Stored zeros get a gradient.
+ *   dW  device float[nnz] in canonical slot order, 16-byte aligned, or NULL;
+ *       overwritten (the caller accumulates if it wants to).  Stored zeros get
+ *       a gradient.
+ * When both dX and dW are requested and B <= 64, the layer also keeps dW in its
+ * transposed order; a following snack_sgd_step with the same dW pointer then
+ * updates both of the layer's value copies without a permutation gather.
  */
 snack_status snack_backward(snack_layer* layer, const float* X, const float* dY,
                             float* dX, float* dW, int32_t B, snack_stream stream);
@@ -143,10 +147,11 @@ snack_status snack_layer_export(const snack_layer* layer, int32_t* rows, int32_t
  * Copy the index structures into caller device buffers ("Padded-CSR" 3.2 and
  * 7.2; SNACK Table 7): row_ptr int32[M+1], perm int32[nnz] (transposed slot ->
  * canonical slot), rows_t int32[nnz] (row of each transposed slot), col_ptr
- * int32[K+1].  Any pointer may be NULL.
+ * int32[K+1], vals_t float[nnz] (the values in transposed order, equal to
+ * vals[perm]).  Any pointer may be NULL.
  */
-snack_status snack_layer_export_index(const snack_layer* layer, int32_t* row_ptr, int32_t* perm,
-                                      int32_t* rows_t, int32_t* col_ptr, snack_stream stream);
+snack_status snack_layer_export_index(snack_layer* layer, int32_t* row_ptr, int32_t* perm,
+                                      int32_t* rows_t, int32_t* col_ptr, float* vals_t, snack_stream stream);
 
 /* Epoch = number of prune_regrow calls so far (resume: create + set_epoch). */
 snack_status snack_layer_get_epoch(const snack_layer* layer, uint64_t* epoch);

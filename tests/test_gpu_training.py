@@ -1,0 +1,95 @@
+"""Training loop on the GPU (forward, MSE gradient, backward, SGD, drop/regrow),
+checked step by step against the oracle with teacher forcing: every check feeds
+the oracle the GPU's own values and inputs of that iteration, so fp32 and fp64
+trajectories are never compared after they drift apart.
+
+Also checks the layer's two value copies stay bit-identical (vals_t ==
+vals[perm]) after SGD updates both of them from dW produced in each order."""
+import numpy as np
+import pytest
+
+import oracle
+from snack_inputs import normal, random_layer, weight_std
+from tests.gpu_util import say, lib, dev, host, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _sgd_close(got, v, g, lr, ulps=2):
+    """fp32 evaluation of v - lr*g (with lr rounded to fp32) is within a couple
+    of ulps of the larger operand of the exact fp64 update."""
+    ref = oracle.sgd(v, g, lr)
+    got = np.asarray(got, np.float32).astype(np.float64)
+    big = np.maximum(np.abs(v.astype(np.float64)), np.abs(lr * g.astype(np.float64)))
+    spacing = np.spacing(big.astype(np.float32)).astype(np.float64)
+    return np.abs(got - ref) <= ulps * spacing + 1e-30
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 16, 40, 64, 100])
+def test_training_steps_teacher_forced(B):
+    import torch
+    L = lib()
+    M, K, sp = 700, 900, 90
+    nnz = M * K * (100 - sp) // 100
+    rows, cols, vals = random_layer(M, K, nnz, f"train/{B}", weight_std(K, sp))
+    say("training create B", B)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=77)
+    lr = 0.01
+    Y = torch.empty(B, M, device="cuda"); dY = torch.empty(B, M, device="cuda")
+    dX = torch.empty(B, K, device="cuda"); dW = torch.empty(nnz, device="cuda")
+    try:
+        for it in range(6):
+            X = normal((B, K), f"train/{B}/X/{it}"); T = normal((B, M), f"train/{B}/T/{it}")
+            r, c, v = (host(t) for t in layer.export())
+            Xd, Td = dev(X), dev(T)
+            say("training iteration", it, "B", B)
+            L.snack_forward(layer.h, Xd, Y)
+            L.snack_mse_grad(Y, Td, dY, 2.0 / (B * M))
+            L.snack_backward(layer.h, Xd, dY, dX, dW)
+            L.snack_sgd_step(layer.h, dW, lr)
+            Yg, dYg, dXg, dWg = host(Y), host(dY), host(dX), host(dW)
+            Yr, Ya = oracle.forward(M, K, r, c, v, X)
+            assert_close(f"Y it={it}", Yg, Yr, Ya)
+            dYr = oracle.mse_grad(Yg, T)
+            assert_close(f"dY it={it}", dYg, dYr, np.abs(dYr), rel=2e-7, atol=1e-12)
+            dXr, dXa = oracle.backward_dx(M, K, r, c, v, dYg)
+            assert_close(f"dX it={it}", dXg, dXr, dXa)
+            dWr, dWa = oracle.backward_dw(M, K, r, c, X, dYg)
+            assert_close(f"dW it={it}", dWg, dWr, dWa)
+            v_new = host(layer.export()[2])
+            assert _sgd_close(v_new, v, dWg, lr).all()
+            rp, pm, rt, cp, vt = (host(t) for t in layer.export_index(with_values=True))
+            assert np.array_equal(vt.view(np.uint32), v_new[pm].view(np.uint32)), "value copies diverged"
+            if it == 2:
+                say("training prune B", B)
+                layer.prune_regrow(nnz * 3 // 10)
+                o = oracle.prune_regrow(M, K, r, c, v_new, nnz * 3 // 10, 77, 0)
+                r2, c2, v2 = (host(t) for t in layer.export())
+                assert np.array_equal(r2, o[0]) and np.array_equal(c2, o[1])
+                assert np.array_equal(v2.view(np.uint32), o[2].view(np.uint32))
+    finally:
+        layer.close()
+
+
+def test_dw_row_and_column_orders_bit_identical():
+    """dW from the fused backward (canonical order) equals the transposed-order
+    copy the layer keeps, bit for bit, for every batch plan."""
+    import torch
+    L = lib()
+    M, K, nnz = 1500, 1100, 80000
+    rows, cols, vals = random_layer(M, K, nnz, "dwt")
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    try:
+        for B in (1, 2, 4, 8, 16, 32, 64):
+            X = dev(normal((B, K), f"dwt/X/{B}")); dY = dev(normal((B, M), f"dwt/dY/{B}"))
+            say("dwt orders B", B)
+            v0 = host(layer.export()[2])
+            dX, dW = layer.backward(X, dY)
+            layer.sgd_step(dW, 1.0)         # updates both copies from dW and its transposed twin
+            v1 = host(layer.export()[2])
+            rp, pm, rt, cp, vt = (host(t) for t in layer.export_index(with_values=True))
+            assert np.array_equal(vt.view(np.uint32), v1[pm].view(np.uint32))
+            # and the canonical update is exactly v - dW in fp32
+            assert np.array_equal(v1, (v0 - host(dW)).astype(np.float32))
+    finally:
+        layer.close()
