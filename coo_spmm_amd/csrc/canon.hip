@@ -137,6 +137,146 @@ __global__ void build_transposed_kernel(const uint32_t* __restrict__ tkeys, cons
     }
 }
 
+// ---- transposed view by a stable counting sort on the column --------------
+// The canonical slots are cut into nb contiguous ranges of E entries, one
+// workgroup each.  tb_count writes the workgroup's column histogram into
+// mat[c * nb + b]; an exclusive scan of mat in that (column-major) order gives
+// every (column, range) pair its first transposed slot.  tb_scatter then walks
+// its range in canonical order with one LDS cursor per column.  A row holds a
+// column at most once, so the entries of one row never collide; rows are taken
+// one after another (a barrier between them), which keeps each column's
+// entries in row order without any sort and without global atomics.
+// Workgroups are dispatched to the 8 XCDs round-robin; range b is given to the
+// workgroup that puts ranges [x*per, (x+1)*per) on XCD x, so the slots of one
+// column written from neighbouring ranges meet in the same L2 and leave it as
+// whole lines.
+constexpr int kTbThreads = 512;
+constexpr int kXcds = 8;
+constexpr int32_t kTbMaxKeys = 15360;            // cursor array of 60 KB in LDS
+constexpr int64_t kTbMatrixMax = 4 << 20;        // nb * K
+
+__global__ void __launch_bounds__(kTbThreads) tb_count_kernel(const int32_t* __restrict__ cols, int64_t nnz,
+                                                              int64_t E, int32_t K, int32_t nb,
+                                                              int32_t* __restrict__ mat)
+{
+    extern __shared__ int32_t hist[];
+    const int32_t per = gridDim.x / kXcds;
+    const int32_t b = (int32_t)(blockIdx.x % kXcds) * per + (int32_t)(blockIdx.x / kXcds);
+    if (b >= nb) return;
+    for (int32_t c = threadIdx.x; c < K; c += kTbThreads) hist[c] = 0;
+    __syncthreads();
+    const int64_t e0 = (int64_t)b * E;
+    const int64_t e1 = e0 + E < nnz ? e0 + E : nnz;
+    // eight loads in flight per thread; indexes clamped so every load is issued
+    for (int64_t base = e0; base < e1; base += 8 * kTbThreads) {
+        int32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t k = base + u * kTbThreads + threadIdx.x;
+            c[u] = cols[k < e1 ? k : e1 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (base + u * kTbThreads + threadIdx.x < e1) atomicAdd(&hist[c[u]], 1);
+    }
+    __syncthreads();
+    for (int32_t c = threadIdx.x; c < K; c += kTbThreads) mat[(int64_t)c * nb + b] = hist[c];
+}
+
+// Loads run two rounds ahead, and every lane issues the same loads and stores
+// (clamped reads; a lane past the range writes zeros into the zero padding
+// after slot nnz), so the compiler's wait before a round covers that round's
+// loads only, never the scattered stores of the rounds before it.
+struct TbEntry {
+    int32_t r, c;
+    float v;
+};
+
+__global__ void __launch_bounds__(kTbThreads) tb_scatter_kernel(
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, const float* __restrict__ vals, int64_t nnz,
+    int64_t E, int32_t K, int32_t nb, const int32_t* __restrict__ mat, int32_t* __restrict__ perm,
+    int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t, float* __restrict__ vals_t,
+    int32_t* __restrict__ col_ptr)
+{
+    extern __shared__ int32_t cur[];
+    __shared__ int32_t s_row[kTbThreads];
+    __shared__ int32_t s_wave[kTbThreads / kWave];
+    const int32_t per = gridDim.x / kXcds;
+    const int32_t b = (int32_t)(blockIdx.x % kXcds) * per + (int32_t)(blockIdx.x / kXcds);
+    if (b >= nb) return;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    for (int32_t c = tid; c < K; c += kTbThreads) {
+        const int32_t v = mat[(int64_t)c * nb + b];
+        cur[c] = v;
+        if (b == 0) col_ptr[c] = v;
+    }
+    if (b == 0 && tid == 0) col_ptr[K] = (int32_t)nnz;
+    const int64_t e0 = (int64_t)b * E;
+    const int64_t e1 = e0 + E < nnz ? e0 + E : nnz;
+    if (e0 >= e1) return;   // uniform over the workgroup
+    auto load = [&](int64_t k, TbEntry& x) {
+        const int64_t kc = k < e1 ? k : e1 - 1;
+        x.r = rows[kc];
+        x.c = cols[kc];
+        x.v = vals[kc];
+    };
+    auto round = [&](int64_t k, const TbEntry& x) {
+        const bool live = k < e1;
+        s_row[tid] = live ? x.r : -1;
+        __syncthreads();
+        const bool start = live && (tid == 0 || s_row[tid - 1] != x.r);
+        const uint64_t m = __ballot(start);
+        const int upto = __popcll(m & (lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1ull)));
+        if (lane == 0) s_wave[w] = __popcll(m);
+        __syncthreads();
+        int before = 0, nseg = 0;
+#pragma unroll
+        for (int i = 0; i < kTbThreads / kWave; ++i) {
+            const int y = s_wave[i];
+            before += i < w ? y : 0;
+            nseg += y;
+        }
+        const int seg = before + upto - 1;
+        int32_t pos = (int32_t)nnz + tid;
+        for (int sg = 0; sg < nseg; ++sg) {
+            if (live && seg == sg) {
+                pos = cur[x.c];
+                cur[x.c] = pos + 1;
+            }
+            __syncthreads();
+        }
+        rows_t[pos] = live ? x.r : 0;
+        cols_t[pos] = live ? x.c : 0;
+        perm[pos] = live ? (int32_t)k : 0;
+        vals_t[pos] = live ? x.v : 0.0f;
+    };
+    TbEntry A, B;
+    int64_t k = e0 + tid;
+    load(k, A);
+    load(k + kTbThreads, B);
+    __syncthreads();
+    for (; k - tid < e1; k += 2 * kTbThreads) {
+        const TbEntry a = A;
+        load(k + 2 * kTbThreads, A);
+        round(k, a);
+        if (k - tid + kTbThreads >= e1) break;   // uniform
+        const TbEntry bb = B;
+        load(k + 3 * kTbThreads, B);
+        round(k + kTbThreads, bb);
+    }
+}
+
+inline void tb_plan(int64_t nnz, int32_t K, int32_t* nb_out, int64_t* e_out)
+{
+    int64_t nb = (nnz + 4095) / 4096;
+    const int64_t lim = kTbMatrixMax / (K > 0 ? K : 1);
+    if (nb > lim) nb = lim;
+    if (nb > 1024) nb = 1024;
+    if (nb < 1) nb = 1;
+    *nb_out = (int32_t)nb;
+    *e_out = (nnz + nb - 1) / nb;
+}
+
 __global__ void refresh_vals_t_kernel(const int32_t* __restrict__ perm, const float* __restrict__ vals, int64_t nnz,
                                       float* __restrict__ vals_t)
 {
@@ -172,7 +312,15 @@ size_t canon_scratch_bytes(const snack_layer* L, int64_t nnz)
     b += radix_sort_scratch_bytes(nnz, kb);
     // empty-key lists of the two views
     const int64_t nk = L->M > L->K ? L->M : L->K;
-    const size_t e = 2 * (((size_t)nk + 63) & ~(size_t)63) * 4 + scan_scratch_bytes(nk) + 256;
+    size_t e = 2 * (((size_t)nk + 63) & ~(size_t)63) * 4 + scan_scratch_bytes(nk) + 256;
+    if (L->K <= kTbMaxKeys) {
+        int32_t nb;
+        int64_t E;
+        tb_plan(nnz, L->K, &nb, &E);
+        const size_t m = (size_t)nb * L->K;
+        const size_t t = ((m * 4 + 255) & ~(size_t)255) + scan_scratch_bytes((int64_t)m);
+        if (t > e) e = t;
+    }
     return (b > e ? b : e) + 256;
 }
 
@@ -220,23 +368,42 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
     hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->rows, nnz, L->M,
                        L->row_ptr);
     SNACK_HIP(hipGetLastError());
-    if (nnz > 0) {
-        char* p = (char*)L->scratch;
-        uint32_t* tkeys = (uint32_t*)p;
-        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
-        uint32_t* tslots = (uint32_t*)p;
-        p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
-        hipLaunchKernelGGL(iota_cols_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->cols, nnz, tkeys, tslots);
+    if (nnz > 0 && L->K <= kTbMaxKeys) {
+        int32_t nb;
+        int64_t E;
+        tb_plan(nnz, L->K, &nb, &E);
+        int32_t* mat = (int32_t*)L->scratch;
+        const size_t m = (size_t)nb * L->K;
+        void* scan_scr = (char*)L->scratch + ((m * 4 + 255) & ~(size_t)255);
+        const size_t lds = (size_t)L->K * 4;
+        const unsigned grid = (unsigned)((nb + kXcds - 1) / kXcds * kXcds);
+        hipLaunchKernelGGL(tb_count_kernel, dim3(grid), dim3(kTbThreads), lds, s, L->cols, nnz, E, L->K, nb, mat);
         SNACK_HIP(hipGetLastError());
-        // canonical order is (row, col), so a stable sort by column yields (col, row)
-        SNACK_CHECK(radix_sort_u32(tkeys, tslots, nnz, bits_for((uint64_t)(L->K - 1)), p, s));
-        hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tkeys, tslots, nnz,
-                           L->rows, L->vals, L->perm, L->rows_t, L->cols_t, L->vals_t);
+        SNACK_CHECK(exclusive_scan_i32(mat, mat, (int64_t)m, nullptr, scan_scr, s));
+        hipLaunchKernelGGL(tb_scatter_kernel, dim3(grid), dim3(kTbThreads), lds, s, L->rows, L->cols, L->vals, nnz, E,
+                           L->K, nb, mat, L->perm, L->rows_t, L->cols_t, L->vals_t, L->col_ptr);
+        SNACK_HIP(hipGetLastError());
+    } else {
+        if (nnz > 0) {
+            // many columns: stable radix sort of the slots by column instead
+            char* p = (char*)L->scratch;
+            uint32_t* tkeys = (uint32_t*)p;
+            p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+            uint32_t* tslots = (uint32_t*)p;
+            p += ((size_t)nnz * 4 + 255) & ~(size_t)255;
+            hipLaunchKernelGGL(iota_cols_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->cols, nnz, tkeys,
+                               tslots);
+            SNACK_HIP(hipGetLastError());
+            // canonical order is (row, col), so a stable sort by column yields (col, row)
+            SNACK_CHECK(radix_sort_u32(tkeys, tslots, nnz, bits_for((uint64_t)(L->K - 1)), p, s));
+            hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tkeys, tslots,
+                               nnz, L->rows, L->vals, L->perm, L->rows_t, L->cols_t, L->vals_t);
+            SNACK_HIP(hipGetLastError());
+        }
+        hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->cols_t, nnz, L->K,
+                           L->col_ptr);
         SNACK_HIP(hipGetLastError());
     }
-    hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->cols_t, nnz, L->K,
-                       L->col_ptr);
-    SNACK_HIP(hipGetLastError());
     L->vals_t_stale = false;
     SNACK_CHECK(build_view_partition(L->fwd, L->scratch, s));
     SNACK_CHECK(build_view_partition(L->tr, L->scratch, s));

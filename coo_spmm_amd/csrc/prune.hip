@@ -11,13 +11,17 @@
 //          generator seeded with the layer seed (Steele, Lea & Flood 2014),
 //          mapped onto [0, M*K) by the high word of the 64x64 product; a
 //          candidate is accepted if its cell is neither kept nor accepted at a
-//          smaller t.  Candidates are tested in batches against an occupancy
-//          bitmap; inside a batch, a stable sort by position keeps the first
-//          occurrence of each cell, and a scan in t order keeps the first
-//          `need` accepted -- so the result never depends on the batch size.
-// The kept entries (already in canonical order) and the grown ones (sorted
-// by position) are merged by a merge-path style rank search, after which the
-// index structures are rebuilt.  Every step is integer work and deterministic.
+//          smaller t.
+// Occupancy lives in two bitmaps over the M*K cells: `kept` and `occ` (kept or
+// grown).  Candidates are tested in batches against `occ`; inside a batch an
+// open-addressing hash table keyed by cell keeps, per cell, the smallest
+// candidate index that named it (an atomic minimum on (cell, index) packed in
+// one word, so the order of the atomics does not matter), and a scan in t
+// order keeps the first `need` accepted -- the result never depends on the
+// batch size.  The new canonical order is then the set bits of `occ` in
+// ascending position: a prefix count of bits per 256-cell group places every
+// entry, and a kept cell takes the next kept value (its rank in `kept`).
+// Every step is integer work and deterministic.
 #include "internal.h"
 
 namespace snack {
@@ -25,8 +29,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
-constexpr int64_t kMaxBatch = 16 * 1024 * 1024;
+constexpr int64_t kMaxBatch = 1 << 21;          // candidates per batch
+constexpr int kTBits = 21;                       // candidate index bits in a table word
+constexpr int kHashBits = 22;                    // table slots (load <= 1/2)
+constexpr uint64_t kEmpty = ~0ull;
 constexpr uint64_t kMaxBitmapBits = 1ull << 34;
+constexpr int kGroupWords = 8;                   // bitmap words per prefix-count group
+constexpr int kSelBlocks = 512;                  // workgroups of one selection pass
+
+static_assert(kMaxBatch <= (1ll << kTBits), "candidate index must fit its field");
 
 inline unsigned grid_for(int64_t n)
 {
@@ -34,13 +45,6 @@ inline unsigned grid_for(int64_t n)
     if (g < 1) g = 1;
     if (g > 65535LL * 8) g = 65535LL * 8;
     return (unsigned)g;
-}
-
-inline int bits_for(uint64_t maxval)
-{
-    int b = 1;
-    while (b < 64 && (maxval >> b) != 0) ++b;
-    return b;
 }
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -54,35 +58,63 @@ __device__ inline uint64_t splitmix64_output(uint64_t z)
 
 __device__ inline uint32_t mag_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
-// state: [0] prefix, [1] rank still to find among keys matching the prefix
-__global__ void sel_hist_kernel(const float* __restrict__ vals, int64_t n, const uint32_t* __restrict__ state,
-                                int shift, uint32_t* __restrict__ hist)
+// ---- drop: radix select ---------------------------------------------------
+// state: [0] prefix, [1] rank still to find among keys matching the prefix.
+// Each workgroup writes its own 256-bin histogram row (no global atomics);
+// a thread adds runs of equal digits before touching LDS, which keeps the
+// first passes (where nearly every key shares a digit) free of contention.
+__global__ void __launch_bounds__(kThreads) sel_hist_kernel(const float* __restrict__ vals, int64_t n,
+                                                            const uint32_t* __restrict__ state, int shift,
+                                                            uint32_t* __restrict__ mat)
 {
     __shared__ uint32_t h[256];
     h[threadIdx.x] = 0;
     __syncthreads();
     const uint32_t prefix = state[0];
     const uint32_t hi_mask = (shift >= 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+    uint32_t run_d = 0, run = 0;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
         const uint32_t key = mag_bits(vals[k]);
-        if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        if ((key & hi_mask) != (prefix & hi_mask)) continue;
+        const uint32_t d = (key >> shift) & 255u;
+        if (d != run_d && run) {
+            atomicAdd(&h[run_d], run);
+            run = 0;
+        }
+        run_d = d;
+        ++run;
     }
+    if (run) atomicAdd(&h[run_d], run);
     __syncthreads();
-    if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
+    mat[(size_t)blockIdx.x * 256 + threadIdx.x] = h[threadIdx.x];
 }
 
-__global__ void sel_pick_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ state, int shift)
+// 1024 threads: four row groups per bin, each with independent accumulators
+__global__ void __launch_bounds__(1024) sel_pick_kernel(const uint32_t* __restrict__ mat, int nblk,
+                                                        uint32_t* __restrict__ state, int shift)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    uint32_t r = state[1];
-    uint32_t d = 0;
-    for (; d < 256; ++d) {
-        if (r < hist[d]) break;
-        r -= hist[d];
+    __shared__ uint32_t part[4][256];
+    const int d = threadIdx.x & 255, q = threadIdx.x >> 8;
+    uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int b = q;
+    for (; b + 28 < nblk; b += 32) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += mat[(size_t)(b + 4 * u) * 256 + d];
     }
-    state[0] |= d << shift;
-    state[1] = r;
-    for (int i = 0; i < 256; ++i) hist[i] = 0;
+    for (; b < nblk; b += 4) acc[0] += mat[(size_t)b * 256 + d];
+    part[q][d] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = state[1];
+        uint32_t dg = 0;
+        for (; dg < 255; ++dg) {
+            const uint32_t t = part[0][dg] + part[1][dg] + part[2][dg] + part[3][dg];
+            if (r < t) break;
+            r -= t;
+        }
+        state[0] |= dg << shift;
+        state[1] = r;
+    }
 }
 
 __global__ void eq_flags_kernel(const float* __restrict__ vals, int64_t n, const uint32_t* __restrict__ state,
@@ -112,128 +144,196 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
         p[i] = v;
 }
 
-__global__ void compact_kept_kernel(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols,
-                                    const float* __restrict__ vals, int64_t n, int32_t K,
-                                    const int32_t* __restrict__ keep, const int32_t* __restrict__ kidx,
-                                    uint64_t* __restrict__ kpos, float* __restrict__ kval,
-                                    uint32_t* __restrict__ bitmap)
+__device__ inline uint64_t cell_of(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, int64_t k,
+                                   int32_t K)
+{
+    return (uint64_t)rows[k] * (uint64_t)K + (uint64_t)cols[k];
+}
+
+// Kept values in canonical order, and the kept bitmap word by word: the first
+// entry of each 32-cell word assembles the word from the entries that follow
+// it (positions ascend, so they are adjacent), hence no atomics.  Both bitmaps
+// start as the kept cells.  Bitmaps must be zero beforehand.
+__global__ void kept_bits_kernel(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols,
+                                 const float* __restrict__ vals, int64_t n, int32_t K,
+                                 const int32_t* __restrict__ keep, const int32_t* __restrict__ kidx,
+                                 float* __restrict__ kval, uint32_t* __restrict__ kept_bm,
+                                 uint32_t* __restrict__ occ_bm)
 {
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-        if (!keep[k]) continue;
-        const uint64_t p = (uint64_t)rows[k] * (uint64_t)K + (uint64_t)cols[k];
-        const int32_t i = kidx[k];
-        kpos[i] = p;
-        kval[i] = vals[k];
-        atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+        if (keep[k]) kval[kidx[k]] = vals[k];
+        const uint64_t p = cell_of(rows, cols, k, K);
+        const uint64_t w = p >> 5;
+        if (k > 0 && (cell_of(rows, cols, k - 1, K) >> 5) == w) continue;
+        uint32_t m = 0;
+        for (int64_t j = k; j < n; ++j) {
+            const uint64_t q = j == k ? p : cell_of(rows, cols, j, K);
+            if ((q >> 5) != w) break;
+            if (keep[j]) m |= 1u << (q & 31);
+        }
+        if (m) {
+            kept_bm[w] = m;
+            occ_bm[w] = m;
+        }
     }
 }
 
-// candidate i of this batch is stream element t0 + i; occupied cells get the sentinel key N
+// ---- grow ------------------------------------------------------------------
+// candidate i of this batch is stream element t0 + i; occupied cells get the sentinel N
 __global__ void gen_candidates_kernel(uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N,
-                                      const uint32_t* __restrict__ bitmap, uint64_t* __restrict__ cpos,
-                                      uint32_t* __restrict__ cidx)
+                                      const uint32_t* __restrict__ occ_bm, uint64_t* __restrict__ cpos)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
         const uint64_t t = t0 + (uint64_t)i;
         const uint64_t x = seed + ((epoch << 40) + t + 1ull) * kGamma;
         const uint64_t pos = __umul64hi(splitmix64_output(x), N);
-        const bool occupied = (bitmap[pos >> 5] >> (pos & 31)) & 1u;
+        const bool occupied = (occ_bm[pos >> 5] >> (pos & 31)) & 1u;
         cpos[i] = occupied ? N : pos;
-        cidx[i] = (uint32_t)i;
     }
 }
 
-// after the stable sort by position: first occurrence of each free cell marks its candidate index
-__global__ void first_occurrence_kernel(const uint64_t* __restrict__ spos, const uint32_t* __restrict__ sidx,
-                                        int64_t T, uint64_t N, int32_t* __restrict__ accepted)
+__global__ void hash_clear_kernel(unsigned long long* __restrict__ tab, int64_t H)
 {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < T; j += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = spos[j];
-        const bool first = p < N && (j == 0 || spos[j - 1] != p);
-        accepted[sidx[j]] = first ? 1 : 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < H; i += (int64_t)gridDim.x * blockDim.x)
+        tab[i] = kEmpty;
+}
+
+__device__ inline uint32_t hash_slot(uint64_t pos) { return (uint32_t)((pos * kGamma) >> (64 - kHashBits)); }
+
+// table word = cell << kTBits | candidate index: words of one cell compare by index
+__global__ void hash_insert_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
+                                   unsigned long long* __restrict__ tab)
+{
+    const uint32_t mask = (1u << kHashBits) - 1u;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t p = cpos[i];
+        if (p >= N) continue;
+        const unsigned long long word = (p << kTBits) | (uint64_t)i;
+        uint32_t h = hash_slot(p);
+        for (uint32_t probe = 0; probe <= mask; ++probe) {
+            const unsigned long long old = atomicCAS(&tab[h], (unsigned long long)kEmpty, word);
+            if (old == kEmpty) break;
+            if ((old >> kTBits) == p) {
+                if (word < old) atomicMin(&tab[h], word);
+                break;
+            }
+            h = (h + 1u) & mask;
+        }
     }
 }
 
-// in position order: keep the accepted candidates whose rank in t order is below `need`
-__global__ void final_flags_kernel(const uint64_t* __restrict__ spos, const uint32_t* __restrict__ sidx, int64_t T,
-                                   uint64_t N, const int32_t* __restrict__ accepted, const int32_t* __restrict__ trank,
-                                   int64_t need, int32_t* __restrict__ fin)
+// accepted[i] = candidate i is free and the first (smallest index) to name its cell
+__global__ void hash_first_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
+                                  const unsigned long long* __restrict__ tab, int32_t* __restrict__ accepted)
 {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < T; j += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = spos[j];
-        const uint32_t i = sidx[j];
-        fin[j] = (p < N && accepted[i] && (int64_t)trank[i] < need) ? 1 : 0;
+    const uint32_t mask = (1u << kHashBits) - 1u;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t p = cpos[i];
+        int32_t a = 0;
+        if (p < N) {
+            uint32_t h = hash_slot(p);
+            for (uint32_t probe = 0; probe <= mask; ++probe) {
+                const unsigned long long w = tab[h];
+                if (w == kEmpty) break;
+                if ((w >> kTBits) == p) {
+                    a = (w & ((1ull << kTBits) - 1ull)) == (uint64_t)i ? 1 : 0;
+                    break;
+                }
+                h = (h + 1u) & mask;
+            }
+        }
+        accepted[i] = a;
     }
 }
 
-__global__ void emit_grown_kernel(const uint64_t* __restrict__ spos, int64_t T, const int32_t* __restrict__ fin,
-                                  const int32_t* __restrict__ fidx, uint64_t* __restrict__ grown, int64_t gbase,
-                                  uint32_t* __restrict__ bitmap)
+// the first `need` accepted candidates in stream order are grown
+__global__ void mark_grown_kernel(const uint64_t* __restrict__ cpos, int64_t T, const int32_t* __restrict__ accepted,
+                                  const int32_t* __restrict__ trank, int64_t need, uint32_t* __restrict__ occ_bm)
 {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < T; j += (int64_t)gridDim.x * blockDim.x) {
-        if (!fin[j]) continue;
-        const uint64_t p = spos[j];
-        grown[gbase + fidx[j]] = p;
-        atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
+        if (!accepted[i] || (int64_t)trank[i] >= need) continue;
+        const uint64_t p = cpos[i];
+        atomicOr(&occ_bm[p >> 5], 1u << (p & 31));
     }
 }
 
-__device__ inline int64_t lower_bound_u64(const uint64_t* __restrict__ a, int64_t n, uint64_t x)
+// ---- rebuild the canonical arrays from the bitmaps ---------------------------
+__global__ void group_counts_kernel(const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm,
+                                    int64_t words, int64_t groups, int32_t* __restrict__ occ_cnt,
+                                    int32_t* __restrict__ kept_cnt)
 {
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = lo + ((hi - lo) >> 1);
-        if (a[mid] < x) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
-__global__ void merge_kept_kernel(const uint64_t* __restrict__ kpos, const float* __restrict__ kval, int64_t nk,
-                                  const uint64_t* __restrict__ grown, int64_t ng, int32_t K, int32_t* __restrict__ rows,
-                                  int32_t* __restrict__ cols, float* __restrict__ vals)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nk; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = kpos[i];
-        const int64_t o = i + lower_bound_u64(grown, ng, p);
-        rows[o] = (int32_t)(p / (uint64_t)K);
-        cols[o] = (int32_t)(p % (uint64_t)K);
-        vals[o] = kval[i];
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += (int64_t)gridDim.x * blockDim.x) {
+        int32_t a = 0, b = 0;
+        for (int j = 0; j < kGroupWords; ++j) {
+            const int64_t w = g * kGroupWords + j;
+            if (w < words) {
+                a += __popc(occ_bm[w]);
+                b += __popc(kept_bm[w]);
+            }
+        }
+        occ_cnt[g] = a;
+        kept_cnt[g] = b;
     }
 }
 
-__global__ void merge_grown_kernel(const uint64_t* __restrict__ kpos, int64_t nk, const uint64_t* __restrict__ grown,
-                                   int64_t ng, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
-                                   float* __restrict__ vals)
+// one thread per bitmap word: its first output slot is the group's prefix plus
+// the bits of the group's earlier words; consecutive words write consecutive slots
+__global__ void emit_entries_kernel(const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm,
+                                    int64_t words, const int32_t* __restrict__ occ_pre,
+                                    const int32_t* __restrict__ kept_pre, const float* __restrict__ kval,
+                                    int64_t nnz, int64_t nkept, int32_t K, int32_t* __restrict__ rows,
+                                    int32_t* __restrict__ cols, float* __restrict__ vals)
 {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < ng; j += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = grown[j];
-        const int64_t o = j + lower_bound_u64(kpos, nk, p);
-        rows[o] = (int32_t)(p / (uint64_t)K);
-        cols[o] = (int32_t)(p % (uint64_t)K);
-        vals[o] = 0.0f;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x) {
+        uint32_t m = occ_bm[w];
+        if (!m) continue;
+        const uint32_t km = kept_bm[w];
+        const int64_t g = w / kGroupWords;
+        int64_t o = occ_pre[g];
+        int64_t i = kept_pre[g];
+        for (int64_t u = g * kGroupWords; u < w; ++u) {
+            o += __popc(occ_bm[u]);
+            i += __popc(kept_bm[u]);
+        }
+        const uint64_t p0 = (uint64_t)w << 5;
+        int64_t r = (int64_t)(p0 / (uint64_t)K);
+        int64_t c = (int64_t)(p0 - (uint64_t)r * (uint64_t)K);
+        int last = 0;
+        while (m && o < nnz) {
+            const int bit = __ffs(m) - 1;
+            m &= m - 1u;
+            c += bit - last;
+            last = bit;
+            while (c >= K) {
+                c -= K;
+                ++r;
+            }
+            rows[o] = (int32_t)r;
+            cols[o] = (int32_t)c;
+            vals[o] = ((km >> bit) & 1u) && i < nkept ? kval[i++] : 0.0f;
+            ++o;
+        }
     }
 }
 
 struct PruneScratch {
-    uint32_t* hist;     // [256]
     uint32_t* state;    // [16]
     int32_t* count;     // [4]
+    uint32_t* selmat;   // [kSelBlocks * 256]
     int32_t* a;         // [nnz] flags / eq
     int32_t* b;         // [nnz] scan result
     int32_t* keep;      // [nnz]
-    uint64_t* kpos;     // [nnz]
     float* kval;        // [nnz]
-    uint64_t* grown;    // [nnz]
-    uint32_t* bitmap;   // [(N+31)/32]
+    uint32_t* kept_bm;  // [words]
+    uint32_t* occ_bm;   // [words]
+    int32_t* occ_cnt;   // [groups]
+    int32_t* kept_cnt;  // [groups]
     uint64_t* cpos;     // [Tm]
-    uint32_t* cidx;     // [Tm]
     int32_t* acc;       // [Tm]
     int32_t* trank;     // [Tm]
-    int32_t* fin;       // [Tm]
-    int32_t* fidx;      // [Tm]
-    void* sort;         // sort + scan scratch
-    int64_t tmax;
+    unsigned long long* tab;   // [2^kHashBits]
+    void* scan;         // scan scratch
+    int64_t tmax, words, groups;
 };
 
 int64_t batch_cap(const snack_layer* L)
@@ -249,44 +349,46 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t n = L->nnz > 0 ? L->nnz : 1;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
     const int64_t words = (int64_t)((N + 31) / 32);
+    const int64_t groups = (words + kGroupWords - 1) / kGroupWords;
     const int64_t tm = batch_cap(L);
-    const int kb = bits_for(N);
-    size_t sortb = radix_sort_scratch_bytes(tm > n ? tm : n, kb > 32 ? 64 : 33);
-    size_t scanb = scan_scratch_bytes(tm > n ? tm : n);
-    size_t sub = sortb > scanb ? sortb : scanb;
+    const int64_t H = (int64_t)1 << kHashBits;
+    int64_t sn = tm > n ? tm : n;
+    if (groups > sn) sn = groups;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
         off += al(bytes);
         return o;
     };
-    size_t o_hist = take(256 * 4), o_state = take(16 * 4), o_count = take(16);
+    size_t o_state = take(16 * 4), o_count = take(16), o_sel = take((size_t)kSelBlocks * 256 * 4);
     size_t o_a = take((size_t)n * 4), o_b = take((size_t)n * 4), o_keep = take((size_t)n * 4);
-    size_t o_kpos = take((size_t)n * 8), o_kval = take((size_t)n * 4), o_grown = take((size_t)n * 8);
-    size_t o_bitmap = take((size_t)words * 4);
-    size_t o_cpos = take((size_t)tm * 8), o_cidx = take((size_t)tm * 4), o_acc = take((size_t)tm * 4);
-    size_t o_trank = take((size_t)tm * 4), o_fin = take((size_t)tm * 4), o_fidx = take((size_t)tm * 4);
-    size_t o_sort = take(sub);
+    size_t o_kval = take((size_t)n * 4);
+    size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4);
+    size_t o_oc = take((size_t)groups * 4), o_kc = take((size_t)groups * 4);
+    size_t o_cpos = take((size_t)tm * 8), o_acc = take((size_t)tm * 4), o_trank = take((size_t)tm * 4);
+    size_t o_tab = take((size_t)H * 8);
+    size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
         char* base = (char*)L->scratch;
-        ps->hist = (uint32_t*)(base + o_hist);
         ps->state = (uint32_t*)(base + o_state);
         ps->count = (int32_t*)(base + o_count);
+        ps->selmat = (uint32_t*)(base + o_sel);
         ps->a = (int32_t*)(base + o_a);
         ps->b = (int32_t*)(base + o_b);
         ps->keep = (int32_t*)(base + o_keep);
-        ps->kpos = (uint64_t*)(base + o_kpos);
         ps->kval = (float*)(base + o_kval);
-        ps->grown = (uint64_t*)(base + o_grown);
-        ps->bitmap = (uint32_t*)(base + o_bitmap);
+        ps->kept_bm = (uint32_t*)(base + o_kbm);
+        ps->occ_bm = (uint32_t*)(base + o_obm);
+        ps->occ_cnt = (int32_t*)(base + o_oc);
+        ps->kept_cnt = (int32_t*)(base + o_kc);
         ps->cpos = (uint64_t*)(base + o_cpos);
-        ps->cidx = (uint32_t*)(base + o_cidx);
         ps->acc = (int32_t*)(base + o_acc);
         ps->trank = (int32_t*)(base + o_trank);
-        ps->fin = (int32_t*)(base + o_fin);
-        ps->fidx = (int32_t*)(base + o_fidx);
-        ps->sort = base + o_sort;
+        ps->tab = (unsigned long long*)(base + o_tab);
+        ps->scan = base + o_scan;
         ps->tmax = tm;
+        ps->words = words;
+        ps->groups = groups;
     }
     return off + 256;
 }
@@ -318,22 +420,23 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     {
         uint32_t init[2] = {0u, (uint32_t)(n_drop - 1)};
         SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.hist, (int64_t)256, 0u);
+        int nblk = (int)grid_for(nnz);
+        if (nblk > kSelBlocks) nblk = kSelBlocks;
         for (int shift = 24; shift >= 0; shift -= 8) {
-            hipLaunchKernelGGL(sel_hist_kernel, dim3(grid_for(nnz) > 2048 ? 2048 : grid_for(nnz)), dim3(kThreads), 0,
-                               s, L->vals, nnz, ps.state, shift, ps.hist);
-            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(64), 0, s, ps.hist, ps.state, shift);
+            hipLaunchKernelGGL(sel_hist_kernel, dim3(nblk), dim3(kThreads), 0, s, L->vals, nnz, ps.state, shift,
+                               ps.selmat);
+            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(1024), 0, s, ps.selmat, nblk, ps.state, shift);
         }
         SNACK_HIP(hipGetLastError());
         hipLaunchKernelGGL(eq_flags_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->vals, nnz, ps.state, ps.a);
-        SNACK_CHECK(exclusive_scan_i32(ps.a, ps.b, nnz, nullptr, ps.sort, s));
+        SNACK_CHECK(exclusive_scan_i32(ps.a, ps.b, nnz, nullptr, ps.scan, s));
         hipLaunchKernelGGL(keep_flags_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->vals, nnz, ps.state, ps.b,
                            ps.keep);
-        SNACK_CHECK(exclusive_scan_i32(ps.keep, ps.b, nnz, nullptr, ps.sort, s));
-        const int64_t words = (int64_t)((N + 31) / 32);
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(words)), dim3(kThreads), 0, s, ps.bitmap, words, 0u);
-        hipLaunchKernelGGL(compact_kept_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->rows, L->cols, L->vals,
-                           nnz, L->K, ps.keep, ps.b, ps.kpos, ps.kval, ps.bitmap);
+        SNACK_CHECK(exclusive_scan_i32(ps.keep, ps.b, nnz, nullptr, ps.scan, s));
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.words, 0u);
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.occ_bm, ps.words, 0u);
+        hipLaunchKernelGGL(kept_bits_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->rows, L->cols, L->vals,
+                           nnz, L->K, ps.keep, ps.b, ps.kval, ps.kept_bm, ps.occ_bm);
         SNACK_HIP(hipGetLastError());
     }
 
@@ -342,44 +445,40 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     int64_t got = 0;
     uint64_t t0 = 0;
     int batches = 0;
-    const int kb = bits_for(N);   // the sentinel N needs bits_for(N) bits
+    const int64_t H = (int64_t)1 << kHashBits;
     while (need > 0) {
         const double p_empty = (double)(N - (uint64_t)kept - (uint64_t)got) / (double)N;
         double want = (double)need / (p_empty > 1e-9 ? p_empty : 1e-9) * 1.03 + 4096.0;
         int64_t T = want > (double)ps.tmax ? ps.tmax : (int64_t)want;
         if (T < 1) T = 1;
         hipLaunchKernelGGL(gen_candidates_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, L->seed, L->epoch, t0, T, N,
-                           ps.bitmap, ps.cpos, ps.cidx);
+                           ps.occ_bm, ps.cpos);
+        hipLaunchKernelGGL(hash_clear_kernel, dim3(grid_for(H)), dim3(kThreads), 0, s, ps.tab, H);
+        hipLaunchKernelGGL(hash_insert_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.tab);
+        hipLaunchKernelGGL(hash_first_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.tab, ps.acc);
         SNACK_HIP(hipGetLastError());
-        SNACK_CHECK(radix_sort_u64(ps.cpos, ps.cidx, T, kb, ps.sort, s));
-        hipLaunchKernelGGL(first_occurrence_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, ps.cidx, T, N,
-                           ps.acc);
-        SNACK_CHECK(exclusive_scan_i32(ps.acc, ps.trank, T, nullptr, ps.sort, s));
-        hipLaunchKernelGGL(final_flags_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, ps.cidx, T, N, ps.acc,
-                           ps.trank, need, ps.fin);
-        SNACK_CHECK(exclusive_scan_i32(ps.fin, ps.fidx, T, ps.count, ps.sort, s));
-        hipLaunchKernelGGL(emit_grown_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, ps.fin, ps.fidx,
-                           ps.grown, got, ps.bitmap);
+        SNACK_CHECK(exclusive_scan_i32(ps.acc, ps.trank, T, ps.count, ps.scan, s));
+        hipLaunchKernelGGL(mark_grown_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, ps.acc, ps.trank,
+                           need, ps.occ_bm);
         SNACK_HIP(hipGetLastError());
-        int32_t accepted = 0;
-        SNACK_HIP(hipMemcpyAsync(&accepted, ps.count, 4, hipMemcpyDeviceToHost, s));
+        int32_t total = 0;
+        SNACK_HIP(hipMemcpyAsync(&total, ps.count, 4, hipMemcpyDeviceToHost, s));
         SNACK_HIP(hipStreamSynchronize(s));
+        const int64_t accepted = total < need ? total : need;
         got += accepted;
         need -= accepted;
         t0 += (uint64_t)T;
         if (++batches > 100000) return SNACK_ERR_UNSUPPORTED;
     }
-    if (batches > 1) {
-        // grown positions of different batches are each sorted; sort the union by position
-        uint32_t* payload = (uint32_t*)ps.a;   // any payload of nnz words; only the keys matter
-        SNACK_CHECK(radix_sort_u64(ps.grown, payload, n_drop, bits_for(N - 1), ps.sort, s));
-    }
 
-    // ---- merge kept and grown into the canonical arrays ----
-    hipLaunchKernelGGL(merge_kept_kernel, dim3(grid_for(kept)), dim3(kThreads), 0, s, ps.kpos, ps.kval, kept,
-                       ps.grown, n_drop, L->K, L->rows, L->cols, L->vals);
-    hipLaunchKernelGGL(merge_grown_kernel, dim3(grid_for(n_drop)), dim3(kThreads), 0, s, ps.kpos, kept, ps.grown,
-                       n_drop, L->K, L->rows, L->cols, L->vals);
+    // ---- new canonical arrays: set bits of occ in ascending position ----
+    hipLaunchKernelGGL(group_counts_kernel, dim3(grid_for(ps.groups)), dim3(kThreads), 0, s, ps.occ_bm, ps.kept_bm,
+                       ps.words, ps.groups, ps.occ_cnt, ps.kept_cnt);
+    SNACK_HIP(hipGetLastError());
+    SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, ps.groups, nullptr, ps.scan, s));
+    SNACK_CHECK(exclusive_scan_i32(ps.kept_cnt, ps.kept_cnt, ps.groups, nullptr, ps.scan, s));
+    hipLaunchKernelGGL(emit_entries_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.occ_bm, ps.kept_bm,
+                       ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows, L->cols, L->vals);
     SNACK_HIP(hipGetLastError());
     SNACK_CHECK(canon_build_index(L, s));
     L->epoch += 1;
