@@ -125,12 +125,14 @@ __global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, 
 
 __global__ void build_transposed_kernel(const uint32_t* __restrict__ tkeys, const uint32_t* __restrict__ tslots,
                                         int64_t nnz, const int32_t* __restrict__ rows, const float* __restrict__ vals,
-                                        int32_t* __restrict__ perm, int32_t* __restrict__ rows_t,
-                                        int32_t* __restrict__ cols_t, float* __restrict__ vals_t)
+                                        int32_t* __restrict__ perm, int32_t* __restrict__ iperm,
+                                        int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t,
+                                        float* __restrict__ vals_t)
 {
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * blockDim.x) {
         const int32_t k = (int32_t)tslots[j];
         perm[j] = k;
+        iperm[k] = (int32_t)j;
         cols_t[j] = (int32_t)tkeys[j];
         rows_t[j] = rows[k];
         vals_t[j] = vals[k];
@@ -195,7 +197,7 @@ struct TbEntry {
 __global__ void __launch_bounds__(kTbThreads) tb_scatter_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, const float* __restrict__ vals, int64_t nnz,
     int64_t E, int32_t K, int32_t nb, const int32_t* __restrict__ mat, int32_t* __restrict__ perm,
-    int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t, float* __restrict__ vals_t,
+    int32_t* __restrict__ iperm, int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t, float* __restrict__ vals_t,
     int32_t* __restrict__ col_ptr)
 {
     extern __shared__ int32_t cur[];
@@ -249,6 +251,7 @@ __global__ void __launch_bounds__(kTbThreads) tb_scatter_kernel(
         cols_t[pos] = live ? x.c : 0;
         perm[pos] = live ? (int32_t)k : 0;
         vals_t[pos] = live ? x.v : 0.0f;
+        iperm[live ? k : nnz + tid] = live ? pos : 0;
     };
     TbEntry A, B;
     int64_t k = e0 + tid;
@@ -381,7 +384,7 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(exclusive_scan_i32(mat, mat, (int64_t)m, nullptr, scan_scr, s));
         hipLaunchKernelGGL(tb_scatter_kernel, dim3(grid), dim3(kTbThreads), lds, s, L->rows, L->cols, L->vals, nnz, E,
-                           L->K, nb, mat, L->perm, L->rows_t, L->cols_t, L->vals_t, L->col_ptr);
+                           L->K, nb, mat, L->perm, L->iperm, L->rows_t, L->cols_t, L->vals_t, L->col_ptr);
         SNACK_HIP(hipGetLastError());
     } else {
         if (nnz > 0) {
@@ -397,7 +400,7 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
             // canonical order is (row, col), so a stable sort by column yields (col, row)
             SNACK_CHECK(radix_sort_u32(tkeys, tslots, nnz, bits_for((uint64_t)(L->K - 1)), p, s));
             hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tkeys, tslots,
-                               nnz, L->rows, L->vals, L->perm, L->rows_t, L->cols_t, L->vals_t);
+                               nnz, L->rows, L->vals, L->perm, L->iperm, L->rows_t, L->cols_t, L->vals_t);
             SNACK_HIP(hipGetLastError());
         }
         hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->cols_t, nnz, L->K,

@@ -69,6 +69,7 @@ struct snack_layer {
     int32_t* row_ptr = nullptr;   // [M+1]
     // transposed (column-sorted) index
     int32_t* perm = nullptr;      // transposed slot -> canonical slot
+    int32_t* iperm = nullptr;     // canonical slot -> transposed slot
     int32_t* rows_t = nullptr;
     int32_t* cols_t = nullptr;    // sorted column keys
     float* vals_t = nullptr;      // values in transposed order

@@ -135,6 +135,7 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(cols, int32_t*, nb4);
     ALLOC(vals, float*, nb4);
     ALLOC(perm, int32_t*, nb4);
+    ALLOC(iperm, int32_t*, nb4);
     ALLOC(rows_t, int32_t*, nb4);
     ALLOC(cols_t, int32_t*, nb4);
     ALLOC(vals_t, float*, nb4);

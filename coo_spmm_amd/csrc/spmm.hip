@@ -526,6 +526,126 @@ __global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs 
     }
 }
 
+// Key-major variant for views whose keys hold many entries (rows or columns
+// of hundreds of entries at the densities of interest).  The wave walks its
+// chunk key by key; group g takes the key's entries g, g+G, g+2G, ..., U of
+// them in flight, and accumulates its batch columns in registers; at the
+// key's end the group sums are added across groups by a fixed xor-shuffle
+// tree and written once.  With DW each entry's dot product over the batch
+// tile is reduced over the group's lanes (fixed tree) and stored.  Indices
+// are read with clamped, unconditional loads so every load stays in flight.
+template <int BT, int NB, int U, bool DW>
+__global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
+{
+    constexpr int G = kWave / BT;
+    constexpr int STEP = G * U;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = (int)(threadIdx.x / kWave);
+    const int g = lane / BT;
+    const int bl = lane - g * BT;
+    const int bid = (int)blockIdx.x;
+    const int vb = (bid % kXcd) * A.per_xcd + bid / kXcd;
+    if (vb >= A.nblocks) return;
+    const int c = vb * kWavesPerBlock + wv;
+    if (c >= A.nchunks) return;
+    const int2 d0 = A.desc[c];
+    const int2 d1 = A.desc[c + 1];
+    const int bcol = (int)blockIdx.y * (BT * NB) + bl * NB;
+    const int32_t* __restrict__ idx = A.idx;
+    const float* __restrict__ vals = A.vals;
+    const float* __restrict__ Gm = A.G;
+    const int nkeys = A.nkeys;
+    int32_t p1 = d0.y;
+    for (int32_t r = d0.x; r < d1.x; ++r) {
+        const int32_t p0 = p1;
+        p1 = A.ptr[r + 1];
+        float acc[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+        float h[NB];
+        if constexpr (DW) load_nb<NB>(A.H + (int64_t)r * bp + bcol, h);
+        // lane l loads entry base + l of the next block (one coalesced index
+        // and value load per lane, issued a block ahead); groups pick their U
+        // entries out of it with shuffles
+        static_assert(STEP <= kWave, "one entry per lane per block");
+        static_assert(!DW || (U == 4 && BT >= 4), "dW reduces four entries over at least four lanes");
+        int32_t nidx_l = 0;
+        float nval_l = 0.0f;
+        auto load_next = [&](int32_t base) {
+            const int32_t k = base + lane;
+            const int32_t kc = k < p1 ? k : p1 - 1;
+            nidx_l = idx[kc];
+            nval_l = vals[kc];
+        };
+        if (p0 < p1) load_next(p0);
+        for (int32_t base = p0; base < p1; base += STEP) {
+            const int32_t ci = nidx_l;
+            const float cv = nval_l;
+            int32_t ii[U];
+            float vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ii[u] = __shfl(ci, u * G + g, kWave);
+                vv[u] = __shfl(cv, u * G + g, kWave);
+            }
+            float y[U][NB];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_nb<NB>(Gm + (int64_t)ii[u] * bp + bcol, y[u]);
+            load_next(base + STEP);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t k = base + u * G + g;
+                const float v = k < p1 ? vv[u] : 0.0f;
+#pragma unroll
+                for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[u][n], acc[n]);
+            }
+            if constexpr (DW) {
+                // four entries' dot products reduced over the group together
+                float d[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) a = fmaf(y[u][n], h[n], a);
+                    d[u] = a;
+                }
+                reduce4_group<BT>(d, bl);
+                constexpr int STRIDE = BT / 4;
+                if ((bl % STRIDE) == 0) {
+                    const int32_t k = base + ((bl / STRIDE) & 3) * G + g;
+                    if (k < p1) A.dwo[k] = d[0];
+                }
+            }
+        }
+#pragma unroll
+        for (int m = BT; m < kWave; m <<= 1)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[n] += __shfl_xor(acc[n], m, kWave);
+        if (g == 0) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const int b = bcol + n;
+                if (b < B) A.out[(int64_t)b * nkeys + r] = acc[n];
+            }
+        }
+    }
+}
+
+// dW in canonical order from dW in transposed order: dw[k] = dwt[iperm[k]].
+// Workgroups are remapped so that XCD x walks one contiguous eighth of the
+// canonical slots (one eighth of the rows); the transposed slots those rows
+// reach are then a few lines per column, which stay in that XCD's L2.
+__global__ void __launch_bounds__(kBlock) permute_dw_kernel(const int32_t* __restrict__ iperm,
+                                                            const float* __restrict__ dwt, int64_t nnz,
+                                                            int64_t per_block, int per_xcd, float* __restrict__ dw)
+{
+    const int bid = (int)blockIdx.x;
+    const int64_t vb = (int64_t)(bid % kXcd) * per_xcd + bid / kXcd;
+    const int64_t k0 = vb * per_block;
+    const int64_t k1 = k0 + per_block < nnz ? k0 + per_block : nnz;
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += kBlock) dw[k] = dwt[iperm[k]];
+}
+
 // dW[k] = sum_b dyt[r_k, b] * xt[c_k, b] over several batch tiles (batches
 // wider than one tile); group g of a wave step takes U consecutive slots and
 // its BT lanes are reduced by a butterfly.
@@ -657,6 +777,29 @@ snack_status dispatch_seg(const BatchPlan& p, int64_t cap, const View& va, const
     }
 }
 
+// key-major kernels: worth it where gathers dominate (wide batch tiles) and
+// keys are long enough to keep every group busy
+inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
+{
+    return p.btile >= 16 && v.nkeys > 0 && nnz / v.nkeys >= 128;
+}
+
+template <bool DW>
+snack_status launch_keyed(const BatchPlan& p, int64_t cap, const View& v, const float* G, const float* H, float* out,
+                          float* dwo, int B, hipStream_t s)
+{
+    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, cap);
+    dim3 grid((unsigned)(a.per_xcd * kXcd), (unsigned)p.ntiles);
+    switch (p.btile) {
+    case 16: hipLaunchKernelGGL((key_kernel<4, 4, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 32: hipLaunchKernelGGL((key_kernel<4, 8, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 64: hipLaunchKernelGGL((key_kernel<8, 8, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    default: return SNACK_ERR_INVALID_ARG;
+    }
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
 }  // namespace
 
 BatchPlan plan_batch(int B)
@@ -680,6 +823,8 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
                           hipStream_t s)
 {
     ProfScope prof(KC_SPMM_FWD, s);
+    if (use_keyed(L->fwd, L->nnz, p))
+        return launch_keyed<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, B, s);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
                                B, s);
 }
@@ -691,8 +836,23 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view
     if (dW && !dX)
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
+    if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
+        // dW once, in column order, then permuted into canonical order
+        SNACK_CHECK(launch_keyed<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, B, s));
+        if (L->nnz > 0) {
+            constexpr int64_t kPerBlock = 4 * kBlock;
+            const int64_t nblocks = (L->nnz + kPerBlock - 1) / kPerBlock;
+            const int per_xcd = (int)((nblocks + kXcd - 1) / kXcd);
+            hipLaunchKernelGGL(permute_dw_kernel, dim3((unsigned)(per_xcd * kXcd)), dim3(kBlock), 0, s, L->iperm, dW_t,
+                               L->nnz, kPerBlock, per_xcd, dW);
+            SNACK_HIP(hipGetLastError());
+        }
+        return SNACK_OK;
+    }
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
+    if (use_keyed(L->tr, L->nnz, p))
+        return launch_keyed<false>(p, L->cap, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
 }
 

@@ -60,6 +60,13 @@ def test_small_shapes_all_batch_plans(M, K, nnz):
     _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 13, 16, 17, 32, 33, 64, 65, 130), f"gpu/small/{M}x{K}")
 
 
+@pytest.mark.parametrize("M,K,nnz", [(4096, 64, 20000), (1000, 800, 200000)])
+def test_long_keys_wide_batches(M, K, nnz):
+    # hundreds of entries per row and per column: the key-major kernels and the
+    # column-order dW permuted into canonical order
+    _check_layer_vs_oracle(M, K, nnz, (9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
+
+
 def test_long_rows_and_columns_span_many_chunks():
     # a row longer than a chunk, a dense column, and many empty rows/columns
     M, K = 50, 6000
