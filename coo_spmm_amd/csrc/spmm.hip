@@ -534,7 +534,7 @@ __global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs 
 // tree and written once.  With DW each entry's dot product over the batch
 // tile is reduced over the group's lanes (fixed tree) and stored.  Indices
 // are read with clamped, unconditional loads so every load stays in flight.
-template <int BT, int NB, int U, bool DW>
+template <int BT, int NB, int U, bool DW, bool SPMM = true>
 __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 {
     constexpr int G = kWave / BT;
@@ -564,40 +564,55 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
         for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
         float h[NB];
         if constexpr (DW) load_nb<NB>(A.H + (int64_t)r * bp + bcol, h);
-        // lane l loads entry base + l of the next block (one coalesced index
-        // and value load per lane, issued a block ahead); groups pick their U
-        // entries out of it with shuffles
-        static_assert(STEP <= kWave, "one entry per lane per block");
-        static_assert(!DW || (U == 4 && BT >= 4), "dW reduces four entries over at least four lanes");
-        int32_t nidx_l = 0;
-        float nval_l = 0.0f;
+        // Blocks of STEP entries; the indices and values of the next block are
+        // loaded while the current one is gathered.  With STEP <= 64 lane l
+        // loads entry base + l and groups pick theirs by shuffles; with wider
+        // steps (one lane per group) each lane loads its own U entries.
+        static_assert(!DW || U == 4, "dW reduces four entries at a time");
+        constexpr bool SHUF = STEP <= kWave;
+        constexpr int NL = SHUF ? 1 : U;
+        int32_t nidx_l[NL];
+        float nval_l[NL];
         auto load_next = [&](int32_t base) {
-            const int32_t k = base + lane;
-            const int32_t kc = k < p1 ? k : p1 - 1;
-            nidx_l = idx[kc];
-            nval_l = vals[kc];
+#pragma unroll
+            for (int q = 0; q < NL; ++q) {
+                const int32_t k = SHUF ? base + lane : base + q * G + g;
+                const int32_t kc = k < p1 ? k : p1 - 1;
+                nidx_l[q] = idx[kc];
+                nval_l[q] = SPMM ? vals[kc] : 0.0f;
+            }
         };
         if (p0 < p1) load_next(p0);
         for (int32_t base = p0; base < p1; base += STEP) {
-            const int32_t ci = nidx_l;
-            const float cv = nval_l;
             int32_t ii[U];
             float vv[U];
+            if constexpr (SHUF) {
+                const int32_t ci = nidx_l[0];
+                const float cv = nval_l[0];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ii[u] = __shfl(ci, u * G + g, kWave);
-                vv[u] = __shfl(cv, u * G + g, kWave);
+                for (int u = 0; u < U; ++u) {
+                    ii[u] = __shfl(ci, u * G + g, kWave);
+                    vv[u] = __shfl(cv, u * G + g, kWave);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    ii[u] = nidx_l[u];
+                    vv[u] = nval_l[u];
+                }
             }
             float y[U][NB];
 #pragma unroll
             for (int u = 0; u < U; ++u) load_nb<NB>(Gm + (int64_t)ii[u] * bp + bcol, y[u]);
             load_next(base + STEP);
+            if constexpr (SPMM) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t k = base + u * G + g;
-                const float v = k < p1 ? vv[u] : 0.0f;
+                for (int u = 0; u < U; ++u) {
+                    const int32_t k = base + u * G + g;
+                    const float v = k < p1 ? vv[u] : 0.0f;
 #pragma unroll
-                for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[u][n], acc[n]);
+                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[u][n], acc[n]);
+                }
             }
             if constexpr (DW) {
                 // four entries' dot products reduced over the group together
@@ -610,22 +625,38 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
                     d[u] = a;
                 }
                 reduce4_group<BT>(d, bl);
-                constexpr int STRIDE = BT / 4;
-                if ((bl % STRIDE) == 0) {
-                    const int32_t k = base + ((bl / STRIDE) & 3) * G + g;
-                    if (k < p1) A.dwo[k] = d[0];
+                if constexpr (BT == 1) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int32_t k = base + u * G + g;
+                        if (k < p1) A.dwo[k] = d[u];
+                    }
+                } else if constexpr (BT == 2) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int32_t k = base + (2 * bl + t) * G + g;
+                        if (k < p1) A.dwo[k] = d[t];
+                    }
+                } else {
+                    constexpr int STRIDE = BT / 4;
+                    if ((bl % STRIDE) == 0) {
+                        const int32_t k = base + ((bl / STRIDE) & 3) * G + g;
+                        if (k < p1) A.dwo[k] = d[0];
+                    }
                 }
             }
         }
+        if constexpr (SPMM) {
 #pragma unroll
-        for (int m = BT; m < kWave; m <<= 1)
+            for (int m = BT; m < kWave; m <<= 1)
 #pragma unroll
-            for (int n = 0; n < NB; ++n) acc[n] += __shfl_xor(acc[n], m, kWave);
-        if (g == 0) {
+                for (int n = 0; n < NB; ++n) acc[n] += __shfl_xor(acc[n], m, kWave);
+            if (g == 0) {
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const int b = bcol + n;
-                if (b < B) A.out[(int64_t)b * nkeys + r] = acc[n];
+                for (int n = 0; n < NB; ++n) {
+                    const int b = bcol + n;
+                    if (b < B) A.out[(int64_t)b * nkeys + r] = acc[n];
+                }
             }
         }
     }
@@ -779,21 +810,27 @@ snack_status dispatch_seg(const BatchPlan& p, int64_t cap, const View& va, const
 
 // key-major kernels: worth it where gathers dominate (wide batch tiles) and
 // keys are long enough to keep every group busy
+constexpr int kKeyedRecomputeMax = 8;   // widest batch tile that recomputes dW over the row view
+
 inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
 {
-    return p.btile >= 16 && v.nkeys > 0 && nnz / v.nkeys >= 128;
+    return p.btile >= 1 && v.nkeys > 0 && nnz / v.nkeys >= 128;
 }
 
-template <bool DW>
+template <bool DW, bool SPMM = true>
 snack_status launch_keyed(const BatchPlan& p, int64_t cap, const View& v, const float* G, const float* H, float* out,
                           float* dwo, int B, hipStream_t s)
 {
     const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, cap);
     dim3 grid((unsigned)(a.per_xcd * kXcd), (unsigned)p.ntiles);
     switch (p.btile) {
-    case 16: hipLaunchKernelGGL((key_kernel<4, 4, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 32: hipLaunchKernelGGL((key_kernel<4, 8, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 64: hipLaunchKernelGGL((key_kernel<8, 8, 4, DW>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 1: hipLaunchKernelGGL((key_kernel<1, 1, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 2: hipLaunchKernelGGL((key_kernel<1, 2, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 4: hipLaunchKernelGGL((key_kernel<1, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 8: hipLaunchKernelGGL((key_kernel<2, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 16: hipLaunchKernelGGL((key_kernel<4, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 32: hipLaunchKernelGGL((key_kernel<4, 8, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 64: hipLaunchKernelGGL((key_kernel<8, 8, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
     default: return SNACK_ERR_INVALID_ARG;
     }
     SNACK_HIP(hipGetLastError());
@@ -834,11 +871,18 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
 {
     ProfScope prof(KC_SPMM_DX, s);
     // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view
-    if (dW && !dX)
+    if (dW && !dX) {
+        if (p.ntiles == 1 && use_keyed(L->fwd, L->nnz, p))
+            return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
+    }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
-        // dW once, in column order, then permuted into canonical order
         SNACK_CHECK(launch_keyed<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, B, s));
+        if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
+            // narrow batches: dW in canonical order by a second (cheap) pass over the row view
+            return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
+        }
+        // wide batches: dW once, in column order, then permuted into canonical order
         if (L->nnz > 0) {
             constexpr int64_t kPerBlock = 4 * kBlock;
             const int64_t nblocks = (L->nnz + kPerBlock - 1) / kPerBlock;

@@ -64,7 +64,30 @@ def test_small_shapes_all_batch_plans(M, K, nnz):
 def test_long_keys_wide_batches(M, K, nnz):
     # hundreds of entries per row and per column: the key-major kernels and the
     # column-order dW permuted into canonical order
-    _check_layer_vs_oracle(M, K, nnz, (9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
+    _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
+
+
+@pytest.mark.parametrize("M,K,nnz", [(130, 70, 2000), (1000, 800, 200000)])
+def test_backward_dx_only_and_dw_only(M, K, nnz):
+    # a first layer needs no dX; a frozen layer needs no dW: both paths alone
+    L = lib()
+    key = f"gpu/partial/{M}x{K}"
+    rows, cols, vals = _make(M, K, nnz, key)
+    ref = oracle.canonicalize(M, K, rows, cols, vals)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    try:
+        for B in (1, 4, 16, 64, 65):
+            X = normal((B, K), f"{key}/X/{B}")
+            dY = normal((B, M), f"{key}/dY/{B}")
+            say("partial backward", key, "B", B)
+            dX, _ = layer.backward(dev(X), dev(dY), want_dw=False)
+            dXr, dXa = oracle.backward_dx(M, K, ref["rows"], ref["cols"], ref["vals"], dY)
+            assert_close(f"dX-only B={B}", host(dX), dXr, dXa)
+            _, dW = layer.backward(dev(X), dev(dY), want_dx=False)
+            dWr, dWa = oracle.backward_dw(M, K, ref["rows"], ref["cols"], X, dY)
+            assert_close(f"dW-only B={B}", host(dW), dWr, dWa)
+    finally:
+        layer.close()
 
 
 def test_long_rows_and_columns_span_many_chunks():
