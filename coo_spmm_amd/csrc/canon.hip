@@ -123,17 +123,14 @@ __global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, 
     }
 }
 
-__global__ void build_transposed_kernel(const uint32_t* __restrict__ tkeys, const uint32_t* __restrict__ tslots,
-                                        int64_t nnz, const int32_t* __restrict__ rows, const float* __restrict__ vals,
-                                        int32_t* __restrict__ perm, int32_t* __restrict__ iperm,
-                                        int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t,
+__global__ void build_transposed_kernel(const uint32_t* __restrict__ tslots, int64_t nnz,
+                                        const int32_t* __restrict__ rows, const float* __restrict__ vals,
+                                        int32_t* __restrict__ iperm, int32_t* __restrict__ rows_t,
                                         float* __restrict__ vals_t)
 {
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * blockDim.x) {
         const int32_t k = (int32_t)tslots[j];
-        perm[j] = k;
         iperm[k] = (int32_t)j;
-        cols_t[j] = (int32_t)tkeys[j];
         rows_t[j] = rows[k];
         vals_t[j] = vals[k];
     }
@@ -196,8 +193,8 @@ struct TbEntry {
 
 __global__ void __launch_bounds__(kTbThreads) tb_scatter_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, const float* __restrict__ vals, int64_t nnz,
-    int64_t E, int32_t K, int32_t nb, const int32_t* __restrict__ mat, int32_t* __restrict__ perm,
-    int32_t* __restrict__ iperm, int32_t* __restrict__ rows_t, int32_t* __restrict__ cols_t, float* __restrict__ vals_t,
+    int64_t E, int32_t K, int32_t nb, const int32_t* __restrict__ mat, int32_t* __restrict__ iperm,
+    int32_t* __restrict__ rows_t, float* __restrict__ vals_t,
     int32_t* __restrict__ col_ptr)
 {
     extern __shared__ int32_t cur[];
@@ -248,8 +245,6 @@ __global__ void __launch_bounds__(kTbThreads) tb_scatter_kernel(
             __syncthreads();
         }
         rows_t[pos] = live ? x.r : 0;
-        cols_t[pos] = live ? x.c : 0;
-        perm[pos] = live ? (int32_t)k : 0;
         vals_t[pos] = live ? x.v : 0.0f;
         iperm[live ? k : nnz + tid] = live ? pos : 0;
     };
@@ -280,11 +275,17 @@ inline void tb_plan(int64_t nnz, int32_t K, int32_t* nb_out, int64_t* e_out)
     *e_out = (nnz + nb - 1) / nb;
 }
 
-__global__ void refresh_vals_t_kernel(const int32_t* __restrict__ perm, const float* __restrict__ vals, int64_t nnz,
+__global__ void refresh_vals_t_kernel(const int32_t* __restrict__ iperm, const float* __restrict__ vals, int64_t nnz,
                                       float* __restrict__ vals_t)
 {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * blockDim.x)
-        vals_t[j] = vals[perm[j]];
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x)
+        vals_t[iperm[k]] = vals[k];
+}
+
+__global__ void invert_iperm_kernel(const int32_t* __restrict__ iperm, int64_t nnz, int32_t* __restrict__ perm)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += (int64_t)gridDim.x * blockDim.x)
+        perm[iperm[k]] = (int32_t)k;
 }
 
 snack_status build_view_partition(View& v, void* scratch, hipStream_t s)
@@ -384,7 +385,7 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(exclusive_scan_i32(mat, mat, (int64_t)m, nullptr, scan_scr, s));
         hipLaunchKernelGGL(tb_scatter_kernel, dim3(grid), dim3(kTbThreads), lds, s, L->rows, L->cols, L->vals, nnz, E,
-                           L->K, nb, mat, L->perm, L->iperm, L->rows_t, L->cols_t, L->vals_t, L->col_ptr);
+                           L->K, nb, mat, L->iperm, L->rows_t, L->vals_t, L->col_ptr);
         SNACK_HIP(hipGetLastError());
     } else {
         if (nnz > 0) {
@@ -399,13 +400,17 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
             SNACK_HIP(hipGetLastError());
             // canonical order is (row, col), so a stable sort by column yields (col, row)
             SNACK_CHECK(radix_sort_u32(tkeys, tslots, nnz, bits_for((uint64_t)(L->K - 1)), p, s));
-            hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tkeys, tslots,
-                               nnz, L->rows, L->vals, L->perm, L->iperm, L->rows_t, L->cols_t, L->vals_t);
+            hipLaunchKernelGGL(build_transposed_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, tslots, nnz,
+                               L->rows, L->vals, L->iperm, L->rows_t, L->vals_t);
+            // the sorted keys are the columns in transposed order
+            hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s,
+                               (const int32_t*)tkeys, nnz, L->K, L->col_ptr);
+            SNACK_HIP(hipGetLastError());
+        } else {
+            hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(1)), dim3(kThreads), 0, s, L->rows, (int64_t)0,
+                               L->K, L->col_ptr);
             SNACK_HIP(hipGetLastError());
         }
-        hipLaunchKernelGGL(build_ptr_kernel, dim3(grid_for(nnz + 1)), dim3(kThreads), 0, s, L->cols_t, nnz, L->K,
-                           L->col_ptr);
-        SNACK_HIP(hipGetLastError());
     }
     L->vals_t_stale = false;
     SNACK_CHECK(build_view_partition(L->fwd, L->scratch, s));
@@ -417,11 +422,20 @@ snack_status refresh_vals_t(snack_layer* L, hipStream_t s)
 {
     if (L->nnz > 0) {
         ProfScope prof(KC_VALS_T_REFRESH, s);
-        hipLaunchKernelGGL(refresh_vals_t_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->perm, L->vals,
+        hipLaunchKernelGGL(refresh_vals_t_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->iperm, L->vals,
                            L->nnz, L->vals_t);
         SNACK_HIP(hipGetLastError());
     }
     L->vals_t_stale = false;
+    return SNACK_OK;
+}
+
+snack_status invert_iperm(const snack_layer* L, int32_t* perm, hipStream_t s)
+{
+    if (L->nnz > 0) {
+        hipLaunchKernelGGL(invert_iperm_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->iperm, L->nnz, perm);
+        SNACK_HIP(hipGetLastError());
+    }
     return SNACK_OK;
 }
 

@@ -37,7 +37,6 @@ enum KernelClass : int {
 struct View {
     int32_t nkeys = 0;      // M (canonical) or K (transposed)
     int32_t nidx = 0;       // K (canonical) or M (transposed)
-    int32_t* keys = nullptr;
     int32_t* idx = nullptr;
     float* vals = nullptr;
     int32_t* ptr = nullptr;         // [nkeys + 1]
@@ -68,10 +67,8 @@ struct snack_layer {
     float* vals = nullptr;
     int32_t* row_ptr = nullptr;   // [M+1]
     // transposed (column-sorted) index
-    int32_t* perm = nullptr;      // transposed slot -> canonical slot
     int32_t* iperm = nullptr;     // canonical slot -> transposed slot
     int32_t* rows_t = nullptr;
-    int32_t* cols_t = nullptr;    // sorted column keys
     float* vals_t = nullptr;      // values in transposed order
     int32_t* col_ptr = nullptr;   // [K+1]
     bool vals_t_stale = true;
@@ -81,8 +78,8 @@ struct snack_layer {
     const float* dwt_for = nullptr;
     bool dwt_valid = false;
 
-    snack::View fwd;   // keys = rows, idx = cols
-    snack::View tr;    // keys = cols_t, idx = rows_t
+    snack::View fwd;   // idx = cols
+    snack::View tr;    // idx = rows_t
 
     // per-batch workspace: feature-major copies of X and dY
     float* ws = nullptr;
@@ -157,8 +154,10 @@ snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t
 // Given canonical rows/cols/vals, build row_ptr, the transposed view, vals_t,
 // and both work partitions.
 snack_status canon_build_index(snack_layer* L, hipStream_t s);
-// vals_t[j] = vals[perm[j]]
+// vals_t[iperm[k]] = vals[k]
 snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
+// perm[iperm[k]] = k: the transposed slot -> canonical slot map, into a caller buffer
+snack_status invert_iperm(const snack_layer* L, int32_t* perm, hipStream_t s);
 
 // ---- kernels ---------------------------------------------------------------
 // Batch tiling for a batch of B columns: B_tile columns per kernel pass, padded

@@ -134,10 +134,8 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(rows, int32_t*, nb4);
     ALLOC(cols, int32_t*, nb4);
     ALLOC(vals, float*, nb4);
-    ALLOC(perm, int32_t*, nb4);
     ALLOC(iperm, int32_t*, nb4);
     ALLOC(rows_t, int32_t*, nb4);
-    ALLOC(cols_t, int32_t*, nb4);
     ALLOC(vals_t, float*, nb4);
     ALLOC(dwt, float*, nb4);
     ALLOC(row_ptr, int32_t*, ((size_t)M + 1) * 4);
@@ -149,7 +147,6 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     if (nchf > INT_MAX / 2 || ncht > INT_MAX / 2) return fail(SNACK_ERR_UNSUPPORTED);
     L->fwd.nkeys = M;
     L->fwd.nidx = K;
-    L->fwd.keys = L->rows;
     L->fwd.idx = L->cols;
     L->fwd.vals = L->vals;
     L->fwd.ptr = L->row_ptr;
@@ -159,7 +156,6 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(fwd.n_empty, int32_t*, 4);
     L->tr.nkeys = K;
     L->tr.nidx = M;
-    L->tr.keys = L->cols_t;
     L->tr.idx = L->rows_t;
     L->tr.vals = L->vals_t;
     L->tr.ptr = L->col_ptr;
@@ -318,7 +314,7 @@ extern "C" snack_status snack_layer_export_index(snack_layer* L, int32_t* row_pt
     if (row_ptr) SNACK_HIP(hipMemcpyAsync(row_ptr, L->row_ptr, ((size_t)L->M + 1) * 4, hipMemcpyDeviceToDevice, s));
     if (col_ptr) SNACK_HIP(hipMemcpyAsync(col_ptr, L->col_ptr, ((size_t)L->K + 1) * 4, hipMemcpyDeviceToDevice, s));
     if (n4) {
-        if (perm) SNACK_HIP(hipMemcpyAsync(perm, L->perm, n4, hipMemcpyDeviceToDevice, s));
+        if (perm) SNACK_CHECK(invert_iperm(L, perm, s));
         if (rows_t) SNACK_HIP(hipMemcpyAsync(rows_t, L->rows_t, n4, hipMemcpyDeviceToDevice, s));
         if (vals_t) {
             if (L->vals_t_stale) SNACK_CHECK(refresh_vals_t(L, s));

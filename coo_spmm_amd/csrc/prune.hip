@@ -60,12 +60,12 @@ __device__ inline uint32_t mag_bits(float v) { return __float_as_uint(v) & 0x7FF
 
 // ---- drop: radix select ---------------------------------------------------
 // state: [0] prefix, [1] rank still to find among keys matching the prefix.
-// Each workgroup writes its own 256-bin histogram row (no global atomics);
-// a thread adds runs of equal digits before touching LDS, which keeps the
-// first passes (where nearly every key shares a digit) free of contention.
+// A thread adds runs of equal digits before touching LDS, which keeps the
+// first passes (where nearly every key shares a digit) free of contention;
+// each workgroup then adds its nonzero bins to the global histogram.
 __global__ void __launch_bounds__(kThreads) sel_hist_kernel(const float* __restrict__ vals, int64_t n,
                                                             const uint32_t* __restrict__ state, int shift,
-                                                            uint32_t* __restrict__ mat)
+                                                            uint32_t* __restrict__ hist)
 {
     __shared__ uint32_t h[256];
     h[threadIdx.x] = 0;
@@ -86,31 +86,23 @@ __global__ void __launch_bounds__(kThreads) sel_hist_kernel(const float* __restr
     }
     if (run) atomicAdd(&h[run_d], run);
     __syncthreads();
-    mat[(size_t)blockIdx.x * 256 + threadIdx.x] = h[threadIdx.x];
+    if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
 }
 
-// 1024 threads: four row groups per bin, each with independent accumulators
-__global__ void __launch_bounds__(1024) sel_pick_kernel(const uint32_t* __restrict__ mat, int nblk,
-                                                        uint32_t* __restrict__ state, int shift)
+// picks the digit holding the wanted rank, then clears the histogram for the next pass
+__global__ void __launch_bounds__(256) sel_pick_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ state,
+                                                       int shift)
 {
-    __shared__ uint32_t part[4][256];
-    const int d = threadIdx.x & 255, q = threadIdx.x >> 8;
-    uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int b = q;
-    for (; b + 28 < nblk; b += 32) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] += mat[(size_t)(b + 4 * u) * 256 + d];
-    }
-    for (; b < nblk; b += 4) acc[0] += mat[(size_t)b * 256 + d];
-    part[q][d] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
+    __shared__ uint32_t tot[256];
+    tot[threadIdx.x] = hist[threadIdx.x];
     __syncthreads();
+    hist[threadIdx.x] = 0;
     if (threadIdx.x == 0) {
         uint32_t r = state[1];
         uint32_t dg = 0;
         for (; dg < 255; ++dg) {
-            const uint32_t t = part[0][dg] + part[1][dg] + part[2][dg] + part[3][dg];
-            if (r < t) break;
-            r -= t;
+            if (r < tot[dg]) break;
+            r -= tot[dg];
         }
         state[0] |= dg << shift;
         state[1] = r;
@@ -319,7 +311,7 @@ __global__ void emit_entries_kernel(const uint32_t* __restrict__ occ_bm, const u
 struct PruneScratch {
     uint32_t* state;    // [16]
     int32_t* count;     // [4]
-    uint32_t* selmat;   // [kSelBlocks * 256]
+    uint32_t* selmat;   // [256] selection histogram
     int32_t* a;         // [nnz] flags / eq
     int32_t* b;         // [nnz] scan result
     int32_t* keep;      // [nnz]
@@ -360,7 +352,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         off += al(bytes);
         return o;
     };
-    size_t o_state = take(16 * 4), o_count = take(16), o_sel = take((size_t)kSelBlocks * 256 * 4);
+    size_t o_state = take(16 * 4), o_count = take(16), o_sel = take((size_t)256 * 4);
     size_t o_a = take((size_t)n * 4), o_b = take((size_t)n * 4), o_keep = take((size_t)n * 4);
     size_t o_kval = take((size_t)n * 4);
     size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4);
@@ -422,10 +414,11 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
         int nblk = (int)grid_for(nnz);
         if (nblk > kSelBlocks) nblk = kSelBlocks;
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.selmat, (int64_t)256, 0u);
         for (int shift = 24; shift >= 0; shift -= 8) {
             hipLaunchKernelGGL(sel_hist_kernel, dim3(nblk), dim3(kThreads), 0, s, L->vals, nnz, ps.state, shift,
                                ps.selmat);
-            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(1024), 0, s, ps.selmat, nblk, ps.state, shift);
+            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(256), 0, s, ps.selmat, ps.state, shift);
         }
         SNACK_HIP(hipGetLastError());
         hipLaunchKernelGGL(eq_flags_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->vals, nnz, ps.state, ps.a);
