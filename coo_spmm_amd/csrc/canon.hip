@@ -80,38 +80,55 @@ __global__ void build_ptr_kernel(const int32_t* __restrict__ keys, int64_t nnz, 
 }
 
 // desc[c] = (r, ptr[r]) with r the smallest key such that ptr[r] + r >= c * work;
-// desc[nchunks] = (nkeys, nnz).
-__global__ void build_chunks_kernel(const int32_t* __restrict__ ptr, int32_t nkeys, int32_t nchunks, int32_t work,
-                                    int2* __restrict__ desc)
+// desc[nchunks] = (nkeys, nnz).  One launch serves both views (blockIdx.y);
+// it also clears the views' empty-key counters for the append that follows.
+struct PartArgs {
+    const int32_t* ptr;
+    int32_t nkeys;
+    int32_t nchunks;
+    int2* desc;
+    int32_t* empty_keys;
+    int32_t* n_empty;
+};
+
+__global__ void build_chunks_kernel(PartArgs va, PartArgs vb, int32_t work)
 {
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c <= nchunks;
+    const PartArgs& v = blockIdx.y == 0 ? va : vb;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *v.n_empty = 0;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c <= v.nchunks;
          c += (int64_t)gridDim.x * blockDim.x) {
-        int32_t key = nkeys;
-        if (c < nchunks) {
+        int32_t key = v.nkeys;
+        if (c < v.nchunks) {
             const int64_t target = c * (int64_t)work;
-            int32_t lo = 0, hi = nkeys;
+            int32_t lo = 0, hi = v.nkeys;
             while (lo < hi) {
                 const int32_t mid = lo + ((hi - lo) >> 1);
-                if ((int64_t)ptr[mid] + mid >= target) hi = mid;
+                if ((int64_t)v.ptr[mid] + mid >= target) hi = mid;
                 else lo = mid + 1;
             }
             key = lo;
         }
-        desc[c] = make_int2(key, ptr[key]);
+        v.desc[c] = make_int2(key, v.ptr[key]);
     }
 }
 
-__global__ void empty_flags_kernel(const int32_t* __restrict__ ptr, int32_t nkeys, int32_t* __restrict__ flags)
+// Keys without entries, in no particular order (the SpMM only writes zeros
+// for them, so the order cannot change any result); one atomic per wave.
+__global__ void empty_keys_kernel(PartArgs va, PartArgs vb)
 {
-    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nkeys; r += (int64_t)gridDim.x * blockDim.x)
-        flags[r] = ptr[r] == ptr[r + 1] ? 1 : 0;
-}
-
-__global__ void empty_compact_kernel(const int32_t* __restrict__ flags, const int32_t* __restrict__ pos,
-                                     int32_t nkeys, int32_t* __restrict__ out)
-{
-    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nkeys; r += (int64_t)gridDim.x * blockDim.x)
-        if (flags[r]) out[pos[r]] = (int32_t)r;
+    const PartArgs& v = blockIdx.y == 0 ? va : vb;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r0 = (int64_t)blockIdx.x * blockDim.x; r0 < v.nkeys; r0 += stride) {
+        const int64_t r = r0 + threadIdx.x;
+        const bool empty = r < v.nkeys && v.ptr[r] == v.ptr[r + 1];
+        const uint64_t m = __ballot(empty);
+        if (m == 0) continue;
+        int32_t base = 0;
+        if (lane == __ffsll((unsigned long long)m) - 1) base = atomicAdd(v.n_empty, __popcll(m));
+        base = __shfl(base, __ffsll((unsigned long long)m) - 1, kWave);
+        if (empty) v.empty_keys[base + __popcll(m & ((1ull << lane) - 1ull))] = (int32_t)r;
+    }
 }
 
 __global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, uint32_t* __restrict__ keys,
@@ -288,17 +305,24 @@ __global__ void invert_iperm_kernel(const int32_t* __restrict__ iperm, int64_t n
         perm[iperm[k]] = (int32_t)k;
 }
 
-snack_status build_view_partition(View& v, void* scratch, hipStream_t s)
+snack_status build_view_partitions(snack_layer* L, hipStream_t s)
 {
-    hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)v.nchunks + 1)), dim3(kThreads), 0, s, v.ptr,
-                       v.nkeys, v.nchunks, kChunkWork, v.desc);
-    int32_t* flags = (int32_t*)scratch;
-    int32_t* pos = flags + (((size_t)v.nkeys + 63) & ~(size_t)63);
-    void* scan_scr = pos + (((size_t)v.nkeys + 63) & ~(size_t)63);
-    hipLaunchKernelGGL(empty_flags_kernel, dim3(grid_for(v.nkeys)), dim3(kThreads), 0, s, v.ptr, v.nkeys, flags);
-    SNACK_CHECK(exclusive_scan_i32(flags, pos, v.nkeys, v.n_empty, scan_scr, s));
-    hipLaunchKernelGGL(empty_compact_kernel, dim3(grid_for(v.nkeys)), dim3(kThreads), 0, s, flags, pos, v.nkeys,
-                       v.empty_keys);
+    auto args = [](const View& v) {
+        PartArgs a;
+        a.ptr = v.ptr;
+        a.nkeys = v.nkeys;
+        a.nchunks = v.nchunks;
+        a.desc = v.desc;
+        a.empty_keys = v.empty_keys;
+        a.n_empty = v.n_empty;
+        return a;
+    };
+    const PartArgs a = args(L->fwd), b = args(L->tr);
+    const int32_t nc = a.nchunks > b.nchunks ? a.nchunks : b.nchunks;
+    const int32_t nk = a.nkeys > b.nkeys ? a.nkeys : b.nkeys;
+    hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)nc + 1), 2), dim3(kThreads), 0, s, a, b,
+                       kChunkWork);
+    hipLaunchKernelGGL(empty_keys_kernel, dim3(grid_for(nk), 2), dim3(kThreads), 0, s, a, b);
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }
@@ -413,8 +437,7 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
         }
     }
     L->vals_t_stale = false;
-    SNACK_CHECK(build_view_partition(L->fwd, L->scratch, s));
-    SNACK_CHECK(build_view_partition(L->tr, L->scratch, s));
+    SNACK_CHECK(build_view_partitions(L, s));
     return SNACK_OK;
 }
 

@@ -8,8 +8,6 @@
 // digit-major histogram.  Integer-only, deterministic.
 #include "internal.h"
 
-#include <atomic>
-
 namespace snack {
 namespace {
 
@@ -55,117 +53,86 @@ __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* smem /*[THREA
     return wave_base + inc - v;
 }
 
-// ---- single-pass scan (decoupled look-back) ----------------------------------
-// A workgroup takes the next tile by ticket, reduces it, publishes its
-// aggregate, and walks back over its predecessors' published words (64 at a
-// time, one per lane of wave 0) until it meets an inclusive prefix; then it
-// publishes its own inclusive prefix and writes the tile.  Each published
-// word packs (call tag, status, value) so it is read and written atomically,
-// and the tag lets a call ignore words left by earlier calls (no clearing).
-// The words are read and written with atomic read-modify-write operations:
-// those are coherent across the XCDs, where a plain load may be served by a
-// stale line in the reader's own L2.
-// A workgroup waits only on tickets handed out before its own, whose holders
-// are already running, so the walk always ends.  The ticket counter is
-// cleared by a one-thread kernel launched just before.
-constexpr int kDlThreads = 256;
-constexpr int kDlRounds = 4;                        // int4 per thread per tile
-constexpr int kDlTile = kDlThreads * 4 * kDlRounds;  // 4096 items
-constexpr uint64_t kDlAgg = 1, kDlIncl = 2;
+// ---- exclusive scan: tile totals, then tiles with their prefix ----------------
+// Kernel 1 reduces each tile of 4096 items (int4 loads) to its total.  Kernel
+// 2 rescans each tile and adds the tile's prefix: with at most kScanDirect
+// tiles the workgroup sums the totals before its tile itself (they are few
+// and stay in L2); with more, the totals are first scanned in place by the
+// same routine (two levels reach 2^36 items).  No atomics, no waiting.
+constexpr int kScanThreads = 256;
+constexpr int kScanRounds = 4;                                // int4 per thread per tile
+constexpr int kScanTile = kScanThreads * 4 * kScanRounds;    // 4096 items
+constexpr int64_t kScanDirect = 4096;
 
-__device__ inline uint64_t dl_word(uint32_t tag, uint64_t status, uint64_t value)
+template <bool VEC>
+__device__ inline int4 scan_load(const int32_t* __restrict__ in, int64_t e, int64_t n)
 {
-    return ((uint64_t)tag << 40) | (status << 38) | (value & ((1ull << 38) - 1));
-}
-
-__global__ void scan_ticket_reset_kernel(unsigned long long* __restrict__ ticket)
-{
-    if (threadIdx.x == 0 && blockIdx.x == 0) atomicExch(ticket, 0ull);
+    int4 x;
+    if (VEC && e + 3 < n) {
+        x = *reinterpret_cast<const int4*>(in + e);
+    } else {
+        x.x = e < n ? in[e] : 0;
+        x.y = e + 1 < n ? in[e + 1] : 0;
+        x.z = e + 2 < n ? in[e + 2] : 0;
+        x.w = e + 3 < n ? in[e + 3] : 0;
+    }
+    return x;
 }
 
 template <bool VEC>
-__global__ void __launch_bounds__(kDlThreads) scan_dl_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out,
-                                                             int64_t n, int32_t* __restrict__ total,
-                                                             unsigned long long* __restrict__ state,
-                                                             unsigned long long* __restrict__ ticket, uint32_t tag,
-                                                             int64_t ntiles)
+__global__ void __launch_bounds__(kScanThreads) scan_tile_sums_kernel(const int32_t* __restrict__ in, int64_t n,
+                                                                      int32_t* __restrict__ sums)
 {
-    __shared__ int32_t smem[kDlThreads / kWave];
-    __shared__ int64_t s_tile;
-    __shared__ int64_t s_prefix;
-    const int lane = lane_id();
-    const int w = threadIdx.x / kWave;
-    if (threadIdx.x == 0) s_tile = (int64_t)atomicAdd(ticket, 1ull);
-    __syncthreads();
-    const int64_t tile = s_tile;
-    const int64_t base = tile * kDlTile;
+    __shared__ int32_t smem[kScanThreads / kWave];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    int32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < kScanRounds; ++q) {
+        const int4 x = scan_load<VEC>(in, base + (int64_t)q * (kScanThreads * 4) + 4 * threadIdx.x, n);
+        s += x.x + x.y + x.z + x.w;
+    }
+    int32_t tot;
+    block_exclusive_scan<kScanThreads>(s, smem, &tot);
+    if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
 
-    int4 x[kDlRounds];
-    int32_t ex[kDlRounds];
-    int32_t sub[kDlRounds];
+// direct: the tile prefix is the sum of sums[0, tile); otherwise sums holds exclusive prefixes
+template <bool VEC, bool DIRECT>
+__global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(const int32_t* __restrict__ in,
+                                                                  int32_t* __restrict__ out, int64_t n,
+                                                                  const int32_t* __restrict__ sums, int64_t ntiles,
+                                                                  int32_t* __restrict__ total)
+{
+    __shared__ int32_t smem[kScanThreads / kWave];
+    const int64_t tile = blockIdx.x;
+    const int64_t base = tile * kScanTile;
+    int32_t prefix;
+    if constexpr (DIRECT) {
+        int32_t part = 0;
+        for (int64_t i = threadIdx.x; i < tile; i += kScanThreads) part += sums[i];
+        int32_t tot;
+        block_exclusive_scan<kScanThreads>(part, smem, &tot);
+        prefix = tot;
+    } else {
+        prefix = sums[tile];
+    }
+    int4 x[kScanRounds];
+    int32_t ex[kScanRounds], sub[kScanRounds];
     int32_t agg = 0;
 #pragma unroll
-    for (int q = 0; q < kDlRounds; ++q) {
-        const int64_t e = base + (int64_t)q * (kDlThreads * 4) + 4 * threadIdx.x;
-        if (VEC && e + 3 < n) {
-            x[q] = *reinterpret_cast<const int4*>(in + e);
-        } else {
-            x[q].x = e < n ? in[e] : 0;
-            x[q].y = e + 1 < n ? in[e + 1] : 0;
-            x[q].z = e + 2 < n ? in[e + 2] : 0;
-            x[q].w = e + 3 < n ? in[e + 3] : 0;
-        }
+    for (int q = 0; q < kScanRounds; ++q) {
+        x[q] = scan_load<VEC>(in, base + (int64_t)q * (kScanThreads * 4) + 4 * threadIdx.x, n);
         int32_t tot;
-        ex[q] = block_exclusive_scan<kDlThreads>(x[q].x + x[q].y + x[q].z + x[q].w, smem, &tot);
+        ex[q] = block_exclusive_scan<kScanThreads>(x[q].x + x[q].y + x[q].z + x[q].w, smem, &tot);
         sub[q] = agg;
         agg += tot;
     }
-
-    if (w == 0) {
-        int64_t prefix = 0;
-        if (tile == 0) {
-            if (lane == 0)
-                atomicExch(&state[0], (unsigned long long)dl_word(tag, kDlIncl, (uint64_t)agg));
-        } else {
-            if (lane == 0)
-                atomicExch(&state[tile], (unsigned long long)dl_word(tag, kDlAgg, (uint64_t)agg));
-            int64_t j = tile - 1;
-            for (;;) {
-                const int64_t idx = j - lane;
-                uint64_t st = kDlIncl, val = 0;
-                if (idx >= 0) {
-                    for (;;) {
-                        const unsigned long long wd = atomicAdd(&state[idx], 0ull);
-                        st = ((uint32_t)(wd >> 40) == tag) ? ((wd >> 38) & 3ull) : 0ull;
-                        val = wd & ((1ull << 38) - 1);
-                        if (st != 0) break;
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-                const uint64_t incl = __ballot(st == kDlIncl);
-                const int stop = incl ? __ffsll((unsigned long long)incl) - 1 : kWave - 1;
-                int64_t v = lane <= stop ? (int64_t)val : 0;
+    if (total && tile == ntiles - 1 && threadIdx.x == 0) *total = prefix + agg;
 #pragma unroll
-                for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-                prefix += v;
-                if (incl) break;
-                j -= kWave;
-            }
-            if (lane == 0)
-                atomicExch(&state[tile], (unsigned long long)dl_word(tag, kDlIncl, (uint64_t)(prefix + agg)));
-        }
-        if (lane == 0) {
-            s_prefix = prefix;
-            if (tile == ntiles - 1 && total) *total = (int32_t)(prefix + agg);
-        }
-    }
-    __syncthreads();
-    const int32_t pre = (int32_t)s_prefix;
-#pragma unroll
-    for (int q = 0; q < kDlRounds; ++q) {
-        const int64_t e = base + (int64_t)q * (kDlThreads * 4) + 4 * threadIdx.x;
+    for (int q = 0; q < kScanRounds; ++q) {
+        const int64_t e = base + (int64_t)q * (kScanThreads * 4) + 4 * threadIdx.x;
         int4 o;
-        o.x = pre + sub[q] + ex[q];
+        o.x = prefix + sub[q] + ex[q];
         o.y = o.x + x[q].x;
         o.z = o.y + x[q].y;
         o.w = o.z + x[q].z;
@@ -298,8 +265,14 @@ snack_status radix_sort_impl(KeyT* keys, uint32_t* vals, int64_t n, int key_bits
 
 size_t scan_scratch_bytes(int64_t n)
 {
-    const int64_t nt = (n + kDlTile - 1) / kDlTile;
-    return (((size_t)nt + 1) * 8 + 255) & ~(size_t)255;
+    size_t b = 0;
+    int64_t m = n;
+    do {
+        const int64_t nt = (m + kScanTile - 1) / kScanTile;
+        b += (((size_t)nt + 64) * 4 + 255) & ~(size_t)255;
+        m = nt;
+    } while (m > kScanDirect);
+    return b;
 }
 
 snack_status exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total_dev, void* scratch,
@@ -309,21 +282,31 @@ snack_status exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int3
         if (total_dev) SNACK_HIP(hipMemsetAsync(total_dev, 0, 4, s));
         return SNACK_OK;
     }
-    // every call gets its own tag (never 0), so stale words and tickets are ignored
-    static std::atomic<uint32_t> calls{0};
-    uint32_t tag = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0xFFFFFFu;
-    if (tag == 0) tag = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0xFFFFFFu;
-    const int64_t nt = (n + kDlTile - 1) / kDlTile;
-    unsigned long long* ticket = (unsigned long long*)scratch;
-    unsigned long long* state = ticket + 1;
+    const int64_t nt = (n + kScanTile - 1) / kScanTile;
+    int32_t* sums = (int32_t*)scratch;
+    void* rest = (char*)scratch + ((((size_t)nt + 64) * 4 + 255) & ~(size_t)255);
     const bool vec = ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
-    hipLaunchKernelGGL(scan_ticket_reset_kernel, dim3(1), dim3(64), 0, s, ticket);
     if (vec)
-        hipLaunchKernelGGL(scan_dl_kernel<true>, dim3((unsigned)nt), dim3(kDlThreads), 0, s, in, out, n, total_dev,
-                           state, ticket, tag, nt);
+        hipLaunchKernelGGL(scan_tile_sums_kernel<true>, dim3((unsigned)nt), dim3(kScanThreads), 0, s, in, n, sums);
     else
-        hipLaunchKernelGGL(scan_dl_kernel<false>, dim3((unsigned)nt), dim3(kDlThreads), 0, s, in, out, n, total_dev,
-                           state, ticket, tag, nt);
+        hipLaunchKernelGGL(scan_tile_sums_kernel<false>, dim3((unsigned)nt), dim3(kScanThreads), 0, s, in, n, sums);
+    SNACK_HIP(hipGetLastError());
+    if (nt <= kScanDirect) {
+        if (vec)
+            hipLaunchKernelGGL((scan_tiles_kernel<true, true>), dim3((unsigned)nt), dim3(kScanThreads), 0, s, in, out,
+                               n, sums, nt, total_dev);
+        else
+            hipLaunchKernelGGL((scan_tiles_kernel<false, true>), dim3((unsigned)nt), dim3(kScanThreads), 0, s, in,
+                               out, n, sums, nt, total_dev);
+    } else {
+        SNACK_CHECK(exclusive_scan_i32(sums, sums, nt, nullptr, rest, s));
+        if (vec)
+            hipLaunchKernelGGL((scan_tiles_kernel<true, false>), dim3((unsigned)nt), dim3(kScanThreads), 0, s, in,
+                               out, n, sums, nt, total_dev);
+        else
+            hipLaunchKernelGGL((scan_tiles_kernel<false, false>), dim3((unsigned)nt), dim3(kScanThreads), 0, s, in,
+                               out, n, sums, nt, total_dev);
+    }
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }
