@@ -13,14 +13,15 @@
 //          candidate is accepted if its cell is neither kept nor accepted at a
 //          smaller t.
 // Occupancy lives in two bitmaps over the M*K cells: `kept` and `occ` (kept or
-// grown).  Candidates are tested in batches against `occ`; inside a batch an
-// open-addressing hash table keyed by cell keeps, per cell, the smallest
-// candidate index that named it (an atomic minimum on (cell, index) packed in
-// one word, so the order of the atomics does not matter), and a scan in t
-// order keeps the first `need` accepted -- the result never depends on the
-// batch size.  The new canonical order is then the set bits of `occ` in
-// ascending position: a prefix count of bits per 256-cell group places every
-// entry, and a kept cell takes the next kept value (its rank in `kept`).
+// grown).  Candidates are tested in batches against `occ`; the free ones claim
+// their cell in `occ` with an atomic OR, and the rare cells claimed twice in a
+// batch are resolved in an open-addressing table that keeps the smallest
+// candidate index per cell (an atomic minimum on (cell, index) packed in one
+// word, so the order of the atomics does not matter).  A scan in t order
+// keeps the first `need` accepted and the rest give their cells back -- the
+// result never depends on the batch size.  The new canonical order is then the set bits of `occ` in
+// ascending position: prefix counts of bits place every entry, and a kept
+// cell takes the next kept value (its rank in `kept`).
 // Every step is integer work and deterministic.
 #include "internal.h"
 
@@ -34,7 +35,6 @@ constexpr int kTBits = 21;                       // candidate index bits in a ta
 constexpr int kHashBits = 22;                    // table slots (load <= 1/2)
 constexpr uint64_t kEmpty = ~0ull;
 constexpr uint64_t kMaxBitmapBits = 1ull << 34;
-constexpr int kGroupWords = 8;                   // bitmap words per prefix-count group
 constexpr int kSelBlocks = 512;                  // workgroups of one selection pass
 
 static_assert(kMaxBatch <= (1ll << kTBits), "candidate index must fit its field");
@@ -192,106 +192,229 @@ __global__ void hash_clear_kernel(unsigned long long* __restrict__ tab, int64_t 
 
 __device__ inline uint32_t hash_slot(uint64_t pos) { return (uint32_t)((pos * kGamma) >> (64 - kHashBits)); }
 
-// table word = cell << kTBits | candidate index: words of one cell compare by index
-__global__ void hash_insert_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
-                                   unsigned long long* __restrict__ tab)
+// Every free candidate claims its cell in `occ`.  Occupied cells were filtered
+// out when the batch was generated, so a claim that finds its bit already set
+// lost to another candidate of this batch: the cell is marked contested.
+__global__ void claim_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N, uint32_t* __restrict__ occ_bm,
+                             uint32_t* __restrict__ con_bm)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t p = cpos[i];
+        if (p >= N) continue;
+        const uint32_t bit = 1u << (p & 31);
+        const uint32_t old = atomicOr(&occ_bm[p >> 5], bit);
+        if (old & bit) atomicOr(&con_bm[p >> 5], bit);
+    }
+}
+
+// Claimants of contested cells register (cell, index) in an open-addressing
+// table; the word packs cell << kTBits | index, so an atomic minimum keeps the
+// smallest index whatever the order of the atomics.
+__global__ void contest_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
+                               const uint32_t* __restrict__ con_bm, unsigned long long* __restrict__ tab,
+                               int32_t* __restrict__ cflag)
 {
     const uint32_t mask = (1u << kHashBits) - 1u;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
         const uint64_t p = cpos[i];
-        if (p >= N) continue;
-        const unsigned long long word = (p << kTBits) | (uint64_t)i;
-        uint32_t h = hash_slot(p);
-        for (uint32_t probe = 0; probe <= mask; ++probe) {
-            const unsigned long long old = atomicCAS(&tab[h], (unsigned long long)kEmpty, word);
-            if (old == kEmpty) break;
-            if ((old >> kTBits) == p) {
-                if (word < old) atomicMin(&tab[h], word);
-                break;
+        int32_t f = 0;
+        if (p < N && ((con_bm[p >> 5] >> (p & 31)) & 1u)) {
+            f = 1;
+            const unsigned long long word = (p << kTBits) | (uint64_t)i;
+            uint32_t h = hash_slot(p);
+            for (uint32_t probe = 0; probe <= mask; ++probe) {
+                const unsigned long long old = atomicCAS(&tab[h], (unsigned long long)kEmpty, word);
+                if (old == kEmpty) break;
+                if ((old >> kTBits) == p) {
+                    if (word < old) atomicMin(&tab[h], word);
+                    break;
+                }
+                h = (h + 1u) & mask;
             }
-            h = (h + 1u) & mask;
         }
+        cflag[i] = f;
     }
 }
 
 // accepted[i] = candidate i is free and the first (smallest index) to name its cell
-__global__ void hash_first_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
-                                  const unsigned long long* __restrict__ tab, int32_t* __restrict__ accepted)
+__global__ void accept_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
+                              const int32_t* __restrict__ cflag, const unsigned long long* __restrict__ tab,
+                              int32_t* __restrict__ accepted)
 {
     const uint32_t mask = (1u << kHashBits) - 1u;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
         const uint64_t p = cpos[i];
         int32_t a = 0;
         if (p < N) {
-            uint32_t h = hash_slot(p);
-            for (uint32_t probe = 0; probe <= mask; ++probe) {
-                const unsigned long long w = tab[h];
-                if (w == kEmpty) break;
-                if ((w >> kTBits) == p) {
-                    a = (w & ((1ull << kTBits) - 1ull)) == (uint64_t)i ? 1 : 0;
-                    break;
+            if (!cflag[i]) {
+                a = 1;
+            } else {
+                uint32_t h = hash_slot(p);
+                for (uint32_t probe = 0; probe <= mask; ++probe) {
+                    const unsigned long long w = tab[h];
+                    if (w == kEmpty) break;
+                    if ((w >> kTBits) == p) {
+                        a = (w & ((1ull << kTBits) - 1ull)) == (uint64_t)i ? 1 : 0;
+                        break;
+                    }
+                    h = (h + 1u) & mask;
                 }
-                h = (h + 1u) & mask;
             }
         }
         accepted[i] = a;
     }
 }
 
-// the first `need` accepted candidates in stream order are grown
-__global__ void mark_grown_kernel(const uint64_t* __restrict__ cpos, int64_t T, const int32_t* __restrict__ accepted,
-                                  const int32_t* __restrict__ trank, int64_t need, uint32_t* __restrict__ occ_bm)
+// Accepted candidates past the first `need` give their cell back; contested
+// marks are cleared so the next batch starts from an empty contested map.
+__global__ void finish_kernel(const uint64_t* __restrict__ cpos, int64_t T, const int32_t* __restrict__ accepted,
+                              const int32_t* __restrict__ trank, const int32_t* __restrict__ cflag, int64_t need,
+                              uint32_t* __restrict__ occ_bm, uint32_t* __restrict__ con_bm)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        if (!accepted[i] || (int64_t)trank[i] >= need) continue;
+        const bool give_back = accepted[i] && (int64_t)trank[i] >= need;
+        const bool contested = cflag[i] != 0;
+        if (!give_back && !contested) continue;
         const uint64_t p = cpos[i];
-        atomicOr(&occ_bm[p >> 5], 1u << (p & 31));
+        const uint32_t bit = 1u << (p & 31);
+        if (give_back) atomicAnd(&occ_bm[p >> 5], ~bit);
+        if (contested) atomicAnd(&con_bm[p >> 5], ~bit);
     }
 }
 
 // ---- rebuild the canonical arrays from the bitmaps ---------------------------
-__global__ void group_counts_kernel(const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm,
-                                    int64_t words, int64_t groups, int32_t* __restrict__ occ_cnt,
-                                    int32_t* __restrict__ kept_cnt)
+// Tiles of 4096 bitmap words (256 threads x 16 consecutive words).  Kernel 1
+// counts each tile's occupied and kept bits; kernel 2 gives every thread its
+// first output slot and kept rank (the tile's prefix -- summed from the tile
+// counts before it when there are few tiles, else read from their scans --
+// plus a block scan of the thread counts) and emits its cells in order.
+constexpr int kEmitThreads = 256;
+constexpr int kEmitWords = 16;
+constexpr int64_t kEmitTile = (int64_t)kEmitThreads * kEmitWords;
+constexpr int64_t kEmitDirect = 4096;
+
+__device__ inline void block_exclusive2(int32_t& a, int32_t& b, int32_t* smem /*[2 * waves]*/, int32_t& ta,
+                                        int32_t& tb)
 {
-    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += (int64_t)gridDim.x * blockDim.x) {
-        int32_t a = 0, b = 0;
-        for (int j = 0; j < kGroupWords; ++j) {
-            const int64_t w = g * kGroupWords + j;
-            if (w < words) {
-                a += __popc(occ_bm[w]);
-                b += __popc(kept_bm[w]);
-            }
+    constexpr int W = kEmitThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int32_t ia = a, ib = b;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t oa = __shfl_up(ia, d, kWave), ob = __shfl_up(ib, d, kWave);
+        if (lane >= d) {
+            ia += oa;
+            ib += ob;
         }
-        occ_cnt[g] = a;
-        kept_cnt[g] = b;
+    }
+    if (lane == kWave - 1) {
+        smem[w] = ia;
+        smem[W + w] = ib;
+    }
+    __syncthreads();
+    int32_t ba = 0, bb = 0;
+    ta = 0;
+    tb = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        const int32_t xa = smem[i], xb = smem[W + i];
+        if (i < w) {
+            ba += xa;
+            bb += xb;
+        }
+        ta += xa;
+        tb += xb;
+    }
+    __syncthreads();
+    a = ba + ia - a;
+    b = bb + ib - b;
+}
+
+__device__ inline void load_words(const uint32_t* __restrict__ bm, int64_t w0, int64_t words,
+                                  uint32_t (&x)[kEmitWords])
+{
+#pragma unroll
+    for (int q = 0; q < kEmitWords / 4; ++q) {
+        const int64_t w = w0 + 4 * q;
+        if (w + 3 < words) {
+            const uint4 v = *reinterpret_cast<const uint4*>(bm + w);
+            x[4 * q] = v.x;
+            x[4 * q + 1] = v.y;
+            x[4 * q + 2] = v.z;
+            x[4 * q + 3] = v.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[4 * q + t] = w + t < words ? bm[w + t] : 0u;
+        }
     }
 }
 
-// one thread per bitmap word: its first output slot is the group's prefix plus
-// the bits of the group's earlier words; consecutive words write consecutive slots
-__global__ void emit_entries_kernel(const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm,
-                                    int64_t words, const int32_t* __restrict__ occ_pre,
-                                    const int32_t* __restrict__ kept_pre, const float* __restrict__ kval,
-                                    int64_t nnz, int64_t nkept, int32_t K, int32_t* __restrict__ rows,
-                                    int32_t* __restrict__ cols, float* __restrict__ vals)
+__global__ void __launch_bounds__(kEmitThreads) bm_tile_counts_kernel(const uint32_t* __restrict__ occ_bm,
+                                                                      const uint32_t* __restrict__ kept_bm,
+                                                                      int64_t words, int32_t* __restrict__ occ_sum,
+                                                                      int32_t* __restrict__ kept_sum)
 {
-    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x) {
-        uint32_t m = occ_bm[w];
-        if (!m) continue;
-        const uint32_t km = kept_bm[w];
-        const int64_t g = w / kGroupWords;
-        int64_t o = occ_pre[g];
-        int64_t i = kept_pre[g];
-        for (int64_t u = g * kGroupWords; u < w; ++u) {
-            o += __popc(occ_bm[u]);
-            i += __popc(kept_bm[u]);
+    __shared__ int32_t smem[2 * (kEmitThreads / kWave)];
+    const int64_t w0 = (int64_t)blockIdx.x * kEmitTile + (int64_t)threadIdx.x * kEmitWords;
+    uint32_t o[kEmitWords], k[kEmitWords];
+    load_words(occ_bm, w0, words, o);
+    load_words(kept_bm, w0, words, k);
+    int32_t a = 0, b = 0;
+#pragma unroll
+    for (int j = 0; j < kEmitWords; ++j) {
+        a += __popc(o[j]);
+        b += __popc(k[j]);
+    }
+    int32_t ta, tb;
+    block_exclusive2(a, b, smem, ta, tb);
+    if (threadIdx.x == 0) {
+        occ_sum[blockIdx.x] = ta;
+        kept_sum[blockIdx.x] = tb;
+    }
+}
+
+template <bool DIRECT>
+__global__ void __launch_bounds__(kEmitThreads) emit_tiles_kernel(
+    const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, int64_t words,
+    const int32_t* __restrict__ occ_sum, const int32_t* __restrict__ kept_sum, const float* __restrict__ kval,
+    int64_t nnz, int64_t nkept, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
+    float* __restrict__ vals)
+{
+    __shared__ int32_t smem[2 * (kEmitThreads / kWave)];
+    const int64_t tile = blockIdx.x;
+    int32_t po, pk;
+    if constexpr (DIRECT) {
+        int32_t a = 0, b = 0;
+        for (int64_t i = threadIdx.x; i < tile; i += kEmitThreads) {
+            a += occ_sum[i];
+            b += kept_sum[i];
         }
+        block_exclusive2(a, b, smem, po, pk);
+    } else {
+        po = occ_sum[tile];
+        pk = kept_sum[tile];
+    }
+    // the tile's words in kEmitWords sweeps of one word per thread: neighbouring
+    // threads write neighbouring entries; the block scan gives each its slot
+    int64_t run_o = po, run_k = pk;
+    for (int it = 0; it < kEmitWords; ++it) {
+        const int64_t w = tile * kEmitTile + (int64_t)it * kEmitThreads + threadIdx.x;
+        const uint32_t om = w < words ? occ_bm[w] : 0u;
+        const uint32_t km = w < words ? kept_bm[w] : 0u;
+        int32_t a = __popc(om), b = __popc(km);
+        int32_t ta, tb;
+        block_exclusive2(a, b, smem, ta, tb);
+        int64_t out = run_o + a;
+        int64_t ki = run_k + b;
+        run_o += ta;
+        run_k += tb;
+        if (!om) continue;
         const uint64_t p0 = (uint64_t)w << 5;
         int64_t r = (int64_t)(p0 / (uint64_t)K);
         int64_t c = (int64_t)(p0 - (uint64_t)r * (uint64_t)K);
         int last = 0;
-        while (m && o < nnz) {
+        uint32_t m = om;
+        while (m && out < nnz) {
             const int bit = __ffs(m) - 1;
             m &= m - 1u;
             c += bit - last;
@@ -300,10 +423,10 @@ __global__ void emit_entries_kernel(const uint32_t* __restrict__ occ_bm, const u
                 c -= K;
                 ++r;
             }
-            rows[o] = (int32_t)r;
-            cols[o] = (int32_t)c;
-            vals[o] = ((km >> bit) & 1u) && i < nkept ? kval[i++] : 0.0f;
-            ++o;
+            rows[out] = (int32_t)r;
+            cols[out] = (int32_t)c;
+            vals[out] = ((km >> bit) & 1u) && ki < nkept ? kval[ki++] : 0.0f;
+            ++out;
         }
     }
 }
@@ -318,8 +441,10 @@ struct PruneScratch {
     float* kval;        // [nnz]
     uint32_t* kept_bm;  // [words]
     uint32_t* occ_bm;   // [words]
-    int32_t* occ_cnt;   // [groups]
-    int32_t* kept_cnt;  // [groups]
+    uint32_t* con_bm;   // [words] contested cells of the current batch
+    int32_t* cflag;     // [Tm] candidate names a contested cell
+    int32_t* occ_cnt;   // [tiles] occupied bits per emit tile (then their scan)
+    int32_t* kept_cnt;  // [tiles] kept bits per emit tile
     uint64_t* cpos;     // [Tm]
     int32_t* acc;       // [Tm]
     int32_t* trank;     // [Tm]
@@ -341,7 +466,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t n = L->nnz > 0 ? L->nnz : 1;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
     const int64_t words = (int64_t)((N + 31) / 32);
-    const int64_t groups = (words + kGroupWords - 1) / kGroupWords;
+    const int64_t groups = (words + kEmitTile - 1) / kEmitTile;
     const int64_t tm = batch_cap(L);
     const int64_t H = (int64_t)1 << kHashBits;
     int64_t sn = tm > n ? tm : n;
@@ -355,9 +480,10 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     size_t o_state = take(16 * 4), o_count = take(16), o_sel = take((size_t)256 * 4);
     size_t o_a = take((size_t)n * 4), o_b = take((size_t)n * 4), o_keep = take((size_t)n * 4);
     size_t o_kval = take((size_t)n * 4);
-    size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4);
+    size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_cbm = take((size_t)words * 4);
     size_t o_oc = take((size_t)groups * 4), o_kc = take((size_t)groups * 4);
     size_t o_cpos = take((size_t)tm * 8), o_acc = take((size_t)tm * 4), o_trank = take((size_t)tm * 4);
+    size_t o_cflag = take((size_t)tm * 4);
     size_t o_tab = take((size_t)H * 8);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
@@ -371,6 +497,8 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         ps->kval = (float*)(base + o_kval);
         ps->kept_bm = (uint32_t*)(base + o_kbm);
         ps->occ_bm = (uint32_t*)(base + o_obm);
+        ps->con_bm = (uint32_t*)(base + o_cbm);
+        ps->cflag = (int32_t*)(base + o_cflag);
         ps->occ_cnt = (int32_t*)(base + o_oc);
         ps->kept_cnt = (int32_t*)(base + o_kc);
         ps->cpos = (uint64_t*)(base + o_cpos);
@@ -428,6 +556,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         SNACK_CHECK(exclusive_scan_i32(ps.keep, ps.b, nnz, nullptr, ps.scan, s));
         hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.words, 0u);
         hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.occ_bm, ps.words, 0u);
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.con_bm, ps.words, 0u);
         hipLaunchKernelGGL(kept_bits_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->rows, L->cols, L->vals,
                            nnz, L->K, ps.keep, ps.b, ps.kval, ps.kept_bm, ps.occ_bm);
         SNACK_HIP(hipGetLastError());
@@ -447,12 +576,15 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         hipLaunchKernelGGL(gen_candidates_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, L->seed, L->epoch, t0, T, N,
                            ps.occ_bm, ps.cpos);
         hipLaunchKernelGGL(hash_clear_kernel, dim3(grid_for(H)), dim3(kThreads), 0, s, ps.tab, H);
-        hipLaunchKernelGGL(hash_insert_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.tab);
-        hipLaunchKernelGGL(hash_first_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.tab, ps.acc);
+        hipLaunchKernelGGL(claim_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.occ_bm, ps.con_bm);
+        hipLaunchKernelGGL(contest_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.con_bm, ps.tab,
+                           ps.cflag);
+        hipLaunchKernelGGL(accept_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.cflag, ps.tab,
+                           ps.acc);
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(exclusive_scan_i32(ps.acc, ps.trank, T, ps.count, ps.scan, s));
-        hipLaunchKernelGGL(mark_grown_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, ps.acc, ps.trank,
-                           need, ps.occ_bm);
+        hipLaunchKernelGGL(finish_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, ps.acc, ps.trank,
+                           ps.cflag, need, ps.occ_bm, ps.con_bm);
         SNACK_HIP(hipGetLastError());
         int32_t total = 0;
         SNACK_HIP(hipMemcpyAsync(&total, ps.count, 4, hipMemcpyDeviceToHost, s));
@@ -465,14 +597,24 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     }
 
     // ---- new canonical arrays: set bits of occ in ascending position ----
-    hipLaunchKernelGGL(group_counts_kernel, dim3(grid_for(ps.groups)), dim3(kThreads), 0, s, ps.occ_bm, ps.kept_bm,
-                       ps.words, ps.groups, ps.occ_cnt, ps.kept_cnt);
-    SNACK_HIP(hipGetLastError());
-    SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, ps.groups, nullptr, ps.scan, s));
-    SNACK_CHECK(exclusive_scan_i32(ps.kept_cnt, ps.kept_cnt, ps.groups, nullptr, ps.scan, s));
-    hipLaunchKernelGGL(emit_entries_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.occ_bm, ps.kept_bm,
-                       ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows, L->cols, L->vals);
-    SNACK_HIP(hipGetLastError());
+    {
+        const int64_t nt = ps.groups;
+        hipLaunchKernelGGL(bm_tile_counts_kernel, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm,
+                           ps.words, ps.occ_cnt, ps.kept_cnt);
+        SNACK_HIP(hipGetLastError());
+        if (nt <= kEmitDirect) {
+            hipLaunchKernelGGL(emit_tiles_kernel<true>, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm,
+                               ps.kept_bm, ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows,
+                               L->cols, L->vals);
+        } else {
+            SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, nt, nullptr, ps.scan, s));
+            SNACK_CHECK(exclusive_scan_i32(ps.kept_cnt, ps.kept_cnt, nt, nullptr, ps.scan, s));
+            hipLaunchKernelGGL(emit_tiles_kernel<false>, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm,
+                               ps.kept_bm, ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows,
+                               L->cols, L->vals);
+        }
+        SNACK_HIP(hipGetLastError());
+    }
     SNACK_CHECK(canon_build_index(L, s));
     L->epoch += 1;
     return SNACK_OK;
