@@ -41,14 +41,37 @@ def fwd_bwd_bytes(nnz, M, K, B):
 
 
 def kernel_bytes(kind, nnz, M, K, B):
-    # per launch, algorithmic: the triple (12 B / entry) plus the dense operands once
+    # per launch, algorithmic: what the kernel's part of the method must move
     if kind == "spmm_forward":
+        # the triple (12 B / entry), X once, Y once
         return 12 * nnz + 4 * B * (K + M)
     if kind == "spmm_dx":
-        return 12 * nnz + 4 * B * (M + K)
-    if kind == "sddmm_dw":
-        return 12 * nnz + 4 * B * (M + K)
+        # column pass: index + value read and dW (column order) written per entry; dY, X once; dX once
+        return 12 * nnz + 4 * B * (M + 2 * K)
     raise KeyError(kind)
+
+
+TRAFFIC_FILES = {"spmm_dx (B=64)": os.path.join(ROOT, "profiles", "spmm_dx_b64_traffic.md")}
+KERNEL_SOURCE = os.path.join(ROOT, "coo_spmm_amd", "csrc", "spmm.hip")
+
+
+def measured_traffic(kernel_label):
+    """HBM bytes per launch from the committed counter summary of this kernel, or None when there is
+    none or when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = TRAFFIC_FILES.get(kernel_label)
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if "traffic_bytes_per_launch" not in fields or "source_sha256" not in fields:
+        return None
+    if hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest() != fields["source_sha256"]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def main():
@@ -60,6 +83,9 @@ def main():
     ap.add_argument("--prune-every", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="time without per-kernel HIP events")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a reference dispatch of known "
+                         "size for hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -75,6 +101,13 @@ def main():
     from snack_inputs import normal, random_layer, weight_std
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     M = K = 10000
     sparsity = 95
     nnz = M * K * (100 - sparsity) // 100
@@ -142,7 +175,7 @@ def main():
             d[name + "_us"] = round(ms * 1e3 / max(iters_per_b, 1), 3)
             if name in ("spmm_forward", "spmm_dx", "sddmm_dw", "transpose", "vals_t_refresh"):
                 tot_us += ms * 1e3 / max(iters_per_b, 1)
-            if name in ("spmm_forward", "spmm_dx", "sddmm_dw") and n > 0:
+            if name in ("spmm_forward", "spmm_dx") and n > 0:
                 if dominant is None or ms > dominant[3]:
                     dominant = (name, B, n, ms)
         d["fwd_bwd_us"] = round(tot_us, 3)
@@ -159,7 +192,7 @@ def main():
         per_launch = kernel_bytes(name, nnz, M, K, B)
         achieved = per_launch * n / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(f"{name} (B={B})"),
                     "kernel": f"{name} (B={B})", "avg_launch_us": round(ms * 1e3 / n, 3),
                     "bytes_per_launch": per_launch}
 

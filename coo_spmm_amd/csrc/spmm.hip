@@ -869,15 +869,20 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
                                  float* dX, float* dW, float* dW_t, hipStream_t s)
 {
-    ProfScope prof(KC_SPMM_DX, s);
-    // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view
+    // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view.
+    // Event classes: the column pass counts as dX, a separate canonical-order dW step as dW.
     if (dW && !dX) {
+        ProfScope prof(KC_SDDMM_DW, s);
         if (p.ntiles == 1 && use_keyed(L->fwd, L->nnz, p))
             return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
-        SNACK_CHECK(launch_keyed<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, B, s));
+        {
+            ProfScope prof(KC_SPMM_DX, s);
+            SNACK_CHECK(launch_keyed<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, B, s));
+        }
+        ProfScope prof(KC_SDDMM_DW, s);
         if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view
             return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
@@ -893,6 +898,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         }
         return SNACK_OK;
     }
+    ProfScope prof(KC_SPMM_DX, s);
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
     if (use_keyed(L->tr, L->nnz, p))
