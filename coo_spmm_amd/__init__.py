@@ -21,6 +21,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m coo_spmm_amd.build` "
                       "(or __graft_entry__.build()); there is no fallback path")
 
+# torch ships its own HIP runtime; loading it before the library makes both use
+# that one runtime instance (loaded the other way round, the library's HIP
+# calls find no device in a process where torch then initialises the GPU)
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 P = ctypes.c_void_p

@@ -97,10 +97,17 @@ struct snack_layer {
 namespace snack {
 
 // ---- error handling ------------------------------------------------------
-#define SNACK_HIP(call)                                   \
-    do {                                                  \
-        hipError_t _e = (call);                           \
-        if (_e != hipSuccess) return SNACK_ERR_HIP;       \
+// With SNACK_DEBUG set in the environment, a failing HIP call is reported on
+// stderr (expression, file, line, HIP's message) before the status returns.
+void report_hip_error(hipError_t e, const char* expr, const char* file, int line);
+
+#define SNACK_HIP(call)                                                   \
+    do {                                                                  \
+        hipError_t _e = (call);                                           \
+        if (_e != hipSuccess) {                                           \
+            ::snack::report_hip_error(_e, #call, __FILE__, __LINE__);     \
+            return SNACK_ERR_HIP;                                         \
+        }                                                                 \
     } while (0)
 
 #define SNACK_CHECK(call)                                 \

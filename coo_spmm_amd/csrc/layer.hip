@@ -5,11 +5,19 @@
 #include "internal.h"
 
 #include <limits.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 using namespace snack;
 
 namespace snack {
+
+void report_hip_error(hipError_t e, const char* expr, const char* file, int line)
+{
+    static const bool on = getenv("SNACK_DEBUG") != nullptr;
+    if (on) fprintf(stderr, "snack: %s failed at %s:%d: %s\n", expr, file, line, hipGetErrorString(e));
+}
 
 snack_status layer_alloc(snack_layer* L, void** p, size_t bytes)
 {
@@ -107,9 +115,13 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     hipStream_t s = as_stream(stream);
 
     snack_layer* L = new snack_layer();
-    if (hipGetDevice(&L->device) != hipSuccess) {
-        delete L;
-        return SNACK_ERR_HIP;
+    {
+        const hipError_t e = hipGetDevice(&L->device);
+        if (e != hipSuccess) {
+            report_hip_error(e, "hipGetDevice", __FILE__, __LINE__);
+            delete L;
+            return SNACK_ERR_HIP;
+        }
     }
     L->M = M;
     L->K = K;
@@ -129,7 +141,11 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
         snack_status _s = layer_alloc(L, &p, (bytes));                \
         if (_s != SNACK_OK) return fail(_s);                          \
         L->field = (type)p;                                           \
-        if (hipMemsetAsync(p, 0, (bytes), s) != hipSuccess) return fail(SNACK_ERR_HIP); \
+        hipError_t _e = hipMemsetAsync(p, 0, (bytes), s);             \
+        if (_e != hipSuccess) {                                       \
+            report_hip_error(_e, "hipMemsetAsync", __FILE__, __LINE__); \
+            return fail(SNACK_ERR_HIP);                               \
+        }                                                             \
     } while (0)
     ALLOC(rows, int32_t*, nb4);
     ALLOC(cols, int32_t*, nb4);
@@ -177,8 +193,14 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     snack_status st = canon_sort_input(L, rows, cols, vals, s);
     if (st != SNACK_OK) return fail(st);
     int32_t flag = 0;
-    if (hipMemcpyAsync(&flag, L->flag, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return fail(SNACK_ERR_HIP);
-    if (hipStreamSynchronize(s) != hipSuccess) return fail(SNACK_ERR_HIP);
+    {
+        hipError_t e = hipMemcpyAsync(&flag, L->flag, 4, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) {
+            report_hip_error(e, "validation flag read", __FILE__, __LINE__);
+            return fail(SNACK_ERR_HIP);
+        }
+    }
     if (flag & 1) return fail(SNACK_ERR_INDEX_RANGE);
     if (flag & 2) return fail(SNACK_ERR_DUPLICATE);
     st = canon_build_index(L, s);

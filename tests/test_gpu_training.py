@@ -71,17 +71,18 @@ def test_training_steps_teacher_forced(B):
         layer.close()
 
 
-def test_dw_row_and_column_orders_bit_identical():
-    """dW from the fused backward (canonical order) equals the transposed-order
-    copy the layer keeps, bit for bit, for every batch plan."""
+@pytest.mark.parametrize("M,K,nnz", [(1500, 1100, 80000), (1000, 800, 200000)])
+def test_dw_row_and_column_orders_bit_identical(M, K, nnz):
+    """dW from the backward (canonical order) equals the transposed-order copy
+    the layer keeps, bit for bit, for every batch plan -- on short keys (the
+    segmented kernels) and on long keys (the key-major kernels)."""
     import torch
     L = lib()
-    M, K, nnz = 1500, 1100, 80000
-    rows, cols, vals = random_layer(M, K, nnz, "dwt")
+    rows, cols, vals = random_layer(M, K, nnz, f"dwt/{M}x{K}")
     layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
     try:
         for B in (1, 2, 4, 8, 16, 32, 64):
-            X = dev(normal((B, K), f"dwt/X/{B}")); dY = dev(normal((B, M), f"dwt/dY/{B}"))
+            X = dev(normal((B, K), f"dwt/{M}x{K}/X/{B}")); dY = dev(normal((B, M), f"dwt/{M}x{K}/dY/{B}"))
             say("dwt orders B", B)
             v0 = host(layer.export()[2])
             dX, dW = layer.backward(X, dY)
