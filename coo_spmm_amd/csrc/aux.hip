@@ -111,10 +111,46 @@ __global__ void gelu_bwd_kernel(const float* __restrict__ X, const float* __rest
 
 }  // namespace
 
+// Flat variant: one thread per 4 consecutive padded batch columns of one
+// feature (bp a multiple of 4): four strided reads, one 16-byte store.  Many
+// small workgroups instead of one 64x64 tile per workgroup.
+namespace {
+__global__ void __launch_bounds__(kThreads) transpose_pad4_kernel(const float* __restrict__ src1,
+                                                                  float* __restrict__ dst1, int n1,
+                                                                  const float* __restrict__ src2,
+                                                                  float* __restrict__ dst2, int n2, int B, int bp)
+{
+    const int q = bp / 4;
+    const int64_t total1 = (int64_t)n1 * q, total = total1 + (int64_t)n2 * q;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const bool first = i < total1;
+        const int64_t j = first ? i : i - total1;
+        const float* __restrict__ src = first ? src1 : src2;
+        float* __restrict__ dst = first ? dst1 : dst2;
+        const int n = first ? n1 : n2;
+        const int c = (int)(j / q);
+        const int b = (int)(j - (int64_t)c * q) * 4;
+        float4 v;
+        v.x = b < B ? src[(int64_t)b * n + c] : 0.0f;
+        v.y = b + 1 < B ? src[(int64_t)(b + 1) * n + c] : 0.0f;
+        v.z = b + 2 < B ? src[(int64_t)(b + 2) * n + c] : 0.0f;
+        v.w = b + 3 < B ? src[(int64_t)(b + 3) * n + c] : 0.0f;
+        *reinterpret_cast<float4*>(dst + (int64_t)c * bp + b) = v;
+    }
+}
+}  // namespace
+
 snack_status transpose_pad(const float* src, float* dst, int n, const float* src2, float* dst2, int n2, int B,
                            int bp, hipStream_t s)
 {
     ProfScope prof(KC_TRANSPOSE, s);
+    if (bp % 4 == 0) {
+        const int64_t total = ((int64_t)n + (src2 ? n2 : 0)) * (bp / 4);
+        hipLaunchKernelGGL(transpose_pad4_kernel, dim3(grid_for(total)), dim3(kThreads), 0, s, src, dst, n, src2, dst2,
+                           src2 ? n2 : 0, B, bp);
+        SNACK_HIP(hipGetLastError());
+        return SNACK_OK;
+    }
     const int nx1 = (n + kTile - 1) / kTile;
     const int nx2 = src2 ? (n2 + kTile - 1) / kTile : 0;
     dim3 grid((unsigned)(nx1 + nx2), (unsigned)((bp + kTile - 1) / kTile));

@@ -663,18 +663,27 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 }
 
 // dW in canonical order from dW in transposed order: dw[k] = dwt[iperm[k]].
-// Workgroups are remapped so that XCD x walks one contiguous eighth of the
-// canonical slots (one eighth of the rows); the transposed slots those rows
-// reach are then a few lines per column, which stay in that XCD's L2.
+// XCD x owns one contiguous eighth of the canonical slots (one eighth of the
+// rows); its workgroups sweep that range together, workgroup w taking chunks
+// w, w + nw, ..., so at any moment the XCD works on a narrow window of rows and
+// the column-order lines those rows reach stay in its L2 until all their
+// entries have been read.
 __global__ void __launch_bounds__(kBlock) permute_dw_kernel(const int32_t* __restrict__ iperm,
                                                             const float* __restrict__ dwt, int64_t nnz,
-                                                            int64_t per_block, int per_xcd, float* __restrict__ dw)
+                                                            int64_t per_xcd, float* __restrict__ dw)
 {
-    const int bid = (int)blockIdx.x;
-    const int64_t vb = (int64_t)(bid % kXcd) * per_xcd + bid / kXcd;
-    const int64_t k0 = vb * per_block;
-    const int64_t k1 = k0 + per_block < nnz ? k0 + per_block : nnz;
-    for (int64_t k = k0 + threadIdx.x; k < k1; k += kBlock) dw[k] = dwt[iperm[k]];
+    const int x = (int)blockIdx.x % kXcd;
+    const int64_t w = blockIdx.x / kXcd, nw = gridDim.x / kXcd;
+    const int64_t k0 = (int64_t)x * per_xcd;
+    const int64_t k1 = k0 + per_xcd < nnz ? k0 + per_xcd : nnz;
+    for (int64_t k = k0 + w * kBlock + threadIdx.x; k < k1; k += 2 * nw * kBlock) {
+        const int64_t k2 = k + nw * kBlock;
+        const int32_t j0 = iperm[k];
+        const int32_t j1 = k2 < k1 ? iperm[k2] : j0;
+        const float v0 = dwt[j0], v1 = dwt[j1];
+        dw[k] = v0;
+        if (k2 < k1) dw[k2] = v1;
+    }
 }
 
 // dW[k] = sum_b dyt[r_k, b] * xt[c_k, b] over several batch tiles (batches
@@ -889,11 +898,11 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         }
         // wide batches: dW once, in column order, then permuted into canonical order
         if (L->nnz > 0) {
-            constexpr int64_t kPerBlock = 4 * kBlock;
-            const int64_t nblocks = (L->nnz + kPerBlock - 1) / kPerBlock;
-            const int per_xcd = (int)((nblocks + kXcd - 1) / kXcd);
-            hipLaunchKernelGGL(permute_dw_kernel, dim3((unsigned)(per_xcd * kXcd)), dim3(kBlock), 0, s, L->iperm, dW_t,
-                               L->nnz, kPerBlock, per_xcd, dW);
+            const int64_t per_xcd = (L->nnz + kXcd - 1) / kXcd;
+            int64_t nw = (per_xcd + kBlock - 1) / kBlock;
+            if (nw > 256) nw = 256;   // about eight resident workgroups per CU
+            hipLaunchKernelGGL(permute_dw_kernel, dim3((unsigned)(nw * kXcd)), dim3(kBlock), 0, s, L->iperm, dW_t,
+                               L->nnz, per_xcd, dW);
             SNACK_HIP(hipGetLastError());
         }
         return SNACK_OK;
