@@ -59,7 +59,8 @@ __device__ inline uint64_t splitmix64_output(uint64_t z)
 __device__ inline uint32_t mag_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
 // ---- drop: radix select ---------------------------------------------------
-// state: [0] prefix, [1] rank still to find among keys matching the prefix.
+// state: [0] prefix, [1] rank still to find among keys matching the prefix,
+// [2] number of keys equal to the final prefix (set by the last pass).
 // A thread adds runs of equal digits before touching LDS, which keeps the
 // first passes (where nearly every key shares a digit) free of contention;
 // each workgroup then adds its nonzero bins to the global histogram.
@@ -106,27 +107,7 @@ __global__ void __launch_bounds__(256) sel_pick_kernel(uint32_t* __restrict__ hi
         }
         state[0] |= dg << shift;
         state[1] = r;
-    }
-}
-
-__global__ void eq_flags_kernel(const float* __restrict__ vals, int64_t n, const uint32_t* __restrict__ state,
-                                int32_t* __restrict__ eq)
-{
-    const uint32_t T = state[0];
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
-        eq[k] = mag_bits(vals[k]) == T ? 1 : 0;
-}
-
-// keep[k] = 0 for the dropped entries: key < T, or key == T among the first (rank+1) ties in slot order
-__global__ void keep_flags_kernel(const float* __restrict__ vals, int64_t n, const uint32_t* __restrict__ state,
-                                  const int32_t* __restrict__ eqrank, int32_t* __restrict__ keep)
-{
-    const uint32_t T = state[0];
-    const uint32_t ties = state[1] + 1;
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t key = mag_bits(vals[k]);
-        const bool drop = key < T || (key == T && (uint32_t)eqrank[k] < ties);
-        keep[k] = drop ? 0 : 1;
+        if (shift == 0) state[2] = tot[dg];
     }
 }
 
@@ -136,36 +117,207 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
         p[i] = v;
 }
 
+// zero four bitmaps of `words` words in one launch
+__global__ void zero4_kernel(uint32_t* __restrict__ a, uint32_t* __restrict__ b, uint32_t* __restrict__ c,
+                             uint32_t* __restrict__ d, int64_t words)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x) {
+        a[i] = 0u;
+        b[i] = 0u;
+        c[i] = 0u;
+        d[i] = 0u;
+    }
+}
+
 __device__ inline uint64_t cell_of(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, int64_t k,
                                    int32_t K)
 {
     return (uint64_t)rows[k] * (uint64_t)K + (uint64_t)cols[k];
 }
 
-// Kept values in canonical order, and the kept bitmap word by word: the first
-// entry of each 32-cell word assembles the word from the entries that follow
-// it (positions ascend, so they are adjacent), hence no atomics.  Both bitmaps
-// start as the kept cells.  Bitmaps must be zero beforehand.
-__global__ void kept_bits_kernel(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols,
-                                 const float* __restrict__ vals, int64_t n, int32_t K,
-                                 const int32_t* __restrict__ keep, const int32_t* __restrict__ kidx,
-                                 float* __restrict__ kval, uint32_t* __restrict__ kept_bm,
-                                 uint32_t* __restrict__ occ_bm)
+// Tiles of 4096 canonical entries (256 threads, four rounds of four entries).
+constexpr int kKeepThreads = 256;
+constexpr int kKeepTile = 4096;
+constexpr int64_t kKeepDirect = 4096; // tiles whose tie prefix is summed directly
+
+__device__ inline bool ties_partial(const uint32_t* __restrict__ state) { return state[1] + 1u != state[2]; }
+
+__device__ inline int32_t block_excl(int32_t v, int32_t* smem /*[waves]*/, int32_t& total)
 {
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-        if (keep[k]) kval[kidx[k]] = vals[k];
-        const uint64_t p = cell_of(rows, cols, k, K);
-        const uint64_t w = p >> 5;
-        if (k > 0 && (cell_of(rows, cols, k - 1, K) >> 5) == w) continue;
-        uint32_t m = 0;
-        for (int64_t j = k; j < n; ++j) {
-            const uint64_t q = j == k ? p : cell_of(rows, cols, j, K);
-            if ((q >> 5) != w) break;
-            if (keep[j]) m |= 1u << (q & 31);
+    constexpr int W = kKeepThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) smem[w] = inc;
+    __syncthreads();
+    int32_t base = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        const int32_t x = smem[i];
+        if (i < w) base += x;
+        total += x;
+    }
+    __syncthreads();
+    return base + inc - v;
+}
+
+// Number of keys equal to T per tile; needed only when the ties are dropped in
+// part (their rank in slot order then decides), otherwise the kernel returns.
+__global__ void __launch_bounds__(kKeepThreads) eq_tiles_kernel(const float* __restrict__ vals, int64_t n,
+                                                                const uint32_t* __restrict__ state,
+                                                                int32_t* __restrict__ tile_eq)
+{
+    __shared__ int32_t smem[kKeepThreads / kWave];
+    if (!ties_partial(state)) return;
+    const uint32_t T = state[0];
+    const int64_t base = (int64_t)blockIdx.x * kKeepTile;
+    int32_t c = 0;
+    for (int i = threadIdx.x; i < kKeepTile; i += kKeepThreads) {
+        const int64_t k = base + i;
+        if (k < n && mag_bits(vals[k]) == T) ++c;
+    }
+    int32_t tot;
+    block_excl(c, smem, tot);
+    if (threadIdx.x == 0) tile_eq[blockIdx.x] = tot;
+}
+
+// The drop decision and the bitmaps, tile by tile.  An entry is dropped when
+// its key is below T, or equal to T and among the first `ties` equal keys in
+// slot order (the rank is counted only when ties are dropped in part).  The
+// tile's cells ascend, so its bits fall in one contiguous run of bitmap words:
+// when the run fits in LDS the words are assembled there and stored coalesced
+// (the first and last word, which neighbouring tiles may share, with atomic
+// ORs); otherwise every entry ORs its bits into global memory.  `old` gets
+// every entry, `kept` and `occ` the kept ones (bitmaps zero beforehand).  The
+// values are copied for the rebuild.
+constexpr int kKeepSpan = 4096;   // bitmap words assembled in LDS per tile
+
+template <bool DIRECT>
+__global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, const float* __restrict__ vals, int64_t n,
+    int32_t K, const uint32_t* __restrict__ state, const int32_t* __restrict__ tile_eq, float* __restrict__ vcopy,
+    uint32_t* __restrict__ kept_bm, uint32_t* __restrict__ occ_bm, uint32_t* __restrict__ old_bm)
+{
+    __shared__ uint32_t w_kept[kKeepSpan];
+    __shared__ uint32_t w_old[kKeepSpan];
+    __shared__ int32_t smem[kKeepThreads / kWave];
+    __shared__ uint64_t s_first, s_last;
+    const uint32_t T = state[0];
+    const uint32_t ties = state[1] + 1u;
+    const bool partial = ties_partial(state);
+    const int64_t tile = blockIdx.x;
+    const int64_t base = tile * kKeepTile;
+    const int64_t cnt = n - base < kKeepTile ? n - base : kKeepTile;
+    if (threadIdx.x == 0) {
+        s_first = cell_of(rows, cols, base, K) >> 5;
+        s_last = cell_of(rows, cols, base + cnt - 1, K) >> 5;
+    }
+    int32_t eqp = 0;
+    if (partial) {
+        if constexpr (DIRECT) {
+            int32_t part = 0;
+            for (int64_t i = threadIdx.x; i < tile; i += kKeepThreads) part += tile_eq[i];
+            block_excl(part, smem, eqp);
+        } else {
+            eqp = tile_eq[tile];
         }
-        if (m) {
-            kept_bm[w] = m;
-            occ_bm[w] = m;
+    }
+    constexpr int R = kKeepTile / (kKeepThreads * 4);
+    float v[R][4];
+    int32_t r[R][4], c[R][4];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int64_t e0 = base + q * (kKeepThreads * 4) + 4 * threadIdx.x;
+        if (e0 + 3 < n) {
+            const float4 vv = *reinterpret_cast<const float4*>(vals + e0);
+            const int4 rr = *reinterpret_cast<const int4*>(rows + e0);
+            const int4 cc = *reinterpret_cast<const int4*>(cols + e0);
+            v[q][0] = vv.x; v[q][1] = vv.y; v[q][2] = vv.z; v[q][3] = vv.w;
+            r[q][0] = rr.x; r[q][1] = rr.y; r[q][2] = rr.z; r[q][3] = rr.w;
+            c[q][0] = cc.x; c[q][1] = cc.y; c[q][2] = cc.z; c[q][3] = cc.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool in = e0 + t < n;
+                v[q][t] = in ? vals[e0 + t] : 0.0f;
+                r[q][t] = in ? rows[e0 + t] : 0;
+                c[q][t] = in ? cols[e0 + t] : 0;
+            }
+        }
+    }
+    __syncthreads();   // s_first, s_last
+    const uint64_t wf = s_first, wl = s_last;
+    const bool in_lds = wl - wf < (uint64_t)kKeepSpan;
+    if (in_lds) {
+        for (int i = threadIdx.x; i <= (int)(wl - wf); i += kKeepThreads) {
+            w_kept[i] = 0u;
+            w_old[i] = 0u;
+        }
+    }
+    __syncthreads();
+    int32_t run = 0;   // equal keys of this tile in earlier rounds
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int64_t e0 = base + q * (kKeepThreads * 4) + 4 * threadIdx.x;
+        if (e0 + 3 < n) {
+            *reinterpret_cast<float4*>(vcopy + e0) = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (e0 + t < n) vcopy[e0 + t] = v[q][t];
+        }
+        uint32_t key[4];
+        int32_t eq = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            key[t] = mag_bits(v[q][t]);
+            eq += (e0 + t < n && key[t] == T) ? 1 : 0;
+        }
+        int32_t ex = 0, tot = 0;
+        if (partial) ex = block_excl(eq, smem, tot);
+        int32_t rank = eqp + run + ex;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (e0 + t >= n) continue;
+            const bool keep = key[t] > T || (key[t] == T && partial && (uint32_t)rank >= ties);
+            if (key[t] == T) ++rank;
+            const uint64_t p = (uint64_t)r[q][t] * (uint64_t)K + (uint64_t)c[q][t];
+            const uint32_t bit = 1u << (p & 31);
+            if (in_lds) {
+                const int i = (int)((p >> 5) - wf);
+                atomicOr(&w_old[i], bit);
+                if (keep) atomicOr(&w_kept[i], bit);
+            } else {
+                atomicOr(&old_bm[p >> 5], bit);
+                if (keep) {
+                    atomicOr(&kept_bm[p >> 5], bit);
+                    atomicOr(&occ_bm[p >> 5], bit);
+                }
+            }
+        }
+        run += tot;
+    }
+    if (!in_lds) return;
+    __syncthreads();
+    const int span = (int)(wl - wf) + 1;
+    for (int i = threadIdx.x; i < span; i += kKeepThreads) {
+        const uint64_t w = wf + i;
+        const uint32_t k = w_kept[i], o = w_old[i];
+        if (i == 0 || i == span - 1) {
+            if (o) atomicOr(&old_bm[w], o);
+            if (k) {
+                atomicOr(&kept_bm[w], k);
+                atomicOr(&occ_bm[w], k);
+            }
+        } else {
+            old_bm[w] = o;
+            kept_bm[w] = k;
+            occ_bm[w] = k;
         }
     }
 }
@@ -283,135 +435,134 @@ __global__ void finish_kernel(const uint64_t* __restrict__ cpos, int64_t T, cons
 }
 
 // ---- rebuild the canonical arrays from the bitmaps ---------------------------
-// Tiles of 4096 bitmap words (256 threads x 16 consecutive words).  Kernel 1
-// counts each tile's occupied and kept bits; kernel 2 gives every thread its
-// first output slot and kept rank (the tile's prefix -- summed from the tile
-// counts before it when there are few tiles, else read from their scans --
-// plus a block scan of the thread counts) and emits its cells in order.
+// Units of 1024 bitmap words, one wavefront each (16 sweeps of one word per
+// lane).  Kernel 1 counts each unit's bits in `occ` (the new entries) and in
+// `old` (the entries before the drop).  Kernel 2 starts every unit at its
+// prefix -- summed from the unit counts before it when there are few units,
+// else read from their scans -- and, per sweep, turns the lanes' counts into
+// slots with a wavefront scan: an occupied cell goes to the next slot; a kept
+// cell takes the value the old entry at its old rank had.
 constexpr int kEmitThreads = 256;
-constexpr int kEmitWords = 16;
-constexpr int64_t kEmitTile = (int64_t)kEmitThreads * kEmitWords;
-constexpr int64_t kEmitDirect = 4096;
+constexpr int kEmitSweeps = 8;
+constexpr int64_t kEmitUnit = (int64_t)kWave * kEmitSweeps;   // words per wavefront
+constexpr int64_t kEmitDirect = 16384;
 
-__device__ inline void block_exclusive2(int32_t& a, int32_t& b, int32_t* smem /*[2 * waves]*/, int32_t& ta,
-                                        int32_t& tb)
+__device__ inline int32_t wave_incl(int32_t v)
 {
-    constexpr int W = kEmitThreads / kWave;
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    int32_t ia = a, ib = b;
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t oa = __shfl_up(ia, d, kWave), ob = __shfl_up(ib, d, kWave);
-        if (lane >= d) {
-            ia += oa;
-            ib += ob;
-        }
+        const int32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
     }
-    if (lane == kWave - 1) {
-        smem[w] = ia;
-        smem[W + w] = ib;
-    }
-    __syncthreads();
-    int32_t ba = 0, bb = 0;
-    ta = 0;
-    tb = 0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-        const int32_t xa = smem[i], xb = smem[W + i];
-        if (i < w) {
-            ba += xa;
-            bb += xb;
-        }
-        ta += xa;
-        tb += xb;
-    }
-    __syncthreads();
-    a = ba + ia - a;
-    b = bb + ib - b;
+    return v;
 }
 
-__device__ inline void load_words(const uint32_t* __restrict__ bm, int64_t w0, int64_t words,
-                                  uint32_t (&x)[kEmitWords])
+__device__ inline int32_t wave_sum(int32_t v)
 {
 #pragma unroll
-    for (int q = 0; q < kEmitWords / 4; ++q) {
-        const int64_t w = w0 + 4 * q;
-        if (w + 3 < words) {
-            const uint4 v = *reinterpret_cast<const uint4*>(bm + w);
-            x[4 * q] = v.x;
-            x[4 * q + 1] = v.y;
-            x[4 * q + 2] = v.z;
-            x[4 * q + 3] = v.w;
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) x[4 * q + t] = w + t < words ? bm[w + t] : 0u;
-        }
-    }
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
 }
 
-__global__ void __launch_bounds__(kEmitThreads) bm_tile_counts_kernel(const uint32_t* __restrict__ occ_bm,
-                                                                      const uint32_t* __restrict__ kept_bm,
-                                                                      int64_t words, int32_t* __restrict__ occ_sum,
-                                                                      int32_t* __restrict__ kept_sum)
+__global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint32_t* __restrict__ occ_bm,
+                                                                      const uint32_t* __restrict__ old_bm,
+                                                                      int64_t words, int64_t units,
+                                                                      int32_t* __restrict__ occ_cnt,
+                                                                      int32_t* __restrict__ old_cnt)
 {
-    __shared__ int32_t smem[2 * (kEmitThreads / kWave)];
-    const int64_t w0 = (int64_t)blockIdx.x * kEmitTile + (int64_t)threadIdx.x * kEmitWords;
-    uint32_t o[kEmitWords], k[kEmitWords];
-    load_words(occ_bm, w0, words, o);
-    load_words(kept_bm, w0, words, k);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
+    if (u >= units) return;
     int32_t a = 0, b = 0;
-#pragma unroll
-    for (int j = 0; j < kEmitWords; ++j) {
-        a += __popc(o[j]);
-        b += __popc(k[j]);
+    for (int it = 0; it < kEmitSweeps; ++it) {
+        const int64_t w = u * kEmitUnit + (int64_t)it * kWave + lane;
+        if (w < words) {
+            a += __popc(occ_bm[w]);
+            b += __popc(old_bm[w]);
+        }
     }
-    int32_t ta, tb;
-    block_exclusive2(a, b, smem, ta, tb);
-    if (threadIdx.x == 0) {
-        occ_sum[blockIdx.x] = ta;
-        kept_sum[blockIdx.x] = tb;
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane == 0) {
+        occ_cnt[u] = a;
+        old_cnt[u] = b;
     }
 }
 
-template <bool DIRECT>
-__global__ void __launch_bounds__(kEmitThreads) emit_tiles_kernel(
-    const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, int64_t words,
-    const int32_t* __restrict__ occ_sum, const int32_t* __restrict__ kept_sum, const float* __restrict__ kval,
-    int64_t nnz, int64_t nkept, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
+template <bool DIRECT, bool WIDE>
+__global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
+    const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, const uint32_t* __restrict__ old_bm,
+    int64_t words, int64_t units, const int32_t* __restrict__ occ_cnt, const int32_t* __restrict__ old_cnt,
+    const float* __restrict__ vold, int64_t nnz, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
     float* __restrict__ vals)
 {
-    __shared__ int32_t smem[2 * (kEmitThreads / kWave)];
-    const int64_t tile = blockIdx.x;
-    int32_t po, pk;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
+    // the workgroup's four units share one prefix: all threads sum the counts
+    // of the units before the workgroup, each wave then adds its neighbours'
+    __shared__ int32_t red[2][kEmitThreads / kWave];
+    const int64_t u0 = (int64_t)blockIdx.x * (kEmitThreads / kWave);
+    int64_t run_o, run_d;
     if constexpr (DIRECT) {
         int32_t a = 0, b = 0;
-        for (int64_t i = threadIdx.x; i < tile; i += kEmitThreads) {
-            a += occ_sum[i];
-            b += kept_sum[i];
+        for (int64_t i = threadIdx.x; i < u0; i += kEmitThreads) {
+            a += occ_cnt[i];
+            b += old_cnt[i];
         }
-        block_exclusive2(a, b, smem, po, pk);
+        a = wave_sum(a);
+        b = wave_sum(b);
+        if (lane == 0) {
+            red[0][threadIdx.x / kWave] = a;
+            red[1][threadIdx.x / kWave] = b;
+        }
+        __syncthreads();
+        run_o = 0;
+        run_d = 0;
+        for (int i = 0; i < kEmitThreads / kWave; ++i) {
+            run_o += red[0][i];
+            run_d += red[1][i];
+        }
+        for (int64_t i = u0; i < u; ++i) {
+            run_o += occ_cnt[i];
+            run_d += old_cnt[i];
+        }
     } else {
-        po = occ_sum[tile];
-        pk = kept_sum[tile];
+        run_o = u < units ? occ_cnt[u] : 0;
+        run_d = u < units ? old_cnt[u] : 0;
     }
-    // the tile's words in kEmitWords sweeps of one word per thread: neighbouring
-    // threads write neighbouring entries; the block scan gives each its slot
-    int64_t run_o = po, run_k = pk;
-    for (int it = 0; it < kEmitWords; ++it) {
-        const int64_t w = tile * kEmitTile + (int64_t)it * kEmitThreads + threadIdx.x;
-        const uint32_t om = w < words ? occ_bm[w] : 0u;
-        const uint32_t km = w < words ? kept_bm[w] : 0u;
-        int32_t a = __popc(om), b = __popc(km);
-        int32_t ta, tb;
-        block_exclusive2(a, b, smem, ta, tb);
-        int64_t out = run_o + a;
-        int64_t ki = run_k + b;
-        run_o += ta;
-        run_k += tb;
+    if (u >= units) return;
+    uint32_t om_[kEmitSweeps], dm_[kEmitSweeps], km_[kEmitSweeps];
+#pragma unroll
+    for (int it = 0; it < kEmitSweeps; ++it) {
+        const int64_t w = u * kEmitUnit + (int64_t)it * kWave + lane;
+        const bool in = w < words;
+        om_[it] = in ? occ_bm[w] : 0u;
+        dm_[it] = in ? old_bm[w] : 0u;
+        km_[it] = in ? kept_bm[w] : 0u;
+    }
+#pragma unroll
+    for (int it = 0; it < kEmitSweeps; ++it) {
+        const int64_t w = u * kEmitUnit + (int64_t)it * kWave + lane;
+        const uint32_t om = om_[it], dm = dm_[it], km = km_[it];
+        const int32_t a = __popc(om), b = __popc(dm);
+        const int32_t ia = wave_incl(a), ib = wave_incl(b);
+        int64_t out = run_o + ia - a;
+        const int64_t oldbase = run_d + ib - b;
+        run_o += __shfl(ia, kWave - 1, kWave);
+        run_d += __shfl(ib, kWave - 1, kWave);
         if (!om) continue;
-        const uint64_t p0 = (uint64_t)w << 5;
-        int64_t r = (int64_t)(p0 / (uint64_t)K);
-        int64_t c = (int64_t)(p0 - (uint64_t)r * (uint64_t)K);
+        int64_t r, c;
+        if constexpr (WIDE) {
+            const uint64_t p0 = (uint64_t)w << 5;
+            r = (int64_t)(p0 / (uint64_t)K);
+            c = (int64_t)(p0 - (uint64_t)r * (uint64_t)K);
+        } else {
+            const uint32_t p0 = (uint32_t)w << 5;
+            const uint32_t rr = p0 / (uint32_t)K;
+            r = rr;
+            c = (int64_t)(p0 - rr * (uint32_t)K);
+        }
         int last = 0;
         uint32_t m = om;
         while (m && out < nnz) {
@@ -423,9 +574,11 @@ __global__ void __launch_bounds__(kEmitThreads) emit_tiles_kernel(
                 c -= K;
                 ++r;
             }
+            float v = 0.0f;
+            if ((km >> bit) & 1u) v = vold[oldbase + __popc(dm & ((1u << bit) - 1u))];
             rows[out] = (int32_t)r;
             cols[out] = (int32_t)c;
-            vals[out] = ((km >> bit) & 1u) && ki < nkept ? kval[ki++] : 0.0f;
+            vals[out] = v;
             ++out;
         }
     }
@@ -434,23 +587,22 @@ __global__ void __launch_bounds__(kEmitThreads) emit_tiles_kernel(
 struct PruneScratch {
     uint32_t* state;    // [16]
     int32_t* count;     // [4]
-    uint32_t* selmat;   // [256] selection histogram
-    int32_t* a;         // [nnz] flags / eq
-    int32_t* b;         // [nnz] scan result
-    int32_t* keep;      // [nnz]
-    float* kval;        // [nnz]
+    uint32_t* hist;     // [256] selection histogram
+    int32_t* tile_eq;   // [keep tiles] keys equal to T per tile (then their scan)
+    float* vcopy;       // [nnz] the values before the rebuild
     uint32_t* kept_bm;  // [words]
     uint32_t* occ_bm;   // [words]
+    uint32_t* old_bm;   // [words] cells of the entries before the drop
     uint32_t* con_bm;   // [words] contested cells of the current batch
-    int32_t* cflag;     // [Tm] candidate names a contested cell
-    int32_t* occ_cnt;   // [tiles] occupied bits per emit tile (then their scan)
-    int32_t* kept_cnt;  // [tiles] kept bits per emit tile
+    int32_t* occ_cnt;   // [units] occupied bits per emit unit (then their scan)
+    int32_t* old_cnt;   // [units] old bits per emit unit
     uint64_t* cpos;     // [Tm]
     int32_t* acc;       // [Tm]
     int32_t* trank;     // [Tm]
+    int32_t* cflag;     // [Tm] candidate names a contested cell
     unsigned long long* tab;   // [2^kHashBits]
     void* scan;         // scan scratch
-    int64_t tmax, words, groups;
+    int64_t tmax, words, units, ktiles;
 };
 
 int64_t batch_cap(const snack_layer* L)
@@ -466,22 +618,23 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t n = L->nnz > 0 ? L->nnz : 1;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
     const int64_t words = (int64_t)((N + 31) / 32);
-    const int64_t groups = (words + kEmitTile - 1) / kEmitTile;
+    const int64_t units = (words + kEmitUnit - 1) / kEmitUnit;
+    const int64_t ktiles = (n + kKeepTile - 1) / kKeepTile;
     const int64_t tm = batch_cap(L);
     const int64_t H = (int64_t)1 << kHashBits;
-    int64_t sn = tm > n ? tm : n;
-    if (groups > sn) sn = groups;
+    int64_t sn = tm > units ? tm : units;
+    if (ktiles > sn) sn = ktiles;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
         off += al(bytes);
         return o;
     };
-    size_t o_state = take(16 * 4), o_count = take(16), o_sel = take((size_t)256 * 4);
-    size_t o_a = take((size_t)n * 4), o_b = take((size_t)n * 4), o_keep = take((size_t)n * 4);
-    size_t o_kval = take((size_t)n * 4);
-    size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_cbm = take((size_t)words * 4);
-    size_t o_oc = take((size_t)groups * 4), o_kc = take((size_t)groups * 4);
+    size_t o_state = take(16 * 4), o_count = take(16), o_hist = take((size_t)256 * 4);
+    size_t o_teq = take((size_t)ktiles * 4), o_vc = take((size_t)n * 4);
+    size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_dbm = take((size_t)words * 4);
+    size_t o_cbm = take((size_t)words * 4);
+    size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
     size_t o_cpos = take((size_t)tm * 8), o_acc = take((size_t)tm * 4), o_trank = take((size_t)tm * 4);
     size_t o_cflag = take((size_t)tm * 4);
     size_t o_tab = take((size_t)H * 8);
@@ -490,25 +643,25 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         char* base = (char*)L->scratch;
         ps->state = (uint32_t*)(base + o_state);
         ps->count = (int32_t*)(base + o_count);
-        ps->selmat = (uint32_t*)(base + o_sel);
-        ps->a = (int32_t*)(base + o_a);
-        ps->b = (int32_t*)(base + o_b);
-        ps->keep = (int32_t*)(base + o_keep);
-        ps->kval = (float*)(base + o_kval);
+        ps->hist = (uint32_t*)(base + o_hist);
+        ps->tile_eq = (int32_t*)(base + o_teq);
+        ps->vcopy = (float*)(base + o_vc);
         ps->kept_bm = (uint32_t*)(base + o_kbm);
         ps->occ_bm = (uint32_t*)(base + o_obm);
+        ps->old_bm = (uint32_t*)(base + o_dbm);
         ps->con_bm = (uint32_t*)(base + o_cbm);
-        ps->cflag = (int32_t*)(base + o_cflag);
         ps->occ_cnt = (int32_t*)(base + o_oc);
-        ps->kept_cnt = (int32_t*)(base + o_kc);
+        ps->old_cnt = (int32_t*)(base + o_dc);
         ps->cpos = (uint64_t*)(base + o_cpos);
         ps->acc = (int32_t*)(base + o_acc);
         ps->trank = (int32_t*)(base + o_trank);
+        ps->cflag = (int32_t*)(base + o_cflag);
         ps->tab = (unsigned long long*)(base + o_tab);
         ps->scan = base + o_scan;
         ps->tmax = tm;
         ps->words = words;
-        ps->groups = groups;
+        ps->units = units;
+        ps->ktiles = ktiles;
     }
     return off + 256;
 }
@@ -538,27 +691,33 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
 
     // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
     {
-        uint32_t init[2] = {0u, (uint32_t)(n_drop - 1)};
+        const uint32_t init[3] = {0u, (uint32_t)(n_drop - 1), 0u};
         SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
         int nblk = (int)grid_for(nnz);
         if (nblk > kSelBlocks) nblk = kSelBlocks;
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.selmat, (int64_t)256, 0u);
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.hist, (int64_t)256, 0u);
         for (int shift = 24; shift >= 0; shift -= 8) {
             hipLaunchKernelGGL(sel_hist_kernel, dim3(nblk), dim3(kThreads), 0, s, L->vals, nnz, ps.state, shift,
-                               ps.selmat);
-            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(256), 0, s, ps.selmat, ps.state, shift);
+                               ps.hist);
+            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(256), 0, s, ps.hist, ps.state, shift);
         }
         SNACK_HIP(hipGetLastError());
-        hipLaunchKernelGGL(eq_flags_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->vals, nnz, ps.state, ps.a);
-        SNACK_CHECK(exclusive_scan_i32(ps.a, ps.b, nnz, nullptr, ps.scan, s));
-        hipLaunchKernelGGL(keep_flags_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->vals, nnz, ps.state, ps.b,
-                           ps.keep);
-        SNACK_CHECK(exclusive_scan_i32(ps.keep, ps.b, nnz, nullptr, ps.scan, s));
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.words, 0u);
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.occ_bm, ps.words, 0u);
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.con_bm, ps.words, 0u);
-        hipLaunchKernelGGL(kept_bits_kernel, dim3(grid_for(nnz)), dim3(kThreads), 0, s, L->rows, L->cols, L->vals,
-                           nnz, L->K, ps.keep, ps.b, ps.kval, ps.kept_bm, ps.occ_bm);
+        hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->vals, nnz,
+                           ps.state, ps.tile_eq);
+        hipLaunchKernelGGL(zero4_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.occ_bm,
+                           ps.old_bm, ps.con_bm, ps.words);
+        SNACK_HIP(hipGetLastError());
+        if (ps.ktiles <= kKeepDirect) {
+            hipLaunchKernelGGL(keep_tiles_kernel<true>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
+                               L->cols, L->vals, nnz, L->K, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm, ps.occ_bm,
+                               ps.old_bm);
+        } else {
+            // a scan of zeros when every tie is dropped (the counts were not written then; they are not used)
+            SNACK_CHECK(exclusive_scan_i32(ps.tile_eq, ps.tile_eq, ps.ktiles, nullptr, ps.scan, s));
+            hipLaunchKernelGGL(keep_tiles_kernel<false>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
+                               L->cols, L->vals, nnz, L->K, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm, ps.occ_bm,
+                               ps.old_bm);
+        }
         SNACK_HIP(hipGetLastError());
     }
 
@@ -598,20 +757,27 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
 
     // ---- new canonical arrays: set bits of occ in ascending position ----
     {
-        const int64_t nt = ps.groups;
-        hipLaunchKernelGGL(bm_tile_counts_kernel, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm,
-                           ps.words, ps.occ_cnt, ps.kept_cnt);
+        const int64_t nu = ps.units;
+        const unsigned grid = (unsigned)((nu + (kEmitThreads / kWave) - 1) / (kEmitThreads / kWave));
+        hipLaunchKernelGGL(bm_unit_counts_kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.old_bm, ps.words,
+                           nu, ps.occ_cnt, ps.old_cnt);
         SNACK_HIP(hipGetLastError());
-        if (nt <= kEmitDirect) {
-            hipLaunchKernelGGL(emit_tiles_kernel<true>, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm,
-                               ps.kept_bm, ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows,
-                               L->cols, L->vals);
+        const bool direct = nu <= kEmitDirect;
+        if (!direct) {
+            SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, nu, nullptr, ps.scan, s));
+            SNACK_CHECK(exclusive_scan_i32(ps.old_cnt, ps.old_cnt, nu, nullptr, ps.scan, s));
+        }
+        const bool wide = N > 0xFFFFFFFFull;
+        auto emit = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm, ps.old_bm,
+                               ps.words, nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals);
+        };
+        if (direct) {
+            if (wide) emit(emit_units_kernel<true, true>);
+            else emit(emit_units_kernel<true, false>);
         } else {
-            SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, nt, nullptr, ps.scan, s));
-            SNACK_CHECK(exclusive_scan_i32(ps.kept_cnt, ps.kept_cnt, nt, nullptr, ps.scan, s));
-            hipLaunchKernelGGL(emit_tiles_kernel<false>, dim3((unsigned)nt), dim3(kEmitThreads), 0, s, ps.occ_bm,
-                               ps.kept_bm, ps.words, ps.occ_cnt, ps.kept_cnt, ps.kval, nnz, kept, L->K, L->rows,
-                               L->cols, L->vals);
+            if (wide) emit(emit_units_kernel<false, true>);
+            else emit(emit_units_kernel<false, false>);
         }
         SNACK_HIP(hipGetLastError());
     }
