@@ -55,6 +55,8 @@ struct Scratch {
 
 struct snack_layer {
     int device = 0;
+    int lds_bytes = 0;   // LDS a workgroup may allocate on that device
+    int cus = 0;         // compute units of that device
     int32_t M = 0, K = 0;
     int64_t nnz = 0;
     int64_t cap = 0;          // element capacity of each nnz-sized array (>= nnz + kPad)

@@ -123,6 +123,18 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
             return SNACK_ERR_HIP;
         }
     }
+    {
+        int lds = 0, cus = 0;
+        const hipError_t e1 = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, L->device);
+        const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+            report_hip_error(e1 != hipSuccess ? e1 : e2, "hipDeviceGetAttribute", __FILE__, __LINE__);
+            delete L;
+            return SNACK_ERR_HIP;
+        }
+        L->lds_bytes = lds;
+        L->cus = cus;
+    }
     L->M = M;
     L->K = K;
     L->nnz = nnz;

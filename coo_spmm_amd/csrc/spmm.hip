@@ -528,33 +528,151 @@ __global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs 
 
 // Key-major variant for views whose keys hold many entries (rows or columns
 // of hundreds of entries at the densities of interest).  The wave walks its
-// chunk key by key; group g takes the key's entries g, g+G, g+2G, ..., U of
-// them in flight, and accumulates its batch columns in registers; at the
-// key's end the group sums are added across groups by a fixed xor-shuffle
-// tree and written once.  With DW each entry's dot product over the batch
-// tile is reduced over the group's lanes (fixed tree) and stored.  Indices
-// are read with clamped, unconditional loads so every load stays in flight.
-template <int BT, int NB, int U, bool DW, bool SPMM = true>
-__global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
+// keys in order; group g takes a key's entries g, g+G, g+2G, ..., U of them
+// in flight, and accumulates its batch columns in registers; at the key's end
+// the group sums are added across groups by a fixed xor-shuffle tree and
+// written once.  With DW each entry's dot product over the batch tile is
+// reduced over the group's lanes (fixed tree) and stored.  Indices are read
+// with clamped, unconditional loads so every load stays in flight.  A key's
+// blocks always start at its first entry, so a key's sums do not depend on
+// which kernel or wave walked it.
+template <int BT, int NB, int U>
+struct KeyBlock {
+    static constexpr int G = kWave / BT;
+    static constexpr int STEP = G * U;
+    // with STEP <= 64 lane l loads entry base + l and groups pick theirs by
+    // shuffles; with wider steps each lane loads its own U entries
+    static constexpr bool SHUF = STEP <= kWave;
+    static constexpr int NL = SHUF ? 1 : U;
+    int32_t nidx[NL];
+    float nval[NL];
+
+    // indices and values of the block at base (entries >= lim clamped)
+    template <bool SPMM>
+    __device__ inline void load(const int32_t* __restrict__ idx, const float* __restrict__ vals, int32_t base,
+                                int32_t lim, int lane, int g)
+    {
+        const int32_t top = lim > 0 ? lim - 1 : 0;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) {
+            const int32_t k = SHUF ? base + lane : base + q * G + g;
+            const int32_t kc = k < lim ? k : top;
+            nidx[q] = idx[kc];
+            nval[q] = SPMM ? vals[kc] : 0.0f;
+        }
+    }
+    // this lane's U entries of the loaded block
+    __device__ inline void take(int32_t (&ii)[U], float (&vv)[U], int g) const
+    {
+        if constexpr (SHUF) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ii[u] = __shfl(nidx[0], u * G + g, kWave);
+                vv[u] = __shfl(nval[0], u * G + g, kWave);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ii[u] = nidx[u];
+                vv[u] = nval[u];
+            }
+        }
+    }
+};
+
+template <int NB, int U>
+__device__ inline void key_gather(const float* __restrict__ Gm, const int32_t (&ii)[U], int bp, int bcol,
+                                  float (&y)[U][NB])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_nb<NB>(Gm + (int64_t)ii[u] * bp + bcol, y[u]);
+}
+
+template <int BT, int NB, int U>
+__device__ inline void key_accumulate(const float (&vv)[U], const float (&y)[U][NB], int32_t base, int32_t p1, int g,
+                                      float (&acc)[NB])
 {
     constexpr int G = kWave / BT;
-    constexpr int STEP = G * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int32_t k = base + u * G + g;
+        const float v = k < p1 ? vv[u] : 0.0f;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[u][n], acc[n]);
+    }
+}
+
+// entries' dot products with h, four at a time reduced over the group
+// together, stored; an entry's result does not depend on U or on its place
+// among the four
+template <int BT, int NB, int U>
+__device__ inline void key_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t p1, int g, int bl,
+                              float* __restrict__ dwo)
+{
+    static_assert(U % 4 == 0, "dW reduces four entries at a time");
+    constexpr int G = kWave / BT;
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q) {
+        const int32_t qb = base + 4 * q * G;
+        float d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float a = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) a = fmaf(y[4 * q + u][n], h[n], a);
+            d[u] = a;
+        }
+        reduce4_group<BT>(d, bl);
+        if constexpr (BT == 1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int32_t k = qb + u * G + g;
+                if (k < p1) dwo[k] = d[u];
+            }
+        } else if constexpr (BT == 2) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int32_t k = qb + (2 * bl + t) * G + g;
+                if (k < p1) dwo[k] = d[t];
+            }
+        } else {
+            constexpr int STRIDE = BT / 4;
+            if ((bl % STRIDE) == 0) {
+                const int32_t k = qb + ((bl / STRIDE) & 3) * G + g;
+                if (k < p1) dwo[k] = d[0];
+            }
+        }
+    }
+}
+
+// group sums of a key added across groups, written once by group 0
+template <int BT, int NB>
+__device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int nkeys, int32_t r, float* __restrict__ out)
+{
+#pragma unroll
+    for (int m = BT; m < kWave; m <<= 1)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] += __shfl_xor(acc[n], m, kWave);
+    if (g == 0) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int b = bcol + n;
+            if (b < B) out[(int64_t)b * nkeys + r] = acc[n];
+        }
+    }
+}
+
+// One chunk's keys; the first block of every key is loaded at the key's start.
+template <int BT, int NB, int U, bool DW, bool SPMM>
+__device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float* __restrict__ Gm, int bp, int B)
+{
+    using KB = KeyBlock<BT, NB, U>;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = (int)(threadIdx.x / kWave);
     const int g = lane / BT;
     const int bl = lane - g * BT;
-    const int bid = (int)blockIdx.x;
-    const int vb = (bid % kXcd) * A.per_xcd + bid / kXcd;
-    if (vb >= A.nblocks) return;
-    const int c = vb * kWavesPerBlock + wv;
-    if (c >= A.nchunks) return;
     const int2 d0 = A.desc[c];
     const int2 d1 = A.desc[c + 1];
     const int bcol = (int)blockIdx.y * (BT * NB) + bl * NB;
-    const int32_t* __restrict__ idx = A.idx;
-    const float* __restrict__ vals = A.vals;
-    const float* __restrict__ Gm = A.G;
-    const int nkeys = A.nkeys;
     int32_t p1 = d0.y;
     for (int32_t r = d0.x; r < d1.x; ++r) {
         const int32_t p0 = p1;
@@ -564,102 +682,228 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
         for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
         float h[NB];
         if constexpr (DW) load_nb<NB>(A.H + (int64_t)r * bp + bcol, h);
-        // Blocks of STEP entries; the indices and values of the next block are
-        // loaded while the current one is gathered.  With STEP <= 64 lane l
-        // loads entry base + l and groups pick theirs by shuffles; with wider
-        // steps (one lane per group) each lane loads its own U entries.
-        static_assert(!DW || U == 4, "dW reduces four entries at a time");
-        constexpr bool SHUF = STEP <= kWave;
-        constexpr int NL = SHUF ? 1 : U;
-        int32_t nidx_l[NL];
-        float nval_l[NL];
-        auto load_next = [&](int32_t base) {
-#pragma unroll
-            for (int q = 0; q < NL; ++q) {
-                const int32_t k = SHUF ? base + lane : base + q * G + g;
-                const int32_t kc = k < p1 ? k : p1 - 1;
-                nidx_l[q] = idx[kc];
-                nval_l[q] = SPMM ? vals[kc] : 0.0f;
-            }
-        };
-        if (p0 < p1) load_next(p0);
-        for (int32_t base = p0; base < p1; base += STEP) {
+        KB blk;
+        if (p0 < p1) blk.template load<SPMM>(A.idx, A.vals, p0, p1, lane, g);
+        for (int32_t base = p0; base < p1; base += KB::STEP) {
             int32_t ii[U];
             float vv[U];
-            if constexpr (SHUF) {
-                const int32_t ci = nidx_l[0];
-                const float cv = nval_l[0];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    ii[u] = __shfl(ci, u * G + g, kWave);
-                    vv[u] = __shfl(cv, u * G + g, kWave);
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    ii[u] = nidx_l[u];
-                    vv[u] = nval_l[u];
-                }
-            }
+            blk.take(ii, vv, g);
             float y[U][NB];
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_nb<NB>(Gm + (int64_t)ii[u] * bp + bcol, y[u]);
-            load_next(base + STEP);
-            if constexpr (SPMM) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int32_t k = base + u * G + g;
-                    const float v = k < p1 ? vv[u] : 0.0f;
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[u][n], acc[n]);
-                }
-            }
-            if constexpr (DW) {
-                // four entries' dot products reduced over the group together
-                float d[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) a = fmaf(y[u][n], h[n], a);
-                    d[u] = a;
-                }
-                reduce4_group<BT>(d, bl);
-                if constexpr (BT == 1) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int32_t k = base + u * G + g;
-                        if (k < p1) A.dwo[k] = d[u];
-                    }
-                } else if constexpr (BT == 2) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int32_t k = base + (2 * bl + t) * G + g;
-                        if (k < p1) A.dwo[k] = d[t];
-                    }
-                } else {
-                    constexpr int STRIDE = BT / 4;
-                    if ((bl % STRIDE) == 0) {
-                        const int32_t k = base + ((bl / STRIDE) & 3) * G + g;
-                        if (k < p1) A.dwo[k] = d[0];
-                    }
-                }
-            }
+            key_gather<NB, U>(Gm, ii, bp, bcol, y);
+            blk.template load<SPMM>(A.idx, A.vals, base + KB::STEP, p1, lane, g);
+            if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
+            if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo);
         }
-        if constexpr (SPMM) {
-#pragma unroll
-            for (int m = BT; m < kWave; m <<= 1)
-#pragma unroll
-                for (int n = 0; n < NB; ++n) acc[n] += __shfl_xor(acc[n], m, kWave);
-            if (g == 0) {
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    const int b = bcol + n;
-                    if (b < B) A.out[(int64_t)b * nkeys + r] = acc[n];
-                }
+        if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out);
+    }
+}
+
+__device__ inline int32_t uni(int32_t v) { return (int32_t)__builtin_amdgcn_readfirstlane(v); }
+
+// Wave-uniform cursor over the keys of the chunks a wave claims from its
+// workgroup's LDS counter.  It holds the current key (r, entries [p0, p1)) and
+// the next one (nr, [np0, np1); nr < 0: none), and the descriptor of the
+// claimed chunk after the next key's.  A chunk whose first key equals the next
+// chunk's (inside a key longer than a chunk) holds no key and is skipped.
+struct KeyCursor {
+    const int32_t* ptr;
+    const int2* desc;
+    int* next_s;
+    int32_t nkeys, cend;
+    int32_t cn, pa_x, pa_y, pb_x;
+    int32_t r, ke, p0, p1;
+    int32_t nr, nke, np0, np1;
+
+    __device__ inline int32_t claim() const
+    {
+        int c = 0;
+        if ((threadIdx.x & (kWave - 1)) == 0) c = atomicAdd(next_s, 1);
+        return uni(c);
+    }
+    __device__ inline int32_t ptr_at(int32_t i) const
+    {
+        return uni(ptr[uni(i < 0 ? 0 : (i < nkeys ? i : nkeys))]);
+    }
+    __device__ inline void load_desc()
+    {
+        const int32_t cc = uni(cn < cend ? cn : cend - 1);
+        pa_x = uni(desc[cc].x);
+        pa_y = uni(desc[cc].y);
+        pb_x = uni(desc[cc + 1].x);
+    }
+    // the first key of the next non-empty claimed chunk into (nr, np0, nke)
+    __device__ inline void pull()
+    {
+        for (;;) {
+            if (uni(cn) >= cend) {
+                nr = -1;
+                return;
+            }
+            const int32_t ax = pa_x, ay = pa_y, bx = pb_x;
+            cn = claim();
+            load_desc();
+            if (uni(ax) < uni(bx)) {
+                nr = uni(ax);
+                np0 = uni(ay);
+                nke = uni(bx);
+                return;
             }
         }
     }
+    __device__ inline void set_next()
+    {
+        if (uni(r + 1) < uni(ke)) {
+            nr = uni(r + 1);
+            np0 = uni(p1);
+            nke = uni(ke);
+        } else {
+            pull();
+        }
+        np1 = ptr_at(nr + 1);
+    }
+    // false when the wave has no key at all (the current key is then the
+    // empty key 0, so loads for it stay in bounds)
+    __device__ inline bool start()
+    {
+        r = 0;
+        ke = 0;
+        p0 = 0;
+        p1 = 0;
+        nr = -1;
+        cn = claim();
+        if (uni(cn) >= cend) return false;
+        load_desc();
+        pull();
+        if (uni(nr) < 0) return false;
+        r = nr;
+        ke = nke;
+        p0 = np0;
+        p1 = ptr_at(nr + 1);
+        set_next();
+        return true;
+    }
+    // false when the current key was the last
+    __device__ inline bool advance()
+    {
+        if (uni(nr) < 0) return false;
+        r = uni(nr);
+        ke = uni(nke);
+        p0 = uni(np0);
+        p1 = uni(np1);
+        set_next();
+        return true;
+    }
+};
+
+// The keys of every chunk a wave claims, walked as one stream: while a key's
+// last block is processed, the next key's first block (possibly in the next
+// claimed chunk) and its dW operand are already in flight.  Key bookkeeping is
+// wave-uniform and kept in scalar registers, so its loads go through the
+// scalar cache and never make the vector loads in flight wait.  `stage` runs
+// on every thread once the first block is in flight (it may hold a barrier).
+template <int BT, int NB, int U, bool DW, bool SPMM, class Stage>
+__device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int cend, const float* __restrict__ Gm,
+                                           int bp, int B, Stage&& stage)
+{
+    using KB = KeyBlock<BT, NB, U>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane / BT;
+    const int bl = lane - g * BT;
+    const int bcol = bl * NB;
+    KeyCursor kc;
+    kc.ptr = A.ptr;
+    kc.desc = A.desc;
+    kc.next_s = next_s;
+    kc.nkeys = A.nkeys;
+    kc.cend = cend;
+    const bool any = kc.start();
+    float acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+    // the block in flight and the dW operand of its key
+    KB blk;
+    float h[NB], hn[NB];
+    blk.template load<SPMM>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
+    if constexpr (DW) load_nb<NB>(A.H + (int64_t)kc.r * bp + bcol, hn);
+    stage();
+    if (!any) return;
+    int32_t base = kc.p0;
+    for (;;) {
+        int32_t ii[U];
+        float vv[U];
+        blk.take(ii, vv, g);
+        if constexpr (DW) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) h[n] = hn[n];
+        }
+        const int32_t p1 = kc.p1;
+        const bool last = uni(base + KB::STEP >= p1 ? 1 : 0) != 0;
+        const int32_t nbase = last ? kc.np0 : base + KB::STEP;
+        const int32_t nlim = last ? kc.np1 : p1;
+        const int32_t nkey = last ? (kc.nr < 0 ? kc.r : kc.nr) : kc.r;
+        if constexpr (DW) load_nb<NB>(A.H + (int64_t)nkey * bp + bcol, hn);
+        blk.template load<SPMM>(A.idx, A.vals, nbase, nlim, lane, g);
+        float y[U][NB];
+        key_gather<NB, U>(Gm, ii, bp, bcol, y);
+        if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
+        if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo);
+        if (!last) {
+            base += KB::STEP;
+            continue;
+        }
+        if constexpr (SPMM) {
+            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out);
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+        }
+        if (!kc.advance()) break;
+        base = kc.p0;
+    }
+}
+
+template <int BT, int NB, int U, bool DW, bool SPMM = true>
+__global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
+{
+    const int bid = (int)blockIdx.x;
+    const int vb = (bid % kXcd) * A.per_xcd + bid / kXcd;
+    if (vb >= A.nblocks) return;
+    const int c = vb * kWavesPerBlock + (int)(threadIdx.x / kWave);
+    if (c >= A.nchunks) return;
+    key_chunk<BT, NB, U, DW, SPMM>(A, c, A.G, bp, B);
+}
+
+// The same walk with the gathered operand [nidx, bp] staged in LDS: gathers
+// become LDS reads, which random indices serve far faster than the vector
+// cache, whose lines the streamed index evicts.  Staging costs one copy of the
+// operand per workgroup, so workgroups are persistent: workgroup i takes an
+// even, contiguous share of the chunks (shares of one XCD adjacent) and its
+// wavefronts stream the keys of the chunks they claim from an LDS counter.
+constexpr int kLdsKeyWaves = 16;
+constexpr int kLdsU = 4;   // entries per lane per step
+
+template <int BT, int NB, int U, bool DW, bool SPMM = true>
+__global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs A, int bp, int B)
+{
+    extern __shared__ float gs_dyn[];
+    __shared__ int next_s;
+    const int nwg = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    const int per = nwg / kXcd;   // the grid is a multiple of kXcd
+    const int vb = (bid % kXcd) * per + bid / kXcd;
+    const int c0 = (int)(((int64_t)A.nchunks * vb) / nwg);
+    const int c1 = (int)(((int64_t)A.nchunks * (vb + 1)) / nwg);
+    if (threadIdx.x == 0) next_s = c0;
+    __syncthreads();
+    // the operand is staged while every wave's first block is in flight
+    auto stage = [&]() {
+        const int64_t n = (int64_t)A.nidx * bp;
+        const int64_t n4 = ((reinterpret_cast<uintptr_t>(A.G) & 15) == 0) ? n / 4 : 0;
+        for (int64_t i = threadIdx.x; i < n4; i += kLdsKeyWaves * kWave)
+            reinterpret_cast<float4*>(gs_dyn)[i] = reinterpret_cast<const float4*>(A.G)[i];
+        for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += kLdsKeyWaves * kWave) gs_dyn[i] = A.G[i];
+        __syncthreads();
+    };
+    key_stream<BT, NB, U, DW, SPMM>(A, &next_s, c1, gs_dyn, bp, B, stage);
 }
 
 // dW in canonical order from dW in transposed order: dw[k] = dwt[iperm[k]].
@@ -827,10 +1071,27 @@ inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
 }
 
 template <bool DW, bool SPMM = true>
-snack_status launch_keyed(const BatchPlan& p, int64_t cap, const View& v, const float* G, const float* H, float* out,
-                          float* dwo, int B, hipStream_t s)
+snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
+                          float* out, float* dwo, int B, hipStream_t s)
 {
-    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, cap);
+    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    const size_t lds = (size_t)v.nidx * p.bp * sizeof(float);
+    if (p.btile <= 4 && p.ntiles == 1 && lds <= (size_t)L->lds_bytes && L->cus > 0 && v.nchunks > 0) {
+        // operand resident in LDS: one or two persistent workgroups per CU
+        int nwg = L->cus * (2 * lds <= (size_t)L->lds_bytes ? 2 : 1);
+        const int want = (v.nchunks + 1) / 2;
+        if (nwg > want) nwg = want;
+        nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+        const dim3 grid((unsigned)nwg), block(kLdsKeyWaves * kWave);
+        switch (p.btile) {
+        case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+        case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+        case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+        default: return SNACK_ERR_INVALID_ARG;
+        }
+        SNACK_HIP(hipGetLastError());
+        return SNACK_OK;
+    }
     dim3 grid((unsigned)(a.per_xcd * kXcd), (unsigned)p.ntiles);
     switch (p.btile) {
     case 1: hipLaunchKernelGGL((key_kernel<1, 1, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
@@ -870,7 +1131,7 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 {
     ProfScope prof(KC_SPMM_FWD, s);
     if (use_keyed(L->fwd, L->nnz, p))
-        return launch_keyed<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, B, s);
+        return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
                                B, s);
 }
@@ -883,18 +1144,18 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (dW && !dX) {
         ProfScope prof(KC_SDDMM_DW, s);
         if (p.ntiles == 1 && use_keyed(L->fwd, L->nnz, p))
-            return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
+            return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         {
             ProfScope prof(KC_SPMM_DX, s);
-            SNACK_CHECK(launch_keyed<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, B, s));
+            SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s));
         }
         ProfScope prof(KC_SDDMM_DW, s);
         if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view
-            return launch_keyed<true, false>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, B, s);
+            return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
         }
         // wide batches: dW once, in column order, then permuted into canonical order
         if (L->nnz > 0) {
@@ -911,7 +1172,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
     if (use_keyed(L->tr, L->nnz, p))
-        return launch_keyed<false>(p, L->cap, L->tr, dyt, xt, dX, nullptr, B, s);
+        return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
 }
 

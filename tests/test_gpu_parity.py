@@ -18,10 +18,10 @@ def _make(M, K, nnz, key, std=None):
     return rows, cols, vals
 
 
-def _check_layer_vs_oracle(M, K, nnz, batches, key, std=None, check_index=True):
+def _check_layer_vs_oracle(M, K, nnz, batches, key, std=None, check_index=True, triple=None):
     import torch
     L = lib()
-    rows, cols, vals = _make(M, K, nnz, key, std)
+    rows, cols, vals = triple if triple is not None else _make(M, K, nnz, key, std)
     ref = oracle.canonicalize(M, K, rows, cols, vals)
     say("create", key, M, K, nnz)
     layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
@@ -65,6 +65,30 @@ def test_long_keys_wide_batches(M, K, nnz):
     # hundreds of entries per row and per column: the key-major kernels and the
     # column-order dW permuted into canonical order
     _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_keyed_keys_longer_than_chunks(transpose):
+    # keys of ~1400 entries (several chunks each, so chunks that start inside a
+    # key hold no key of their own) and one empty key, on the key-major path;
+    # transposed, the same structure reaches the column view
+    n, L_ = 8, 3000
+    rng = np.random.default_rng(11)
+    r, c = [], []
+    for key in range(n):
+        if key == 3:
+            continue
+        idx = np.sort(rng.choice(L_, 1400, replace=False))
+        r.append(np.full(idx.shape[0], key)); c.append(idx)
+    r = np.concatenate(r).astype(np.int32); c = np.concatenate(c).astype(np.int32)
+    perm = rng.permutation(r.shape[0])
+    r, c = r[perm], c[perm]
+    v = rng.standard_normal(r.shape[0]).astype(np.float32)
+    M, K = (n, L_) if not transpose else (L_, n)
+    if transpose:
+        r, c = c, r
+    _check_layer_vs_oracle(M, K, r.shape[0], (1, 2, 3, 4, 5, 8, 16, 64), f"gpu/keyedlong/{int(transpose)}",
+                           triple=(r, c, v))
 
 
 @pytest.mark.parametrize("M,K,nnz", [(130, 70, 2000), (1000, 800, 200000)])

@@ -71,11 +71,12 @@ def test_training_steps_teacher_forced(B):
         layer.close()
 
 
-@pytest.mark.parametrize("M,K,nnz", [(1500, 1100, 80000), (1000, 800, 200000)])
+@pytest.mark.parametrize("M,K,nnz", [(1500, 1100, 80000), (1000, 800, 200000), (12000, 300, 1800000)])
 def test_dw_row_and_column_orders_bit_identical(M, K, nnz):
     """dW from the backward (canonical order) equals the transposed-order copy
     the layer keeps, bit for bit, for every batch plan -- on short keys (the
-    segmented kernels) and on long keys (the key-major kernels)."""
+    segmented kernels), on long keys (the key-major kernels), and where one
+    view's gathered operand fits in LDS and the other's does not."""
     import torch
     L = lib()
     rows, cols, vals = random_layer(M, K, nnz, f"dwt/{M}x{K}")
