@@ -437,6 +437,10 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
         }
     }
     L->vals_t_stale = false;
+    for (int i = 0; i < kTileWidths; ++i) {
+        L->fwd.split[i].valid = false;
+        L->tr.split[i].valid = false;
+    }
     SNACK_CHECK(build_view_partitions(L, s));
     return SNACK_OK;
 }

@@ -31,6 +31,17 @@ enum KernelClass : int {
     KC_COUNT
 };
 
+// For the slice-tiled kernels: the gathered operand's rows split into S
+// slices that each fit in LDS; tab[s * nkeys + r] is the first entry of key r
+// whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
+// change of the index.
+constexpr int kTileWidths = 3;   // batch tiles 16, 32, 64
+struct SplitTab {
+    int32_t S = 0;
+    int32_t* tab = nullptr;
+    mutable bool valid = false;
+};
+
 // One sorted view of the triple: keys ascending (rows for the canonical view,
 // cols for the transposed one), the gathered index, the values, the key
 // pointer [nkeys+1] and the work partition into key-aligned chunks.
@@ -44,6 +55,7 @@ struct View {
     int2* desc = nullptr;           // [nchunks + 1]: (first key, first entry) of each chunk
     int32_t* empty_keys = nullptr;  // [nkeys]: keys with no entry, ascending
     int32_t* n_empty = nullptr;     // device count of empty_keys
+    SplitTab split[kTileWidths];
 };
 
 struct Scratch {
@@ -195,6 +207,14 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 // Requires a single batch tile when dW or dW_t is requested.
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
                                  float* dX, float* dW, float* dW_t, hipStream_t s);
+
+// slice-tiled SpMM support: slices of view v for a batch tile (0 = not used),
+// the split tables' allocation (at create) and the workspace the partial sums
+// need for a batch plan
+int tile_splits(const snack_layer* L, const View& v, int btile);
+snack_status alloc_split_tables(snack_layer* L);
+size_t tile_part_bytes(const snack_layer* L, const BatchPlan& p);
+float* ws_part(const snack_layer* L, const BatchPlan& p);   // layer.hip
 
 // dW for batches wider than one tile (loops over the tiles)
 snack_status sddmm_dw_tiles(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,

@@ -53,7 +53,7 @@ size_t ws_need(const snack_layer* L, const BatchPlan& p)
 {
     const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
     const size_t b = (((size_t)L->M * p.bp * 4) + 255) & ~(size_t)255;
-    return a + b;
+    return a + b + tile_part_bytes(L, p);
 }
 
 snack_status ensure_ws(snack_layer* L, const BatchPlan& p)
@@ -79,6 +79,19 @@ snack_status ensure_ws(snack_layer* L, const BatchPlan& p)
 }
 
 float* ws_x(snack_layer* L) { return L->ws; }
+
+}  // namespace
+
+// partial sums of the slice-tiled kernels: after both feature-major copies
+float* snack::ws_part(const snack_layer* L, const BatchPlan& p)
+{
+    const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
+    const size_t b = (((size_t)L->M * p.bp * 4) + 255) & ~(size_t)255;
+    return (float*)((char*)L->ws + a + b);
+}
+
+namespace {
+
 float* ws_dy(snack_layer* L, const BatchPlan& p)
 {
     const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
@@ -191,6 +204,11 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(tr.desc, int2*, ((size_t)L->tr.nchunks + 1) * 8);
     ALLOC(tr.empty_keys, int32_t*, (size_t)K * 4);
     ALLOC(tr.n_empty, int32_t*, 4);
+
+    {
+        snack_status _s = alloc_split_tables(L);
+        if (_s != SNACK_OK) return fail(_s);
+    }
 
     size_t scr = canon_scratch_bytes(L, nnz);
     const size_t pscr = prune_scratch_bytes(L);

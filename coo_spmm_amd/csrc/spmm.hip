@@ -906,6 +906,439 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs 
     key_stream<BT, NB, U, DW, SPMM>(A, &next_s, c1, gs_dyn, bp, B, stage);
 }
 
+// ---- slice-tiled key-major kernel (batch tiles of 16 to 64 columns) --------
+// A wide batch makes every entry gather a long operand row (256 bytes at 64
+// columns), which the vector caches serve far below LDS rates.  The operand's
+// rows are split into S slices that each fit in LDS; workgroup (slice s, key
+// block) stages slice s once and its wavefronts walk the segments of their
+// keys that fall in it -- every gather is an LDS read of a row laid out so a
+// quarter-wave reads 256 contiguous bytes.  Each wavefront streams the blocks
+// of its keys' segments with kTileDepth blocks in flight (a ring of statically
+// indexed registers, so no in-flight register is ever copied); the lanes of a
+// group receive their entries, and sum across groups, through DPP and lane
+// swaps, so the LDS pipe carries nothing but the gathers.  Slice partial
+// sums of a key are written to a [S][nkeys][tile] buffer and added in slice
+// order by a second kernel: no atomics, results bit-reproducible.  Per-entry
+// dW needs no such step (an entry lies in exactly one slice).
+constexpr int kTileWaves = 16;
+constexpr int kTileDepth = 8;     // blocks in flight per wavefront
+constexpr int kTileDepthDw = 4;   // with dW: each block also holds its key's operand row
+constexpr int kMaxSplits = 64;
+constexpr int kTileStaticLds = 1024;   // bytes kept back from the slice buffer
+
+__host__ __device__ inline int32_t split_start(int32_t s, int32_t S, int32_t nidx)
+{
+    return (int32_t)(((int64_t)s * nidx) / S);
+}
+
+struct TileArgs {
+    const int32_t* tab;   // slice bounds of key r in slice s: tab[s * tstride + r], tab[(s + 1) * tstride + r]
+    int64_t tstride;
+    float* part;          // [S][nkeys][tile] partial sums, or null to write the outputs (S == 1)
+    int32_t S, KB, R;     // slices, key blocks, keys per block
+};
+
+// one block of a key's segment: entries [base, lim) of key r (all uniform)
+struct TileDesc {
+    int32_t base, lim, r, last, valid;
+};
+
+// a wavefront's keys r0, r0 + kTileWaves, ... (nk <= 64 of them); lane j
+// holds key j's slice bounds
+struct TileCursor {
+    int32_t tlo, thi;
+    int32_t j, nk, r0, base, p1;
+
+    __device__ inline void next(TileDesc& d, int32_t step)
+    {
+        if (j >= nk) {
+            d.valid = 0;
+            d.base = 0;
+            d.lim = 0;
+            d.r = r0;
+            d.last = 0;
+            return;
+        }
+        d.valid = 1;
+        d.base = base;
+        d.lim = p1;
+        d.r = r0 + kTileWaves * j;
+        d.last = base + step >= p1 ? 1 : 0;
+        if (d.last) {
+            ++j;
+            if (j < nk) {
+                base = uni(__builtin_amdgcn_readlane(tlo, j));
+                p1 = uni(__builtin_amdgcn_readlane(thi, j));
+            }
+        } else {
+            base += step;
+        }
+    }
+};
+
+// ---- lane exchanges on the VALU (DPP and gfx950 lane swaps) ---------------
+// The tile kernel keeps the LDS pipe for its gathers: every other exchange
+// between lanes goes through data-parallel primitives instead of LDS-routed
+// shuffles.
+template <int CTRL, int BANKS = 0xF>
+__device__ inline float dpp_f(float old, float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, 0xF, BANKS, false));
+}
+template <int CTRL, int BANKS = 0xF>
+__device__ inline int32_t dpp_i(int32_t old, int32_t x)
+{
+    return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xF, BANKS, false);
+}
+// x[lane ^ M] for M < 16 (within a row of 16 lanes)
+template <int M>
+__device__ inline float lane_xor(float x)
+{
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "within a row");
+    if constexpr (M == 1) return dpp_f<0xB1>(0.0f, x);            // quad_perm [1,0,3,2]
+    else if constexpr (M == 2) return dpp_f<0x4E>(0.0f, x);       // quad_perm [2,3,0,1]
+    else if constexpr (M == 4) return dpp_f<0x1B>(0.0f, dpp_f<0x141>(0.0f, x));   // half-row mirror, quad reverse
+    else return dpp_f<0x128>(0.0f, x);                            // row rotate by 8
+}
+// value of lane U0 of this lane's group of BT lanes (groups are rows, half
+// rows or quads)
+template <int BT, int U0>
+__device__ inline int32_t group_bcast(int32_t x)
+{
+    if constexpr (BT == 16) return __builtin_amdgcn_mov_dpp(x, 0x150 + U0, 0xF, 0xF, false);   // row broadcast
+    else if constexpr (BT == 8) return dpp_i<0x158 + U0, 0xC>(dpp_i<0x150 + U0, 0x3>(x, x), x);
+    else return __builtin_amdgcn_mov_dpp(x, U0 * 0x55, 0xF, 0xF, false);                // quad broadcast
+}
+// group_bcast with zero in lanes a masked broadcast leaves untouched; the form
+// the compiler folds into a following add
+template <int BT, int U0>
+__device__ inline int32_t group_bcast0(int32_t x)
+{
+    if constexpr (BT == 16) return dpp_i<0x150 + U0>(0, x);
+    else if constexpr (BT == 8) return dpp_i<0x158 + U0, 0xC>(dpp_i<0x150 + U0, 0x3>(0, x), x);
+    else return dpp_i<U0 * 0x55>(0, x);
+}
+// the partner's value across lane bit 5 (HALF = 32) or bit 4 (HALF = 16)
+template <int HALF>
+__device__ inline float lane_swap_recv(float x, bool hi)
+{
+    const auto r = HALF == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(hi ? r[0] : r[1]);
+}
+// Four values summed over the G groups of a wave with three exchanges: lane l
+// ends with the total of value ((l >> 5) & 1) * 2 + ((l >> 4) & 1); groups of
+// fewer than 16 lanes hold it on every lane of the row with the same l % BT.
+template <int BT>
+__device__ inline float group_reduce4(const float (&a)[4], int lane)
+{
+    const bool h5 = (lane & 32) != 0;
+    const bool h4 = (lane & 16) != 0;
+    const float r0 = lane_swap_recv<32>(h5 ? a[0] : a[2], h5);
+    const float r1 = lane_swap_recv<32>(h5 ? a[1] : a[3], h5);
+    const float b0 = (h5 ? a[2] : a[0]) + r0;
+    const float b1 = (h5 ? a[3] : a[1]) + r1;
+    const float r = lane_swap_recv<16>(h4 ? b0 : b1, h4);
+    float c = (h4 ? b1 : b0) + r;
+    if constexpr (BT <= 8) c += lane_xor<8>(c);
+    if constexpr (BT <= 4) c += lane_xor<4>(c);
+    return c;
+}
+
+// reduce4_group with its exchanges on the VALU (groups of 4, 8 or 16 lanes)
+template <int BT>
+__device__ inline void reduce4_dpp(float (&d)[4], int bl)
+{
+    static_assert(BT >= 4 && BT <= 16, "groups of 4 to 16 lanes");
+    {
+        constexpr int m = BT / 2;
+        const bool hi = (bl & m) != 0;
+        const float s0 = hi ? d[0] : d[2];
+        const float s1 = hi ? d[1] : d[3];
+        const float r0 = lane_xor<m>(s0);
+        const float r1 = lane_xor<m>(s1);
+        d[0] = (hi ? d[2] : d[0]) + r0;
+        d[1] = (hi ? d[3] : d[1]) + r1;
+    }
+    {
+        constexpr int m = BT / 4;
+        const bool hi = (bl & m) != 0;
+        const float sv = hi ? d[0] : d[1];
+        const float r = lane_xor<m>(sv);
+        d[0] = (hi ? d[1] : d[0]) + r;
+    }
+    if constexpr (BT >= 16) d[0] += lane_xor<2>(d[0]);
+    if constexpr (BT >= 8) d[0] += lane_xor<1>(d[0]);
+}
+
+// A block of the tile kernel: group g owns entries base + g*U + u (u < U);
+// lane u of the group loads entry u (clamped, unconditional loads keep every
+// block in flight), and the group's lanes get each entry by a broadcast
+// inside the group.  Before use, entries outside [base, lim) are neutralised
+// per lane -- value 0 and the slice's first row -- so the per-entry work needs
+// no masks, and the index becomes the entry's byte offset into the slice.
+template <int BT, int U>
+struct TileBlock {
+    static constexpr int G = kWave / BT;
+    static constexpr int STEP = G * U;
+    static_assert(U <= BT && (U % 4) == 0, "a group's lanes load its entries");
+    int32_t nidx;
+    float nval;
+    int32_t noff;
+    float mval;
+
+    template <bool SPMM>
+    __device__ inline void load(const int32_t* __restrict__ idx, const float* __restrict__ vals, int32_t base,
+                                int32_t lim, int g, int bl)
+    {
+        const int32_t top = lim > 0 ? lim - 1 : 0;
+        const int32_t k = base + g * U + (bl < U ? bl : U - 1);
+        const uint32_t kc = (uint32_t)(k < lim ? k : top);
+        nidx = idx[kc];
+        nval = SPMM ? vals[kc] : 0.0f;
+    }
+    __device__ inline void prepare(int32_t base, int32_t lim, int g, int bl, int32_t i0, int32_t row_bytes)
+    {
+        const bool in = base + g * U + (bl < U ? bl : U - 1) < lim;
+        noff = in ? (nidx - i0) * row_bytes : 0;
+        mval = in ? nval : 0.0f;
+    }
+    // entry u's offset plus this lane's column offset (the broadcast folds
+    // into the add), and its value
+    template <int U0>
+    __device__ inline int32_t off_at(int32_t lane_off) const
+    {
+        return group_bcast0<BT, U0>(noff) + lane_off;
+    }
+    template <int U0>
+    __device__ inline float val_at() const
+    {
+        return __int_as_float(group_bcast<BT, U0>(__float_as_int(mval)));
+    }
+};
+
+// the U entries' staged rows (NB = 4 floats of this lane each) and values
+template <int U, int U0 = 0, class TB>
+__device__ inline void tile_gather(const TB& b, int32_t lane_off, float (&y)[U][4])
+{
+    extern __shared__ float gs_dyn[];
+    if constexpr (U0 < U) {
+        const int32_t off = b.template off_at<U0>(lane_off);
+        const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(gs_dyn) + off);
+        y[U0][0] = v.x;
+        y[U0][1] = v.y;
+        y[U0][2] = v.z;
+        y[U0][3] = v.w;
+        tile_gather<U, U0 + 1>(b, lane_off, y);
+    }
+}
+template <int U, int U0 = 0, class TB>
+__device__ inline void tile_vals(const TB& b, float (&vv)[U])
+{
+    if constexpr (U0 < U) {
+        vv[U0] = b.template val_at<U0>();
+        tile_vals<U, U0 + 1>(b, vv);
+    }
+}
+
+template <int BT, int NB, int U>
+__device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t lim, int g, int bl,
+                               float* __restrict__ dwo)
+{
+    constexpr int STRIDE = BT / 4;
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q) {
+        float d[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float a = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) a = fmaf(y[4 * q + t][n], h[n], a);
+            d[t] = a;
+        }
+        reduce4_dpp<BT>(d, bl);
+        if ((bl % STRIDE) == 0) {
+            const int32_t k = base + g * U + 4 * q + ((bl / STRIDE) & 3);
+            if (k < lim) dwo[k] = d[0];
+        }
+    }
+}
+
+template <int BT, int U, int D, bool DW, bool SPMM>
+__global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, TileArgs T, int bp, int B)
+{
+    constexpr int NB = 4;
+    constexpr int BTILE = BT * NB;
+    using TB = TileBlock<BT, U>;
+    extern __shared__ float gs_dyn[];
+    const int nwg = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    const int per = nwg / kXcd;   // the grid is a multiple of kXcd
+    // workgroups of one XCD take consecutive (slice, key block) pairs: they share slices in L2
+    const int lg = (bid % kXcd) * per + bid / kXcd;
+    const int s = lg / T.KB;
+    const int kb = lg - s * T.KB;
+    if (s >= T.S) return;
+    const int nkeys = A.nkeys;
+    const int32_t i0 = split_start(s, T.S, A.nidx);
+    const int32_t nrow = split_start(s + 1, T.S, A.nidx) - i0;
+    {
+        // the batch is a single tile, so the slice's rows are contiguous
+        const int64_t n4 = (int64_t)nrow * (BTILE / 4);
+        const float4* __restrict__ src = reinterpret_cast<const float4*>(A.G + (int64_t)i0 * bp);
+        float4* dst = reinterpret_cast<float4*>(gs_dyn);
+        constexpr int SB = 8;
+        constexpr int NT = kTileWaves * kWave;
+        for (int64_t q0 = threadIdx.x; q0 < n4; q0 += (int64_t)SB * NT) {
+            float4 v[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int64_t q = q0 + (int64_t)k * NT;
+                v[k] = src[q < n4 ? q : n4 - 1];
+            }
+            // clamped, unconditional stores (tail lanes rewrite the last element
+            // with its own value) keep all SB loads in flight together
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int64_t q = q0 + (int64_t)k * NT;
+                dst[q < n4 ? q : n4 - 1] = v[k];
+            }
+        }
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = uni((int)(threadIdx.x / kWave));
+    const int g = lane / BT;
+    const int bl = lane - g * BT;
+    const int bcol = bl * NB;
+    const int32_t rb = kb * T.R;
+    const int32_t re = rb + T.R < nkeys ? rb + T.R : nkeys;
+    const int32_t r0 = rb + wv;
+    const int32_t nk = r0 < re ? (re - r0 + kTileWaves - 1) / kTileWaves : 0;
+    if (nk == 0) return;
+    TileCursor cur;
+    {
+        const int32_t rj = r0 + kTileWaves * (lane < nk ? lane : 0);
+        cur.tlo = T.tab[(int64_t)s * T.tstride + rj];
+        cur.thi = T.tab[(int64_t)(s + 1) * T.tstride + rj];
+    }
+    cur.j = 0;
+    cur.nk = nk;
+    cur.r0 = r0;
+    cur.base = uni(__builtin_amdgcn_readlane(cur.tlo, 0));
+    cur.p1 = uni(__builtin_amdgcn_readlane(cur.thi, 0));
+
+    TileDesc d[D];
+    TB blk[D];
+    float hb[D][NB];
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+        cur.next(d[q], TB::STEP);
+        blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
+        if constexpr (DW) load_nb<NB>(A.H + (int64_t)d[q].r * bp + bcol, hb[q]);
+    }
+    const int32_t lane_off = bcol * 4;
+    float acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+    // every slot of a round is processed (an exhausted cursor yields empty,
+    // fully masked blocks), so the loop has a single exit and each slot keeps
+    // its registers across rounds
+    for (;;) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4);
+            float y[U][NB];
+            tile_gather<U>(blk[q], lane_off, y);
+            if constexpr (SPMM) {
+                float vv[U];
+                tile_vals<U>(blk[q], vv);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(vv[u], y[u][n], acc[n]);
+            }
+            if constexpr (DW) tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, g, bl, A.dwo);
+            if constexpr (SPMM) {
+                if (d[q].last) {
+                    // lane holds column bcol + v of the key's sum; one lane per column stores
+                    const float tot = group_reduce4<BT>(acc, lane);
+                    const int b = bcol + (((lane >> 5) & 1) << 1) + ((lane >> 4) & 1);
+                    if ((lane & (16 - BT)) == 0) {
+                        if (T.part) T.part[((int64_t)s * nkeys + d[q].r) * BTILE + b] = tot;
+                        else if (b < B) A.out[(int64_t)b * nkeys + d[q].r] = tot;
+                    }
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+                }
+            }
+            cur.next(d[q], TB::STEP);
+            blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
+            if constexpr (DW) load_nb<NB>(A.H + (int64_t)d[q].r * bp + bcol, hb[q]);
+        }
+        if (!d[0].valid) break;
+    }
+}
+
+// out[b, r] = sum over slices s = 0, 1, ... of part[s][r][b], in that order
+template <int BTILE>
+__global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part, int S, int nkeys, int B,
+                                                           float* __restrict__ out)
+{
+    constexpr int Q = BTILE / 4;
+    constexpr int KPB = 64;
+    __shared__ float t[KPB][BTILE + 1];
+    const int r0 = (int)blockIdx.x * KPB;
+    const int64_t sstride = (int64_t)nkeys * Q;
+    for (int e = threadIdx.x; e < KPB * Q; e += 256) {
+        const int kk = e / Q;
+        const int c4 = e - kk * Q;
+        const int r = r0 + kk;
+        float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (r < nkeys) {
+            const float4* __restrict__ pp = reinterpret_cast<const float4*>(part) + (int64_t)r * Q + c4;
+#pragma unroll 4
+            for (int s = 0; s < S; ++s) {
+                const float4 v = pp[s * sstride];
+                a.x += v.x;
+                a.y += v.y;
+                a.z += v.z;
+                a.w += v.w;
+            }
+        }
+        t[kk][c4 * 4 + 0] = a.x;
+        t[kk][c4 * 4 + 1] = a.y;
+        t[kk][c4 * 4 + 2] = a.z;
+        t[kk][c4 * 4 + 3] = a.w;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < KPB * BTILE; e += 256) {
+        const int b = e / KPB;
+        const int kk = e - b * KPB;
+        const int r = r0 + kk;
+        if (b < B && r < nkeys) out[(int64_t)b * nkeys + r] = t[kk][b];
+    }
+}
+
+// tab[s * nkeys + r] = first entry of key r whose index is at least the start of slice s
+__global__ void split_table_kernel(const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, int32_t nkeys,
+                                   int32_t nidx, int32_t S, int32_t* __restrict__ tab)
+{
+    const int64_t n = (int64_t)(S + 1) * nkeys;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t sl = (int32_t)(t / nkeys);
+        const int32_t r = (int32_t)(t - (int64_t)sl * nkeys);
+        int32_t lo = ptr[r], hi = ptr[r + 1];
+        const int32_t v = split_start(sl, S, nidx);
+        while (lo < hi) {
+            const int32_t mid = lo + ((hi - lo) >> 1);
+            if (idx[mid] < v) lo = mid + 1;
+            else hi = mid;
+        }
+        tab[t] = lo;
+    }
+}
+
 // dW in canonical order from dW in transposed order: dw[k] = dwt[iperm[k]].
 // XCD x owns one contiguous eighth of the canonical slots (one eighth of the
 // rows); its workgroups sweep that range together, workgroup w taking chunks
@@ -1107,7 +1540,113 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     return SNACK_OK;
 }
 
+inline int tile_index(int btile) { return btile == 16 ? 0 : btile == 32 ? 1 : btile == 64 ? 2 : -1; }
+
+// slice-tiled kernels for batch tiles of 16 and 64 columns on long keys (at 32
+// columns the 8-lane groups need two DPP moves per broadcast and the
+// key-major kernel is faster)
+inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
+{
+    const int i = tile_index(p.btile);
+    return i >= 0 && p.btile != 32 && p.ntiles == 1 && L->nnz > 0 && use_keyed(v, L->nnz, p) && v.split[i].S >= 1;
+}
+
+template <bool DW, bool SPMM>
+snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
+                         float* out, float* dwo, int B, hipStream_t s)
+{
+    const SplitTab& st = v.split[tile_index(p.btile)];
+    if (st.S >= 2 && !st.valid) {
+        const int64_t n = (int64_t)(st.S + 1) * v.nkeys;
+        int64_t grid = (n + 255) / 256;
+        if (grid > 4096) grid = 4096;
+        hipLaunchKernelGGL(split_table_kernel, dim3((unsigned)grid), dim3(256), 0, s, v.ptr, v.idx, v.nkeys, v.nidx,
+                           st.S, st.tab);
+        SNACK_HIP(hipGetLastError());
+        st.valid = true;
+    }
+    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    TileArgs t;
+    t.S = st.S;
+    t.tab = st.S >= 2 ? st.tab : v.ptr;
+    t.tstride = st.S >= 2 ? v.nkeys : 1;
+    t.part = (st.S >= 2 && SPMM) ? ws_part(L, p) : nullptr;
+    // about one workgroup per CU over all slices, at most 64 keys per wavefront
+    int kbn = (L->cus + t.S / 2) / t.S;
+    const int minkb = (v.nkeys + kTileWaves * 64 - 1) / (kTileWaves * 64);
+    const int maxkb = (v.nkeys + kTileWaves - 1) / kTileWaves;
+    if (kbn > maxkb) kbn = maxkb;
+    if (kbn < minkb) kbn = minkb;
+    if (kbn < 1) kbn = 1;
+    t.KB = kbn;
+    t.R = (v.nkeys + kbn - 1) / kbn;
+    int64_t nwg = (int64_t)t.S * t.KB;
+    nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+    const int32_t rows = (v.nidx + t.S - 1) / t.S;
+    const size_t lds = (size_t)rows * p.btile * sizeof(float);
+    const dim3 grid((unsigned)nwg), block(kTileWaves * kWave);
+    switch (p.btile) {
+    case 16: hipLaunchKernelGGL((tile_kernel<4, 4, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 32: hipLaunchKernelGGL((tile_kernel<8, 8, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 64: hipLaunchKernelGGL((tile_kernel<16, 8, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    default: return SNACK_ERR_INVALID_ARG;
+    }
+    SNACK_HIP(hipGetLastError());
+    if (t.part) {
+        const dim3 rg((unsigned)((v.nkeys + 63) / 64));
+        switch (p.btile) {
+        case 16: hipLaunchKernelGGL((split_reduce_kernel<16>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
+        case 32: hipLaunchKernelGGL((split_reduce_kernel<32>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
+        default: hipLaunchKernelGGL((split_reduce_kernel<64>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
+        }
+        SNACK_HIP(hipGetLastError());
+    }
+    return SNACK_OK;
+}
+
 }  // namespace
+
+int tile_splits(const snack_layer* L, const View& v, int btile)
+{
+    if (L->lds_bytes <= kTileStaticLds || v.nidx <= 0 || v.nkeys <= 0) return 0;
+    const int64_t rows = (int64_t)(L->lds_bytes - kTileStaticLds) / ((int64_t)btile * 4);
+    if (rows < 1) return 0;
+    const int64_t S = (v.nidx + rows - 1) / rows;
+    return S <= kMaxSplits ? (int)S : 0;
+}
+
+snack_status alloc_split_tables(snack_layer* L)
+{
+    View* views[2] = {&L->fwd, &L->tr};
+    for (View* v : views) {
+        for (int i = 0; i < kTileWidths; ++i) {
+            SplitTab& st = v->split[i];
+            st.S = tile_splits(L, *v, 16 << i);
+            st.tab = nullptr;
+            st.valid = false;
+            if (st.S >= 2) {
+                void* q = nullptr;
+                SNACK_CHECK(layer_alloc(L, &q, (size_t)(st.S + 1) * v->nkeys * sizeof(int32_t)));
+                st.tab = (int32_t*)q;
+            }
+        }
+    }
+    return SNACK_OK;
+}
+
+size_t tile_part_bytes(const snack_layer* L, const BatchPlan& p)
+{
+    size_t need = 0;
+    const View* views[2] = {&L->fwd, &L->tr};
+    for (const View* v : views) {
+        if (!use_tile(L, *v, p)) continue;
+        const SplitTab& st = v->split[tile_index(p.btile)];
+        if (st.S < 2) continue;
+        const size_t b = (size_t)st.S * v->nkeys * p.btile * sizeof(float);
+        if (b > need) need = b;
+    }
+    return (need + 255) & ~(size_t)255;
+}
 
 BatchPlan plan_batch(int B)
 {
@@ -1130,6 +1669,7 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
                           hipStream_t s)
 {
     ProfScope prof(KC_SPMM_FWD, s);
+    if (use_tile(L, L->fwd, p)) return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
     if (use_keyed(L->fwd, L->nnz, p))
         return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -1150,7 +1690,8 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         {
             ProfScope prof(KC_SPMM_DX, s);
-            SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s));
+            if (use_tile(L, L->tr, p)) SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s)));
+            else SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s));
         }
         ProfScope prof(KC_SDDMM_DW, s);
         if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
@@ -1171,6 +1712,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     ProfScope prof(KC_SPMM_DX, s);
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
+    if (use_tile(L, L->tr, p)) return launch_tile<false, true>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     if (use_keyed(L->tr, L->nnz, p))
         return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
