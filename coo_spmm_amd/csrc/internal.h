@@ -198,15 +198,21 @@ BatchPlan plan_batch(int B);
 snack_status transpose_pad(const float* src, float* dst, int n, const float* src2, float* dst2, int n2, int B,
                            int bp, hipStream_t s);
 
-// Y[b, key] = sum over the canonical view's entries of v * Xt[idx, b]
+// Whether every kernel of a forward (fwd) or backward (dx, dw requested) pass
+// can take the caller's batch-major [B][n] arrays directly, so no
+// feature-major copy is needed (batch tiles up to 4, operands staged in LDS).
+bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool dx, bool dw);
+
+// Y[b, key] = sum over the canonical view's entries of v * Xt[idx, b]; with rm
+// the operand is the batch-major X itself
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s);
+                          hipStream_t s, bool rm = false);
 
 // one launch: dX over the transposed view (plus dW in transposed order when
 // dW_t is non-null) and dW over the canonical view; either output may be null.
 // Requires a single batch tile when dW or dW_t is requested.
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
-                                 float* dX, float* dW, float* dW_t, hipStream_t s);
+                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm = false);
 
 // slice-tiled SpMM support: slices of view v for a batch tile (0 = not used),
 // the split tables' allocation (at create) and the workspace the partial sums

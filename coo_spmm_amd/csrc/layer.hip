@@ -256,6 +256,7 @@ extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, 
     if (!L || !X || !Y || B < 1) return SNACK_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
+    if (spmm_batch_major(L, p, true, false, false)) return spmm_forward(L, X, p, B, Y, s, true);
     const float* feat = X;
     if (p.bp > 1) {
         SNACK_CHECK(ensure_ws(L, p));
@@ -274,9 +275,10 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
     if (!dX && !dW) return SNACK_OK;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
+    const bool rm = spmm_batch_major(L, p, false, dX != nullptr, dW != nullptr);
     const float* dyt = dY;
     const float* xt = X;
-    if (p.bp > 1) {
+    if (p.bp > 1 && !rm) {
         SNACK_CHECK(ensure_ws(L, p));
         SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), L->M, dW ? X : nullptr, ws_x(L), L->K, B, p.bp, s));
         dyt = ws_dy(L, p);
@@ -287,7 +289,7 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
     if (p.ntiles == 1) {
         // one launch: dX (+ dW in transposed order) over the column view, dW over the row view
         float* dwt = (dX && dW) ? L->dwt : nullptr;
-        SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, dW, dwt, s));
+        SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, dW, dwt, s, rm));
         if (dwt) {
             L->dwt_for = dW;
             L->dwt_valid = true;

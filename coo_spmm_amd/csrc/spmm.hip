@@ -801,7 +801,29 @@ struct KeyCursor {
 // wave-uniform and kept in scalar registers, so its loads go through the
 // scalar cache and never make the vector loads in flight wait.  `stage` runs
 // on every thread once the first block is in flight (it may hold a barrier).
-template <int BT, int NB, int U, bool DW, bool SPMM, class Stage>
+// a key's dW operand: NB batch columns from bcol of row key of a feature-major
+// [n][bp] array, or (RM) of column key of a batch-major [B][nkeys] array, the
+// columns past B read as zero as in the padded feature-major copy
+template <int NB, bool RM>
+__device__ inline void load_h(const float* __restrict__ H, int64_t key, int bp, int bcol, int B, int nkeys,
+                              float (&h)[NB])
+{
+    if constexpr (RM) {
+        // clamped, unconditional loads; the columns past B zeroed after
+        float t[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int b = bcol + n;
+            t[n] = H[(int64_t)(b < B ? b : B - 1) * nkeys + key];
+        }
+#pragma unroll
+        for (int n = 0; n < NB; ++n) h[n] = bcol + n < B ? t[n] : 0.0f;
+    } else {
+        load_nb<NB>(H + key * bp + bcol, h);
+    }
+}
+
+template <int BT, int NB, int U, bool DW, bool SPMM, bool RM, class Stage>
 __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int cend, const float* __restrict__ Gm,
                                            int bp, int B, Stage&& stage)
 {
@@ -824,7 +846,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
     KB blk;
     float h[NB], hn[NB];
     blk.template load<SPMM>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
-    if constexpr (DW) load_nb<NB>(A.H + (int64_t)kc.r * bp + bcol, hn);
+    if constexpr (DW) load_h<NB, RM>(A.H, kc.r, bp, bcol, B, A.nkeys, hn);
     stage();
     if (!any) return;
     int32_t base = kc.p0;
@@ -841,7 +863,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
         const int32_t nbase = last ? kc.np0 : base + KB::STEP;
         const int32_t nlim = last ? kc.np1 : p1;
         const int32_t nkey = last ? (kc.nr < 0 ? kc.r : kc.nr) : kc.r;
-        if constexpr (DW) load_nb<NB>(A.H + (int64_t)nkey * bp + bcol, hn);
+        if constexpr (DW) load_h<NB, RM>(A.H, nkey, bp, bcol, B, A.nkeys, hn);
         blk.template load<SPMM>(A.idx, A.vals, nbase, nlim, lane, g);
         float y[U][NB];
         key_gather<NB, U>(Gm, ii, bp, bcol, y);
@@ -881,7 +903,7 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 constexpr int kLdsKeyWaves = 16;
 constexpr int kLdsU = 4;   // entries per lane per step
 
-template <int BT, int NB, int U, bool DW, bool SPMM = true>
+template <int BT, int NB, int U, bool DW, bool SPMM = true, bool RM = false>
 __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs A, int bp, int B)
 {
     extern __shared__ float gs_dyn[];
@@ -896,14 +918,69 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs 
     __syncthreads();
     // the operand is staged while every wave's first block is in flight
     auto stage = [&]() {
-        const int64_t n = (int64_t)A.nidx * bp;
-        const int64_t n4 = ((reinterpret_cast<uintptr_t>(A.G) & 15) == 0) ? n / 4 : 0;
-        for (int64_t i = threadIdx.x; i < n4; i += kLdsKeyWaves * kWave)
-            reinterpret_cast<float4*>(gs_dyn)[i] = reinterpret_cast<const float4*>(A.G)[i];
-        for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += kLdsKeyWaves * kWave) gs_dyn[i] = A.G[i];
+        constexpr int NT = kLdsKeyWaves * kWave;
+        if constexpr (RM) {
+            // batch-major [B][nidx] source: a thread loads 16 bytes of every
+            // batch row at four consecutive features and writes the four LDS
+            // rows they make (a 4 x NB transpose in registers); columns past B
+            // are zero, as in the padded feature-major copy
+            static_assert(BT == 1, "one lane per batch tile");
+            const int n = A.nidx;
+            const bool vec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(A.G) & 15) == 0;
+            const int n4 = vec ? n / 4 : 0;
+            constexpr int SB = 2;
+            for (int q0 = threadIdx.x; q0 < n4; q0 += SB * NT) {
+                float4 v[SB][NB];
+#pragma unroll
+                for (int k = 0; k < SB; ++k) {
+                    const int q = q0 + k * NT;
+                    const int qc = q < n4 ? q : n4 - 1;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        v[k][b] = reinterpret_cast<const float4*>(A.G + (int64_t)(b < B ? b : B - 1) * n)[qc];
+                }
+#pragma unroll
+                for (int k = 0; k < SB; ++k) {
+                    const int q = q0 + k * NT;
+                    const int qc = q < n4 ? q : n4 - 1;
+                    float* d = gs_dyn + qc * 4 * NB;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        if (b >= B) v[k][b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    }
+                    if constexpr (NB == 4) {
+                        reinterpret_cast<float4*>(d)[0] = make_float4(v[k][0].x, v[k][1].x, v[k][2].x, v[k][3].x);
+                        reinterpret_cast<float4*>(d)[1] = make_float4(v[k][0].y, v[k][1].y, v[k][2].y, v[k][3].y);
+                        reinterpret_cast<float4*>(d)[2] = make_float4(v[k][0].z, v[k][1].z, v[k][2].z, v[k][3].z);
+                        reinterpret_cast<float4*>(d)[3] = make_float4(v[k][0].w, v[k][1].w, v[k][2].w, v[k][3].w);
+                    } else if constexpr (NB == 2) {
+                        reinterpret_cast<float4*>(d)[0] = make_float4(v[k][0].x, v[k][1].x, v[k][0].y, v[k][1].y);
+                        reinterpret_cast<float4*>(d)[1] = make_float4(v[k][0].z, v[k][1].z, v[k][0].w, v[k][1].w);
+                    } else {
+                        *reinterpret_cast<float4*>(d) = v[k][0];
+                    }
+                }
+            }
+            for (int q = n4 * 4 * B + threadIdx.x; q < n * B; q += NT) {   // rows not in 16-byte units
+                const int b = q / n;
+                const int i = q - b * n;
+                gs_dyn[i * NB + b] = A.G[q];
+            }
+            for (int q = threadIdx.x; q < n * (NB - B); q += NT) {          // zero columns
+                const int b = B + q / n;
+                const int i = q - (b - B) * n;
+                gs_dyn[i * NB + b] = 0.0f;
+            }
+        } else {
+            const int64_t n = (int64_t)A.nidx * bp;
+            const int64_t n4 = ((reinterpret_cast<uintptr_t>(A.G) & 15) == 0) ? n / 4 : 0;
+            for (int64_t i = threadIdx.x; i < n4; i += NT)
+                reinterpret_cast<float4*>(gs_dyn)[i] = reinterpret_cast<const float4*>(A.G)[i];
+            for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += NT) gs_dyn[i] = A.G[i];
+        }
         __syncthreads();
     };
-    key_stream<BT, NB, U, DW, SPMM>(A, &next_s, c1, gs_dyn, bp, B, stage);
+    key_stream<BT, NB, U, DW, SPMM, RM>(A, &next_s, c1, gs_dyn, bp, B, stage);
 }
 
 // ---- slice-tiled key-major kernel (batch tiles of 16 to 64 columns) --------
@@ -1503,9 +1580,18 @@ inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
     return p.btile >= 1 && v.nkeys > 0 && nnz / v.nkeys >= 128;
 }
 
+// the key-major kernel with the whole gathered operand in LDS applies
+inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
+{
+    return p.btile <= 4 && p.ntiles == 1 && L->cus > 0 && v.nchunks > 0 && use_keyed(v, L->nnz, p) &&
+           (size_t)v.nidx * p.bp * sizeof(float) <= (size_t)L->lds_bytes;
+}
+
+// rm: G and H are batch-major [B][n] (the caller's arrays); only the LDS
+// kernel takes them, transposing G while it stages it
 template <bool DW, bool SPMM = true>
 snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
-                          float* out, float* dwo, int B, hipStream_t s)
+                          float* out, float* dwo, int B, hipStream_t s, bool rm = false)
 {
     const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     const size_t lds = (size_t)v.nidx * p.bp * sizeof(float);
@@ -1516,15 +1602,25 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
         if (nwg > want) nwg = want;
         nwg = (nwg + kXcd - 1) / kXcd * kXcd;
         const dim3 grid((unsigned)nwg), block(kLdsKeyWaves * kWave);
-        switch (p.btile) {
-        case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
-        case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
-        case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
-        default: return SNACK_ERR_INVALID_ARG;
+        if (rm) {
+            switch (p.btile) {
+            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
+            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
+            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
+            default: return SNACK_ERR_INVALID_ARG;
+            }
+        } else {
+            switch (p.btile) {
+            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+            default: return SNACK_ERR_INVALID_ARG;
+            }
         }
         SNACK_HIP(hipGetLastError());
         return SNACK_OK;
     }
+    if (rm) return SNACK_ERR_INVALID_ARG;   // callers check spmm_batch_major first
     dim3 grid((unsigned)(a.per_xcd * kXcd), (unsigned)p.ntiles);
     switch (p.btile) {
     case 1: hipLaunchKernelGGL((key_kernel<1, 1, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
@@ -1665,10 +1761,21 @@ BatchPlan plan_batch(int B)
     return p;
 }
 
+bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool dx, bool dw)
+{
+    if (p.bp <= 1) return false;   // one column: both layouts coincide
+    if (fwd) return keyed_lds(L, L->fwd, p);
+    if (dw && !dx) return keyed_lds(L, L->fwd, p);
+    if (dx && !dw) return keyed_lds(L, L->tr, p);
+    // dX and dW: the column pass, then dW recomputed over the row view
+    return dx && dw && p.btile <= kKeyedRecomputeMax && keyed_lds(L, L->tr, p) && keyed_lds(L, L->fwd, p);
+}
+
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s)
+                          hipStream_t s, bool rm)
 {
     ProfScope prof(KC_SPMM_FWD, s);
+    if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true);
     if (use_tile(L, L->fwd, p)) return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
     if (use_keyed(L->fwd, L->nnz, p))
         return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
@@ -1677,8 +1784,26 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 }
 
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
-                                 float* dX, float* dW, float* dW_t, hipStream_t s)
+                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm)
 {
+    if (rm) {
+        // batch-major operands: every pass is the LDS key-major kernel
+        if (dW && !dX) {
+            ProfScope prof(KC_SDDMM_DW, s);
+            return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true);
+        }
+        if (dX && !dW) {
+            ProfScope prof(KC_SPMM_DX, s);
+            return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s, true);
+        }
+        if (!dW_t) return SNACK_ERR_INVALID_ARG;
+        {
+            ProfScope prof(KC_SPMM_DX, s);
+            SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s, true));
+        }
+        ProfScope prof(KC_SDDMM_DW, s);
+        return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true);
+    }
     // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view.
     // Event classes: the column pass counts as dX, a separate canonical-order dW step as dW.
     if (dW && !dX) {
