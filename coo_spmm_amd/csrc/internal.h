@@ -35,7 +35,7 @@ enum KernelClass : int {
 // slices that each fit in LDS; tab[s * nkeys + r] is the first entry of key r
 // whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
 // change of the index.
-constexpr int kTileWidths = 3;   // batch tiles 16, 32, 64
+constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
 struct SplitTab {
     int32_t S = 0;
     int32_t* tab = nullptr;

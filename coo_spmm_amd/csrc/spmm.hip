@@ -1084,7 +1084,8 @@ __device__ inline int32_t group_bcast(int32_t x)
 {
     if constexpr (BT == 16) return __builtin_amdgcn_mov_dpp(x, 0x150 + U0, 0xF, 0xF, false);   // row broadcast
     else if constexpr (BT == 8) return dpp_i<0x158 + U0, 0xC>(dpp_i<0x150 + U0, 0x3>(x, x), x);
-    else return __builtin_amdgcn_mov_dpp(x, U0 * 0x55, 0xF, 0xF, false);                // quad broadcast
+    else if constexpr (BT == 4) return __builtin_amdgcn_mov_dpp(x, U0 * 0x55, 0xF, 0xF, false);   // quad broadcast
+    else return __builtin_amdgcn_mov_dpp(x, U0 | (U0 << 2) | ((2 + U0) << 4) | ((2 + U0) << 6), 0xF, 0xF, false);
 }
 // group_bcast with zero in lanes a masked broadcast leaves untouched; the form
 // the compiler folds into a following add
@@ -1093,7 +1094,8 @@ __device__ inline int32_t group_bcast0(int32_t x)
 {
     if constexpr (BT == 16) return dpp_i<0x150 + U0>(0, x);
     else if constexpr (BT == 8) return dpp_i<0x158 + U0, 0xC>(dpp_i<0x150 + U0, 0x3>(0, x), x);
-    else return dpp_i<U0 * 0x55>(0, x);
+    else if constexpr (BT == 4) return dpp_i<U0 * 0x55>(0, x);
+    else return dpp_i<U0 | (U0 << 2) | ((2 + U0) << 4) | ((2 + U0) << 6)>(0, x);   // pair broadcast
 }
 // the partner's value across lane bit 5 (HALF = 32) or bit 4 (HALF = 16)
 template <int HALF>
@@ -1103,23 +1105,60 @@ __device__ inline float lane_swap_recv(float x, bool hi)
                               : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(hi ? r[0] : r[1]);
 }
-// Four values summed over the G groups of a wave with three exchanges: lane l
-// ends with the total of value ((l >> 5) & 1) * 2 + ((l >> 4) & 1); groups of
-// fewer than 16 lanes hold it on every lane of the row with the same l % BT.
-template <int BT>
-__device__ inline float group_reduce4(const float (&a)[4], int lane)
+// The partner's value across lane bit BIT (bits 5 and 4 by lane swaps, lower
+// bits by DPP inside a row).
+template <int BIT>
+__device__ inline float xrecv(float x, bool hi)
 {
-    const bool h5 = (lane & 32) != 0;
-    const bool h4 = (lane & 16) != 0;
-    const float r0 = lane_swap_recv<32>(h5 ? a[0] : a[2], h5);
-    const float r1 = lane_swap_recv<32>(h5 ? a[1] : a[3], h5);
-    const float b0 = (h5 ? a[2] : a[0]) + r0;
-    const float b1 = (h5 ? a[3] : a[1]) + r1;
-    const float r = lane_swap_recv<16>(h4 ? b0 : b1, h4);
-    float c = (h4 ? b1 : b0) + r;
-    if constexpr (BT <= 8) c += lane_xor<8>(c);
-    if constexpr (BT <= 4) c += lane_xor<4>(c);
+    if constexpr (BIT == 5) return lane_swap_recv<32>(x, hi);
+    else if constexpr (BIT == 4) return lane_swap_recv<16>(x, hi);
+    else return lane_xor<(1 << BIT)>(x);
+}
+// one exchange-halves level over lane bit BIT on the first CNT values
+template <int BIT, int CNT, int NB>
+__device__ inline void xlevel(float (&a)[NB], int lane)
+{
+    const bool hi = ((lane >> BIT) & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < CNT / 2; ++i) {
+        const float sv = hi ? a[i] : a[i + CNT / 2];
+        const float kv = hi ? a[i + CNT / 2] : a[i];
+        a[i] = kv + xrecv<BIT>(sv, hi);
+    }
+}
+// NB values (4 or 8) summed over the G = 64 / BT groups of a wave: exchange
+// halves over the top log2(NB) lane bits, then plain sums over the remaining
+// group bits.  Lane l ends with the total of value v = (l >> (6 - log2 NB)), the
+// value's column being 4 * (l % BT + BT * (v >> 2)) + (v & 3); lanes that
+// differ only in the plain-summed bits hold the same total.
+template <int BT, int NB>
+__device__ inline float group_reduce(float (&a)[NB], int lane)
+{
+    static_assert(NB == 4 || NB == 8, "four or eight values per lane");
+    static_assert(64 / BT >= NB, "at least one group per value");
+    xlevel<5, NB>(a, lane);
+    xlevel<4, NB / 2>(a, lane);
+    if constexpr (NB == 8) xlevel<3, 2>(a, lane);
+    float c = a[0];
+    constexpr int LOWX = NB == 8 ? 3 : 4;   // lowest exchanged lane bit
+    if constexpr (LOWX > 3 && BT <= 8) c += lane_xor<8>(c);   // lane bit 3 is a group bit
+    if constexpr (BT <= 4) c += lane_xor<4>(c);               // bit 2
+    if constexpr (BT <= 2) c += lane_xor<2>(c);               // bit 1
+    if constexpr (BT <= 1) c += lane_xor<1>(c);               // bit 0
     return c;
+}
+template <int BT, int NB>
+__device__ inline int group_reduce_col(int lane)
+{
+    constexpr int SH = NB == 8 ? 3 : 4;
+    const int v = lane >> SH;
+    return 4 * ((lane % BT) + BT * (v >> 2)) + (v & 3);
+}
+template <int BT, int NB>
+__device__ inline bool group_reduce_owner(int lane)
+{
+    constexpr int SH = NB == 8 ? 3 : 4;
+    return (lane & ((1 << SH) - 1) & ~(BT - 1)) == 0;
 }
 
 // reduce4_group with its exchanges on the VALU (groups of 4, 8 or 16 lanes)
@@ -1158,7 +1197,7 @@ template <int BT, int U>
 struct TileBlock {
     static constexpr int G = kWave / BT;
     static constexpr int STEP = G * U;
-    static_assert(U <= BT && (U % 4) == 0, "a group's lanes load its entries");
+    static_assert(U <= BT && (U % 2) == 0, "a group's lanes load its entries");
     int32_t nidx;
     float nval;
     int32_t noff;
@@ -1194,19 +1233,28 @@ struct TileBlock {
     }
 };
 
-// the U entries' staged rows (NB = 4 floats of this lane each) and values
-template <int U, int U0 = 0, class TB>
-__device__ inline void tile_gather(const TB& b, int32_t lane_off, float (&y)[U][4])
+// the U entries' staged rows -- NB floats of this lane each: 16-byte chunk
+// lane % BT of the row, and for NB = 8 also chunk lane % BT + BT -- and values
+template <int U, int BT, int NB, int U0 = 0, class TB>
+__device__ inline void tile_gather(const TB& b, int32_t lane_off, float (&y)[U][NB])
 {
     extern __shared__ float gs_dyn[];
     if constexpr (U0 < U) {
         const int32_t off = b.template off_at<U0>(lane_off);
-        const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(gs_dyn) + off);
+        const char* base = reinterpret_cast<const char*>(gs_dyn) + off;
+        const float4 v = *reinterpret_cast<const float4*>(base);
         y[U0][0] = v.x;
         y[U0][1] = v.y;
         y[U0][2] = v.z;
         y[U0][3] = v.w;
-        tile_gather<U, U0 + 1>(b, lane_off, y);
+        if constexpr (NB == 8) {
+            const float4 w = *reinterpret_cast<const float4*>(base + BT * 16);
+            y[U0][4] = w.x;
+            y[U0][5] = w.y;
+            y[U0][6] = w.z;
+            y[U0][7] = w.w;
+        }
+        tile_gather<U, BT, NB, U0 + 1>(b, lane_off, y);
     }
 }
 template <int U, int U0 = 0, class TB>
@@ -1218,33 +1266,73 @@ __device__ inline void tile_vals(const TB& b, float (&vv)[U])
     }
 }
 
+// per-entry dot products with the key's operand row, reduced over the group
+// (pairs for 2-lane groups, fours otherwise) and stored; an entry's result is
+// the same sum of the same per-lane partials as in the key-major kernels
 template <int BT, int NB, int U>
 __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t lim, int g, int bl,
                                float* __restrict__ dwo)
 {
-    constexpr int STRIDE = BT / 4;
+    if constexpr (BT == 2) {
 #pragma unroll
-    for (int q = 0; q < U / 4; ++q) {
-        float d[4];
+        for (int q = 0; q < U / 2; ++q) {
+            float d[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float a = 0.0f;
+            for (int t = 0; t < 2; ++t) {
+                float a = 0.0f;
 #pragma unroll
-            for (int n = 0; n < NB; ++n) a = fmaf(y[4 * q + t][n], h[n], a);
-            d[t] = a;
+                for (int n = 0; n < NB; ++n) a = fmaf(y[2 * q + t][n], h[n], a);
+                d[t] = a;
+            }
+            const bool hi = (bl & 1) != 0;
+            const float r = lane_xor<1>(hi ? d[0] : d[1]);
+            const float tot = (hi ? d[1] : d[0]) + r;
+            const int32_t k = base + g * U + 2 * q + bl;
+            if (k < lim) dwo[k] = tot;
         }
-        reduce4_dpp<BT>(d, bl);
-        if ((bl % STRIDE) == 0) {
-            const int32_t k = base + g * U + 4 * q + ((bl / STRIDE) & 3);
-            if (k < lim) dwo[k] = d[0];
+    } else {
+        constexpr int STRIDE = BT / 4;
+#pragma unroll
+        for (int q = 0; q < U / 4; ++q) {
+            float d[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float a = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NB; ++n) a = fmaf(y[4 * q + t][n], h[n], a);
+                d[t] = a;
+            }
+            reduce4_dpp<BT>(d, bl);
+            if ((bl % STRIDE) == 0) {
+                const int32_t k = base + g * U + 4 * q + ((bl / STRIDE) & 3);
+                if (k < lim) dwo[k] = d[0];
+            }
         }
     }
 }
 
-template <int BT, int U, int D, bool DW, bool SPMM>
+// the key's dW operand: the lane's NB columns of row key of a feature-major array
+template <int BT, int NB>
+__device__ inline void tile_h(const float* __restrict__ H, int64_t key, int bp, int bl, float (&h)[NB])
+{
+    const float* p = H + key * bp + 4 * bl;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    h[0] = a.x;
+    h[1] = a.y;
+    h[2] = a.z;
+    h[3] = a.w;
+    if constexpr (NB == 8) {
+        const float4 b = *reinterpret_cast<const float4*>(p + 4 * BT);
+        h[4] = b.x;
+        h[5] = b.y;
+        h[6] = b.z;
+        h[7] = b.w;
+    }
+}
+
+template <int BT, int NB, int U, int D, bool DW, bool SPMM>
 __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, TileArgs T, int bp, int B)
 {
-    constexpr int NB = 4;
     constexpr int BTILE = BT * NB;
     using TB = TileBlock<BT, U>;
     extern __shared__ float gs_dyn[];
@@ -1287,7 +1375,6 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     const int wv = uni((int)(threadIdx.x / kWave));
     const int g = lane / BT;
     const int bl = lane - g * BT;
-    const int bcol = bl * NB;
     const int32_t rb = kb * T.R;
     const int32_t re = rb + T.R < nkeys ? rb + T.R : nkeys;
     const int32_t r0 = rb + wv;
@@ -1312,9 +1399,9 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     for (int q = 0; q < D; ++q) {
         cur.next(d[q], TB::STEP);
         blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
-        if constexpr (DW) load_nb<NB>(A.H + (int64_t)d[q].r * bp + bcol, hb[q]);
+        if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, bl, hb[q]);
     }
-    const int32_t lane_off = bcol * 4;
+    const int32_t lane_off = bl * 16;
     float acc[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
@@ -1326,7 +1413,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
         for (int q = 0; q < D; ++q) {
             blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4);
             float y[U][NB];
-            tile_gather<U>(blk[q], lane_off, y);
+            tile_gather<U, BT, NB>(blk[q], lane_off, y);
             if constexpr (SPMM) {
                 float vv[U];
                 tile_vals<U>(blk[q], vv);
@@ -1338,10 +1425,10 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
             if constexpr (DW) tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, g, bl, A.dwo);
             if constexpr (SPMM) {
                 if (d[q].last) {
-                    // lane holds column bcol + v of the key's sum; one lane per column stores
-                    const float tot = group_reduce4<BT>(acc, lane);
-                    const int b = bcol + (((lane >> 5) & 1) << 1) + ((lane >> 4) & 1);
-                    if ((lane & (16 - BT)) == 0) {
+                    // each lane ends with one column of the key's sum; one lane per column stores
+                    const float tot = group_reduce<BT, NB>(acc, lane);
+                    const int b = group_reduce_col<BT, NB>(lane);
+                    if (group_reduce_owner<BT, NB>(lane)) {
                         if (T.part) T.part[((int64_t)s * nkeys + d[q].r) * BTILE + b] = tot;
                         else if (b < B) A.out[(int64_t)b * nkeys + d[q].r] = tot;
                     }
@@ -1351,7 +1438,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
             }
             cur.next(d[q], TB::STEP);
             blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
-            if constexpr (DW) load_nb<NB>(A.H + (int64_t)d[q].r * bp + bcol, hb[q]);
+            if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, bl, hb[q]);
         }
         if (!d[0].valid) break;
     }
@@ -1636,15 +1723,16 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     return SNACK_OK;
 }
 
-inline int tile_index(int btile) { return btile == 16 ? 0 : btile == 32 ? 1 : btile == 64 ? 2 : -1; }
+inline int tile_index(int btile)
+{
+    return btile == 8 ? 0 : btile == 16 ? 1 : btile == 32 ? 2 : btile == 64 ? 3 : -1;
+}
 
-// slice-tiled kernels for batch tiles of 16 and 64 columns on long keys (at 32
-// columns the 8-lane groups need two DPP moves per broadcast and the
-// key-major kernel is faster)
+// slice-tiled kernels for batch tiles of 8 to 64 columns on long keys
 inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
 {
     const int i = tile_index(p.btile);
-    return i >= 0 && p.btile != 32 && p.ntiles == 1 && L->nnz > 0 && use_keyed(v, L->nnz, p) && v.split[i].S >= 1;
+    return i >= 0 && p.ntiles == 1 && L->nnz > 0 && use_keyed(v, L->nnz, p) && v.split[i].S >= 1;
 }
 
 template <bool DW, bool SPMM>
@@ -1681,16 +1769,20 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     const int32_t rows = (v.nidx + t.S - 1) / t.S;
     const size_t lds = (size_t)rows * p.btile * sizeof(float);
     const dim3 grid((unsigned)nwg), block(kTileWaves * kWave);
+    // group width x values per lane: 2 x 4, 4 x 4, 4 x 8, 16 x 4
+    constexpr int Dp = DW ? kTileDepthDw : kTileDepth;
     switch (p.btile) {
-    case 16: hipLaunchKernelGGL((tile_kernel<4, 4, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
-    case 32: hipLaunchKernelGGL((tile_kernel<8, 8, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
-    case 64: hipLaunchKernelGGL((tile_kernel<16, 8, DW ? kTileDepthDw : kTileDepth, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 8: hipLaunchKernelGGL((tile_kernel<2, 4, 2, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 16: hipLaunchKernelGGL((tile_kernel<4, 4, 4, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 32: hipLaunchKernelGGL((tile_kernel<4, 8, 4, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 64: hipLaunchKernelGGL((tile_kernel<16, 4, 8, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
     default: return SNACK_ERR_INVALID_ARG;
     }
     SNACK_HIP(hipGetLastError());
     if (t.part) {
         const dim3 rg((unsigned)((v.nkeys + 63) / 64));
         switch (p.btile) {
+        case 8: hipLaunchKernelGGL((split_reduce_kernel<8>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
         case 16: hipLaunchKernelGGL((split_reduce_kernel<16>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
         case 32: hipLaunchKernelGGL((split_reduce_kernel<32>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
         default: hipLaunchKernelGGL((split_reduce_kernel<64>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
@@ -1717,7 +1809,7 @@ snack_status alloc_split_tables(snack_layer* L)
     for (View* v : views) {
         for (int i = 0; i < kTileWidths; ++i) {
             SplitTab& st = v->split[i];
-            st.S = tile_splits(L, *v, 16 << i);
+            st.S = tile_splits(L, *v, 8 << i);
             st.tab = nullptr;
             st.valid = false;
             if (st.S >= 2) {
@@ -1821,6 +1913,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         ProfScope prof(KC_SDDMM_DW, s);
         if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view
+            if (use_tile(L, L->fwd, p)) return launch_tile<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
             return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
         }
         // wide batches: dW once, in column order, then permuted into canonical order
