@@ -1660,7 +1660,10 @@ snack_status dispatch_seg(const BatchPlan& p, int64_t cap, const View& va, const
 
 // key-major kernels: worth it where gathers dominate (wide batch tiles) and
 // keys are long enough to keep every group busy
-constexpr int kKeyedRecomputeMax = 8;   // widest batch tile that recomputes dW over the row view
+// widest batch tile that recomputes dW over the row view instead of permuting
+// the column-order dW; up to here every kernel pair that can meet gives each
+// lane the same batch columns, so the two dW orders agree bit for bit
+constexpr int kKeyedRecomputeMax = 16;
 
 inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
 {
@@ -1769,13 +1772,16 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     const int32_t rows = (v.nidx + t.S - 1) / t.S;
     const size_t lds = (size_t)rows * p.btile * sizeof(float);
     const dim3 grid((unsigned)nwg), block(kTileWaves * kWave);
-    // group width x values per lane: 2 x 4, 4 x 4, 4 x 8, 16 x 4
+    // group width x values per lane x entries per group: 2 x 4 x 2, 4 x 4 x 4,
+    // 4 x 8 x 4, 16 x 4 x 8 (x 4 with dW: short slice segments waste less)
     constexpr int Dp = DW ? kTileDepthDw : kTileDepth;
+    constexpr int U64 = DW ? 4 : 8;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a, t, p.bp, B); };
     switch (p.btile) {
-    case 8: hipLaunchKernelGGL((tile_kernel<2, 4, 2, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
-    case 16: hipLaunchKernelGGL((tile_kernel<4, 4, 4, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
-    case 32: hipLaunchKernelGGL((tile_kernel<4, 8, 4, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
-    case 64: hipLaunchKernelGGL((tile_kernel<16, 4, 8, Dp, DW, SPMM>), grid, block, lds, s, a, t, p.bp, B); break;
+    case 8: go(tile_kernel<2, 4, 2, Dp, DW, SPMM>); break;
+    case 16: go(tile_kernel<4, 4, 4, Dp, DW, SPMM>); break;
+    case 32: go(tile_kernel<4, 8, 4, Dp, DW, SPMM>); break;
+    case 64: go(tile_kernel<16, 4, U64, Dp, DW, SPMM>); break;
     default: return SNACK_ERR_INVALID_ARG;
     }
     SNACK_HIP(hipGetLastError());
@@ -1853,6 +1859,20 @@ BatchPlan plan_batch(int B)
     return p;
 }
 
+// dW[k] = dW_t[iperm[k]]
+static snack_status permute_dw(const snack_layer* L, const float* dW_t, float* dW, hipStream_t s)
+{
+    if (L->nnz > 0) {
+        const int64_t per_xcd = (L->nnz + kXcd - 1) / kXcd;
+        int64_t nw = (per_xcd + kBlock - 1) / kBlock;
+        if (nw > 256) nw = 256;   // about eight resident workgroups per CU
+        hipLaunchKernelGGL(permute_dw_kernel, dim3((unsigned)(nw * kXcd)), dim3(kBlock), 0, s, L->iperm, dW_t, L->nnz,
+                           per_xcd, dW);
+        SNACK_HIP(hipGetLastError());
+    }
+    return SNACK_OK;
+}
+
 bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool dx, bool dw)
 {
     if (p.bp <= 1) return false;   // one column: both layouts coincide
@@ -1917,15 +1937,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
         }
         // wide batches: dW once, in column order, then permuted into canonical order
-        if (L->nnz > 0) {
-            const int64_t per_xcd = (L->nnz + kXcd - 1) / kXcd;
-            int64_t nw = (per_xcd + kBlock - 1) / kBlock;
-            if (nw > 256) nw = 256;   // about eight resident workgroups per CU
-            hipLaunchKernelGGL(permute_dw_kernel, dim3((unsigned)(nw * kXcd)), dim3(kBlock), 0, s, L->iperm, dW_t,
-                               L->nnz, per_xcd, dW);
-            SNACK_HIP(hipGetLastError());
-        }
-        return SNACK_OK;
+        return permute_dw(L, dW_t, dW, s);
     }
     ProfScope prof(KC_SPMM_DX, s);
     if (dW)
