@@ -1191,8 +1191,9 @@ __device__ inline void reduce4_dpp(float (&d)[4], int bl)
 // lane u of the group loads entry u (clamped, unconditional loads keep every
 // block in flight), and the group's lanes get each entry by a broadcast
 // inside the group.  Before use, entries outside [base, lim) are neutralised
-// per lane -- value 0 and the slice's first row -- so the per-entry work needs
-// no masks, and the index becomes the entry's byte offset into the slice.
+// per lane -- value 0 and an all-zero row staged after the slice -- so the
+// per-entry work needs no masks, and the index becomes the entry's byte offset
+// into the slice.
 template <int BT, int U>
 struct TileBlock {
     static constexpr int G = kWave / BT;
@@ -1213,10 +1214,13 @@ struct TileBlock {
         nidx = idx[kc];
         nval = SPMM ? vals[kc] : 0.0f;
     }
-    __device__ inline void prepare(int32_t base, int32_t lim, int g, int bl, int32_t i0, int32_t row_bytes)
+    // zero_off: the all-zero row staged after the slice, so a neutral entry
+    // adds exactly 0 whatever the activations hold
+    __device__ inline void prepare(int32_t base, int32_t lim, int g, int bl, int32_t i0, int32_t row_bytes,
+                                   int32_t zero_off)
     {
         const bool in = base + g * U + (bl < U ? bl : U - 1) < lim;
-        noff = in ? (nidx - i0) * row_bytes : 0;
+        noff = in ? (nidx - i0) * row_bytes : zero_off;
         mval = in ? nval : 0.0f;
     }
     // entry u's offset plus this lane's column offset (the broadcast folds
@@ -1369,6 +1373,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
                 dst[q < n4 ? q : n4 - 1] = v[k];
             }
         }
+        if (threadIdx.x < BTILE / 4) dst[n4 + threadIdx.x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);   // zero row
         __syncthreads();
     }
     const int lane = threadIdx.x & (kWave - 1);
@@ -1411,7 +1416,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     for (;;) {
 #pragma unroll
         for (int q = 0; q < D; ++q) {
-            blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4);
+            blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4, nrow * BTILE * 4);
             float y[U][NB];
             tile_gather<U, BT, NB>(blk[q], lane_off, y);
             if constexpr (SPMM) {
@@ -1769,7 +1774,7 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     t.R = (v.nkeys + kbn - 1) / kbn;
     int64_t nwg = (int64_t)t.S * t.KB;
     nwg = (nwg + kXcd - 1) / kXcd * kXcd;
-    const int32_t rows = (v.nidx + t.S - 1) / t.S;
+    const int32_t rows = (v.nidx + t.S - 1) / t.S + 1;   // the slice and a zero row
     const size_t lds = (size_t)rows * p.btile * sizeof(float);
     const dim3 grid((unsigned)nwg), block(kTileWaves * kWave);
     // group width x values per lane x entries per group: 2 x 4 x 2, 4 x 4 x 4,

@@ -91,6 +91,39 @@ def test_keyed_keys_longer_than_chunks(transpose):
                            triple=(r, c, v))
 
 
+def test_non_finite_activations_outside_the_support():
+    # +inf in a feature no entry reads (feature 0, the first staged row of the
+    # first slice) and in an output gradient no entry reads: entries the
+    # kernels neutralise must add exactly zero, so every output stays finite
+    # and matches the oracle
+    import torch
+    L = lib()
+    M, K, nnz = 1000, 800, 200000
+    rows, cols, vals = _make(M, K, nnz, "gpu/nonfinite")
+    keep = (cols != 0) & (rows != 0)
+    rows, cols, vals = rows[keep], cols[keep], vals[keep]
+    ref = oracle.canonicalize(M, K, rows, cols, vals)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    try:
+        for B in (1, 2, 4, 8, 16, 32, 64):
+            X = normal((B, K), f"gpu/nonfinite/X/{B}")
+            dY = normal((B, M), f"gpu/nonfinite/dY/{B}")
+            X[:, 0] = np.inf
+            dY[:, 0] = np.inf
+            say("non-finite outside the support B", B)
+            Y = host(layer.forward(dev(X)))
+            dX, dW = (host(t) for t in layer.backward(dev(X), dev(dY)))
+            assert np.isfinite(Y).all() and np.isfinite(dX[:, 1:]).all() and np.isfinite(dW).all()
+            Yr, Ya = oracle.forward(M, K, ref["rows"], ref["cols"], ref["vals"], X)
+            assert_close(f"Y B={B}", Y, Yr, Ya)
+            dXr, dXa = oracle.backward_dx(M, K, ref["rows"], ref["cols"], ref["vals"], dY)
+            assert_close(f"dX B={B}", dX, dXr, dXa)
+            dWr, dWa = oracle.backward_dw(M, K, ref["rows"], ref["cols"], X, dY)
+            assert_close(f"dW B={B}", dW, dWr, dWa)
+    finally:
+        layer.close()
+
+
 @pytest.mark.parametrize("M,K,nnz", [(130, 70, 2000), (1000, 800, 200000)])
 def test_backward_dx_only_and_dw_only(M, K, nnz):
     # a first layer needs no dX; a frozen layer needs no dW: both paths alone
