@@ -1489,22 +1489,58 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
     }
 }
 
-// tab[s * nkeys + r] = first entry of key r whose index is at least the start of slice s
-__global__ void split_table_kernel(const int32_t* __restrict__ ptr, const int32_t* __restrict__ idx, int32_t nkeys,
-                                   int32_t nidx, int32_t S, int32_t* __restrict__ tab)
+// The slice tables of one view for up to kTileWidths slice counts in one
+// pass over its index: a wavefront per key reads the key's ascending indices
+// once; an entry whose slice passes its predecessor's is the first entry of
+// every slice in between (tab[s * nkeys + key]), slices up to the first entry's
+// start at the key's first entry and slices past the last entry at its end.
+struct TabSet {
+    int32_t S[kTileWidths];
+    int32_t* tab[kTileWidths];   // null: not built
+    double inv_nidx;             // 1 / nidx
+};
+
+// the slice s with split_start(s) <= i < split_start(s + 1), i.e.
+// floor(((i + 1) S - 1) / nidx); the numerator is an integer below 2^38 and
+// the exact quotient's distance from the next integer is at least 1 / nidx,
+// far above the rounding error of the reciprocal product, so the floor is exact
+__device__ inline int32_t slice_of(int32_t i, int32_t S, double inv_nidx)
 {
-    const int64_t n = (int64_t)(S + 1) * nkeys;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t sl = (int32_t)(t / nkeys);
-        const int32_t r = (int32_t)(t - (int64_t)sl * nkeys);
-        int32_t lo = ptr[r], hi = ptr[r + 1];
-        const int32_t v = split_start(sl, S, nidx);
-        while (lo < hi) {
-            const int32_t mid = lo + ((hi - lo) >> 1);
-            if (idx[mid] < v) lo = mid + 1;
-            else hi = mid;
+    return (int32_t)floor(((double)(i + 1) * (double)S - 1.0) * inv_nidx);
+}
+
+__global__ void __launch_bounds__(256) split_tables_kernel(const int32_t* __restrict__ ptr,
+                                                           const int32_t* __restrict__ idx, int32_t nkeys,
+                                                           int32_t nidx, TabSet ts)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t r = (int32_t)blockIdx.x * (256 / kWave) + (int32_t)(threadIdx.x / kWave);
+    if (r >= nkeys) return;
+    const int32_t p0 = ptr[r], p1 = ptr[r + 1];
+    int32_t carry[kTileWidths];   // slice of the entry before this step's first
+#pragma unroll
+    for (int w = 0; w < kTileWidths; ++w) carry[w] = -1;
+    for (int32_t base = p0; base < p1; base += kWave) {
+        const int32_t k = base + lane;
+        const int32_t i = idx[k < p1 ? k : p1 - 1];
+#pragma unroll
+        for (int w = 0; w < kTileWidths; ++w) {
+            if (!ts.tab[w]) continue;
+            const int32_t S = ts.S[w];
+            const int32_t t = slice_of(i, S, ts.inv_nidx);
+            const int32_t up = __shfl_up(t, 1, kWave);
+            const int32_t tp = lane == 0 ? carry[w] : up;
+            carry[w] = __shfl(t, kWave - 1, kWave);
+            if (k < p1)
+                for (int32_t sl = tp + 1; sl <= t; ++sl) ts.tab[w][(int64_t)sl * nkeys + r] = k;
         }
-        tab[t] = lo;
+    }
+#pragma unroll
+    for (int w = 0; w < kTileWidths; ++w) {
+        if (!ts.tab[w]) continue;
+        const int32_t S = ts.S[w];
+        const int32_t tl = p1 > p0 ? slice_of(idx[p1 - 1], S, ts.inv_nidx) : -1;
+        for (int32_t sl = tl + 1 + lane; sl <= S; sl += kWave) ts.tab[w][(int64_t)sl * nkeys + r] = p1;
     }
 }
 
@@ -1749,13 +1785,20 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
 {
     const SplitTab& st = v.split[tile_index(p.btile)];
     if (st.S >= 2 && !st.valid) {
-        const int64_t n = (int64_t)(st.S + 1) * v.nkeys;
-        int64_t grid = (n + 255) / 256;
-        if (grid > 4096) grid = 4096;
-        hipLaunchKernelGGL(split_table_kernel, dim3((unsigned)grid), dim3(256), 0, s, v.ptr, v.idx, v.nkeys, v.nidx,
-                           st.S, st.tab);
+        // every stale table of this view in one pass over its index
+        TabSet ts;
+        ts.inv_nidx = 1.0 / (double)v.nidx;
+        for (int w = 0; w < kTileWidths; ++w) {
+            const SplitTab& sw = v.split[w];
+            const bool build = sw.S >= 2 && !sw.valid;
+            ts.S[w] = sw.S;
+            ts.tab[w] = build ? sw.tab : nullptr;
+        }
+        hipLaunchKernelGGL(split_tables_kernel, dim3((unsigned)((v.nkeys + 3) / 4)), dim3(256), 0, s, v.ptr, v.idx,
+                           v.nkeys, v.nidx, ts);
         SNACK_HIP(hipGetLastError());
-        st.valid = true;
+        for (int w = 0; w < kTileWidths; ++w)
+            if (ts.tab[w]) v.split[w].valid = true;
     }
     const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     TileArgs t;
