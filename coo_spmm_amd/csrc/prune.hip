@@ -23,6 +23,9 @@
 // ascending position: prefix counts of bits place every entry, and a kept
 // cell takes the next kept value (its rank in `kept`).
 // Every step is integer work and deterministic.
+#include <algorithm>
+#include <cmath>
+
 #include "internal.h"
 
 namespace snack {
@@ -31,13 +34,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr int64_t kMaxBatch = 1 << 21;          // candidates per batch
-constexpr int kTBits = 21;                       // candidate index bits in a table word
-constexpr int kHashBits = 22;                    // table slots (load <= 1/2)
-constexpr uint64_t kEmpty = ~0ull;
+constexpr uint64_t kEmpty = ~0ull;              // empty table word
 constexpr uint64_t kMaxBitmapBits = 1ull << 34;
 constexpr int kSelBlocks = 512;                  // workgroups of one selection pass
 
-static_assert(kMaxBatch <= (1ll << kTBits), "candidate index must fit its field");
 
 inline unsigned grid_for(int64_t n)
 {
@@ -57,6 +57,24 @@ __device__ inline uint64_t splitmix64_output(uint64_t z)
 }
 
 __device__ inline uint32_t mag_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+__device__ inline int32_t wave_incl(int32_t v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ inline int32_t wave_sum(int32_t v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
 
 // ---- drop: radix select ---------------------------------------------------
 // state: [0] prefix, [1] rank still to find among keys matching the prefix,
@@ -117,16 +135,17 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
         p[i] = v;
 }
 
-// zero four bitmaps of `words` words in one launch
-__global__ void zero4_kernel(uint32_t* __restrict__ a, uint32_t* __restrict__ b, uint32_t* __restrict__ c,
-                             uint32_t* __restrict__ d, int64_t words)
+// zero three bitmaps of `words` words and `nfill` counters in one launch
+__global__ void zero_bitmaps_kernel(uint32_t* __restrict__ a, uint32_t* __restrict__ b, uint32_t* __restrict__ c,
+                                    int64_t words, int32_t* __restrict__ fill, int32_t nfill)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < words; i += (int64_t)gridDim.x * blockDim.x) {
         a[i] = 0u;
         b[i] = 0u;
         c[i] = 0u;
-        d[i] = 0u;
     }
+    for (int64_t i = i0; i < nfill; i += (int64_t)gridDim.x * blockDim.x) fill[i] = 0;
 }
 
 __device__ inline uint64_t cell_of(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, int64_t k,
@@ -323,115 +342,310 @@ __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
 }
 
 // ---- grow ------------------------------------------------------------------
-// candidate i of this batch is stream element t0 + i; occupied cells get the sentinel N
-__global__ void gen_candidates_kernel(uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N,
-                                      const uint32_t* __restrict__ occ_bm, uint64_t* __restrict__ cpos)
+// One batch takes the candidates t0 .. t0+T-1 in five launches, with no global
+// atomic per candidate:
+//   gen_bucket    every candidate's cell, grouped by region (2^rb consecutive
+//                 cells, so a region owns whole bitmap words); a workgroup
+//                 counts its candidates per region in LDS and reserves each
+//                 region's run with one atomic.  The order inside a bucket is
+//                 arbitrary: nothing downstream depends on it.
+//   region_claim  one workgroup per region: the region's `occ` words in LDS,
+//                 an LDS table keeps the smallest candidate index per free
+//                 cell, the winners are marked accepted and their bits set,
+//                 and the words are written back whole.
+//   tile_sum/cut  accepted counts per tile of candidate indices; the tile
+//                 holding the need-th accepted one is scanned to find it.
+//   give_back     accepted candidates past that one clear their bits again.
+// A region's bucket has a fixed capacity far above its expected size; if one
+// ever overflows, the batch changes nothing and is taken again at half size
+// (the outcome does not depend on the batch size).
+constexpr int kGenThreads = 1024;
+constexpr int kGenPer = 16;
+constexpr int64_t kGenTile = (int64_t)kGenThreads * kGenPer;
+constexpr int32_t kMaxRegions = 8192;
+constexpr int kSubBits = 18;          // cells of one LDS pass of region_claim (a 32 KB bitmap)
+constexpr int kClaimThreads = 1024;
+constexpr int kTabBits = 13;
+constexpr int kTabSlots = 1 << kTabBits;   // LDS table: 64 KB
+constexpr int kTlBits = 21;           // candidate index within a batch
+constexpr int64_t kSumTile = 8192;    // candidate indices per accepted-count tile
+constexpr int kStOverflow = 8, kStTaken = 9, kStCut = 10;   // words of the prune state
+
+static_assert(kMaxBatch <= (1ll << kTlBits), "candidate index must fit its field");
+static_assert(kMaxBatch / kSumTile <= 1024, "one workgroup scans the tile counts");
+
+__device__ inline uint64_t candidate_pos(uint64_t seed, uint64_t epoch, uint64_t t, uint64_t N)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t t = t0 + (uint64_t)i;
-        const uint64_t x = seed + ((epoch << 40) + t + 1ull) * kGamma;
-        const uint64_t pos = __umul64hi(splitmix64_output(x), N);
-        const bool occupied = (occ_bm[pos >> 5] >> (pos & 31)) & 1u;
-        cpos[i] = occupied ? N : pos;
+    const uint64_t x = seed + ((epoch << 40) + t + 1ull) * kGamma;
+    return __umul64hi(splitmix64_output(x), N);
+}
+
+__device__ inline uint32_t tab_slot(uint32_t c) { return (c * 0x9E3779B1u) >> (32 - kTabBits); }
+
+// bucket entry: candidate index within the batch << 32 | cell within the region
+__global__ void __launch_bounds__(kGenThreads) gen_bucket_kernel(uint64_t seed, uint64_t epoch, uint64_t t0,
+                                                                 int64_t T, uint64_t N, int rb, int32_t R,
+                                                                 int32_t cap, int32_t* __restrict__ fill,
+                                                                 uint64_t* __restrict__ bucket,
+                                                                 uint8_t* __restrict__ acc8,
+                                                                 uint32_t* __restrict__ state)
+{
+    __shared__ int32_t cur[kMaxRegions];
+    for (int32_t r = threadIdx.x; r < R; r += kGenThreads) cur[r] = 0;
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * kGenTile + threadIdx.x;
+    uint64_t pos[kGenPer];
+#pragma unroll
+    for (int u = 0; u < kGenPer; ++u) {
+        const int64_t i = i0 + (int64_t)u * kGenThreads;
+        pos[u] = candidate_pos(seed, epoch, t0 + (uint64_t)i, N);
+        if (i < T) {
+            atomicAdd(&cur[(int32_t)(pos[u] >> rb)], 1);
+            acc8[i] = 0;
+        }
+    }
+    __syncthreads();
+    for (int32_t r = threadIdx.x; r < R; r += kGenThreads) {
+        const int32_t c = cur[r];
+        if (c) cur[r] = atomicAdd(&fill[r], c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kGenPer; ++u) {
+        const int64_t i = i0 + (int64_t)u * kGenThreads;
+        if (i >= T) continue;
+        const int32_t r = (int32_t)(pos[u] >> rb);
+        const int32_t slot = atomicAdd(&cur[r], 1);
+        if (slot < cap)
+            bucket[(int64_t)r * cap + slot] = ((uint64_t)i << 32) | (uint64_t)(uint32_t)(pos[u] - ((uint64_t)r << rb));
+        else
+            atomicOr(&state[kStOverflow], 1u);
     }
 }
 
-__global__ void hash_clear_kernel(unsigned long long* __restrict__ tab, int64_t H)
+// Region r in passes of 2^sb cells.  Table words pack cell << kTlBits | index,
+// so an atomic minimum keeps the smallest index of a cell whatever the order.
+// The table never fills: a pass holds at most 2^sb <= 4096 distinct cells when
+// sb <= 12, and a bucket holds at most 4096 candidates otherwise.
+__global__ void __launch_bounds__(kClaimThreads) region_claim_kernel(int rb, int sb, uint64_t words_total,
+                                                                     int32_t cap, int32_t* __restrict__ fill,
+                                                                     const uint64_t* __restrict__ bucket,
+                                                                     uint32_t* __restrict__ occ_bm,
+                                                                     uint8_t* __restrict__ acc8,
+                                                                     const uint32_t* __restrict__ state)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < H; i += (int64_t)gridDim.x * blockDim.x)
-        tab[i] = kEmpty;
-}
-
-__device__ inline uint32_t hash_slot(uint64_t pos) { return (uint32_t)((pos * kGamma) >> (64 - kHashBits)); }
-
-// Every free candidate claims its cell in `occ`.  Occupied cells were filtered
-// out when the batch was generated, so a claim that finds its bit already set
-// lost to another candidate of this batch: the cell is marked contested.
-__global__ void claim_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N, uint32_t* __restrict__ occ_bm,
-                             uint32_t* __restrict__ con_bm)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = cpos[i];
-        if (p >= N) continue;
-        const uint32_t bit = 1u << (p & 31);
-        const uint32_t old = atomicOr(&occ_bm[p >> 5], bit);
-        if (old & bit) atomicOr(&con_bm[p >> 5], bit);
+    extern __shared__ unsigned long long tab[];   // kTabSlots words, then the pass's bitmap words
+    uint32_t* bm = reinterpret_cast<uint32_t*>(tab + kTabSlots);
+    __shared__ int32_t s_n, s_err;
+    const int32_t r = blockIdx.x;
+    if (threadIdx.x == 0) {
+        const int32_t f = fill[r];
+        s_n = f < cap ? f : cap;
+        s_err = state[kStOverflow] != 0u;
+        fill[r] = 0;   // ready for the next batch
     }
-}
-
-// Claimants of contested cells register (cell, index) in an open-addressing
-// table; the word packs cell << kTBits | index, so an atomic minimum keeps the
-// smallest index whatever the order of the atomics.
-__global__ void contest_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
-                               const uint32_t* __restrict__ con_bm, unsigned long long* __restrict__ tab,
-                               int32_t* __restrict__ cflag)
-{
-    const uint32_t mask = (1u << kHashBits) - 1u;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = cpos[i];
-        int32_t f = 0;
-        if (p < N && ((con_bm[p >> 5] >> (p & 31)) & 1u)) {
-            f = 1;
-            const unsigned long long word = (p << kTBits) | (uint64_t)i;
-            uint32_t h = hash_slot(p);
-            for (uint32_t probe = 0; probe <= mask; ++probe) {
+    __syncthreads();
+    if (s_err) return;
+    const int32_t n = s_n;
+    const uint64_t* __restrict__ e = bucket + (int64_t)r * cap;
+    const uint32_t cmask = (1u << sb) - 1u;
+    const int passes = 1 << (rb - sb);
+    for (int p = 0; p < passes; ++p) {
+        const uint64_t w0 = (((uint64_t)r << rb) + ((uint64_t)p << sb)) >> 5;
+        if (w0 >= words_total) break;   // uniform
+        const uint64_t left = words_total - w0;
+        const uint32_t nw = left < (uint64_t)(1u << (sb - 5)) ? (uint32_t)left : (1u << (sb - 5));
+        for (uint32_t i = threadIdx.x; i < nw; i += kClaimThreads) bm[i] = occ_bm[w0 + i];
+        for (int i = threadIdx.x; i < kTabSlots; i += kClaimThreads) tab[i] = kEmpty;
+        __syncthreads();
+        for (int32_t k = threadIdx.x; k < n; k += kClaimThreads) {
+            const uint64_t x = e[k];
+            const uint32_t cell = (uint32_t)x;
+            if ((cell >> sb) != (uint32_t)p) continue;
+            const uint32_t c = cell & cmask;
+            if ((bm[c >> 5] >> (c & 31)) & 1u) continue;
+            const unsigned long long word = ((unsigned long long)c << kTlBits) | (x >> 32);
+            uint32_t h = tab_slot(c);
+            for (int probe = 0; probe < kTabSlots; ++probe) {
                 const unsigned long long old = atomicCAS(&tab[h], (unsigned long long)kEmpty, word);
                 if (old == kEmpty) break;
-                if ((old >> kTBits) == p) {
+                if ((old >> kTlBits) == c) {
                     if (word < old) atomicMin(&tab[h], word);
                     break;
                 }
-                h = (h + 1u) & mask;
+                h = (h + 1u) & (kTabSlots - 1);
             }
         }
-        cflag[i] = f;
-    }
-}
-
-// accepted[i] = candidate i is free and the first (smallest index) to name its cell
-__global__ void accept_kernel(const uint64_t* __restrict__ cpos, int64_t T, uint64_t N,
-                              const int32_t* __restrict__ cflag, const unsigned long long* __restrict__ tab,
-                              int32_t* __restrict__ accepted)
-{
-    const uint32_t mask = (1u << kHashBits) - 1u;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t p = cpos[i];
-        int32_t a = 0;
-        if (p < N) {
-            if (!cflag[i]) {
-                a = 1;
-            } else {
-                uint32_t h = hash_slot(p);
-                for (uint32_t probe = 0; probe <= mask; ++probe) {
-                    const unsigned long long w = tab[h];
-                    if (w == kEmpty) break;
-                    if ((w >> kTBits) == p) {
-                        a = (w & ((1ull << kTBits) - 1ull)) == (uint64_t)i ? 1 : 0;
-                        break;
+        __syncthreads();
+        // a cell is in the table exactly when it was free; only now do bits change
+        for (int32_t k = threadIdx.x; k < n; k += kClaimThreads) {
+            const uint64_t x = e[k];
+            const uint32_t cell = (uint32_t)x;
+            if ((cell >> sb) != (uint32_t)p) continue;
+            const uint32_t c = cell & cmask;
+            const uint64_t tl = x >> 32;
+            uint32_t h = tab_slot(c);
+            for (int probe = 0; probe < kTabSlots; ++probe) {
+                const unsigned long long w = tab[h];
+                if (w == kEmpty) break;
+                if ((w >> kTlBits) == c) {
+                    if ((w & ((1ull << kTlBits) - 1ull)) == tl) {
+                        acc8[tl] = 1;
+                        atomicOr(&bm[c >> 5], 1u << (c & 31));
                     }
-                    h = (h + 1u) & mask;
+                    break;
                 }
+                h = (h + 1u) & (kTabSlots - 1);
             }
         }
-        accepted[i] = a;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nw; i += kClaimThreads) occ_bm[w0 + i] = bm[i];
+        __syncthreads();
     }
 }
 
-// Accepted candidates past the first `need` give their cell back; contested
-// marks are cleared so the next batch starts from an empty contested map.
-__global__ void finish_kernel(const uint64_t* __restrict__ cpos, int64_t T, const int32_t* __restrict__ accepted,
-                              const int32_t* __restrict__ trank, const int32_t* __restrict__ cflag, int64_t need,
-                              uint32_t* __restrict__ occ_bm, uint32_t* __restrict__ con_bm)
+// accepted candidates per tile of kSumTile indices (flags are 0/1 bytes)
+__global__ void __launch_bounds__(256) tile_sum_kernel(const uint8_t* __restrict__ acc8, int64_t T,
+                                                       int32_t* __restrict__ tsum, const uint32_t* __restrict__ state)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        const bool give_back = accepted[i] && (int64_t)trank[i] >= need;
-        const bool contested = cflag[i] != 0;
-        if (!give_back && !contested) continue;
-        const uint64_t p = cpos[i];
-        const uint32_t bit = 1u << (p & 31);
-        if (give_back) atomicAnd(&occ_bm[p >> 5], ~bit);
-        if (contested) atomicAnd(&con_bm[p >> 5], ~bit);
+    __shared__ int32_t red[256 / kWave];
+    if (state[kStOverflow]) return;
+    const int64_t b0 = (int64_t)blockIdx.x * kSumTile;
+    const int64_t b1 = b0 + kSumTile < T ? b0 + kSumTile : T;
+    int32_t c = 0;
+    for (int64_t i = b0 + 4 * threadIdx.x; i < b1; i += 4 * 256) {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(acc8 + i);
+        if (i + 4 > b1) w &= (1u << (8 * (b1 - i))) - 1u;
+        c += __popc(w);
     }
+    c = wave_sum(c);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+        for (int i = 0; i < 256 / kWave; ++i) t += red[i];
+        tsum[blockIdx.x] = t;
+    }
+}
+
+__device__ inline int32_t block_incl_1024(int32_t v, int32_t* smem /*[16]*/)
+{
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int32_t inc = wave_incl(v);
+    if (lane == kWave - 1) smem[w] = inc;
+    __syncthreads();
+    int32_t base = 0;
+    for (int i = 0; i < w; ++i) base += smem[i];
+    __syncthreads();
+    return base + inc;
+}
+
+// The first `need` accepted candidates in index order are taken: state[kStCut]
+// is one past the last one taken (T when every accepted one is), state[kStTaken]
+// how many were taken.
+__global__ void __launch_bounds__(1024) cut_kernel(const int32_t* __restrict__ tsum, int32_t ntiles,
+                                                   const uint8_t* __restrict__ acc8, int64_t T, int64_t need,
+                                                   uint32_t* __restrict__ state)
+{
+    __shared__ int32_t smem[1024 / kWave];
+    __shared__ int32_t s_j, s_q, s_cut;
+    if (state[kStOverflow]) {
+        if (threadIdx.x == 0) state[kStTaken] = 0u;
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int32_t v = tid < ntiles ? tsum[tid] : 0;
+    const int32_t inc = block_incl_1024(v, smem);
+    if (tid == 0) s_j = -1;
+    __syncthreads();
+    // the tile where the running count first reaches need
+    if (tid < ntiles && (int64_t)inc >= need && (int64_t)(inc - v) < need) {
+        s_j = tid;
+        s_q = (int32_t)(need - (inc - v));
+    }
+    __syncthreads();
+    const int32_t j = s_j;
+    if (j < 0) {   // fewer than need accepted: take them all
+        if (tid == 1023) {
+            state[kStTaken] = (uint32_t)inc;
+            state[kStCut] = (uint32_t)T;
+        }
+        return;
+    }
+    // the q-th accepted flag of tile j; each thread reads eight consecutive flags
+    const int32_t q = s_q;
+    const int64_t b0 = (int64_t)j * kSumTile;
+    const int64_t lo = b0 + 8 * tid;
+    uint8_t f[8];
+    int32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        f[u] = lo + u < T ? acc8[lo + u] : 0;
+        cnt += f[u];
+    }
+    const int32_t ci = block_incl_1024(cnt, smem);
+    if (ci >= q && ci - cnt < q) {
+        int32_t k = ci - cnt;
+        for (int u = 0; u < 8; ++u) {
+            k += f[u];
+            if (f[u] && k == q) {
+                s_cut = (int32_t)(lo + u + 1);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        state[kStTaken] = (uint32_t)need;
+        state[kStCut] = (uint32_t)s_cut;
+    }
+}
+
+// accepted candidates at or past the cut give their cell back (few: the batch
+// is sized to overshoot need only slightly)
+__global__ void give_back_kernel(uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N,
+                                 const uint8_t* __restrict__ acc8, uint32_t* __restrict__ occ_bm,
+                                 const uint32_t* __restrict__ state)
+{
+    if (state[kStOverflow]) return;
+    const int64_t cut = (int64_t)state[kStCut];
+    for (int64_t i = cut + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
+        if (!acc8[i]) continue;
+        const uint64_t p = candidate_pos(seed, epoch, t0 + (uint64_t)i, N);
+        atomicAnd(&occ_bm[p >> 5], ~(1u << (p & 31)));
+    }
+}
+
+struct GrowPlan {
+    int rb, sb;
+    int32_t R, cap;
+};
+
+// Regions hold about 2048 candidates (at most kMaxRegions regions); the bucket
+// capacity is the mean plus eight standard deviations plus 64.
+GrowPlan grow_plan(uint64_t N, int64_t T)
+{
+    GrowPlan g;
+    int rb = 5;
+    while (rb < kSubBits && ((uint64_t)T << (rb + 1)) <= 2048ull * N) ++rb;
+    auto regions = [&](int b) { return (N + (1ull << b) - 1) >> b; };
+    while (regions(rb) > (uint64_t)kMaxRegions) ++rb;
+    g.rb = rb;
+    g.sb = rb < kSubBits ? rb : kSubBits;
+    g.R = (int32_t)regions(rb);
+    const double mu = (double)T * (double)(1ull << rb) / (double)N;
+    const double c = std::ceil(mu + 8.0 * std::sqrt(mu) + 64.0);
+    g.cap = c >= (double)T ? (int32_t)T : (int32_t)c;
+    return g;
+}
+
+// bucket entries any batch of at most `tmax` candidates can need: R * cap <=
+// 2T + 8 sqrt(R * R mu) + 65 R with R mu <= 2T and R <= kMaxRegions
+int64_t bucket_bound(uint64_t N, int64_t tmax)
+{
+    const double rmax = (double)std::min<uint64_t>((uint64_t)kMaxRegions, (N + 31) / 32);
+    const double b = 2.0 * (double)tmax + 8.0 * std::sqrt(rmax * 2.0 * (double)tmax) + 65.0 * rmax + 1024.0;
+    return (int64_t)std::ceil(b);
 }
 
 // ---- rebuild the canonical arrays from the bitmaps ---------------------------
@@ -446,24 +660,6 @@ constexpr int kEmitThreads = 256;
 constexpr int kEmitSweeps = 8;
 constexpr int64_t kEmitUnit = (int64_t)kWave * kEmitSweeps;   // words per wavefront
 constexpr int64_t kEmitDirect = 16384;
-
-__device__ inline int32_t wave_incl(int32_t v)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
-__device__ inline int32_t wave_sum(int32_t v)
-{
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
 
 __global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint32_t* __restrict__ occ_bm,
                                                                       const uint32_t* __restrict__ old_bm,
@@ -586,23 +782,20 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
 
 struct PruneScratch {
     uint32_t* state;    // [16]
-    int32_t* count;     // [4]
     uint32_t* hist;     // [256] selection histogram
     int32_t* tile_eq;   // [keep tiles] keys equal to T per tile (then their scan)
     float* vcopy;       // [nnz] the values before the rebuild
     uint32_t* kept_bm;  // [words]
     uint32_t* occ_bm;   // [words]
     uint32_t* old_bm;   // [words] cells of the entries before the drop
-    uint32_t* con_bm;   // [words] contested cells of the current batch
     int32_t* occ_cnt;   // [units] occupied bits per emit unit (then their scan)
     int32_t* old_cnt;   // [units] old bits per emit unit
-    uint64_t* cpos;     // [Tm]
-    int32_t* acc;       // [Tm]
-    int32_t* trank;     // [Tm]
-    int32_t* cflag;     // [Tm] candidate names a contested cell
-    unsigned long long* tab;   // [2^kHashBits]
+    uint8_t* acc8;      // [tmax] accepted flag per candidate of the batch
+    int32_t* tsum;      // [tmax / kSumTile] accepted per tile
+    int32_t* fill;      // [kMaxRegions] bucket fill per region
+    uint64_t* bucket;   // [nbucket] candidates grouped by region
     void* scan;         // scan scratch
-    int64_t tmax, words, units, ktiles;
+    int64_t tmax, words, units, ktiles, nbucket;
 };
 
 int64_t batch_cap(const snack_layer* L)
@@ -621,47 +814,42 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t units = (words + kEmitUnit - 1) / kEmitUnit;
     const int64_t ktiles = (n + kKeepTile - 1) / kKeepTile;
     const int64_t tm = batch_cap(L);
-    const int64_t H = (int64_t)1 << kHashBits;
-    int64_t sn = tm > units ? tm : units;
-    if (ktiles > sn) sn = ktiles;
+    const int64_t nb = bucket_bound(N, tm);
+    int64_t sn = units > ktiles ? units : ktiles;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
         off += al(bytes);
         return o;
     };
-    size_t o_state = take(16 * 4), o_count = take(16), o_hist = take((size_t)256 * 4);
+    size_t o_state = take(16 * 4), o_hist = take((size_t)256 * 4);
     size_t o_teq = take((size_t)ktiles * 4), o_vc = take((size_t)n * 4);
     size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_dbm = take((size_t)words * 4);
-    size_t o_cbm = take((size_t)words * 4);
     size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
-    size_t o_cpos = take((size_t)tm * 8), o_acc = take((size_t)tm * 4), o_trank = take((size_t)tm * 4);
-    size_t o_cflag = take((size_t)tm * 4);
-    size_t o_tab = take((size_t)H * 8);
+    size_t o_acc = take((size_t)tm + 8), o_tsum = take((size_t)(tm / kSumTile + 1) * 4);
+    size_t o_fill = take((size_t)kMaxRegions * 4), o_bucket = take((size_t)nb * 8);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
         char* base = (char*)L->scratch;
         ps->state = (uint32_t*)(base + o_state);
-        ps->count = (int32_t*)(base + o_count);
         ps->hist = (uint32_t*)(base + o_hist);
         ps->tile_eq = (int32_t*)(base + o_teq);
         ps->vcopy = (float*)(base + o_vc);
         ps->kept_bm = (uint32_t*)(base + o_kbm);
         ps->occ_bm = (uint32_t*)(base + o_obm);
         ps->old_bm = (uint32_t*)(base + o_dbm);
-        ps->con_bm = (uint32_t*)(base + o_cbm);
         ps->occ_cnt = (int32_t*)(base + o_oc);
         ps->old_cnt = (int32_t*)(base + o_dc);
-        ps->cpos = (uint64_t*)(base + o_cpos);
-        ps->acc = (int32_t*)(base + o_acc);
-        ps->trank = (int32_t*)(base + o_trank);
-        ps->cflag = (int32_t*)(base + o_cflag);
-        ps->tab = (unsigned long long*)(base + o_tab);
+        ps->acc8 = (uint8_t*)(base + o_acc);
+        ps->tsum = (int32_t*)(base + o_tsum);
+        ps->fill = (int32_t*)(base + o_fill);
+        ps->bucket = (uint64_t*)(base + o_bucket);
         ps->scan = base + o_scan;
         ps->tmax = tm;
         ps->words = words;
         ps->units = units;
         ps->ktiles = ktiles;
+        ps->nbucket = nb;
     }
     return off + 256;
 }
@@ -691,7 +879,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
 
     // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
     {
-        const uint32_t init[3] = {0u, (uint32_t)(n_drop - 1), 0u};
+        const uint32_t init[16] = {0u, (uint32_t)(n_drop - 1), 0u};
         SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
         int nblk = (int)grid_for(nnz);
         if (nblk > kSelBlocks) nblk = kSelBlocks;
@@ -704,8 +892,8 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         SNACK_HIP(hipGetLastError());
         hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->vals, nnz,
                            ps.state, ps.tile_eq);
-        hipLaunchKernelGGL(zero4_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.occ_bm,
-                           ps.old_bm, ps.con_bm, ps.words);
+        hipLaunchKernelGGL(zero_bitmaps_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm,
+                           ps.occ_bm, ps.old_bm, ps.words, ps.fill, kMaxRegions);
         SNACK_HIP(hipGetLastError());
         if (ps.ktiles <= kKeepDirect) {
             hipLaunchKernelGGL(keep_tiles_kernel<true>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
@@ -726,33 +914,43 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     int64_t got = 0;
     uint64_t t0 = 0;
     int batches = 0;
-    const int64_t H = (int64_t)1 << kHashBits;
+    int shrink = 0;   // halvings of the batch after a bucket overflow
+    const uint64_t words_total = (uint64_t)ps.words;
     while (need > 0) {
         const double p_empty = (double)(N - (uint64_t)kept - (uint64_t)got) / (double)N;
         double want = (double)need / (p_empty > 1e-9 ? p_empty : 1e-9) * 1.03 + 4096.0;
         int64_t T = want > (double)ps.tmax ? ps.tmax : (int64_t)want;
+        T >>= shrink;
         if (T < 1) T = 1;
-        hipLaunchKernelGGL(gen_candidates_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, L->seed, L->epoch, t0, T, N,
-                           ps.occ_bm, ps.cpos);
-        hipLaunchKernelGGL(hash_clear_kernel, dim3(grid_for(H)), dim3(kThreads), 0, s, ps.tab, H);
-        hipLaunchKernelGGL(claim_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.occ_bm, ps.con_bm);
-        hipLaunchKernelGGL(contest_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.con_bm, ps.tab,
-                           ps.cflag);
-        hipLaunchKernelGGL(accept_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, N, ps.cflag, ps.tab,
-                           ps.acc);
+        const GrowPlan g = grow_plan(N, T);
+        const size_t lds = (size_t)kTabSlots * 8 + ((size_t)1 << g.sb) / 8;
+        if ((int64_t)g.R * g.cap > ps.nbucket || lds > (size_t)L->lds_bytes) return SNACK_ERR_UNSUPPORTED;
+        const unsigned ntiles = (unsigned)((T + kGenTile - 1) / kGenTile);
+        const int32_t nsum = (int32_t)((T + kSumTile - 1) / kSumTile);
+        hipLaunchKernelGGL(gen_bucket_kernel, dim3(ntiles), dim3(kGenThreads), 0, s, L->seed, L->epoch, t0, T, N,
+                           g.rb, g.R, g.cap, ps.fill, ps.bucket, ps.acc8, ps.state);
+        hipLaunchKernelGGL(region_claim_kernel, dim3((unsigned)g.R), dim3(kClaimThreads), lds, s, g.rb, g.sb,
+                           words_total, g.cap, ps.fill, ps.bucket, ps.occ_bm, ps.acc8, ps.state);
+        hipLaunchKernelGGL(tile_sum_kernel, dim3((unsigned)nsum), dim3(256), 0, s, ps.acc8, T, ps.tsum, ps.state);
+        hipLaunchKernelGGL(cut_kernel, dim3(1), dim3(1024), 0, s, ps.tsum, nsum, ps.acc8, T, need, ps.state);
+        hipLaunchKernelGGL(give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kThreads), 0, s,
+                           L->seed, L->epoch, t0, T, N, ps.acc8, ps.occ_bm, ps.state);
         SNACK_HIP(hipGetLastError());
-        SNACK_CHECK(exclusive_scan_i32(ps.acc, ps.trank, T, ps.count, ps.scan, s));
-        hipLaunchKernelGGL(finish_kernel, dim3(grid_for(T)), dim3(kThreads), 0, s, ps.cpos, T, ps.acc, ps.trank,
-                           ps.cflag, need, ps.occ_bm, ps.con_bm);
-        SNACK_HIP(hipGetLastError());
-        int32_t total = 0;
-        SNACK_HIP(hipMemcpyAsync(&total, ps.count, 4, hipMemcpyDeviceToHost, s));
+        uint32_t res[2] = {0u, 0u};   // overflow flag, taken
+        SNACK_HIP(hipMemcpyAsync(res, ps.state + kStOverflow, sizeof res, hipMemcpyDeviceToHost, s));
         SNACK_HIP(hipStreamSynchronize(s));
-        const int64_t accepted = total < need ? total : need;
-        got += accepted;
-        need -= accepted;
-        t0 += (uint64_t)T;
         if (++batches > 100000) return SNACK_ERR_UNSUPPORTED;
+        if (res[0]) {   // nothing was changed: take the same candidates in a smaller batch
+            hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.state + kStOverflow, (int64_t)1, 0u);
+            SNACK_HIP(hipGetLastError());
+            ++shrink;
+            continue;
+        }
+        shrink = 0;
+        const int64_t taken = (int64_t)res[1];
+        got += taken;
+        need -= taken;
+        t0 += (uint64_t)T;
     }
 
     // ---- new canonical arrays: set bits of occ in ascending position ----

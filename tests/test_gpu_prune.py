@@ -57,3 +57,9 @@ def test_prune_ties_signed_zero_nan():
 def test_prune_full_scale_10000_square():
     # 10000 x 10000 at 95 %: drop 30 % of 5,000,000 twice (two epochs)
     _run(10000, 10000, 5_000_000, (0.3,), "gpu/prune/c4", rounds=2)
+
+
+def test_prune_regions_wider_than_one_pass():
+    # 50000 x 50000 = 2.5e9 cells: the grow step's regions are wider than one
+    # LDS pass, so each is claimed in several; the column view takes the sort path
+    _run(50000, 50000, 200_000, (0.3, 0.7), "gpu/prune/wide")
