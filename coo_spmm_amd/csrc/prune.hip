@@ -36,7 +36,6 @@ constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr int64_t kMaxBatch = 1 << 21;          // candidates per batch
 constexpr uint64_t kEmpty = ~0ull;              // empty table word
 constexpr uint64_t kMaxBitmapBits = 1ull << 34;
-constexpr int kSelBlocks = 512;                  // workgroups of one selection pass
 
 
 inline unsigned grid_for(int64_t n)
@@ -79,23 +78,47 @@ __device__ inline int32_t wave_sum(int32_t v)
 // ---- drop: radix select ---------------------------------------------------
 // state: [0] prefix, [1] rank still to find among keys matching the prefix,
 // [2] number of keys equal to the final prefix (set by the last pass).
-// A thread adds runs of equal digits before touching LDS, which keeps the
-// first passes (where nearly every key shares a digit) free of contention;
-// each workgroup then adds its nonzero bins to the global histogram.
-__global__ void __launch_bounds__(kThreads) sel_hist_kernel(const float* __restrict__ vals, int64_t n,
-                                                            const uint32_t* __restrict__ state, int shift,
-                                                            uint32_t* __restrict__ hist)
+// Each thread takes sixteen consecutive keys (four 16-byte loads) and adds runs
+// of equal digits before touching LDS, which keeps the first passes (where
+// nearly every key shares a digit) free of contention; each workgroup adds its
+// nonzero bins to one of kSelCopies global histograms.
+constexpr int kSelThreads = 256;
+constexpr int kSelPer = 16;
+constexpr int kSelCopies = 32;   // histogram copies
+
+__global__ void __launch_bounds__(kSelThreads) sel_pass_kernel(const float* __restrict__ vals, int64_t n,
+                                                               uint32_t* __restrict__ state, int shift,
+                                                               uint32_t* __restrict__ hist)
 {
     __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
+    const int tid = threadIdx.x;
+    h[tid] = 0;
     __syncthreads();
     const uint32_t prefix = state[0];
     const uint32_t hi_mask = (shift >= 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const int64_t k0 = ((int64_t)blockIdx.x * kSelThreads + tid) * kSelPer;
+    uint32_t key[kSelPer];
+    if (k0 + kSelPer <= n) {
+#pragma unroll
+        for (int q = 0; q < kSelPer / 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4*>(vals + k0 + 4 * q);
+            key[4 * q] = mag_bits(f.x);
+            key[4 * q + 1] = mag_bits(f.y);
+            key[4 * q + 2] = mag_bits(f.z);
+            key[4 * q + 3] = mag_bits(f.w);
+        }
+    } else {
+        // past the end: a key whose high bits never match the prefix
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) key[u] = k0 + u < n ? mag_bits(vals[k0 + u]) : ~prefix;
+    }
+    const bool all_match = hi_mask == 0u;
     uint32_t run_d = 0, run = 0;
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-        const uint32_t key = mag_bits(vals[k]);
-        if ((key & hi_mask) != (prefix & hi_mask)) continue;
-        const uint32_t d = (key >> shift) & 255u;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        if (!all_match && (key[u] & hi_mask) != (prefix & hi_mask)) continue;
+        if (all_match && k0 + u >= n) continue;
+        const uint32_t d = (key[u] >> shift) & 255u;
         if (d != run_d && run) {
             atomicAdd(&h[run_d], run);
             run = 0;
@@ -105,17 +128,22 @@ __global__ void __launch_bounds__(kThreads) sel_hist_kernel(const float* __restr
     }
     if (run) atomicAdd(&h[run_d], run);
     __syncthreads();
-    if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
+    // atomics on one address are serialised: spread them over kSelCopies copies
+    if (h[tid]) atomicAdd(&hist[(blockIdx.x % kSelCopies) * 256 + tid], h[tid]);
 }
 
-// picks the digit holding the wanted rank, then clears the histogram for the next pass
+// picks the digit holding the wanted rank, then clears the histograms for the next pass
 __global__ void __launch_bounds__(256) sel_pick_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ state,
                                                        int shift)
 {
     __shared__ uint32_t tot[256];
-    tot[threadIdx.x] = hist[threadIdx.x];
+    uint32_t t = 0;
+    for (int c = 0; c < kSelCopies; ++c) {
+        t += hist[c * 256 + threadIdx.x];
+        hist[c * 256 + threadIdx.x] = 0u;
+    }
+    tot[threadIdx.x] = t;
     __syncthreads();
-    hist[threadIdx.x] = 0;
     if (threadIdx.x == 0) {
         uint32_t r = state[1];
         uint32_t dg = 0;
@@ -782,7 +810,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
 
 struct PruneScratch {
     uint32_t* state;    // [16]
-    uint32_t* hist;     // [256] selection histogram
+    uint32_t* hist;     // [kSelCopies * 256] selection histograms
     int32_t* tile_eq;   // [keep tiles] keys equal to T per tile (then their scan)
     float* vcopy;       // [nnz] the values before the rebuild
     uint32_t* kept_bm;  // [words]
@@ -822,7 +850,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         off += al(bytes);
         return o;
     };
-    size_t o_state = take(16 * 4), o_hist = take((size_t)256 * 4);
+    size_t o_state = take(16 * 4), o_hist = take((size_t)kSelCopies * 256 * 4);
     size_t o_teq = take((size_t)ktiles * 4), o_vc = take((size_t)n * 4);
     size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_dbm = take((size_t)words * 4);
     size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
@@ -881,11 +909,11 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     {
         const uint32_t init[16] = {0u, (uint32_t)(n_drop - 1), 0u};
         SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
-        int nblk = (int)grid_for(nnz);
-        if (nblk > kSelBlocks) nblk = kSelBlocks;
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.hist, (int64_t)256, 0u);
+        const unsigned nsel = (unsigned)((nnz + (int64_t)kSelThreads * kSelPer - 1) / ((int64_t)kSelThreads * kSelPer));
+        hipLaunchKernelGGL(fill_u32_kernel, dim3(8), dim3(kThreads), 0, s, ps.hist,
+                           (int64_t)kSelCopies * 256, 0u);
         for (int shift = 24; shift >= 0; shift -= 8) {
-            hipLaunchKernelGGL(sel_hist_kernel, dim3(nblk), dim3(kThreads), 0, s, L->vals, nnz, ps.state, shift,
+            hipLaunchKernelGGL(sel_pass_kernel, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, shift,
                                ps.hist);
             hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(256), 0, s, ps.hist, ps.state, shift);
         }
