@@ -436,6 +436,11 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
             SNACK_HIP(hipGetLastError());
         }
     }
+    return canon_index_tail(L, s);
+}
+
+snack_status canon_index_tail(snack_layer* L, hipStream_t s)
+{
     L->vals_t_stale = false;
     for (int i = 0; i < kTileWidths; ++i) {
         L->fwd.split[i].valid = false;

@@ -175,6 +175,9 @@ snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t
 // Given canonical rows/cols/vals, build row_ptr, the transposed view, vals_t,
 // and both work partitions.
 snack_status canon_build_index(snack_layer* L, hipStream_t s);
+// The part of canon_build_index after row_ptr and the transposed view exist
+// (for callers that build those themselves): partitions of both views, flags.
+snack_status canon_index_tail(snack_layer* L, hipStream_t s);
 // vals_t[iperm[k]] = vals[k]
 snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
 // perm[iperm[k]] = k: the transposed slot -> canonical slot map, into a caller buffer

@@ -683,7 +683,8 @@ int64_t bucket_bound(uint64_t N, int64_t tmax)
 // prefix -- summed from the unit counts before it when there are few units,
 // else read from their scans -- and, per sweep, turns the lanes' counts into
 // slots with a wavefront scan: an occupied cell goes to the next slot; a kept
-// cell takes the value the old entry at its old rank had.
+// cell takes the value the old entry at its old rank had.  With `wpre` it also
+// stores every word's first slot (the set bits of `occ` before the word).
 constexpr int kEmitThreads = 256;
 constexpr int kEmitSweeps = 8;
 constexpr int64_t kEmitUnit = (int64_t)kWave * kEmitSweeps;   // words per wavefront
@@ -719,7 +720,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, const uint32_t* __restrict__ old_bm,
     int64_t words, int64_t units, const int32_t* __restrict__ occ_cnt, const int32_t* __restrict__ old_cnt,
     const float* __restrict__ vold, int64_t nnz, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
-    float* __restrict__ vals)
+    float* __restrict__ vals, int32_t* __restrict__ wpre)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
@@ -775,6 +776,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         const int64_t oldbase = run_d + ib - b;
         run_o += __shfl(ia, kWave - 1, kWave);
         run_d += __shfl(ib, kWave - 1, kWave);
+        if (wpre && w < words) wpre[w] = (int32_t)out;
         if (!om) continue;
         int64_t r, c;
         if constexpr (WIDE) {
@@ -808,6 +810,342 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     }
 }
 
+// ---- the column view from the new bitmap -----------------------------------
+// The cells in tiles of 256 rows x 256 columns.  A tile's bits go to LDS row by
+// row; ballots turn them into column words.  Pass 1 counts each column's entries
+// per row block (and writes row_ptr from the word prefixes); after a scan of
+// those counts down each column and across the column totals, pass 2 walks each
+// column's bits in row order: an entry's transposed slot is its column's start
+// in this row block plus its rank there, its canonical slot the word prefix of
+// its row plus the bits before it.  A column's entries of one tile are written
+// as one contiguous run, and the tiles of one column band are dispatched to one
+// XCD, so the runs of neighbouring row blocks meet in the same L2.
+constexpr int kCvDim = 256;              // rows and columns of a tile
+constexpr int kCvWords = kCvDim / 32;    // bitmap words of a tile row
+constexpr int kCvPad = kCvWords + 1;     // LDS row stride (spreads the banks)
+constexpr int kCvThreads = 256;
+constexpr int kXcds = 8;
+
+struct CvTileShape {
+    int32_t r0, c0, nrows, ncols;
+};
+
+__device__ inline CvTileShape cv_shape(int32_t bi, int32_t bj, int32_t M, int32_t K)
+{
+    CvTileShape t;
+    t.r0 = bi * kCvDim;
+    t.c0 = bj * kCvDim;
+    t.nrows = M - t.r0 < kCvDim ? M - t.r0 : kCvDim;
+    t.ncols = K - t.c0 < kCvDim ? K - t.c0 : kCvDim;
+    return t;
+}
+
+// Tile of a workgroup: XCD x (workgroups are dealt to the XCDs in turn) owns
+// the column bands [x * per, (x + 1) * per) and walks them row block by row
+// block, so the bands that share bitmap lines, and the runs that neighbouring
+// row blocks write into one column, meet in the same L2.  False past the grid.
+__device__ inline bool cv_tile_of(int32_t nbi, int32_t nbj, int32_t& bi, int32_t& bj)
+{
+    const int32_t per = (nbj + kXcds - 1) / kXcds;
+    const int32_t xcd = (int32_t)(blockIdx.x % kXcds), slot = (int32_t)(blockIdx.x / kXcds);
+    bi = slot / per;
+    bj = xcd * per + slot % per;
+    return bi < nbi && bj < nbj;
+}
+
+// the tile's bits, row-major: rowbits[rr * kCvPad + i] holds columns c0+32i .. c0+32i+31
+__device__ inline void cv_load_rows(const uint32_t* __restrict__ occ_bm, uint64_t words, int32_t K,
+                                    const CvTileShape& t, uint32_t* rowbits)
+{
+#pragma unroll
+    for (int n = 0; n < kCvDim * kCvWords / kCvThreads; ++n) {
+        const int q = threadIdx.x + n * kCvThreads;
+        const int rr = q / kCvWords, i = q % kCvWords;
+        uint32_t x = 0u;
+        const int32_t cb = 32 * i;
+        if (rr < t.nrows && cb < t.ncols) {
+            const uint64_t cell = (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + cb);
+            const uint64_t w = cell >> 5;
+            const int sh = (int)(cell & 31);
+            const uint32_t lo = occ_bm[w];
+            const uint32_t hi = (sh && w + 1 < words) ? occ_bm[w + 1] : 0u;
+            x = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+            const int32_t valid = t.ncols - cb;
+            if (valid < 32) x &= (1u << valid) - 1u;
+        }
+        rowbits[rr * kCvPad + i] = x;
+    }
+}
+
+// column words: colbits[c * kCvPad + j] holds rows 32j .. 32j+31 of column c
+__device__ inline void cv_transpose(const uint32_t* rowbits, uint32_t* colbits)
+{
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int i = 0; i < kCvWords; ++i) {
+        const uint32_t x = rowbits[(wv * kWave + lane) * kCvPad + i];
+        uint64_t mine = 0;
+#pragma unroll
+        for (int b = 0; b < 32; ++b) {
+            const uint64_t m = __ballot((x >> b) & 1u);
+            if (lane == b) mine = m;
+        }
+        if (lane < 32) {
+            colbits[(32 * i + lane) * kCvPad + 2 * wv] = (uint32_t)mine;
+            colbits[(32 * i + lane) * kCvPad + 2 * wv + 1] = (uint32_t)(mine >> 32);
+        }
+    }
+}
+
+// the first canonical slot at or after `cell`: word prefix plus the bits before it
+__device__ inline int32_t cv_slot_at(const uint32_t* __restrict__ occ_bm, const int32_t* __restrict__ wpre,
+                                     uint64_t cell)
+{
+    const uint64_t w = cell >> 5;
+    const int sh = (int)(cell & 31);
+    return wpre[w] + (sh ? __popc(occ_bm[w] & ((1u << sh) - 1u)) : 0);
+}
+
+__global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __restrict__ occ_bm, uint64_t words,
+                                                              const int32_t* __restrict__ wpre, int32_t M, int32_t K,
+                                                              int32_t nbi, int32_t nbj, int64_t nnz, int32_t* __restrict__ cnt,
+                                                              int32_t* __restrict__ row_ptr,
+                                                              int32_t* __restrict__ col_ptr)
+{
+    __shared__ uint32_t rowbits[kCvDim * kCvPad];
+    __shared__ int32_t colcnt[kCvDim];
+    int32_t bi, bj;
+    if (!cv_tile_of(nbi, nbj, bi, bj)) return;
+    const CvTileShape t = cv_shape(bi, bj, M, K);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    colcnt[tid] = 0;
+    if (bj == 0 && tid < t.nrows) row_ptr[t.r0 + tid] = cv_slot_at(occ_bm, wpre, (uint64_t)(t.r0 + tid) * (uint64_t)K);
+    if (bi == 0 && bj == 0 && tid == 0) {
+        row_ptr[M] = (int32_t)nnz;
+        col_ptr[K] = (int32_t)nnz;
+    }
+    cv_load_rows(occ_bm, words, K, t, rowbits);
+    __syncthreads();
+    for (int i = 0; i < kCvWords; ++i) {
+        const uint32_t x = rowbits[(wv * kWave + lane) * kCvPad + i];
+        int32_t mine = 0;
+#pragma unroll
+        for (int b = 0; b < 32; ++b) {
+            const int32_t c = __popcll(__ballot((x >> b) & 1u));
+            if (lane == b) mine = c;
+        }
+        if (lane < 32 && mine) atomicAdd(&colcnt[32 * i + lane], mine);
+    }
+    __syncthreads();
+    if (tid < t.ncols) cnt[(int64_t)bi * K + t.c0 + tid] = colcnt[tid];
+}
+
+// down each column: counts -> exclusive prefix over the row blocks; totals out
+__global__ void cv_column_scan_kernel(int32_t* __restrict__ cnt, int32_t nbi, int32_t K, int32_t* __restrict__ tot)
+{
+    constexpr int kBatch = 16;   // loads in flight per thread
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= K) return;
+    int32_t run = 0;
+    for (int32_t b0 = 0; b0 < nbi; b0 += kBatch) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) v[u] = b0 + u < nbi ? cnt[(int64_t)(b0 + u) * K + c] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (b0 + u < nbi) cnt[(int64_t)(b0 + u) * K + c] = run;
+            run += v[u];
+        }
+    }
+    tot[c] = run;
+}
+
+// last index i in [0, n) with a[i] <= x (a ascending, a[0] <= x)
+__device__ inline int32_t cv_last_le(const int32_t* a, int32_t n, int32_t x)
+{
+    int32_t lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (a[mid] <= x) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int kCvScatterThreads = 1024;
+constexpr int32_t kCvStage = 4096;   // tile entries handled through LDS lists
+
+// One tile per workgroup.  Entries are numbered twice inside the tile: x in
+// row order (a row's entries are consecutive canonical slots, starting at
+// rowk) and e in column order (a column's entries are consecutive transposed
+// slots, starting at colbase).  Bit walks over the tile's words fill LDS lists
+// (row of x; row-order index and column of e), after which every pass over
+// the entries is striped across the threads: values are read and iperm
+// written as row runs, rows_t and vals_t written as column runs.  A tile with
+// more than kCvStage entries finds each entry's column by binary search and
+// reads and writes global memory directly.
+__global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
+    const uint32_t* __restrict__ occ_bm, uint64_t words, const int32_t* __restrict__ wpre, int32_t M, int32_t K,
+    int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ col_ptr,
+    const float* __restrict__ vals, int32_t* __restrict__ rows_t, float* __restrict__ vals_t,
+    int32_t* __restrict__ iperm)
+{
+    constexpr int W = kCvScatterThreads / kWave;
+    __shared__ uint32_t rowbits[kCvDim * kCvPad];
+    __shared__ uint32_t colbits[kCvDim * kCvPad];
+    __shared__ uint8_t rwp[kCvDim * kCvWords];    // entries of a row before each of its words
+    __shared__ uint8_t cwp[kCvDim * kCvWords];    // entries of a column before each of its words
+    __shared__ int32_t rowk[kCvDim];              // canonical slot of a row's first entry in the tile
+    __shared__ int32_t rowoff[kCvDim + 1];        // x of a row's first entry
+    __shared__ int32_t colstart[kCvDim + 1];      // e of a column's first entry
+    __shared__ int32_t colbase[kCvDim];           // transposed slot of a column's first entry
+    __shared__ uint8_t xrow[kCvStage];
+    __shared__ uint16_t eloc[kCvStage];
+    __shared__ uint8_t ecol[kCvStage];
+    __shared__ float sval[kCvStage];
+    __shared__ int32_t sslot[kCvStage];
+    __shared__ int32_t red[2][kCvDim / kWave];
+    int32_t bi, bj;
+    if (!cv_tile_of(nbi, nbj, bi, bj)) return;
+    const CvTileShape t = cv_shape(bi, bj, M, K);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+
+    // rows, as in cv_load_rows, two words per thread
+#pragma unroll
+    for (int n = 0; n < kCvDim * kCvWords / kCvScatterThreads; ++n) {
+        const int q = tid + n * kCvScatterThreads;
+        const int rr = q / kCvWords, i = q % kCvWords;
+        uint32_t x = 0u;
+        const int32_t cb = 32 * i;
+        if (rr < t.nrows && cb < t.ncols) {
+            const uint64_t cell = (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + cb);
+            const uint64_t w = cell >> 5;
+            const int sh = (int)(cell & 31);
+            const uint32_t lo = occ_bm[w];
+            const uint32_t hi = (sh && w + 1 < words) ? occ_bm[w + 1] : 0u;
+            x = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+            const int32_t valid = t.ncols - cb;
+            if (valid < 32) x &= (1u << valid) - 1u;
+        }
+        rowbits[rr * kCvPad + i] = x;
+    }
+    if (tid < kCvDim) {
+        colbase[tid] = tid < t.ncols ? col_ptr[t.c0 + tid] + cnt[(int64_t)bi * K + t.c0 + tid] : 0;
+        rowk[tid] = tid < t.nrows ? cv_slot_at(occ_bm, wpre, (uint64_t)(t.r0 + tid) * (uint64_t)K + (uint64_t)t.c0)
+                                  : 0;
+    }
+    __syncthreads();
+    // transpose: wave w takes rows 64 (w % 4) .. +63 and row words 2 (w / 4), 2 (w / 4) + 1
+    {
+        const int g = wv & 3;
+        for (int i = 2 * (wv >> 2); i < 2 * (wv >> 2) + 2; ++i) {
+            const uint32_t x = rowbits[(g * kWave + lane) * kCvPad + i];
+            uint64_t mine = 0;
+#pragma unroll
+            for (int b = 0; b < 32; ++b) {
+                const uint64_t m = __ballot((x >> b) & 1u);
+                if (lane == b) mine = m;
+            }
+            if (lane < 32) {
+                colbits[(32 * i + lane) * kCvPad + 2 * g] = (uint32_t)mine;
+                colbits[(32 * i + lane) * kCvPad + 2 * g + 1] = (uint32_t)(mine >> 32);
+            }
+        }
+    }
+    __syncthreads();
+    // word prefixes and counts: threads 0..255 rows, 256..511 columns
+    int32_t cntv = 0;
+    if (tid < 2 * kCvDim) {
+        const bool row = tid < kCvDim;
+        const int a = row ? tid : tid - kCvDim;
+        const uint32_t* bits = row ? rowbits : colbits;
+        uint8_t* pre = row ? rwp : cwp;
+#pragma unroll
+        for (int i = 0; i < kCvWords; ++i) {
+            pre[a * kCvWords + i] = (uint8_t)cntv;
+            cntv += __popc(bits[a * kCvPad + i]);
+        }
+        const int32_t inc = wave_incl(cntv);
+        if (lane == kWave - 1) red[row ? 0 : 1][(tid % kCvDim) / kWave] = inc;
+    }
+    __syncthreads();
+    if (tid < 2 * kCvDim) {
+        const bool row = tid < kCvDim;
+        const int a = row ? tid : tid - kCvDim;
+        int32_t before = 0;
+        for (int i = 0; i < a / kWave; ++i) before += red[row ? 0 : 1][i];
+        const int32_t ex = before + wave_incl(cntv) - cntv;
+        (row ? rowoff : colstart)[a] = ex;
+        if (a == kCvDim - 1) (row ? rowoff : colstart)[kCvDim] = ex + cntv;
+    }
+    __syncthreads();
+    const int32_t E = colstart[kCvDim];
+    if (E <= kCvStage) {   // uniform
+        // lists: two row words and two column words per thread
+#pragma unroll
+        for (int n = 0; n < kCvDim * kCvWords / kCvScatterThreads; ++n) {
+            const int q = tid + n * kCvScatterThreads;
+            const int a = q / kCvWords, i = q % kCvWords;
+            uint32_t m = rowbits[a * kCvPad + i];
+            int32_t x = rowoff[a] + rwp[a * kCvWords + i];
+            while (m) {
+                m &= m - 1u;
+                xrow[x++] = (uint8_t)a;
+            }
+            // column a, rows 32i .. 32i+31
+            m = colbits[a * kCvPad + i];
+            int32_t e = colstart[a] + cwp[a * kCvWords + i];
+            const int ci = a >> 5;
+            const uint32_t below = (1u << (a & 31)) - 1u;
+            while (m) {
+                const int rr = 32 * i + __ffs(m) - 1;
+                m &= m - 1u;
+                eloc[e] = (uint16_t)(rowoff[rr] + rwp[rr * kCvWords + ci] + __popc(rowbits[rr * kCvPad + ci] & below));
+                ecol[e] = (uint8_t)a;
+                ++e;
+            }
+        }
+        __syncthreads();
+        for (int32_t x = tid; x < E; x += kCvScatterThreads) {
+            const int rr = xrow[x];
+            sval[x] = vals[rowk[rr] + (x - rowoff[rr])];
+        }
+        __syncthreads();
+        for (int32_t e = tid; e < E; e += kCvScatterThreads) {
+            const int c = ecol[e];
+            const int32_t loc = eloc[e];
+            const int32_t kt = colbase[c] + (e - colstart[c]);
+            rows_t[kt] = t.r0 + xrow[loc];
+            vals_t[kt] = sval[loc];
+            sslot[loc] = kt;
+        }
+        __syncthreads();
+        for (int32_t x = tid; x < E; x += kCvScatterThreads) {
+            const int rr = xrow[x];
+            iperm[rowk[rr] + (x - rowoff[rr])] = sslot[x];
+        }
+        return;
+    }
+    // a dense tile: column by binary search, row by a walk of the column's words
+    for (int32_t e = tid; e < E; e += kCvScatterThreads) {
+        const int32_t c = cv_last_le(colstart, kCvDim, e);
+        int32_t rank = e - colstart[c];
+        const int32_t kt = colbase[c] + rank;
+        int j = 0;
+        uint32_t m = colbits[c * kCvPad];
+        for (int n = __popc(m); rank >= n; n = __popc(m)) {
+            rank -= n;
+            m = colbits[c * kCvPad + (++j)];
+        }
+        for (; rank > 0; --rank) m &= m - 1u;
+        const int rr = 32 * j + __ffs(m) - 1;
+        const int ci = c >> 5;
+        const int32_t k = rowk[rr] + rwp[rr * kCvWords + ci] + __popc(rowbits[rr * kCvPad + ci] & ((1u << (c & 31)) - 1u));
+        rows_t[kt] = t.r0 + rr;
+        vals_t[kt] = vals[k];
+        iperm[k] = kt;
+    }
+}
+
 struct PruneScratch {
     uint32_t* state;    // [16]
     uint32_t* hist;     // [kSelCopies * 256] selection histograms
@@ -822,9 +1160,21 @@ struct PruneScratch {
     int32_t* tsum;      // [tmax / kSumTile] accepted per tile
     int32_t* fill;      // [kMaxRegions] bucket fill per region
     uint64_t* bucket;   // [nbucket] candidates grouped by region
+    int32_t* wpre;      // [words] first canonical slot of every bitmap word (column view from the bitmap)
+    int32_t* cvcnt;     // [row blocks * K] entries per column and row block, then their prefixes
+    int32_t* cvtot;     // [K] entries per column
     void* scan;         // scan scratch
     int64_t tmax, words, units, ktiles, nbucket;
 };
+
+// The column view is rebuilt from the bitmap when the bitmap is small next to
+// the entries (two passes over it cost less than sorting the entries);
+// otherwise by the general index build.
+inline bool cv_from_bitmap(const snack_layer* L)
+{
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    return L->nnz > 0 && N <= 256ull * (uint64_t)L->nnz;
+}
 
 int64_t batch_cap(const snack_layer* L)
 {
@@ -843,7 +1193,9 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t ktiles = (n + kKeepTile - 1) / kKeepTile;
     const int64_t tm = batch_cap(L);
     const int64_t nb = bucket_bound(N, tm);
+    const int64_t nbi = (L->M + kCvDim - 1) / kCvDim;
     int64_t sn = units > ktiles ? units : ktiles;
+    if (L->K > sn) sn = L->K;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -856,6 +1208,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
     size_t o_acc = take((size_t)tm + 8), o_tsum = take((size_t)(tm / kSumTile + 1) * 4);
     size_t o_fill = take((size_t)kMaxRegions * 4), o_bucket = take((size_t)nb * 8);
+    size_t o_wpre = take((size_t)words * 4), o_cvcnt = take((size_t)nbi * L->K * 4), o_cvtot = take((size_t)L->K * 4);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
         char* base = (char*)L->scratch;
@@ -872,6 +1225,9 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         ps->tsum = (int32_t*)(base + o_tsum);
         ps->fill = (int32_t*)(base + o_fill);
         ps->bucket = (uint64_t*)(base + o_bucket);
+        ps->wpre = (int32_t*)(base + o_wpre);
+        ps->cvcnt = (int32_t*)(base + o_cvcnt);
+        ps->cvtot = (int32_t*)(base + o_cvtot);
         ps->scan = base + o_scan;
         ps->tmax = tm;
         ps->words = words;
@@ -994,9 +1350,11 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
             SNACK_CHECK(exclusive_scan_i32(ps.old_cnt, ps.old_cnt, nu, nullptr, ps.scan, s));
         }
         const bool wide = N > 0xFFFFFFFFull;
+        int32_t* wpre = cv_from_bitmap(L) ? ps.wpre : nullptr;
         auto emit = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm, ps.old_bm,
-                               ps.words, nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals);
+                               ps.words, nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals,
+                               wpre);
         };
         if (direct) {
             if (wide) emit(emit_units_kernel<true, true>);
@@ -1007,7 +1365,25 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         }
         SNACK_HIP(hipGetLastError());
     }
-    SNACK_CHECK(canon_build_index(L, s));
+    if (cv_from_bitmap(L)) {
+        ProfScope pc(KC_CANON, s);
+        const int32_t M = L->M, K = L->K;
+        const int32_t nbi = (M + kCvDim - 1) / kCvDim, nbj = (K + kCvDim - 1) / kCvDim;
+        const uint64_t words = (uint64_t)ps.words;
+        const int64_t nslots = (int64_t)kXcds * ((nbj + kXcds - 1) / kXcds) * nbi;
+        hipLaunchKernelGGL(cv_count_kernel, dim3((unsigned)nslots), dim3(kCvThreads), 0, s, ps.occ_bm, words, ps.wpre,
+                           M, K, nbi, nbj, nnz, ps.cvcnt, L->row_ptr, L->col_ptr);
+        hipLaunchKernelGGL(cv_column_scan_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, ps.cvcnt, nbi, K,
+                           ps.cvtot);
+        SNACK_HIP(hipGetLastError());
+        SNACK_CHECK(exclusive_scan_i32(ps.cvtot, L->col_ptr, K, nullptr, ps.scan, s));
+        hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm, words,
+                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, L->col_ptr, L->vals, L->rows_t, L->vals_t, L->iperm);
+        SNACK_HIP(hipGetLastError());
+        SNACK_CHECK(canon_index_tail(L, s));
+    } else {
+        SNACK_CHECK(canon_build_index(L, s));
+    }
     L->epoch += 1;
     return SNACK_OK;
 }

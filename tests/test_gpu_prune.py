@@ -42,7 +42,7 @@ def _run(M, K, nnz, fracs, key, seed=12345, vals=None, rounds=1):
 
 
 @pytest.mark.parametrize("M,K,nnz", [(6, 5, 14), (40, 30, 300), (500, 500, 12500), (64, 64, 4096),
-                                     (3000, 700, 105000)])
+                                     (3000, 700, 105000), (600, 600, 180000)])
 def test_prune_regrow_matches_oracle(M, K, nnz):
     _run(M, K, nnz, (0.3, 0.0, 0.5, 1.0), f"gpu/prune/{M}x{K}")
 
