@@ -853,46 +853,59 @@ __device__ inline bool cv_tile_of(int32_t nbi, int32_t nbj, int32_t& bi, int32_t
     return bi < nbi && bj < nbj;
 }
 
-// the tile's bits, row-major: rowbits[rr * kCvPad + i] holds columns c0+32i .. c0+32i+31
+// The tile's bits, row-major: rowbits[rr * kCvPad + i] holds columns
+// c0+32i .. c0+32i+31 of tile row rr (zero outside the matrix).  Every thread
+// issues all its loads (clamped indexes, both words of each unaligned span)
+// before it writes any of them, so none waits behind another.
+template <int T>
 __device__ inline void cv_load_rows(const uint32_t* __restrict__ occ_bm, uint64_t words, int32_t K,
                                     const CvTileShape& t, uint32_t* rowbits)
 {
+    constexpr int R = kCvDim * kCvWords / T;
+    uint32_t lo[R], hi[R];
+    uint64_t cell[R];
 #pragma unroll
-    for (int n = 0; n < kCvDim * kCvWords / kCvThreads; ++n) {
-        const int q = threadIdx.x + n * kCvThreads;
+    for (int n = 0; n < R; ++n) {
+        const int q = threadIdx.x + n * T;
         const int rr = q / kCvWords, i = q % kCvWords;
-        uint32_t x = 0u;
-        const int32_t cb = 32 * i;
-        if (rr < t.nrows && cb < t.ncols) {
-            const uint64_t cell = (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + cb);
-            const uint64_t w = cell >> 5;
-            const int sh = (int)(cell & 31);
-            const uint32_t lo = occ_bm[w];
-            const uint32_t hi = (sh && w + 1 < words) ? occ_bm[w + 1] : 0u;
-            x = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
-            const int32_t valid = t.ncols - cb;
-            if (valid < 32) x &= (1u << valid) - 1u;
-        }
-        rowbits[rr * kCvPad + i] = x;
+        const bool in = rr < t.nrows && 32 * i < t.ncols;
+        cell[n] = in ? (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + 32 * i) : 0ull;
+        const uint64_t w = cell[n] >> 5;
+        lo[n] = occ_bm[w];
+        hi[n] = occ_bm[w + 1 < words ? w + 1 : w];
+    }
+#pragma unroll
+    for (int n = 0; n < R; ++n) {
+        const int q = threadIdx.x + n * T;
+        const int rr = q / kCvWords, i = q % kCvWords;
+        const int sh = (int)(cell[n] & 31);
+        uint32_t x = sh ? (lo[n] >> sh) | (hi[n] << (32 - sh)) : lo[n];
+        const int32_t valid = t.ncols - 32 * i;
+        if (valid < 32) x &= (1u << valid) - 1u;
+        rowbits[rr * kCvPad + i] = (rr < t.nrows && valid > 0) ? x : 0u;
     }
 }
 
-// column words: colbits[c * kCvPad + j] holds rows 32j .. 32j+31 of column c
+// Column words: colbits[c * kCvPad + j] holds rows 32j .. 32j+31 of column c.
+// The tile is 8 x 8 blocks of 32 x 32 bits; a block sits in 32 lanes (lane l
+// holds row l) and five butterfly stages exchange ever smaller sub-blocks
+// with the lane 16, 8, 4, 2, 1 away, after which lane l holds column l.
+template <int T>
 __device__ inline void cv_transpose(const uint32_t* rowbits, uint32_t* colbits)
 {
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    for (int i = 0; i < kCvWords; ++i) {
-        const uint32_t x = rowbits[(wv * kWave + lane) * kCvPad + i];
-        uint64_t mine = 0;
+    const int lane = threadIdx.x & (kWave - 1), l = lane & 31;
+    for (int blk = 2 * (int)(threadIdx.x / kWave) + (lane >> 5); blk < kCvWords * kCvWords; blk += T / 32) {
+        const int j = blk / kCvWords, i = blk % kCvWords;
+        uint32_t x = rowbits[(32 * j + l) * kCvPad + i];
 #pragma unroll
-        for (int b = 0; b < 32; ++b) {
-            const uint64_t m = __ballot((x >> b) & 1u);
-            if (lane == b) mine = m;
+        for (int st = 0; st < 5; ++st) {
+            const int d = 16 >> st;
+            const uint32_t m = st == 0 ? 0x0000FFFFu : st == 1 ? 0x00FF00FFu : st == 2 ? 0x0F0F0F0Fu
+                             : st == 3 ? 0x33333333u : 0x55555555u;
+            const uint32_t y = __shfl_xor(x, d, kWave);
+            x = (l & d) ? (((y >> d) & m) | (x & ~m)) : ((x & m) | ((y << d) & ~m));
         }
-        if (lane < 32) {
-            colbits[(32 * i + lane) * kCvPad + 2 * wv] = (uint32_t)mine;
-            colbits[(32 * i + lane) * kCvPad + 2 * wv + 1] = (uint32_t)(mine >> 32);
-        }
+        colbits[(32 * i + l) * kCvPad + j] = x;
     }
 }
 
@@ -901,8 +914,7 @@ __device__ inline int32_t cv_slot_at(const uint32_t* __restrict__ occ_bm, const 
                                      uint64_t cell)
 {
     const uint64_t w = cell >> 5;
-    const int sh = (int)(cell & 31);
-    return wpre[w] + (sh ? __popc(occ_bm[w] & ((1u << sh) - 1u)) : 0);
+    return wpre[w] + __popc(occ_bm[w] & ((1u << (cell & 31)) - 1u));
 }
 
 __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __restrict__ occ_bm, uint64_t words,
@@ -912,31 +924,28 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __
                                                               int32_t* __restrict__ col_ptr)
 {
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
-    __shared__ int32_t colcnt[kCvDim];
+    __shared__ uint32_t colbits[kCvDim * kCvPad];
     int32_t bi, bj;
     if (!cv_tile_of(nbi, nbj, bi, bj)) return;
     const CvTileShape t = cv_shape(bi, bj, M, K);
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    colcnt[tid] = 0;
-    if (bj == 0 && tid < t.nrows) row_ptr[t.r0 + tid] = cv_slot_at(occ_bm, wpre, (uint64_t)(t.r0 + tid) * (uint64_t)K);
+    const int tid = threadIdx.x;
+    if (bj == 0) {
+        const int32_t r = t.r0 + (tid < t.nrows ? tid : t.nrows - 1);
+        const int32_t k = cv_slot_at(occ_bm, wpre, (uint64_t)r * (uint64_t)K);
+        if (tid < t.nrows) row_ptr[r] = k;
+    }
     if (bi == 0 && bj == 0 && tid == 0) {
         row_ptr[M] = (int32_t)nnz;
         col_ptr[K] = (int32_t)nnz;
     }
-    cv_load_rows(occ_bm, words, K, t, rowbits);
+    cv_load_rows<kCvThreads>(occ_bm, words, K, t, rowbits);
     __syncthreads();
-    for (int i = 0; i < kCvWords; ++i) {
-        const uint32_t x = rowbits[(wv * kWave + lane) * kCvPad + i];
-        int32_t mine = 0;
+    cv_transpose<kCvThreads>(rowbits, colbits);
+    __syncthreads();
+    int32_t c = 0;
 #pragma unroll
-        for (int b = 0; b < 32; ++b) {
-            const int32_t c = __popcll(__ballot((x >> b) & 1u));
-            if (lane == b) mine = c;
-        }
-        if (lane < 32 && mine) atomicAdd(&colcnt[32 * i + lane], mine);
-    }
-    __syncthreads();
-    if (tid < t.ncols) cnt[(int64_t)bi * K + t.c0 + tid] = colcnt[tid];
+    for (int j = 0; j < kCvWords; ++j) c += __popc(colbits[tid * kCvPad + j]);
+    if (tid < t.ncols) cnt[(int64_t)bi * K + t.c0 + tid] = c;
 }
 
 // down each column: counts -> exclusive prefix over the row blocks; totals out
@@ -1009,48 +1018,17 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     const CvTileShape t = cv_shape(bi, bj, M, K);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 
-    // rows, as in cv_load_rows, two words per thread
-#pragma unroll
-    for (int n = 0; n < kCvDim * kCvWords / kCvScatterThreads; ++n) {
-        const int q = tid + n * kCvScatterThreads;
-        const int rr = q / kCvWords, i = q % kCvWords;
-        uint32_t x = 0u;
-        const int32_t cb = 32 * i;
-        if (rr < t.nrows && cb < t.ncols) {
-            const uint64_t cell = (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + cb);
-            const uint64_t w = cell >> 5;
-            const int sh = (int)(cell & 31);
-            const uint32_t lo = occ_bm[w];
-            const uint32_t hi = (sh && w + 1 < words) ? occ_bm[w + 1] : 0u;
-            x = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
-            const int32_t valid = t.ncols - cb;
-            if (valid < 32) x &= (1u << valid) - 1u;
-        }
-        rowbits[rr * kCvPad + i] = x;
-    }
+    cv_load_rows<kCvScatterThreads>(occ_bm, words, K, t, rowbits);
     if (tid < kCvDim) {
-        colbase[tid] = tid < t.ncols ? col_ptr[t.c0 + tid] + cnt[(int64_t)bi * K + t.c0 + tid] : 0;
-        rowk[tid] = tid < t.nrows ? cv_slot_at(occ_bm, wpre, (uint64_t)(t.r0 + tid) * (uint64_t)K + (uint64_t)t.c0)
-                                  : 0;
+        const int32_t c = t.c0 + (tid < t.ncols ? tid : t.ncols - 1);
+        const int32_t r = t.r0 + (tid < t.nrows ? tid : t.nrows - 1);
+        const int32_t cb = col_ptr[c] + cnt[(int64_t)bi * K + c];
+        const int32_t k = cv_slot_at(occ_bm, wpre, (uint64_t)r * (uint64_t)K + (uint64_t)t.c0);
+        colbase[tid] = tid < t.ncols ? cb : 0;
+        rowk[tid] = tid < t.nrows ? k : 0;
     }
     __syncthreads();
-    // transpose: wave w takes rows 64 (w % 4) .. +63 and row words 2 (w / 4), 2 (w / 4) + 1
-    {
-        const int g = wv & 3;
-        for (int i = 2 * (wv >> 2); i < 2 * (wv >> 2) + 2; ++i) {
-            const uint32_t x = rowbits[(g * kWave + lane) * kCvPad + i];
-            uint64_t mine = 0;
-#pragma unroll
-            for (int b = 0; b < 32; ++b) {
-                const uint64_t m = __ballot((x >> b) & 1u);
-                if (lane == b) mine = m;
-            }
-            if (lane < 32) {
-                colbits[(32 * i + lane) * kCvPad + 2 * g] = (uint32_t)mine;
-                colbits[(32 * i + lane) * kCvPad + 2 * g + 1] = (uint32_t)(mine >> 32);
-            }
-        }
-    }
+    cv_transpose<kCvScatterThreads>(rowbits, colbits);
     __syncthreads();
     // word prefixes and counts: threads 0..255 rows, 256..511 columns
     int32_t cntv = 0;
@@ -1105,9 +1083,21 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
             }
         }
         __syncthreads();
-        for (int32_t x = tid; x < E; x += kCvScatterThreads) {
-            const int rr = xrow[x];
-            sval[x] = vals[rowk[rr] + (x - rowoff[rr])];
+        {
+            constexpr int R = kCvStage / kCvScatterThreads;
+            float v[R];
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int32_t x = tid + u * kCvScatterThreads;
+                const int32_t xc = x < E ? x : 0;
+                const int rr = xrow[xc];
+                v[u] = vals[x < E ? rowk[rr] + (x - rowoff[rr]) : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int32_t x = tid + u * kCvScatterThreads;
+                if (x < E) sval[x] = v[u];
+            }
         }
         __syncthreads();
         for (int32_t e = tid; e < E; e += kCvScatterThreads) {
