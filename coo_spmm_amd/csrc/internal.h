@@ -36,6 +36,11 @@ enum KernelClass : int {
 // whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
 // change of the index.
 constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
+// first index of slice s when [0, nidx) is cut into S slices
+__host__ __device__ inline int32_t split_start(int32_t s, int32_t S, int32_t nidx)
+{
+    return (int32_t)(((int64_t)s * nidx) / S);
+}
 struct SplitTab {
     int32_t S = 0;
     int32_t* tab = nullptr;

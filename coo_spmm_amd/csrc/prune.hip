@@ -980,6 +980,36 @@ __device__ inline int32_t cv_last_le(const int32_t* a, int32_t n, int32_t x)
     return lo;
 }
 
+// The slice tables of both views (null where a width has none): row view
+// (keys rows, slices over columns) and column view (keys columns, slices over rows).
+struct CvTabs {
+    int32_t rS[kTileWidths], cS[kTileWidths];
+    int32_t* rtab[kTileWidths];
+    int32_t* ctab[kTileWidths];
+};
+
+// a view's slice-table entries for boundaries inside one tile: keys along the
+// tile's one side (lane a < nkey), boundaries along the other, starting at
+// `o0` with `n` positions; the last tile along the boundary side also writes
+// the end entry (s = S).  Entry = slot of the key's first entry in the tile
+// (`first`) plus the key's entries before the boundary (word prefixes `pre`
+// and the bits of the boundary's word).
+__device__ inline void cv_tab_side(int32_t* tab, int32_t S, int32_t nidx, int32_t nkeys, int32_t o0, int32_t n,
+                                   bool last, int32_t key0, int a, int32_t nkey, int32_t first,
+                                   const uint8_t* pre, const uint32_t* bits, int32_t total)
+{
+    for (int32_t s = (int32_t)(((int64_t)o0 * S + nidx - 1) / nidx); s <= S; ++s) {
+        const int32_t b = split_start(s, S, nidx);
+        if (b >= o0 + n && !(s == S && last)) break;
+        if (a < nkey) {
+            const int32_t lb = b - o0;
+            const int32_t before = lb >= kCvDim ? total
+                                   : pre[a * kCvWords + (lb >> 5)] + __popc(bits[a * kCvPad + (lb >> 5)] & ((1u << (lb & 31)) - 1u));
+            tab[(int64_t)s * nkeys + key0 + a] = first + before;
+        }
+    }
+}
+
 constexpr int kCvScatterThreads = 1024;
 constexpr int32_t kCvStage = 4096;   // tile entries handled through LDS lists
 
@@ -996,9 +1026,8 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     const uint32_t* __restrict__ occ_bm, uint64_t words, const int32_t* __restrict__ wpre, int32_t M, int32_t K,
     int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ col_ptr,
     const float* __restrict__ vals, int32_t* __restrict__ rows_t, float* __restrict__ vals_t,
-    int32_t* __restrict__ iperm)
+    int32_t* __restrict__ iperm, CvTabs tabs)
 {
-    constexpr int W = kCvScatterThreads / kWave;
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
     __shared__ uint32_t colbits[kCvDim * kCvPad];
     __shared__ uint8_t rwp[kCvDim * kCvWords];    // entries of a row before each of its words
@@ -1056,6 +1085,23 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
         if (a == kCvDim - 1) (row ? rowoff : colstart)[kCvDim] = ex + cntv;
     }
     __syncthreads();
+    // slice tables: threads 0..255 the rows' entries (row view), 256..511 the columns'
+    if (tid < 2 * kCvDim) {
+        const bool row = tid < kCvDim;
+        const int a = row ? tid : tid - kCvDim;
+        for (int w = 0; w < kTileWidths; ++w) {
+            if (row && tabs.rtab[w]) {
+                const int32_t total = a < t.nrows ? rowoff[a + 1] - rowoff[a] : 0;
+                cv_tab_side(tabs.rtab[w], tabs.rS[w], K, M, t.c0, t.ncols, bj == nbj - 1, t.r0, a, t.nrows,
+                            a < t.nrows ? rowk[a] : 0, rwp, rowbits, total);
+            }
+            if (!row && tabs.ctab[w]) {
+                const int32_t total = a < t.ncols ? colstart[a + 1] - colstart[a] : 0;
+                cv_tab_side(tabs.ctab[w], tabs.cS[w], M, K, t.r0, t.nrows, bi == nbi - 1, t.c0, a, t.ncols,
+                            a < t.ncols ? colbase[a] : 0, cwp, colbits, total);
+            }
+        }
+    }
     const int32_t E = colstart[kCvDim];
     if (E <= kCvStage) {   // uniform
         // lists: two row words and two column words per thread
@@ -1367,10 +1413,22 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
                            ps.cvtot);
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(exclusive_scan_i32(ps.cvtot, L->col_ptr, K, nullptr, ps.scan, s));
+        CvTabs tabs;
+        for (int w = 0; w < kTileWidths; ++w) {
+            tabs.rS[w] = L->fwd.split[w].S;
+            tabs.rtab[w] = L->fwd.split[w].S >= 2 ? L->fwd.split[w].tab : nullptr;
+            tabs.cS[w] = L->tr.split[w].S;
+            tabs.ctab[w] = L->tr.split[w].S >= 2 ? L->tr.split[w].tab : nullptr;
+        }
         hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm, words,
-                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, L->col_ptr, L->vals, L->rows_t, L->vals_t, L->iperm);
+                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, L->col_ptr, L->vals, L->rows_t, L->vals_t, L->iperm,
+                           tabs);
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(canon_index_tail(L, s));
+        for (int w = 0; w < kTileWidths; ++w) {
+            if (tabs.rtab[w]) L->fwd.split[w].valid = true;
+            if (tabs.ctab[w]) L->tr.split[w].valid = true;
+        }
     } else {
         SNACK_CHECK(canon_build_index(L, s));
     }

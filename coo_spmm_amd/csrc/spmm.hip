@@ -1003,11 +1003,6 @@ constexpr int kTileDepthDw = 4;   // with dW: each block also holds its key's op
 constexpr int kMaxSplits = 64;
 constexpr int kTileStaticLds = 1024;   // bytes kept back from the slice buffer
 
-__host__ __device__ inline int32_t split_start(int32_t s, int32_t S, int32_t nidx)
-{
-    return (int32_t)(((int64_t)s * nidx) / S);
-}
-
 struct TileArgs {
     const int32_t* tab;   // slice bounds of key r in slice s: tab[s * tstride + r], tab[(s + 1) * tstride + r]
     int64_t tstride;

@@ -3,8 +3,8 @@ import numpy as np
 import pytest
 
 import oracle
-from snack_inputs import random_layer
-from tests.gpu_util import say, lib, dev, host
+from snack_inputs import normal, random_layer
+from tests.gpu_util import say, lib, dev, host, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -63,3 +63,29 @@ def test_prune_regions_wider_than_one_pass():
     # 50000 x 50000 = 2.5e9 cells: the grow step's regions are wider than one
     # LDS pass, so each is claimed in several; the column view takes the sort path
     _run(50000, 50000, 200_000, (0.3, 0.7), "gpu/prune/wide")
+
+
+@pytest.mark.parametrize("M,K", [(3000, 3000), (1700, 6100)])
+def test_batch_tiled_passes_after_drop_regrow(M, K):
+    """Drop/regrow rebuilds the slice tables the batch-tiled kernels read; the
+    forward and backward that follow match the oracle for every batch tile,
+    on both views (keys long enough that the tables have two or more slices)."""
+    L = lib()
+    nnz = M * K // 20
+    rows, cols, v = random_layer(M, K, nnz, f"gpu/prune/tiles/{M}x{K}")
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(v), seed=31)
+    try:
+        say("tiles after prune", M, K)
+        layer.prune_regrow(nnz * 3 // 10)
+        r, c, vv = (host(t) for t in layer.export())
+        for B in (8, 16, 32, 64):
+            X = normal((B, K), f"gpu/prune/tiles/{M}x{K}/X/{B}")
+            dY = normal((B, M), f"gpu/prune/tiles/{M}x{K}/dY/{B}")
+            say("tiles after prune B", B)
+            Y = host(layer.forward(dev(X)))
+            dX, dW = (host(t) for t in layer.backward(dev(X), dev(dY)))
+            assert_close(f"Y B={B}", Y, *oracle.forward(M, K, r, c, vv, X))
+            assert_close(f"dX B={B}", dX, *oracle.backward_dx(M, K, r, c, vv, dY))
+            assert_close(f"dW B={B}", dW, *oracle.backward_dw(M, K, r, c, X, dY))
+    finally:
+        layer.close()
