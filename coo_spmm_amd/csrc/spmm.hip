@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs 
     constexpr int LDS_Q = (BT > 1) ? E / 4 : 1;   // int4 per array per wave
     __shared__ int32_t slice_s[WPB][kChunkWork + 2];
     __shared__ int4 blk_s[WPB][2][LDS_Q];
-    extern __shared__ float xs_dyn[];   // the gathered operand, when staged in LDS
+    extern __shared__ __align__(16) float xs_dyn[];   // the gathered operand, when staged in LDS
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = (int)(threadIdx.x / kWave);
@@ -906,7 +906,7 @@ constexpr int kLdsU = 4;   // entries per lane per step
 template <int BT, int NB, int U, bool DW, bool SPMM = true, bool RM = false>
 __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs A, int bp, int B)
 {
-    extern __shared__ float gs_dyn[];
+    extern __shared__ __align__(16) float gs_dyn[];
     __shared__ int next_s;
     const int nwg = (int)gridDim.x;
     const int bid = (int)blockIdx.x;
@@ -1237,7 +1237,7 @@ struct TileBlock {
 template <int U, int BT, int NB, int U0 = 0, class TB>
 __device__ inline void tile_gather(const TB& b, int32_t lane_off, float (&y)[U][NB])
 {
-    extern __shared__ float gs_dyn[];
+    extern __shared__ __align__(16) float gs_dyn[];
     if constexpr (U0 < U) {
         const int32_t off = b.template off_at<U0>(lane_off);
         const char* base = reinterpret_cast<const char*>(gs_dyn) + off;
@@ -1334,7 +1334,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
 {
     constexpr int BTILE = BT * NB;
     using TB = TileBlock<BT, U>;
-    extern __shared__ float gs_dyn[];
+    extern __shared__ __align__(16) float gs_dyn[];
     const int nwg = (int)gridDim.x;
     const int bid = (int)blockIdx.x;
     const int per = nwg / kXcd;   // the grid is a multiple of kXcd
