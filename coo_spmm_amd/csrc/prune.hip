@@ -76,26 +76,83 @@ __device__ inline int32_t wave_sum(int32_t v)
 }
 
 // ---- drop: radix select ---------------------------------------------------
-// state: [0] prefix, [1] rank still to find among keys matching the prefix,
-// [2] number of keys equal to the final prefix (set by the last pass).
+// Four passes over the magnitude keys, eight bits each, most significant
+// first.  state: [0] the n_drop-th smallest key T, [1] its rank among the keys
+// equal to T, [2] the number of keys equal to T (all three written after the
+// last pass); [3 + 3j .. 5 + 3j] the prefix, rank and count after pass j's pick.
+// Pass j writes histogram set j; the digit of pass j is picked by every
+// workgroup of the next kernel from set j (no separate launch), and workgroup 0
+// records it in its own state slot, which no workgroup of that kernel reads.
 // Each thread takes sixteen consecutive keys (four 16-byte loads) and adds runs
 // of equal digits before touching LDS, which keeps the first passes (where
 // nearly every key shares a digit) free of contention; each workgroup adds its
-// nonzero bins to one of kSelCopies global histograms.
+// nonzero bins to one of kSelCopies copies (atomics on one address serialise).
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;
-constexpr int kSelCopies = 32;   // histogram copies
+constexpr int kSelCopies = 32;
+constexpr int kSelPasses = 4;
+constexpr int kSelHist = kSelCopies * 256;   // words of one pass's histograms
 
+__global__ void prune_init_kernel(uint32_t* __restrict__ state, uint32_t* __restrict__ hist, uint32_t rank0)
+{
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < (int64_t)kSelPasses * kSelHist; i += (int64_t)gridDim.x * blockDim.x) hist[i] = 0u;
+    if (i0 < 16) state[i0] = i0 == 1 ? rank0 : 0u;
+}
+
+struct SelPick {
+    uint32_t prefix, rank, equal;
+};
+
+// The digit (at `shift`) holding rank `rank` among the keys that match
+// `prefix`, from the histograms of the pass that counted them: the first digit
+// whose running count passes the rank (the last digit if none does).  Called
+// by every thread of a 256-thread workgroup.
+__device__ inline SelPick sel_pick(const uint32_t* __restrict__ hist, uint32_t prefix, uint32_t rank, int shift)
+{
+    __shared__ uint32_t s_red[256 / kWave];
+    __shared__ SelPick s_pick;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kSelCopies; ++c) t += hist[c * 256 + tid];
+    const uint32_t inc = (uint32_t)wave_incl((int32_t)t);
+    if (lane == kWave - 1) s_red[w] = inc;
+    __syncthreads();
+    uint32_t ex = inc - t;
+    for (int i = 0; i < w; ++i) ex += s_red[i];
+    if ((rank >= ex && rank < ex + t) || (tid == 255 && rank >= ex + t)) {
+        s_pick.prefix = prefix | ((uint32_t)tid << shift);
+        s_pick.rank = rank - ex;
+        s_pick.equal = t;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
+template <int PASS>
 __global__ void __launch_bounds__(kSelThreads) sel_pass_kernel(const float* __restrict__ vals, int64_t n,
-                                                               uint32_t* __restrict__ state, int shift,
+                                                               uint32_t* __restrict__ state,
                                                                uint32_t* __restrict__ hist)
 {
+    constexpr int shift = 24 - 8 * PASS;
     __shared__ uint32_t h[256];
     const int tid = threadIdx.x;
     h[tid] = 0;
+    uint32_t prefix = 0;
+    if constexpr (PASS > 0) {
+        const uint32_t p0 = PASS == 1 ? 0u : state[3 + 3 * (PASS - 2)];
+        const uint32_t r0 = PASS == 1 ? state[1] : state[4 + 3 * (PASS - 2)];
+        const SelPick pk = sel_pick(hist + (PASS - 1) * kSelHist, p0, r0, shift + 8);
+        if (blockIdx.x == 0 && tid == 0) {
+            state[3 + 3 * (PASS - 1)] = pk.prefix;
+            state[4 + 3 * (PASS - 1)] = pk.rank;
+            state[5 + 3 * (PASS - 1)] = pk.equal;
+        }
+        prefix = pk.prefix;
+    }
     __syncthreads();
-    const uint32_t prefix = state[0];
-    const uint32_t hi_mask = (shift >= 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const uint32_t hi_mask = PASS == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     const int64_t k0 = ((int64_t)blockIdx.x * kSelThreads + tid) * kSelPer;
     uint32_t key[kSelPer];
     if (k0 + kSelPer <= n) {
@@ -112,12 +169,11 @@ __global__ void __launch_bounds__(kSelThreads) sel_pass_kernel(const float* __re
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) key[u] = k0 + u < n ? mag_bits(vals[k0 + u]) : ~prefix;
     }
-    const bool all_match = hi_mask == 0u;
     uint32_t run_d = 0, run = 0;
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
-        if (!all_match && (key[u] & hi_mask) != (prefix & hi_mask)) continue;
-        if (all_match && k0 + u >= n) continue;
+        if (PASS > 0 && (key[u] & hi_mask) != (prefix & hi_mask)) continue;
+        if (PASS == 0 && k0 + u >= n) continue;
         const uint32_t d = (key[u] >> shift) & 255u;
         if (d != run_d && run) {
             atomicAdd(&h[run_d], run);
@@ -128,33 +184,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_pass_kernel(const float* __re
     }
     if (run) atomicAdd(&h[run_d], run);
     __syncthreads();
-    // atomics on one address are serialised: spread them over kSelCopies copies
-    if (h[tid]) atomicAdd(&hist[(blockIdx.x % kSelCopies) * 256 + tid], h[tid]);
-}
-
-// picks the digit holding the wanted rank, then clears the histograms for the next pass
-__global__ void __launch_bounds__(256) sel_pick_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ state,
-                                                       int shift)
-{
-    __shared__ uint32_t tot[256];
-    uint32_t t = 0;
-    for (int c = 0; c < kSelCopies; ++c) {
-        t += hist[c * 256 + threadIdx.x];
-        hist[c * 256 + threadIdx.x] = 0u;
-    }
-    tot[threadIdx.x] = t;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = state[1];
-        uint32_t dg = 0;
-        for (; dg < 255; ++dg) {
-            if (r < tot[dg]) break;
-            r -= tot[dg];
-        }
-        state[0] |= dg << shift;
-        state[1] = r;
-        if (shift == 0) state[2] = tot[dg];
-    }
+    if (h[tid]) atomicAdd(&hist[PASS * kSelHist + (blockIdx.x % kSelCopies) * 256 + tid], h[tid]);
 }
 
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
@@ -216,12 +246,21 @@ __device__ inline int32_t block_excl(int32_t v, int32_t* smem /*[waves]*/, int32
 // Number of keys equal to T per tile; needed only when the ties are dropped in
 // part (their rank in slot order then decides), otherwise the kernel returns.
 __global__ void __launch_bounds__(kKeepThreads) eq_tiles_kernel(const float* __restrict__ vals, int64_t n,
-                                                                const uint32_t* __restrict__ state,
+                                                                uint32_t* __restrict__ state,
+                                                                const uint32_t* __restrict__ hist,
                                                                 int32_t* __restrict__ tile_eq)
 {
     __shared__ int32_t smem[kKeepThreads / kWave];
-    if (!ties_partial(state)) return;
-    const uint32_t T = state[0];
+    // the last pass's pick gives T, the rank among keys equal to T, and their count
+    const SelPick pk = sel_pick(hist + (kSelPasses - 1) * kSelHist, state[3 + 3 * (kSelPasses - 2)],
+                                state[4 + 3 * (kSelPasses - 2)], 0);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        state[0] = pk.prefix;
+        state[1] = pk.rank;
+        state[2] = pk.equal;
+    }
+    if (pk.rank + 1u == pk.equal) return;   // every key equal to T is dropped
+    const uint32_t T = pk.prefix;
     const int64_t base = (int64_t)blockIdx.x * kKeepTile;
     int32_t c = 0;
     for (int i = threadIdx.x; i < kKeepTile; i += kKeepThreads) {
@@ -397,7 +436,7 @@ constexpr int kTabBits = 13;
 constexpr int kTabSlots = 1 << kTabBits;   // LDS table: 64 KB
 constexpr int kTlBits = 21;           // candidate index within a batch
 constexpr int64_t kSumTile = 8192;    // candidate indices per accepted-count tile
-constexpr int kStOverflow = 8, kStTaken = 9, kStCut = 10;   // words of the prune state
+constexpr int kStOverflow = 12, kStTaken = 13, kStCut = 14;   // words of the prune state
 
 static_assert(kMaxBatch <= (1ll << kTlBits), "candidate index must fit its field");
 static_assert(kMaxBatch / kSumTile <= 1024, "one workgroup scans the tile counts");
@@ -1184,7 +1223,7 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
 
 struct PruneScratch {
     uint32_t* state;    // [16]
-    uint32_t* hist;     // [kSelCopies * 256] selection histograms
+    uint32_t* hist;     // [kSelPasses * kSelHist] selection histograms
     int32_t* tile_eq;   // [keep tiles] keys equal to T per tile (then their scan)
     float* vcopy;       // [nnz] the values before the rebuild
     uint32_t* kept_bm;  // [words]
@@ -1238,7 +1277,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         off += al(bytes);
         return o;
     };
-    size_t o_state = take(16 * 4), o_hist = take((size_t)kSelCopies * 256 * 4);
+    size_t o_state = take(16 * 4), o_hist = take((size_t)kSelPasses * kSelHist * 4);
     size_t o_teq = take((size_t)ktiles * 4), o_vc = take((size_t)n * 4);
     size_t o_kbm = take((size_t)words * 4), o_obm = take((size_t)words * 4), o_dbm = take((size_t)words * 4);
     size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
@@ -1299,19 +1338,15 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
 
     // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
     {
-        const uint32_t init[16] = {0u, (uint32_t)(n_drop - 1), 0u};
-        SNACK_HIP(hipMemcpyAsync(ps.state, init, sizeof init, hipMemcpyHostToDevice, s));
+        hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1));
         const unsigned nsel = (unsigned)((nnz + (int64_t)kSelThreads * kSelPer - 1) / ((int64_t)kSelThreads * kSelPer));
-        hipLaunchKernelGGL(fill_u32_kernel, dim3(8), dim3(kThreads), 0, s, ps.hist,
-                           (int64_t)kSelCopies * 256, 0u);
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            hipLaunchKernelGGL(sel_pass_kernel, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, shift,
-                               ps.hist);
-            hipLaunchKernelGGL(sel_pick_kernel, dim3(1), dim3(256), 0, s, ps.hist, ps.state, shift);
-        }
+        hipLaunchKernelGGL(sel_pass_kernel<0>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<1>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<2>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<3>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
         SNACK_HIP(hipGetLastError());
         hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->vals, nnz,
-                           ps.state, ps.tile_eq);
+                           ps.state, ps.hist, ps.tile_eq);
         hipLaunchKernelGGL(zero_bitmaps_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm,
                            ps.occ_bm, ps.old_bm, ps.words, ps.fill, kMaxRegions);
         SNACK_HIP(hipGetLastError());
