@@ -135,8 +135,9 @@ def main():
         b = bufs[B]
         L.snack_forward(layer.h, b["X"], b["Y"], stream)
         L.snack_mse_grad(b["Y"], b["T"], b["dY"], 2.0 / (B * M), stream)
-        L.snack_backward(layer.h, b["X"], b["dY"], b["dX"], b["dW"], stream)
-        L.snack_sgd_step(layer.h, b["dW"], lr, stream)
+        # backward (dX, dW) and the SGD step in one call: the column pass steps the
+        # column-ordered value copy in place (same results as backward + sgd_step)
+        L.snack_backward_sgd(layer.h, b["X"], b["dY"], b["dX"], b["dW"], lr, stream)
         it_counter[0] += 1
         if args.prune_every > 0 and it_counter[0] % args.prune_every == 0:
             L.snack_profile_set_tag(-1)

@@ -39,6 +39,7 @@ _SIGS = {
     "snack_layer_reserve": ([P, i32], ST),
     "snack_forward": ([P, P, P, i32, P], ST),
     "snack_backward": ([P, P, P, P, P, i32, P], ST),
+    "snack_backward_sgd": ([P, P, P, P, P, f32, i32, P], ST),
     "snack_prune_regrow": ([P, i64, P], ST),
     "snack_layer_shape": ([P, ctypes.POINTER(i32), ctypes.POINTER(i32)], ST),
     "snack_layer_nnz": ([P, ctypes.POINTER(i64)], ST),
@@ -145,6 +146,12 @@ def snack_forward(h, X, Y, stream=None):
 def snack_backward(h, X, dY, dX=None, dW=None, stream=None):
     B = dY.shape[0]
     _check(_lib.snack_backward(h, _ptr(X), _ptr(dY), _ptr(dX), _ptr(dW), B, _stream(stream)), "snack_backward")
+
+
+def snack_backward_sgd(h, X, dY, dX, dW, lr, stream=None):
+    B = dY.shape[0]
+    _check(_lib.snack_backward_sgd(h, _ptr(X), _ptr(dY), _ptr(dX), _ptr(dW), float(lr), B, _stream(stream)),
+           "snack_backward_sgd")
 
 
 def snack_prune_regrow(h, n_drop, stream=None):
@@ -304,6 +311,15 @@ class SnackLayer:
             dW = torch.empty((self.nnz,), dtype=torch.float32, device=dY.device)
         snack_backward(self.h, X, dY, dX if want_dx else None, dW if want_dw else None, stream)
         return (dX if want_dx else None), (dW if want_dw else None)
+
+    def backward_sgd(self, X, dY, lr, want_dx=True, dX=None, dW=None, stream=None):
+        import torch
+        if want_dx and dX is None:
+            dX = torch.empty((dY.shape[0], self.K), dtype=torch.float32, device=dY.device)
+        if dW is None:
+            dW = torch.empty((self.nnz,), dtype=torch.float32, device=dY.device)
+        snack_backward_sgd(self.h, X, dY, dX if want_dx else None, dW, lr, stream)
+        return (dX if want_dx else None), dW
 
     def prune_regrow(self, n_drop, stream=None):
         snack_prune_regrow(self.h, n_drop, stream)

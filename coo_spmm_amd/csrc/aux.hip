@@ -55,11 +55,11 @@ __global__ void sgd_kernel(float* __restrict__ v, const float* __restrict__ g, f
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
         float4 a = reinterpret_cast<float4*>(v)[i];
         const float4 d = reinterpret_cast<const float4*>(g)[i];
-        a.x = a.x - lr * d.x; a.y = a.y - lr * d.y; a.z = a.z - lr * d.z; a.w = a.w - lr * d.w;
+        a.x = sgd_value(a.x, d.x, lr); a.y = sgd_value(a.y, d.y, lr); a.z = sgd_value(a.z, d.z, lr); a.w = sgd_value(a.w, d.w, lr);
         reinterpret_cast<float4*>(v)[i] = a;
     }
     for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        v[i] = v[i] - lr * g[i];
+        v[i] = sgd_value(v[i], g[i], lr);
 }
 
 // both value copies in one launch: (v, g) and (v2, g2), each n long
@@ -74,12 +74,12 @@ __global__ void sgd2_kernel(float* __restrict__ v, const float* __restrict__ g, 
         const float4* __restrict__ pg = reinterpret_cast<const float4*>(second ? g2 : g);
         float4 a = pv[j];
         const float4 d = pg[j];
-        a.x = a.x - lr * d.x; a.y = a.y - lr * d.y; a.z = a.z - lr * d.z; a.w = a.w - lr * d.w;
+        a.x = sgd_value(a.x, d.x, lr); a.y = sgd_value(a.y, d.y, lr); a.z = sgd_value(a.z, d.z, lr); a.w = sgd_value(a.w, d.w, lr);
         pv[j] = a;
     }
     for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        v[i] = v[i] - lr * g[i];
-        v2[i] = v2[i] - lr * g2[i];
+        v[i] = sgd_value(v[i], g[i], lr);
+        v2[i] = sgd_value(v2[i], g2[i], lr);
     }
 }
 
@@ -177,6 +177,17 @@ snack_status sgd_update(snack_layer* L, const float* dW, const float* dW_t, floa
             L->vals_t_stale = true;
         }
     }
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+snack_status sgd_update_values(snack_layer* L, const float* dW, float lr, hipStream_t s)
+{
+    if (L->nnz == 0) return SNACK_OK;
+    ProfScope prof(KC_SGD, s);
+    const bool aligned = ((uintptr_t)dW & 15) == 0;
+    hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(L->nnz / 4 + 1)), dim3(kThreads), 0, s, L->vals, dW, lr, L->nnz,
+                       aligned ? 1 : 0);
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }

@@ -36,6 +36,10 @@ enum KernelClass : int {
 // whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
 // change of the index.
 constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
+// one SGD step on one value: v - lr * g with a single rounding; every update of
+// either value copy goes through it, so the two copies stay bit-identical
+__device__ inline float sgd_value(float v, float g, float lr) { return fmaf(-lr, g, v); }
+
 // first index of slice s when [0, nidx) is cut into S slices
 __host__ __device__ inline int32_t split_start(int32_t s, int32_t S, int32_t nidx)
 {
@@ -219,8 +223,16 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 // one launch: dX over the transposed view (plus dW in transposed order when
 // dW_t is non-null) and dW over the canonical view; either output may be null.
 // Requires a single batch tile when dW or dW_t is requested.
+// With `step`, where the column pass supports it, that pass also takes the SGD
+// step vals_t -= lr * dW in place (from the values it loads) and *step->done is
+// set; dW_t is then written only where the canonical dW is permuted from it.
+struct SgdStep {
+    float lr;
+    bool done;
+};
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
-                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm = false);
+                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm = false,
+                                 SgdStep* step = nullptr);
 
 // slice-tiled SpMM support: slices of view v for a batch tile (0 = not used),
 // the split tables' allocation (at create) and the workspace the partial sums
@@ -236,6 +248,8 @@ snack_status sddmm_dw_tiles(const snack_layer* L, const float* xt, const float* 
 
 // values -= lr * dW; also vals_t -= lr * dW_t when dW_t is non-null
 snack_status sgd_update(snack_layer* L, const float* dW, const float* dW_t, float lr, hipStream_t s);
+// values -= lr * dW only (vals_t already took the step in the column pass)
+snack_status sgd_update_values(snack_layer* L, const float* dW, float lr, hipStream_t s);
 snack_status mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale, hipStream_t s);
 snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s);
 snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hipStream_t s);

@@ -266,14 +266,13 @@ extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, 
     return spmm_forward(L, feat, p, B, Y, s);
 }
 
-extern "C" snack_status snack_backward(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
-                                       int32_t B, snack_stream stream)
+namespace {
+
+// the backward of snack_backward; with `step`, the column pass may also take the
+// SGD step of vals_t in place (step->done tells whether it did)
+snack_status backward_impl(snack_layer* L, const float* X, const float* dY, float* dX, float* dW, int32_t B,
+                           hipStream_t s, SgdStep* step)
 {
-    if (!L || !dY || B < 1) return SNACK_ERR_INVALID_ARG;
-    if (dW && !X) return SNACK_ERR_INVALID_ARG;
-    if (dW && ((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;   // 16-byte vector stores
-    if (!dX && !dW) return SNACK_OK;
-    hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
     const bool rm = spmm_batch_major(L, p, false, dX != nullptr, dW != nullptr);
     const float* dyt = dY;
@@ -289,8 +288,8 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
     if (p.ntiles == 1) {
         // one launch: dX (+ dW in transposed order) over the column view, dW over the row view
         float* dwt = (dX && dW) ? L->dwt : nullptr;
-        SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, dW, dwt, s, rm));
-        if (dwt) {
+        SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, dW, dwt, s, rm, step));
+        if (dwt && !(step && step->done)) {
             L->dwt_for = dW;
             L->dwt_valid = true;
         }
@@ -299,6 +298,36 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
         if (dW) SNACK_CHECK(sddmm_dw_tiles(L, xt, dyt, p, dW, s));
     }
     return SNACK_OK;
+}
+
+}  // namespace
+
+extern "C" snack_status snack_backward(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
+                                       int32_t B, snack_stream stream)
+{
+    if (!L || !dY || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (dW && !X) return SNACK_ERR_INVALID_ARG;
+    if (dW && ((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;   // 16-byte vector stores
+    if (!dX && !dW) return SNACK_OK;
+    return backward_impl(L, X, dY, dX, dW, B, as_stream(stream), nullptr);
+}
+
+extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
+                                           float lr, int32_t B, snack_stream stream)
+{
+    if (!L || !X || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    SgdStep step{lr, false};
+    SNACK_CHECK(backward_impl(L, X, dY, dX, dW, B, s, &step));
+    if (!step.done) {
+        // the column pass did not take the step: as snack_sgd_step would
+        const float* dwt = (L->dwt_valid && dW == L->dwt_for) ? L->dwt : nullptr;
+        L->dwt_valid = false;
+        return sgd_update(L, dW, dwt, lr, s);
+    }
+    L->dwt_valid = false;
+    return sgd_update_values(L, dW, lr, s);
 }
 
 extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack_stream stream)

@@ -53,6 +53,8 @@ struct RoleArgs {
     const float* H;      // indexed by key: [nkeys, bp] (dW only)
     float* out;          // [B, nkeys] or null
     float* dwo;          // dW in this view's slot order, or null
+    float* apply;        // values in this view's slot order to take an SGD step with dW, or null
+    float lr;            // (SPMM passes only: the step uses the entry values they load)
     int64_t cap;         // padded length of idx / vals
     int32_t nchunks;
     int32_t nkeys;
@@ -605,9 +607,10 @@ __device__ inline void key_accumulate(const float (&vv)[U], const float (&y)[U][
 // entries' dot products with h, four at a time reduced over the group
 // together, stored; an entry's result does not depend on U or on its place
 // among the four
+// (with `apply`, the entry's value also takes its SGD step, from its value vv)
 template <int BT, int NB, int U>
 __device__ inline void key_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t p1, int g, int bl,
-                              float* __restrict__ dwo)
+                              float* __restrict__ dwo, const float (&vv)[U], float* __restrict__ apply, float lr)
 {
     static_assert(U % 4 == 0, "dW reduces four entries at a time");
     constexpr int G = kWave / BT;
@@ -627,19 +630,29 @@ __device__ inline void key_dw(const float (&y)[U][NB], const float (&h)[NB], int
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int32_t k = qb + u * G + g;
-                if (k < p1) dwo[k] = d[u];
+                if (k < p1) {
+                    if (dwo) dwo[k] = d[u];
+                    if (apply) apply[k] = sgd_value(vv[4 * q + u], d[u], lr);
+                }
             }
         } else if constexpr (BT == 2) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int32_t k = qb + (2 * bl + t) * G + g;
-                if (k < p1) dwo[k] = d[t];
+                if (k < p1) {
+                    if (dwo) dwo[k] = d[t];
+                    if (apply) apply[k] = sgd_value(vv[4 * q + 2 * bl + t], d[t], lr);
+                }
             }
         } else {
             constexpr int STRIDE = BT / 4;
             if ((bl % STRIDE) == 0) {
-                const int32_t k = qb + ((bl / STRIDE) & 3) * G + g;
-                if (k < p1) dwo[k] = d[0];
+                const int e = (bl / STRIDE) & 3;
+                const int32_t k = qb + e * G + g;
+                if (k < p1) {
+                    if (dwo) dwo[k] = d[0];
+                    if (apply) apply[k] = sgd_value(vv[4 * q + e], d[0], lr);
+                }
             }
         }
     }
@@ -692,7 +705,7 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
             key_gather<NB, U>(Gm, ii, bp, bcol, y);
             blk.template load<SPMM>(A.idx, A.vals, base + KB::STEP, p1, lane, g);
             if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
-            if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo);
+            if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
         }
         if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out);
     }
@@ -868,7 +881,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
         float y[U][NB];
         key_gather<NB, U>(Gm, ii, bp, bcol, y);
         if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
-        if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo);
+        if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
         if (!last) {
             base += KB::STEP;
             continue;
@@ -1268,9 +1281,10 @@ __device__ inline void tile_vals(const TB& b, float (&vv)[U])
 // per-entry dot products with the key's operand row, reduced over the group
 // (pairs for 2-lane groups, fours otherwise) and stored; an entry's result is
 // the same sum of the same per-lane partials as in the key-major kernels
+// (with `apply`, the entry's value also takes its SGD step, from its value vv)
 template <int BT, int NB, int U>
 __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t lim, int g, int bl,
-                               float* __restrict__ dwo)
+                               float* __restrict__ dwo, const float (&vv)[U], float* __restrict__ apply, float lr)
 {
     if constexpr (BT == 2) {
 #pragma unroll
@@ -1287,7 +1301,10 @@ __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], in
             const float r = lane_xor<1>(hi ? d[0] : d[1]);
             const float tot = (hi ? d[1] : d[0]) + r;
             const int32_t k = base + g * U + 2 * q + bl;
-            if (k < lim) dwo[k] = tot;
+            if (k < lim) {
+                if (dwo) dwo[k] = tot;
+                if (apply) apply[k] = sgd_value(vv[2 * q + bl], tot, lr);
+            }
         }
     } else {
         constexpr int STRIDE = BT / 4;
@@ -1303,8 +1320,12 @@ __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], in
             }
             reduce4_dpp<BT>(d, bl);
             if ((bl % STRIDE) == 0) {
-                const int32_t k = base + g * U + 4 * q + ((bl / STRIDE) & 3);
-                if (k < lim) dwo[k] = d[0];
+                const int e = (bl / STRIDE) & 3;
+                const int32_t k = base + g * U + 4 * q + e;
+                if (k < lim) {
+                    if (dwo) dwo[k] = d[0];
+                    if (apply) apply[k] = sgd_value(vv[4 * q + e], d[0], lr);
+                }
             }
         }
     }
@@ -1414,15 +1435,18 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
             blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4, nrow * BTILE * 4);
             float y[U][NB];
             tile_gather<U, BT, NB>(blk[q], lane_off, y);
+            float vv[U];
             if constexpr (SPMM) {
-                float vv[U];
                 tile_vals<U>(blk[q], vv);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int n = 0; n < NB; ++n) acc[n] = fmaf(vv[u], y[u][n], acc[n]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) vv[u] = 0.0f;
             }
-            if constexpr (DW) tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, g, bl, A.dwo);
+            if constexpr (DW) tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, g, bl, A.dwo, vv, A.apply, A.lr);
             if constexpr (SPMM) {
                 if (d[q].last) {
                     // each lane ends with one column of the key's sum; one lane per column stores
@@ -1632,6 +1656,8 @@ RoleArgs role_for(const View& v, const float* G, const float* H, float* out, flo
     a.H = H;
     a.out = out;
     a.dwo = dwo;
+    a.apply = nullptr;
+    a.lr = 0.0f;
     a.nchunks = v.nchunks;
     a.nkeys = v.nkeys;
     a.nidx = v.nidx;
@@ -1717,9 +1743,12 @@ inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
 // kernel takes them, transposing G while it stages it
 template <bool DW, bool SPMM = true>
 snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
-                          float* out, float* dwo, int B, hipStream_t s, bool rm = false)
+                          float* out, float* dwo, int B, hipStream_t s, bool rm = false, float* apply = nullptr,
+                          float lr = 0.0f)
 {
-    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    a.apply = apply;
+    a.lr = lr;
     const size_t lds = (size_t)v.nidx * p.bp * sizeof(float);
     if (p.btile <= 4 && p.ntiles == 1 && lds <= (size_t)L->lds_bytes && L->cus > 0 && v.nchunks > 0) {
         // operand resident in LDS: one or two persistent workgroups per CU
@@ -1776,7 +1805,7 @@ inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
 
 template <bool DW, bool SPMM>
 snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
-                         float* out, float* dwo, int B, hipStream_t s)
+                         float* out, float* dwo, int B, hipStream_t s, float* apply = nullptr, float lr = 0.0f)
 {
     const SplitTab& st = v.split[tile_index(p.btile)];
     if (st.S >= 2 && !st.valid) {
@@ -1795,7 +1824,9 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
         for (int w = 0; w < kTileWidths; ++w)
             if (ts.tab[w]) v.split[w].valid = true;
     }
-    const RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+    a.apply = apply;
+    a.lr = lr;
     TileArgs t;
     t.S = st.S;
     t.tab = st.S >= 2 ? st.tab : v.ptr;
@@ -1939,8 +1970,11 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 }
 
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
-                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm)
+                                 float* dX, float* dW, float* dW_t, hipStream_t s, bool rm, SgdStep* step)
 {
+    // the in-place step applies to the column pass that also yields dW (single batch tile)
+    float* apply = (step && dX && dW && p.ntiles == 1) ? L->vals_t : nullptr;
+    const float lr = step ? step->lr : 0.0f;
     if (rm) {
         // batch-major operands: every pass is the LDS key-major kernel
         if (dW && !dX) {
@@ -1951,10 +1985,12 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             ProfScope prof(KC_SPMM_DX, s);
             return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s, true);
         }
-        if (!dW_t) return SNACK_ERR_INVALID_ARG;
+        if (!dW_t && !apply) return SNACK_ERR_INVALID_ARG;
         {
+            // the canonical dW is recomputed below, so with the step the column order needs no dW of its own
             ProfScope prof(KC_SPMM_DX, s);
-            SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s, true));
+            SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, apply ? nullptr : dW_t, B, s, true, apply, lr));
+            if (apply) step->done = true;
         }
         ProfScope prof(KC_SDDMM_DW, s);
         return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true);
@@ -1969,9 +2005,14 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         {
+            // with the step, dW in column order is still needed where the canonical dW is permuted from it
+            const bool recompute = p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p);
+            float* dwo = (apply && recompute) ? nullptr : dW_t;
             ProfScope prof(KC_SPMM_DX, s);
-            if (use_tile(L, L->tr, p)) SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s)));
-            else SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dW_t, B, s));
+            if (use_tile(L, L->tr, p))
+                SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, apply, lr)));
+            else SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, false, apply, lr));
+            if (apply) step->done = true;
         }
         ProfScope prof(KC_SDDMM_DW, s);
         if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {

@@ -110,6 +110,18 @@ snack_status snack_backward(snack_layer* layer, const float* X, const float* dY,
                             float* dX, float* dW, int32_t B, snack_stream stream);
 
 /*
+ * Backward and the SGD step of the "Padded-CSR" post's section 7.3 training loop
+ * (the values move against their gradient) in one call: the same results, bit
+ * for bit, as snack_backward(layer, X, dY, dX, dW, B) followed by
+ * snack_sgd_step(layer, dW, lr).  X, dY, dW are required (dW written as by
+ * snack_backward); dX may be NULL.  Where the column pass computes dW, it also
+ * steps the layer's column-ordered value copy in place, so the step moves one
+ * copy's worth of bytes less than the two separate calls.
+ */
+snack_status snack_backward_sgd(snack_layer* layer, const float* X, const float* dY, float* dX, float* dW,
+                                float lr, int32_t B, snack_stream stream);
+
+/*
  * In-place drop / regrow with nnz fixed ("Padded-CSR" section 4.3: drop some
  * live entries, grow the same number elsewhere; SNACK paper Figure 1: in place
  * on the triple).  Drops the n_drop entries of smallest |value| -- order key

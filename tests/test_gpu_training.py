@@ -95,3 +95,43 @@ def test_dw_row_and_column_orders_bit_identical(M, K, nnz):
             assert np.array_equal(v1, (v0 - host(dW)).astype(np.float32))
     finally:
         layer.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(2000, 1500, 300000), (768, 3072, 23593), (10000, 10000, 5_000_000)])
+def test_backward_sgd_matches_backward_then_sgd(M, K, nnz):
+    """The fused backward + SGD step equals snack_backward followed by
+    snack_sgd_step bit for bit (dX, dW and both value copies), for every batch
+    plan; twice per plan, so the second call starts from stepped values.  The
+    768 x 3072 layer's short keys take the fallback (no in-place step)."""
+    L = lib()
+    rows, cols, vals = random_layer(M, K, nnz, f"fused/{M}x{K}")
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    lr = 0.01
+    try:
+        for B in (1, 2, 3, 4, 8, 16, 32, 64, 100):
+            X = dev(normal((B, K), f"fused/{M}x{K}/X/{B}"))
+            dY = dev(normal((B, M), f"fused/{M}x{K}/dY/{B}"))
+            for it in range(2):
+                say("fused backward+sgd", M, K, "B", B, "it", it)
+                dXa, dWa = a.backward(X, dY)
+                a.sgd_step(dWa, lr)
+                dXb, dWb = b.backward_sgd(X, dY, lr)
+                assert np.array_equal(host(dXa).view(np.uint32), host(dXb).view(np.uint32)), f"dX B={B}"
+                assert np.array_equal(host(dWa).view(np.uint32), host(dWb).view(np.uint32)), f"dW B={B}"
+                va, vb = host(a.export()[2]), host(b.export()[2])
+                assert np.array_equal(va.view(np.uint32), vb.view(np.uint32)), f"values B={B}"
+                _, pm, _, _, vta = (host(t) for t in a.export_index(with_values=True))
+                _, _, _, _, vtb = (host(t) for t in b.export_index(with_values=True))
+                assert np.array_equal(vta.view(np.uint32), vtb.view(np.uint32)), f"column-order values B={B}"
+                assert np.array_equal(vtb.view(np.uint32), vb[pm].view(np.uint32)), f"copies diverged B={B}"
+        # without dX the column pass does not run: the step falls back to the separate update
+        X = dev(normal((8, K), f"fused/{M}x{K}/X/nodx")); dY = dev(normal((8, M), f"fused/{M}x{K}/dY/nodx"))
+        _, dWa = a.backward(X, dY, want_dx=False)
+        a.sgd_step(dWa, lr)
+        _, dWb = b.backward_sgd(X, dY, lr, want_dx=False)
+        assert np.array_equal(host(dWa).view(np.uint32), host(dWb).view(np.uint32))
+        assert np.array_equal(host(a.export()[2]).view(np.uint32), host(b.export()[2]).view(np.uint32))
+    finally:
+        a.close()
+        b.close()
