@@ -754,6 +754,42 @@ __global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint
     }
 }
 
+// The bit walk is divergent (lanes hold different numbers of set bits), so it
+// only records each entry -- row, column and the old slot its value comes from
+// (-1: a grown cell, value 0) -- in a per-wave LDS list at the entry's offset
+// from the list's first output slot; the list is then written out with every
+// lane active, entries lane, lane+64, ..., so rows, cols and vals are stored as
+// contiguous runs and the old values are read four at a time per lane.
+constexpr int kEmitList = 512;   // entries per wave
+
+__device__ inline void emit_flush(const int32_t* lr, const int32_t* lc, const int32_t* ls, int32_t n, int64_t out0,
+                                  int64_t nnz, const float* __restrict__ vold, int32_t* __restrict__ rows,
+                                  int32_t* __restrict__ cols, float* __restrict__ vals, int lane)
+{
+    if ((int64_t)n > nnz - out0) n = (int32_t)(nnz - out0);   // never past the triple (occ holds nnz bits)
+    __builtin_amdgcn_wave_barrier();
+    for (int32_t i0 = 0; i0 < n; i0 += 4 * kWave) {
+        float v[4];
+        int32_t src[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int32_t i = i0 + q * kWave + lane;
+            src[q] = i < n ? ls[i] : -1;
+            v[q] = vold[src[q] >= 0 ? src[q] : 0];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int32_t i = i0 + q * kWave + lane;
+            if (i < n) {
+                rows[out0 + i] = lr[i];
+                cols[out0 + i] = lc[i];
+                vals[out0 + i] = src[q] >= 0 ? v[q] : 0.0f;
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <bool DIRECT, bool WIDE>
 __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, const uint32_t* __restrict__ old_bm,
@@ -769,10 +805,23 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     const int64_t u0 = (int64_t)blockIdx.x * (kEmitThreads / kWave);
     int64_t run_o, run_d;
     if constexpr (DIRECT) {
+        // eight loads of each count in flight per thread (clamped indexes, no branch around a load)
         int32_t a = 0, b = 0;
-        for (int64_t i = threadIdx.x; i < u0; i += kEmitThreads) {
-            a += occ_cnt[i];
-            b += old_cnt[i];
+        for (int64_t i0 = threadIdx.x; i0 < u0; i0 += 8 * kEmitThreads) {
+            int32_t x[8], y[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t i = i0 + q * kEmitThreads;
+                const int64_t ic = i < u0 ? i : 0;
+                x[q] = occ_cnt[ic];
+                y[q] = old_cnt[ic];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool in = i0 + q * kEmitThreads < u0;
+                a += in ? x[q] : 0;
+                b += in ? y[q] : 0;
+            }
         }
         a = wave_sum(a);
         b = wave_sum(b);
@@ -795,7 +844,15 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         run_o = u < units ? occ_cnt[u] : 0;
         run_d = u < units ? old_cnt[u] : 0;
     }
+    __shared__ int32_t lr_[kEmitThreads / kWave][kEmitList];
+    __shared__ int32_t lc_[kEmitThreads / kWave][kEmitList];
+    __shared__ int32_t ls_[kEmitThreads / kWave][kEmitList];
     if (u >= units) return;
+    int32_t* lr = lr_[threadIdx.x / kWave];
+    int32_t* lc = lc_[threadIdx.x / kWave];
+    int32_t* ls = ls_[threadIdx.x / kWave];
+    int32_t nl = 0;      // entries in the list (wave-uniform)
+    int64_t lout0 = 0;   // output slot of the list's first entry
     uint32_t om_[kEmitSweeps], dm_[kEmitSweeps], km_[kEmitSweeps];
 #pragma unroll
     for (int it = 0; it < kEmitSweeps; ++it) {
@@ -811,11 +868,22 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         const uint32_t om = om_[it], dm = dm_[it], km = km_[it];
         const int32_t a = __popc(om), b = __popc(dm);
         const int32_t ia = wave_incl(a), ib = wave_incl(b);
+        const int32_t ta = __shfl(ia, kWave - 1, kWave);
+        const int64_t sweep0 = run_o;
         int64_t out = run_o + ia - a;
         const int64_t oldbase = run_d + ib - b;
-        run_o += __shfl(ia, kWave - 1, kWave);
+        run_o += ta;
         run_d += __shfl(ib, kWave - 1, kWave);
         if (wpre && w < words) wpre[w] = (int32_t)out;
+        // the list takes this sweep if it fits (sweeps of a dense layer may not)
+        const bool listed = ta <= kEmitList;
+        if (nl > 0 && (!listed || nl + ta > kEmitList)) {
+            emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, lane);
+            nl = 0;
+        }
+        if (listed && nl == 0) lout0 = sweep0;
+        int32_t lp = (int32_t)(out - lout0);
+        if (listed) nl += ta;
         if (!om) continue;
         int64_t r, c;
         if constexpr (WIDE) {
@@ -839,14 +907,21 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
                 c -= K;
                 ++r;
             }
-            float v = 0.0f;
-            if ((km >> bit) & 1u) v = vold[oldbase + __popc(dm & ((1u << bit) - 1u))];
-            rows[out] = (int32_t)r;
-            cols[out] = (int32_t)c;
-            vals[out] = v;
+            const int32_t src = ((km >> bit) & 1u) ? (int32_t)(oldbase + __popc(dm & ((1u << bit) - 1u))) : -1;
+            if (listed) {
+                lr[lp] = (int32_t)r;
+                lc[lp] = (int32_t)c;
+                ls[lp] = src;
+                ++lp;
+            } else {
+                rows[out] = (int32_t)r;
+                cols[out] = (int32_t)c;
+                vals[out] = src >= 0 ? vold[src] : 0.0f;
+            }
             ++out;
         }
     }
+    if (nl > 0) emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, lane);
 }
 
 // ---- the column view from the new bitmap -----------------------------------
