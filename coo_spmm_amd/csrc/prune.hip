@@ -93,10 +93,12 @@ constexpr int kSelCopies = 32;
 constexpr int kSelPasses = 4;
 constexpr int kSelHist = kSelCopies * 256;   // words of one pass's histograms
 
-__global__ void prune_init_kernel(uint32_t* __restrict__ state, uint32_t* __restrict__ hist, uint32_t rank0)
+__global__ void prune_init_kernel(uint32_t* __restrict__ state, uint32_t* __restrict__ hist, uint32_t rank0,
+                                  int32_t* __restrict__ fill, int32_t nfill)
 {
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int64_t i = i0; i < (int64_t)kSelPasses * kSelHist; i += (int64_t)gridDim.x * blockDim.x) hist[i] = 0u;
+    for (int64_t i = i0; i < nfill; i += (int64_t)gridDim.x * blockDim.x) fill[i] = 0;
     if (i0 < 16) state[i0] = i0 == 1 ? rank0 : 0u;
 }
 
@@ -193,17 +195,13 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
         p[i] = v;
 }
 
-// zero three bitmaps of `words` words and `nfill` counters in one launch
-__global__ void zero_bitmaps_kernel(uint32_t* __restrict__ a, uint32_t* __restrict__ b, uint32_t* __restrict__ c,
-                                    int64_t words, int32_t* __restrict__ fill, int32_t nfill)
+// clear two bitmaps of `words` words (layers whose bitmap is large next to the entries)
+__global__ void zero2_kernel(uint32_t* __restrict__ a, uint32_t* __restrict__ b, int64_t words)
 {
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t i = i0; i < words; i += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x) {
         a[i] = 0u;
         b[i] = 0u;
-        c[i] = 0u;
     }
-    for (int64_t i = i0; i < nfill; i += (int64_t)gridDim.x * blockDim.x) fill[i] = 0;
 }
 
 __device__ inline uint64_t cell_of(const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, int64_t k,
@@ -245,12 +243,23 @@ __device__ inline int32_t block_excl(int32_t v, int32_t* smem /*[waves]*/, int32
 
 // Number of keys equal to T per tile; needed only when the ties are dropped in
 // part (their rank in slot order then decides), otherwise the kernel returns.
-__global__ void __launch_bounds__(kKeepThreads) eq_tiles_kernel(const float* __restrict__ vals, int64_t n,
+__global__ void __launch_bounds__(kKeepThreads) eq_tiles_kernel(const int32_t* __restrict__ rows,
+                                                                const int32_t* __restrict__ cols,
+                                                                const float* __restrict__ vals, int64_t n, int32_t K,
                                                                 uint32_t* __restrict__ state,
                                                                 const uint32_t* __restrict__ hist,
-                                                                int32_t* __restrict__ tile_eq)
+                                                                int32_t* __restrict__ tile_eq,
+                                                                uint32_t* __restrict__ kept_bm,
+                                                                uint32_t* __restrict__ old_bm)
 {
     __shared__ int32_t smem[kKeepThreads / kWave];
+    // the word of this tile's first entry is the only one it may share with the
+    // tile before, which both fill with atomic ORs: clear it for them
+    if (threadIdx.x == 0 && blockIdx.x > 0) {
+        const uint64_t w = cell_of(rows, cols, (int64_t)blockIdx.x * kKeepTile, K) >> 5;
+        kept_bm[w] = 0u;
+        old_bm[w] = 0u;
+    }
     // the last pass's pick gives T, the rank among keys equal to T, and their count
     const SelPick pk = sel_pick(hist + (kSelPasses - 1) * kSelHist, state[3 + 3 * (kSelPasses - 2)],
                                 state[4 + 3 * (kSelPasses - 2)], 0);
@@ -275,24 +284,29 @@ __global__ void __launch_bounds__(kKeepThreads) eq_tiles_kernel(const float* __r
 // The drop decision and the bitmaps, tile by tile.  An entry is dropped when
 // its key is below T, or equal to T and among the first `ties` equal keys in
 // slot order (the rank is counted only when ties are dropped in part).  The
-// tile's cells ascend, so its bits fall in one contiguous run of bitmap words:
-// when the run fits in LDS the words are assembled there and stored coalesced
-// (the first and last word, which neighbouring tiles may share, with atomic
-// ORs); otherwise every entry ORs its bits into global memory.  `old` gets
-// every entry, `kept` and `occ` the kept ones (bitmaps zero beforehand).  The
+// tile's cells ascend, so its bits fall in one contiguous run of bitmap words;
+// the tile owns every word from its first entry's word up to the next tile's
+// first entry's word (tile 0 also those before, the last tile those after) and
+// stores each whole, zeros included, so the bitmaps need no clearing.  Only a
+// tile's first and last words can hold another tile's bits: those two are
+// combined with atomic ORs (the first word of every tile was cleared before).
+// When the run fits in LDS the words are assembled there and stored coalesced;
+// otherwise the tile clears the words it alone holds and every entry ORs its
+// bits into global memory.  `old` gets every entry, `kept` the kept ones.  The
 // values are copied for the rebuild.
 constexpr int kKeepSpan = 4096;   // bitmap words assembled in LDS per tile
 
 template <bool DIRECT>
 __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ cols, const float* __restrict__ vals, int64_t n,
-    int32_t K, const uint32_t* __restrict__ state, const int32_t* __restrict__ tile_eq, float* __restrict__ vcopy,
-    uint32_t* __restrict__ kept_bm, uint32_t* __restrict__ occ_bm, uint32_t* __restrict__ old_bm)
+    int32_t K, int64_t words, int cleared, const uint32_t* __restrict__ state, const int32_t* __restrict__ tile_eq,
+    float* __restrict__ vcopy, uint32_t* __restrict__ kept_bm, uint32_t* __restrict__ old_bm)
 {
     __shared__ uint32_t w_kept[kKeepSpan];
     __shared__ uint32_t w_old[kKeepSpan];
     __shared__ int32_t smem[kKeepThreads / kWave];
-    __shared__ uint64_t s_first, s_last;
+    __shared__ uint64_t s_first, s_last, s_end;
+    __shared__ int s_pshared, s_nshared;
     const uint32_t T = state[0];
     const uint32_t ties = state[1] + 1u;
     const bool partial = ties_partial(state);
@@ -302,6 +316,12 @@ __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
     if (threadIdx.x == 0) {
         s_first = cell_of(rows, cols, base, K) >> 5;
         s_last = cell_of(rows, cols, base + cnt - 1, K) >> 5;
+        // words up to (not including) the next tile's first word are this tile's
+        const bool more = base + cnt < n;
+        const uint64_t next = more ? cell_of(rows, cols, base + cnt, K) >> 5 : (uint64_t)words;
+        s_end = next;
+        s_nshared = more && next == s_last;
+        s_pshared = tile > 0 && (cell_of(rows, cols, base - 1, K) >> 5) == s_first;
     }
     int32_t eqp = 0;
     if (partial) {
@@ -336,13 +356,36 @@ __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
             }
         }
     }
-    __syncthreads();   // s_first, s_last
-    const uint64_t wf = s_first, wl = s_last;
+    __syncthreads();   // s_first, s_last, s_end, s_*shared
+    const uint64_t wf = s_first, wl = s_last, we = s_end;
+    const bool pshared = s_pshared != 0, nshared = s_nshared != 0;
     const bool in_lds = wl - wf < (uint64_t)kKeepSpan;
+    // words this tile holds alone and no entry of it sets: before its first word
+    // (tile 0) and between its last word and the next tile's first (a sparse
+    // layer's bitmaps are cleared beforehand by a full grid instead)
+    if (!cleared) {
+        const uint64_t g0 = tile == 0 ? 0ull : wf;
+        for (uint64_t w = g0 + threadIdx.x; w < wf; w += kKeepThreads) {
+            kept_bm[w] = 0u;
+            old_bm[w] = 0u;
+        }
+        for (uint64_t w = wl + 1 + threadIdx.x; w < we; w += kKeepThreads) {
+            kept_bm[w] = 0u;
+            old_bm[w] = 0u;
+        }
+    }
     if (in_lds) {
         for (int i = threadIdx.x; i <= (int)(wl - wf); i += kKeepThreads) {
             w_kept[i] = 0u;
             w_old[i] = 0u;
+        }
+    } else if (!cleared) {
+        // the words of the run no other tile touches are cleared here first
+        // (atomic stores: the ORs below are atomics on the same words)
+        const int64_t c0 = (int64_t)wf + (pshared ? 1 : 0), c1 = (int64_t)wl - (nshared ? 1 : 0);
+        for (int64_t w = c0 + threadIdx.x; w <= c1; w += kKeepThreads) {
+            __hip_atomic_store(&kept_bm[w], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&old_bm[w], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     __syncthreads();
@@ -380,10 +423,7 @@ __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
                 if (keep) atomicOr(&w_kept[i], bit);
             } else {
                 atomicOr(&old_bm[p >> 5], bit);
-                if (keep) {
-                    atomicOr(&kept_bm[p >> 5], bit);
-                    atomicOr(&occ_bm[p >> 5], bit);
-                }
+                if (keep) atomicOr(&kept_bm[p >> 5], bit);
             }
         }
         run += tot;
@@ -394,16 +434,12 @@ __global__ void __launch_bounds__(kKeepThreads) keep_tiles_kernel(
     for (int i = threadIdx.x; i < span; i += kKeepThreads) {
         const uint64_t w = wf + i;
         const uint32_t k = w_kept[i], o = w_old[i];
-        if (i == 0 || i == span - 1) {
+        if ((i == 0 && pshared) || (i == span - 1 && nshared)) {
             if (o) atomicOr(&old_bm[w], o);
-            if (k) {
-                atomicOr(&kept_bm[w], k);
-                atomicOr(&occ_bm[w], k);
-            }
+            if (k) atomicOr(&kept_bm[w], k);
         } else {
             old_bm[w] = o;
             kept_bm[w] = k;
-            occ_bm[w] = k;
         }
     }
 }
@@ -497,6 +533,7 @@ __global__ void __launch_bounds__(kGenThreads) gen_bucket_kernel(uint64_t seed, 
 __global__ void __launch_bounds__(kClaimThreads) region_claim_kernel(int rb, int sb, uint64_t words_total,
                                                                      int32_t cap, int32_t* __restrict__ fill,
                                                                      const uint64_t* __restrict__ bucket,
+                                                                     const uint32_t* __restrict__ src_bm,
                                                                      uint32_t* __restrict__ occ_bm,
                                                                      uint8_t* __restrict__ acc8,
                                                                      const uint32_t* __restrict__ state)
@@ -522,7 +559,7 @@ __global__ void __launch_bounds__(kClaimThreads) region_claim_kernel(int rb, int
         if (w0 >= words_total) break;   // uniform
         const uint64_t left = words_total - w0;
         const uint32_t nw = left < (uint64_t)(1u << (sb - 5)) ? (uint32_t)left : (1u << (sb - 5));
-        for (uint32_t i = threadIdx.x; i < nw; i += kClaimThreads) bm[i] = occ_bm[w0 + i];
+        for (uint32_t i = threadIdx.x; i < nw; i += kClaimThreads) bm[i] = src_bm[w0 + i];
         for (int i = threadIdx.x; i < kTabSlots; i += kClaimThreads) tab[i] = kEmpty;
         __syncthreads();
         for (int32_t k = threadIdx.x; k < n; k += kClaimThreads) {
@@ -1413,27 +1450,31 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
 
     // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
     {
-        hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1));
+        hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1),
+                           ps.fill, kMaxRegions);
         const unsigned nsel = (unsigned)((nnz + (int64_t)kSelThreads * kSelPer - 1) / ((int64_t)kSelThreads * kSelPer));
         hipLaunchKernelGGL(sel_pass_kernel<0>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
         hipLaunchKernelGGL(sel_pass_kernel<1>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
         hipLaunchKernelGGL(sel_pass_kernel<2>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
         hipLaunchKernelGGL(sel_pass_kernel<3>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
         SNACK_HIP(hipGetLastError());
-        hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->vals, nnz,
-                           ps.state, ps.hist, ps.tile_eq);
-        hipLaunchKernelGGL(zero_bitmaps_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm,
-                           ps.occ_bm, ps.old_bm, ps.words, ps.fill, kMaxRegions);
+        hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows, L->cols,
+                           L->vals, nnz, L->K, ps.state, ps.hist, ps.tile_eq, ps.kept_bm, ps.old_bm);
+        // a sparse layer's bitmap is cleared by a full grid (the tiles would each clear long gaps)
+        const int cleared = ps.words > ps.ktiles * (int64_t)kKeepSpan ? 1 : 0;
+        if (cleared)
+            hipLaunchKernelGGL(zero2_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.old_bm,
+                               ps.words);
         SNACK_HIP(hipGetLastError());
         if (ps.ktiles <= kKeepDirect) {
             hipLaunchKernelGGL(keep_tiles_kernel<true>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
-                               L->cols, L->vals, nnz, L->K, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm, ps.occ_bm,
+                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
                                ps.old_bm);
         } else {
             // a scan of zeros when every tie is dropped (the counts were not written then; they are not used)
             SNACK_CHECK(exclusive_scan_i32(ps.tile_eq, ps.tile_eq, ps.ktiles, nullptr, ps.scan, s));
             hipLaunchKernelGGL(keep_tiles_kernel<false>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
-                               L->cols, L->vals, nnz, L->K, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm, ps.occ_bm,
+                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
                                ps.old_bm);
         }
         SNACK_HIP(hipGetLastError());
@@ -1445,6 +1486,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     uint64_t t0 = 0;
     int batches = 0;
     int shrink = 0;   // halvings of the batch after a bucket overflow
+    bool claimed = false;   // a batch has written occ
     const uint64_t words_total = (uint64_t)ps.words;
     while (need > 0) {
         const double p_empty = (double)(N - (uint64_t)kept - (uint64_t)got) / (double)N;
@@ -1459,8 +1501,10 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         const int32_t nsum = (int32_t)((T + kSumTile - 1) / kSumTile);
         hipLaunchKernelGGL(gen_bucket_kernel, dim3(ntiles), dim3(kGenThreads), 0, s, L->seed, L->epoch, t0, T, N,
                            g.rb, g.R, g.cap, ps.fill, ps.bucket, ps.acc8, ps.state);
+        // the first batch starts from the kept cells (occ is first written, whole, by this pass)
         hipLaunchKernelGGL(region_claim_kernel, dim3((unsigned)g.R), dim3(kClaimThreads), lds, s, g.rb, g.sb,
-                           words_total, g.cap, ps.fill, ps.bucket, ps.occ_bm, ps.acc8, ps.state);
+                           words_total, g.cap, ps.fill, ps.bucket, claimed ? ps.occ_bm : ps.kept_bm, ps.occ_bm,
+                           ps.acc8, ps.state);
         hipLaunchKernelGGL(tile_sum_kernel, dim3((unsigned)nsum), dim3(256), 0, s, ps.acc8, T, ps.tsum, ps.state);
         hipLaunchKernelGGL(cut_kernel, dim3(1), dim3(1024), 0, s, ps.tsum, nsum, ps.acc8, T, need, ps.state);
         hipLaunchKernelGGL(give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kThreads), 0, s,
@@ -1477,6 +1521,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
             continue;
         }
         shrink = 0;
+        claimed = true;
         const int64_t taken = (int64_t)res[1];
         got += taken;
         need -= taken;
