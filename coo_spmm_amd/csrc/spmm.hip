@@ -1972,8 +1972,11 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
                                  float* dX, float* dW, float* dW_t, hipStream_t s, bool rm, SgdStep* step)
 {
-    // the in-place step applies to the column pass that also yields dW (single batch tile)
-    float* apply = (step && dX && dW && p.ntiles == 1) ? L->vals_t : nullptr;
+    // the in-place step applies to the column pass that also yields dW (single batch tile).  At the
+    // 64-column tile that pass is bound by issue slots and must write dW in column order anyway (the
+    // canonical dW is permuted from it): there the extra store costs more than the separate step of
+    // both copies, which takes over.
+    float* apply = (step && dX && dW && p.ntiles == 1 && p.btile <= 32) ? L->vals_t : nullptr;
     const float lr = step ? step->lr : 0.0f;
     if (rm) {
         // batch-major operands: every pass is the LDS key-major kernel
