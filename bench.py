@@ -20,8 +20,10 @@ region runs without instrumentation; the same number of steps then runs a
 second time with HIP events around every kernel class, which gives
 `per_batch` (forward+backward microseconds per iteration: fwd, dX, dW and
 their activation transposes) and `roofline` (the dominant kernel against the
-8 TB/s HBM peak).  `cpu_baseline` is the fp64 oracle timed on one host core on
-a bounded sample.
+8 TB/s HBM peak).  `cold` times forward + backward once per repetition right
+after a 512 MiB write that evicts the Infinity Cache and the L2s (the triple
+then streams from HBM; the warm figures above run with it cache-resident).
+`cpu_baseline` is the fp64 oracle timed on one host core on a bounded sample.
 """
 from __future__ import annotations
 
@@ -88,6 +90,9 @@ def main():
     ap.add_argument("--prune-every", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="time without per-kernel HIP events")
+    ap.add_argument("--cold-reps", type=int, default=3,
+                    help="cold forward + backward timings per batch size, each after a 512 MiB write that "
+                         "evicts the Infinity Cache and the L2s (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a reference dispatch of known "
                          "size for hardware byte counters)")
@@ -182,6 +187,29 @@ def main():
         wall_prof = time.perf_counter() - t2
         L.snack_profile_enable(False)
 
+    # cold: forward + backward alone, each right after a 512 MiB write (more than the 256 MB Infinity
+    # Cache plus the L2s), so the triple and the index come from HBM; timed with events on the launch stream
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cold = {"reps": args.cold_reps, "flush_mib": 512, "per_batch": {}}
+        for B in batches:
+            b = bufs[B]
+            ts = []
+            for rep in range(args.cold_reps):
+                flush.fill_(float(rep + 1))
+                e0.record(stream)
+                L.snack_forward(layer.h, b["X"], b["Y"], stream)
+                L.snack_backward(layer.h, b["X"], b["dY"], b["dX"], b["dW"], stream)
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = sorted(ts)[len(ts) // 2]
+            cold["per_batch"][str(B)] = {"fwd_bwd_us": round(us, 2),
+                                         "fwd_bwd_GBps": round(fwd_bwd_bytes(nnz, M, K, B) / (us * 1e-6) / 1e9, 1)}
+        del flush
+
     iters_per_b = args.steps
     credited = sum((fwd_bwd_bytes(nnz, M, K, B) + 12 * B * M + 12 * nnz) * iters_per_b for B in batches)
     value_gbps = credited / wall / 1e9
@@ -240,6 +268,7 @@ def main():
         "prune_regrow_us_per_call": round(ms_pr * 1e3 / n_pr, 1) if n_pr else None,
         "prune_regrow_calls": n_pr,
         "roofline": roofline,
+        "cold": cold,
     }
 
     if not args.no_cpu_baseline:
