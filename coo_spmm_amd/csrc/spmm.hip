@@ -1725,7 +1725,7 @@ snack_status dispatch_seg(const BatchPlan& p, int64_t cap, const View& va, const
 // widest batch tile that recomputes dW over the row view instead of permuting
 // the column-order dW; up to here every kernel pair that can meet gives each
 // lane the same batch columns, so the two dW orders agree bit for bit
-constexpr int kKeyedRecomputeMax = 16;
+constexpr int kKeyedRecomputeMax = 32;
 
 inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
 {
@@ -1801,6 +1801,17 @@ inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
 {
     const int i = tile_index(p.btile);
     return i >= 0 && p.ntiles == 1 && L->nnz > 0 && use_keyed(v, L->nnz, p) && v.split[i].S >= 1;
+}
+
+// dW in canonical order by its own pass over the row view (else permuted from
+// the column pass's dW).  The two orders must agree bit for bit: up to batch
+// tile 16 every kernel pair that can meet gives a lane the same columns and the
+// same reduction; at 32 the tiled kernel interleaves a lane's columns and the
+// key-major one does not, so both views must take the same family.
+inline bool recompute_dw(const snack_layer* L, const BatchPlan& p)
+{
+    if (p.btile > kKeyedRecomputeMax || !use_keyed(L->fwd, L->nnz, p)) return false;
+    return p.btile <= 16 || use_tile(L, L->tr, p) == use_tile(L, L->fwd, p);
 }
 
 template <bool DW, bool SPMM>
@@ -2009,7 +2020,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         {
             // with the step, dW in column order is still needed where the canonical dW is permuted from it
-            const bool recompute = p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p);
+            const bool recompute = recompute_dw(L, p);
             float* dwo = (apply && recompute) ? nullptr : dW_t;
             ProfScope prof(KC_SPMM_DX, s);
             if (use_tile(L, L->tr, p))
@@ -2018,7 +2029,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             if (apply) step->done = true;
         }
         ProfScope prof(KC_SDDMM_DW, s);
-        if (p.btile <= kKeyedRecomputeMax && use_keyed(L->fwd, L->nnz, p)) {
+        if (recompute_dw(L, p)) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view
             if (use_tile(L, L->fwd, p)) return launch_tile<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
             return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
