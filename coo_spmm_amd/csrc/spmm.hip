@@ -1082,7 +1082,8 @@ __device__ inline float lane_xor(float x)
     static_assert(M == 1 || M == 2 || M == 4 || M == 8, "within a row");
     if constexpr (M == 1) return dpp_f<0xB1>(0.0f, x);            // quad_perm [1,0,3,2]
     else if constexpr (M == 2) return dpp_f<0x4E>(0.0f, x);       // quad_perm [2,3,0,1]
-    else if constexpr (M == 4) return dpp_f<0x1B>(0.0f, dpp_f<0x141>(0.0f, x));   // half-row mirror, quad reverse
+    else if constexpr (M == 4)   // half-row mirror, then quad reverse (every source lane exists: no old value)
+        return dpp_f<0x1B>(0.0f, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true)));
     else return dpp_f<0x128>(0.0f, x);                            // row rotate by 8
 }
 // value of lane U0 of this lane's group of BT lanes (groups are rows, half
@@ -1105,33 +1106,32 @@ __device__ inline int32_t group_bcast0(int32_t x)
     else if constexpr (BT == 4) return dpp_i<U0 * 0x55>(0, x);
     else return dpp_i<U0 | (U0 << 2) | ((2 + U0) << 4) | ((2 + U0) << 6)>(0, x);   // pair broadcast
 }
-// the partner's value across lane bit 5 (HALF = 32) or bit 4 (HALF = 16)
-template <int HALF>
-__device__ inline float lane_swap_recv(float x, bool hi)
-{
-    const auto r = HALF == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
-                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(hi ? r[0] : r[1]);
-}
-// The partner's value across lane bit BIT (bits 5 and 4 by lane swaps, lower
-// bits by DPP inside a row).
-template <int BIT>
-__device__ inline float xrecv(float x, bool hi)
-{
-    if constexpr (BIT == 5) return lane_swap_recv<32>(x, hi);
-    else if constexpr (BIT == 4) return lane_swap_recv<16>(x, hi);
-    else return lane_xor<(1 << BIT)>(x);
-}
-// one exchange-halves level over lane bit BIT on the first CNT values
+// one exchange-halves level over lane bit BIT on the first CNT values: the
+// lanes with the bit clear end with value i summed over both halves in a[i],
+// the others with value i + CNT / 2.  Across bits 5 and 4 one lane swap of the
+// pair does the exchange (the swap leaves value i of both halves in one
+// register and value i + CNT / 2 of both in the other, each in the lanes that
+// keep it); lower bits select what to send and take the partner's by DPP.
 template <int BIT, int CNT, int NB>
 __device__ inline void xlevel(float (&a)[NB], int lane)
 {
-    const bool hi = ((lane >> BIT) & 1) != 0;
+    if constexpr (BIT >= 4) {
 #pragma unroll
-    for (int i = 0; i < CNT / 2; ++i) {
-        const float sv = hi ? a[i] : a[i + CNT / 2];
-        const float kv = hi ? a[i + CNT / 2] : a[i];
-        a[i] = kv + xrecv<BIT>(sv, hi);
+        for (int i = 0; i < CNT / 2; ++i) {
+            const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]),
+                                                                       __float_as_uint(a[i + CNT / 2]), false, false)
+                                    : __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]),
+                                                                       __float_as_uint(a[i + CNT / 2]), false, false);
+            a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    } else {
+        const bool hi = ((lane >> BIT) & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < CNT / 2; ++i) {
+            const float sv = hi ? a[i] : a[i + CNT / 2];
+            const float kv = hi ? a[i + CNT / 2] : a[i];
+            a[i] = kv + lane_xor<(1 << BIT)>(sv);
+        }
     }
 }
 // NB values (4 or 8) summed over the G = 64 / BT groups of a wave: exchange
@@ -1196,8 +1196,9 @@ __device__ inline void reduce4_dpp(float (&d)[4], int bl)
 }
 
 // A block of the tile kernel: group g owns entries base + g*U + u (u < U);
-// lane u of the group loads entry u (clamped, unconditional loads keep every
-// block in flight), and the group's lanes get each entry by a broadcast
+// lane bl of the group loads entry bl / (BT / U) (clamped, unconditional loads
+// keep every block in flight; the lane that ends up owning an entry's reduced
+// dW is one that loaded it), and the group's lanes get each entry by a broadcast
 // inside the group.  Before use, entries outside [base, lim) are neutralised
 // per lane -- value 0 and an all-zero row staged after the slice -- so the
 // per-entry work needs no masks, and the index becomes the entry's byte offset
@@ -1206,28 +1207,30 @@ template <int BT, int U>
 struct TileBlock {
     static constexpr int G = kWave / BT;
     static constexpr int STEP = G * U;
-    static_assert(U <= BT && (U % 2) == 0, "a group's lanes load its entries");
+    static constexpr int LS = BT / U;   // lanes per loaded entry
+    static_assert(U <= BT && (U % 2) == 0 && BT % U == 0, "a group's lanes load its entries");
     int32_t nidx;
     float nval;
     int32_t noff;
     float mval;
 
+    // lk = g * U + bl / LS: the lane's entry within the block.  The block's
+    // base pointers are uniform, so the per-lane part is a small byte offset.
     template <bool SPMM>
     __device__ inline void load(const int32_t* __restrict__ idx, const float* __restrict__ vals, int32_t base,
-                                int32_t lim, int g, int bl)
+                                int32_t lim, int32_t lk)
     {
-        const int32_t top = lim > 0 ? lim - 1 : 0;
-        const int32_t k = base + g * U + (bl < U ? bl : U - 1);
-        const uint32_t kc = (uint32_t)(k < lim ? k : top);
-        nidx = idx[kc];
-        nval = SPMM ? vals[kc] : 0.0f;
+        const int32_t span = lim - base;
+        const uint32_t ob = (uint32_t)min(lk, span > 0 ? span - 1 : 0) * 4u;
+        nidx = *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(idx + base) + ob);
+        nval = SPMM ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(vals + base) + ob) : 0.0f;
     }
     // zero_off: the all-zero row staged after the slice, so a neutral entry
     // adds exactly 0 whatever the activations hold
-    __device__ inline void prepare(int32_t base, int32_t lim, int g, int bl, int32_t i0, int32_t row_bytes,
+    __device__ inline void prepare(int32_t base, int32_t lim, int32_t lk, int32_t i0, int32_t row_bytes,
                                    int32_t zero_off)
     {
-        const bool in = base + g * U + (bl < U ? bl : U - 1) < lim;
+        const bool in = lk < lim - base;
         noff = in ? (nidx - i0) * row_bytes : zero_off;
         mval = in ? nval : 0.0f;
     }
@@ -1236,12 +1239,12 @@ struct TileBlock {
     template <int U0>
     __device__ inline int32_t off_at(int32_t lane_off) const
     {
-        return group_bcast0<BT, U0>(noff) + lane_off;
+        return group_bcast0<BT, U0 * LS>(noff) + lane_off;
     }
     template <int U0>
     __device__ inline float val_at() const
     {
-        return __int_as_float(group_bcast<BT, U0>(__float_as_int(mval)));
+        return __int_as_float(group_bcast<BT, U0 * LS>(__float_as_int(mval)));
     }
 };
 
@@ -1278,14 +1281,23 @@ __device__ inline void tile_vals(const TB& b, float (&vv)[U])
     }
 }
 
+// element i (0 <= i < 2^30) of an array whose base is uniform: a small
+// per-lane byte offset on a scalar base
+__device__ inline float* lane_at(float* base, int32_t i)
+{
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(base) + (uint32_t)i * 4u);
+}
+
 // per-entry dot products with the key's operand row, reduced over the group
 // (pairs for 2-lane groups, fours otherwise) and stored; an entry's result is
-// the same sum of the same per-lane partials as in the key-major kernels
-// (with `apply`, the entry's value also takes its SGD step, from its value vv)
+// the same sum of the same per-lane partials as in the key-major kernels.
+// The lane left holding entry e's sum is one that loaded entry e (lk, value
+// own), so with `apply` the value takes its SGD step without a lane exchange.
 template <int BT, int NB, int U>
-__device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t lim, int g, int bl,
-                               float* __restrict__ dwo, const float (&vv)[U], float* __restrict__ apply, float lr)
+__device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], int32_t base, int32_t lim, int32_t lk,
+                               int bl, float* __restrict__ dwo, float own, float* __restrict__ apply, float lr)
 {
+    static_assert((BT == 2 && U == 2) || (BT >= 4 && U == 4), "owner lanes are loader lanes");
     if constexpr (BT == 2) {
 #pragma unroll
         for (int q = 0; q < U / 2; ++q) {
@@ -1300,10 +1312,9 @@ __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], in
             const bool hi = (bl & 1) != 0;
             const float r = lane_xor<1>(hi ? d[0] : d[1]);
             const float tot = (hi ? d[1] : d[0]) + r;
-            const int32_t k = base + g * U + 2 * q + bl;
-            if (k < lim) {
-                if (dwo) dwo[k] = tot;
-                if (apply) apply[k] = sgd_value(vv[2 * q + bl], tot, lr);
+            if (lk < lim - base) {
+                if (dwo) *lane_at(dwo + base, lk) = tot;
+                if (apply) *lane_at(apply + base, lk) = sgd_value(own, tot, lr);
             }
         }
     } else {
@@ -1319,13 +1330,10 @@ __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], in
                 d[t] = a;
             }
             reduce4_dpp<BT>(d, bl);
-            if ((bl % STRIDE) == 0) {
-                const int e = (bl / STRIDE) & 3;
-                const int32_t k = base + g * U + 4 * q + e;
-                if (k < lim) {
-                    if (dwo) dwo[k] = d[0];
-                    if (apply) apply[k] = sgd_value(vv[4 * q + e], d[0], lr);
-                }
+            // lane bl holds entry bl / STRIDE, the entry it loaded
+            if ((bl % STRIDE) == 0 && lk < lim - base) {
+                if (dwo) *lane_at(dwo + base, lk) = d[0];
+                if (apply) *lane_at(apply + base, lk) = sgd_value(own, d[0], lr);
             }
         }
     }
@@ -1333,9 +1341,9 @@ __device__ inline void tile_dw(const float (&y)[U][NB], const float (&h)[NB], in
 
 // the key's dW operand: the lane's NB columns of row key of a feature-major array
 template <int BT, int NB>
-__device__ inline void tile_h(const float* __restrict__ H, int64_t key, int bp, int bl, float (&h)[NB])
+__device__ inline void tile_h(const float* __restrict__ H, int64_t key, int bp, int32_t lane_off, float (&h)[NB])
 {
-    const float* p = H + key * bp + 4 * bl;
+    const float* p = reinterpret_cast<const float*>(reinterpret_cast<const char*>(H + key * bp) + (uint32_t)lane_off);
     const float4 a = *reinterpret_cast<const float4*>(p);
     h[0] = a.x;
     h[1] = a.y;
@@ -1413,16 +1421,17 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     cur.base = uni(__builtin_amdgcn_readlane(cur.tlo, 0));
     cur.p1 = uni(__builtin_amdgcn_readlane(cur.thi, 0));
 
+    const int32_t lk = g * U + bl / TB::LS;   // the lane's entry within a block
+    const int32_t lane_off = bl * 16;
     TileDesc d[D];
     TB blk[D];
     float hb[D][NB];
 #pragma unroll
     for (int q = 0; q < D; ++q) {
         cur.next(d[q], TB::STEP);
-        blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
-        if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, bl, hb[q]);
+        blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, lk);
+        if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, lane_off, hb[q]);
     }
-    const int32_t lane_off = bl * 16;
     float acc[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
@@ -1432,21 +1441,19 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     for (;;) {
 #pragma unroll
         for (int q = 0; q < D; ++q) {
-            blk[q].prepare(d[q].base, d[q].lim, g, bl, i0, BTILE * 4, nrow * BTILE * 4);
+            blk[q].prepare(d[q].base, d[q].lim, lk, i0, BTILE * 4, nrow * BTILE * 4);
             float y[U][NB];
             tile_gather<U, BT, NB>(blk[q], lane_off, y);
-            float vv[U];
             if constexpr (SPMM) {
+                float vv[U];
                 tile_vals<U>(blk[q], vv);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int n = 0; n < NB; ++n) acc[n] = fmaf(vv[u], y[u][n], acc[n]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) vv[u] = 0.0f;
             }
-            if constexpr (DW) tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, g, bl, A.dwo, vv, A.apply, A.lr);
+            if constexpr (DW)
+                tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, lk, bl, A.dwo, blk[q].mval, A.apply, A.lr);
             if constexpr (SPMM) {
                 if (d[q].last) {
                     // each lane ends with one column of the key's sum; one lane per column stores
@@ -1461,8 +1468,8 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
                 }
             }
             cur.next(d[q], TB::STEP);
-            blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, g, bl);
-            if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, bl, hb[q]);
+            blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, lk);
+            if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, lane_off, hb[q]);
         }
         if (!d[0].valid) break;
     }
