@@ -224,11 +224,14 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 // dW_t is non-null) and dW over the canonical view; either output may be null.
 // Requires a single batch tile when dW or dW_t is requested.
 // With `step`, where the column pass supports it, that pass also takes the SGD
-// step vals_t -= lr * dW in place (from the values it loads) and *step->done is
+// step vals_t -= lr * dW in place (from the values it loads) and step->done is
 // set; dW_t is then written only where the canonical dW is permuted from it.
+// Where the canonical dW comes from its own pass over the row view, that pass
+// also steps vals in place and step->canon_done is set.
 struct SgdStep {
     float lr;
-    bool done;
+    bool done;         // vals_t stepped
+    bool canon_done;   // vals stepped
 };
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
                                  float* dX, float* dW, float* dW_t, hipStream_t s, bool rm = false,

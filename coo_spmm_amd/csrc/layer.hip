@@ -318,7 +318,7 @@ extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const
     if (!L || !X || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
     if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
-    SgdStep step{lr, false};
+    SgdStep step{lr, false, false};
     SNACK_CHECK(backward_impl(L, X, dY, dX, dW, B, s, &step));
     if (!step.done) {
         // the column pass did not take the step: as snack_sgd_step would
@@ -327,6 +327,7 @@ extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const
         return sgd_update(L, dW, dwt, lr, s);
     }
     L->dwt_valid = false;
+    if (step.canon_done) return SNACK_OK;   // the row pass stepped the canonical values too
     return sgd_update_values(L, dW, lr, s);
 }
 

@@ -676,7 +676,9 @@ __device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int n
 }
 
 // One chunk's keys; the first block of every key is loaded at the key's start.
-template <int BT, int NB, int U, bool DW, bool SPMM>
+// VAL: the entries' values are loaded (always with SPMM; for a dW-only pass,
+// where `apply` takes each value's SGD step)
+template <int BT, int NB, int U, bool DW, bool SPMM, bool VAL>
 __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float* __restrict__ Gm, int bp, int B)
 {
     using KB = KeyBlock<BT, NB, U>;
@@ -696,14 +698,14 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
         float h[NB];
         if constexpr (DW) load_nb<NB>(A.H + (int64_t)r * bp + bcol, h);
         KB blk;
-        if (p0 < p1) blk.template load<SPMM>(A.idx, A.vals, p0, p1, lane, g);
+        if (p0 < p1) blk.template load<SPMM || VAL>(A.idx, A.vals, p0, p1, lane, g);
         for (int32_t base = p0; base < p1; base += KB::STEP) {
             int32_t ii[U];
             float vv[U];
             blk.take(ii, vv, g);
             float y[U][NB];
             key_gather<NB, U>(Gm, ii, bp, bcol, y);
-            blk.template load<SPMM>(A.idx, A.vals, base + KB::STEP, p1, lane, g);
+            blk.template load<SPMM || VAL>(A.idx, A.vals, base + KB::STEP, p1, lane, g);
             if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
             if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
         }
@@ -836,7 +838,7 @@ __device__ inline void load_h(const float* __restrict__ H, int64_t key, int bp, 
     }
 }
 
-template <int BT, int NB, int U, bool DW, bool SPMM, bool RM, class Stage>
+template <int BT, int NB, int U, bool DW, bool SPMM, bool RM, bool VAL, class Stage>
 __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int cend, const float* __restrict__ Gm,
                                            int bp, int B, Stage&& stage)
 {
@@ -858,7 +860,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
     // the block in flight and the dW operand of its key
     KB blk;
     float h[NB], hn[NB];
-    blk.template load<SPMM>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
+    blk.template load<SPMM || VAL>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
     if constexpr (DW) load_h<NB, RM>(A.H, kc.r, bp, bcol, B, A.nkeys, hn);
     stage();
     if (!any) return;
@@ -877,7 +879,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
         const int32_t nlim = last ? kc.np1 : p1;
         const int32_t nkey = last ? (kc.nr < 0 ? kc.r : kc.nr) : kc.r;
         if constexpr (DW) load_h<NB, RM>(A.H, nkey, bp, bcol, B, A.nkeys, hn);
-        blk.template load<SPMM>(A.idx, A.vals, nbase, nlim, lane, g);
+        blk.template load<SPMM || VAL>(A.idx, A.vals, nbase, nlim, lane, g);
         float y[U][NB];
         key_gather<NB, U>(Gm, ii, bp, bcol, y);
         if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
@@ -896,7 +898,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
     }
 }
 
-template <int BT, int NB, int U, bool DW, bool SPMM = true>
+template <int BT, int NB, int U, bool DW, bool SPMM = true, bool VAL = SPMM>
 __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 {
     const int bid = (int)blockIdx.x;
@@ -904,7 +906,7 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
     if (vb >= A.nblocks) return;
     const int c = vb * kWavesPerBlock + (int)(threadIdx.x / kWave);
     if (c >= A.nchunks) return;
-    key_chunk<BT, NB, U, DW, SPMM>(A, c, A.G, bp, B);
+    key_chunk<BT, NB, U, DW, SPMM, VAL>(A, c, A.G, bp, B);
 }
 
 // The same walk with the gathered operand [nidx, bp] staged in LDS: gathers
@@ -916,7 +918,7 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 constexpr int kLdsKeyWaves = 16;
 constexpr int kLdsU = 4;   // entries per lane per step
 
-template <int BT, int NB, int U, bool DW, bool SPMM = true, bool RM = false>
+template <int BT, int NB, int U, bool DW, bool SPMM = true, bool RM = false, bool VAL = SPMM>
 __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs A, int bp, int B)
 {
     extern __shared__ __align__(16) float gs_dyn[];
@@ -993,7 +995,7 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs 
         }
         __syncthreads();
     };
-    key_stream<BT, NB, U, DW, SPMM, RM>(A, &next_s, c1, gs_dyn, bp, B, stage);
+    key_stream<BT, NB, U, DW, SPMM, RM, VAL>(A, &next_s, c1, gs_dyn, bp, B, stage);
 }
 
 // ---- slice-tiled key-major kernel (batch tiles of 16 to 64 columns) --------
@@ -1358,7 +1360,7 @@ __device__ inline void tile_h(const float* __restrict__ H, int64_t key, int bp, 
     }
 }
 
-template <int BT, int NB, int U, int D, bool DW, bool SPMM>
+template <int BT, int NB, int U, int D, bool DW, bool SPMM, bool VAL = SPMM>
 __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, TileArgs T, int bp, int B)
 {
     constexpr int BTILE = BT * NB;
@@ -1429,7 +1431,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
 #pragma unroll
     for (int q = 0; q < D; ++q) {
         cur.next(d[q], TB::STEP);
-        blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, lk);
+        blk[q].template load<SPMM || VAL>(A.idx, A.vals, d[q].base, d[q].lim, lk);
         if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, lane_off, hb[q]);
     }
     float acc[NB];
@@ -1468,7 +1470,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
                 }
             }
             cur.next(d[q], TB::STEP);
-            blk[q].template load<SPMM>(A.idx, A.vals, d[q].base, d[q].lim, lk);
+            blk[q].template load<SPMM || VAL>(A.idx, A.vals, d[q].base, d[q].lim, lk);
             if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, lane_off, hb[q]);
         }
         if (!d[0].valid) break;
@@ -1748,11 +1750,14 @@ inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
 
 // rm: G and H are batch-major [B][n] (the caller's arrays); only the LDS
 // kernel takes them, transposing G while it stages it
-template <bool DW, bool SPMM = true>
+// VAL: load the entries' values in a dW-only pass (needed for `apply`)
+template <bool DW, bool SPMM = true, bool VAL = false>
 snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
                           float* out, float* dwo, int B, hipStream_t s, bool rm = false, float* apply = nullptr,
                           float lr = 0.0f)
 {
+    constexpr bool LV = SPMM || VAL;
+    if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
     RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     a.apply = apply;
     a.lr = lr;
@@ -1766,16 +1771,16 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
         const dim3 grid((unsigned)nwg), block(kLdsKeyWaves * kWave);
         if (rm) {
             switch (p.btile) {
-            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
-            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
-            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, true>), grid, block, lds, s, a, p.bp, B); break;
+            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
+            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
+            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
             default: return SNACK_ERR_INVALID_ARG;
             }
         } else {
             switch (p.btile) {
-            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
-            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
-            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM>), grid, block, lds, s, a, p.bp, B); break;
+            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
+            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
+            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
             default: return SNACK_ERR_INVALID_ARG;
             }
         }
@@ -1785,13 +1790,13 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     if (rm) return SNACK_ERR_INVALID_ARG;   // callers check spmm_batch_major first
     dim3 grid((unsigned)(a.per_xcd * kXcd), (unsigned)p.ntiles);
     switch (p.btile) {
-    case 1: hipLaunchKernelGGL((key_kernel<1, 1, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 2: hipLaunchKernelGGL((key_kernel<1, 2, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 4: hipLaunchKernelGGL((key_kernel<1, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 8: hipLaunchKernelGGL((key_kernel<2, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 16: hipLaunchKernelGGL((key_kernel<4, 4, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 32: hipLaunchKernelGGL((key_kernel<4, 8, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
-    case 64: hipLaunchKernelGGL((key_kernel<8, 8, 4, DW, SPMM>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 1: hipLaunchKernelGGL((key_kernel<1, 1, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 2: hipLaunchKernelGGL((key_kernel<1, 2, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 4: hipLaunchKernelGGL((key_kernel<1, 4, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 8: hipLaunchKernelGGL((key_kernel<2, 4, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 16: hipLaunchKernelGGL((key_kernel<4, 4, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 32: hipLaunchKernelGGL((key_kernel<4, 8, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
+    case 64: hipLaunchKernelGGL((key_kernel<8, 8, 4, DW, SPMM, LV>), grid, dim3(kBlock), 0, s, a, p.bp, B); break;
     default: return SNACK_ERR_INVALID_ARG;
     }
     SNACK_HIP(hipGetLastError());
@@ -1821,10 +1826,12 @@ inline bool recompute_dw(const snack_layer* L, const BatchPlan& p)
     return p.btile <= 16 || use_tile(L, L->tr, p) == use_tile(L, L->fwd, p);
 }
 
-template <bool DW, bool SPMM>
+template <bool DW, bool SPMM, bool VAL = false>
 snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
                          float* out, float* dwo, int B, hipStream_t s, float* apply = nullptr, float lr = 0.0f)
 {
+    constexpr bool LV = SPMM || VAL;
+    if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
     const SplitTab& st = v.split[tile_index(p.btile)];
     if (st.S >= 2 && !st.valid) {
         // every stale table of this view in one pass over its index
@@ -1870,10 +1877,10 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     constexpr int U64 = DW ? 4 : 8;
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a, t, p.bp, B); };
     switch (p.btile) {
-    case 8: go(tile_kernel<2, 4, 2, Dp, DW, SPMM>); break;
-    case 16: go(tile_kernel<4, 4, 4, Dp, DW, SPMM>); break;
-    case 32: go(tile_kernel<4, 8, 4, Dp, DW, SPMM>); break;
-    case 64: go(tile_kernel<16, 4, U64, Dp, DW, SPMM>); break;
+    case 8: go(tile_kernel<2, 4, 2, Dp, DW, SPMM, LV>); break;
+    case 16: go(tile_kernel<4, 4, 4, Dp, DW, SPMM, LV>); break;
+    case 32: go(tile_kernel<4, 8, 4, Dp, DW, SPMM, LV>); break;
+    case 64: go(tile_kernel<16, 4, U64, Dp, DW, SPMM, LV>); break;
     default: return SNACK_ERR_INVALID_ARG;
     }
     SNACK_HIP(hipGetLastError());
@@ -2011,10 +2018,14 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             // the canonical dW is recomputed below, so with the step the column order needs no dW of its own
             ProfScope prof(KC_SPMM_DX, s);
             SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, apply ? nullptr : dW_t, B, s, true, apply, lr));
-            if (apply) step->done = true;
         }
         ProfScope prof(KC_SDDMM_DW, s);
-        return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true);
+        if (!apply) return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true);
+        // the row pass steps the canonical values in place from the dW it computes
+        SNACK_CHECK((launch_keyed<true, false, true>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, true, L->vals, lr)));
+        step->done = true;
+        step->canon_done = true;
+        return SNACK_OK;
     }
     // role A: dX (and dW in column order) over the transposed view; role B: dW over the canonical view.
     // Event classes: the column pass counts as dX, a separate canonical-order dW step as dW.
@@ -2037,9 +2048,18 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         }
         ProfScope prof(KC_SDDMM_DW, s);
         if (recompute_dw(L, p)) {
-            // narrow batches: dW in canonical order by a second (cheap) pass over the row view
-            if (use_tile(L, L->fwd, p)) return launch_tile<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
-            return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
+            // narrow batches: dW in canonical order by a second (cheap) pass over the row view, which
+            // with the step also steps the canonical values in place
+            if (!apply) {
+                if (use_tile(L, L->fwd, p)) return launch_tile<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
+                return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
+            }
+            if (use_tile(L, L->fwd, p))
+                SNACK_CHECK((launch_tile<true, false, true>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, L->vals, lr)));
+            else SNACK_CHECK((launch_keyed<true, false, true>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s, false, L->vals,
+                                                               lr)));
+            step->canon_done = true;
+            return SNACK_OK;
         }
         // wide batches: dW once, in column order, then permuted into canonical order
         return permute_dw(L, dW_t, dW, s);
