@@ -1596,6 +1596,158 @@ __global__ void __launch_bounds__(kBlock) permute_dw_kernel(const int32_t* __res
     }
 }
 
+// dW in canonical order from the column order, one tile of the matrix per
+// workgroup: the entries whose rows lie in slice a of the column view's split
+// table and whose columns lie in slice b of the row view's.  Inside a tile each
+// column's entries are one run of the column order and each row's one run of
+// the canonical order, so the tile's column-order dW is copied into LDS run by
+// run and the canonical runs are written from there (an entry's LDS place is
+// its column's offset plus its rank in the column, from iperm): every global
+// access is a run about a cache line long instead of a scattered word.  A
+// half wavefront takes a run, kPermU runs at a time so their loads overlap
+// (the kernel waits on memory, not on issue).  A
+// tile larger than the buffer gathers directly.  With vals, each value also
+// takes its SGD step with its dW.
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kPermU = 10;   // runs per half wavefront in flight
+
+struct PermArgs {
+    const int32_t* ttab;   // column view: column c's run in row slice a is [ttab[a*ts + c], ttab[(a+1)*ts + c])
+    int64_t ts;
+    const int32_t* ftab;   // row view: row r's run in column slice b is [ftab[b*fs + r], ftab[(b+1)*fs + r])
+    int64_t fs;
+    int32_t SA, SB, M, K;
+    int32_t cap;             // entries the LDS buffer holds
+    int32_t ncmax, nrmax;    // most columns / rows of a tile
+    const int32_t* iperm;
+    const int32_t* cols;
+    const float* dwt;
+    float* dw;
+    float* vals;
+    float lr;
+};
+
+__global__ void __launch_bounds__(kPermThreads) permute_tiles_kernel(PermArgs P)
+{
+    extern __shared__ __align__(16) float pt_dyn[];
+    __shared__ int32_t wsum[kPermWaves];
+    float* ent = pt_dyn;
+    int32_t* cbeg = reinterpret_cast<int32_t*>(pt_dyn + P.cap);   // [ncmax] a column run's first slot
+    int32_t* coff = cbeg + P.ncmax;                                // [ncmax + 1] its place in ent
+    int32_t* rbeg = coff + P.ncmax + 1;                            // [nrmax] a row run's bounds
+    int32_t* rend = rbeg + P.nrmax;
+    const int a = (int)blockIdx.x / P.SB, b = (int)blockIdx.x % P.SB;
+    const int32_t r0 = split_start(a, P.SA, P.M), nr = split_start(a + 1, P.SA, P.M) - r0;
+    const int32_t c0 = split_start(b, P.SB, P.K), nc = split_start(b + 1, P.SB, P.K) - c0;
+    const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+
+    // column runs and their exclusive prefix (each thread a few consecutive columns)
+    const int per = (nc + kPermThreads - 1) / kPermThreads;
+    int32_t loc = 0;
+    for (int i = 0; i < per; ++i) {
+        const int ci = tid * per + i;
+        if (ci < nc) {
+            const int32_t s0 = P.ttab[(int64_t)a * P.ts + c0 + ci];
+            const int32_t s1 = P.ttab[(int64_t)(a + 1) * P.ts + c0 + ci];
+            cbeg[ci] = s0;
+            coff[ci] = s1 - s0;
+            loc += s1 - s0;
+        }
+    }
+    int32_t inc = loc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t t = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += t;
+    }
+    if (lane == kWave - 1) wsum[wv] = inc;
+    for (int ri = tid; ri < nr; ri += kPermThreads) {
+        rbeg[ri] = P.ftab[(int64_t)b * P.fs + r0 + ri];
+        rend[ri] = P.ftab[(int64_t)(b + 1) * P.fs + r0 + ri];
+    }
+    __syncthreads();
+    int32_t run = inc - loc;
+    for (int w = 0; w < wv; ++w) run += wsum[w];
+    for (int i = 0; i < per; ++i) {
+        const int ci = tid * per + i;
+        if (ci < nc) {
+            const int32_t len = coff[ci];
+            coff[ci] = run;
+            run += len;
+        }
+    }
+    if (tid == kPermThreads - 1) coff[nc] = run;
+    __syncthreads();
+    const int32_t E = coff[nc];
+    if (E > P.cap) {   // uniform: gather the tile's row runs directly
+        for (int ri = wv; ri < nr; ri += kPermWaves) {
+            const int32_t k1 = rend[ri];
+            for (int32_t k = rbeg[ri] + lane; k < k1; k += kWave) {
+                const float x = P.dwt[P.iperm[k]];
+                P.dw[k] = x;
+                if (P.vals) P.vals[k] = sgd_value(P.vals[k], x, P.lr);
+            }
+        }
+        return;
+    }
+    const int half = lane >> 5, hl = lane & 31;
+    // column runs into LDS
+    for (int c = wv * 2 * kPermU; c < nc; c += kPermWaves * 2 * kPermU) {
+        int32_t sb[kPermU], so[kPermU], sl[kPermU], mx = 0;
+#pragma unroll
+        for (int u = 0; u < kPermU; ++u) {
+            const int ci = c + 2 * u + half;
+            const bool ok = ci < nc;
+            sb[u] = ok ? cbeg[ci] : 0;
+            so[u] = ok ? coff[ci] : 0;
+            sl[u] = ok ? coff[ci + 1] - coff[ci] : 0;
+            mx = max(mx, sl[u]);
+        }
+        for (int t = hl; t < mx; t += 32) {
+            float v[kPermU];
+#pragma unroll
+            for (int u = 0; u < kPermU; ++u) v[u] = P.dwt[sb[u] + min(t, max(sl[u] - 1, 0))];
+#pragma unroll
+            for (int u = 0; u < kPermU; ++u)
+                if (t < sl[u]) ent[so[u] + t] = v[u];
+        }
+    }
+    __syncthreads();
+    // canonical row runs from LDS
+    for (int r = wv * 2 * kPermU; r < nr; r += kPermWaves * 2 * kPermU) {
+        int32_t kb[kPermU], kl[kPermU], mx = 0;
+#pragma unroll
+        for (int u = 0; u < kPermU; ++u) {
+            const int ri = r + 2 * u + half;
+            const bool ok = ri < nr;
+            kb[u] = ok ? rbeg[ri] : 0;
+            kl[u] = ok ? rend[ri] - rbeg[ri] : 0;
+            mx = max(mx, kl[u]);
+        }
+        for (int t = hl; t < mx; t += 32) {
+            int32_t j[kPermU], c[kPermU];
+            float v[kPermU];
+#pragma unroll
+            for (int u = 0; u < kPermU; ++u) {
+                const int32_t k = kb[u] + min(t, max(kl[u] - 1, 0));
+                j[u] = P.iperm[k];
+                c[u] = P.cols[k];
+                v[u] = P.vals ? P.vals[k] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kPermU; ++u) {
+                if (t < kl[u]) {
+                    const int ci = c[u] - c0;
+                    const float x = ent[coff[ci] + (j[u] - cbeg[ci])];
+                    P.dw[kb[u] + t] = x;
+                    if (P.vals) P.vals[kb[u] + t] = sgd_value(v[u], x, P.lr);
+                }
+            }
+        }
+    }
+}
+
 // dW[k] = sum_b dyt[r_k, b] * xt[c_k, b] over several batch tiles (batches
 // wider than one tile); group g of a wave step takes U consecutive slots and
 // its BT lanes are reduced by a butterfly.
@@ -1803,6 +1955,27 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     return SNACK_OK;
 }
 
+// the split table of width index w of view v, valid: when it is stale, every
+// stale table of the view is rebuilt in one pass over its index
+snack_status ensure_split(const View& v, int w, hipStream_t s)
+{
+    if (v.split[w].S < 2 || v.split[w].valid) return SNACK_OK;
+    TabSet ts;
+    ts.inv_nidx = 1.0 / (double)v.nidx;
+    for (int i = 0; i < kTileWidths; ++i) {
+        const SplitTab& si = v.split[i];
+        const bool build = si.S >= 2 && !si.valid;
+        ts.S[i] = si.S;
+        ts.tab[i] = build ? si.tab : nullptr;
+    }
+    hipLaunchKernelGGL(split_tables_kernel, dim3((unsigned)((v.nkeys + 3) / 4)), dim3(256), 0, s, v.ptr, v.idx,
+                       v.nkeys, v.nidx, ts);
+    SNACK_HIP(hipGetLastError());
+    for (int i = 0; i < kTileWidths; ++i)
+        if (ts.tab[i]) v.split[i].valid = true;
+    return SNACK_OK;
+}
+
 inline int tile_index(int btile)
 {
     return btile == 8 ? 0 : btile == 16 ? 1 : btile == 32 ? 2 : btile == 64 ? 3 : -1;
@@ -1833,22 +2006,7 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     constexpr bool LV = SPMM || VAL;
     if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
     const SplitTab& st = v.split[tile_index(p.btile)];
-    if (st.S >= 2 && !st.valid) {
-        // every stale table of this view in one pass over its index
-        TabSet ts;
-        ts.inv_nidx = 1.0 / (double)v.nidx;
-        for (int w = 0; w < kTileWidths; ++w) {
-            const SplitTab& sw = v.split[w];
-            const bool build = sw.S >= 2 && !sw.valid;
-            ts.S[w] = sw.S;
-            ts.tab[w] = build ? sw.tab : nullptr;
-        }
-        hipLaunchKernelGGL(split_tables_kernel, dim3((unsigned)((v.nkeys + 3) / 4)), dim3(256), 0, s, v.ptr, v.idx,
-                           v.nkeys, v.nidx, ts);
-        SNACK_HIP(hipGetLastError());
-        for (int w = 0; w < kTileWidths; ++w)
-            if (ts.tab[w]) v.split[w].valid = true;
-    }
+    SNACK_CHECK(ensure_split(v, tile_index(p.btile), s));
     RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     a.apply = apply;
     a.lr = lr;
@@ -1958,9 +2116,58 @@ BatchPlan plan_batch(int B)
     return p;
 }
 
-// dW[k] = dW_t[iperm[k]]
-static snack_status permute_dw(const snack_layer* L, const float* dW_t, float* dW, hipStream_t s)
+// The tiled permutation for width index w: the tiles of the width-w split
+// tables of both views, when there are enough of them and an average tile's
+// entries (with a margin) fit in LDS; false when it does not apply.
+static bool perm_tiles_plan(const snack_layer* L, int w, PermArgs* P, size_t* lds)
 {
+    if (L->nnz <= 0 || w < 0 || L->tr.split[w].S < 2 || L->fwd.split[w].S < 2) return false;
+    P->SA = L->tr.split[w].S;
+    P->SB = L->fwd.split[w].S;
+    P->M = L->M;
+    P->K = L->K;
+    P->nrmax = (L->M + P->SA - 1) / P->SA + 1;
+    P->ncmax = (L->K + P->SB - 1) / P->SB + 1;
+    const int64_t tiles = (int64_t)P->SA * P->SB;
+    const int64_t tables = (int64_t)(2 * P->nrmax + 2 * P->ncmax + 1) * 4;
+    const int64_t budget = (int64_t)L->lds_bytes - 1024 - tables;
+    const double avg = (double)L->nnz / (double)tiles;
+    const int64_t want = (int64_t)(avg * 1.25) + 1024;
+    if (tiles < 64 || budget / 4 < want) return false;
+    P->cap = (int32_t)want;
+    *lds = (size_t)want * 4 + (size_t)tables;
+    return true;
+}
+
+// dW[k] = dW_t[iperm[k]] (with vals: also vals[k] -= lr * dW[k]), by tiles
+// where perm_tiles_plan allows; *stepped tells whether vals took the step.
+static snack_status permute_dw(const snack_layer* L, int w, const float* dW_t, float* dW, float* vals, float lr,
+                               bool* stepped, hipStream_t s)
+{
+    *stepped = false;
+    {
+        PermArgs P;
+        size_t lds = 0;
+        if (perm_tiles_plan(L, w, &P, &lds)) {
+            const int64_t tiles = (int64_t)P.SA * P.SB;
+            SNACK_CHECK(ensure_split(L->tr, w, s));
+            SNACK_CHECK(ensure_split(L->fwd, w, s));
+            P.ttab = L->tr.split[w].tab;
+            P.ts = L->tr.nkeys;
+            P.ftab = L->fwd.split[w].tab;
+            P.fs = L->fwd.nkeys;
+            P.iperm = L->iperm;
+            P.cols = L->cols;
+            P.dwt = dW_t;
+            P.dw = dW;
+            P.vals = vals;
+            P.lr = lr;
+            hipLaunchKernelGGL(permute_tiles_kernel, dim3((unsigned)tiles), dim3(kPermThreads), lds, s, P);
+            SNACK_HIP(hipGetLastError());
+            *stepped = vals != nullptr;
+            return SNACK_OK;
+        }
+    }
     if (L->nnz > 0) {
         const int64_t per_xcd = (L->nnz + kXcd - 1) / kXcd;
         int64_t nw = (per_xcd + kBlock - 1) / kBlock;
@@ -2036,18 +2243,24 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
+        const bool recompute = recompute_dw(L, p);
+        // wider tiles: where the permutation into canonical order goes by tiles, it also steps the canonical
+        // values, so with the step the column pass steps vals_t there too
+        PermArgs pp;
+        size_t pl = 0;
+        const bool tiled = !recompute && perm_tiles_plan(L, tile_index(p.btile), &pp, &pl);
+        float* ap = (apply || (step && tiled)) ? L->vals_t : nullptr;
         {
             // with the step, dW in column order is still needed where the canonical dW is permuted from it
-            const bool recompute = recompute_dw(L, p);
-            float* dwo = (apply && recompute) ? nullptr : dW_t;
+            float* dwo = (ap && recompute) ? nullptr : dW_t;
             ProfScope prof(KC_SPMM_DX, s);
             if (use_tile(L, L->tr, p))
-                SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, apply, lr)));
-            else SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, false, apply, lr));
-            if (apply) step->done = true;
+                SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, ap, lr)));
+            else SNACK_CHECK(launch_keyed<true>(p, L, L->tr, dyt, xt, dX, dwo, B, s, false, ap, lr));
+            if (ap) step->done = true;
         }
         ProfScope prof(KC_SDDMM_DW, s);
-        if (recompute_dw(L, p)) {
+        if (recompute) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view, which
             // with the step also steps the canonical values in place
             if (!apply) {
@@ -2062,7 +2275,10 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             return SNACK_OK;
         }
         // wide batches: dW once, in column order, then permuted into canonical order
-        return permute_dw(L, dW_t, dW, s);
+        bool stepped = false;
+        SNACK_CHECK(permute_dw(L, tile_index(p.btile), dW_t, dW, (ap && tiled) ? L->vals : nullptr, lr, &stepped, s));
+        if (stepped) step->canon_done = true;
+        return SNACK_OK;
     }
     ProfScope prof(KC_SPMM_DX, s);
     if (dW)

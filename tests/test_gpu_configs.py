@@ -137,7 +137,7 @@ def test_c4_10000_square_batch_sweep_with_drop_regrow():
     M = K = 10000
     batches = (1, 2, 4, 8, 16, 32, 64)
     lr, period, iters, seed = 0.01, 10, 20, 4242
-    checks = {1, 10, 11, 20}
+    checks = {1, 7, 10, 11, 14, 20}   # batches 1, 64, 4, 8, 64 (after a drop/regrow), 32
     layer, _ = _layer(M, K, 95, "c4/layer", seed=seed)
     nnz = layer.nnz
     n_drop = nnz * 3 // 10
