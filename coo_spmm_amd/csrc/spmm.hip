@@ -1479,11 +1479,14 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
 
 // out[b, r] = sum over slices s = 0, 1, ... of part[s][r][b], in that order
 template <int BTILE>
+constexpr int kSplitReduceKeys = 1024 / BTILE;   // keys per workgroup of split_reduce_kernel
+
+template <int BTILE>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part, int S, int nkeys, int B,
                                                            float* __restrict__ out)
 {
     constexpr int Q = BTILE / 4;
-    constexpr int KPB = 64;
+    constexpr int KPB = kSplitReduceKeys<BTILE>;   // one float4 of the tile per thread
     __shared__ float t[KPB][BTILE + 1];
     const int r0 = (int)blockIdx.x * KPB;
     const int64_t sstride = (int64_t)nkeys * Q;
@@ -1494,7 +1497,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
         float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (r < nkeys) {
             const float4* __restrict__ pp = reinterpret_cast<const float4*>(part) + (int64_t)r * Q + c4;
-#pragma unroll 4
+#pragma unroll 8
             for (int s = 0; s < S; ++s) {
                 const float4 v = pp[s * sstride];
                 a.x += v.x;
@@ -2043,12 +2046,24 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     }
     SNACK_HIP(hipGetLastError());
     if (t.part) {
-        const dim3 rg((unsigned)((v.nkeys + 63) / 64));
+        auto rg = [&](int kpb) { return dim3((unsigned)((v.nkeys + kpb - 1) / kpb)); };
         switch (p.btile) {
-        case 8: hipLaunchKernelGGL((split_reduce_kernel<8>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
-        case 16: hipLaunchKernelGGL((split_reduce_kernel<16>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
-        case 32: hipLaunchKernelGGL((split_reduce_kernel<32>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
-        default: hipLaunchKernelGGL((split_reduce_kernel<64>), rg, dim3(256), 0, s, t.part, t.S, v.nkeys, B, out); break;
+        case 8:
+            hipLaunchKernelGGL((split_reduce_kernel<8>), rg(kSplitReduceKeys<8>), dim3(256), 0, s, t.part, t.S, v.nkeys,
+                               B, out);
+            break;
+        case 16:
+            hipLaunchKernelGGL((split_reduce_kernel<16>), rg(kSplitReduceKeys<16>), dim3(256), 0, s, t.part, t.S,
+                               v.nkeys, B, out);
+            break;
+        case 32:
+            hipLaunchKernelGGL((split_reduce_kernel<32>), rg(kSplitReduceKeys<32>), dim3(256), 0, s, t.part, t.S,
+                               v.nkeys, B, out);
+            break;
+        default:
+            hipLaunchKernelGGL((split_reduce_kernel<64>), rg(kSplitReduceKeys<64>), dim3(256), 0, s, t.part, t.S,
+                               v.nkeys, B, out);
+            break;
         }
         SNACK_HIP(hipGetLastError());
     }
