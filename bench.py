@@ -50,11 +50,11 @@ def kernel_bytes(kind, nnz, M, K, B):
         # the triple (12 B / entry), X once, Y once
         return 12 * nnz + 4 * B * (K + M)
     if kind == "spmm_dx":
-        # column pass of the fused backward + SGD: index + value read per entry and one float written per
-        # entry -- the value after its SGD step (batch tiles up to 32, the canonical dW is recomputed over
-        # the row view) or dW in column order (tile 64: the canonical dW is permuted from it and the step
-        # is a separate pass); dY, X once; dX once
-        return 12 * nnz + 4 * B * (M + 2 * K)
+        # column pass of the fused backward + SGD: index + value read per entry; written per entry, the
+        # value after its SGD step, and at the 64-column tile also dW in column order (the canonical dW is
+        # permuted from it there; narrower tiles recompute it over the row view); dY, X once; dX once
+        per_entry = 12 + (4 if B > 32 else 0)
+        return per_entry * nnz + 4 * B * (M + 2 * K)
     raise KeyError(kind)
 
 
