@@ -6,7 +6,8 @@ Workload: one 10000 x 10000 layer at 95 % unstructured sparsity (nnz =
 the batch sweep B in {1, 2, 4, 8, 16, 32, 64}.  One *step* is one training
 iteration at every batch size of the sweep, each iteration being forward
 Y = X W^T, MSE gradient, backward (dX and dW on the support) and an SGD update
-(lr 0.01) of the values; after every 10th iteration the layer drops the 30 %
+(lr 0.01) of the values, issued as one snack_train_step_mse call per
+iteration; after every 10th iteration the layer drops the 30 %
 smallest-|w| entries and regrows as many at random empty positions (SET-style,
 nnz fixed).  Inputs are synthetic (seeded N(0,1) activations and targets) and
 resident in device memory before the timed region starts.
@@ -141,11 +142,10 @@ def main():
 
     def iteration(B):
         b = bufs[B]
-        L.snack_forward(layer.h, b["X"], b["Y"], stream)
-        L.snack_mse_grad(b["Y"], b["T"], b["dY"], 2.0 / (B * M), stream)
-        # backward (dX, dW) and the SGD step in one call: the column pass steps the
-        # column-ordered value copy in place (same results as backward + sgd_step)
-        L.snack_backward_sgd(layer.h, b["X"], b["dY"], b["dX"], b["dW"], lr, stream)
+        # forward, MSE gradient, backward (dX, dW) and the SGD step in one call (the same
+        # results, bit for bit, as snack_forward + snack_mse_grad + snack_backward_sgd)
+        L.snack_train_step_mse(layer.h, b["X"], b["T"], b["Y"], b["dY"], b["dX"], b["dW"], 2.0 / (B * M), lr,
+                               stream)
         it_counter[0] += 1
         if args.prune_every > 0 and it_counter[0] % args.prune_every == 0:
             L.snack_profile_set_tag(-1)

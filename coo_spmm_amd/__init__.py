@@ -40,6 +40,7 @@ _SIGS = {
     "snack_forward": ([P, P, P, i32, P], ST),
     "snack_backward": ([P, P, P, P, P, i32, P], ST),
     "snack_backward_sgd": ([P, P, P, P, P, f32, i32, P], ST),
+    "snack_train_step_mse": ([P, P, P, P, P, P, P, f32, f32, i32, P], ST),
     "snack_prune_regrow": ([P, i64, P], ST),
     "snack_layer_shape": ([P, ctypes.POINTER(i32), ctypes.POINTER(i32)], ST),
     "snack_layer_nnz": ([P, ctypes.POINTER(i64)], ST),
@@ -152,6 +153,12 @@ def snack_backward_sgd(h, X, dY, dX, dW, lr, stream=None):
     B = dY.shape[0]
     _check(_lib.snack_backward_sgd(h, _ptr(X), _ptr(dY), _ptr(dX), _ptr(dW), float(lr), B, _stream(stream)),
            "snack_backward_sgd")
+
+
+def snack_train_step_mse(h, X, T, Y, dY, dX, dW, scale, lr, stream=None):
+    B = X.shape[0]
+    _check(_lib.snack_train_step_mse(h, _ptr(X), _ptr(T), _ptr(Y), _ptr(dY), _ptr(dX), _ptr(dW), float(scale),
+                                     float(lr), B, _stream(stream)), "snack_train_step_mse")
 
 
 def snack_prune_regrow(h, n_drop, stream=None):
@@ -320,6 +327,23 @@ class SnackLayer:
             dW = torch.empty((self.nnz,), dtype=torch.float32, device=dY.device)
         snack_backward_sgd(self.h, X, dY, dX if want_dx else None, dW, lr, stream)
         return (dX if want_dx else None), dW
+
+    def train_step_mse(self, X, T, lr, want_dx=True, scale=None, out=None, stream=None):
+        """Forward, MSE gradient (scale defaults to the mean's 2 / (B * M)), backward and SGD step in one
+        call; returns (Y, dY, dX, dW).  `out` may supply that tuple of preallocated tensors."""
+        import torch
+        B = X.shape[0]
+        if scale is None:
+            scale = 2.0 / (B * self.M)
+        if out is None:
+            dev = X.device
+            out = (torch.empty((B, self.M), dtype=torch.float32, device=dev),
+                   torch.empty((B, self.M), dtype=torch.float32, device=dev),
+                   torch.empty((B, self.K), dtype=torch.float32, device=dev) if want_dx else None,
+                   torch.empty((self.nnz,), dtype=torch.float32, device=dev))
+        Y, dY, dX, dW = out
+        snack_train_step_mse(self.h, X, T, Y, dY, dX if want_dx else None, dW, scale, lr, stream)
+        return Y, dY, (dX if want_dx else None), dW
 
     def prune_regrow(self, n_drop, stream=None):
         snack_prune_regrow(self.h, n_drop, stream)

@@ -215,10 +215,23 @@ snack_status transpose_pad(const float* src, float* dst, int n, const float* src
 // feature-major copy is needed (batch tiles up to 4, operands staged in LDS).
 bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool dx, bool dw);
 
+// The MSE gradient of a forward's output written by the forward itself:
+// dY = scale * (Y - T) (batch-major [B][M]) and, where dYt is set and the
+// forward's last pass can, its feature-major copy [M][bp] (zero past B).
+// done / dyt_done tell what the forward wrote.
+struct MseFuse {
+    const float* T;
+    float* dY;
+    float* dYt;
+    float scale;
+    bool done;
+    bool dyt_done;
+};
+
 // Y[b, key] = sum over the canonical view's entries of v * Xt[idx, b]; with rm
 // the operand is the batch-major X itself
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s, bool rm = false);
+                          hipStream_t s, bool rm = false, MseFuse* mse = nullptr);
 
 // one launch: dX over the transposed view (plus dW in transposed order when
 // dW_t is non-null) and dW over the canonical view; either output may be null.

@@ -269,9 +269,11 @@ extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, 
 namespace {
 
 // the backward of snack_backward; with `step`, the column pass may also take the
-// SGD step of vals_t in place (step->done tells whether it did)
+// SGD step of vals_t in place (step->done tells whether it did).  x_ready /
+// dy_ready: the workspace already holds the feature-major copy of X / dY for
+// this batch plan (written by the forward of the same training step).
 snack_status backward_impl(snack_layer* L, const float* X, const float* dY, float* dX, float* dW, int32_t B,
-                           hipStream_t s, SgdStep* step)
+                           hipStream_t s, SgdStep* step, bool x_ready = false, bool dy_ready = false)
 {
     const BatchPlan p = plan_batch(B);
     const bool rm = spmm_batch_major(L, p, false, dX != nullptr, dW != nullptr);
@@ -279,7 +281,9 @@ snack_status backward_impl(snack_layer* L, const float* X, const float* dY, floa
     const float* xt = X;
     if (p.bp > 1 && !rm) {
         SNACK_CHECK(ensure_ws(L, p));
-        SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), L->M, dW ? X : nullptr, ws_x(L), L->K, B, p.bp, s));
+        const float* xs = (dW && !x_ready) ? X : nullptr;
+        if (!dy_ready) SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), L->M, xs, ws_x(L), L->K, B, p.bp, s));
+        else if (xs) SNACK_CHECK(transpose_pad(xs, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
         dyt = ws_dy(L, p);
         xt = ws_x(L);
     }
@@ -312,14 +316,14 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
     return backward_impl(L, X, dY, dX, dW, B, as_stream(stream), nullptr);
 }
 
-extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
-                                           float lr, int32_t B, snack_stream stream)
+namespace {
+
+// snack_backward_sgd after its argument checks
+snack_status backward_sgd_impl(snack_layer* L, const float* X, const float* dY, float* dX, float* dW, float lr,
+                               int32_t B, hipStream_t s, bool x_ready, bool dy_ready)
 {
-    if (!L || !X || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
-    if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
-    hipStream_t s = as_stream(stream);
     SgdStep step{lr, false, false};
-    SNACK_CHECK(backward_impl(L, X, dY, dX, dW, B, s, &step));
+    SNACK_CHECK(backward_impl(L, X, dY, dX, dW, B, s, &step, x_ready, dy_ready));
     if (!step.done) {
         // the column pass did not take the step: as snack_sgd_step would
         const float* dwt = (L->dwt_valid && dW == L->dwt_for) ? L->dwt : nullptr;
@@ -329,6 +333,45 @@ extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const
     L->dwt_valid = false;
     if (step.canon_done) return SNACK_OK;   // the row pass stepped the canonical values too
     return sgd_update_values(L, dW, lr, s);
+}
+
+}  // namespace
+
+extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
+                                           float lr, int32_t B, snack_stream stream)
+{
+    if (!L || !X || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
+    return backward_sgd_impl(L, X, dY, dX, dW, lr, B, as_stream(stream), false, false);
+}
+
+extern "C" snack_status snack_train_step_mse(snack_layer* L, const float* X, const float* T, float* Y, float* dY,
+                                             float* dX, float* dW, float scale, float lr, int32_t B,
+                                             snack_stream stream)
+{
+    if (!L || !X || !T || !Y || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const BatchPlan p = plan_batch(B);
+    MseFuse m{T, dY, nullptr, scale, false, false};
+    bool x_ready = false;
+    if (spmm_batch_major(L, p, true, false, false)) {
+        SNACK_CHECK(spmm_forward(L, X, p, B, Y, s, true, &m));
+    } else {
+        const float* feat = X;
+        if (p.bp > 1) {
+            // one feature-major copy of X for the forward and the backward; the forward's last pass can
+            // write dY's feature-major copy too, where the backward takes one
+            SNACK_CHECK(ensure_ws(L, p));
+            SNACK_CHECK(transpose_pad(X, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
+            feat = ws_x(L);
+            x_ready = true;
+            if (!spmm_batch_major(L, p, false, dX != nullptr, true)) m.dYt = ws_dy(L, p);
+        }
+        SNACK_CHECK(spmm_forward(L, feat, p, B, Y, s, false, &m));
+    }
+    if (!m.done) SNACK_CHECK(mse_grad(Y, T, dY, (int64_t)B * L->M, scale, s));
+    return backward_sgd_impl(L, X, dY, dX, dW, lr, B, s, x_ready, m.dyt_done);
 }
 
 extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack_stream stream)

@@ -54,7 +54,13 @@ struct RoleArgs {
     float* out;          // [B, nkeys] or null
     float* dwo;          // dW in this view's slot order, or null
     float* apply;        // values in this view's slot order to take an SGD step with dW, or null
-    float lr;            // (SPMM passes only: the step uses the entry values they load)
+    float lr;            // (the step uses the entry values the pass loads)
+    // with dyo: the MSE gradient of the output written beside it, dyo = mse_scale * (out - tgt)
+    // (batch-major like out), and where dyto is set also feature-major [nkeys][bp] (zero past B)
+    const float* tgt;
+    float* dyo;
+    float* dyto;
+    float mse_scale;
     int64_t cap;         // padded length of idx / vals
     int32_t nchunks;
     int32_t nkeys;
@@ -658,9 +664,11 @@ __device__ inline void key_dw(const float (&y)[U][NB], const float (&h)[NB], int
     }
 }
 
-// group sums of a key added across groups, written once by group 0
+// group sums of a key added across groups, written once by group 0 (with
+// A.dyo, the MSE gradient of each written value beside it)
 template <int BT, int NB>
-__device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int nkeys, int32_t r, float* __restrict__ out)
+__device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int nkeys, int32_t r, float* __restrict__ out,
+                                 const RoleArgs& A)
 {
 #pragma unroll
     for (int m = BT; m < kWave; m <<= 1)
@@ -670,7 +678,11 @@ __device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int n
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
             const int b = bcol + n;
-            if (b < B) out[(int64_t)b * nkeys + r] = acc[n];
+            if (b < B) {
+                const int64_t o = (int64_t)b * nkeys + r;
+                out[o] = acc[n];
+                if (A.dyo) A.dyo[o] = A.mse_scale * (acc[n] - A.tgt[o]);
+            }
         }
     }
 }
@@ -709,7 +721,7 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
             if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
             if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
         }
-        if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out);
+        if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out, A);
     }
 }
 
@@ -889,7 +901,7 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
             continue;
         }
         if constexpr (SPMM) {
-            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out);
+            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out, A);
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
         }
@@ -1481,9 +1493,18 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
 template <int BTILE>
 constexpr int kSplitReduceKeys = 1024 / BTILE;   // keys per workgroup of split_reduce_kernel
 
+// With dyo: dyo = scale * (out - tgt) beside out, and with dyt also the
+// feature-major copy dyt[r * BTILE + b] (zero for b >= B).
+struct MseOut {
+    const float* tgt;
+    float* dyo;
+    float* dyt;
+    float scale;
+};
+
 template <int BTILE>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part, int S, int nkeys, int B,
-                                                           float* __restrict__ out)
+                                                           float* __restrict__ out, MseOut mse)
 {
     constexpr int Q = BTILE / 4;
     constexpr int KPB = kSplitReduceKeys<BTILE>;   // one float4 of the tile per thread
@@ -1516,7 +1537,27 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
         const int b = e / KPB;
         const int kk = e - b * KPB;
         const int r = r0 + kk;
-        if (b < B && r < nkeys) out[(int64_t)b * nkeys + r] = t[kk][b];
+        if (b < B && r < nkeys) {
+            const int64_t o = (int64_t)b * nkeys + r;
+            out[o] = t[kk][b];
+            if (mse.dyo) {
+                const float d = mse.scale * (t[kk][b] - mse.tgt[o]);
+                mse.dyo[o] = d;
+                t[kk][b] = d;   // only this thread reads (kk, b)
+            }
+        }
+    }
+    if (mse.dyo && mse.dyt) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < KPB * Q; e += 256) {
+            const int kk = e / Q;
+            const int b = (e - kk * Q) * 4;
+            const int r = r0 + kk;
+            if (r < nkeys)
+                *reinterpret_cast<float4*>(mse.dyt + (int64_t)r * BTILE + b) =
+                    make_float4(b < B ? t[kk][b] : 0.0f, b + 1 < B ? t[kk][b + 1] : 0.0f,
+                                b + 2 < B ? t[kk][b + 2] : 0.0f, b + 3 < B ? t[kk][b + 3] : 0.0f);
+        }
     }
 }
 
@@ -1822,6 +1863,10 @@ RoleArgs role_for(const View& v, const float* G, const float* H, float* out, flo
     a.dwo = dwo;
     a.apply = nullptr;
     a.lr = 0.0f;
+    a.tgt = nullptr;
+    a.dyo = nullptr;
+    a.dyto = nullptr;
+    a.mse_scale = 0.0f;
     a.nchunks = v.nchunks;
     a.nkeys = v.nkeys;
     a.nidx = v.nidx;
@@ -1906,16 +1951,24 @@ inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
 // rm: G and H are batch-major [B][n] (the caller's arrays); only the LDS
 // kernel takes them, transposing G while it stages it
 // VAL: load the entries' values in a dW-only pass (needed for `apply`)
+// mse: the MSE gradient written beside the output by the key stores (batch-major only)
 template <bool DW, bool SPMM = true, bool VAL = false>
 snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
                           float* out, float* dwo, int B, hipStream_t s, bool rm = false, float* apply = nullptr,
-                          float lr = 0.0f)
+                          float lr = 0.0f, MseFuse* mse = nullptr)
 {
     constexpr bool LV = SPMM || VAL;
     if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
+    if (mse && !SPMM) return SNACK_ERR_INVALID_ARG;
     RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     a.apply = apply;
     a.lr = lr;
+    if (mse) {
+        a.tgt = mse->T;
+        a.dyo = mse->dY;
+        a.mse_scale = mse->scale;
+        mse->done = true;
+    }
     const size_t lds = (size_t)v.nidx * p.bp * sizeof(float);
     if (p.btile <= 4 && p.ntiles == 1 && lds <= (size_t)L->lds_bytes && L->cus > 0 && v.nchunks > 0) {
         // operand resident in LDS: one or two persistent workgroups per CU
@@ -2002,9 +2055,12 @@ inline bool recompute_dw(const snack_layer* L, const BatchPlan& p)
     return p.btile <= 16 || use_tile(L, L->tr, p) == use_tile(L, L->fwd, p);
 }
 
+// mse: the MSE gradient (and its feature-major copy) written by the slice
+// reduction where there is one
 template <bool DW, bool SPMM, bool VAL = false>
 snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
-                         float* out, float* dwo, int B, hipStream_t s, float* apply = nullptr, float lr = 0.0f)
+                         float* out, float* dwo, int B, hipStream_t s, float* apply = nullptr, float lr = 0.0f,
+                         MseFuse* mse = nullptr)
 {
     constexpr bool LV = SPMM || VAL;
     if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
@@ -2046,23 +2102,29 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     }
     SNACK_HIP(hipGetLastError());
     if (t.part) {
+        MseOut mo{nullptr, nullptr, nullptr, 0.0f};
+        if (mse) {
+            mo = MseOut{mse->T, mse->dY, mse->dYt, mse->scale};
+            mse->done = true;
+            mse->dyt_done = mse->dYt != nullptr;
+        }
         auto rg = [&](int kpb) { return dim3((unsigned)((v.nkeys + kpb - 1) / kpb)); };
         switch (p.btile) {
         case 8:
             hipLaunchKernelGGL((split_reduce_kernel<8>), rg(kSplitReduceKeys<8>), dim3(256), 0, s, t.part, t.S, v.nkeys,
-                               B, out);
+                               B, out, mo);
             break;
         case 16:
             hipLaunchKernelGGL((split_reduce_kernel<16>), rg(kSplitReduceKeys<16>), dim3(256), 0, s, t.part, t.S,
-                               v.nkeys, B, out);
+                               v.nkeys, B, out, mo);
             break;
         case 32:
             hipLaunchKernelGGL((split_reduce_kernel<32>), rg(kSplitReduceKeys<32>), dim3(256), 0, s, t.part, t.S,
-                               v.nkeys, B, out);
+                               v.nkeys, B, out, mo);
             break;
         default:
             hipLaunchKernelGGL((split_reduce_kernel<64>), rg(kSplitReduceKeys<64>), dim3(256), 0, s, t.part, t.S,
-                               v.nkeys, B, out);
+                               v.nkeys, B, out, mo);
             break;
         }
         SNACK_HIP(hipGetLastError());
@@ -2205,13 +2267,14 @@ bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool d
 }
 
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s, bool rm)
+                          hipStream_t s, bool rm, MseFuse* mse)
 {
     ProfScope prof(KC_SPMM_FWD, s);
-    if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true);
-    if (use_tile(L, L->fwd, p)) return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
+    if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true, nullptr, 0.0f, mse);
+    if (use_tile(L, L->fwd, p))
+        return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse);
     if (use_keyed(L->fwd, L->nnz, p))
-        return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s);
+        return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, false, nullptr, 0.0f, mse);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
                                B, s);
 }

@@ -122,6 +122,23 @@ snack_status snack_backward_sgd(snack_layer* layer, const float* X, const float*
                                 float lr, int32_t B, snack_stream stream);
 
 /*
+ * One iteration of the "Padded-CSR" post's section 7.3 training loop with the
+ * mean-squared-error loss of its section 8 benchmarks, in one call: forward,
+ * loss gradient, backward and SGD step.  The same results, bit for bit, as
+ *   snack_forward(layer, X, Y, B);
+ *   snack_mse_grad(Y, T, dY, B * M, scale);
+ *   snack_backward_sgd(layer, X, dY, dX, dW, lr, B);
+ * (scale = 2 / (B * M) for the mean).  X device float[B, K]; T device
+ * float[B, M] (the targets); Y, dY device float[B, M], overwritten; dX device
+ * float[B, K] or NULL; dW device float[nnz], 16-byte aligned, overwritten.  The
+ * forward's last pass writes dY beside Y (and the feature-major copy the
+ * backward reads), and X is copied to feature-major order once for both
+ * passes, so the call launches fewer passes than the three separate ones.
+ */
+snack_status snack_train_step_mse(snack_layer* layer, const float* X, const float* T, float* Y, float* dY,
+                                  float* dX, float* dW, float scale, float lr, int32_t B, snack_stream stream);
+
+/*
  * In-place drop / regrow with nnz fixed ("Padded-CSR" section 4.3: drop some
  * live entries, grow the same number elsewhere; SNACK paper Figure 1: in place
  * on the triple).  Drops the n_drop entries of smallest |value| -- order key

@@ -135,3 +135,48 @@ def test_backward_sgd_matches_backward_then_sgd(M, K, nnz):
     finally:
         a.close()
         b.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(10000, 10000, 5_000_000), (2000, 1500, 300000), (768, 3072, 23593)])
+def test_train_step_matches_separate_calls(M, K, nnz):
+    """The one-call training step (forward, MSE gradient, backward, SGD) equals
+    snack_forward + snack_mse_grad + snack_backward_sgd bit for bit (Y, dY, dX,
+    dW and both value copies) for every batch plan, twice per plan.  The layers
+    reach the forward that writes dY beside Y (slice reduction or key stores)
+    and the paths where the gradient is a separate pass."""
+    import torch
+    L = lib()
+    rows, cols, vals = random_layer(M, K, nnz, f"tstep/{M}x{K}")
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    lr = 0.01
+    u32 = lambda t: host(t).view(np.uint32)
+    try:
+        for B in (1, 2, 3, 4, 8, 16, 32, 64, 100):
+            X = dev(normal((B, K), f"tstep/{M}x{K}/X/{B}"))
+            T = dev(normal((B, M), f"tstep/{M}x{K}/T/{B}"))
+            scale = 2.0 / (B * M)
+            for it in range(2):
+                say("train step", M, K, "B", B, "it", it)
+                Ya = torch.empty(B, M, device="cuda"); dYa = torch.empty(B, M, device="cuda")
+                L.snack_forward(a.h, X, Ya)
+                L.snack_mse_grad(Ya, T, dYa, scale)
+                dXa, dWa = a.backward_sgd(X, dYa, lr)
+                Yb, dYb, dXb, dWb = b.train_step_mse(X, T, lr, scale=scale)
+                for name, x, y in (("Y", Ya, Yb), ("dY", dYa, dYb), ("dX", dXa, dXb), ("dW", dWa, dWb)):
+                    assert np.array_equal(u32(x), u32(y)), f"{name} B={B} it={it}"
+                assert np.array_equal(u32(a.export()[2]), u32(b.export()[2])), f"values B={B}"
+                _, pm, _, _, vtb = (host(t) for t in b.export_index(with_values=True))
+                assert np.array_equal(vtb.view(np.uint32), host(b.export()[2])[pm].view(np.uint32)), f"copies B={B}"
+        # without dX
+        X = dev(normal((8, K), f"tstep/{M}x{K}/X/nodx")); T = dev(normal((8, M), f"tstep/{M}x{K}/T/nodx"))
+        Ya = torch.empty(8, M, device="cuda"); dYa = torch.empty(8, M, device="cuda")
+        L.snack_forward(a.h, X, Ya)
+        L.snack_mse_grad(Ya, T, dYa, 2.0 / (8 * M))
+        _, dWa = a.backward_sgd(X, dYa, lr, want_dx=False)
+        _, _, _, dWb = b.train_step_mse(X, T, lr, want_dx=False)
+        assert np.array_equal(u32(dWa), u32(dWb))
+        assert np.array_equal(u32(a.export()[2]), u32(b.export()[2]))
+    finally:
+        a.close()
+        b.close()
