@@ -664,11 +664,22 @@ __device__ inline void key_dw(const float (&y)[U][NB], const float (&h)[NB], int
     }
 }
 
+// the MSE targets of key r's NB columns from bcol (clamped, unconditional
+// loads: A.tgt is always a valid [B][nkeys] array, the output itself when no
+// gradient is written), issued when the key starts so its end does not wait
+template <int NB>
+__device__ inline void key_targets(const RoleArgs& A, int bcol, int B, int32_t r, float (&tg)[NB])
+{
+#pragma unroll
+    for (int n = 0; n < NB; ++n) tg[n] = A.tgt[(int64_t)(bcol + n < B ? bcol + n : B - 1) * A.nkeys + r];
+}
+
 // group sums of a key added across groups, written once by group 0 (with
-// A.dyo, the MSE gradient of each written value beside it)
+// A.dyo, the MSE gradient of each written value beside it, from the key's
+// targets tg)
 template <int BT, int NB>
 __device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int nkeys, int32_t r, float* __restrict__ out,
-                                 const RoleArgs& A)
+                                 const RoleArgs& A, const float (&tg)[NB])
 {
 #pragma unroll
     for (int m = BT; m < kWave; m <<= 1)
@@ -681,7 +692,7 @@ __device__ inline void key_store(float (&acc)[NB], int g, int bcol, int B, int n
             if (b < B) {
                 const int64_t o = (int64_t)b * nkeys + r;
                 out[o] = acc[n];
-                if (A.dyo) A.dyo[o] = A.mse_scale * (acc[n] - A.tgt[o]);
+                if (A.dyo) A.dyo[o] = A.mse_scale * (acc[n] - tg[n]);
             }
         }
     }
@@ -709,6 +720,8 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
         for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
         float h[NB];
         if constexpr (DW) load_nb<NB>(A.H + (int64_t)r * bp + bcol, h);
+        float tg[NB];
+        if constexpr (SPMM) key_targets<NB>(A, bcol, B, r, tg);
         KB blk;
         if (p0 < p1) blk.template load<SPMM || VAL>(A.idx, A.vals, p0, p1, lane, g);
         for (int32_t base = p0; base < p1; base += KB::STEP) {
@@ -721,7 +734,7 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
             if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
             if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
         }
-        if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out, A);
+        if constexpr (SPMM) key_store<BT, NB>(acc, g, bcol, B, A.nkeys, r, A.out, A, tg);
     }
 }
 
@@ -871,9 +884,10 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
     for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
     // the block in flight and the dW operand of its key
     KB blk;
-    float h[NB], hn[NB];
+    float h[NB], hn[NB], tg[NB];
     blk.template load<SPMM || VAL>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
     if constexpr (DW) load_h<NB, RM>(A.H, kc.r, bp, bcol, B, A.nkeys, hn);
+    if constexpr (SPMM) key_targets<NB>(A, bcol, B, kc.r, tg);
     stage();
     if (!any) return;
     int32_t base = kc.p0;
@@ -901,11 +915,12 @@ __device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int c
             continue;
         }
         if constexpr (SPMM) {
-            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out, A);
+            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out, A, tg);
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
         }
         if (!kc.advance()) break;
+        if constexpr (SPMM) key_targets<NB>(A, bcol, B, kc.r, tg);
         base = kc.p0;
     }
 }
@@ -1963,6 +1978,7 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     RoleArgs a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
     a.apply = apply;
     a.lr = lr;
+    a.tgt = out;   // the key stores read targets unconditionally: any valid [B][nkeys] array
     if (mse) {
         a.tgt = mse->T;
         a.dyo = mse->dY;
