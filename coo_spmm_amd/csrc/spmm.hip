@@ -1052,9 +1052,14 @@ struct TileArgs {
     int32_t S, KB, R;     // slices, key blocks, keys per block
 };
 
-// one block of a key's segment: entries [base, lim) of key r (all uniform)
+// one block of a key's segment: entries [base, lim) of key r (all uniform);
+// an exhausted cursor yields lim = -1 < base = 0 (no entries, no key end).
+// The flags are compares of base and lim, so they stay in scalar registers.
 struct TileDesc {
-    int32_t base, lim, r, last, valid;
+    int32_t base, lim, r;
+    __device__ inline bool valid() const { return lim >= base; }
+    template <int STEP>
+    __device__ inline bool last() const { return lim >= base && base + STEP >= lim; }
 };
 
 // a wavefront's keys r0, r0 + kTileWaves, ... (nk <= 64 of them); lane j
@@ -1066,19 +1071,15 @@ struct TileCursor {
     __device__ inline void next(TileDesc& d, int32_t step)
     {
         if (j >= nk) {
-            d.valid = 0;
             d.base = 0;
-            d.lim = 0;
+            d.lim = -1;
             d.r = r0;
-            d.last = 0;
             return;
         }
-        d.valid = 1;
         d.base = base;
         d.lim = p1;
         d.r = r0 + kTileWaves * j;
-        d.last = base + step >= p1 ? 1 : 0;
-        if (d.last) {
+        if (base + step >= p1) {
             ++j;
             if (j < nk) {
                 base = uni(__builtin_amdgcn_readlane(tlo, j));
@@ -1109,11 +1110,13 @@ template <int M>
 __device__ inline float lane_xor(float x)
 {
     static_assert(M == 1 || M == 2 || M == 4 || M == 8, "within a row");
-    if constexpr (M == 1) return dpp_f<0xB1>(0.0f, x);            // quad_perm [1,0,3,2]
-    else if constexpr (M == 2) return dpp_f<0x4E>(0.0f, x);       // quad_perm [2,3,0,1]
+    // every source lane exists for these patterns, so no old value is needed
+    // (plain moves, which the compiler folds into the following add)
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
     else if constexpr (M == 4)   // half-row mirror, then quad reverse (every source lane exists: no old value)
         return dpp_f<0x1B>(0.0f, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true)));
-    else return dpp_f<0x128>(0.0f, x);                            // row rotate by 8
+    else return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));   // row ror 8
 }
 // value of lane U0 of this lane's group of BT lanes (groups are rows, half
 // rows or quads)
@@ -1484,7 +1487,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
             if constexpr (DW)
                 tile_dw<BT, NB, U>(y, hb[q], d[q].base, d[q].lim, lk, bl, A.dwo, blk[q].mval, A.apply, A.lr);
             if constexpr (SPMM) {
-                if (d[q].last) {
+                if (d[q].template last<TB::STEP>()) {
                     // each lane ends with one column of the key's sum; one lane per column stores
                     const float tot = group_reduce<BT, NB>(acc, lane);
                     const int b = group_reduce_col<BT, NB>(lane);
@@ -1500,7 +1503,7 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
             blk[q].template load<SPMM || VAL>(A.idx, A.vals, d[q].base, d[q].lim, lk);
             if constexpr (DW) tile_h<BT, NB>(A.H, d[q].r, bp, lane_off, hb[q]);
         }
-        if (!d[0].valid) break;
+        if (!d[0].valid()) break;
     }
 }
 
@@ -1523,9 +1526,24 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
 {
     constexpr int Q = BTILE / 4;
     constexpr int KPB = kSplitReduceKeys<BTILE>;   // one float4 of the tile per thread
+    constexpr int NOUT = KPB * BTILE / 256;        // output elements per thread
     __shared__ float t[KPB][BTILE + 1];
     const int r0 = (int)blockIdx.x * KPB;
     const int64_t sstride = (int64_t)nkeys * Q;
+    // the targets of this thread's outputs, loaded first so they arrive with the
+    // partial sums (clamped, unconditional loads: without a gradient they come
+    // from part, which is longer than any [B][nkeys] array)
+    float tg[NOUT];
+    {
+        const float* __restrict__ src = mse.dyo ? mse.tgt : part;
+#pragma unroll
+        for (int i = 0; i < NOUT; ++i) {
+            const int e = (int)threadIdx.x + 256 * i;
+            const int b = e / KPB;
+            const int r = r0 + (e - b * KPB);
+            tg[i] = src[(int64_t)(b < B ? b : B - 1) * nkeys + (r < nkeys ? r : nkeys - 1)];
+        }
+    }
     for (int e = threadIdx.x; e < KPB * Q; e += 256) {
         const int kk = e / Q;
         const int c4 = e - kk * Q;
@@ -1548,7 +1566,9 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
         t[kk][c4 * 4 + 3] = a.w;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < KPB * BTILE; e += 256) {
+#pragma unroll
+    for (int i = 0; i < NOUT; ++i) {
+        const int e = (int)threadIdx.x + 256 * i;
         const int b = e / KPB;
         const int kk = e - b * KPB;
         const int r = r0 + kk;
@@ -1556,7 +1576,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
             const int64_t o = (int64_t)b * nkeys + r;
             out[o] = t[kk][b];
             if (mse.dyo) {
-                const float d = mse.scale * (t[kk][b] - mse.tgt[o]);
+                const float d = mse.scale * (t[kk][b] - tg[i]);
                 mse.dyo[o] = d;
                 t[kk][b] = d;   // only this thread reads (kk, b)
             }
