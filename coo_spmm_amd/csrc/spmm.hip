@@ -1684,9 +1684,8 @@ __global__ void __launch_bounds__(kBlock) permute_dw_kernel(const int32_t* __res
 // its column's offset plus its rank in the column, from iperm): every global
 // access is a run about a cache line long instead of a scattered word.  A
 // half wavefront takes a run, kPermU runs at a time so their loads overlap
-// (the kernel waits on memory, not on issue).  A
-// tile larger than the buffer gathers directly.  With vals, each value also
-// takes its SGD step with its dW.
+// (the kernel waits on memory, not on issue).  A tile larger than the buffer
+// gathers directly.
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kPermU = 10;   // runs per half wavefront in flight
@@ -1703,8 +1702,6 @@ struct PermArgs {
     const int32_t* cols;
     const float* dwt;
     float* dw;
-    float* vals;
-    float lr;
 };
 
 __global__ void __launch_bounds__(kPermThreads) permute_tiles_kernel(PermArgs P)
@@ -1762,11 +1759,7 @@ __global__ void __launch_bounds__(kPermThreads) permute_tiles_kernel(PermArgs P)
     if (E > P.cap) {   // uniform: gather the tile's row runs directly
         for (int ri = wv; ri < nr; ri += kPermWaves) {
             const int32_t k1 = rend[ri];
-            for (int32_t k = rbeg[ri] + lane; k < k1; k += kWave) {
-                const float x = P.dwt[P.iperm[k]];
-                P.dw[k] = x;
-                if (P.vals) P.vals[k] = sgd_value(P.vals[k], x, P.lr);
-            }
+            for (int32_t k = rbeg[ri] + lane; k < k1; k += kWave) P.dw[k] = P.dwt[P.iperm[k]];
         }
         return;
     }
@@ -1806,21 +1799,17 @@ __global__ void __launch_bounds__(kPermThreads) permute_tiles_kernel(PermArgs P)
         }
         for (int t = hl; t < mx; t += 32) {
             int32_t j[kPermU], c[kPermU];
-            float v[kPermU];
 #pragma unroll
             for (int u = 0; u < kPermU; ++u) {
                 const int32_t k = kb[u] + min(t, max(kl[u] - 1, 0));
                 j[u] = P.iperm[k];
                 c[u] = P.cols[k];
-                v[u] = P.vals ? P.vals[k] : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < kPermU; ++u) {
                 if (t < kl[u]) {
                     const int ci = c[u] - c0;
-                    const float x = ent[coff[ci] + (j[u] - cbeg[ci])];
-                    P.dw[kb[u] + t] = x;
-                    if (P.vals) P.vals[kb[u] + t] = sgd_value(v[u], x, P.lr);
+                    P.dw[kb[u] + t] = ent[coff[ci] + (j[u] - cbeg[ci])];
                 }
             }
         }
@@ -2252,12 +2241,9 @@ static bool perm_tiles_plan(const snack_layer* L, int w, PermArgs* P, size_t* ld
     return true;
 }
 
-// dW[k] = dW_t[iperm[k]] (with vals: also vals[k] -= lr * dW[k]), by tiles
-// where perm_tiles_plan allows; *stepped tells whether vals took the step.
-static snack_status permute_dw(const snack_layer* L, int w, const float* dW_t, float* dW, float* vals, float lr,
-                               bool* stepped, hipStream_t s)
+// dW[k] = dW_t[iperm[k]], by tiles where perm_tiles_plan allows
+static snack_status permute_dw(const snack_layer* L, int w, const float* dW_t, float* dW, hipStream_t s)
 {
-    *stepped = false;
     {
         PermArgs P;
         size_t lds = 0;
@@ -2273,11 +2259,8 @@ static snack_status permute_dw(const snack_layer* L, int w, const float* dW_t, f
             P.cols = L->cols;
             P.dwt = dW_t;
             P.dw = dW;
-            P.vals = vals;
-            P.lr = lr;
             hipLaunchKernelGGL(permute_tiles_kernel, dim3((unsigned)tiles), dim3(kPermThreads), lds, s, P);
             SNACK_HIP(hipGetLastError());
-            *stepped = vals != nullptr;
             return SNACK_OK;
         }
     }
@@ -2318,10 +2301,8 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
                                  float* dX, float* dW, float* dW_t, hipStream_t s, bool rm, SgdStep* step)
 {
-    // the in-place step applies to the column pass that also yields dW (single batch tile).  At the
-    // 64-column tile that pass is bound by issue slots and must write dW in column order anyway (the
-    // canonical dW is permuted from it): there the extra store costs more than the separate step of
-    // both copies, which takes over.
+    // the in-place step of vals_t by the column pass that also yields dW (single batch tile), for the
+    // batch-major passes (the slice-tiled and key-major passes decide below)
     float* apply = (step && dX && dW && p.ntiles == 1 && p.btile <= 32) ? L->vals_t : nullptr;
     const float lr = step ? step->lr : 0.0f;
     if (rm) {
@@ -2358,12 +2339,10 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         const bool recompute = recompute_dw(L, p);
-        // wider tiles: where the permutation into canonical order goes by tiles, it also steps the canonical
-        // values, so with the step the column pass steps vals_t there too
-        PermArgs pp;
-        size_t pl = 0;
-        const bool tiled = !recompute && perm_tiles_plan(L, tile_index(p.btile), &pp, &pl);
-        float* ap = (apply || (step && tiled)) ? L->vals_t : nullptr;
+        // with the step the column pass steps vals_t in place; where the canonical dW is permuted from the
+        // column order, the canonical values then take their step in a separate pass (cheaper than in the
+        // permutation, which waits on memory)
+        float* ap = step ? L->vals_t : nullptr;
         {
             // with the step, dW in column order is still needed where the canonical dW is permuted from it
             float* dwo = (ap && recompute) ? nullptr : dW_t;
@@ -2377,7 +2356,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
         if (recompute) {
             // narrow batches: dW in canonical order by a second (cheap) pass over the row view, which
             // with the step also steps the canonical values in place
-            if (!apply) {
+            if (!ap) {
                 if (use_tile(L, L->fwd, p)) return launch_tile<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
                 return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
             }
@@ -2389,10 +2368,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
             return SNACK_OK;
         }
         // wide batches: dW once, in column order, then permuted into canonical order
-        bool stepped = false;
-        SNACK_CHECK(permute_dw(L, tile_index(p.btile), dW_t, dW, (ap && tiled) ? L->vals : nullptr, lr, &stepped, s));
-        if (stepped) step->canon_done = true;
-        return SNACK_OK;
+        return permute_dw(L, tile_index(p.btile), dW_t, dW, s);
     }
     ProfScope prof(KC_SPMM_DX, s);
     if (dW)
