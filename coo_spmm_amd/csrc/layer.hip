@@ -340,7 +340,7 @@ snack_status backward_sgd_impl(snack_layer* L, const float* X, const float* dY, 
 extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const float* dY, float* dX, float* dW,
                                            float lr, int32_t B, snack_stream stream)
 {
-    if (!L || !X || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (!L || !X || !dY || B < 1 || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
     if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
     return backward_sgd_impl(L, X, dY, dX, dW, lr, B, as_stream(stream), false, false);
 }
@@ -349,7 +349,7 @@ extern "C" snack_status snack_train_step_mse(snack_layer* L, const float* X, con
                                              float* dX, float* dW, float scale, float lr, int32_t B,
                                              snack_stream stream)
 {
-    if (!L || !X || !T || !Y || !dY || !dW || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (!L || !X || !T || !Y || !dY || B < 1 || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
     if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);

@@ -114,7 +114,7 @@ snack_status snack_backward(snack_layer* layer, const float* X, const float* dY,
  * (the values move against their gradient) in one call: the same results, bit
  * for bit, as snack_backward(layer, X, dY, dX, dW, B) followed by
  * snack_sgd_step(layer, dW, lr).  X, dY, dW are required (dW written as by
- * snack_backward); dX may be NULL.  Where the column pass computes dW, it also
+ * snack_backward; NULL only for a layer with no entries); dX may be NULL.  Where the column pass computes dW, it also
  * steps the layer's column-ordered value copy in place, so the step moves one
  * copy's worth of bytes less than the two separate calls.
  */
@@ -130,7 +130,8 @@ snack_status snack_backward_sgd(snack_layer* layer, const float* X, const float*
  *   snack_backward_sgd(layer, X, dY, dX, dW, lr, B);
  * (scale = 2 / (B * M) for the mean).  X device float[B, K]; T device
  * float[B, M] (the targets); Y, dY device float[B, M], overwritten; dX device
- * float[B, K] or NULL; dW device float[nnz], 16-byte aligned, overwritten.  The
+ * float[B, K] or NULL; dW device float[nnz], 16-byte aligned, overwritten (NULL
+ * only for a layer with no entries).  The
  * forward's last pass writes dY beside Y (and the feature-major copy the
  * backward reads), and X is copied to feature-major order once for both
  * passes, so the call launches fewer passes than the three separate ones.

@@ -180,3 +180,33 @@ def test_train_step_matches_separate_calls(M, K, nnz):
     finally:
         a.close()
         b.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(1, 1, 1), (1, 300, 17), (300, 1, 29), (7, 9, 0), (64, 4096, 20000)])
+def test_train_step_small_and_degenerate_shapes(M, K, nnz):
+    """The one-call training step on one-row, one-column, empty and short-key
+    layers over ragged batch plans: bit for bit the separate calls."""
+    import torch
+    L = lib()
+    rows, cols, vals = random_layer(M, K, nnz, f"tstep-small/{M}x{K}")
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    u32 = lambda t: host(t).view(np.uint32)
+    try:
+        for B in (1, 2, 3, 5, 8, 13, 33, 64, 65):
+            X = dev(normal((B, K), f"tstep-small/{M}x{K}/X/{B}"))
+            T = dev(normal((B, M), f"tstep-small/{M}x{K}/T/{B}"))
+            say("train step small", M, K, nnz, "B", B)
+            Ya = torch.empty(B, M, device="cuda"); dYa = torch.empty(B, M, device="cuda")
+            L.snack_forward(a.h, X, Ya)
+            L.snack_mse_grad(Ya, T, dYa, 2.0 / (B * M))
+            dXa, dWa = a.backward_sgd(X, dYa, 0.01)
+            Yb, dYb, dXb, dWb = b.train_step_mse(X, T, 0.01)
+            for name, x, y in (("Y", Ya, Yb), ("dY", dYa, dYb), ("dX", dXa, dXb)):
+                assert np.array_equal(u32(x), u32(y)), f"{name} B={B}"
+            if nnz:
+                assert np.array_equal(u32(dWa), u32(dWb)), f"dW B={B}"
+                assert np.array_equal(u32(a.export()[2]), u32(b.export()[2])), f"values B={B}"
+    finally:
+        a.close()
+        b.close()
