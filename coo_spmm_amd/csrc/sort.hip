@@ -96,6 +96,50 @@ __global__ void __launch_bounds__(kScanThreads) scan_tile_sums_kernel(const int3
     if (threadIdx.x == 0) sums[blockIdx.x] = tot;
 }
 
+// Inputs of up to kScanSmallMax items in one launch: one workgroup copies them
+// to LDS with coalesced loads (all in flight), each thread scans a contiguous
+// run there (summed, block-scanned, then rewritten with running prefixes), and
+// the result is copied back coalesced.  In and out may be the same array.
+constexpr int kScanSmallThreads = 1024;
+constexpr int kScanSmallPer = 16;
+constexpr int64_t kScanSmallMax = (int64_t)kScanSmallPer * kScanSmallThreads;
+
+__global__ void __launch_bounds__(kScanSmallThreads) scan_small_kernel(const int32_t* in, int32_t* out, int64_t n,
+                                                                       int32_t* __restrict__ total)
+{
+    __shared__ int32_t buf[kScanSmallMax];
+    __shared__ int32_t smem[kScanSmallThreads / kWave];
+    const int tid = (int)threadIdx.x;
+    const int nn = (int)n;
+#pragma unroll
+    for (int i = 0; i < kScanSmallPer; ++i) {
+        const int e = tid + i * kScanSmallThreads;
+        if (e < nn) buf[e] = in[e];
+    }
+    __syncthreads();
+    const int per = (nn + kScanSmallThreads - 1) / kScanSmallThreads;
+    const int b = tid * per;
+    int32_t s = 0;
+    for (int i = 0; i < per; ++i)
+        if (b + i < nn) s += buf[b + i];
+    int32_t tot;
+    int32_t run = block_exclusive_scan<kScanSmallThreads>(s, smem, &tot);
+    for (int i = 0; i < per; ++i) {
+        if (b + i < nn) {
+            const int32_t v = buf[b + i];
+            buf[b + i] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanSmallPer; ++i) {
+        const int e = tid + i * kScanSmallThreads;
+        if (e < nn) out[e] = buf[e];
+    }
+    if (total && tid == 0) *total = tot;
+}
+
 // direct: the tile prefix is the sum of sums[0, tile); otherwise sums holds exclusive prefixes
 template <bool VEC, bool DIRECT>
 __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(const int32_t* __restrict__ in,
@@ -280,6 +324,11 @@ snack_status exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int3
 {
     if (n <= 0) {
         if (total_dev) SNACK_HIP(hipMemsetAsync(total_dev, 0, 4, s));
+        return SNACK_OK;
+    }
+    if (n <= kScanSmallMax) {
+        hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kScanSmallThreads), 0, s, in, out, n, total_dev);
+        SNACK_HIP(hipGetLastError());
         return SNACK_OK;
     }
     const int64_t nt = (n + kScanTile - 1) / kScanTile;
