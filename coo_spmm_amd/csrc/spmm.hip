@@ -1048,7 +1048,8 @@ constexpr int kTileStaticLds = 1024;   // bytes kept back from the slice buffer
 struct TileArgs {
     const int32_t* tab;   // slice bounds of key r in slice s: tab[s * tstride + r], tab[(s + 1) * tstride + r]
     int64_t tstride;
-    float* part;          // [S][nkeys][tile] partial sums, or null to write the outputs (S == 1)
+    float* part;          // [S][nkeys][tile] partial sums per batch tile, or null to write the outputs (S == 1)
+    int64_t pstride;      // floats between two batch tiles' partial sums
     int32_t S, KB, R;     // slices, key blocks, keys per block
 };
 
@@ -1405,12 +1406,17 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     const int kb = lg - s * T.KB;
     if (s >= T.S) return;
     const int nkeys = A.nkeys;
+    // batch tile (passes without dW may span several; grid dimension y)
+    const int tile = (int)blockIdx.y;
     const int32_t i0 = split_start(s, T.S, A.nidx);
     const int32_t nrow = split_start(s + 1, T.S, A.nidx) - i0;
     {
-        // the batch is a single tile, so the slice's rows are contiguous
-        const int64_t n4 = (int64_t)nrow * (BTILE / 4);
-        const float4* __restrict__ src = reinterpret_cast<const float4*>(A.G + (int64_t)i0 * bp);
+        // the tile's columns of the slice's rows: rows of BTILE floats, bp apart
+        // (contiguous when the batch is a single tile)
+        constexpr int Q = BTILE / 4;
+        const int64_t n4 = (int64_t)nrow * Q;
+        const int64_t rs4 = bp / 4;
+        const float4* __restrict__ src = reinterpret_cast<const float4*>(A.G + (int64_t)i0 * bp + (int64_t)tile * BTILE);
         float4* dst = reinterpret_cast<float4*>(gs_dyn);
         constexpr int SB = 8;
         constexpr int NT = kTileWaves * kWave;
@@ -1419,7 +1425,8 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
 #pragma unroll
             for (int k = 0; k < SB; ++k) {
                 const int64_t q = q0 + (int64_t)k * NT;
-                v[k] = src[q < n4 ? q : n4 - 1];
+                const int64_t qc = q < n4 ? q : n4 - 1;
+                v[k] = src[(qc / Q) * rs4 + (qc % Q)];
             }
             // clamped, unconditional stores (tail lanes rewrite the last element
             // with its own value) keep all SB loads in flight together
@@ -1492,8 +1499,8 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
                     const float tot = group_reduce<BT, NB>(acc, lane);
                     const int b = group_reduce_col<BT, NB>(lane);
                     if (group_reduce_owner<BT, NB>(lane)) {
-                        if (T.part) T.part[((int64_t)s * nkeys + d[q].r) * BTILE + b] = tot;
-                        else if (b < B) A.out[(int64_t)b * nkeys + d[q].r] = tot;
+                        if (T.part) T.part[tile * T.pstride + ((int64_t)s * nkeys + d[q].r) * BTILE + b] = tot;
+                        else if (tile * BTILE + b < B) A.out[(int64_t)(tile * BTILE + b) * nkeys + d[q].r] = tot;
                     }
 #pragma unroll
                     for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
@@ -1530,6 +1537,10 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
     __shared__ float t[KPB][BTILE + 1];
     const int r0 = (int)blockIdx.x * KPB;
     const int64_t sstride = (int64_t)nkeys * Q;
+    // batch tile blockIdx.y (the gradient is only written for a single tile)
+    part += (int64_t)blockIdx.y * S * nkeys * BTILE;
+    out += (int64_t)blockIdx.y * BTILE * nkeys;
+    B -= (int)blockIdx.y * BTILE;
     // the targets of this thread's outputs, loaded first so they arrive with the
     // partial sums (clamped, unconditional loads: without a gradient they come
     // from part, which is longer than any [B][nkeys] array)
@@ -2063,10 +2074,38 @@ inline int tile_index(int btile)
 }
 
 // slice-tiled kernels for batch tiles of 8 to 64 columns on long keys
-inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
+// (use_tile: a single batch tile, for passes with dW; use_tile_spmm: passes
+// without dW, which also take several 64-column tiles, one grid row each)
+// key blocks per slice: about one workgroup per CU over all slices and batch
+// tiles (each stages a whole slice, so with many tiles each workgroup takes
+// more keys), at most 64 keys per wavefront
+inline int tile_key_blocks(const snack_layer* L, const View& v, int S, int ntiles)
+{
+    const int64_t sweeps = (int64_t)S * ntiles;
+    int kbn = (int)((L->cus + sweeps / 2) / sweeps);
+    const int minkb = (v.nkeys + kTileWaves * 64 - 1) / (kTileWaves * 64);
+    const int maxkb = (v.nkeys + kTileWaves - 1) / kTileWaves;
+    if (kbn > maxkb) kbn = maxkb;
+    if (kbn < minkb) kbn = minkb;
+    return kbn < 1 ? 1 : kbn;
+}
+
+constexpr int64_t kTilePartMaxBytes = 256ll << 20;   // partial sums of all batch tiles at most
+constexpr int64_t kTileMinEntries = 8192;            // entries per workgroup for several tiles
+inline bool use_tile_spmm(const snack_layer* L, const View& v, const BatchPlan& p)
 {
     const int i = tile_index(p.btile);
-    return i >= 0 && p.ntiles == 1 && L->nnz > 0 && use_keyed(v, L->nnz, p) && v.split[i].S >= 1;
+    if (i < 0 || L->nnz <= 0 || !use_keyed(v, L->nnz, p) || v.split[i].S < 1) return false;
+    if (p.ntiles == 1) return true;
+    // several tiles: every workgroup stages a slice once per tile, which pays only
+    // when it has enough entries to walk
+    const int S = v.split[i].S;
+    return (int64_t)p.ntiles * S * v.nkeys * p.btile * 4 <= kTilePartMaxBytes &&
+           L->nnz / ((int64_t)S * tile_key_blocks(L, v, S, p.ntiles)) >= kTileMinEntries;
+}
+inline bool use_tile(const snack_layer* L, const View& v, const BatchPlan& p)
+{
+    return p.ntiles == 1 && use_tile_spmm(L, v, p);
 }
 
 // dW in canonical order by its own pass over the row view (else permuted from
@@ -2098,21 +2137,17 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     t.S = st.S;
     t.tab = st.S >= 2 ? st.tab : v.ptr;
     t.tstride = st.S >= 2 ? v.nkeys : 1;
+    if (DW && p.ntiles != 1) return SNACK_ERR_INVALID_ARG;   // dW passes take a single batch tile
     t.part = (st.S >= 2 && SPMM) ? ws_part(L, p) : nullptr;
-    // about one workgroup per CU over all slices, at most 64 keys per wavefront
-    int kbn = (L->cus + t.S / 2) / t.S;
-    const int minkb = (v.nkeys + kTileWaves * 64 - 1) / (kTileWaves * 64);
-    const int maxkb = (v.nkeys + kTileWaves - 1) / kTileWaves;
-    if (kbn > maxkb) kbn = maxkb;
-    if (kbn < minkb) kbn = minkb;
-    if (kbn < 1) kbn = 1;
+    t.pstride = (int64_t)t.S * v.nkeys * p.btile;
+    const int kbn = tile_key_blocks(L, v, t.S, p.ntiles);
     t.KB = kbn;
     t.R = (v.nkeys + kbn - 1) / kbn;
     int64_t nwg = (int64_t)t.S * t.KB;
     nwg = (nwg + kXcd - 1) / kXcd * kXcd;
     const int32_t rows = (v.nidx + t.S - 1) / t.S + 1;   // the slice and a zero row
     const size_t lds = (size_t)rows * p.btile * sizeof(float);
-    const dim3 grid((unsigned)nwg), block(kTileWaves * kWave);
+    const dim3 grid((unsigned)nwg, (unsigned)p.ntiles), block(kTileWaves * kWave);
     // group width x values per lane x entries per group: 2 x 4 x 2, 4 x 4 x 4,
     // 4 x 8 x 4, 16 x 4 x 8 (x 4 with dW: short slice segments waste less)
     constexpr int Dp = DW ? kTileDepthDw : kTileDepth;
@@ -2128,12 +2163,12 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     SNACK_HIP(hipGetLastError());
     if (t.part) {
         MseOut mo{nullptr, nullptr, nullptr, 0.0f};
-        if (mse) {
+        if (mse && p.ntiles == 1) {
             mo = MseOut{mse->T, mse->dY, mse->dYt, mse->scale};
             mse->done = true;
             mse->dyt_done = mse->dYt != nullptr;
         }
-        auto rg = [&](int kpb) { return dim3((unsigned)((v.nkeys + kpb - 1) / kpb)); };
+        auto rg = [&](int kpb) { return dim3((unsigned)((v.nkeys + kpb - 1) / kpb), (unsigned)p.ntiles); };
         switch (p.btile) {
         case 8:
             hipLaunchKernelGGL((split_reduce_kernel<8>), rg(kSplitReduceKeys<8>), dim3(256), 0, s, t.part, t.S, v.nkeys,
@@ -2192,10 +2227,10 @@ size_t tile_part_bytes(const snack_layer* L, const BatchPlan& p)
     size_t need = 0;
     const View* views[2] = {&L->fwd, &L->tr};
     for (const View* v : views) {
-        if (!use_tile(L, *v, p)) continue;
+        if (!use_tile_spmm(L, *v, p)) continue;
         const SplitTab& st = v->split[tile_index(p.btile)];
         if (st.S < 2) continue;
-        const size_t b = (size_t)st.S * v->nkeys * p.btile * sizeof(float);
+        const size_t b = (size_t)p.ntiles * st.S * v->nkeys * p.btile * sizeof(float);
         if (b > need) need = b;
     }
     return (need + 255) & ~(size_t)255;
@@ -2290,7 +2325,7 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 {
     ProfScope prof(KC_SPMM_FWD, s);
     if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true, nullptr, 0.0f, mse);
-    if (use_tile(L, L->fwd, p))
+    if (use_tile_spmm(L, L->fwd, p))
         return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse);
     if (use_keyed(L->fwd, L->nnz, p))
         return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, false, nullptr, 0.0f, mse);
@@ -2373,7 +2408,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     ProfScope prof(KC_SPMM_DX, s);
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
-    if (use_tile(L, L->tr, p)) return launch_tile<false, true>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
+    if (use_tile_spmm(L, L->tr, p)) return launch_tile<false, true>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     if (use_keyed(L->tr, L->nnz, p))
         return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);

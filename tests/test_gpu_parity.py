@@ -67,6 +67,15 @@ def test_long_keys_wide_batches(M, K, nnz):
     _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
 
 
+def test_slice_tiled_several_batch_tiles():
+    # long keys with operands of three and four slices per view; at 449 and 500
+    # columns (eight 64-column tiles, the first with a last tile of one column)
+    # the slice-tiled forward and dX passes run one grid row per tile, at 65
+    # columns the workgroups would have too few entries and the key-major
+    # kernels run instead (dW for these widths takes its own pass)
+    _check_layer_vs_oracle(2000, 1500, 300000, (65, 449, 500), "gpu/multitile/2000x1500", check_index=False)
+
+
 @pytest.mark.parametrize("transpose", [False, True])
 def test_keyed_keys_longer_than_chunks(transpose):
     # keys of ~1400 entries (several chunks each, so chunks that start inside a
