@@ -2092,10 +2092,15 @@ inline int tile_key_blocks(const snack_layer* L, const View& v, int S, int ntile
 
 constexpr int64_t kTilePartMaxBytes = 256ll << 20;   // partial sums of all batch tiles at most
 constexpr int64_t kTileMinEntries = 8192;            // entries per workgroup for several tiles
+constexpr int64_t kTileMinKey64 = 32;                // average entries per key at the 64-column tile
 inline bool use_tile_spmm(const snack_layer* L, const View& v, const BatchPlan& p)
 {
     const int i = tile_index(p.btile);
-    if (i < 0 || L->nnz <= 0 || !use_keyed(v, L->nnz, p) || v.split[i].S < 1) return false;
+    if (i < 0 || L->nnz <= 0 || v.split[i].S < 1) return false;
+    // keys of 128 entries on average; at the 64-column tile also shorter ones (a
+    // block's 16 entries carry 64 columns each, so short segments still pay)
+    if (!use_keyed(v, L->nnz, p) && !(p.btile == 64 && v.nkeys > 0 && L->nnz / v.nkeys >= kTileMinKey64))
+        return false;
     if (p.ntiles == 1) return true;
     // several tiles: every workgroup stages a slice once per tile, which pays only
     // when it has enough entries to walk
