@@ -7,7 +7,7 @@
 // (transposed slot -> canonical slot) and the column pointer (the CSC of the
 // SNACK paper's Table 7).  Both views carry a key-aligned work partition:
 // desc[c] = (first key, first entry) of chunk c, cut so that each chunk holds
-// about kChunkWork units of (entries + keys); a key is never split, so the
+// about the layer's chunk_work units of (entries + keys); a key is never split, so the
 // SpMM needs no cross-chunk fix-up and writes every output row once.  Each view
 // also lists its keys without entries, whose outputs are zero.
 #include "internal.h"
@@ -321,7 +321,7 @@ snack_status build_view_partitions(snack_layer* L, hipStream_t s)
     const int32_t nc = a.nchunks > b.nchunks ? a.nchunks : b.nchunks;
     const int32_t nk = a.nkeys > b.nkeys ? a.nkeys : b.nkeys;
     hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)nc + 1), 2), dim3(kThreads), 0, s, a, b,
-                       kChunkWork);
+                       L->chunk_work);
     hipLaunchKernelGGL(empty_keys_kernel, dim3(grid_for(nk), 2), dim3(kThreads), 0, s, a, b);
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;

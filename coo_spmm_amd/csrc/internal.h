@@ -13,7 +13,9 @@
 namespace snack {
 
 constexpr int kWave = 64;              // CDNA wavefront width
-constexpr int kChunkWork = 512;        // target work (entries + keys) per SpMM chunk
+constexpr int kChunkWork = 512;        // most work (entries + keys) per SpMM chunk
+constexpr int kChunkWorkMin = 128;     // least, for layers too small to fill the GPU with the most
+constexpr int kChunkTarget = 1024;     // chunks per view a layer is cut into at least, where it can
 constexpr int kPad = 2048;             // slack elements after every nnz-sized array
 
 // Kernel classes for the profiling hooks (order = snack_profile_name ids).
@@ -81,6 +83,7 @@ struct snack_layer {
     int32_t M = 0, K = 0;
     int64_t nnz = 0;
     int64_t cap = 0;          // element capacity of each nnz-sized array (>= nnz + kPad)
+    int32_t chunk_work = 0;   // work units per SpMM chunk (kChunkWorkMin .. kChunkWork)
     uint64_t seed = 0;
     uint64_t epoch = 0;
 

@@ -183,8 +183,14 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     ALLOC(col_ptr, int32_t*, ((size_t)K + 1) * 4);
     ALLOC(flag, int32_t*, 64);
 
-    const int64_t nchf = (nnz + M + kChunkWork - 1) / kChunkWork;
-    const int64_t ncht = (nnz + K + kChunkWork - 1) / kChunkWork;
+    {
+        // chunks of up to kChunkWork units, smaller for small layers so that the
+        // chunk-per-wavefront kernels still have about kChunkTarget chunks
+        const int64_t w = (nnz + (M > K ? M : K)) / kChunkTarget;
+        L->chunk_work = (int32_t)(w > kChunkWork ? kChunkWork : (w < kChunkWorkMin ? kChunkWorkMin : w));
+    }
+    const int64_t nchf = (nnz + M + L->chunk_work - 1) / L->chunk_work;
+    const int64_t ncht = (nnz + K + L->chunk_work - 1) / L->chunk_work;
     if (nchf > INT_MAX / 2 || ncht > INT_MAX / 2) return fail(SNACK_ERR_UNSUPPORTED);
     L->fwd.nkeys = M;
     L->fwd.nidx = K;
