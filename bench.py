@@ -97,6 +97,10 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a reference dispatch of known "
                          "size for hardware byte counters)")
+    ap.add_argument("--layers", choices=("gpt2",), default=None,
+                    help="instead of the default workload: time forward, backward and the one-call training step "
+                         "of the GPT-2-small MLP layer shapes (768 -> 3072 and 3072 -> 768 at 90 and 99 %% "
+                         "sparsity) at 64, 256 and 1024 tokens; prints one JSON line of per-layer timings")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +108,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.layers == "gpt2":
+        return layer_shapes(args)
 
     import numpy as np
     import torch
@@ -276,6 +282,56 @@ def main():
 
     layer.close()
     print(json.dumps(out), flush=True)
+
+
+def layer_shapes(args):
+    """Per-layer timings of the GPT-2-small MLP shapes (not the default workload):
+    synthetic N(0,1) activations and targets, uniform random supports; each
+    call timed with events over `--steps` repetitions after `--warmup`."""
+    import torch
+    import coo_spmm_amd as L
+    from snack_inputs import normal, random_layer
+
+    torch.cuda.set_device(0)
+    res = {}
+    for (M, K) in ((3072, 768), (768, 3072)):
+        for sp in (90, 99):
+            nnz = M * K * (100 - sp) // 100
+            r, c, v = random_layer(M, K, nnz, f"gpt2/{M}x{K}/{sp}")
+            layer = L.SnackLayer(M, K, torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda(),
+                                 torch.from_numpy(v).cuda())
+            try:
+                layer.reserve(1024)
+                for B in (64, 256, 1024):
+                    X = torch.from_numpy(normal((B, K), f"gpt2/X/{K}/{B}")).cuda()
+                    T = torch.from_numpy(normal((B, M), f"gpt2/T/{M}/{B}")).cuda()
+                    Y = torch.empty(B, M, device="cuda"); dY = torch.empty(B, M, device="cuda")
+                    dX = torch.empty(B, K, device="cuda"); dW = torch.empty(nnz, device="cuda")
+                    calls = {
+                        "fwd": lambda: L.snack_forward(layer.h, X, Y),
+                        "bwd": lambda: L.snack_backward(layer.h, X, dY, dX, dW),
+                        "train_step": lambda: L.snack_train_step_mse(layer.h, X, T, Y, dY, dX, dW,
+                                                                     2.0 / (B * M), 0.0),
+                    }
+                    d = {}
+                    for name, f in calls.items():
+                        for _ in range(args.warmup):
+                            f()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        torch.cuda.synchronize()
+                        e0.record()
+                        for _ in range(args.steps):
+                            f()
+                        e1.record()
+                        e1.synchronize()
+                        d[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
+                    d["fwd_TFLOPs"] = round(2.0 * B * nnz / (d["fwd_us"] * 1e-6) / 1e12, 2)
+                    d["bwd_TFLOPs"] = round(4.0 * B * nnz / (d["bwd_us"] * 1e-6) / 1e12, 2)
+                    res[f"{M}x{K}/s{sp}/B{B}"] = d
+            finally:
+                layer.close()
+    print(json.dumps({"layers": "gpt2-small MLP shapes", "data": "synthetic", "dtype": "f32",
+                      "steps": args.steps, "warmup": args.warmup, "timings": res}))
 
 
 def cpu_baseline(layer, M, K, nnz, batches, lr, min_seconds=10.0, max_steps=20):
