@@ -138,12 +138,64 @@ __global__ void __launch_bounds__(kThreads) transpose_pad4_kernel(const float* _
         *reinterpret_cast<float4*>(dst + (int64_t)c * bp + b) = v;
     }
 }
+// Wide batches: one 64-feature x 64-column tile per workgroup, read as 16-byte
+// pieces of batch rows (16 threads per 256-byte row), transposed through LDS
+// (rows padded to 65 floats, so the column reads hit distinct banks) and
+// written as 16-byte pieces of feature rows.  Needs n % 4 == 0, bp % 64 == 0
+// and 16-byte aligned arrays.  Blocks x in [0, nx1) handle (src, dst, n).
+// (Narrow batches: the flat variant below issues one 16-byte store per
+// thread and launches many more workgroups.)
+__global__ void __launch_bounds__(kThreads) transpose_tile4_kernel(const float* __restrict__ src1,
+                                                                   float* __restrict__ dst1, int n1,
+                                                                   const float* __restrict__ src2,
+                                                                   float* __restrict__ dst2, int n2, int nx1, int B,
+                                                                   int bp)
+{
+    __shared__ float tile[kTile][kTile + 1];
+    const bool first = (int)blockIdx.x < nx1;
+    const float* __restrict__ src = first ? src1 : src2;
+    float* __restrict__ dst = first ? dst1 : dst2;
+    const int n = first ? n1 : n2;
+    const int c0 = (first ? (int)blockIdx.x : (int)blockIdx.x - nx1) * kTile;
+    const int b0 = (int)blockIdx.y * kTile;
+    const int q = (int)threadIdx.x & 15, r = (int)threadIdx.x >> 4;   // 16-byte piece, row within a group of 16
+#pragma unroll
+    for (int i = 0; i < kTile / 16; ++i) {
+        const int bb = r + 16 * i, b = b0 + bb, c = c0 + 4 * q;
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (b < B && c < n) v = *reinterpret_cast<const float4*>(src + (int64_t)b * n + c);
+        tile[bb][4 * q + 0] = v.x;
+        tile[bb][4 * q + 1] = v.y;
+        tile[bb][4 * q + 2] = v.z;
+        tile[bb][4 * q + 3] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTile / 16; ++i) {
+        const int cc = r + 16 * i, c = c0 + cc;
+        if (c < n)
+            *reinterpret_cast<float4*>(dst + (int64_t)c * bp + b0 + 4 * q) =
+                make_float4(tile[4 * q + 0][cc], tile[4 * q + 1][cc], tile[4 * q + 2][cc], tile[4 * q + 3][cc]);
+    }
+}
+
 }  // namespace
 
 snack_status transpose_pad(const float* src, float* dst, int n, const float* src2, float* dst2, int n2, int B,
                            int bp, hipStream_t s)
 {
     ProfScope prof(KC_TRANSPOSE, s);
+    const bool a16 = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
+                       reinterpret_cast<uintptr_t>(src2) | reinterpret_cast<uintptr_t>(dst2)) & 15) == 0;
+    // from two tiles of columns on (with one, the grid is too small to beat the flat variant)
+    if (bp % kTile == 0 && bp >= 2 * kTile && n % 4 == 0 && (!src2 || n2 % 4 == 0) && a16) {
+        const int nx1 = (n + kTile - 1) / kTile;
+        const int nx2 = src2 ? (n2 + kTile - 1) / kTile : 0;
+        hipLaunchKernelGGL(transpose_tile4_kernel, dim3((unsigned)(nx1 + nx2), (unsigned)(bp / kTile)),
+                           dim3(kThreads), 0, s, src, dst, n, src2, dst2, n2, nx1, B, bp);
+        SNACK_HIP(hipGetLastError());
+        return SNACK_OK;
+    }
     if (bp % 4 == 0) {
         const int64_t total = ((int64_t)n + (src2 ? n2 : 0)) * (bp / 4);
         hipLaunchKernelGGL(transpose_pad4_kernel, dim3(grid_for(total)), dim3(kThreads), 0, s, src, dst, n, src2, dst2,
