@@ -115,6 +115,8 @@ struct snack_layer {
     void* scratch = nullptr;
     size_t scratch_bytes = 0;
     int32_t* flag = nullptr;      // device error / count word(s)
+    uint32_t* host_res = nullptr; // pinned words the drop/regrow grow result is copied into
+    hipEvent_t grow_ev = nullptr; // recorded after that copy
 
     size_t device_bytes = 0;
     std::vector<void*> allocations;

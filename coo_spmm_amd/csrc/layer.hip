@@ -44,6 +44,8 @@ void free_layer(snack_layer* L)
     (void)hipDeviceSynchronize();
     for (void* p : L->allocations) (void)hipFree(p);
     if (L->ws) (void)hipFree(L->ws);
+    if (L->host_res) (void)hipHostFree(L->host_res);
+    if (L->grow_ev) (void)hipEventDestroy(L->grow_ev);
     delete L;
 }
 
@@ -223,6 +225,14 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
         snack_status _s = layer_alloc(L, &L->scratch, scr);
         if (_s != SNACK_OK) return fail(_s);
         L->scratch_bytes = scr;
+    }
+    if (hipHostMalloc((void**)&L->host_res, 64, hipHostMallocDefault) != hipSuccess) {
+        L->host_res = nullptr;
+        return fail(SNACK_ERR_ALLOC);
+    }
+    if (hipEventCreateWithFlags(&L->grow_ev, hipEventDisableTiming) != hipSuccess) {
+        L->grow_ev = nullptr;
+        return fail(SNACK_ERR_HIP);
     }
 #undef ALLOC
 

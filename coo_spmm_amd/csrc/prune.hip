@@ -705,6 +705,18 @@ __global__ void __launch_bounds__(1024) cut_kernel(const int32_t* __restrict__ t
     }
 }
 
+// Runs between a batch and a rebuild queued behind it before the host has
+// seen the batch's result: when the batch overflowed or fell short, the old
+// cells are put back into occ, so the rebuild sees a complete set of exactly
+// nnz cells (its output is then replaced once the grow is redone).
+__global__ void occ_guard_kernel(const uint32_t* __restrict__ state, uint32_t need,
+                                 const uint32_t* __restrict__ old_bm, uint32_t* __restrict__ occ_bm, int64_t words)
+{
+    if (state[kStOverflow] == 0u && state[kStTaken] == need) return;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x)
+        occ_bm[w] = old_bm[w];
+}
+
 // accepted candidates at or past the cut give their cell back (few: the batch
 // is sized to overshoot need only slightly)
 __global__ void give_back_kernel(uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N,
@@ -1434,100 +1446,13 @@ size_t prune_scratch_bytes(const snack_layer* L)
     return layout(L, nullptr);
 }
 
-snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
+namespace {
+
+// The canonical arrays and both views from the occupancy bitmap.
+snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
 {
     const int64_t nnz = L->nnz;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
-    if (n_drop == 0) {
-        L->epoch += 1;
-        return SNACK_OK;
-    }
-    if (N > kMaxBitmapBits || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
-    ProfScope prof(KC_PRUNE, s);
-    PruneScratch ps;
-    layout(L, &ps);
-    const int64_t kept = nnz - n_drop;
-
-    // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
-    {
-        hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1),
-                           ps.fill, kMaxRegions);
-        const unsigned nsel = (unsigned)((nnz + (int64_t)kSelThreads * kSelPer - 1) / ((int64_t)kSelThreads * kSelPer));
-        hipLaunchKernelGGL(sel_pass_kernel<0>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
-        hipLaunchKernelGGL(sel_pass_kernel<1>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
-        hipLaunchKernelGGL(sel_pass_kernel<2>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
-        hipLaunchKernelGGL(sel_pass_kernel<3>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
-        SNACK_HIP(hipGetLastError());
-        hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows, L->cols,
-                           L->vals, nnz, L->K, ps.state, ps.hist, ps.tile_eq, ps.kept_bm, ps.old_bm);
-        // a sparse layer's bitmap is cleared by a full grid (the tiles would each clear long gaps)
-        const int cleared = ps.words > ps.ktiles * (int64_t)kKeepSpan ? 1 : 0;
-        if (cleared)
-            hipLaunchKernelGGL(zero2_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.old_bm,
-                               ps.words);
-        SNACK_HIP(hipGetLastError());
-        if (ps.ktiles <= kKeepDirect) {
-            hipLaunchKernelGGL(keep_tiles_kernel<true>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
-                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
-                               ps.old_bm);
-        } else {
-            // a scan of zeros when every tie is dropped (the counts were not written then; they are not used)
-            SNACK_CHECK(exclusive_scan_i32(ps.tile_eq, ps.tile_eq, ps.ktiles, nullptr, ps.scan, s));
-            hipLaunchKernelGGL(keep_tiles_kernel<false>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
-                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
-                               ps.old_bm);
-        }
-        SNACK_HIP(hipGetLastError());
-    }
-
-    // ---- grow: walk the candidate stream in batches ----
-    int64_t need = n_drop;
-    int64_t got = 0;
-    uint64_t t0 = 0;
-    int batches = 0;
-    int shrink = 0;   // halvings of the batch after a bucket overflow
-    bool claimed = false;   // a batch has written occ
-    const uint64_t words_total = (uint64_t)ps.words;
-    while (need > 0) {
-        const double p_empty = (double)(N - (uint64_t)kept - (uint64_t)got) / (double)N;
-        double want = (double)need / (p_empty > 1e-9 ? p_empty : 1e-9) * 1.03 + 4096.0;
-        int64_t T = want > (double)ps.tmax ? ps.tmax : (int64_t)want;
-        T >>= shrink;
-        if (T < 1) T = 1;
-        const GrowPlan g = grow_plan(N, T);
-        const size_t lds = (size_t)kTabSlots * 8 + ((size_t)1 << g.sb) / 8;
-        if ((int64_t)g.R * g.cap > ps.nbucket || lds > (size_t)L->lds_bytes) return SNACK_ERR_UNSUPPORTED;
-        const unsigned ntiles = (unsigned)((T + kGenTile - 1) / kGenTile);
-        const int32_t nsum = (int32_t)((T + kSumTile - 1) / kSumTile);
-        hipLaunchKernelGGL(gen_bucket_kernel, dim3(ntiles), dim3(kGenThreads), 0, s, L->seed, L->epoch, t0, T, N,
-                           g.rb, g.R, g.cap, ps.fill, ps.bucket, ps.acc8, ps.state);
-        // the first batch starts from the kept cells (occ is first written, whole, by this pass)
-        hipLaunchKernelGGL(region_claim_kernel, dim3((unsigned)g.R), dim3(kClaimThreads), lds, s, g.rb, g.sb,
-                           words_total, g.cap, ps.fill, ps.bucket, claimed ? ps.occ_bm : ps.kept_bm, ps.occ_bm,
-                           ps.acc8, ps.state);
-        hipLaunchKernelGGL(tile_sum_kernel, dim3((unsigned)nsum), dim3(256), 0, s, ps.acc8, T, ps.tsum, ps.state);
-        hipLaunchKernelGGL(cut_kernel, dim3(1), dim3(1024), 0, s, ps.tsum, nsum, ps.acc8, T, need, ps.state);
-        hipLaunchKernelGGL(give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kThreads), 0, s,
-                           L->seed, L->epoch, t0, T, N, ps.acc8, ps.occ_bm, ps.state);
-        SNACK_HIP(hipGetLastError());
-        uint32_t res[2] = {0u, 0u};   // overflow flag, taken
-        SNACK_HIP(hipMemcpyAsync(res, ps.state + kStOverflow, sizeof res, hipMemcpyDeviceToHost, s));
-        SNACK_HIP(hipStreamSynchronize(s));
-        if (++batches > 100000) return SNACK_ERR_UNSUPPORTED;
-        if (res[0]) {   // nothing was changed: take the same candidates in a smaller batch
-            hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.state + kStOverflow, (int64_t)1, 0u);
-            SNACK_HIP(hipGetLastError());
-            ++shrink;
-            continue;
-        }
-        shrink = 0;
-        claimed = true;
-        const int64_t taken = (int64_t)res[1];
-        got += taken;
-        need -= taken;
-        t0 += (uint64_t)T;
-    }
-
     // ---- new canonical arrays: set bits of occ in ascending position ----
     {
         const int64_t nu = ps.units;
@@ -1587,6 +1512,143 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     } else {
         SNACK_CHECK(canon_build_index(L, s));
     }
+    return SNACK_OK;
+}
+
+}  // namespace
+
+snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
+{
+    const int64_t nnz = L->nnz;
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    if (n_drop == 0) {
+        L->epoch += 1;
+        return SNACK_OK;
+    }
+    if (N > kMaxBitmapBits || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
+    ProfScope prof(KC_PRUNE, s);
+    PruneScratch ps;
+    layout(L, &ps);
+    const int64_t kept = nnz - n_drop;
+
+    // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
+    {
+        hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1),
+                           ps.fill, kMaxRegions);
+        const unsigned nsel = (unsigned)((nnz + (int64_t)kSelThreads * kSelPer - 1) / ((int64_t)kSelThreads * kSelPer));
+        hipLaunchKernelGGL(sel_pass_kernel<0>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<1>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<2>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        hipLaunchKernelGGL(sel_pass_kernel<3>, dim3(nsel), dim3(kSelThreads), 0, s, L->vals, nnz, ps.state, ps.hist);
+        SNACK_HIP(hipGetLastError());
+        hipLaunchKernelGGL(eq_tiles_kernel, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows, L->cols,
+                           L->vals, nnz, L->K, ps.state, ps.hist, ps.tile_eq, ps.kept_bm, ps.old_bm);
+        // a sparse layer's bitmap is cleared by a full grid (the tiles would each clear long gaps)
+        const int cleared = ps.words > ps.ktiles * (int64_t)kKeepSpan ? 1 : 0;
+        if (cleared)
+            hipLaunchKernelGGL(zero2_kernel, dim3(grid_for(ps.words)), dim3(kThreads), 0, s, ps.kept_bm, ps.old_bm,
+                               ps.words);
+        SNACK_HIP(hipGetLastError());
+        if (ps.ktiles <= kKeepDirect) {
+            hipLaunchKernelGGL(keep_tiles_kernel<true>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
+                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
+                               ps.old_bm);
+        } else {
+            // a scan of zeros when every tie is dropped (the counts were not written then; they are not used)
+            SNACK_CHECK(exclusive_scan_i32(ps.tile_eq, ps.tile_eq, ps.ktiles, nullptr, ps.scan, s));
+            hipLaunchKernelGGL(keep_tiles_kernel<false>, dim3((unsigned)ps.ktiles), dim3(kKeepThreads), 0, s, L->rows,
+                               L->cols, L->vals, nnz, L->K, ps.words, cleared, ps.state, ps.tile_eq, ps.vcopy, ps.kept_bm,
+                               ps.old_bm);
+        }
+        SNACK_HIP(hipGetLastError());
+    }
+
+    // ---- grow: walk the candidate stream in batches ----
+    int64_t need = n_drop;
+    int64_t got = 0;
+    uint64_t t0 = 0;
+    int batches = 0;
+    int shrink = 0;   // halvings of the batch after a bucket overflow
+    bool claimed = false;   // a batch has written occ
+    const uint64_t words_total = (uint64_t)ps.words;
+    // The first batch nearly always completes the grow, so the rebuild is
+    // queued right behind it, before its result is read (the host would
+    // otherwise leave the GPU idle while it waits and relaunches); a guard
+    // kernel keeps that rebuild consistent if the batch did not complete it,
+    // and the grow then starts over from the kept cells.  Only the bitmap
+    // rebuild qualifies: it uses no scratch that the grow needs.
+    bool speculate = cv_from_bitmap(L);
+    bool rebuilt = false;
+    while (need > 0) {
+        const double p_empty = (double)(N - (uint64_t)kept - (uint64_t)got) / (double)N;
+        double want = (double)need / (p_empty > 1e-9 ? p_empty : 1e-9) * 1.03 + 4096.0;
+        int64_t T = want > (double)ps.tmax ? ps.tmax : (int64_t)want;
+        T >>= shrink;
+        if (T < 1) T = 1;
+        const GrowPlan g = grow_plan(N, T);
+        const size_t lds = (size_t)kTabSlots * 8 + ((size_t)1 << g.sb) / 8;
+        if ((int64_t)g.R * g.cap > ps.nbucket || lds > (size_t)L->lds_bytes) return SNACK_ERR_UNSUPPORTED;
+        const unsigned ntiles = (unsigned)((T + kGenTile - 1) / kGenTile);
+        const int32_t nsum = (int32_t)((T + kSumTile - 1) / kSumTile);
+        hipLaunchKernelGGL(gen_bucket_kernel, dim3(ntiles), dim3(kGenThreads), 0, s, L->seed, L->epoch, t0, T, N,
+                           g.rb, g.R, g.cap, ps.fill, ps.bucket, ps.acc8, ps.state);
+        // the first batch starts from the kept cells (occ is first written, whole, by this pass)
+        hipLaunchKernelGGL(region_claim_kernel, dim3((unsigned)g.R), dim3(kClaimThreads), lds, s, g.rb, g.sb,
+                           words_total, g.cap, ps.fill, ps.bucket, claimed ? ps.occ_bm : ps.kept_bm, ps.occ_bm,
+                           ps.acc8, ps.state);
+        hipLaunchKernelGGL(tile_sum_kernel, dim3((unsigned)nsum), dim3(256), 0, s, ps.acc8, T, ps.tsum, ps.state);
+        hipLaunchKernelGGL(cut_kernel, dim3(1), dim3(1024), 0, s, ps.tsum, nsum, ps.acc8, T, need, ps.state);
+        hipLaunchKernelGGL(give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kThreads), 0, s,
+                           L->seed, L->epoch, t0, T, N, ps.acc8, ps.occ_bm, ps.state);
+        SNACK_HIP(hipGetLastError());
+        // overflow flag, taken
+        SNACK_HIP(hipMemcpyAsync(L->host_res, ps.state + kStOverflow, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                                 s));
+        SNACK_HIP(hipEventRecord(L->grow_ev, s));
+        const bool queued = speculate;
+        if (queued) {
+            hipLaunchKernelGGL(occ_guard_kernel, dim3(grid_for(ps.words) < 1024u ? grid_for(ps.words) : 1024u),
+                               dim3(kThreads), 0, s, ps.state, (uint32_t)need, ps.old_bm, ps.occ_bm, ps.words);
+            SNACK_HIP(hipGetLastError());
+            SNACK_CHECK(rebuild(L, ps, s));
+            speculate = false;
+        }
+        SNACK_HIP(hipEventSynchronize(L->grow_ev));
+        const uint32_t res[2] = {L->host_res[0], L->host_res[1]};
+        if (++batches > 100000) return SNACK_ERR_UNSUPPORTED;
+        if (queued) {
+            if (res[0] == 0u && (int64_t)res[1] == need) {
+                rebuilt = true;
+                break;
+            }
+            // the guard has put the old cells back: take the grow again from the start
+            if (res[0]) {
+                hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.state + kStOverflow,
+                                   (int64_t)1, 0u);
+                SNACK_HIP(hipGetLastError());
+                ++shrink;
+            }
+            need = n_drop;
+            got = 0;
+            t0 = 0;
+            claimed = false;
+            continue;
+        }
+        if (res[0]) {   // nothing was changed: take the same candidates in a smaller batch
+            hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(kThreads), 0, s, ps.state + kStOverflow, (int64_t)1, 0u);
+            SNACK_HIP(hipGetLastError());
+            ++shrink;
+            continue;
+        }
+        shrink = 0;
+        claimed = true;
+        const int64_t taken = (int64_t)res[1];
+        got += taken;
+        need -= taken;
+        t0 += (uint64_t)T;
+    }
+
+    if (!rebuilt) SNACK_CHECK(rebuild(L, ps, s));
     L->epoch += 1;
     return SNACK_OK;
 }
