@@ -86,6 +86,7 @@ struct snack_layer {
     int32_t chunk_work = 0;   // work units per SpMM chunk (kChunkWorkMin .. kChunkWork)
     uint64_t seed = 0;
     uint64_t epoch = 0;
+    int32_t grow_cap_max = 0;   // > 0: limit on the grow step's per-region buckets (retry-path tests)
 
     // canonical (row-sorted) triple
     int32_t* rows = nullptr;

@@ -154,6 +154,10 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     L->K = K;
     L->nnz = nnz;
     L->seed = seed;
+    if (const char* e = getenv("SNACK_GROW_BUCKET_CAP")) {
+        const long c = strtol(e, nullptr, 10);
+        if (c > 0 && c < INT_MAX) L->grow_cap_max = (int32_t)c;
+    }
     L->epoch = 0;
     L->cap = ((nnz + 255) / 256) * 256 + kPad;
 

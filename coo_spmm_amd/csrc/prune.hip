@@ -1585,7 +1585,8 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         int64_t T = want > (double)ps.tmax ? ps.tmax : (int64_t)want;
         T >>= shrink;
         if (T < 1) T = 1;
-        const GrowPlan g = grow_plan(N, T);
+        GrowPlan g = grow_plan(N, T);
+        if (L->grow_cap_max > 0 && g.cap > L->grow_cap_max) g.cap = L->grow_cap_max;
         const size_t lds = (size_t)kTabSlots * 8 + ((size_t)1 << g.sb) / 8;
         if ((int64_t)g.R * g.cap > ps.nbucket || lds > (size_t)L->lds_bytes) return SNACK_ERR_UNSUPPORTED;
         const unsigned ntiles = (unsigned)((T + kGenTile - 1) / kGenTile);

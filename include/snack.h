@@ -150,7 +150,12 @@ snack_status snack_train_step_mse(snack_layer* layer, const float* X, const floa
  * [0, M*K) by the high word of the 64x64-bit product; a candidate is accepted
  * if its position is neither kept nor accepted earlier in the stream.  The
  * triple is re-canonicalised and the epoch incremented.  0 <= n_drop <= nnz.
- * May synchronise `stream` (once per candidate batch, normally once).
+ * May synchronise `stream` (once per candidate batch, normally once).  The
+ * candidates are grouped by region in buckets of a fixed capacity; a batch
+ * whose bucket overflows is taken again at half size, which does not change
+ * the result.  For tests of that path, the environment variable
+ * SNACK_GROW_BUCKET_CAP (a positive integer, read when a layer is created)
+ * lowers the capacity of that layer's buckets.
  */
 snack_status snack_prune_regrow(snack_layer* layer, int64_t n_drop, snack_stream stream);
 

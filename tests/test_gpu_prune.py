@@ -54,6 +54,15 @@ def test_prune_ties_signed_zero_nan():
     _run(M, K, nnz, (0.1, 0.3, 0.6), "gpu/prune/ties", vals=vals)
 
 
+@pytest.mark.parametrize("M,K,nnz,cap", [(500, 500, 12500, 24), (64, 64, 4096, 16)])
+def test_prune_bucket_overflow_retries(M, K, nnz, cap, monkeypatch):
+    # tiny buckets overflow on most batches: each is taken again at half size
+    # (and the rebuild queued behind the first batch is replaced), the result
+    # being the same as with one large batch
+    monkeypatch.setenv("SNACK_GROW_BUCKET_CAP", str(cap))
+    _run(M, K, nnz, (0.3, 0.05), f"gpu/prune/overflow/{M}x{K}")
+
+
 def test_prune_full_scale_10000_square():
     # 10000 x 10000 at 95 %: drop 30 % of 5,000,000 twice (two epochs)
     _run(10000, 10000, 5_000_000, (0.3,), "gpu/prune/c4", rounds=2)
