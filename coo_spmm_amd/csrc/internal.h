@@ -262,6 +262,12 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
 int tile_splits(const snack_layer* L, const View& v, int btile);
 snack_status alloc_split_tables(snack_layer* L);
 size_t tile_part_bytes(const snack_layer* L, const BatchPlan& p);
+// several 64-column batch tiles: dX and dW in one slice-tiled column pass (one dW slab per tile,
+// added up in tile order into dW_t, then permuted into canonical order into dW)
+bool wide_dw_fused(const snack_layer* L, const BatchPlan& p);
+size_t wide_dw_bytes(const snack_layer* L, const BatchPlan& p);   // the slabs; 0 where not taken
+snack_status spmm_backward_wide(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
+                                float* dX, float* dW, float* dW_t, float* slabs, hipStream_t s);
 float* ws_part(const snack_layer* L, const BatchPlan& p);   // layer.hip
 
 // dW for batches wider than one tile (loops over the tiles)

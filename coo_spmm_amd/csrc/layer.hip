@@ -55,7 +55,7 @@ size_t ws_need(const snack_layer* L, const BatchPlan& p)
 {
     const size_t a = (((size_t)L->K * p.bp * 4) + 255) & ~(size_t)255;
     const size_t b = (((size_t)L->M * p.bp * 4) + 255) & ~(size_t)255;
-    return a + b + tile_part_bytes(L, p);
+    return a + b + tile_part_bytes(L, p) + wide_dw_bytes(L, p);
 }
 
 snack_status ensure_ws(snack_layer* L, const BatchPlan& p)
@@ -93,6 +93,12 @@ float* snack::ws_part(const snack_layer* L, const BatchPlan& p)
 }
 
 namespace {
+
+// the per-tile dW slabs of the several-tile column pass: after the partial sums
+float* ws_dw_slabs(snack_layer* L, const BatchPlan& p)
+{
+    return (float*)((char*)ws_part(L, p) + tile_part_bytes(L, p));
+}
 
 float* ws_dy(snack_layer* L, const BatchPlan& p)
 {
@@ -317,6 +323,11 @@ snack_status backward_impl(snack_layer* L, const float* X, const float* dY, floa
             L->dwt_for = dW;
             L->dwt_valid = true;
         }
+    } else if (dX && dW && wide_dw_fused(L, p)) {
+        // one column pass for dX and dW over all batch tiles; dW in column order stays for the SGD step
+        SNACK_CHECK(spmm_backward_wide(L, xt, dyt, p, B, dX, dW, L->dwt, ws_dw_slabs(L, p), s));
+        L->dwt_for = dW;
+        L->dwt_valid = true;
     } else {
         if (dX) SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, nullptr, nullptr, s));
         if (dW) SNACK_CHECK(sddmm_dw_tiles(L, xt, dyt, p, dW, s));

@@ -1050,6 +1050,7 @@ struct TileArgs {
     int64_t tstride;
     float* part;          // [S][nkeys][tile] partial sums per batch tile, or null to write the outputs (S == 1)
     int64_t pstride;      // floats between two batch tiles' partial sums
+    int64_t dwstride;     // floats between two batch tiles' dW (several tiles: one dW slab per tile)
     int32_t S, KB, R;     // slices, key blocks, keys per block
 };
 
@@ -1406,8 +1407,13 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     const int kb = lg - s * T.KB;
     if (s >= T.S) return;
     const int nkeys = A.nkeys;
-    // batch tile (passes without dW may span several; grid dimension y)
+    // batch tile (grid dimension y); over several tiles, a dW pass reads the
+    // tile's columns of the key's row and writes the tile's own dW slab
     const int tile = (int)blockIdx.y;
+    if constexpr (DW) {
+        A.H += (int64_t)tile * BTILE;
+        A.dwo += (int64_t)tile * T.dwstride;
+    }
     const int32_t i0 = split_start(s, T.S, A.nidx);
     const int32_t nrow = split_start(s + 1, T.S, A.nidx) - i0;
     {
@@ -2142,7 +2148,10 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     t.S = st.S;
     t.tab = st.S >= 2 ? st.tab : v.ptr;
     t.tstride = st.S >= 2 ? v.nkeys : 1;
-    if (DW && p.ntiles != 1) return SNACK_ERR_INVALID_ARG;   // dW passes take a single batch tile
+    // over several batch tiles a dW pass writes one dW slab per tile (L->cap floats apart), to be
+    // added up afterwards: no in-place step and no value-stepping row pass there
+    if ((DW || VAL) && p.ntiles != 1 && (VAL || apply || !dwo)) return SNACK_ERR_INVALID_ARG;
+    t.dwstride = p.ntiles != 1 ? L->cap : 0;
     t.part = (st.S >= 2 && SPMM) ? ws_part(L, p) : nullptr;
     t.pstride = (int64_t)t.S * v.nkeys * p.btile;
     const int kbn = tile_key_blocks(L, v, t.S, p.ntiles);
@@ -2417,6 +2426,61 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (use_keyed(L->tr, L->nnz, p))
         return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
+}
+
+namespace {
+
+// dW in column order from the per-tile slabs: dwt[e] = sum over tiles, in tile order
+__global__ void dw_slab_sum_kernel(const float* __restrict__ slabs, int64_t stride, int ntiles, int64_t nnz,
+                                   float* __restrict__ dwt)
+{
+    const int64_t n4 = nnz >> 2;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += step) {
+        float4 a = *reinterpret_cast<const float4*>(slabs + 4 * q);
+        for (int t = 1; t < ntiles; ++t) {
+            const float4 b = *reinterpret_cast<const float4*>(slabs + (int64_t)t * stride + 4 * q);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        *reinterpret_cast<float4*>(dwt + 4 * q) = a;
+    }
+    for (int64_t e = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += step) {
+        float a = slabs[e];
+        for (int t = 1; t < ntiles; ++t) a += slabs[(int64_t)t * stride + e];
+        dwt[e] = a;
+    }
+}
+
+}  // namespace
+
+bool wide_dw_fused(const snack_layer* L, const BatchPlan& p)
+{
+    return p.ntiles > 1 && p.btile == 64 && L->nnz > 0 && L->cap % 4 == 0 &&
+           (int64_t)p.ntiles * L->cap * 4 <= kTilePartMaxBytes && use_tile_spmm(L, L->tr, p);
+}
+
+size_t wide_dw_bytes(const snack_layer* L, const BatchPlan& p)
+{
+    return wide_dw_fused(L, p) ? (((size_t)p.ntiles * L->cap * 4) + 255) & ~(size_t)255 : 0;
+}
+
+snack_status spmm_backward_wide(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
+                                float* dX, float* dW, float* dW_t, float* slabs, hipStream_t s)
+{
+    if (!wide_dw_fused(L, p) || !dX || !dW || !dW_t || !slabs) return SNACK_ERR_INVALID_ARG;
+    {
+        ProfScope prof(KC_SPMM_DX, s);
+        SNACK_CHECK((launch_tile<true, true>(p, L, L->tr, dyt, xt, dX, slabs, B, s)));
+    }
+    ProfScope prof(KC_SDDMM_DW, s);
+    const int64_t n4 = (L->nnz + 3) / 4;
+    const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(dw_slab_sum_kernel, dim3(grid), dim3(256), 0, s, slabs, L->cap, p.ntiles, L->nnz, dW_t);
+    SNACK_HIP(hipGetLastError());
+    return permute_dw(L, tile_index(p.btile), dW_t, dW, s);
 }
 
 snack_status sddmm_dw_tiles(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,

@@ -70,9 +70,10 @@ def test_long_keys_wide_batches(M, K, nnz):
 def test_slice_tiled_several_batch_tiles():
     # long keys with operands of three and four slices per view; at 449 and 500
     # columns (eight 64-column tiles, the first with a last tile of one column)
-    # the slice-tiled forward and dX passes run one grid row per tile, at 65
-    # columns the workgroups would have too few entries and the key-major
-    # kernels run instead (dW for these widths takes its own pass)
+    # the slice-tiled forward and column passes run one grid row per tile (the
+    # column pass writing one dW slab per tile, added up and permuted into
+    # canonical order afterwards); at 65 columns the workgroups would have too
+    # few entries and the key-major kernels and a separate dW pass run instead
     _check_layer_vs_oracle(2000, 1500, 300000, (65, 449, 500), "gpu/multitile/2000x1500", check_index=False)
 
 

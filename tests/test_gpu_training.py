@@ -152,7 +152,7 @@ def test_train_step_matches_separate_calls(M, K, nnz):
     lr = 0.01
     u32 = lambda t: host(t).view(np.uint32)
     try:
-        for B in (1, 2, 3, 4, 8, 16, 32, 64, 100):
+        for B in (1, 2, 3, 4, 8, 16, 32, 64, 100, 449):
             X = dev(normal((B, K), f"tstep/{M}x{K}/X/{B}"))
             T = dev(normal((B, M), f"tstep/{M}x{K}/T/{B}"))
             scale = 2.0 / (B * M)
