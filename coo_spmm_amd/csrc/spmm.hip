@@ -1543,9 +1543,14 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
     __shared__ float t[KPB][BTILE + 1];
     const int r0 = (int)blockIdx.x * KPB;
     const int64_t sstride = (int64_t)nkeys * Q;
-    // batch tile blockIdx.y (the gradient is only written for a single tile)
+    // batch tile blockIdx.y: its partial sums, and its rows of the batch-major
+    // arrays (outputs, targets, gradient)
     part += (int64_t)blockIdx.y * S * nkeys * BTILE;
     out += (int64_t)blockIdx.y * BTILE * nkeys;
+    if (mse.dyo) {
+        mse.tgt += (int64_t)blockIdx.y * BTILE * nkeys;
+        mse.dyo += (int64_t)blockIdx.y * BTILE * nkeys;
+    }
     B -= (int)blockIdx.y * BTILE;
     // the targets of this thread's outputs, loaded first so they arrive with the
     // partial sums (clamped, unconditional loads: without a gradient they come
@@ -1606,7 +1611,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
             const int b = (e - kk * Q) * 4;
             const int r = r0 + kk;
             if (r < nkeys)
-                *reinterpret_cast<float4*>(mse.dyt + (int64_t)r * BTILE + b) =
+                *reinterpret_cast<float4*>(mse.dyt + (int64_t)r * BTILE * gridDim.y + blockIdx.y * BTILE + b) =
                     make_float4(b < B ? t[kk][b] : 0.0f, b + 1 < B ? t[kk][b + 1] : 0.0f,
                                 b + 2 < B ? t[kk][b + 2] : 0.0f, b + 3 < B ? t[kk][b + 3] : 0.0f);
         }
@@ -2177,7 +2182,7 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     SNACK_HIP(hipGetLastError());
     if (t.part) {
         MseOut mo{nullptr, nullptr, nullptr, 0.0f};
-        if (mse && p.ntiles == 1) {
+        if (mse) {
             mo = MseOut{mse->T, mse->dY, mse->dYt, mse->scale};
             mse->done = true;
             mse->dyt_done = mse->dYt != nullptr;
