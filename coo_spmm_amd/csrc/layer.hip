@@ -274,7 +274,23 @@ extern "C" snack_status snack_layer_destroy(snack_layer* layer)
 extern "C" snack_status snack_layer_reserve(snack_layer* L, int32_t max_batch)
 {
     if (!L || max_batch < 1) return SNACK_ERR_INVALID_ARG;
-    return ensure_ws(L, plan_batch(max_batch));
+    // the largest workspace of any batch plan up to max_batch (the slice-tiled
+    // passes' buffers are only taken below size limits, so a smaller batch can
+    // need more than max_batch itself): one batch per plan
+    BatchPlan best = plan_batch(1);
+    size_t need = 0;
+    for (int32_t b = 1;;) {
+        const BatchPlan p = plan_batch(b);
+        const size_t n = ws_need(L, p);
+        if (n > need) {
+            need = n;
+            best = p;
+        }
+        if (b >= max_batch) break;
+        const int32_t next = b < 64 ? 2 * b : (b > INT32_MAX - 64 ? INT32_MAX : b + 64);
+        b = next < max_batch ? next : max_batch;
+    }
+    return ensure_ws(L, best);
 }
 
 extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, int32_t B, snack_stream stream)

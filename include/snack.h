@@ -77,9 +77,10 @@ snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz,
 snack_status snack_layer_destroy(snack_layer* layer);
 
 /*
- * Pre-size the per-batch workspace (feature-major copies of X and dY) for
- * batches up to max_batch, so that later forward/backward calls with B <=
- * max_batch allocate nothing.  A larger B grows the workspace on first use.
+ * Pre-size the per-batch workspace (feature-major copies of X and dY, and the
+ * partial sums of the batch-tiled passes) for every batch up to max_batch, so
+ * that later forward/backward calls with B <= max_batch allocate nothing.  A
+ * larger B grows the workspace on first use.
  */
 snack_status snack_layer_reserve(snack_layer* layer, int32_t max_batch);
 

@@ -253,3 +253,25 @@ def test_create_errors_leave_no_layer():
     with pytest.raises(L.SnackError) as e:
         L.SnackLayer(4, 4, dev(np.array([1, -1], np.int32)), dev(np.array([3, 3], np.int32)))
     assert e.value.code == L.ERR_INDEX_RANGE
+
+
+def test_reserve_covers_every_batch_up_to_it():
+    """After snack_layer_reserve(max_batch), calls at any batch up to it
+    allocate nothing: the workspace is sized for the largest plan, which need
+    not be max_batch's own (the batch-tiled buffers have size limits)."""
+    L = lib()
+    M, K, nnz = 2000, 1500, 300000
+    rows, cols, vals = _make(M, K, nnz, "gpu/reserve", None)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    try:
+        layer.reserve(600)
+        before = layer.device_bytes()
+        for B in (600, 1, 8, 64, 65, 449, 500, 130):
+            say("reserve", "B", B)
+            X = dev(normal((B, K), f"gpu/reserve/X/{B}"))
+            dY = dev(normal((B, M), f"gpu/reserve/dY/{B}"))
+            layer.forward(X)
+            layer.backward(X, dY)
+            assert layer.device_bytes() == before, f"B={B} grew the workspace"
+    finally:
+        layer.close()
