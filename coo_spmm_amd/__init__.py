@@ -69,7 +69,7 @@ for _name, (_args, _res) in _SIGS.items():
 
 EXPORTED = tuple(_SIGS)
 
-OK, ERR_INVALID_ARG, ERR_INDEX_RANGE, ERR_DUPLICATE, ERR_ALLOC, ERR_HIP, ERR_UNSUPPORTED = range(7)
+OK, ERR_INVALID_ARG, ERR_INDEX_RANGE, ERR_DUPLICATE, ERR_ALLOC, ERR_HIP, ERR_UNSUPPORTED, ERR_WORKSPACE = range(8)
 
 
 class SnackError(RuntimeError):
@@ -287,10 +287,13 @@ def profile_snapshot():
 class SnackLayer:
     """Owns one layer handle.  Tensors are torch device tensors."""
 
-    def __init__(self, M, K, rows, cols, vals=None, seed=0, stream=None):
+    def __init__(self, M, K, rows, cols, vals=None, seed=0, stream=None, max_batch=None):
+        """max_batch: also reserve the workspace for batches up to it (create covers up to 64)."""
         self.M, self.K = int(M), int(K)
         self.h = snack_layer_create(self.M, self.K, rows, cols, vals, seed, stream)
         self.nnz = snack_layer_nnz(self.h)
+        if max_batch is not None:
+            snack_layer_reserve(self.h, int(max_batch))
 
     def close(self):
         if getattr(self, "h", None):

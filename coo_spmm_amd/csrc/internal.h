@@ -17,6 +17,8 @@ constexpr int kChunkWork = 512;        // most work (entries + keys) per SpMM ch
 constexpr int kChunkWorkMin = 128;     // least, for layers too small to fill the GPU with the most
 constexpr int kChunkTarget = 1024;     // chunks per view a layer is cut into at least, where it can
 constexpr int kPad = 2048;             // slack elements after every nnz-sized array
+constexpr int32_t kMaxBatch = 1 << 20; // largest batch a call accepts
+constexpr int32_t kDefaultReserve = 64; // batches a layer's workspace covers from create on
 
 // Kernel classes for the profiling hooks (order = snack_profile_name ids).
 enum KernelClass : int {
@@ -235,9 +237,13 @@ struct MseFuse {
 };
 
 // Y[b, key] = sum over the canonical view's entries of v * Xt[idx, b]; with rm
-// the operand is the batch-major X itself
+// the operand is the batch-major X itself.  part: where the slice-tiled pass
+// keeps its partial sums (forward_part_bytes of them); null selects the
+// layer's workspace
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s, bool rm = false, MseFuse* mse = nullptr);
+                          hipStream_t s, bool rm = false, MseFuse* mse = nullptr, float* part = nullptr);
+// bytes of slice partial sums the forward of plan p writes (0: none)
+size_t forward_part_bytes(const snack_layer* L, const BatchPlan& p);
 
 // one launch: dX over the transposed view (plus dW in transposed order when
 // dW_t is non-null) and dW over the canonical view; either output may be null.

@@ -58,26 +58,62 @@ size_t ws_need(const snack_layer* L, const BatchPlan& p)
     return a + b + tile_part_bytes(L, p) + wide_dw_bytes(L, p);
 }
 
+// grow the workspace to hold plan p (never shrinks); the new buffer is
+// allocated before the old one is released, so a failed grow keeps the old
+// reserve
 snack_status ensure_ws(snack_layer* L, const BatchPlan& p)
 {
     const size_t need = ws_need(L, p);
     if (need <= L->ws_bytes) return SNACK_OK;
-    if (L->ws) {
-        SNACK_HIP(hipDeviceSynchronize());
-        (void)hipFree(L->ws);
-        L->device_bytes -= L->ws_bytes;
-        L->ws = nullptr;
-        L->ws_bytes = 0;
-    }
     void* p2 = nullptr;
     if (hipMalloc(&p2, need) != hipSuccess) {
         (void)hipGetLastError();
         return SNACK_ERR_ALLOC;
     }
+    if (L->ws) {
+        // work queued on any stream may still read the old buffer
+        const hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            report_hip_error(e, "hipDeviceSynchronize", __FILE__, __LINE__);
+            (void)hipFree(p2);
+            return SNACK_ERR_HIP;
+        }
+        (void)hipFree(L->ws);
+        L->device_bytes -= L->ws_bytes;
+    }
     L->ws = (float*)p2;
     L->ws_bytes = need;
     L->device_bytes += need;
     return SNACK_OK;
+}
+
+// the compute entry points never allocate: a batch plan whose workspace is not
+// reserved is refused before anything is launched
+snack_status ws_check(const snack_layer* L, const BatchPlan& p)
+{
+    return ws_need(L, p) <= L->ws_bytes ? SNACK_OK : SNACK_ERR_WORKSPACE;
+}
+
+// the largest workspace of any batch plan up to max_batch (the slice-tiled
+// passes' buffers are only taken below size limits, so a smaller batch can
+// need more than max_batch itself): one batch per plan, at most
+// kMaxBatch / 64 + 7 of them
+snack_status reserve_ws(snack_layer* L, int32_t max_batch)
+{
+    BatchPlan best = plan_batch(1);
+    size_t need = 0;
+    for (int32_t b = 1;;) {
+        const BatchPlan p = plan_batch(b);
+        const size_t n = ws_need(L, p);
+        if (n > need) {
+            need = n;
+            best = p;
+        }
+        if (b >= max_batch) break;
+        const int32_t next = b < 64 ? 2 * b : b + 64;
+        b = next < max_batch ? next : max_batch;
+    }
+    return ensure_ws(L, best);
 }
 
 float* ws_x(snack_layer* L) { return L->ws; }
@@ -118,6 +154,7 @@ extern "C" const char* snack_status_string(snack_status s)
     case SNACK_ERR_ALLOC: return "device allocation failed";
     case SNACK_ERR_HIP: return "HIP runtime error";
     case SNACK_ERR_UNSUPPORTED: return "unsupported size";
+    case SNACK_ERR_WORKSPACE: return "batch exceeds the reserved workspace (snack_layer_reserve)";
     }
     return "unknown status";
 }
@@ -261,6 +298,8 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     if (flag & 2) return fail(SNACK_ERR_DUPLICATE);
     st = canon_build_index(L, s);
     if (st != SNACK_OK) return fail(st);
+    st = reserve_ws(L, kDefaultReserve);
+    if (st != SNACK_OK) return fail(st);
     *out = L;
     return SNACK_OK;
 }
@@ -274,34 +313,20 @@ extern "C" snack_status snack_layer_destroy(snack_layer* layer)
 extern "C" snack_status snack_layer_reserve(snack_layer* L, int32_t max_batch)
 {
     if (!L || max_batch < 1) return SNACK_ERR_INVALID_ARG;
-    // the largest workspace of any batch plan up to max_batch (the slice-tiled
-    // passes' buffers are only taken below size limits, so a smaller batch can
-    // need more than max_batch itself): one batch per plan
-    BatchPlan best = plan_batch(1);
-    size_t need = 0;
-    for (int32_t b = 1;;) {
-        const BatchPlan p = plan_batch(b);
-        const size_t n = ws_need(L, p);
-        if (n > need) {
-            need = n;
-            best = p;
-        }
-        if (b >= max_batch) break;
-        const int32_t next = b < 64 ? 2 * b : (b > INT32_MAX - 64 ? INT32_MAX : b + 64);
-        b = next < max_batch ? next : max_batch;
-    }
-    return ensure_ws(L, best);
+    if (max_batch > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
+    return reserve_ws(L, max_batch);
 }
 
 extern "C" snack_status snack_forward(snack_layer* L, const float* X, float* Y, int32_t B, snack_stream stream)
 {
     if (!L || !X || !Y || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
     if (spmm_batch_major(L, p, true, false, false)) return spmm_forward(L, X, p, B, Y, s, true);
     const float* feat = X;
     if (p.bp > 1) {
-        SNACK_CHECK(ensure_ws(L, p));
+        SNACK_CHECK(ws_check(L, p));
         SNACK_CHECK(transpose_pad(X, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
         feat = ws_x(L);
     }
@@ -322,7 +347,7 @@ snack_status backward_impl(snack_layer* L, const float* X, const float* dY, floa
     const float* dyt = dY;
     const float* xt = X;
     if (p.bp > 1 && !rm) {
-        SNACK_CHECK(ensure_ws(L, p));
+        SNACK_CHECK(ws_check(L, p));
         const float* xs = (dW && !x_ready) ? X : nullptr;
         if (!dy_ready) SNACK_CHECK(transpose_pad(dY, ws_dy(L, p), L->M, xs, ws_x(L), L->K, B, p.bp, s));
         else if (xs) SNACK_CHECK(transpose_pad(xs, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
@@ -357,6 +382,7 @@ extern "C" snack_status snack_backward(snack_layer* L, const float* X, const flo
                                        int32_t B, snack_stream stream)
 {
     if (!L || !dY || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
     if (dW && !X) return SNACK_ERR_INVALID_ARG;
     if (dW && ((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;   // 16-byte vector stores
     if (!dX && !dW) return SNACK_OK;
@@ -388,6 +414,7 @@ extern "C" snack_status snack_backward_sgd(snack_layer* L, const float* X, const
                                            float lr, int32_t B, snack_stream stream)
 {
     if (!L || !X || !dY || B < 1 || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
     if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
     return backward_sgd_impl(L, X, dY, dX, dW, lr, B, as_stream(stream), false, false);
 }
@@ -397,6 +424,7 @@ extern "C" snack_status snack_train_step_mse(snack_layer* L, const float* X, con
                                              snack_stream stream)
 {
     if (!L || !X || !T || !Y || !dY || B < 1 || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
     if (((uintptr_t)dW & 15) != 0) return SNACK_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     const BatchPlan p = plan_batch(B);
@@ -409,7 +437,7 @@ extern "C" snack_status snack_train_step_mse(snack_layer* L, const float* X, con
         if (p.bp > 1) {
             // one feature-major copy of X for the forward and the backward; the forward's last pass can
             // write dY's feature-major copy too, where the backward takes one
-            SNACK_CHECK(ensure_ws(L, p));
+            SNACK_CHECK(ws_check(L, p));
             SNACK_CHECK(transpose_pad(X, ws_x(L), L->K, nullptr, nullptr, 0, B, p.bp, s));
             feat = ws_x(L);
             x_ready = true;
@@ -515,9 +543,11 @@ extern "C" snack_status snack_layer_set_epoch(snack_layer* L, uint64_t epoch)
 extern "C" snack_status snack_sgd_step(snack_layer* L, const float* dW, float lr, snack_stream stream)
 {
     if (!L || (!dW && L->nnz > 0)) return SNACK_ERR_INVALID_ARG;
-    const float* dwt = (L->dwt_valid && dW == L->dwt_for) ? L->dwt : nullptr;
+    // the caller may have changed dW since the backward (clipping, scaling), so
+    // the column-ordered copy is refreshed from the stepped values before the
+    // next pass that reads it, never stepped with a column-order dW of its own
     L->dwt_valid = false;
-    return sgd_update(L, dW, dwt, lr, as_stream(stream));
+    return sgd_update(L, dW, nullptr, lr, as_stream(stream));
 }
 
 extern "C" snack_status snack_mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale,

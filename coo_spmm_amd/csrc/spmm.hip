@@ -2140,7 +2140,7 @@ inline bool recompute_dw(const snack_layer* L, const BatchPlan& p)
 template <bool DW, bool SPMM, bool VAL = false>
 snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v, const float* G, const float* H,
                          float* out, float* dwo, int B, hipStream_t s, float* apply = nullptr, float lr = 0.0f,
-                         MseFuse* mse = nullptr)
+                         MseFuse* mse = nullptr, float* part = nullptr)
 {
     constexpr bool LV = SPMM || VAL;
     if (apply && !LV) return SNACK_ERR_INVALID_ARG;   // the step needs the values
@@ -2157,7 +2157,8 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     // added up afterwards: no in-place step and no value-stepping row pass there
     if ((DW || VAL) && p.ntiles != 1 && (VAL || apply || !dwo)) return SNACK_ERR_INVALID_ARG;
     t.dwstride = p.ntiles != 1 ? L->cap : 0;
-    t.part = (st.S >= 2 && SPMM) ? ws_part(L, p) : nullptr;
+    // the slice partial sums: the layer's workspace unless the caller brings a buffer
+    t.part = (st.S >= 2 && SPMM) ? (part ? part : ws_part(L, p)) : nullptr;
     t.pstride = (int64_t)t.S * v.nkeys * p.btile;
     const int kbn = tile_key_blocks(L, v, t.S, p.ntiles);
     t.KB = kbn;
@@ -2239,6 +2240,15 @@ snack_status alloc_split_tables(snack_layer* L)
         }
     }
     return SNACK_OK;
+}
+
+size_t forward_part_bytes(const snack_layer* L, const BatchPlan& p)
+{
+    if (!use_tile_spmm(L, L->fwd, p)) return 0;
+    const SplitTab& st = L->fwd.split[tile_index(p.btile)];
+    if (st.S < 2) return 0;
+    const size_t b = (size_t)p.ntiles * st.S * L->fwd.nkeys * p.btile * sizeof(float);
+    return (b + 255) & ~(size_t)255;
 }
 
 size_t tile_part_bytes(const snack_layer* L, const BatchPlan& p)
@@ -2340,12 +2350,12 @@ bool spmm_batch_major(const snack_layer* L, const BatchPlan& p, bool fwd, bool d
 }
 
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
-                          hipStream_t s, bool rm, MseFuse* mse)
+                          hipStream_t s, bool rm, MseFuse* mse, float* part)
 {
     ProfScope prof(KC_SPMM_FWD, s);
     if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true, nullptr, 0.0f, mse);
     if (use_tile_spmm(L, L->fwd, p))
-        return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse);
+        return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse, part);
     if (use_keyed(L->fwd, L->nnz, p))
         return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, false, nullptr, 0.0f, mse);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,

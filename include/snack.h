@@ -24,6 +24,13 @@
  *    is returned as SNACK_ERR_HIP; asynchronous device faults surface at the
  *    next synchronising call.  No C++ exception crosses this interface.
  *  - Index type is int32: nnz, M and K must each be below 2^31.
+ *  - Device memory is allocated only by snack_layer_create and
+ *    snack_layer_reserve.  Forward, backward, the fused training calls and
+ *    drop/regrow allocate nothing and never synchronise the device (drop/regrow
+ *    may wait on its own stream, see there).  A batch B is accepted when
+ *    1 <= B <= 2^20 (else SNACK_ERR_UNSUPPORTED) and B is covered by the
+ *    layer's reserved workspace (else SNACK_ERR_WORKSPACE); a refused call
+ *    launches nothing and leaves the layer unchanged.
  *  - Canonical slot order: stored positions sorted by linear position
  *    row*K + col (row-major: by row, then column), as the sorted COO with a row
  *    pointer of the "Padded-CSR" post, section 3.2.  Values and dW are always
@@ -45,7 +52,8 @@ typedef enum snack_status {
     SNACK_ERR_DUPLICATE = 3,     /* two entries name the same position */
     SNACK_ERR_ALLOC = 4,         /* device allocation failed */
     SNACK_ERR_HIP = 5,           /* a HIP runtime or launch error */
-    SNACK_ERR_UNSUPPORTED = 6    /* sizes beyond the int32 index range */
+    SNACK_ERR_UNSUPPORTED = 6,   /* sizes beyond the int32 index range, or a batch above 2^20 */
+    SNACK_ERR_WORKSPACE = 7      /* the batch needs more workspace than is reserved (snack_layer_reserve) */
 } snack_status;
 
 typedef struct snack_layer snack_layer;
@@ -66,8 +74,10 @@ const char* snack_status_string(snack_status s);
  *   seed        keys the regrow candidate stream; the epoch starts at 0.
  * The layer copies the triple (the caller may free its buffers on return),
  * sorts it into canonical order, builds the row pointer, the transposed index
- * and its work partition, and synchronises `stream` once to report
- * SNACK_ERR_INDEX_RANGE / SNACK_ERR_DUPLICATE.  On error *out is set to NULL.
+ * and its work partition, reserves the per-batch workspace for every batch up
+ * to 64 (as snack_layer_reserve(layer, 64)), and synchronises `stream` once to
+ * report SNACK_ERR_INDEX_RANGE / SNACK_ERR_DUPLICATE.  On error *out is set to
+ * NULL.
  */
 snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz,
                                 const int32_t* rows, const int32_t* cols, const float* vals,
@@ -77,10 +87,15 @@ snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz,
 snack_status snack_layer_destroy(snack_layer* layer);
 
 /*
- * Pre-size the per-batch workspace (feature-major copies of X and dY, and the
- * partial sums of the batch-tiled passes) for every batch up to max_batch, so
- * that later forward/backward calls with B <= max_batch allocate nothing.  A
- * larger B grows the workspace on first use.
+ * Size the per-batch workspace (feature-major copies of X and dY, and the
+ * partial sums of the batch-tiled passes) for every batch up to max_batch
+ * (1 <= max_batch <= 2^20, else SNACK_ERR_INVALID_ARG / SNACK_ERR_UNSUPPORTED).
+ * The workspace never shrinks: a max_batch below the current reserve changes
+ * nothing.  Growing it allocates the new workspace, synchronises the device
+ * and frees the old one (SNACK_ERR_ALLOC when the allocation fails; the old
+ * reserve then stays as it was).
+ * Compute calls whose batch the reserve does not cover return
+ * SNACK_ERR_WORKSPACE.
  */
 snack_status snack_layer_reserve(snack_layer* layer, int32_t max_batch);
 
@@ -103,16 +118,14 @@ snack_status snack_forward(snack_layer* layer, const float* X, float* Y, int32_t
  *   dW  device float[nnz] in canonical slot order, 16-byte aligned, or NULL;
  *       overwritten (the caller accumulates if it wants to).  Stored zeros get
  *       a gradient.
- * When both dX and dW are requested and B <= 64, the layer also keeps dW in its
- * transposed order; a following snack_sgd_step with the same dW pointer then
- * updates both of the layer's value copies without a permutation gather.
  */
 snack_status snack_backward(snack_layer* layer, const float* X, const float* dY,
                             float* dX, float* dW, int32_t B, snack_stream stream);
 
 /*
- * Backward and the SGD step of the "Padded-CSR" post's section 7.3 training loop
- * (the values move against their gradient) in one call: the same results, bit
+ * Backward and the plain SGD step of the training loop in the "Padded-CSR"
+ * post's section 8.2 ("Try It": loss.backward() then opt.step() of
+ * torch.optim.SGD, i.e. each value moves against its gradient) in one call: the same results, bit
  * for bit, as snack_backward(layer, X, dY, dX, dW, B) followed by
  * snack_sgd_step(layer, dW, lr).  X, dY, dW are required (dW written as by
  * snack_backward; NULL only for a layer with no entries); dX may be NULL.  Where the column pass computes dW, it also
@@ -123,9 +136,12 @@ snack_status snack_backward_sgd(snack_layer* layer, const float* X, const float*
                                 float lr, int32_t B, snack_stream stream);
 
 /*
- * One iteration of the "Padded-CSR" post's section 7.3 training loop with the
- * mean-squared-error loss of its section 8 benchmarks, in one call: forward,
- * loss gradient, backward and SGD step.  The same results, bit for bit, as
+ * One iteration of the training loop in the "Padded-CSR" post's section 8.2
+ * ("Try It": forward, loss.backward(), opt.step() of plain SGD), in one call:
+ * forward, loss gradient, backward and SGD step.  The loss is the mean squared
+ * error against targets T; the pages' loop uses model(x).sum() instead, so the
+ * MSE is this library's choice for training benchmarks, not the pages'.  The
+ * same results, bit for bit, as
  *   snack_forward(layer, X, Y, B);
  *   snack_mse_grad(Y, T, dY, B * M, scale);
  *   snack_backward_sgd(layer, X, dY, dX, dW, lr, B);
@@ -195,7 +211,11 @@ snack_status snack_layer_set_epoch(snack_layer* layer, uint64_t epoch);
 
 /*
  * Training-loop helpers (elementwise fp32; not part of the sparse method).
- *   snack_sgd_step:  values[k] -= lr * dW[k]   (dW device float[nnz], canonical order)
+ *   snack_sgd_step:  values[k] -= lr * dW[k]   (dW device float[nnz], canonical order;
+ *                    dW may be any array, e.g. a gradient the caller clipped
+ *                    or scaled after snack_backward; the layer's column-ordered
+ *                    value copy is rebuilt from the stepped values before the
+ *                    next pass that reads it)
  *   snack_mse_grad:  dY[i] = scale * (Y[i] - T[i]), i < n   (MSE mean: scale = 2/n)
  *   snack_gelu_fwd:  Y = 0.5 X (1 + erf(X / sqrt 2))
  *   snack_gelu_bwd:  dX = dY * (Phi(X) + X phi(X))

@@ -37,10 +37,11 @@ def _sgd_close(got, v, g, lr, ulps=2):
     return np.abs(got - ref) <= ulps * spacing + 1e-30
 
 
-def _layer(M, K, sp, key, seed=1):
+def _layer(M, K, sp, key, seed=1, max_batch=None):
     L = lib()
     rows, cols, vals = random_layer(M, K, nnz_for(M, K, sp), key, weight_std(K, sp))
-    return L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=seed), (rows, cols, vals)
+    return (L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=seed, max_batch=max_batch),
+            (rows, cols, vals))
 
 
 def _export(layer):
@@ -137,7 +138,10 @@ def test_c4_10000_square_batch_sweep_with_drop_regrow():
     M = K = 10000
     batches = (1, 2, 4, 8, 16, 32, 64)
     lr, period, iters, seed = 0.01, 10, 20, 4242
-    checks = {1, 7, 10, 11, 14, 20}   # batches 1, 64, 4, 8, 64 (after a drop/regrow), 32
+    # every iteration of the first sweep (t = 1..7: batches 1, 2, 4, 8, 16, 32, 64), the last
+    # before the first drop/regrow (t = 10, batch 4), the first after it (t = 11, batch 8),
+    # batch 64 after it (t = 14) and the last before the second (t = 20, batch 32)
+    checks = {1, 2, 3, 4, 5, 6, 7, 10, 11, 14, 20}
     layer, _ = _layer(M, K, 95, "c4/layer", seed=seed)
     nnz = layer.nnz
     n_drop = nnz * 3 // 10
@@ -184,7 +188,8 @@ class _Stack:
         self.layers = []
         for b in range(blocks):
             for (M, K, name) in ((3072, 768, "fc"), (768, 3072, "proj")):
-                layer, _ = _layer(M, K, sp, f"c5/s{sp}/{b}/{name}", seed=seed0 + len(self.layers))
+                layer, _ = _layer(M, K, sp, f"c5/s{sp}/{b}/{name}", seed=seed0 + len(self.layers),
+                                  max_batch=1024)
                 self.layers.append(layer)
 
     def close(self):

@@ -24,7 +24,7 @@ def _check_layer_vs_oracle(M, K, nnz, batches, key, std=None, check_index=True, 
     rows, cols, vals = triple if triple is not None else _make(M, K, nnz, key, std)
     ref = oracle.canonicalize(M, K, rows, cols, vals)
     say("create", key, M, K, nnz)
-    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1, max_batch=max(batches))
     try:
         if check_index:
             r, c, v = layer.export()
@@ -141,7 +141,7 @@ def test_backward_dx_only_and_dw_only(M, K, nnz):
     key = f"gpu/partial/{M}x{K}"
     rows, cols, vals = _make(M, K, nnz, key)
     ref = oracle.canonicalize(M, K, rows, cols, vals)
-    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1, max_batch=65)
     try:
         for B in (1, 4, 16, 64, 65):
             X = normal((B, K), f"{key}/X/{B}")
@@ -275,3 +275,73 @@ def test_reserve_covers_every_batch_up_to_it():
             assert layer.device_bytes() == before, f"B={B} grew the workspace"
     finally:
         layer.close()
+
+
+def test_batch_beyond_reserve_is_refused_cleanly():
+    """Forward, backward and the fused training calls allocate nothing: a layer
+    reserves batches up to 64 at create, a larger batch is refused with
+    SNACK_ERR_WORKSPACE before anything is launched (outputs untouched, device
+    bytes unchanged), batches up to the reserve run, and after
+    snack_layer_reserve the larger batch runs too.  Batches above 2^20 are
+    refused as unsupported."""
+    import torch
+    L = lib()
+    M, K, nnz = 2000, 1500, 300000
+    rows, cols, vals = _make(M, K, nnz, "gpu/refuse", None)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=1)
+    try:
+        before = layer.device_bytes()
+        B = 600   # its feature-major copies alone (9 MB) exceed what batches up to 64 need here (2.4 MB)
+        X = dev(normal((B, K), "gpu/refuse/X"))
+        T = dev(normal((B, M), "gpu/refuse/T"))
+        dY = dev(normal((B, M), "gpu/refuse/dY"))
+        Y = torch.full((B, M), 7.0, device="cuda")
+        dX = torch.full((B, K), 7.0, device="cuda")
+        dW = torch.full((nnz,), 7.0, device="cuda")
+        v0 = host(layer.export()[2])
+        say("refuse: B", B, "beyond the default reserve")
+        calls = (
+            lambda: L.snack_forward(layer.h, X, Y),
+            lambda: L.snack_backward(layer.h, X, dY, dX, dW),
+            lambda: L.snack_backward(layer.h, X, dY, dX, None),
+            lambda: L.snack_backward_sgd(layer.h, X, dY, dX, dW, 0.01),
+            lambda: L.snack_train_step_mse(layer.h, X, T, Y, dY.clone(), dX, dW, 2.0 / (B * M), 0.01),
+        )
+        for f in calls:
+            with pytest.raises(L.SnackError) as e:
+                f()
+            assert e.value.code == L.ERR_WORKSPACE
+        torch.cuda.synchronize()
+        assert layer.device_bytes() == before
+        assert bool((Y == 7.0).all()) and bool((dX == 7.0).all()) and bool((dW == 7.0).all())
+        assert np.array_equal(host(layer.export()[2]).view(np.uint32), v0.view(np.uint32))
+        for b in (1, 2, 4, 8, 16, 32, 64):
+            say("refuse: B", b, "inside the default reserve")
+            Xb = dev(normal((b, K), f"gpu/refuse/X/{b}"))
+            Tb = dev(normal((b, M), f"gpu/refuse/T/{b}"))
+            layer.forward(Xb)
+            layer.train_step_mse(Xb, Tb, 0.0)
+        torch.cuda.synchronize()
+        assert layer.device_bytes() == before
+        layer.reserve(B)
+        assert layer.device_bytes() > before
+        say("refuse: B", B, "after reserve")
+        L.snack_forward(layer.h, X, Y)
+        Yr, Ya = oracle.forward(M, K, *(host(t) for t in layer.export()), host(X))
+        assert_close("Y after reserve", host(Y), Yr, Ya)
+        with pytest.raises(L.SnackError) as e:
+            layer.reserve(2 ** 20 + 1)
+        assert e.value.code == L.ERR_UNSUPPORTED
+    finally:
+        layer.close()
+    small = L.SnackLayer(3, 1, dev(np.array([0, 2], np.int32)), dev(np.array([0, 0], np.int32)),
+                         dev(np.array([1.0, 2.0], np.float32)))
+    try:
+        Xh = torch.zeros((2 ** 20 + 1, 1), device="cuda")
+        Yh = torch.zeros((2 ** 20 + 1, 3), device="cuda")
+        say("refuse: B above 2^20")
+        with pytest.raises(L.SnackError) as e:
+            L.snack_forward(small.h, Xh, Yh)
+        assert e.value.code == L.ERR_UNSUPPORTED
+    finally:
+        small.close()

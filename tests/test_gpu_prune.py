@@ -98,3 +98,58 @@ def test_batch_tiled_passes_after_drop_regrow(M, K):
             assert_close(f"dW B={B}", dW, *oracle.backward_dw(M, K, r, c, X, dY))
     finally:
         layer.close()
+
+
+@pytest.mark.parametrize("M,K,nnz", [(500, 500, 12500), (3000, 700, 105000)])
+def test_resume_from_export_continues_drop_regrow(M, K, nnz):
+    """Checkpoint / resume: export the triple after some drop/regrow epochs,
+    create a new layer from it with the same seed, set its epoch, and the next
+    drop/regrow calls give bit for bit what the uninterrupted layer gives (and
+    what the oracle gives at that epoch)."""
+    import torch
+    L = lib()
+    seed = 777
+    rows, cols, v = random_layer(M, K, nnz, f"gpu/resume/{M}x{K}")
+    n_drop = nnz * 3 // 10
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(v), seed=seed)
+    b = None
+    try:
+        for _ in range(2):
+            a.prune_regrow(n_drop)
+        assert a.epoch == 2
+        say("resume: checkpoint at epoch", a.epoch)
+        r, c, vv = a.export()
+        epoch = a.epoch
+        # the checkpoint crosses the host, as a saved state would
+        r, c, vv = (torch.from_numpy(host(t)).cuda() for t in (r, c, vv))
+        b = L.SnackLayer(M, K, r, c, vv, seed=seed)
+        b.epoch = epoch
+        cur = (host(r), host(c), host(vv))
+        for step in range(2):
+            say("resume: drop/regrow after resume", step)
+            a.prune_regrow(n_drop)
+            b.prune_regrow(n_drop)
+            ta = [host(t) for t in a.export()]
+            tb = [host(t) for t in b.export()]
+            assert np.array_equal(ta[0], tb[0]) and np.array_equal(ta[1], tb[1])
+            assert np.array_equal(ta[2].view(np.uint32), tb[2].view(np.uint32))
+            o = oracle.prune_regrow(M, K, cur[0], cur[1], cur[2], n_drop, seed, epoch + step)
+            assert np.array_equal(tb[0], o[0]) and np.array_equal(tb[1], o[1])
+            assert np.array_equal(tb[2].view(np.uint32), o[2].view(np.uint32))
+            assert a.epoch == b.epoch == epoch + step + 1
+            cur = o[:3]
+        # a fresh layer left at epoch 0 draws another stream: the epoch matters
+        c0 = L.SnackLayer(M, K, dev(cur[0]), dev(cur[1]), dev(cur[2]), seed=seed)
+        try:
+            c0.prune_regrow(n_drop)
+            o0 = oracle.prune_regrow(M, K, cur[0], cur[1], cur[2], n_drop, seed, 0)
+            r0 = host(c0.export()[0])
+            assert np.array_equal(r0, o0[0])
+            o4 = oracle.prune_regrow(M, K, cur[0], cur[1], cur[2], n_drop, seed, 4)
+            assert not (np.array_equal(o0[0], o4[0]) and np.array_equal(o0[1], o4[1]))
+        finally:
+            c0.close()
+    finally:
+        a.close()
+        if b is not None:
+            b.close()

@@ -33,7 +33,7 @@ def test_training_steps_teacher_forced(B):
     nnz = M * K * (100 - sp) // 100
     rows, cols, vals = random_layer(M, K, nnz, f"train/{B}", weight_std(K, sp))
     say("training create B", B)
-    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=77)
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), seed=77, max_batch=B)
     lr = 0.01
     Y = torch.empty(B, M, device="cuda"); dY = torch.empty(B, M, device="cuda")
     dX = torch.empty(B, K, device="cuda"); dW = torch.empty(nnz, device="cuda")
@@ -105,8 +105,8 @@ def test_backward_sgd_matches_backward_then_sgd(M, K, nnz):
     768 x 3072 layer's short keys take the fallback (no in-place step)."""
     L = lib()
     rows, cols, vals = random_layer(M, K, nnz, f"fused/{M}x{K}")
-    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
-    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=100)
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=100)
     lr = 0.01
     try:
         for B in (1, 2, 3, 4, 8, 16, 32, 64, 100):
@@ -147,8 +147,8 @@ def test_train_step_matches_separate_calls(M, K, nnz):
     import torch
     L = lib()
     rows, cols, vals = random_layer(M, K, nnz, f"tstep/{M}x{K}")
-    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
-    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=449)
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=449)
     lr = 0.01
     u32 = lambda t: host(t).view(np.uint32)
     try:
@@ -189,8 +189,8 @@ def test_train_step_small_and_degenerate_shapes(M, K, nnz):
     import torch
     L = lib()
     rows, cols, vals = random_layer(M, K, nnz, f"tstep-small/{M}x{K}")
-    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
-    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    a = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=65)
+    b = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals), max_batch=65)
     u32 = lambda t: host(t).view(np.uint32)
     try:
         for B in (1, 2, 3, 5, 8, 13, 33, 64, 65):
@@ -210,3 +210,38 @@ def test_train_step_small_and_degenerate_shapes(M, K, nnz):
     finally:
         a.close()
         b.close()
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_sgd_step_with_gradient_changed_in_place(B):
+    """A caller may change dW between snack_backward and snack_sgd_step
+    (clipping, scaling): the step uses the dW it is given, and the layer's
+    column-ordered value copy follows the canonical values exactly, so the next
+    backward's dX is the oracle's for the stepped values."""
+    import torch
+    L = lib()
+    M, K, nnz = 900, 700, 63000
+    rows, cols, vals = random_layer(M, K, nnz, f"inplace/{B}")
+    layer = L.SnackLayer(M, K, dev(rows), dev(cols), dev(vals))
+    lr = 0.01
+    try:
+        X = normal((B, K), f"inplace/X/{B}")
+        dY = normal((B, M), f"inplace/dY/{B}")
+        say("in-place dW B", B)
+        v0 = host(layer.export()[2])
+        dX, dW = layer.backward(dev(X), dev(dY))
+        dW.mul_(-3.0)   # the caller rescales the gradient in place
+        g = host(dW)
+        layer.sgd_step(dW, lr)
+        r, c, v1 = (host(t) for t in layer.export())
+        want = (v0.astype(np.float64) - np.float64(np.float32(lr)) * g.astype(np.float64))
+        assert _sgd_close(v1, v0, g, lr).all()
+        assert np.abs(v1 - want).max() <= 1e-6 * (1 + np.abs(want).max())
+        _, pm, _, _, vt = (host(t) for t in layer.export_index(with_values=True))
+        assert np.array_equal(vt.view(np.uint32), v1[pm].view(np.uint32))
+        # the next backward reads the column-ordered copy
+        dY2 = normal((B, M), f"inplace/dY2/{B}")
+        dX2, _ = layer.backward(dev(X), dev(dY2), want_dw=False)
+        assert_close(f"dX after in-place step B={B}", host(dX2), *oracle.backward_dx(M, K, r, c, v1, dY2))
+    finally:
+        layer.close()

@@ -251,6 +251,28 @@ def test_gelu_closed_forms_and_derivative():
     assert abs(d[2] - 0.5) < 1e-15                          # gelu'(0) = 1/2
 
 
+def test_gelu_pinned_to_normal_table_values():
+    # GELU(x) = x * Phi(x) with Phi the standard normal CDF, so its values at +-1
+    # and its slope at 1 are fixed by the normal table: Phi(1) = 0.8413447460685429,
+    # phi(1) = exp(-1/2) / sqrt(2 pi) = 0.24197072451914337.  A missing 1/sqrt(2)
+    # inside erf (x * (1 + erf(x)) / 2 gives 0.9213503964748575 at 1) or the tanh
+    # approximation (0.8411919906082768 at 1) fails these by far more than the
+    # tolerance.
+    phi1_cdf = 0.8413447460685429
+    phi1_pdf = 0.24197072451914337
+    x = np.array([1.0, -1.0, 2.0], np.float32)
+    g = oracle.gelu_fwd(x)
+    assert abs(g[0] - phi1_cdf) < 1e-15
+    assert abs(g[1] - (-(1.0 - phi1_cdf))) < 1e-15              # Phi(-1) = 1 - Phi(1)
+    assert abs(g[2] - 2.0 * 0.9772498680518208) < 1e-15         # Phi(2) from the table
+    d = oracle.gelu_bwd(x, np.ones_like(x))
+    assert abs(d[0] - (phi1_cdf + phi1_pdf)) < 1e-15            # Phi(1) + 1 * phi(1)
+    assert abs(d[1] - ((1.0 - phi1_cdf) - phi1_pdf)) < 1e-15    # Phi(-1) + (-1) * phi(-1)
+    # the chain rule: the incoming gradient scales the derivative
+    d2 = oracle.gelu_bwd(x[:1], np.array([-3.0], np.float32))
+    assert abs(d2[0] + 3.0 * (phi1_cdf + phi1_pdf)) < 1e-14
+
+
 def test_sgd_closed_form():
     v = np.array([1.0, -2.0, 0.5], np.float32); g = np.array([10.0, 0.0, -4.0], np.float32)
     assert oracle.sgd(v, g, 0.25).tolist() == [1.0 - 2.5, -2.0, 0.5 + 1.0]
