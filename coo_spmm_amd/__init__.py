@@ -38,6 +38,7 @@ _SIGS = {
     "snack_layer_destroy": ([P], ST),
     "snack_layer_reserve": ([P, i32], ST),
     "snack_forward": ([P, P, P, i32, P], ST),
+    "snack_forward_noalloc": ([P, P, P, i32, P], ST),
     "snack_backward": ([P, P, P, P, P, i32, P], ST),
     "snack_backward_sgd": ([P, P, P, P, P, f32, i32, P], ST),
     "snack_train_step_mse": ([P, P, P, P, P, P, P, f32, f32, i32, P], ST),
@@ -142,6 +143,11 @@ def snack_layer_reserve(h, max_batch):
 def snack_forward(h, X, Y, stream=None):
     B = X.shape[0]
     _check(_lib.snack_forward(h, _ptr(X), _ptr(Y), B, _stream(stream)), "snack_forward")
+
+
+def snack_forward_noalloc(h, X, Y, stream=None):
+    B = X.shape[0]
+    _check(_lib.snack_forward_noalloc(h, _ptr(X), _ptr(Y), B, _stream(stream)), "snack_forward_noalloc")
 
 
 def snack_backward(h, X, dY, dX=None, dW=None, stream=None):

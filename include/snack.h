@@ -109,6 +109,21 @@ snack_status snack_layer_reserve(snack_layer* layer, int32_t max_batch);
 snack_status snack_forward(snack_layer* layer, const float* X, float* Y, int32_t B, snack_stream stream);
 
 /*
+ * Forward for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * results, bit for bit, as snack_forward, with the scratch the forward needs
+ * (the feature-major copy of X and the slice partial sums of the batch-tiled
+ * pass) taken from one static device array of 48 MiB per device instead of
+ * the layer's workspace; the call never allocates and needs no
+ * snack_layer_reserve.  Plans needing more scratch than that array holds
+ * return SNACK_ERR_WORKSPACE (at 10000 x 10000 and 95 % the limit admits
+ * every batch up to 64).  The array is shared by every call on a device and
+ * holds the last call's contents: calls that overlap on one device (two
+ * streams, two threads) race and must be serialised by the caller.
+ */
+snack_status snack_forward_noalloc(snack_layer* layer, const float* X, float* Y, int32_t B, snack_stream stream);
+
+/*
  * Backward.  "Padded-CSR" section 7.1: dX = dY W (the SpMM with the transpose,
  * run over the cached transposed index of section 7.2) and dW restricted to the
  * stored positions, dW[k] = sum_b dY[b, r_k] X[b, c_k]; the SNACK paper's
