@@ -439,8 +439,40 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s)
     return canon_index_tail(L, s);
 }
 
+// 16-bit copies of a view's indices: four per thread, the padding past nnz zero
+__global__ void idx16_kernel(const int32_t* __restrict__ a, uint16_t* __restrict__ a16, const int32_t* __restrict__ b,
+                             uint16_t* __restrict__ b16, int64_t cap)
+{
+    const int64_t n4 = cap / 4;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += step) {
+        if (a16) {
+            const int4 v = reinterpret_cast<const int4*>(a)[q];
+            reinterpret_cast<uint2*>(a16)[q] = make_uint2((uint32_t)v.x | ((uint32_t)v.y << 16),
+                                                          (uint32_t)v.z | ((uint32_t)v.w << 16));
+        }
+        if (b16) {
+            const int4 v = reinterpret_cast<const int4*>(b)[q];
+            reinterpret_cast<uint2*>(b16)[q] = make_uint2((uint32_t)v.x | ((uint32_t)v.y << 16),
+                                                          (uint32_t)v.z | ((uint32_t)v.w << 16));
+        }
+    }
+}
+
+snack_status build_idx16(snack_layer* L, hipStream_t s)
+{
+    if (!L->fwd.idx16 && !L->tr.idx16) return SNACK_OK;
+    ProfScope prof(KC_CANON, s);
+    const int64_t n4 = L->cap / 4;
+    hipLaunchKernelGGL(idx16_kernel, dim3(grid_for(n4 < 4096 * 256 ? n4 : 4096 * 256)), dim3(kThreads), 0, s,
+                       L->fwd.idx, L->fwd.idx16, L->tr.idx, L->tr.idx16, L->cap);
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
 snack_status canon_index_tail(snack_layer* L, hipStream_t s)
 {
+    SNACK_CHECK(build_idx16(L, s));
     L->vals_t_stale = false;
     for (int i = 0; i < kTileWidths; ++i) {
         L->fwd.split[i].valid = false;

@@ -19,6 +19,7 @@ constexpr int kChunkTarget = 1024;     // chunks per view a layer is cut into at
 constexpr int kPad = 2048;             // slack elements after every nnz-sized array
 constexpr int32_t kMaxBatch = 1 << 20; // largest batch a call accepts
 constexpr int32_t kDefaultReserve = 64; // batches a layer's workspace covers from create on
+constexpr int32_t kIdx16Max = 65534;   // largest nidx whose indices (and the zero row past them) fit 16 bits
 
 // Kernel classes for the profiling hooks (order = snack_profile_name ids).
 enum KernelClass : int {
@@ -62,6 +63,7 @@ struct View {
     int32_t nkeys = 0;      // M (canonical) or K (transposed)
     int32_t nidx = 0;       // K (canonical) or M (transposed)
     int32_t* idx = nullptr;
+    uint16_t* idx16 = nullptr;      // the same indices in 16 bits, where nidx < 65535 (else null)
     float* vals = nullptr;
     int32_t* ptr = nullptr;         // [nkeys + 1]
     int32_t nchunks = 0;
@@ -197,6 +199,8 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s);
 snack_status canon_index_tail(snack_layer* L, hipStream_t s);
 // vals_t[iperm[k]] = vals[k]
 snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
+// the views' 16-bit index copies from their 32-bit indices (where allocated)
+snack_status build_idx16(snack_layer* L, hipStream_t s);
 // perm[iperm[k]] = k: the transposed slot -> canonical slot map, into a caller buffer
 snack_status invert_iperm(const snack_layer* L, int32_t* perm, hipStream_t s);
 

@@ -256,6 +256,9 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     L->tr.vals = L->vals_t;
     L->tr.ptr = L->col_ptr;
     L->tr.nchunks = (int32_t)(ncht < 1 ? 1 : ncht);
+    // 16-bit copies of the gathered indices for the narrow-batch streams (cap is a multiple of 4)
+    if (K <= kIdx16Max) ALLOC(fwd.idx16, uint16_t*, (size_t)L->cap * 2);
+    if (M <= kIdx16Max) ALLOC(tr.idx16, uint16_t*, (size_t)L->cap * 2);
     ALLOC(tr.desc, int2*, ((size_t)L->tr.nchunks + 1) * 8);
     ALLOC(tr.empty_keys, int32_t*, (size_t)K * 4);
     ALLOC(tr.n_empty, int32_t*, 4);

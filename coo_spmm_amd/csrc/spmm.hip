@@ -35,6 +35,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 namespace snack {
 namespace {
 
@@ -44,6 +46,7 @@ constexpr int kXcd = 8;
 
 struct RoleArgs {
     const int32_t* idx;
+    const uint16_t* idx16;   // the same indices in 16 bits, or null
     const float* vals;
     const int32_t* ptr;
     const int2* desc;
@@ -740,107 +743,6 @@ __device__ __forceinline__ void key_chunk(const RoleArgs& A, int c, const float*
 
 __device__ inline int32_t uni(int32_t v) { return (int32_t)__builtin_amdgcn_readfirstlane(v); }
 
-// Wave-uniform cursor over the keys of the chunks a wave claims from its
-// workgroup's LDS counter.  It holds the current key (r, entries [p0, p1)) and
-// the next one (nr, [np0, np1); nr < 0: none), and the descriptor of the
-// claimed chunk after the next key's.  A chunk whose first key equals the next
-// chunk's (inside a key longer than a chunk) holds no key and is skipped.
-struct KeyCursor {
-    const int32_t* ptr;
-    const int2* desc;
-    int* next_s;
-    int32_t nkeys, cend;
-    int32_t cn, pa_x, pa_y, pb_x;
-    int32_t r, ke, p0, p1;
-    int32_t nr, nke, np0, np1;
-
-    __device__ inline int32_t claim() const
-    {
-        int c = 0;
-        if ((threadIdx.x & (kWave - 1)) == 0) c = atomicAdd(next_s, 1);
-        return uni(c);
-    }
-    __device__ inline int32_t ptr_at(int32_t i) const
-    {
-        return uni(ptr[uni(i < 0 ? 0 : (i < nkeys ? i : nkeys))]);
-    }
-    __device__ inline void load_desc()
-    {
-        const int32_t cc = uni(cn < cend ? cn : cend - 1);
-        pa_x = uni(desc[cc].x);
-        pa_y = uni(desc[cc].y);
-        pb_x = uni(desc[cc + 1].x);
-    }
-    // the first key of the next non-empty claimed chunk into (nr, np0, nke)
-    __device__ inline void pull()
-    {
-        for (;;) {
-            if (uni(cn) >= cend) {
-                nr = -1;
-                return;
-            }
-            const int32_t ax = pa_x, ay = pa_y, bx = pb_x;
-            cn = claim();
-            load_desc();
-            if (uni(ax) < uni(bx)) {
-                nr = uni(ax);
-                np0 = uni(ay);
-                nke = uni(bx);
-                return;
-            }
-        }
-    }
-    __device__ inline void set_next()
-    {
-        if (uni(r + 1) < uni(ke)) {
-            nr = uni(r + 1);
-            np0 = uni(p1);
-            nke = uni(ke);
-        } else {
-            pull();
-        }
-        np1 = ptr_at(nr + 1);
-    }
-    // false when the wave has no key at all (the current key is then the
-    // empty key 0, so loads for it stay in bounds)
-    __device__ inline bool start()
-    {
-        r = 0;
-        ke = 0;
-        p0 = 0;
-        p1 = 0;
-        nr = -1;
-        cn = claim();
-        if (uni(cn) >= cend) return false;
-        load_desc();
-        pull();
-        if (uni(nr) < 0) return false;
-        r = nr;
-        ke = nke;
-        p0 = np0;
-        p1 = ptr_at(nr + 1);
-        set_next();
-        return true;
-    }
-    // false when the current key was the last
-    __device__ inline bool advance()
-    {
-        if (uni(nr) < 0) return false;
-        r = uni(nr);
-        ke = uni(nke);
-        p0 = uni(np0);
-        p1 = uni(np1);
-        set_next();
-        return true;
-    }
-};
-
-// The keys of every chunk a wave claims, walked as one stream: while a key's
-// last block is processed, the next key's first block (possibly in the next
-// claimed chunk) and its dW operand are already in flight.  Key bookkeeping is
-// wave-uniform and kept in scalar registers, so its loads go through the
-// scalar cache and never make the vector loads in flight wait.  `stage` runs
-// on every thread once the first block is in flight (it may hold a barrier).
 // a key's dW operand: NB batch columns from bcol of row key of a feature-major
 // [n][bp] array, or (RM) of column key of a batch-major [B][nkeys] array, the
 // columns past B read as zero as in the padded feature-major copy
@@ -863,68 +765,6 @@ __device__ inline void load_h(const float* __restrict__ H, int64_t key, int bp, 
     }
 }
 
-template <int BT, int NB, int U, bool DW, bool SPMM, bool RM, bool VAL, class Stage>
-__device__ __forceinline__ void key_stream(const RoleArgs& A, int* next_s, int cend, const float* __restrict__ Gm,
-                                           int bp, int B, Stage&& stage)
-{
-    using KB = KeyBlock<BT, NB, U>;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane / BT;
-    const int bl = lane - g * BT;
-    const int bcol = bl * NB;
-    KeyCursor kc;
-    kc.ptr = A.ptr;
-    kc.desc = A.desc;
-    kc.next_s = next_s;
-    kc.nkeys = A.nkeys;
-    kc.cend = cend;
-    const bool any = kc.start();
-    float acc[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
-    // the block in flight and the dW operand of its key
-    KB blk;
-    float h[NB], hn[NB], tg[NB];
-    blk.template load<SPMM || VAL>(A.idx, A.vals, kc.p0, kc.p1, lane, g);
-    if constexpr (DW) load_h<NB, RM>(A.H, kc.r, bp, bcol, B, A.nkeys, hn);
-    if constexpr (SPMM) key_targets<NB>(A, bcol, B, kc.r, tg);
-    stage();
-    if (!any) return;
-    int32_t base = kc.p0;
-    for (;;) {
-        int32_t ii[U];
-        float vv[U];
-        blk.take(ii, vv, g);
-        if constexpr (DW) {
-#pragma unroll
-            for (int n = 0; n < NB; ++n) h[n] = hn[n];
-        }
-        const int32_t p1 = kc.p1;
-        const bool last = uni(base + KB::STEP >= p1 ? 1 : 0) != 0;
-        const int32_t nbase = last ? kc.np0 : base + KB::STEP;
-        const int32_t nlim = last ? kc.np1 : p1;
-        const int32_t nkey = last ? (kc.nr < 0 ? kc.r : kc.nr) : kc.r;
-        if constexpr (DW) load_h<NB, RM>(A.H, nkey, bp, bcol, B, A.nkeys, hn);
-        blk.template load<SPMM || VAL>(A.idx, A.vals, nbase, nlim, lane, g);
-        float y[U][NB];
-        key_gather<NB, U>(Gm, ii, bp, bcol, y);
-        if constexpr (SPMM) key_accumulate<BT, NB, U>(vv, y, base, p1, g, acc);
-        if constexpr (DW) key_dw<BT, NB, U>(y, h, base, p1, g, bl, A.dwo, vv, A.apply, A.lr);
-        if (!last) {
-            base += KB::STEP;
-            continue;
-        }
-        if constexpr (SPMM) {
-            key_store<BT, NB>(acc, g, bcol, B, A.nkeys, kc.r, A.out, A, tg);
-#pragma unroll
-            for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
-        }
-        if (!kc.advance()) break;
-        if constexpr (SPMM) key_targets<NB>(A, bcol, B, kc.r, tg);
-        base = kc.p0;
-    }
-}
-
 template <int BT, int NB, int U, bool DW, bool SPMM = true, bool VAL = SPMM>
 __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
 {
@@ -936,94 +776,8 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
     key_chunk<BT, NB, U, DW, SPMM, VAL>(A, c, A.G, bp, B);
 }
 
-// The same walk with the gathered operand [nidx, bp] staged in LDS: gathers
-// become LDS reads, which random indices serve far faster than the vector
-// cache, whose lines the streamed index evicts.  Staging costs one copy of the
-// operand per workgroup, so workgroups are persistent: workgroup i takes an
-// even, contiguous share of the chunks (shares of one XCD adjacent) and its
-// wavefronts stream the keys of the chunks they claim from an LDS counter.
+// workgroup size of the streamed kernel (batch tiles 1-4, operand in LDS)
 constexpr int kLdsKeyWaves = 16;
-constexpr int kLdsU = 4;   // entries per lane per step
-
-template <int BT, int NB, int U, bool DW, bool SPMM = true, bool RM = false, bool VAL = SPMM>
-__global__ void __launch_bounds__(kLdsKeyWaves * kWave) key_lds_kernel(RoleArgs A, int bp, int B)
-{
-    extern __shared__ __align__(16) float gs_dyn[];
-    __shared__ int next_s;
-    const int nwg = (int)gridDim.x;
-    const int bid = (int)blockIdx.x;
-    const int per = nwg / kXcd;   // the grid is a multiple of kXcd
-    const int vb = (bid % kXcd) * per + bid / kXcd;
-    const int c0 = (int)(((int64_t)A.nchunks * vb) / nwg);
-    const int c1 = (int)(((int64_t)A.nchunks * (vb + 1)) / nwg);
-    if (threadIdx.x == 0) next_s = c0;
-    __syncthreads();
-    // the operand is staged while every wave's first block is in flight
-    auto stage = [&]() {
-        constexpr int NT = kLdsKeyWaves * kWave;
-        if constexpr (RM) {
-            // batch-major [B][nidx] source: a thread loads 16 bytes of every
-            // batch row at four consecutive features and writes the four LDS
-            // rows they make (a 4 x NB transpose in registers); columns past B
-            // are zero, as in the padded feature-major copy
-            static_assert(BT == 1, "one lane per batch tile");
-            const int n = A.nidx;
-            const bool vec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(A.G) & 15) == 0;
-            const int n4 = vec ? n / 4 : 0;
-            constexpr int SB = 2;
-            for (int q0 = threadIdx.x; q0 < n4; q0 += SB * NT) {
-                float4 v[SB][NB];
-#pragma unroll
-                for (int k = 0; k < SB; ++k) {
-                    const int q = q0 + k * NT;
-                    const int qc = q < n4 ? q : n4 - 1;
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        v[k][b] = reinterpret_cast<const float4*>(A.G + (int64_t)(b < B ? b : B - 1) * n)[qc];
-                }
-#pragma unroll
-                for (int k = 0; k < SB; ++k) {
-                    const int q = q0 + k * NT;
-                    const int qc = q < n4 ? q : n4 - 1;
-                    float* d = gs_dyn + qc * 4 * NB;
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        if (b >= B) v[k][b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    }
-                    if constexpr (NB == 4) {
-                        reinterpret_cast<float4*>(d)[0] = make_float4(v[k][0].x, v[k][1].x, v[k][2].x, v[k][3].x);
-                        reinterpret_cast<float4*>(d)[1] = make_float4(v[k][0].y, v[k][1].y, v[k][2].y, v[k][3].y);
-                        reinterpret_cast<float4*>(d)[2] = make_float4(v[k][0].z, v[k][1].z, v[k][2].z, v[k][3].z);
-                        reinterpret_cast<float4*>(d)[3] = make_float4(v[k][0].w, v[k][1].w, v[k][2].w, v[k][3].w);
-                    } else if constexpr (NB == 2) {
-                        reinterpret_cast<float4*>(d)[0] = make_float4(v[k][0].x, v[k][1].x, v[k][0].y, v[k][1].y);
-                        reinterpret_cast<float4*>(d)[1] = make_float4(v[k][0].z, v[k][1].z, v[k][0].w, v[k][1].w);
-                    } else {
-                        *reinterpret_cast<float4*>(d) = v[k][0];
-                    }
-                }
-            }
-            for (int q = n4 * 4 * B + threadIdx.x; q < n * B; q += NT) {   // rows not in 16-byte units
-                const int b = q / n;
-                const int i = q - b * n;
-                gs_dyn[i * NB + b] = A.G[q];
-            }
-            for (int q = threadIdx.x; q < n * (NB - B); q += NT) {          // zero columns
-                const int b = B + q / n;
-                const int i = q - (b - B) * n;
-                gs_dyn[i * NB + b] = 0.0f;
-            }
-        } else {
-            const int64_t n = (int64_t)A.nidx * bp;
-            const int64_t n4 = ((reinterpret_cast<uintptr_t>(A.G) & 15) == 0) ? n / 4 : 0;
-            for (int64_t i = threadIdx.x; i < n4; i += NT)
-                reinterpret_cast<float4*>(gs_dyn)[i] = reinterpret_cast<const float4*>(A.G)[i];
-            for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += NT) gs_dyn[i] = A.G[i];
-        }
-        __syncthreads();
-    };
-    key_stream<BT, NB, U, DW, SPMM, RM, VAL>(A, &next_s, c1, gs_dyn, bp, B, stage);
-}
 
 // ---- slice-tiled key-major kernel (batch tiles of 16 to 64 columns) --------
 // A wide batch makes every entry gather a long operand row (256 bytes at 64
@@ -1520,6 +1274,356 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     }
 }
 
+// ---- streamed kernel for batch tiles of 1 to 4 columns, operand in LDS ----
+// At narrow batches every pass is a stream of the view's index and values (8
+// bytes per entry) with a handful of instructions per entry, so what bounds it
+// is how many bytes each wavefront keeps in flight.  Each lane owns four
+// consecutive entries of a 256-entry block (one 16-byte load each for indices
+// and values, every block one coalesced kilobyte per array), and a wavefront
+// keeps D blocks in flight in a ring of statically indexed registers while it
+// works on the oldest.  Blocks never cross a key: a key's blocks start at its
+// first entry rounded down to four, so a block's lanes mask the entries
+// outside the key (value 0 on an all-zero LDS row past the operand: a masked
+// entry adds exactly 0 whatever the activations hold).  A lane owns every
+// batch column of its entries, so the dW of an entry is one fused multiply-add
+// chain over the columns in order -- the same arithmetic as every other
+// one-lane-per-tile kernel here, so the row and column views give bit-identical
+// dW.  Key sums are added over the wavefront by a fixed tree when the key's
+// last block is done and stored once: no atomics, bit-reproducible.  The
+// grid is persistent (every workgroup stages the operand once); wavefront w of
+// W takes the keys [nkeys w / W, nkeys (w+1) / W), whose pointer it reads as a
+// window across its lanes, so every block address follows from registers
+// (supports drawn uniformly give every key about the same length, hence every
+// wavefront about the same work).  The operand's staging loads, and then the
+// first D blocks, are issued before anything waits on them.
+constexpr int kStreamBlock = 256;   // entries per block: 4 per lane
+
+// one block: the entries [base, base + 256) of key r that lie in [lo, hi);
+// flags bit 0: the key's first block, bit 1: its last.  hi < lo: no block
+// (an exhausted cursor), which touches nothing.  All fields wave-uniform.
+struct StreamDesc {
+    int32_t base, lo, hi, r, flags;
+    __device__ inline bool valid() const { return hi >= lo; }
+};
+
+// A wavefront's keys [ra, rb), walked block by block.  The key pointer of up
+// to 64 keys at a time sits in a register across the lanes (lane j holds
+// ptr[wb + j]), so producing the next block needs no memory access except a
+// reload after every 63 keys.
+struct StreamCursor {
+    const int32_t* ptr;
+    int32_t nkeys;
+    int32_t rb;          // end of the wavefront's keys
+    int32_t wb, j;       // window base key, current key wb + j
+    int32_t win;         // this lane's ptr[min(wb + lane, nkeys)]
+    int32_t p0, p1, base;
+    bool done;
+
+    __device__ inline void load_window(int lane)
+    {
+        const int32_t k = wb + lane;
+        win = ptr[k < nkeys ? k : nkeys];
+    }
+    __device__ inline void start(int32_t ra, int32_t rend, int lane)
+    {
+        rb = rend;
+        wb = ra;
+        j = 0;
+        done = ra >= rend;
+        load_window(lane);
+        p0 = uni(__builtin_amdgcn_readlane(win, 0));
+        p1 = uni(__builtin_amdgcn_readlane(win, 1));
+        base = p0 & ~3;
+    }
+    __device__ inline void next(StreamDesc& d, int lane)
+    {
+        if (done) {
+            d.base = 0;
+            d.lo = 1;
+            d.hi = 0;
+            d.r = 0;
+            d.flags = 0;
+            return;
+        }
+        d.base = base;
+        d.lo = p0;
+        d.hi = p1;
+        d.r = wb + j;
+        int f = base == (p0 & ~3) ? 1 : 0;
+        if (base + kStreamBlock >= p1) {
+            f |= 2;
+            if (wb + j + 1 >= rb) {
+                done = true;
+            } else {
+                ++j;
+                if (j == kWave - 1) {
+                    wb += kWave - 1;
+                    j = 0;
+                    load_window(lane);
+                }
+                p0 = p1;
+                p1 = uni(__builtin_amdgcn_readlane(win, j + 1));
+                base = p0 & ~3;
+            }
+        } else {
+            base += kStreamBlock;
+        }
+        d.flags = f;
+    }
+};
+
+// x summed over the 64 lanes of the wavefront by a fixed tree (every lane ends
+// with the total)
+__device__ inline float wave_sum(float x)
+{
+    x += lane_xor<1>(x);
+    x += lane_xor<2>(x);
+    x += lane_xor<4>(x);
+    x += lane_xor<8>(x);
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+template <int NB>
+__device__ inline void lds_row(const float* __restrict__ g, int32_t i, float (&y)[NB])
+{
+    if constexpr (NB == 4) {
+        const float4 a = reinterpret_cast<const float4*>(g)[i];
+        y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
+    } else if constexpr (NB == 2) {
+        const float2 a = reinterpret_cast<const float2*>(g)[i];
+        y[0] = a.x; y[1] = a.y;
+    } else {
+        y[0] = g[i];
+    }
+}
+
+// The operand [nidx][NB] (feature-major, the row of feature i at i * NB) staged
+// into LDS by the streamed kernel's 1024 threads: load() issues every load of a
+// thread's share (at most 10 rows of 16 bytes: LDS holds at most 160 KB), and
+// store() writes them.  With RM the source is the caller's batch-major
+// [B][nidx] array, read as 16-byte runs of four features per batch row and
+// transposed in registers; batch columns past B are zero, as in the padded
+// feature-major copy.  Sources that are not 16-byte aligned or whose rows are
+// not a multiple of four floats take a plain loop in store().
+template <int NB, bool RM>
+struct StreamStage {
+    static constexpr int NT = kLdsKeyWaves * kWave;
+    static constexpr int QU = RM ? (10 + NB - 1) / NB : 10;   // 16-byte loads per batch row and thread
+    float4 v[QU][RM ? NB : 1];
+    bool vec;
+
+    __device__ inline void load(const float* __restrict__ G, int nidx, int B)
+    {
+        const int tid = threadIdx.x;
+        if constexpr (RM) {
+            vec = (nidx % 4) == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
+            const int n4 = vec ? nidx / 4 : 0;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                const int q = tid + u * NT;
+                const int qc = q < n4 ? q : (n4 > 0 ? n4 - 1 : 0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    v[u][b] = n4 > 0 ? reinterpret_cast<const float4*>(G + (int64_t)(b < B ? b : B - 1) * nidx)[qc]
+                                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        } else {
+            const int n = nidx * NB;
+            vec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
+            const int n4 = vec ? n / 4 : 0;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                const int q = tid + u * NT;
+                const int qc = q < n4 ? q : (n4 > 0 ? n4 - 1 : 0);
+                v[u][0] = n4 > 0 ? reinterpret_cast<const float4*>(G)[qc] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+    }
+    __device__ inline void store(float* gs, const float* __restrict__ G, int nidx, int B)
+    {
+        const int tid = threadIdx.x;
+        if (!vec) {
+            // unaligned or ragged source: element by element
+            for (int q = tid; q < nidx * NB; q += NT) {
+                const int i = q / NB;
+                const int b = q - i * NB;
+                gs[q] = RM ? (b < B ? G[(int64_t)b * nidx + i] : 0.0f) : G[q];
+            }
+            return;
+        }
+        if constexpr (RM) {
+            const int n4 = nidx / 4;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                const int q = tid + u * NT;
+                if (q >= n4) break;
+                float4 w[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) w[b] = b < B ? v[u][b] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                float4* d = reinterpret_cast<float4*>(gs + q * 4 * NB);
+                if constexpr (NB == 4) {
+                    d[0] = make_float4(w[0].x, w[1].x, w[2].x, w[3].x);
+                    d[1] = make_float4(w[0].y, w[1].y, w[2].y, w[3].y);
+                    d[2] = make_float4(w[0].z, w[1].z, w[2].z, w[3].z);
+                    d[3] = make_float4(w[0].w, w[1].w, w[2].w, w[3].w);
+                } else if constexpr (NB == 2) {
+                    d[0] = make_float4(w[0].x, w[1].x, w[0].y, w[1].y);
+                    d[1] = make_float4(w[0].z, w[1].z, w[0].w, w[1].w);
+                } else {
+                    d[0] = w[0];
+                }
+            }
+        } else {
+            const int n4 = nidx * NB / 4;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                const int q = tid + u * NT;
+                if (q >= n4) break;
+                reinterpret_cast<float4*>(gs)[q] = v[u][0];
+            }
+        }
+    }
+};
+
+template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16>
+__global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleArgs A, int bp, int B)
+{
+    static_assert(NB == 1 || NB == 2 || NB == 4, "one to four columns per lane");
+    extern __shared__ __align__(16) float gs_dyn[];
+    const int nwg = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    const int per = nwg / kXcd;   // the grid is a multiple of kXcd
+    const int vb = (bid % kXcd) * per + bid / kXcd;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = uni((int)(threadIdx.x / kWave));
+    const int nidx = A.nidx;
+    const int nkeys = A.nkeys;
+    constexpr bool LV = SPMM || VAL;
+
+    // wavefront gw of the grid takes an even share of the keys (workgroups of
+    // one XCD adjacent shares)
+    StreamCursor cur;
+    cur.ptr = A.ptr;
+    cur.nkeys = nkeys;
+    {
+        const int64_t nw = (int64_t)nwg * kLdsKeyWaves;
+        const int64_t gw = (int64_t)vb * kLdsKeyWaves + wv;
+        cur.start((int32_t)(nkeys * gw / nw), (int32_t)(nkeys * (gw + 1) / nw), lane);
+    }
+
+    // the ring: D blocks in flight (indices, values, the key's dW operand and
+    // the MSE target of the lane's column), refilled as each is consumed
+    StreamDesc d[D];
+    int4 bi[D];
+    float4 bv[D];
+    float hb[D][NB];
+    float tq[D];
+    const int tcol = lane < B ? lane : B - 1;   // the column whose output this lane would store
+    auto issue = [&](int q) {
+        cur.next(d[q], lane);
+        const int32_t o = d[q].base + 4 * lane;
+        if constexpr (I16) {
+            // four 16-bit indices in 8 bytes: the index stream at half the bytes
+            const uint2 u = *reinterpret_cast<const uint2*>(A.idx16 + o);
+            bi[q] = make_int4((int)(u.x & 0xffffu), (int)(u.x >> 16), (int)(u.y & 0xffffu), (int)(u.y >> 16));
+        } else {
+            bi[q] = *reinterpret_cast<const int4*>(A.idx + o);
+        }
+        if constexpr (LV) bv[q] = *reinterpret_cast<const float4*>(A.vals + o);
+        if constexpr (DW) load_h<NB, RM>(A.H, d[q].r, bp, 0, B, nkeys, hb[q]);
+        if constexpr (SPMM) tq[q] = A.tgt[(int64_t)tcol * nkeys + d[q].r];
+    };
+
+    // stage the operand (and the zero row after it): every load of this
+    // thread's share is issued at once, then the ring's first blocks, then the
+    // staged values are stored -- so the staging and the first blocks share one
+    // memory latency
+    StreamStage<NB, RM> st;
+    st.load(A.G, nidx, B);
+#pragma unroll
+    for (int q = 0; q < D; ++q) issue(q);
+    st.store(gs_dyn, A.G, nidx, B);
+    if (threadIdx.x < NB) gs_dyn[nidx * NB + threadIdx.x] = 0.0f;
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+    for (;;) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            const StreamDesc dq = d[q];
+            const int32_t k0 = dq.base + 4 * lane;
+            const int32_t ii[4] = {bi[q].x, bi[q].y, bi[q].z, bi[q].w};
+            const float vv[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+            bool in[4];
+            float y[4][NB];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                in[t] = k0 + t >= dq.lo && k0 + t < dq.hi;
+                lds_row<NB>(gs_dyn, in[t] ? ii[t] : nidx, y[t]);
+            }
+            if constexpr (SPMM) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float v = in[t] ? vv[t] : 0.0f;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = fmaf(v, y[t][n], acc[n]);
+                }
+            }
+            if constexpr (DW) {
+                float g[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) a = fmaf(y[t][n], hb[q][n], a);
+                    g[t] = a;
+                }
+                float* __restrict__ dwo = A.dwo;
+                float* __restrict__ apply = A.apply;
+                if (in[0] && in[3]) {
+                    if (dwo) *reinterpret_cast<float4*>(dwo + k0) = make_float4(g[0], g[1], g[2], g[3]);
+                    if (apply)
+                        *reinterpret_cast<float4*>(apply + k0) =
+                            make_float4(sgd_value(vv[0], g[0], A.lr), sgd_value(vv[1], g[1], A.lr),
+                                        sgd_value(vv[2], g[2], A.lr), sgd_value(vv[3], g[3], A.lr));
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (in[t]) {
+                            if (dwo) dwo[k0 + t] = g[t];
+                            if (apply) apply[k0 + t] = sgd_value(vv[t], g[t], A.lr);
+                        }
+                    }
+                }
+            }
+            if constexpr (SPMM) {
+                if (dq.flags & 2) {
+                    // the key's sums over the wavefront; lane b stores column b
+                    float s[NB];
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) s[n] = wave_sum(acc[n]);
+                    float sv = s[0];
+#pragma unroll
+                    for (int n = 1; n < NB; ++n) sv = lane == n ? s[n] : sv;
+                    if (lane < NB && lane < B) {
+                        const int64_t o = (int64_t)lane * nkeys + dq.r;
+                        A.out[o] = sv;
+                        if (A.dyo) A.dyo[o] = A.mse_scale * (sv - tq[q]);
+                    }
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc[n] = 0.0f;
+                }
+            }
+            issue(q);
+        }
+        if (!d[0].valid()) break;
+    }
+}
+
 // out[b, r] = sum over slices s = 0, 1, ... of part[s][r][b], in that order
 template <int BTILE>
 constexpr int kSplitReduceKeys = 1024 / BTILE;   // keys per workgroup of split_reduce_kernel
@@ -1898,6 +2002,7 @@ RoleArgs role_for(const View& v, const float* G, const float* H, float* out, flo
     RoleArgs a;
     a.cap = cap;
     a.idx = v.idx;
+    a.idx16 = v.idx16;
     a.vals = v.vals;
     a.ptr = v.ptr;
     a.desc = v.desc;
@@ -1987,12 +2092,32 @@ inline bool use_keyed(const View& v, int64_t nnz, const BatchPlan& p)
     return p.btile >= 1 && v.nkeys > 0 && nnz / v.nkeys >= 128;
 }
 
-// the key-major kernel with the whole gathered operand in LDS applies
+// LDS of the streamed kernel: the operand and one zero row
+inline size_t stream_lds_bytes(const View& v, const BatchPlan& p)
+{
+    return ((size_t)v.nidx + 1) * p.bp * sizeof(float);
+}
+
+// the streamed kernel with the whole gathered operand in LDS applies
 inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
 {
     return p.btile <= 4 && p.ntiles == 1 && L->cus > 0 && v.nchunks > 0 && use_keyed(v, L->nnz, p) &&
-           (size_t)v.nidx * p.bp * sizeof(float) <= (size_t)L->lds_bytes;
+           stream_lds_bytes(v, p) <= (size_t)L->lds_bytes;
 }
+
+// blocks in flight per wavefront of the streamed kernel (registers allow more
+// at narrower tiles)
+#ifndef SNACK_STREAM_D1
+#define SNACK_STREAM_D1 8
+#endif
+#ifndef SNACK_STREAM_D2
+#define SNACK_STREAM_D2 6
+#endif
+#ifndef SNACK_STREAM_D4
+#define SNACK_STREAM_D4 4
+#endif
+template <int NB>
+constexpr int kStreamDepthFor = NB == 4 ? SNACK_STREAM_D4 : (NB == 2 ? SNACK_STREAM_D2 : SNACK_STREAM_D1);
 
 // rm: G and H are batch-major [B][n] (the caller's arrays); only the LDS
 // kernel takes them, transposing G while it stages it
@@ -2016,29 +2141,35 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
         a.mse_scale = mse->scale;
         mse->done = true;
     }
-    const size_t lds = (size_t)v.nidx * p.bp * sizeof(float);
+    const size_t lds = stream_lds_bytes(v, p);
     if (p.btile <= 4 && p.ntiles == 1 && lds <= (size_t)L->lds_bytes && L->cus > 0 && v.nchunks > 0) {
-        // operand resident in LDS: one or two persistent workgroups per CU
-        int nwg = L->cus * (2 * lds <= (size_t)L->lds_bytes ? 2 : 1);
-        const int want = (v.nchunks + 1) / 2;
-        if (nwg > want) nwg = want;
-        nwg = (nwg + kXcd - 1) / kXcd * kXcd;
-        const dim3 grid((unsigned)nwg), block(kLdsKeyWaves * kWave);
-        if (rm) {
+        // operand resident in LDS: persistent workgroups, as many per CU as stay
+        // resident together (at most two), each wavefront an even share of the keys
+        const dim3 block(kLdsKeyWaves * kWave);
+        auto go = [&](auto kern) {
+            int occ = 1;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, (int)block.x, lds) != hipSuccess || occ < 1)
+                occ = 1;
+            int nwg = L->cus * (occ > 2 ? 2 : occ);
+            const int want = (v.nkeys + kLdsKeyWaves - 1) / kLdsKeyWaves;   // no workgroup without keys
+            if (nwg > want) nwg = want;
+            nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+            hipLaunchKernelGGL(kern, dim3((unsigned)nwg), block, lds, s, a, p.bp, B);
+        };
+        auto pick = [&](auto rmc, auto i16c) {
+            constexpr bool R = decltype(rmc)::value, I = decltype(i16c)::value;
             switch (p.btile) {
-            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
-            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
-            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, true, LV>), grid, block, lds, s, a, p.bp, B); break;
-            default: return SNACK_ERR_INVALID_ARG;
+            case 1: go(stream_lds_kernel<1, kStreamDepthFor<1>, DW, SPMM, R, LV, I>); return true;
+            case 2: go(stream_lds_kernel<2, kStreamDepthFor<2>, DW, SPMM, R, LV, I>); return true;
+            case 4: go(stream_lds_kernel<4, kStreamDepthFor<4>, DW, SPMM, R, LV, I>); return true;
+            default: return false;
             }
-        } else {
-            switch (p.btile) {
-            case 1: hipLaunchKernelGGL((key_lds_kernel<1, 1, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
-            case 2: hipLaunchKernelGGL((key_lds_kernel<1, 2, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
-            case 4: hipLaunchKernelGGL((key_lds_kernel<1, 4, kLdsU, DW, SPMM, false, LV>), grid, block, lds, s, a, p.bp, B); break;
-            default: return SNACK_ERR_INVALID_ARG;
-            }
-        }
+        };
+        using T = std::true_type;
+        using F = std::false_type;
+        const bool i16 = v.idx16 != nullptr;
+        const bool ok = rm ? (i16 ? pick(T{}, T{}) : pick(T{}, F{})) : (i16 ? pick(F{}, T{}) : pick(F{}, F{}));
+        if (!ok) return SNACK_ERR_INVALID_ARG;
         SNACK_HIP(hipGetLastError());
         return SNACK_OK;
     }
