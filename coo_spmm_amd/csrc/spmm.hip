@@ -1355,14 +1355,20 @@ struct StreamCursor {
             if (wb + j + 1 >= rb) {
                 done = true;
             } else {
-                ++j;
-                if (j == kWave - 1) {
+                // the reloaded window is read inside its own branch, so the wait
+                // for that load stays there and the common path waits on nothing
+                int32_t np1;
+                if (j + 1 == kWave - 1) {
                     wb += kWave - 1;
                     j = 0;
                     load_window(lane);
+                    np1 = uni(__builtin_amdgcn_readlane(win, 1));
+                } else {
+                    ++j;
+                    np1 = uni(__builtin_amdgcn_readlane(win, j + 1));
                 }
                 p0 = p1;
-                p1 = uni(__builtin_amdgcn_readlane(win, j + 1));
+                p1 = np1;
                 base = p0 & ~3;
             }
         } else {
@@ -1487,15 +1493,12 @@ struct StreamStage {
     }
 };
 
+// One role of the streamed kernel on workgroup vb of the nwg that take it.
 template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16>
-__global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleArgs A, int bp, int B)
+__device__ __forceinline__ void stream_role(const RoleArgs& A, int bp, int B, int vb, int nwg)
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one to four columns per lane");
     extern __shared__ __align__(16) float gs_dyn[];
-    const int nwg = (int)gridDim.x;
-    const int bid = (int)blockIdx.x;
-    const int per = nwg / kXcd;   // the grid is a multiple of kXcd
-    const int vb = (bid % kXcd) * per + bid / kXcd;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = uni((int)(threadIdx.x / kWave));
     const int nidx = A.nidx;
@@ -1520,7 +1523,9 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleAr
     float4 bv[D];
     float hb[D][NB];
     float tq[D];
-    const int tcol = lane < B ? lane : B - 1;   // the column whose output this lane would store
+    // the column whose output this lane would store at a key's end (see the key-end reduction)
+    const int tcol0 = NB == 4 ? (lane >> 4) : (NB == 2 ? (lane >> 5) : 0);
+    const int tcol = tcol0 < B ? tcol0 : B - 1;
     auto issue = [&](int q) {
         cur.next(d[q], lane);
         const int32_t o = d[q].base + 4 * lane;
@@ -1602,15 +1607,35 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleAr
             }
             if constexpr (SPMM) {
                 if (dq.flags & 2) {
-                    // the key's sums over the wavefront; lane b stores column b
-                    float s[NB];
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) s[n] = wave_sum(acc[n]);
-                    float sv = s[0];
-#pragma unroll
-                    for (int n = 1; n < NB; ++n) sv = lane == n ? s[n] : sv;
-                    if (lane < NB && lane < B) {
-                        const int64_t o = (int64_t)lane * nkeys + dq.r;
+                    // the key's sums over the wavefront (fixed trees): lane sl ends
+                    // with the total of column sc and stores it
+                    float sv;
+                    int sc, sl;
+                    if constexpr (NB == 4) {
+                        // halves exchanged over lane bits 5 and 4, then sums over bits 3-0:
+                        // lane 16 c holds column c
+                        sv = group_reduce<1, 4>(acc, lane);
+                        sc = lane >> 4;
+                        sl = sc << 4;
+                    } else if constexpr (NB == 2) {
+                        // halves exchanged over lane bit 5, then sums over bits 4-0:
+                        // lane 32 c holds column c
+                        xlevel<5, 2, 2>(acc, lane);
+                        sv = acc[0];
+                        sv += __shfl_xor(sv, 16, kWave);
+                        sv += lane_xor<8>(sv);
+                        sv += lane_xor<4>(sv);
+                        sv += lane_xor<2>(sv);
+                        sv += lane_xor<1>(sv);
+                        sc = lane >> 5;
+                        sl = sc << 5;
+                    } else {
+                        sv = wave_sum(acc[0]);
+                        sc = 0;
+                        sl = 0;
+                    }
+                    if (lane == sl && sc < B) {
+                        const int64_t o = (int64_t)sc * nkeys + dq.r;
                         A.out[o] = sv;
                         if (A.dyo) A.dyo[o] = A.mse_scale * (sv - tq[q]);
                     }
@@ -1622,6 +1647,34 @@ __global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleAr
         }
         if (!d[0].valid()) break;
     }
+}
+
+// workgroup index with the workgroups of one XCD adjacent (the grid is a multiple of kXcd)
+__device__ inline int xcd_major_block()
+{
+    const int nwg = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    return (bid % kXcd) * (nwg / kXcd) + bid / kXcd;
+}
+
+template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16>
+__global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleArgs A, int bp, int B)
+{
+    stream_role<NB, D, DW, SPMM, RM, VAL, I16>(A, bp, B, xcd_major_block(), (int)gridDim.x);
+}
+
+// The two passes of a backward with dX and dW in one launch: workgroups
+// [0, g0) run the column pass (dX, and dW in column order or the column-ordered
+// values stepped), the rest the row pass (dW in canonical order, optionally the
+// canonical values stepped).  The passes are independent, so they overlap
+// instead of paying two launches and two ramps; the split follows their bytes.
+template <int NB, int D, bool RM, bool I16, bool VALR>
+__global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_bwd_kernel(RoleArgs Ac, RoleArgs Ar, int g0, int bp,
+                                                                          int B)
+{
+    const int vb = xcd_major_block();
+    if (vb < g0) stream_role<NB, D, true, true, RM, true, I16>(Ac, bp, B, vb, g0);
+    else stream_role<NB, D, true, false, RM, VALR, I16>(Ar, bp, B, vb - g0, (int)gridDim.x - g0);
 }
 
 // out[b, r] = sum over slices s = 0, 1, ... of part[s][r][b], in that order
@@ -2189,6 +2242,58 @@ snack_status launch_keyed(const BatchPlan& p, const snack_layer* L, const View& 
     return SNACK_OK;
 }
 
+// dX and dW at batch tiles 1-4 with both operands in LDS: the column pass over
+// the transposed view (dX; dW in column order into dwo_t unless null; with
+// apply_t its values stepped in place) and the row pass over the canonical view
+// (dW; with apply its values stepped) in one launch of the two-role kernel.
+snack_status launch_stream_bwd(const BatchPlan& p, const snack_layer* L, const float* dyt, const float* xt, float* dX,
+                               float* dwo_t, float* apply_t, float* dW, float* apply, float lr, int B, hipStream_t s,
+                               bool rm)
+{
+    if (!keyed_lds(L, L->tr, p) || !keyed_lds(L, L->fwd, p)) return SNACK_ERR_INVALID_ARG;
+    RoleArgs ac = role_for(L->tr, dyt, xt, dX, dwo_t, kWavesPerBlock, L->cap);
+    ac.apply = apply_t;
+    ac.lr = lr;
+    ac.tgt = dX;   // the key stores read targets unconditionally: any valid [B][nkeys] array
+    RoleArgs ar = role_for(L->fwd, xt, dyt, nullptr, dW, kWavesPerBlock, L->cap);
+    ar.apply = apply;
+    ar.lr = lr;
+    const size_t lc = stream_lds_bytes(L->tr, p), lr_ = stream_lds_bytes(L->fwd, p);
+    const size_t lds = lc > lr_ ? lc : lr_;
+    const dim3 block(kLdsKeyWaves * kWave);
+    // the column pass moves index + value in, value (or dW) out; the row pass index + value in, dW and value out
+    const double bc = 10.0, br = apply ? 14.0 : 10.0;
+    auto go = [&](auto kern) {
+        int occ = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, (int)block.x, lds) != hipSuccess || occ < 1)
+            occ = 1;
+        int nwg = L->cus * (occ > 2 ? 2 : occ);
+        nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+        int g0 = (int)(nwg * bc / (bc + br) + 0.5);
+        if (g0 < 1) g0 = 1;
+        if (g0 > nwg - 1) g0 = nwg - 1;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), block, lds, s, ac, ar, g0, p.bp, B);
+    };
+    const bool i16 = L->tr.idx16 != nullptr && L->fwd.idx16 != nullptr;
+    auto pick = [&](auto rmc, auto i16c, auto valc) {
+        constexpr bool R = decltype(rmc)::value, I = decltype(i16c)::value, V = decltype(valc)::value;
+        switch (p.btile) {
+        case 1: go(stream_bwd_kernel<1, kStreamDepthFor<1>, R, I, V>); return true;
+        case 2: go(stream_bwd_kernel<2, kStreamDepthFor<2>, R, I, V>); return true;
+        case 4: go(stream_bwd_kernel<4, kStreamDepthFor<4>, R, I, V>); return true;
+        default: return false;
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    bool ok;
+    if (apply) ok = rm ? (i16 ? pick(T{}, T{}, T{}) : pick(T{}, F{}, T{})) : (i16 ? pick(F{}, T{}, T{}) : pick(F{}, F{}, T{}));
+    else ok = rm ? (i16 ? pick(T{}, T{}, F{}) : pick(T{}, F{}, F{})) : (i16 ? pick(F{}, T{}, F{}) : pick(F{}, F{}, F{}));
+    if (!ok) return SNACK_ERR_INVALID_ARG;
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
 // the split table of width index w of view v, valid: when it is stale, every
 // stale table of the view is rebuilt in one pass over its index
 snack_status ensure_split(const View& v, int w, hipStream_t s)
@@ -2500,6 +2605,18 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     // batch-major passes (the slice-tiled and key-major passes decide below)
     float* apply = (step && dX && dW && p.ntiles == 1 && p.btile <= 32) ? L->vals_t : nullptr;
     const float lr = step ? step->lr : 0.0f;
+    if (dX && dW && p.ntiles == 1 && p.btile <= 4 && keyed_lds(L, L->tr, p) && keyed_lds(L, L->fwd, p)) {
+        // both passes in one launch of the two-role streamed kernel (counted as the column pass); with
+        // the step both value copies are stepped in place and no column-order dW is written
+        ProfScope prof(KC_SPMM_DX, s);
+        SNACK_CHECK(launch_stream_bwd(p, L, dyt, xt, dX, step ? nullptr : dW_t, step ? L->vals_t : nullptr, dW,
+                                      step ? L->vals : nullptr, lr, B, s, rm));
+        if (step) {
+            step->done = true;
+            step->canon_done = true;
+        }
+        return SNACK_OK;
+    }
     if (rm) {
         // batch-major operands: every pass is the LDS key-major kernel
         if (dW && !dX) {
