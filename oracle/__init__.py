@@ -17,6 +17,9 @@ What each function computes, and the passage it follows, is documented in
   (Padded-CSR 4.3; SNACK Figure 1).  The candidate stream is SplitMix64:
   parity of the stream itself is pinned only to SplitMix64's published output
   and a uniformity test, since the pages name no generator.
+* ``prune_regrow_grad`` -- the same drop, regrow at the empty cells of largest
+  |dL/dW| for a batch (Padded-CSR 4.3: RigL grows "at high-gradient
+  locations"; SNACK Tables 8-9).
 """
 from __future__ import annotations
 
@@ -70,6 +73,10 @@ def _load():
         lib.oracle_regrow_candidate.restype = u64
         lib.oracle_prune_regrow.argtypes = [i32, i32, i64, P, P, P, i64, u64, u64, P, P, P, P]
         lib.oracle_prune_regrow.restype = ctypes.c_int
+        lib.oracle_grow_key.argtypes = [i32, i32, i32, P, P, i32, i32]
+        lib.oracle_grow_key.restype = ctypes.c_uint32
+        lib.oracle_prune_regrow_grad.argtypes = [i32, i32, i64, P, P, P, i64, i32, P, P, P, P, P]
+        lib.oracle_prune_regrow_grad.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -187,6 +194,30 @@ def prune_regrow(M, K, rows, cols, vals, n_drop, seed, epoch):
     if rc != OK:
         raise OracleError(rc)
     return o_r, o_c, o_v, int(used.value)
+
+
+def grow_key(M, K, X, dY, r, c):
+    """The regrow score key of cell (r, c): IEEE bits of |sum_b dY[b, r] X[b, c]| accumulated in fp32 with
+    one fused multiply-add per batch row, in batch order (a NaN counts as 0)."""
+    X, dY = _f32(X), _f32(dY)
+    B = X.shape[0]
+    assert X.shape == (B, K) and dY.shape == (B, M)
+    return int(_load().oracle_grow_key(M, K, B, _p(X), _p(dY), int(r), int(c)))
+
+
+def prune_regrow_grad(M, K, rows, cols, vals, n_drop, X, dY):
+    """Drop the n_drop smallest |v| (as prune_regrow), grow n_drop empty cells with the largest gradient
+    score for the batch (X [B, K], dY [B, M]); canonical triple in and out."""
+    rows, cols, vals, X, dY = _i32(rows), _i32(cols), _f32(vals), _f32(X), _f32(dY)
+    nnz = rows.shape[0]
+    B = X.shape[0]
+    assert X.shape == (B, K) and dY.shape == (B, M)
+    o_r, o_c, o_v = np.empty(nnz, np.int32), np.empty(nnz, np.int32), np.empty(nnz, np.float32)
+    rc = _load().oracle_prune_regrow_grad(M, K, nnz, _p(rows), _p(cols), _p(vals), int(n_drop), B, _p(X), _p(dY),
+                                          _p(o_r), _p(o_c), _p(o_v))
+    if rc != OK:
+        raise OracleError(rc)
+    return o_r, o_c, o_v
 
 
 def tolerance_ok(got, ref, abs_sum, rel=1e-5, atol=1e-6):

@@ -380,3 +380,119 @@ int oracle_prune_regrow(int32_t M, int32_t K, int64_t nnz,
     free(d); free(dropped); free(occ); free(pos); free(pv); free(grown);
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Drop / regrow with the regrow at high-gradient cells (RigL-style).        */
+/* [PCSR 4.3]: a RigL update drops a fraction of the live entries and grows   */
+/* the same number "at high-gradient locations"; [SNACK Tables 8-9] run RigL  */
+/* on the truly sparse layer.  Drop: exactly as oracle_prune_regrow (the      */
+/* n_drop smallest |v|, ties by slot).  Grow: among the cells empty after the */
+/* drop, the n_drop cells with the largest |dL/dW[r, c]|, where dL/dW[r, c] = */
+/* sum over b of dY[b, r] X[b, c] is the dense weight gradient of the layer   */
+/* at that cell for the batch (X, dY) ([PCSR 7.1]: the gradient of W is       */
+/* dY^T X; on the support it is the sampled product).  The decision is taken */
+/* on the fp32 value of that sum accumulated in batch order with a fused      */
+/* multiply-add per term (the precision the layer computes in), so both sides */
+/* rank the same numbers; the order key is the IEEE bits of |g| (a NaN counts */
+/* as 0), larger first, ties by smaller linear position r*K + c.  Grown       */
+/* entries hold +0.0.                                                         */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    uint32_t key;
+    int64_t pos;
+} growkey_t;
+
+static int cmp_growkey(const void* a, const void* b)
+{
+    const growkey_t* x = (const growkey_t*)a;
+    const growkey_t* y = (const growkey_t*)b;
+    if (x->key > y->key) return -1;   /* larger score first */
+    if (x->key < y->key) return 1;
+    if (x->pos < y->pos) return -1;   /* then smaller position */
+    if (x->pos > y->pos) return 1;
+    return 0;
+}
+
+/* the grow score key of cell (r, c): IEEE bits of |sum_b dY[b, r] X[b, c]| */
+uint32_t oracle_grow_key(int32_t M, int32_t K, int32_t B, const float* X, const float* dY, int32_t r, int32_t c)
+{
+    float g = 0.0f;
+    for (int32_t b = 0; b < B; ++b) g = fmaf(dY[(int64_t)b * M + r], X[(int64_t)b * K + c], g);
+    if (isnan(g)) return 0u;
+    const float a = fabsf(g);
+    uint32_t bits;
+    memcpy(&bits, &a, sizeof bits);
+    return bits;
+}
+
+int oracle_prune_regrow_grad(int32_t M, int32_t K, int64_t nnz,
+                             const int32_t* rows, const int32_t* cols, const float* vals,
+                             int64_t n_drop, int32_t B, const float* X, const float* dY,
+                             int32_t* o_rows, int32_t* o_cols, float* o_vals)
+{
+    if (n_drop < 0 || n_drop > nnz || B < 1) return OR_INVALID;
+    const uint64_t N = (uint64_t)M * (uint64_t)K;
+    const size_t n1 = (size_t)(nnz > 0 ? nnz : 1);
+    dropkey_t* d = (dropkey_t*)malloc(sizeof(dropkey_t) * n1);
+    unsigned char* dropped = (unsigned char*)calloc(n1, 1);
+    unsigned char* occ = (unsigned char*)calloc((size_t)(N / 8 + 1), 1);
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * n1);
+    float* pv = (float*)malloc(sizeof(float) * n1);
+    const uint64_t nempty = N - (uint64_t)(nnz - n_drop);
+    growkey_t* cand = (growkey_t*)malloc(sizeof(growkey_t) * (size_t)(nempty > 0 ? nempty : 1));
+    if (!d || !dropped || !occ || !pos || !pv || !cand) {
+        free(d); free(dropped); free(occ); free(pos); free(pv); free(cand);
+        return OR_NOMEM;
+    }
+    /* drop: the same total order as the SET-style update */
+    for (int64_t k = 0; k < nnz; ++k) {
+        float a = fabsf(vals[k]);
+        uint32_t bits;
+        memcpy(&bits, &a, sizeof bits);
+        d[k].mag = bits;
+        d[k].slot = k;
+    }
+    qsort(d, (size_t)nnz, sizeof(dropkey_t), cmp_dropkey);
+    for (int64_t i = 0; i < n_drop; ++i) dropped[d[i].slot] = 1;
+    int64_t m = 0;
+    for (int64_t k = 0; k < nnz; ++k) {
+        if (dropped[k]) continue;
+        const int64_t p = (int64_t)rows[k] * K + cols[k];
+        occ[p >> 3] |= (unsigned char)(1u << (p & 7));
+        pos[m] = p;
+        pv[m] = vals[k];
+        ++m;
+    }
+    /* grow: every empty cell with its score, best n_drop first */
+    uint64_t e = 0;
+    for (uint64_t p = 0; p < N; ++p) {
+        if (occ[p >> 3] & (1u << (p & 7))) continue;
+        cand[e].key = oracle_grow_key(M, K, B, X, dY, (int32_t)(p / (uint64_t)K), (int32_t)(p % (uint64_t)K));
+        cand[e].pos = (int64_t)p;
+        ++e;
+    }
+    qsort(cand, (size_t)e, sizeof(growkey_t), cmp_growkey);
+    int64_t* grown = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_drop > 0 ? n_drop : 1));
+    if (!grown) {
+        free(d); free(dropped); free(occ); free(pos); free(pv); free(cand);
+        return OR_NOMEM;
+    }
+    for (int64_t g = 0; g < n_drop; ++g) grown[g] = cand[g].pos;
+    qsort(grown, (size_t)n_drop, sizeof(int64_t), cmp_i64);
+    /* merge the two position-sorted lists */
+    int64_t i = 0, j = 0, o = 0;
+    while (i < m || j < n_drop) {
+        int take_kept;
+        if (i >= m) take_kept = 0;
+        else if (j >= n_drop) take_kept = 1;
+        else take_kept = pos[i] < grown[j];
+        const int64_t p = take_kept ? pos[i] : grown[j];
+        o_rows[o] = (int32_t)(p / K);
+        o_cols[o] = (int32_t)(p % K);
+        o_vals[o] = take_kept ? pv[i] : 0.0f;
+        if (take_kept) ++i; else ++j;
+        ++o;
+    }
+    free(d); free(dropped); free(occ); free(pos); free(pv); free(cand); free(grown);
+    return OR_OK;
+}
