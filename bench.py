@@ -457,6 +457,23 @@ def config_legs():
                                         step="snack_train_step_mse (forward, MSE gradient, dX, dW, SGD)",
                                         peak_memory="layer device bytes + torch peak for the caller's tensors")
 
+    print("[bench] gradient-driven drop/regrow at 10000x10000, 95 %", file=sys.stderr, flush=True)
+    lay = make(10000, 10000, 95, "c4/s95", seed=2024)
+    grad = {}
+    for B in (4, 64):
+        X = torch.from_numpy(normal((B, 10000), f"rigl/X/{B}")).cuda()
+        dY = torch.from_numpy(normal((B, 10000), f"rigl/dY/{B}")).cuda()
+        n = lay.nnz * 3 // 10
+        us = _event_us(lambda: L.snack_prune_regrow_grad(lay.h, n, X, dY), 5, warmup=1)
+        # five sweeps over the 10^8 cells, each one fused multiply-add per cell and batch row
+        flops = 5 * 2.0 * B * 10000 * 10000
+        grad[f"b{B}"] = {"us_per_call": round(us, 1), "score_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+                         "frac_valu": round(flops / (us * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4)}
+    lay.close()
+    res["n2_gradient_regrow_10000x10000_s95"] = dict(grad, n_drop="30 % of 5,000,000",
+                                                     step="drop the smallest |w|, regrow at the empty cells of "
+                                                          "largest |dY^T X| for a batch of B rows")
+
     print("[bench] GPT-2-small MLP stack, 1024 tokens", file=sys.stderr, flush=True)
     c5 = {}
     tokens = 1024

@@ -43,6 +43,7 @@ _SIGS = {
     "snack_backward_sgd": ([P, P, P, P, P, f32, i32, P], ST),
     "snack_train_step_mse": ([P, P, P, P, P, P, P, f32, f32, i32, P], ST),
     "snack_prune_regrow": ([P, i64, P], ST),
+    "snack_prune_regrow_grad": ([P, i64, P, P, i32, P], ST),
     "snack_layer_shape": ([P, ctypes.POINTER(i32), ctypes.POINTER(i32)], ST),
     "snack_layer_nnz": ([P, ctypes.POINTER(i64)], ST),
     "snack_layer_device_bytes": ([P, ctypes.POINTER(i64)], ST),
@@ -169,6 +170,15 @@ def snack_train_step_mse(h, X, T, Y, dY, dX, dW, scale, lr, stream=None):
 
 def snack_prune_regrow(h, n_drop, stream=None):
     _check(_lib.snack_prune_regrow(h, int(n_drop), _stream(stream)), "snack_prune_regrow")
+
+
+def snack_prune_regrow_grad(h, n_drop, X, dY, stream=None):
+    """X [B, K], dY [B, M]: the batch whose dense weight gradient picks the grown cells."""
+    B = X.shape[0]
+    if dY.shape[0] != B:
+        raise ValueError("X and dY must have the same batch")
+    _check(_lib.snack_prune_regrow_grad(h, int(n_drop), _ptr(X), _ptr(dY), B, _stream(stream)),
+           "snack_prune_regrow_grad")
 
 
 def snack_layer_shape(h):
@@ -356,6 +366,9 @@ class SnackLayer:
 
     def prune_regrow(self, n_drop, stream=None):
         snack_prune_regrow(self.h, n_drop, stream)
+
+    def prune_regrow_grad(self, n_drop, X, dY, stream=None):
+        snack_prune_regrow_grad(self.h, n_drop, X, dY, stream)
 
     def sgd_step(self, dW, lr, stream=None):
         snack_sgd_step(self.h, dW, lr, stream)

@@ -295,5 +295,29 @@ snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hip
 // ---- prune / regrow (prune.hip) ---------------------------------------------
 size_t prune_scratch_bytes(const snack_layer* L);
 snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s);
+// the same drop, then the regrow at the empty cells of largest |dL/dW| for the batch (X, dY)
+snack_status prune_regrow_grad(snack_layer* L, int64_t n_drop, const float* X, const float* dY, int32_t B,
+                               hipStream_t s);
+
+// ---- gradient regrow (rigl.hip) ----------------------------------------------
+// Cells are scored in tiles of kGradTile x kGradTile; ties at the threshold are
+// counted per row and column tile.
+constexpr int kGradTile = 128;
+constexpr int kGradHistWords = 2048 + 4096 + 256;
+inline int64_t grad_col_tiles(int32_t K) { return ((int64_t)K + kGradTile - 1) / kGradTile; }
+struct GradGrow {
+    const uint32_t* kept_bm;   // cells kept by the drop (the grow picks among the others)
+    uint32_t* occ_bm;          // written: the kept cells and the grown ones
+    int64_t words;
+    int64_t need;              // cells to grow
+    const float* X;            // [B][K] batch-major
+    const float* dY;           // [B][M] batch-major
+    int32_t B;
+    uint32_t* state;           // [16]
+    uint32_t* hist;            // [kGradHistWords]
+    int32_t* tie_cnt;          // [M * grad_col_tiles(K)]
+    void* scan;                // scan scratch for M * grad_col_tiles(K) elements
+};
+snack_status grow_by_gradient(const snack_layer* L, const GradGrow& g, hipStream_t s);
 
 }  // namespace snack

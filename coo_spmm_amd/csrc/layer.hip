@@ -459,6 +459,16 @@ extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack
     return snack::prune_regrow(L, n_drop, as_stream(stream));
 }
 
+extern "C" snack_status snack_prune_regrow_grad(snack_layer* L, int64_t n_drop, const float* X, const float* dY,
+                                                int32_t B, snack_stream stream)
+{
+    if (!L || n_drop < 0 || n_drop > L->nnz) return SNACK_ERR_INVALID_ARG;
+    if (n_drop > 0 && (!X || !dY || B < 1)) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
+    L->dwt_valid = false;
+    return snack::prune_regrow_grad(L, n_drop, X, dY, B, as_stream(stream));
+}
+
 extern "C" snack_status snack_layer_shape(const snack_layer* L, int32_t* M, int32_t* K)
 {
     if (!L || !M || !K) return SNACK_ERR_INVALID_ARG;

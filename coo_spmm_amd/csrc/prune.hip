@@ -1362,6 +1362,9 @@ struct PruneScratch {
     int32_t* wpre;      // [words] first canonical slot of every bitmap word (column view from the bitmap)
     int32_t* cvcnt;     // [row blocks * K] entries per column and row block, then their prefixes
     int32_t* cvtot;     // [K] entries per column
+    uint32_t* gstate;   // [16] gradient grow: thresholds and counts
+    uint32_t* ghist;    // [kGradHistWords] gradient grow: digit histograms
+    int32_t* tie_cnt;   // [M * grad_col_tiles(K)] gradient grow: threshold ties per row and column tile
     void* scan;         // scan scratch
     int64_t tmax, words, units, ktiles, nbucket;
 };
@@ -1395,6 +1398,8 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     const int64_t nbi = (L->M + kCvDim - 1) / kCvDim;
     int64_t sn = units > ktiles ? units : ktiles;
     if (L->K > sn) sn = L->K;
+    const int64_t nties = (int64_t)L->M * grad_col_tiles(L->K);
+    if (nties > sn) sn = nties;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -1408,6 +1413,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     size_t o_acc = take((size_t)tm + 8), o_tsum = take((size_t)(tm / kSumTile + 1) * 4);
     size_t o_fill = take((size_t)kMaxRegions * 4), o_bucket = take((size_t)nb * 8);
     size_t o_wpre = take((size_t)words * 4), o_cvcnt = take((size_t)nbi * L->K * 4), o_cvtot = take((size_t)L->K * 4);
+    size_t o_gst = take(16 * 4), o_gh = take((size_t)kGradHistWords * 4), o_tie = take((size_t)nties * 4);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
         char* base = (char*)L->scratch;
@@ -1427,6 +1433,9 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         ps->wpre = (int32_t*)(base + o_wpre);
         ps->cvcnt = (int32_t*)(base + o_cvcnt);
         ps->cvtot = (int32_t*)(base + o_cvtot);
+        ps->gstate = (uint32_t*)(base + o_gst);
+        ps->ghist = (uint32_t*)(base + o_gh);
+        ps->tie_cnt = (int32_t*)(base + o_tie);
         ps->scan = base + o_scan;
         ps->tmax = tm;
         ps->words = words;
@@ -1517,20 +1526,12 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
 
 }  // namespace
 
-snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
+// The drop: the n_drop smallest magnitudes (order key: IEEE bits of |v|, then
+// slot) leave; kept_bm holds the kept cells, old_bm every cell before the
+// drop, vcopy the values.
+snack_status drop_stage(snack_layer* L, const PruneScratch& ps, int64_t n_drop, hipStream_t s)
 {
     const int64_t nnz = L->nnz;
-    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
-    if (n_drop == 0) {
-        L->epoch += 1;
-        return SNACK_OK;
-    }
-    if (N > kMaxBitmapBits || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
-    ProfScope prof(KC_PRUNE, s);
-    PruneScratch ps;
-    layout(L, &ps);
-    const int64_t kept = nnz - n_drop;
-
     // ---- drop: the n_drop-th smallest magnitude key T and its tie rank ----
     {
         hipLaunchKernelGGL(prune_init_kernel, dim3(32), dim3(256), 0, s, ps.state, ps.hist, (uint32_t)(n_drop - 1),
@@ -1562,6 +1563,23 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         }
         SNACK_HIP(hipGetLastError());
     }
+    return SNACK_OK;
+}
+
+snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
+{
+    const int64_t nnz = L->nnz;
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    if (n_drop == 0) {
+        L->epoch += 1;
+        return SNACK_OK;
+    }
+    if (N > kMaxBitmapBits || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
+    ProfScope prof(KC_PRUNE, s);
+    PruneScratch ps;
+    layout(L, &ps);
+    const int64_t kept = nnz - n_drop;
+    SNACK_CHECK(drop_stage(L, ps, n_drop, s));
 
     // ---- grow: walk the candidate stream in batches ----
     int64_t need = n_drop;
@@ -1650,6 +1668,37 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     }
 
     if (!rebuilt) SNACK_CHECK(rebuild(L, ps, s));
+    L->epoch += 1;
+    return SNACK_OK;
+}
+
+snack_status prune_regrow_grad(snack_layer* L, int64_t n_drop, const float* X, const float* dY, int32_t B,
+                               hipStream_t s)
+{
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    if (n_drop == 0) {
+        L->epoch += 1;
+        return SNACK_OK;
+    }
+    if (N >= (1ull << 32) || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
+    ProfScope prof(KC_PRUNE, s);
+    PruneScratch ps;
+    layout(L, &ps);
+    SNACK_CHECK(drop_stage(L, ps, n_drop, s));
+    GradGrow g;
+    g.kept_bm = ps.kept_bm;
+    g.occ_bm = ps.occ_bm;
+    g.words = ps.words;
+    g.need = n_drop;
+    g.X = X;
+    g.dY = dY;
+    g.B = B;
+    g.state = ps.gstate;
+    g.hist = ps.ghist;
+    g.tie_cnt = ps.tie_cnt;
+    g.scan = ps.scan;
+    SNACK_CHECK(grow_by_gradient(L, g, s));
+    SNACK_CHECK(rebuild(L, ps, s));
     L->epoch += 1;
     return SNACK_OK;
 }

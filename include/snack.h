@@ -191,6 +191,28 @@ snack_status snack_train_step_mse(snack_layer* layer, const float* X, const floa
  */
 snack_status snack_prune_regrow(snack_layer* layer, int64_t n_drop, snack_stream stream);
 
+/*
+ * Drop / regrow with the regrow driven by the gradient (RigL-style): the
+ * "Padded-CSR" post (section 4.3) has RigL drop a fraction of the live entries
+ * and grow the same number "at high-gradient locations"; the SNACK paper
+ * (Tables 8-9) trains with RigL on the truly sparse layer.  Drops the n_drop
+ * entries of smallest |value| exactly as snack_prune_regrow, then grows n_drop
+ * entries (value +0.0) at the cells empty after the drop whose dense weight
+ * gradient for the batch (X, dY) is largest in magnitude:
+ *   g[r, c] = sum over b of dY[b, r] X[b, c]   ("Padded-CSR" 7.1: dL/dW = dY^T X)
+ * accumulated in fp32 with one fused multiply-add per batch row in batch
+ * order; order key the IEEE bits of |g| (a NaN counts as 0), larger first,
+ * ties by smaller linear position r*K + c.  No M*K array is stored: the
+ * scores are recomputed by five sweeps over the cells (about 6 B M K flops
+ * each).  The triple is re-canonicalised and the epoch incremented (the
+ * random stream of snack_prune_regrow is not used).
+ *   X   device float[B, K], dY device float[B, M]: batch-major (e.g. the last
+ *       backward's input and output gradient); 1 <= B <= 2^20.
+ *   0 <= n_drop <= nnz; requires M * K < 2^32 (else SNACK_ERR_UNSUPPORTED).
+ */
+snack_status snack_prune_regrow_grad(snack_layer* layer, int64_t n_drop, const float* X, const float* dY,
+                                     int32_t B, snack_stream stream);
+
 /* Shape and size queries (host outputs). */
 snack_status snack_layer_shape(const snack_layer* layer, int32_t* M, int32_t* K);
 snack_status snack_layer_nnz(const snack_layer* layer, int64_t* nnz);
