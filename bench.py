@@ -457,6 +457,41 @@ def config_legs():
                                         step="snack_train_step_mse (forward, MSE gradient, dX, dW, SGD)",
                                         peak_memory="layer device bytes + torch peak for the caller's tensors")
 
+    print("[bench] inference at batch 1: 5000x5000 layers, bf16 values, a chained stack", file=sys.stderr, flush=True)
+    inf = {}
+    for sp in (90, 95, 99):
+        lay = make(5000, 5000, sp, f"c2/layer/s{sp}")
+        X = torch.from_numpy(normal((1, 5000), "n3/X")).cuda()
+        Y = torch.empty(1, 5000, device="cuda")
+        fw = _event_us(lambda: L.snack_forward_infer(lay.h, X, Y), 2000)
+        fb = _event_us(lambda: L.snack_forward_infer(lay.h, X, Y, bf16_values=True), 2000)
+        inf[f"s{sp}"] = {"nnz": lay.nnz, "fp32_values_us": round(fw, 2), "bf16_values_us": round(fb, 2),
+                         "bytes_per_entry": {"fp32": 6, "bf16": 4},
+                         "bf16_GBps_of_12B_triple": round(12 * lay.nnz / (fb * 1e-6) / 1e9, 1)}
+        lay.close()
+    layers = [make(5000, 5000, 95, f"n3/chain/{i}") for i in range(4)]
+    acts = [L.ACT_GELU, L.ACT_GELU, L.ACT_GELU, L.ACT_NONE]
+    X = torch.from_numpy(normal((1, 5000), "n3/chain/X")).cuda()
+    Ys = [torch.empty(1, 5000, device="cuda") for _ in layers]
+    eager = _event_us(lambda: L.snack_forward_chain([l.h for l in layers], acts, X, Ys, bf16_values=True), 500)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.snack_forward_chain([l.h for l in layers], acts, X, Ys, bf16_values=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.snack_forward_chain([l.h for l in layers], acts, X, Ys, bf16_values=True)
+    replay = _event_us(graph.replay, 500)
+    del graph
+    for l in layers:
+        l.close()
+    inf["chain_4x5000x5000_s95_gelu"] = {"eager_us": round(eager, 2), "graph_replay_us": round(replay, 2),
+                                         "values": "bf16"}
+    res["n3_inference_b1"] = dict(inf, reps=2000, note="snack_forward_infer: 16-bit column indices, fp32 or bf16 "
+                                                       "values, GELU fused into the stores")
+
     print("[bench] gradient-driven drop/regrow at 10000x10000, 95 %", file=sys.stderr, flush=True)
     lay = make(10000, 10000, 95, "c4/s95", seed=2024)
     grad = {}

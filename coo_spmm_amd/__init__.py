@@ -39,6 +39,8 @@ _SIGS = {
     "snack_layer_reserve": ([P, i32], ST),
     "snack_forward": ([P, P, P, i32, P], ST),
     "snack_forward_noalloc": ([P, P, P, i32, P], ST),
+    "snack_forward_infer": ([P, P, P, i32, i32, i32, P], ST),
+    "snack_forward_chain": ([ctypes.POINTER(P), i32, ctypes.POINTER(i32), P, ctypes.POINTER(P), i32, i32, P], ST),
     "snack_backward": ([P, P, P, P, P, i32, P], ST),
     "snack_backward_sgd": ([P, P, P, P, P, f32, i32, P], ST),
     "snack_train_step_mse": ([P, P, P, P, P, P, P, f32, f32, i32, P], ST),
@@ -149,6 +151,27 @@ def snack_forward(h, X, Y, stream=None):
 def snack_forward_noalloc(h, X, Y, stream=None):
     B = X.shape[0]
     _check(_lib.snack_forward_noalloc(h, _ptr(X), _ptr(Y), B, _stream(stream)), "snack_forward_noalloc")
+
+
+ACT_NONE, ACT_GELU = 0, 1
+
+
+def snack_forward_infer(h, X, Y, act=ACT_NONE, bf16_values=False, stream=None):
+    B = X.shape[0]
+    _check(_lib.snack_forward_infer(h, _ptr(X), _ptr(Y), B, int(act), 1 if bf16_values else 0, _stream(stream)),
+           "snack_forward_infer")
+
+
+def snack_forward_chain(handles, acts, X, Ys, bf16_values=False, stream=None):
+    """handles: layer handles; acts: activation codes; Ys: output tensors, one per layer."""
+    n = len(handles)
+    if len(acts) != n or len(Ys) != n:
+        raise ValueError("one activation and one output per layer")
+    hs = (P * n)(*handles)
+    ac = (i32 * n)(*[int(a) for a in acts])
+    ys = (P * n)(*[_ptr(y) for y in Ys])
+    _check(_lib.snack_forward_chain(hs, n, ac, _ptr(X), ys, X.shape[0], 1 if bf16_values else 0, _stream(stream)),
+           "snack_forward_chain")
 
 
 def snack_backward(h, X, dY, dX=None, dW=None, stream=None):

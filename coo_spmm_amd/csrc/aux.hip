@@ -93,8 +93,7 @@ __global__ void mse_grad_kernel(const float* __restrict__ Y, const float* __rest
 __global__ void gelu_fwd_kernel(const float* __restrict__ X, float* __restrict__ Y, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const float x = X[i];
-        Y[i] = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+        Y[i] = gelu_value(X[i]);
     }
 }
 
@@ -106,6 +105,19 @@ __global__ void gelu_bwd_kernel(const float* __restrict__ X, const float* __rest
         const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
         const float pdf = 0.39894228040143268f * expf(-0.5f * x * x);
         dX[i] = dY[i] * (cdf + x * pdf);
+    }
+}
+
+// round to nearest even: add 0x7FFF plus the kept word's lowest bit, keep the
+// high half; NaN stays a quiet NaN of the same sign
+__global__ void pack_bf16_kernel(const float* __restrict__ v, uint16_t* __restrict__ o, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t b = __float_as_uint(v[i]);
+        uint16_t h;
+        if ((b & 0x7FFFFFFFu) > 0x7F800000u) h = (uint16_t)((b >> 16) | 0x0040u);
+        else h = (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+        o[i] = h;
     }
 }
 
@@ -259,6 +271,18 @@ snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s)
     ProfScope prof(KC_ELEMENTWISE, s);
     hipLaunchKernelGGL(gelu_fwd_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, X, Y, n);
     SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
+}
+
+snack_status pack_bf16(snack_layer* L, hipStream_t s)
+{
+    if (!L->vals16) return SNACK_ERR_UNSUPPORTED;
+    if (L->nnz > 0) {
+        ProfScope prof(KC_ELEMENTWISE, s);
+        hipLaunchKernelGGL(pack_bf16_kernel, dim3(grid_for(L->nnz)), dim3(kThreads), 0, s, L->vals, L->vals16, L->nnz);
+        SNACK_HIP(hipGetLastError());
+    }
+    L->b16_version = L->vals_version;
     return SNACK_OK;
 }
 

@@ -44,6 +44,10 @@ constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
 // one SGD step on one value: v - lr * g with a single rounding; every update of
 // either value copy goes through it, so the two copies stay bit-identical
 __device__ inline float sgd_value(float v, float g, float lr) { return fmaf(-lr, g, v); }
+// exact (erf) GELU of one value: every kernel that applies it goes through this
+__device__ inline float gelu_value(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// activation codes of the inference forward
+constexpr int kActNone = 0, kActGelu = 1;
 
 // first index of slice s when [0, nidx) is cut into S slices
 __host__ __device__ inline int32_t split_start(int32_t s, int32_t S, int32_t nidx)
@@ -101,6 +105,11 @@ struct snack_layer {
     int32_t* iperm = nullptr;     // canonical slot -> transposed slot
     int32_t* rows_t = nullptr;
     float* vals_t = nullptr;      // values in transposed order
+    // bf16 copy of the canonical values for the inference forward (round to
+    // nearest even), remade when vals_version has moved past b16_version
+    uint16_t* vals16 = nullptr;
+    uint64_t vals_version = 1;
+    uint64_t b16_version = 0;
     int32_t* col_ptr = nullptr;   // [K+1]
     bool vals_t_stale = true;
     // dW in transposed order from the last backward (bit-identical to the
@@ -290,6 +299,13 @@ snack_status sgd_update(snack_layer* L, const float* dW, const float* dW_t, floa
 snack_status sgd_update_values(snack_layer* L, const float* dW, float lr, hipStream_t s);
 snack_status mse_grad(const float* Y, const float* T, float* dY, int64_t n, float scale, hipStream_t s);
 snack_status gelu_fwd(const float* X, float* Y, int64_t n, hipStream_t s);
+// vals16 = the values rounded to bf16 (nearest even)
+snack_status pack_bf16(snack_layer* L, hipStream_t s);
+// the inference forward (batch tiles up to 4, operand in LDS): Y = act(X W^T), with
+// the values from the bf16 copy when b16; SNACK_ERR_UNSUPPORTED where it does not apply
+snack_status spmm_forward_infer(const snack_layer* L, const float* X, float* Y, int B, int act, bool b16,
+                                hipStream_t s);
+bool infer_supported(const snack_layer* L, int B, bool b16);
 snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hipStream_t s);
 
 // ---- prune / regrow (prune.hip) ---------------------------------------------

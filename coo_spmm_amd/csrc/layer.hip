@@ -258,6 +258,7 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
     L->tr.nchunks = (int32_t)(ncht < 1 ? 1 : ncht);
     // 16-bit copies of the gathered indices for the narrow-batch streams (cap is a multiple of 4)
     if (K <= kIdx16Max) ALLOC(fwd.idx16, uint16_t*, (size_t)L->cap * 2);
+    if (K <= kIdx16Max) ALLOC(vals16, uint16_t*, (size_t)L->cap * 2);   // the inference forward's values
     if (M <= kIdx16Max) ALLOC(tr.idx16, uint16_t*, (size_t)L->cap * 2);
     ALLOC(tr.desc, int2*, ((size_t)L->tr.nchunks + 1) * 8);
     ALLOC(tr.empty_keys, int32_t*, (size_t)K * 4);
@@ -399,6 +400,7 @@ snack_status backward_sgd_impl(snack_layer* L, const float* X, const float* dY, 
                                int32_t B, hipStream_t s, bool x_ready, bool dy_ready)
 {
     SgdStep step{lr, false, false};
+    ++L->vals_version;
     SNACK_CHECK(backward_impl(L, X, dY, dX, dW, B, s, &step, x_ready, dy_ready));
     if (!step.done) {
         // the column pass did not take the step: as snack_sgd_step would
@@ -452,10 +454,53 @@ extern "C" snack_status snack_train_step_mse(snack_layer* L, const float* X, con
     return backward_sgd_impl(L, X, dY, dX, dW, lr, B, s, x_ready, m.dyt_done);
 }
 
+namespace {
+
+// the inference forward of one layer, with the bf16 copy remade first when the
+// values changed since it was made
+snack_status forward_infer_one(snack_layer* L, const float* X, float* Y, int32_t B, int32_t act, bool b16,
+                               hipStream_t s)
+{
+    if (act != kActNone && act != kActGelu) return SNACK_ERR_INVALID_ARG;
+    if (!infer_supported(L, B, b16)) return SNACK_ERR_UNSUPPORTED;
+    if (b16 && L->b16_version != L->vals_version) SNACK_CHECK(pack_bf16(L, s));
+    return spmm_forward_infer(L, X, Y, B, act, b16, s);
+}
+
+}  // namespace
+
+extern "C" snack_status snack_forward_infer(snack_layer* L, const float* X, float* Y, int32_t B, int32_t act,
+                                            int32_t bf16_values, snack_stream stream)
+{
+    if (!L || !X || !Y || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
+    return forward_infer_one(L, X, Y, B, act, bf16_values != 0, as_stream(stream));
+}
+
+extern "C" snack_status snack_forward_chain(snack_layer* const* layers, int32_t n, const int32_t* acts,
+                                            const float* X, float* const* Y, int32_t B, int32_t bf16_values,
+                                            snack_stream stream)
+{
+    if (!layers || n < 1 || !acts || !X || !Y || B < 1) return SNACK_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
+    // every check before the first launch, so a refused chain launches nothing
+    for (int32_t i = 0; i < n; ++i) {
+        const snack_layer* L = layers[i];
+        if (!L || !Y[i] || (acts[i] != kActNone && acts[i] != kActGelu)) return SNACK_ERR_INVALID_ARG;
+        if (i > 0 && L->K != layers[i - 1]->M) return SNACK_ERR_INVALID_ARG;
+        if (!infer_supported(L, B, bf16_values != 0)) return SNACK_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = as_stream(stream);
+    for (int32_t i = 0; i < n; ++i)
+        SNACK_CHECK(forward_infer_one(layers[i], i == 0 ? X : Y[i - 1], Y[i], B, acts[i], bf16_values != 0, s));
+    return SNACK_OK;
+}
+
 extern "C" snack_status snack_prune_regrow(snack_layer* L, int64_t n_drop, snack_stream stream)
 {
     if (!L || n_drop < 0 || n_drop > L->nnz) return SNACK_ERR_INVALID_ARG;
     L->dwt_valid = false;
+    ++L->vals_version;
     return snack::prune_regrow(L, n_drop, as_stream(stream));
 }
 
@@ -466,6 +511,7 @@ extern "C" snack_status snack_prune_regrow_grad(snack_layer* L, int64_t n_drop, 
     if (n_drop > 0 && (!X || !dY || B < 1)) return SNACK_ERR_INVALID_ARG;
     if (B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
     L->dwt_valid = false;
+    ++L->vals_version;
     return snack::prune_regrow_grad(L, n_drop, X, dY, B, as_stream(stream));
 }
 
@@ -503,6 +549,7 @@ extern "C" snack_status snack_layer_values_updated(snack_layer* L)
     if (!L) return SNACK_ERR_INVALID_ARG;
     L->vals_t_stale = true;
     L->dwt_valid = false;
+    ++L->vals_version;
     return SNACK_OK;
 }
 
@@ -560,6 +607,7 @@ extern "C" snack_status snack_sgd_step(snack_layer* L, const float* dW, float lr
     // the column-ordered copy is refreshed from the stepped values before the
     // next pass that reads it, never stepped with a column-order dW of its own
     L->dwt_valid = false;
+    ++L->vals_version;
     return sgd_update(L, dW, nullptr, lr, as_stream(stream));
 }
 

@@ -47,6 +47,8 @@ constexpr int kXcd = 8;
 struct RoleArgs {
     const int32_t* idx;
     const uint16_t* idx16;   // the same indices in 16 bits, or null
+    const uint16_t* vals16;  // the values rounded to bf16 (inference forward), or null
+    int act;                 // activation applied to the outputs as they are stored (inference forward)
     const float* vals;
     const int32_t* ptr;
     const int2* desc;
@@ -1494,7 +1496,8 @@ struct StreamStage {
 };
 
 // One role of the streamed kernel on workgroup vb of the nwg that take it.
-template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16>
+// V16: the values come from their bf16 copy (forward only).
+template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16, bool V16 = false>
 __device__ __forceinline__ void stream_role(const RoleArgs& A, int bp, int B, int vb, int nwg)
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one to four columns per lane");
@@ -1536,7 +1539,14 @@ __device__ __forceinline__ void stream_role(const RoleArgs& A, int bp, int B, in
         } else {
             bi[q] = *reinterpret_cast<const int4*>(A.idx + o);
         }
-        if constexpr (LV) bv[q] = *reinterpret_cast<const float4*>(A.vals + o);
+        if constexpr (V16) {
+            // four bf16 values in 8 bytes, widened exactly
+            const uint2 u = *reinterpret_cast<const uint2*>(A.vals16 + o);
+            bv[q] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+        } else if constexpr (LV) {
+            bv[q] = *reinterpret_cast<const float4*>(A.vals + o);
+        }
         if constexpr (DW) load_h<NB, RM>(A.H, d[q].r, bp, 0, B, nkeys, hb[q]);
         if constexpr (SPMM) tq[q] = A.tgt[(int64_t)tcol * nkeys + d[q].r];
     };
@@ -1636,6 +1646,7 @@ __device__ __forceinline__ void stream_role(const RoleArgs& A, int bp, int B, in
                     }
                     if (lane == sl && sc < B) {
                         const int64_t o = (int64_t)sc * nkeys + dq.r;
+                        if (A.act == kActGelu) sv = gelu_value(sv);
                         A.out[o] = sv;
                         if (A.dyo) A.dyo[o] = A.mse_scale * (sv - tq[q]);
                     }
@@ -1657,10 +1668,10 @@ __device__ inline int xcd_major_block()
     return (bid % kXcd) * (nwg / kXcd) + bid / kXcd;
 }
 
-template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16>
+template <int NB, int D, bool DW, bool SPMM, bool RM, bool VAL, bool I16, bool V16 = false>
 __global__ void __launch_bounds__(kLdsKeyWaves * kWave) stream_lds_kernel(RoleArgs A, int bp, int B)
 {
-    stream_role<NB, D, DW, SPMM, RM, VAL, I16>(A, bp, B, xcd_major_block(), (int)gridDim.x);
+    stream_role<NB, D, DW, SPMM, RM, VAL, I16, V16>(A, bp, B, xcd_major_block(), (int)gridDim.x);
 }
 
 // The two passes of a backward with dX and dW in one launch: workgroups
@@ -2056,6 +2067,8 @@ RoleArgs role_for(const View& v, const float* G, const float* H, float* out, flo
     a.cap = cap;
     a.idx = v.idx;
     a.idx16 = v.idx16;
+    a.vals16 = nullptr;
+    a.act = kActNone;
     a.vals = v.vals;
     a.ptr = v.ptr;
     a.desc = v.desc;
@@ -2151,11 +2164,15 @@ inline size_t stream_lds_bytes(const View& v, const BatchPlan& p)
     return ((size_t)v.nidx + 1) * p.bp * sizeof(float);
 }
 
-// the streamed kernel with the whole gathered operand in LDS applies
+// the streamed kernel with the whole gathered operand in LDS applies: its
+// blocks never span two keys, so keys down to 16 entries on average still pay
+// (a block's loads then cover neighbouring keys, which the next block re-reads
+// from the L2)
+constexpr int64_t kStreamMinKey = 16;
 inline bool keyed_lds(const snack_layer* L, const View& v, const BatchPlan& p)
 {
-    return p.btile <= 4 && p.ntiles == 1 && L->cus > 0 && v.nchunks > 0 && use_keyed(v, L->nnz, p) &&
-           stream_lds_bytes(v, p) <= (size_t)L->lds_bytes;
+    return p.btile <= 4 && p.ntiles == 1 && L->cus > 0 && v.nchunks > 0 && v.nkeys > 0 &&
+           L->nnz / v.nkeys >= kStreamMinKey && stream_lds_bytes(v, p) <= (size_t)L->lds_bytes;
 }
 
 // blocks in flight per wavefront of the streamed kernel (registers allow more
@@ -2592,10 +2609,59 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
     if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true, nullptr, 0.0f, mse);
     if (use_tile_spmm(L, L->fwd, p))
         return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse, part);
-    if (use_keyed(L->fwd, L->nnz, p))
+    if (use_keyed(L->fwd, L->nnz, p) || keyed_lds(L, L->fwd, p))
         return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, false, nullptr, 0.0f, mse);
     return dispatch_seg<false>(p, L->cap, L->fwd, feat_t, nullptr, out, nullptr, nullptr, nullptr, nullptr, nullptr,
                                B, s);
+}
+
+bool infer_supported(const snack_layer* L, int B, bool b16)
+{
+    const BatchPlan p = plan_batch(B);
+    return p.ntiles == 1 && p.btile <= 4 && keyed_lds(L, L->fwd, p) && (!b16 || (L->fwd.idx16 && L->vals16));
+}
+
+snack_status spmm_forward_infer(const snack_layer* L, const float* X, float* Y, int B, int act, bool b16,
+                                hipStream_t s)
+{
+    if (!infer_supported(L, B, b16)) return SNACK_ERR_UNSUPPORTED;
+    ProfScope prof(KC_SPMM_FWD, s);
+    const BatchPlan p = plan_batch(B);
+    const bool rm = p.bp > 1;   // one column: both layouts coincide
+    RoleArgs a = role_for(L->fwd, X, nullptr, Y, nullptr, kWavesPerBlock, L->cap);
+    a.tgt = Y;
+    a.act = act;
+    a.vals16 = b16 ? L->vals16 : nullptr;
+    const size_t lds = stream_lds_bytes(L->fwd, p);
+    const dim3 block(kLdsKeyWaves * kWave);
+    auto go = [&](auto kern) {
+        int occ = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, (int)block.x, lds) != hipSuccess || occ < 1)
+            occ = 1;
+        int nwg = L->cus * (occ > 2 ? 2 : occ);
+        const int want = (L->fwd.nkeys + kLdsKeyWaves - 1) / kLdsKeyWaves;
+        if (nwg > want) nwg = want;
+        nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), block, lds, s, a, p.bp, B);
+    };
+    const bool i16 = L->fwd.idx16 != nullptr;
+    auto pick = [&](auto rmc, auto i16c, auto v16c) {
+        constexpr bool R = decltype(rmc)::value, I = decltype(i16c)::value, V = decltype(v16c)::value;
+        switch (p.btile) {
+        case 1: go(stream_lds_kernel<1, kStreamDepthFor<1>, false, true, R, true, I, V>); return true;
+        case 2: go(stream_lds_kernel<2, kStreamDepthFor<2>, false, true, R, true, I, V>); return true;
+        case 4: go(stream_lds_kernel<4, kStreamDepthFor<4>, false, true, R, true, I, V>); return true;
+        default: return false;
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    bool ok;
+    if (b16) ok = rm ? pick(T{}, T{}, T{}) : pick(F{}, T{}, T{});
+    else ok = rm ? (i16 ? pick(T{}, T{}, F{}) : pick(T{}, F{}, F{})) : (i16 ? pick(F{}, T{}, F{}) : pick(F{}, F{}, F{}));
+    if (!ok) return SNACK_ERR_INVALID_ARG;
+    SNACK_HIP(hipGetLastError());
+    return SNACK_OK;
 }
 
 snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, int B,
@@ -2645,7 +2711,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     // Event classes: the column pass counts as dX, a separate canonical-order dW step as dW.
     if (dW && !dX) {
         ProfScope prof(KC_SDDMM_DW, s);
-        if (p.ntiles == 1 && use_keyed(L->fwd, L->nnz, p))
+        if (p.ntiles == 1 && (use_keyed(L->fwd, L->nnz, p) || keyed_lds(L, L->fwd, p)))
             return launch_keyed<true, false>(p, L, L->fwd, xt, dyt, nullptr, dW, B, s);
         return dispatch_seg<true>(p, L->cap, L->fwd, xt, dyt, nullptr, dW, nullptr, nullptr, nullptr, nullptr, B, s);
     }
@@ -2686,7 +2752,7 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     if (dW)
         return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, &L->fwd, xt, dyt, dW, B, s);
     if (use_tile_spmm(L, L->tr, p)) return launch_tile<false, true>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
-    if (use_keyed(L->tr, L->nnz, p))
+    if (use_keyed(L->tr, L->nnz, p) || keyed_lds(L, L->tr, p))
         return launch_keyed<false>(p, L, L->tr, dyt, xt, dX, nullptr, B, s);
     return dispatch_seg<true>(p, L->cap, L->tr, dyt, xt, dX, dW_t, nullptr, nullptr, nullptr, nullptr, B, s);
 }

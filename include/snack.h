@@ -124,6 +124,35 @@ snack_status snack_forward(snack_layer* layer, const float* X, float* Y, int32_t
 snack_status snack_forward_noalloc(snack_layer* layer, const float* X, float* Y, int32_t B, snack_stream stream);
 
 /*
+ * Inference forward: Y = act(X W^T) for batches up to 4 whose operand fits in
+ * LDS (SNACK paper, Table 6: single-stream inference at batch 1 on the truly
+ * sparse layer; "Padded-CSR" section 9.3: narrower index and value streams).
+ * The streamed kernel reads 16-bit column indices (layers with in_features
+ * below 65535) and either the fp32 values (6 bytes per entry) or, with
+ * bf16_values, a copy of them rounded to bf16, nearest even (4 bytes per
+ * entry); sums are fp32.  The copy is remade by the call itself whenever the
+ * values changed since it was made (training calls, drop/regrow,
+ * snack_layer_values_updated).  act: 0 none, 1 the exact GELU of
+ * snack_gelu_fwd, applied to each output as it is stored.  With
+ * bf16_values = 0 and act = 0 the result equals snack_forward bit for bit.
+ *   X device float[B, K], Y device float[B, M] (overwritten).
+ *   SNACK_ERR_UNSUPPORTED where the conditions above do not hold.
+ */
+snack_status snack_forward_infer(snack_layer* layer, const float* X, float* Y, int32_t B, int32_t act,
+                                 int32_t bf16_values, snack_stream stream);
+
+/*
+ * A stack of layers run forward back to back, as snack_forward_infer each:
+ * Y[0] = act[0](X W_0^T), Y[i] = act[i](Y[i-1] W_i^T).  layers, acts and Y are
+ * host arrays of n entries; Y[i] is a device float[B, M_i]; the in_features of
+ * layer i must equal the out_features of layer i-1.  Every argument is checked
+ * before anything is launched.  The call allocates nothing and never
+ * synchronises, so a caller may capture it in a HIP graph and replay it.
+ */
+snack_status snack_forward_chain(snack_layer* const* layers, int32_t n, const int32_t* acts, const float* X,
+                                 float* const* Y, int32_t B, int32_t bf16_values, snack_stream stream);
+
+/*
  * Backward.  "Padded-CSR" section 7.1: dX = dY W (the SpMM with the transpose,
  * run over the cached transposed index of section 7.2) and dW restricted to the
  * stored positions, dW[k] = sum_b dY[b, r_k] X[b, c_k]; the SNACK paper's

@@ -17,6 +17,8 @@ What each function computes, and the passage it follows, is documented in
   (Padded-CSR 4.3; SNACK Figure 1).  The candidate stream is SplitMix64:
   parity of the stream itself is pinned only to SplitMix64's published output
   and a uniformity test, since the pages name no generator.
+* ``round_bf16``    -- values rounded to bf16 for the inference forward with a
+  narrower value stream (Padded-CSR 9.3).
 * ``prune_regrow_grad`` -- the same drop, regrow at the empty cells of largest
   |dL/dW| for a batch (Padded-CSR 4.3: RigL grows "at high-gradient
   locations"; SNACK Tables 8-9).
@@ -73,6 +75,8 @@ def _load():
         lib.oracle_regrow_candidate.restype = u64
         lib.oracle_prune_regrow.argtypes = [i32, i32, i64, P, P, P, i64, u64, u64, P, P, P, P]
         lib.oracle_prune_regrow.restype = ctypes.c_int
+        lib.oracle_round_bf16.argtypes = [ctypes.c_float]
+        lib.oracle_round_bf16.restype = ctypes.c_float
         lib.oracle_grow_key.argtypes = [i32, i32, i32, P, P, i32, i32]
         lib.oracle_grow_key.restype = ctypes.c_uint32
         lib.oracle_prune_regrow_grad.argtypes = [i32, i32, i64, P, P, P, i64, i32, P, P, P, P, P]
@@ -218,6 +222,13 @@ def prune_regrow_grad(M, K, rows, cols, vals, n_drop, X, dY):
     if rc != OK:
         raise OracleError(rc)
     return o_r, o_c, o_v
+
+
+def round_bf16(v):
+    """Each value rounded to bf16 (nearest, ties to even), returned as float32."""
+    v = _f32(v)
+    f = _load().oracle_round_bf16
+    return np.array([f(float(x)) for x in v.reshape(-1)], np.float32).reshape(v.shape)
 
 
 def tolerance_ok(got, ref, abs_sum, rel=1e-5, atol=1e-6):

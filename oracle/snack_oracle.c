@@ -496,3 +496,27 @@ int oracle_prune_regrow_grad(int32_t M, int32_t K, int64_t nnz,
     free(d); free(dropped); free(occ); free(pos); free(pv); free(cand); free(grown);
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* bf16 rounding of a value for the inference forward with narrower value    */
+/* streams ([PCSR 9.3]: narrower index and value encodings).  bf16 keeps 8   */
+/* significant bits and fp32's exponent range: a finite x is rounded to the  */
+/* nearest multiple of its bf16 spacing, 2^(e-7) for 2^e <= |x| < 2^(e+1)     */
+/* (2^-133 below 2^-126), ties to the even multiple; results of magnitude    */
+/* 2^128 or more become infinities.  Computed in double, where every step is */
+/* exact.                                                                    */
+/* ------------------------------------------------------------------------- */
+float oracle_round_bf16(float x)
+{
+    if (isnan(x) || isinf(x) || x == 0.0f) return x;
+    const double ax = fabs((double)x);
+    int e;
+    (void)frexp(ax, &e);             /* ax = m 2^e, 0.5 <= m < 1: 2^(e-1) <= ax < 2^e */
+    int lo = e - 1;                  /* the binade's exponent */
+    if (lo < -126) lo = -126;        /* subnormal bf16: fixed spacing */
+    const double spacing = ldexp(1.0, lo - 7);
+    const double q = nearbyint(ax / spacing);    /* default rounding: to nearest, ties to even */
+    double r = q * spacing;
+    if (r >= ldexp(1.0, 128)) r = INFINITY;
+    return (float)(x < 0.0f ? -r : r);
+}

@@ -27,6 +27,7 @@ void oracle_gelu_fwd(int64_t n, const float* X, double* Y);
 void oracle_gelu_bwd(int64_t n, const float* X, const float* dY, double* dX);
 void oracle_sgd(int64_t n, const float* v, const float* g, double lr, double* out);
 uint64_t oracle_regrow_candidate(uint64_t seed, uint64_t epoch, uint64_t t, uint64_t N);
+float oracle_round_bf16(float x);
 uint32_t oracle_grow_key(int32_t M, int32_t K, int32_t B, const float* X, const float* dY, int32_t r, int32_t c);
 int oracle_prune_regrow_grad(int32_t M, int32_t K, int64_t nnz, const int32_t* rows, const int32_t* cols,
                              const float* vals, int64_t n_drop, int32_t B, const float* X, const float* dY,
@@ -136,6 +137,9 @@ static int run_case(int32_t M, int32_t K, int64_t nnz, int32_t B, int special)
     }
     (void)oracle_regrow_candidate(~0ULL, (1ULL << 23) - 1, (1ULL << 40) - 1, (uint64_t)N);
     (void)oracle_grow_key(M, K, B, X, dY, M - 1, K - 1);
+    for (int64_t k = 0; k < nnz; ++k) (void)oracle_round_bf16(cv[k]);
+    (void)oracle_round_bf16(3.4028235e38f);
+    (void)oracle_round_bf16(1e-45f);
 
     free(r); free(c); free(v); free(cr); free(cc); free(cv); free(rp); free(pm); free(rt); free(cp);
     free(X); free(dY); free(Y); free(Ya); free(dX); free(dXa); free(dW); free(dWa); free(Yf); free(g);
