@@ -17,6 +17,9 @@ What each function computes, and the passage it follows, is documented in
   (Padded-CSR 4.3; SNACK Figure 1).  The candidate stream is SplitMix64:
   parity of the stream itself is pinned only to SplitMix64's published output
   and a uniformity test, since the pages name no generator.
+* ``prune_regrow_rows`` -- row-local variants: every row keeps its nnz, drops
+  its smallest |w| and regrows inside itself, at random or by gradient
+  (Padded-CSR 8.3: SparseLab's SET and RigL keep per-row nnz fixed).
 * ``round_bf16``    -- values rounded to bf16 for the inference forward with a
   narrower value stream (Padded-CSR 9.3).
 * ``prune_regrow_grad`` -- the same drop, regrow at the empty cells of largest
@@ -75,6 +78,11 @@ def _load():
         lib.oracle_regrow_candidate.restype = u64
         lib.oracle_prune_regrow.argtypes = [i32, i32, i64, P, P, P, i64, u64, u64, P, P, P, P]
         lib.oracle_prune_regrow.restype = ctypes.c_int
+        lib.oracle_row_candidate.argtypes = [u64, u64, i32, u64, i32]
+        lib.oracle_row_candidate.restype = i32
+        lib.oracle_prune_regrow_rows.argtypes = [i32, i32, i64, P, P, P, i64, i64, ctypes.c_int, u64, u64, i32, P, P,
+                                                 P, P, P]
+        lib.oracle_prune_regrow_rows.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [ctypes.c_float]
         lib.oracle_round_bf16.restype = ctypes.c_float
         lib.oracle_grow_key.argtypes = [i32, i32, i32, P, P, i32, i32]
@@ -219,6 +227,29 @@ def prune_regrow_grad(M, K, rows, cols, vals, n_drop, X, dY):
     o_r, o_c, o_v = np.empty(nnz, np.int32), np.empty(nnz, np.int32), np.empty(nnz, np.float32)
     rc = _load().oracle_prune_regrow_grad(M, K, nnz, _p(rows), _p(cols), _p(vals), int(n_drop), B, _p(X), _p(dY),
                                           _p(o_r), _p(o_c), _p(o_v))
+    if rc != OK:
+        raise OracleError(rc)
+    return o_r, o_c, o_v
+
+
+def row_candidate(seed, epoch, row, t, K):
+    return int(_load().oracle_row_candidate(seed & (2**64 - 1), int(epoch), int(row), int(t), int(K)))
+
+
+def prune_regrow_rows(M, K, rows, cols, vals, num, den, mode, seed=0, epoch=0, X=None, dY=None):
+    """Row-local drop / regrow (each row keeps its nnz): canonical triple in and out.  mode 0: random regrow
+    inside the row; mode 1: regrow at the row's empty cells of largest |dY^T X| for the batch (X, dY)."""
+    rows, cols, vals = _i32(rows), _i32(cols), _f32(vals)
+    nnz = rows.shape[0]
+    B = 0
+    if mode == 1:
+        X, dY = _f32(X), _f32(dY)
+        B = X.shape[0]
+        assert X.shape == (B, K) and dY.shape == (B, M)
+    o_r, o_c, o_v = np.empty(nnz, np.int32), np.empty(nnz, np.int32), np.empty(nnz, np.float32)
+    rc = _load().oracle_prune_regrow_rows(M, K, nnz, _p(rows), _p(cols), _p(vals), int(num), int(den), int(mode),
+                                          seed & (2**64 - 1), int(epoch), B, _p(X), _p(dY), _p(o_r), _p(o_c),
+                                          _p(o_v))
     if rc != OK:
         raise OracleError(rc)
     return o_r, o_c, o_v

@@ -520,3 +520,111 @@ float oracle_round_bf16(float x)
     if (r >= ldexp(1.0, 128)) r = INFINITY;
     return (float)(x < 0.0f ? -r : r);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Row-local drop / regrow: every row keeps its number of entries.  [PCSR    */
+/* 8.3]: SparseLab's SET and RigL keep each row's nnz fixed (adaptive-density */
+/* variants change it); [PCSR 4.3]: drop a fraction of the live entries and   */
+/* grow as many.  Row i with n_i entries drops d_i = floor(n_i * num / den)   */
+/* of them -- the smallest |v| in the row, ties by slot -- and grows d_i      */
+/* cells of the same row, empty after the row's drop, value +0.0:             */
+/*  mode 0 (SET):  candidate t of row i is column high64(u_t * K), u_t the    */
+/*                 SplitMix64 output of s_i + (t + 1) * gamma, where s_i =    */
+/*                 mix64(seed ^ mix64(epoch * 2^32 + i)); a candidate is      */
+/*                 accepted when its column is neither kept nor accepted at   */
+/*                 a smaller t; candidates t < 64 K + 4096 are tried, and     */
+/*                 grows still missing after them take the smallest empty     */
+/*                 columns in order;                                          */
+/*  mode 1 (RigL): the d_i empty columns of largest |dY^T X| score (the key   */
+/*                 of oracle_grow_key), ties by smaller column.               */
+/* ------------------------------------------------------------------------- */
+static uint64_t row_stream_base(uint64_t seed, uint64_t epoch, int32_t row)
+{
+    return oracle_splitmix64_mix(seed ^ oracle_splitmix64_mix((epoch << 32) + (uint64_t)(uint32_t)row));
+}
+
+int32_t oracle_row_candidate(uint64_t seed, uint64_t epoch, int32_t row, uint64_t t, int32_t K)
+{
+    const uint64_t x = row_stream_base(seed, epoch, row) + (t + 1ULL) * 0x9E3779B97F4A7C15ULL;
+    const uint64_t u = oracle_splitmix64_mix(x);
+    return (int32_t)(((unsigned __int128)u * (unsigned __int128)(uint64_t)K) >> 64);
+}
+
+int oracle_prune_regrow_rows(int32_t M, int32_t K, int64_t nnz,
+                             const int32_t* rows, const int32_t* cols, const float* vals,
+                             int64_t num, int64_t den, int mode, uint64_t seed, uint64_t epoch,
+                             int32_t B, const float* X, const float* dY,
+                             int32_t* o_rows, int32_t* o_cols, float* o_vals)
+{
+    if (num < 0 || den < 1 || num > den || (mode != 0 && mode != 1)) return OR_INVALID;
+    if (mode == 1 && (B < 1 || !X || !dY)) return OR_INVALID;
+    unsigned char* kept = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
+    unsigned char* grown = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
+    dropkey_t* d = (dropkey_t*)malloc(sizeof(dropkey_t) * (size_t)(nnz > 0 ? nnz : 1));
+    growkey_t* cand = (growkey_t*)malloc(sizeof(growkey_t) * (size_t)(K > 0 ? K : 1));
+    float* kv = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+    if (!kept || !grown || !d || !cand || !kv) {
+        free(kept); free(grown); free(d); free(cand); free(kv);
+        return OR_NOMEM;
+    }
+    int64_t p0 = 0, o = 0;
+    for (int32_t i = 0; i < M; ++i) {
+        int64_t p1 = p0;
+        while (p1 < nnz && rows[p1] == i) ++p1;
+        const int64_t n = p1 - p0;
+        const int64_t drop = n * num / den;
+        /* drop: the row's smallest |v|, ties by slot */
+        for (int64_t k = 0; k < n; ++k) {
+            float a = fabsf(vals[p0 + k]);
+            uint32_t bits;
+            memcpy(&bits, &a, sizeof bits);
+            d[k].mag = bits;
+            d[k].slot = p0 + k;
+        }
+        qsort(d, (size_t)n, sizeof(dropkey_t), cmp_dropkey);
+        memset(kept, 0, (size_t)K);
+        memset(grown, 0, (size_t)K);
+        for (int64_t k = drop; k < n; ++k) {
+            kept[cols[d[k].slot]] = 1;
+            kv[cols[d[k].slot]] = vals[d[k].slot];
+        }
+        /* grow inside the row */
+        int64_t need = drop;
+        if (mode == 0) {
+            const uint64_t tmax = 64ULL * (uint64_t)K + 4096ULL;
+            for (uint64_t t = 0; t < tmax && need > 0; ++t) {
+                const int32_t c = oracle_row_candidate(seed, epoch, i, t, K);
+                if (kept[c] || grown[c]) continue;
+                grown[c] = 1;
+                --need;
+            }
+            for (int32_t c = 0; c < K && need > 0; ++c) {
+                if (kept[c] || grown[c]) continue;
+                grown[c] = 1;
+                --need;
+            }
+        } else {
+            int64_t e = 0;
+            for (int32_t c = 0; c < K; ++c) {
+                if (kept[c]) continue;
+                cand[e].key = oracle_grow_key(M, K, B, X, dY, i, c);
+                cand[e].pos = c;
+                ++e;
+            }
+            qsort(cand, (size_t)e, sizeof(growkey_t), cmp_growkey);
+            for (int64_t g = 0; g < need; ++g) grown[cand[g].pos] = 1;
+            need = 0;
+        }
+        /* the row, ascending by column */
+        for (int32_t c = 0; c < K; ++c) {
+            if (!kept[c] && !grown[c]) continue;
+            o_rows[o] = i;
+            o_cols[o] = c;
+            o_vals[o] = kept[c] ? kv[c] : 0.0f;
+            ++o;
+        }
+        p0 = p1;
+    }
+    free(kept); free(grown); free(d); free(cand); free(kv);
+    return o == nnz ? OR_OK : OR_INVALID;
+}

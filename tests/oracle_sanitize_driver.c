@@ -32,6 +32,11 @@ uint32_t oracle_grow_key(int32_t M, int32_t K, int32_t B, const float* X, const 
 int oracle_prune_regrow_grad(int32_t M, int32_t K, int64_t nnz, const int32_t* rows, const int32_t* cols,
                              const float* vals, int64_t n_drop, int32_t B, const float* X, const float* dY,
                              int32_t* o_rows, int32_t* o_cols, float* o_vals);
+int oracle_prune_regrow_rows(int32_t M, int32_t K, int64_t nnz, const int32_t* rows, const int32_t* cols,
+                             const float* vals, int64_t num, int64_t den, int mode, uint64_t seed, uint64_t epoch,
+                             int32_t B, const float* X, const float* dY, int32_t* o_rows, int32_t* o_cols,
+                             float* o_vals);
+int32_t oracle_row_candidate(uint64_t seed, uint64_t epoch, int32_t row, uint64_t t, int32_t K);
 int oracle_prune_regrow(int32_t M, int32_t K, int64_t nnz, const int32_t* rows, const int32_t* cols,
                         const float* vals, int64_t n_drop, uint64_t seed, uint64_t epoch, int32_t* o_rows,
                         int32_t* o_cols, float* o_vals, uint64_t* candidates_used);
@@ -131,12 +136,20 @@ static int run_case(int32_t M, int32_t K, int64_t nnz, int32_t B, int special)
         if (oracle_prune_regrow(M, K, nnz, cr, cc, cv, drops[d], 99, (uint64_t)d, orow, ocol, oval, &used) != 0)
             return 2;
         if (oracle_prune_regrow_grad(M, K, nnz, cr, cc, cv, drops[d], B, X, dY, orow, ocol, oval) != 0) return 5;
+        /* row-local: the same three fractions of every row (0, 3/10, all) */
+        const int64_t num = d == 0 ? 0 : (d == 1 ? 3 : 1), den = d == 1 ? 10 : 1;
+        if (oracle_prune_regrow_rows(M, K, nnz, cr, cc, cv, num, den, 0, 99, (uint64_t)d, 0, NULL, NULL, orow, ocol,
+                                     oval) != 0)
+            return 6;
+        if (oracle_prune_regrow_rows(M, K, nnz, cr, cc, cv, num, den, 1, 0, 0, B, X, dY, orow, ocol, oval) != 0)
+            return 7;
         free(orow);
         free(ocol);
         free(oval);
     }
     (void)oracle_regrow_candidate(~0ULL, (1ULL << 23) - 1, (1ULL << 40) - 1, (uint64_t)N);
     (void)oracle_grow_key(M, K, B, X, dY, M - 1, K - 1);
+    (void)oracle_row_candidate(~0ULL, 0xFFFFFFFFULL, M - 1, (uint64_t)64 * K + 4095, K);
     for (int64_t k = 0; k < nnz; ++k) (void)oracle_round_bf16(cv[k]);
     (void)oracle_round_bf16(3.4028235e38f);
     (void)oracle_round_bf16(1e-45f);
