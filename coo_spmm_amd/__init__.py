@@ -46,6 +46,7 @@ _SIGS = {
     "snack_train_step_mse": ([P, P, P, P, P, P, P, f32, f32, i32, P], ST),
     "snack_prune_regrow": ([P, i64, P], ST),
     "snack_prune_regrow_grad": ([P, i64, P, P, i32, P], ST),
+    "snack_prune_regrow_rows": ([P, i64, i64, i32, P, P, i32, P], ST),
     "snack_layer_shape": ([P, ctypes.POINTER(i32), ctypes.POINTER(i32)], ST),
     "snack_layer_nnz": ([P, ctypes.POINTER(i64)], ST),
     "snack_layer_device_bytes": ([P, ctypes.POINTER(i64)], ST),
@@ -154,6 +155,7 @@ def snack_forward_noalloc(h, X, Y, stream=None):
 
 
 ACT_NONE, ACT_GELU = 0, 1
+REGROW_RANDOM, REGROW_GRADIENT = 0, 1
 
 
 def snack_forward_infer(h, X, Y, act=ACT_NONE, bf16_values=False, stream=None):
@@ -202,6 +204,19 @@ def snack_prune_regrow_grad(h, n_drop, X, dY, stream=None):
         raise ValueError("X and dY must have the same batch")
     _check(_lib.snack_prune_regrow_grad(h, int(n_drop), _ptr(X), _ptr(dY), B, _stream(stream)),
            "snack_prune_regrow_grad")
+
+
+def snack_prune_regrow_rows(h, drop_num, drop_den, mode, X=None, dY=None, stream=None):
+    """Row-local drop / regrow: each row drops floor(n_i * drop_num / drop_den) of its smallest |w| and
+    regrows as many inside itself, at random (REGROW_RANDOM) or at the largest |dY^T X| (REGROW_GRADIENT,
+    X [B, K], dY [B, M])."""
+    B = 0
+    if X is not None or dY is not None:
+        if X is None or dY is None or dY.shape[0] != X.shape[0]:
+            raise ValueError("X and dY must both be given, with the same batch")
+        B = X.shape[0]
+    _check(_lib.snack_prune_regrow_rows(h, int(drop_num), int(drop_den), int(mode), _ptr(X), _ptr(dY), B,
+                                        _stream(stream)), "snack_prune_regrow_rows")
 
 
 def snack_layer_shape(h):
@@ -392,6 +407,9 @@ class SnackLayer:
 
     def prune_regrow_grad(self, n_drop, X, dY, stream=None):
         snack_prune_regrow_grad(self.h, n_drop, X, dY, stream)
+
+    def prune_regrow_rows(self, drop_num, drop_den, mode=REGROW_RANDOM, X=None, dY=None, stream=None):
+        snack_prune_regrow_rows(self.h, drop_num, drop_den, mode, X, dY, stream)
 
     def sgd_step(self, dW, lr, stream=None):
         snack_sgd_step(self.h, dW, lr, stream)

@@ -312,6 +312,28 @@ snack_status gelu_bwd(const float* X, const float* dY, float* dX, int64_t n, hip
 size_t prune_scratch_bytes(const snack_layer* L);
 snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s);
 // the same drop, then the regrow at the empty cells of largest |dL/dW| for the batch (X, dY)
+// Row-local drop / regrow (rows.hip): the bitmaps and value copy that the
+// rebuild of the global drop / regrow takes.
+struct RowDst {
+    const int32_t* row_ptr;
+    const int32_t* cols;
+    const float* vals;
+    float* vcopy;
+    uint32_t* old_bm;
+    uint32_t* kept_bm;
+    uint32_t* occ_bm;
+    int32_t M, K;
+    int64_t num, den;
+    bool gradient;
+    uint64_t seed, epoch;
+    const float* X;
+    const float* dY;
+    int32_t B;
+};
+int64_t rows_lds_per_wave(int32_t K);
+snack_status rows_drop_grow(const RowDst& r, int lds_limit, hipStream_t s);
+snack_status prune_regrow_rows(snack_layer* L, int64_t num, int64_t den, bool gradient, const float* X,
+                               const float* dY, int32_t B, hipStream_t s);
 snack_status prune_regrow_grad(snack_layer* L, int64_t n_drop, const float* X, const float* dY, int32_t B,
                                hipStream_t s);
 

@@ -515,6 +515,19 @@ extern "C" snack_status snack_prune_regrow_grad(snack_layer* L, int64_t n_drop, 
     return snack::prune_regrow_grad(L, n_drop, X, dY, B, as_stream(stream));
 }
 
+extern "C" snack_status snack_prune_regrow_rows(snack_layer* L, int64_t drop_num, int64_t drop_den, int32_t mode,
+                                                const float* X, const float* dY, int32_t B, snack_stream stream)
+{
+    if (!L || drop_den < 1 || drop_den > 0x7FFFFFFFll || drop_num < 0 || drop_num > drop_den) return SNACK_ERR_INVALID_ARG;
+    if (mode != SNACK_REGROW_RANDOM && mode != SNACK_REGROW_GRADIENT) return SNACK_ERR_INVALID_ARG;
+    const bool gradient = mode == SNACK_REGROW_GRADIENT;
+    if (gradient && drop_num > 0 && (!X || !dY || B < 1)) return SNACK_ERR_INVALID_ARG;
+    if (gradient && B > kMaxBatch) return SNACK_ERR_UNSUPPORTED;
+    L->dwt_valid = false;
+    ++L->vals_version;
+    return snack::prune_regrow_rows(L, drop_num, drop_den, gradient, X, dY, B, as_stream(stream));
+}
+
 extern "C" snack_status snack_layer_shape(const snack_layer* L, int32_t* M, int32_t* K)
 {
     if (!L || !M || !K) return SNACK_ERR_INVALID_ARG;

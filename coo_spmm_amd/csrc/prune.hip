@@ -1672,6 +1672,45 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     return SNACK_OK;
 }
 
+// Row-local: each row drops and regrows inside itself (rows.hip writes the
+// bitmaps), then the same rebuild.
+snack_status prune_regrow_rows(snack_layer* L, int64_t num, int64_t den, bool gradient, const float* X,
+                               const float* dY, int32_t B, hipStream_t s)
+{
+    const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    if (num == 0 || L->nnz == 0) {
+        L->epoch += 1;
+        return SNACK_OK;
+    }
+    if (N > kMaxBitmapBits || L->scratch_bytes < layout(L, nullptr)) return SNACK_ERR_UNSUPPORTED;
+    if (rows_lds_per_wave(L->K) > L->lds_bytes) return SNACK_ERR_UNSUPPORTED;
+    ProfScope prof(KC_PRUNE, s);
+    PruneScratch ps;
+    layout(L, &ps);
+    RowDst r;
+    r.row_ptr = L->row_ptr;
+    r.cols = L->cols;
+    r.vals = L->vals;
+    r.vcopy = ps.vcopy;
+    r.old_bm = ps.old_bm;
+    r.kept_bm = ps.kept_bm;
+    r.occ_bm = ps.occ_bm;
+    r.M = L->M;
+    r.K = L->K;
+    r.num = num;
+    r.den = den;
+    r.gradient = gradient;
+    r.seed = L->seed;
+    r.epoch = L->epoch;
+    r.X = X;
+    r.dY = dY;
+    r.B = B;
+    SNACK_CHECK(rows_drop_grow(r, L->lds_bytes, s));
+    SNACK_CHECK(rebuild(L, ps, s));
+    L->epoch += 1;
+    return SNACK_OK;
+}
+
 snack_status prune_regrow_grad(snack_layer* L, int64_t n_drop, const float* X, const float* dY, int32_t B,
                                hipStream_t s)
 {

@@ -242,6 +242,36 @@ snack_status snack_prune_regrow(snack_layer* layer, int64_t n_drop, snack_stream
 snack_status snack_prune_regrow_grad(snack_layer* layer, int64_t n_drop, const float* X, const float* dY,
                                      int32_t B, snack_stream stream);
 
+/*
+ * Row-local drop / regrow: every row keeps its number of entries.  The
+ * "Padded-CSR" post (section 8.3) notes that SparseLab's SET and RigL keep
+ * per-row nnz fixed (only adaptive-density variants change it), so both the
+ * drop and the regrow happen inside each row.  Row i with n_i entries drops
+ * d_i = floor(n_i * drop_num / drop_den) of them -- its smallest |value|,
+ * order key (IEEE bits of |v|, canonical slot) -- and grows d_i cells of the
+ * same row that are empty after its drop, value +0.0:
+ *   SNACK_REGROW_RANDOM (SET): candidate t of row i is the column
+ *     high64(u_t * K), u_t = mix(s_i + (t + 1) * 0x9E3779B97F4A7C15) with
+ *     s_i = mix(seed ^ mix(epoch * 2^32 + i)) and mix the SplitMix64 output
+ *     function; a candidate is accepted if its cell is neither kept nor
+ *     accepted at a smaller t.  Candidates t < 64 K + 4096 are tried; grows
+ *     still missing after them (practically never) take the row's smallest
+ *     empty columns.  X, dY and B are ignored.
+ *   SNACK_REGROW_GRADIENT (RigL): the d_i empty cells of the row of largest
+ *     |g|, g[i, c] = sum over b of dY[b, i] X[b, c] (the dense weight
+ *     gradient, "Padded-CSR" 7.1), fp32 with one fused multiply-add per batch
+ *     row in batch order, a NaN counting as 0; ties by smaller column.
+ *     X device float[B, K], dY device float[B, M], batch-major, 1 <= B <= 2^20.
+ * 0 <= drop_num <= drop_den, 1 <= drop_den <= 2^31 - 1.  The triple is
+ * re-canonicalised and the epoch incremented (also when nothing moves).
+ * Needs about 8 * (K / 32 + 130) bytes of LDS per row processed at once:
+ * K up to about 650 000 (else SNACK_ERR_UNSUPPORTED).  Never synchronises.
+ */
+#define SNACK_REGROW_RANDOM 0
+#define SNACK_REGROW_GRADIENT 1
+snack_status snack_prune_regrow_rows(snack_layer* layer, int64_t drop_num, int64_t drop_den, int32_t mode,
+                                     const float* X, const float* dY, int32_t B, snack_stream stream);
+
 /* Shape and size queries (host outputs). */
 snack_status snack_layer_shape(const snack_layer* layer, int32_t* M, int32_t* K);
 snack_status snack_layer_nnz(const snack_layer* layer, int64_t* nnz);
