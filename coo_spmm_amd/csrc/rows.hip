@@ -96,7 +96,8 @@ __device__ inline void hist_add(uint32_t* h, bool act, uint32_t dig)
 // when ASC, else from the largest down) that holds the rank-th key (1-based),
 // and the rank within that digit.  Every lane returns the same pair.
 template <bool ASC>
-__device__ inline void pick_digit(const uint32_t* h, uint32_t rank, uint32_t& digit, uint32_t& rest)
+__device__ inline void pick_digit(const uint32_t* h, uint32_t rank, uint32_t& digit, uint32_t& rest,
+                                  uint32_t* total = nullptr)
 {
     const int lane = lane_id();
     uint32_t c[4], t[4];
@@ -120,6 +121,7 @@ __device__ inline void pick_digit(const uint32_t* h, uint32_t rank, uint32_t& di
     }
     digit = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
     rest = (uint32_t)__builtin_amdgcn_readlane((int)r, L);
+    if (total) *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
 }
 
 struct RowArgs {
@@ -296,9 +298,10 @@ __global__ void __launch_bounds__(256) row_drop_kernel(RowArgs a)
 }
 
 // ---- gradient grow --------------------------------------------------------
-constexpr int kGR = 16;          // rows per workgroup
+constexpr int kGR = 8;           // rows per workgroup
 constexpr int kGThreadsR = 256;  // one column per thread and chunk
 constexpr int kGWaves = kGThreadsR / kWave;
+constexpr int kGB = 8;           // batch rows whose operands are loaded together
 
 struct RowGradArgs {
     const float* X;
@@ -310,6 +313,24 @@ struct RowGradArgs {
     uint32_t* occ_bm;
 };
 
+// NB batch rows of the 16 score chains of a column: their X operands are
+// loaded before any is used (the dY operands are uniform: scalar loads)
+template <bool FULL, int NB>
+__device__ inline void score_group(const RowGradArgs& a, int32_t r0, const float* __restrict__ xp, int32_t b,
+                                   float (&acc)[kGR])
+{
+    const int32_t last = a.M - 1 - r0;
+    float x[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) x[j] = xp[(int64_t)(b + j) * a.K];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const float* __restrict__ dy = a.dY + (int64_t)(b + j) * a.M + r0;
+#pragma unroll
+        for (int i = 0; i < kGR; ++i) acc[i] = fmaf(dy[FULL ? i : (i < last ? i : last)], x[j], acc[i]);
+    }
+}
+
 // the 16 scores of column c: acc[i] = sum_b dY[b, r0 + i] X[b, c], one fused
 // multiply-add per b in batch order (rows past M repeat the last row)
 template <bool FULL>
@@ -318,140 +339,372 @@ __device__ inline void col_scores(const RowGradArgs& a, int32_t r0, int32_t c, f
 #pragma unroll
     for (int i = 0; i < kGR; ++i) acc[i] = 0.0f;
     const float* __restrict__ xp = a.X + c;
-    const int32_t last = a.M - 1 - r0;
-#pragma unroll 4
-    for (int32_t b = 0; b < a.B; ++b) {
-        const float x = xp[(int64_t)b * a.K];
-        const float* __restrict__ dy = a.dY + (int64_t)b * a.M + r0;
-#pragma unroll
-        for (int i = 0; i < kGR; ++i) acc[i] = fmaf(dy[FULL ? i : (i < last ? i : last)], x, acc[i]);
+    int32_t b = 0;
+    for (; b + kGB <= a.B; b += kGB) score_group<FULL, kGB>(a, r0, xp, b, acc);
+    if (a.B - b >= 4) {
+        score_group<FULL, 4>(a, r0, xp, b, acc);
+        b += 4;
     }
+    if (a.B - b >= 2) {
+        score_group<FULL, 2>(a, r0, xp, b, acc);
+        b += 2;
+    }
+    if (a.B - b >= 1) score_group<FULL, 1>(a, r0, xp, b, acc);
 }
 
 __device__ inline bool kept_at(const uint32_t* __restrict__ bm, uint64_t p) { return (bm[p >> 5] >> (p & 31)) & 1u; }
 
-struct RowGradLds {
-    uint32_t hist[kGR][257];
-    uint32_t need[kGR], pref[kGR], run[kGR];
-    int32_t d[kGR];
-    uint32_t cnt[2][kGWaves][kGR];
-};
+// the words of the kept bitmap holding column c of the 16 rows (rows past M
+// read row M - 1), and the bits taken out of them once they have arrived
+template <bool FULL>
+__device__ inline void kept_words(const uint32_t* __restrict__ bm, int32_t r0, int32_t M, uint64_t K, int32_t c,
+                                  uint32_t (&w)[kGR])
+{
+#pragma unroll
+    for (int i = 0; i < kGR; ++i) {
+        const int32_t r = FULL ? r0 + i : (r0 + i < M ? r0 + i : M - 1);
+        w[i] = bm[((uint64_t)r * K + (uint64_t)c) >> 5];
+    }
+}
 
 template <bool FULL>
-__device__ void row_grad_block(const RowGradArgs& a, int32_t r0, RowGradLds& sh)
+__device__ inline uint32_t kept_bits(const uint32_t (&w)[kGR], int32_t r0, int32_t M, uint64_t K, int32_t c)
 {
-    auto& hist = sh.hist;
-    auto& s_need = sh.need;
-    auto& s_pref = sh.pref;
-    auto& s_run = sh.run;
-    auto& s_d = sh.d;
-    auto& s_cnt = sh.cnt;
-    const int tid = (int)threadIdx.x, wv = tid / kWave, lane = lane_id();
-    if (tid < kGR) {
-        const int32_t r = r0 + tid;
-        int64_t d = 0;
-        if (r < a.M) d = (int64_t)(a.row_ptr[r + 1] - a.row_ptr[r]) * a.num / a.den;
-        s_d[tid] = (int32_t)d;
-        s_need[tid] = (uint32_t)d;
-        s_pref[tid] = 0u;
-        s_run[tid] = 0u;
-    }
-    __syncthreads();
-    int any = 0;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < kGR; ++i) any |= s_d[i];
-    if (!any) return;
-    const uint64_t K = (uint64_t)a.K;
-    // ---- four digit passes ----
+    for (int i = 0; i < kGR; ++i) {
+        const int32_t r = FULL ? r0 + i : (r0 + i < M ? r0 + i : M - 1);
+        const uint32_t bit = ((uint32_t)r * (uint32_t)K + (uint32_t)c) & 31u;   // low bits of the cell index
+        m |= ((w[i] >> bit) & 1u) << i;
+    }
+    return m;
+}
+
+constexpr int kGS = 512;                  // sampled columns per row (at most)
+constexpr uint32_t kOccupied = 0xFFFFFFFFu;  // sample entry of a cell that is not empty
+
+struct RowGradLds {
+    union {
+        uint32_t hist[kGR][257];    // digit histograms of the passes
+        uint32_t samp[kGR][kGS];    // keys of the sampled cells
+    };
+    uint32_t whist[kGWaves][256];   // one wavefront's histogram of the sample selection
+    uint32_t need[kGR], pref[kGR], run[kGR], lo[kGR];
+    uint32_t base[kGR], span[kGR];   // the key range a pass counts (emit: the lowest key set, and the shift)
+    int32_t live[kGR];
+    int32_t shift[kGR];   // the digits picked so far are key >> shift
+    int32_t open[kGR];    // the row's threshold is not yet resolved
+    int32_t first[kGR];   // the first digit is not yet picked
+    int32_t d[kGR];
+    int64_t e[kGR];       // empty cells of the row
+    uint64_t ties[2][kGWaves][kGR];   // per chunk, wavefront and row: the lanes holding a cell at the threshold
+};
+
+// The rank-th largest (1-based) of the non-occupied keys in a row of the
+// sample: a radix select by one wavefront.
+__device__ inline uint32_t sample_select(const uint32_t* samp, int S, uint32_t rank, uint32_t* h)
+{
+    const int lane = lane_id();
+    uint32_t prefix = 0u;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int q = tid; q < kGR * 257; q += kGThreadsR) (&hist[0][0])[q] = 0u;
-        uint32_t pref[kGR];
-        bool live[kGR];
-#pragma unroll
-        for (int i = 0; i < kGR; ++i) {
-            pref[i] = s_pref[i];
-            live[i] = s_d[i] > 0;
+        for (int q = lane; q < 256; q += kWave) h[q] = 0u;
+        wave_lds_sync();
+        for (int j0 = 0; j0 < S; j0 += kWave) {
+            const int j = j0 + lane;
+            const uint32_t k = j < S ? samp[j] : kOccupied;
+            const bool in = k != kOccupied && (pass == 0 || (k >> (shift + 8 < 32 ? shift + 8 : 31)) == prefix);
+            hist_add(h, in, (k >> shift) & 0xFFu);
         }
-        __syncthreads();
-        for (int32_t c0 = 0; c0 < a.K; c0 += kGThreadsR) {
-            const int32_t c = c0 + tid;
-            const bool valid = c < a.K;
-            float acc[kGR];
-            col_scores<FULL>(a, r0, valid ? c : 0, acc);
-#pragma unroll
-            for (int i = 0; i < kGR; ++i) {
-                if (!live[i]) continue;
-                const uint32_t k = grad_key(acc[i]);
-                const bool empty = valid && !kept_at(a.kept_bm, (uint64_t)(r0 + i) * K + (uint64_t)c);
-                const bool match = empty && (pass == 0 || (k >> (shift + 8 < 32 ? shift + 8 : 31)) == pref[i]);
-                hist_add(hist[i], match, (k >> shift) & 0xFFu);
-            }
-        }
-        __syncthreads();
-        for (int i = wv; i < kGR; i += kGWaves) {
-            if (s_d[i] <= 0) continue;
-            uint32_t dig, rest;
-            pick_digit<false>(hist[i], s_need[i], dig, rest);
-            if (lane == 0) {
-                s_pref[i] = (s_pref[i] << 8) | dig;
-                s_need[i] = rest;
-            }
-        }
-        __syncthreads();
+        wave_lds_sync();
+        uint32_t dig, rest;
+        pick_digit<false>(h, rank, dig, rest);
+        prefix = (prefix << 8) | dig;
+        rank = rest;
+        wave_lds_sync();
     }
-    // ---- set the cells above each row's threshold and the first ties at it ----
-    uint32_t T[kGR], take[kGR];
-    bool live[kGR];
+    return prefix;
+}
+
+// The first digit pass over the row block: the top digit of every empty cell
+// at or above the row's bound.  It meets cells of nearly every row in every
+// chunk, so the kept words are loaded with the operands.  Without a bound
+// (every cell counts) a wavefront's keys carry few distinct top digits: one
+// add per digit; above a bound only a few lanes count: one add per lane.
+template <bool FULL>
+__device__ void sweep_first(const RowGradArgs& a, int32_t r0, RowGradLds& sh)
+{
+    const int tid = (int)threadIdx.x;
+    const uint64_t K = (uint64_t)a.K;
+    // the rows' parameters, uniform for the whole sweep (scalar registers)
+    uint32_t live = 0u, bs[kGR];
 #pragma unroll
     for (int i = 0; i < kGR; ++i) {
-        T[i] = s_pref[i];
-        take[i] = s_need[i];
-        live[i] = s_d[i] > 0;
+        bs[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.base[i]);
+        live |= (uint32_t)(__builtin_amdgcn_readfirstlane(sh.live[i]) != 0) << i;
     }
+    for (int32_t c0 = 0; c0 < a.K; c0 += kGThreadsR) {
+        const int32_t c = c0 + tid;
+        const bool valid = c < a.K;
+        const int32_t cc = valid ? c : 0;
+        uint32_t kw[kGR];
+        kept_words<FULL>(a.kept_bm, r0, a.M, K, cc, kw);
+        float acc[kGR];
+        col_scores<FULL>(a, r0, cc, acc);
+        const uint32_t kept = kept_bits<FULL>(kw, r0, a.M, K, cc);
+#pragma unroll
+        for (int i = 0; i < kGR; ++i) {
+            if (!((live >> i) & 1u)) continue;
+            const uint32_t k = grad_key(acc[i]);
+            const bool in = valid && k >= bs[i];
+            if (!__ballot(in)) continue;
+            const bool match = in && !((kept >> i) & 1u);
+            if (bs[i] == 0u) hist_add(sh.hist[i], match, k >> 24);
+            else if (match) atomicAdd(&sh.hist[i][k >> 24], 1u);
+        }
+    }
+}
+
+// A later digit pass: only the cells whose key has the row's prefix count.
+// The second pass still meets a few cells of most rows in most chunks (the
+// picked top digit spans two binades), so it loads the kept words with the
+// operands; the later ones look a row's word up only when a lane has a cell.
+template <bool FULL, bool UPFRONT>
+__device__ void sweep_later(const RowGradArgs& a, int32_t r0, int shift, RowGradLds& sh)
+{
+    const int tid = (int)threadIdx.x;
+    const uint64_t K = (uint64_t)a.K;
+    uint32_t live = 0u, bs[kGR];
+#pragma unroll
+    for (int i = 0; i < kGR; ++i) {
+        bs[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.base[i]);
+        live |= (uint32_t)(__builtin_amdgcn_readfirstlane(sh.live[i]) != 0) << i;
+    }
+    const uint32_t span = 1u << (shift + 8);
+    for (int32_t c0 = 0; c0 < a.K; c0 += kGThreadsR) {
+        const int32_t c = c0 + tid;
+        const bool valid = c < a.K;
+        const int32_t cc = valid ? c : 0;
+        uint32_t kw[kGR];
+        if (UPFRONT) kept_words<FULL>(a.kept_bm, r0, a.M, K, cc, kw);
+        float acc[kGR];
+        col_scores<FULL>(a, r0, cc, acc);
+        const uint32_t kept = UPFRONT ? kept_bits<FULL>(kw, r0, a.M, K, cc) : 0u;
+#pragma unroll
+        for (int i = 0; i < kGR; ++i) {
+            if (!((live >> i) & 1u)) continue;
+            const uint32_t k = grad_key(acc[i]);
+            const bool in = valid && k - bs[i] < span;
+            if (!__ballot(in)) continue;
+            if (in) {
+                bool emp;
+                if (UPFRONT) {
+                    emp = !((kept >> i) & 1u);
+                } else {
+                    const uint64_t p = (uint64_t)(r0 + i) * K + (uint64_t)c;
+                    emp = !kept_at(a.kept_bm, p);
+                }
+                if (emp) atomicAdd(&sh.hist[i][(k >> shift) & 0xFFu], 1u);
+            }
+        }
+    }
+}
+
+// Per row: a sample of the row's columns gives a lower bound `lo` on its
+// threshold (the sample key whose rank predicts about 4 d + 64 cells above
+// it); the first digit pass counts only the cells at or above it, and a row
+// whose bound was too high takes the first pass again without it.  After each
+// digit pass the row's threshold is a prefix P of the key (key >> shift == P)
+// and `need` cells with that prefix are still to be taken; when the prefix's
+// whole bin is taken the row needs no further pass.  The emit pass sets the
+// empty cells whose prefix is above P and the first `need` with prefix P in
+// column order.  Every pass skips a row's chunk at once when no lane's key
+// falls in the row's range.
+template <bool FULL>
+__device__ void row_grad_block(const RowGradArgs& a, int32_t r0, RowGradLds& sh)
+{
+    const int tid = (int)threadIdx.x, wv = tid / kWave, lane = lane_id();
+    if (tid < kGR) {
+        const int32_t r = r0 + tid;
+        int64_t d = 0, n = 0;
+        if (r < a.M) {
+            n = a.row_ptr[r + 1] - a.row_ptr[r];
+            d = n * a.num / a.den;
+        }
+        sh.d[tid] = (int32_t)d;
+        sh.e[tid] = (int64_t)a.K - (n - d);
+        sh.need[tid] = (uint32_t)d;
+        sh.pref[tid] = 0u;
+        sh.run[tid] = 0u;
+        sh.lo[tid] = 0u;
+        sh.shift[tid] = 31;
+        sh.open[tid] = d > 0 ? 1 : 0;
+        sh.first[tid] = d > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    int anyd = 0;
+#pragma unroll
+    for (int i = 0; i < kGR; ++i) anyd |= sh.d[i];
+    if (!anyd) return;
+    const uint64_t K = (uint64_t)a.K;
+
+    // ---- the sample: columns j K / S, j < S ----
+    const int S = a.K < kGS ? a.K : kGS;
+    for (int j = tid; j < S; j += kGThreadsR) {
+        const int32_t c = (int32_t)(((int64_t)j * a.K) / S);
+        uint32_t kw[kGR];
+        kept_words<FULL>(a.kept_bm, r0, a.M, K, c, kw);
+        float acc[kGR];
+        col_scores<FULL>(a, r0, c, acc);
+        const uint32_t kept = kept_bits<FULL>(kw, r0, a.M, K, c);
+#pragma unroll
+        for (int i = 0; i < kGR; ++i) sh.samp[i][j] = ((kept >> i) & 1u) ? kOccupied : grad_key(acc[i]);
+    }
+    __syncthreads();
+    for (int i = wv; i < kGR; i += kGWaves) {
+        if (sh.d[i] <= 0) continue;
+        uint32_t se = 0u;
+        for (int j = lane; j < S; j += kWave) se += sh.samp[i][j] != kOccupied ? 1u : 0u;
+        se = wave_incl_u32(se);
+        se = (uint32_t)__builtin_amdgcn_readlane((int)se, kWave - 1);
+        const int64_t want = 4 * (int64_t)sh.d[i] + 64;
+        const int64_t r = (want * (int64_t)se + sh.e[i] - 1) / sh.e[i];
+        uint32_t lo = 0u;
+        if (r < (int64_t)se) lo = sample_select(sh.samp[i], S, (uint32_t)r, sh.whist[wv]);
+        if (lane == 0) sh.lo[i] = lo;
+    }
+    __syncthreads();
+
+    // ---- digit passes, most significant first (the first one at most twice) ----
+#pragma unroll 1
+    for (int pass = 0, round = 0; pass < 4;) {
+        const int shift = 24 - 8 * pass;
+        if (tid < kGR) {
+            const int i = tid;
+            sh.live[i] = sh.open[i] != 0 && (pass > 0 || sh.first[i] != 0);
+            if (pass == 0) {
+                sh.base[i] = sh.lo[i];
+                sh.span[i] = 0x80000000u - sh.lo[i];
+            } else {
+                sh.base[i] = sh.pref[i] << (shift + 8);
+                sh.span[i] = 1u << (shift + 8);
+            }
+        }
+        __syncthreads();
+        int any = 0;
+#pragma unroll
+        for (int i = 0; i < kGR; ++i) any |= sh.live[i];
+        if (!any) {
+            if (pass == 0) {   // no row (left) for the first pass
+                pass = 1;
+                round = 1;
+                continue;
+            }
+            break;             // every row is resolved
+        }
+        for (int q = tid; q < kGR * 257; q += kGThreadsR) (&sh.hist[0][0])[q] = 0u;
+        __syncthreads();
+        if (pass == 0) sweep_first<FULL>(a, r0, sh);
+        else if (pass == 1) sweep_later<FULL, true>(a, r0, shift, sh);
+        else sweep_later<FULL, false>(a, r0, shift, sh);
+        __syncthreads();
+        for (int i = wv; i < kGR; i += kGWaves) {
+            if (!sh.live[i]) continue;
+            uint32_t dig, rest, total;
+            pick_digit<false>(sh.hist[i], sh.need[i], dig, rest, &total);
+            if (lane == 0) {
+                if (total < sh.need[i]) {
+                    sh.lo[i] = 0u;   // the bound was too high: the first pass again, over every cell
+                } else {
+                    sh.pref[i] = (sh.pref[i] << 8) | dig;
+                    sh.need[i] = rest;
+                    sh.shift[i] = shift;
+                    sh.first[i] = 0;
+                    // the whole bin is taken: done, unless cells below the bound share it
+                    const bool whole = rest == sh.hist[i][dig] && (pass > 0 || sh.lo[i] == 0u ||
+                                                                   (sh.lo[i] >> 24) < dig);
+                    if (whole || pass == 3) sh.open[i] = 0;
+                }
+            }
+        }
+        __syncthreads();
+        if (pass == 0 && round == 0) {
+            round = 1;   // rows whose bound was too high take the first pass once more
+        } else {
+            ++pass;
+        }
+    }
+    // ---- set the cells above each row's threshold and the first `need` at it ----
+    if (tid < kGR) {
+        sh.base[tid] = sh.pref[tid] << sh.shift[tid];
+        sh.live[tid] = sh.d[tid] > 0;
+    }
+    __syncthreads();
     int par = 0;
     for (int32_t c0 = 0; c0 < a.K; c0 += kGThreadsR, par ^= 1) {
         const int32_t c = c0 + tid;
         const bool valid = c < a.K;
+        const int32_t cc = valid ? c : 0;
         float acc[kGR];
-        col_scores<FULL>(a, r0, valid ? c : 0, acc);
-        uint64_t tm[kGR];
+        col_scores<FULL>(a, r0, cc, acc);
 #pragma unroll
         for (int i = 0; i < kGR; ++i) {
-            tm[i] = 0ull;
-            if (!live[i]) continue;
+            if (!sh.live[i]) continue;
             const uint32_t k = grad_key(acc[i]);
-            const uint64_t p = (uint64_t)(r0 + i) * K + (uint64_t)c;
-            const bool empty = valid && !kept_at(a.kept_bm, p);
-            if (empty && k > T[i]) atomicOr(&a.occ_bm[p >> 5], 1u << (p & 31));
-            tm[i] = __ballot(empty && k == T[i]);
-            if (lane == 0) s_cnt[par][wv][i] = (uint32_t)__popcll(tm[i]);
+            bool in = valid && k >= sh.base[i];
+            uint64_t tm = 0ull;
+            if (__ballot(in)) {
+                const uint64_t p = (uint64_t)(r0 + i) * K + (uint64_t)c;
+                in = in && !kept_at(a.kept_bm, p);
+                const uint32_t kp = k >> sh.shift[i];
+                const uint32_t P = sh.pref[i];
+                if (in && kp > P) atomicOr(&a.occ_bm[p >> 5], 1u << (p & 31));
+                tm = __ballot(in && kp == P);
+            }
+            if (lane == 0) sh.ties[par][wv][i] = tm;
         }
         __syncthreads();
-#pragma unroll
+        // the cells at the threshold: their rank in column order decides
+#pragma unroll 1
         for (int i = 0; i < kGR; ++i) {
-            if (!tm[i]) continue;
-            uint32_t rank = s_run[i];
-            for (int w = 0; w < wv; ++w) rank += s_cnt[par][w][i];
-            rank += (uint32_t)__popcll(tm[i] & lanes_below());
-            if (((tm[i] >> lane) & 1ull) && rank < take[i]) {
+            if (!sh.live[i]) continue;
+            const uint64_t tm = sh.ties[par][wv][i];
+            if (!tm) continue;
+            uint32_t rank = sh.run[i];
+            for (int w = 0; w < wv; ++w) rank += (uint32_t)__popcll(sh.ties[par][w][i]);
+            rank += (uint32_t)__popcll(tm & lanes_below());
+            if (((tm >> lane) & 1ull) && rank < sh.need[i]) {
                 const uint64_t p = (uint64_t)(r0 + i) * K + (uint64_t)c;
                 atomicOr(&a.occ_bm[p >> 5], 1u << (p & 31));
             }
         }
         __syncthreads();
-        if (tid < kGR) {
+        if (tid < kGR && sh.live[tid]) {
             uint32_t add = 0u;
-            for (int w = 0; w < kGWaves; ++w) add += s_cnt[par][w][tid];
-            if (s_d[tid] > 0) s_run[tid] += add;
+            for (int w = 0; w < kGWaves; ++w) add += (uint32_t)__popcll(sh.ties[par][w][tid]);
+            sh.run[tid] += add;
         }
     }
 }
 
-__global__ void __launch_bounds__(kGThreadsR) row_grad_kernel(RowGradArgs a)
+__global__ void __launch_bounds__(kGThreadsR)
+row_grad_kernel(const float* __restrict__ X, const float* __restrict__ dY, const int32_t* __restrict__ row_ptr,
+                const uint32_t* __restrict__ kept_bm, uint32_t* __restrict__ occ_bm, int32_t B, int32_t M, int32_t K,
+                int64_t num, int64_t den)
 {
     __shared__ RowGradLds sh;
+    RowGradArgs a;
+    a.X = X;
+    a.dY = dY;
+    a.row_ptr = row_ptr;
+    a.kept_bm = kept_bm;
+    a.occ_bm = occ_bm;
+    a.B = B;
+    a.M = M;
+    a.K = K;
+    a.num = num;
+    a.den = den;
     const int32_t r0 = (int32_t)blockIdx.x * kGR;
     if (r0 + kGR <= a.M) row_grad_block<true>(a, r0, sh);
     else row_grad_block<false>(a, r0, sh);
@@ -514,7 +767,8 @@ snack_status rows_drop_grow(const RowDst& r, int lds_limit, hipStream_t s)
         g.kept_bm = r.kept_bm;
         g.occ_bm = r.occ_bm;
         const int64_t blocks = ((int64_t)r.M + kGR - 1) / kGR;
-        hipLaunchKernelGGL(row_grad_kernel, dim3((unsigned)blocks), dim3(kGThreadsR), 0, s, g);
+        hipLaunchKernelGGL(row_grad_kernel, dim3((unsigned)blocks), dim3(kGThreadsR), 0, s, g.X, g.dY, g.row_ptr,
+                           g.kept_bm, g.occ_bm, g.B, g.M, g.K, g.num, g.den);
         SNACK_HIP(hipGetLastError());
     }
     return SNACK_OK;
