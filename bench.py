@@ -509,6 +509,21 @@ def config_legs():
                                                      step="drop the smallest |w|, regrow at the empty cells of "
                                                           "largest |dY^T X| for a batch of B rows")
 
+    print("[bench] row-local drop/regrow at 10000x10000, 95 %", file=sys.stderr, flush=True)
+    lay = make(10000, 10000, 95, "c4/s95", seed=2024)
+    rows_leg = {"random_us_per_call": round(_event_us(lambda: L.snack_prune_regrow_rows(
+        lay.h, 3, 10, L.REGROW_RANDOM), 10, warmup=1), 1)}
+    for B in (4, 64):
+        X = torch.from_numpy(normal((B, 10000), f"rigl/X/{B}")).cuda()
+        dY = torch.from_numpy(normal((B, 10000), f"rigl/dY/{B}")).cuda()
+        rows_leg[f"gradient_b{B}_us_per_call"] = round(_event_us(lambda: L.snack_prune_regrow_rows(
+            lay.h, 3, 10, L.REGROW_GRADIENT, X, dY), 5, warmup=1), 1)
+    lay.close()
+    res["n4_row_local_regrow_10000x10000_s95"] = dict(
+        rows_leg, drop="floor(3 n_i / 10) of every row i", step="each row drops its smallest |w| and regrows as "
+                                                                "many cells inside itself (random, or largest "
+                                                                "|dY^T X| for a batch of B rows)")
+
     print("[bench] GPT-2-small MLP stack, 1024 tokens", file=sys.stderr, flush=True)
     c5 = {}
     tokens = 1024
