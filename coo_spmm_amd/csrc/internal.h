@@ -255,6 +255,14 @@ struct MseFuse {
 // layer's workspace
 snack_status spmm_forward(const snack_layer* L, const float* feat_t, const BatchPlan& p, int B, float* out,
                           hipStream_t s, bool rm = false, MseFuse* mse = nullptr, float* part = nullptr);
+// Wide batches (more than one batch tile) over a view whose keys hold few
+// entries (wide.hip): out[b, key] = sum of v * ft[idx, b] over the key's
+// entries (ft feature-major [nidx][bp]), and dW[e] = sum_b dyt[r_e, b] xt[c_e, b]
+bool wide_short(const snack_layer* L, const View& v, const BatchPlan& p);
+snack_status wide_spmm(const snack_layer* L, const View& v, const float* ft, const BatchPlan& p, int B, float* out,
+                       hipStream_t s);
+snack_status wide_sddmm(const snack_layer* L, const float* xt, const float* dyt, const BatchPlan& p, float* dW,
+                        hipStream_t s);
 // bytes of slice partial sums the forward of plan p writes (0: none)
 size_t forward_part_bytes(const snack_layer* L, const BatchPlan& p);
 

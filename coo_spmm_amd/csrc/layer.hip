@@ -368,14 +368,28 @@ snack_status backward_impl(snack_layer* L, const float* X, const float* dY, floa
             L->dwt_for = dW;
             L->dwt_valid = true;
         }
-    } else if (dX && dW && wide_dw_fused(L, p)) {
-        // one column pass for dX and dW over all batch tiles; dW in column order stays for the SGD step
-        SNACK_CHECK(spmm_backward_wide(L, xt, dyt, p, B, dX, dW, L->dwt, ws_dw_slabs(L, p), s));
-        L->dwt_for = dW;
-        L->dwt_valid = true;
     } else {
-        if (dX) SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, nullptr, nullptr, s));
-        if (dW) SNACK_CHECK(sddmm_dw_tiles(L, xt, dyt, p, dW, s));
+        // short keys: a pass of its own for each of dX and dW
+        const bool wx = dX && wide_short(L, L->tr, p), ww = dW && wide_short(L, L->fwd, p);
+        if (!wx && !ww && dX && dW && wide_dw_fused(L, p)) {
+            // one column pass for dX and dW over all batch tiles; dW in column order stays for the SGD step
+            SNACK_CHECK(spmm_backward_wide(L, xt, dyt, p, B, dX, dW, L->dwt, ws_dw_slabs(L, p), s));
+            L->dwt_for = dW;
+            L->dwt_valid = true;
+        } else {
+            if (wx) {
+                ProfScope prof(KC_SPMM_DX, s);
+                SNACK_CHECK(wide_spmm(L, L->tr, dyt, p, B, dX, s));
+            } else if (dX) {
+                SNACK_CHECK(spmm_backward_fused(L, xt, dyt, p, B, dX, nullptr, nullptr, s));
+            }
+            if (ww) {
+                ProfScope prof(KC_SDDMM_DW, s);
+                SNACK_CHECK(wide_sddmm(L, xt, dyt, p, dW, s));
+            } else if (dW) {
+                SNACK_CHECK(sddmm_dw_tiles(L, xt, dyt, p, dW, s));
+            }
+        }
     }
     return SNACK_OK;
 }

@@ -2607,6 +2607,7 @@ snack_status spmm_forward(const snack_layer* L, const float* feat_t, const Batch
 {
     ProfScope prof(KC_SPMM_FWD, s);
     if (rm) return launch_keyed<false>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, true, nullptr, 0.0f, mse);
+    if (wide_short(L, L->fwd, p)) return wide_spmm(L, L->fwd, feat_t, p, B, out, s);
     if (use_tile_spmm(L, L->fwd, p))
         return launch_tile<false, true>(p, L, L->fwd, feat_t, nullptr, out, nullptr, B, s, nullptr, 0.0f, mse, part);
     if (use_keyed(L->fwd, L->nnz, p) || keyed_lds(L, L->fwd, p))
