@@ -470,9 +470,9 @@ snack_status build_idx16(snack_layer* L, hipStream_t s)
     return SNACK_OK;
 }
 
-snack_status canon_index_tail(snack_layer* L, hipStream_t s)
+snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done)
 {
-    SNACK_CHECK(build_idx16(L, s));
+    if (!idx16_done) SNACK_CHECK(build_idx16(L, s));
     L->vals_t_stale = false;
     for (int i = 0; i < kTileWidths; ++i) {
         L->fwd.split[i].valid = false;

@@ -129,7 +129,8 @@ struct snack_layer {
     void* scratch = nullptr;
     size_t scratch_bytes = 0;
     int32_t* flag = nullptr;      // device error / count word(s)
-    uint32_t* host_res = nullptr; // pinned words the drop/regrow grow result is copied into
+    uint32_t* host_res = nullptr; // coherent pinned words the drop/regrow's grow result is written into
+    uint32_t* host_res_dev = nullptr; // the same words as the device addresses them
     hipEvent_t grow_ev = nullptr; // recorded after that copy
 
     size_t device_bytes = 0;
@@ -204,8 +205,9 @@ snack_status canon_sort_input(snack_layer* L, const int32_t* rows, const int32_t
 // and both work partitions.
 snack_status canon_build_index(snack_layer* L, hipStream_t s);
 // The part of canon_build_index after row_ptr and the transposed view exist
-// (for callers that build those themselves): partitions of both views, flags.
-snack_status canon_index_tail(snack_layer* L, hipStream_t s);
+// (for callers that build those themselves): partitions of both views, flags,
+// and the 16-bit index copies unless the caller wrote them (idx16_done).
+snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done = false);
 // vals_t[iperm[k]] = vals[k]
 snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
 // the views' 16-bit index copies from their 32-bit indices (where allocated)

@@ -277,10 +277,12 @@ extern "C" snack_status snack_layer_create(int32_t M, int32_t K, int64_t nnz, co
         if (_s != SNACK_OK) return fail(_s);
         L->scratch_bytes = scr;
     }
-    if (hipHostMalloc((void**)&L->host_res, 64, hipHostMallocDefault) != hipSuccess) {
+    // coherent pinned words the drop/regrow's kernels write its result into (system-scope stores)
+    if (hipHostMalloc((void**)&L->host_res, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
         L->host_res = nullptr;
         return fail(SNACK_ERR_ALLOC);
     }
+    if (hipHostGetDevicePointer((void**)&L->host_res_dev, L->host_res, 0) != hipSuccess) return fail(SNACK_ERR_HIP);
     if (hipEventCreateWithFlags(&L->grow_ev, hipEventDisableTiming) != hipSuccess) {
         L->grow_ev = nullptr;
         return fail(SNACK_ERR_HIP);

@@ -632,7 +632,19 @@ __global__ void __launch_bounds__(256) tile_sum_kernel(const uint8_t* __restrict
     }
 }
 
-__device__ inline int32_t block_incl_1024(int32_t v, int32_t* smem /*[16]*/)
+// The first `need` accepted candidates in index order are taken, and the
+// accepted ones at or past the cut give their cell back (few: the batch is
+// sized to overshoot need only slightly).  Every workgroup finds the cut
+// itself -- from the tile counts, then the flags of the tile where the
+// running count reaches need -- so no launch of its own is spent on it.
+// Workgroup 0 records how many were taken (state[kStTaken]; all when fewer
+// than need were accepted) and writes the batch's result words (overflow,
+// taken) to the host (`res`, mapped pinned memory, stored at system scope).
+constexpr int kCutThreads = 256;
+static_assert(kMaxBatch / kSumTile <= 4 * kCutThreads, "four tile counts per thread");
+static_assert(kSumTile == 32 * kCutThreads, "32 flags of the cut tile per thread");
+
+__device__ inline int32_t block_incl_256(int32_t v, int32_t* smem /*[4]*/)
 {
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     int32_t inc = wave_incl(v);
@@ -644,64 +656,86 @@ __device__ inline int32_t block_incl_1024(int32_t v, int32_t* smem /*[16]*/)
     return base + inc;
 }
 
-// The first `need` accepted candidates in index order are taken: state[kStCut]
-// is one past the last one taken (T when every accepted one is), state[kStTaken]
-// how many were taken.
-__global__ void __launch_bounds__(1024) cut_kernel(const int32_t* __restrict__ tsum, int32_t ntiles,
-                                                   const uint8_t* __restrict__ acc8, int64_t T, int64_t need,
-                                                   uint32_t* __restrict__ state)
+__global__ void __launch_bounds__(kCutThreads) cut_give_back_kernel(
+    uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N, const int32_t* __restrict__ tsum,
+    int32_t ntiles, int64_t need, const uint8_t* __restrict__ acc8, uint32_t* __restrict__ occ_bm,
+    uint32_t* __restrict__ state, uint32_t* __restrict__ res)
 {
-    __shared__ int32_t smem[1024 / kWave];
-    __shared__ int32_t s_j, s_q, s_cut;
+    __shared__ int32_t smem[kCutThreads / kWave];
+    __shared__ int32_t s_j, s_q, s_cut, s_all;
+    const int tid = threadIdx.x;
     if (state[kStOverflow]) {
-        if (threadIdx.x == 0) state[kStTaken] = 0u;
+        if (blockIdx.x == 0 && tid == 0) {
+            state[kStTaken] = 0u;
+            __hip_atomic_store(&res[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&res[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
         return;
     }
-    const int tid = threadIdx.x;
-    const int32_t v = tid < ntiles ? tsum[tid] : 0;
-    const int32_t inc = block_incl_1024(v, smem);
+    // the tile where the running count first reaches need (four consecutive tiles per thread)
+    int32_t v[4], loc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int ti = 4 * tid + u;
+        v[u] = ti < ntiles ? tsum[ti] : 0;
+        loc += v[u];
+    }
+    const int32_t inc = block_incl_256(loc, smem);
     if (tid == 0) s_j = -1;
+    if (tid == kCutThreads - 1) s_all = inc;
     __syncthreads();
-    // the tile where the running count first reaches need
-    if (tid < ntiles && (int64_t)inc >= need && (int64_t)(inc - v) < need) {
-        s_j = tid;
-        s_q = (int32_t)(need - (inc - v));
+    {
+        int32_t run = inc - loc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if ((int64_t)(run + v[u]) >= need && (int64_t)run < need) {
+                s_j = 4 * tid + u;
+                s_q = (int32_t)(need - run);
+            }
+            run += v[u];
+        }
     }
     __syncthreads();
     const int32_t j = s_j;
-    if (j < 0) {   // fewer than need accepted: take them all
-        if (tid == 1023) {
-            state[kStTaken] = (uint32_t)inc;
-            state[kStCut] = (uint32_t)T;
-        }
-        return;
-    }
-    // the q-th accepted flag of tile j; each thread reads eight consecutive flags
-    const int32_t q = s_q;
-    const int64_t b0 = (int64_t)j * kSumTile;
-    const int64_t lo = b0 + 8 * tid;
-    uint8_t f[8];
-    int32_t cnt = 0;
+    int64_t cut = T;
+    uint32_t taken = (uint32_t)need;
+    if (j < 0) {
+        taken = (uint32_t)s_all;   // fewer than need accepted: all are taken
+    } else {
+        // the q-th accepted flag of tile j: 32 consecutive flags per thread
+        const int32_t q = s_q;
+        const int64_t lo = (int64_t)j * kSumTile + 32 * tid;
+        uint8_t f[32];
+        int32_t cnt = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        f[u] = lo + u < T ? acc8[lo + u] : 0;
-        cnt += f[u];
-    }
-    const int32_t ci = block_incl_1024(cnt, smem);
-    if (ci >= q && ci - cnt < q) {
-        int32_t k = ci - cnt;
-        for (int u = 0; u < 8; ++u) {
-            k += f[u];
-            if (f[u] && k == q) {
-                s_cut = (int32_t)(lo + u + 1);
-                break;
+        for (int u = 0; u < 32; ++u) {
+            f[u] = lo + u < T ? acc8[lo + u] : 0;
+            cnt += f[u];
+        }
+        const int32_t ci = block_incl_256(cnt, smem);
+        if (ci >= q && ci - cnt < q) {
+            int32_t k = ci - cnt;
+            for (int u = 0; u < 32; ++u) {
+                k += f[u];
+                if (f[u] && k == q) {
+                    s_cut = (int32_t)(lo + u + 1);
+                    break;
+                }
             }
         }
+        __syncthreads();
+        cut = s_cut;
     }
-    __syncthreads();
-    if (tid == 0) {
-        state[kStTaken] = (uint32_t)need;
-        state[kStCut] = (uint32_t)s_cut;
+    if (blockIdx.x == 0 && tid == 0) {
+        state[kStTaken] = taken;
+        state[kStCut] = (uint32_t)cut;
+        __hip_atomic_store(&res[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&res[1], taken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    for (int64_t i = cut + (int64_t)blockIdx.x * kCutThreads + tid; i < T; i += (int64_t)gridDim.x * kCutThreads) {
+        if (!acc8[i]) continue;
+        const uint64_t p = candidate_pos(seed, epoch, t0 + (uint64_t)i, N);
+        atomicAnd(&occ_bm[p >> 5], ~(1u << (p & 31)));
     }
 }
 
@@ -715,21 +749,6 @@ __global__ void occ_guard_kernel(const uint32_t* __restrict__ state, uint32_t ne
     if (state[kStOverflow] == 0u && state[kStTaken] == need) return;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x)
         occ_bm[w] = old_bm[w];
-}
-
-// accepted candidates at or past the cut give their cell back (few: the batch
-// is sized to overshoot need only slightly)
-__global__ void give_back_kernel(uint64_t seed, uint64_t epoch, uint64_t t0, int64_t T, uint64_t N,
-                                 const uint8_t* __restrict__ acc8, uint32_t* __restrict__ occ_bm,
-                                 const uint32_t* __restrict__ state)
-{
-    if (state[kStOverflow]) return;
-    const int64_t cut = (int64_t)state[kStCut];
-    for (int64_t i = cut + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T; i += (int64_t)gridDim.x * blockDim.x) {
-        if (!acc8[i]) continue;
-        const uint64_t p = candidate_pos(seed, epoch, t0 + (uint64_t)i, N);
-        atomicAnd(&occ_bm[p >> 5], ~(1u << (p & 31)));
-    }
 }
 
 struct GrowPlan {
@@ -813,7 +832,8 @@ constexpr int kEmitList = 512;   // entries per wave
 
 __device__ inline void emit_flush(const int32_t* lr, const int32_t* lc, const int32_t* ls, int32_t n, int64_t out0,
                                   int64_t nnz, const float* __restrict__ vold, int32_t* __restrict__ rows,
-                                  int32_t* __restrict__ cols, float* __restrict__ vals, int lane)
+                                  int32_t* __restrict__ cols, float* __restrict__ vals, uint16_t* __restrict__ cols16,
+                                  int lane)
 {
     if ((int64_t)n > nnz - out0) n = (int32_t)(nnz - out0);   // never past the triple (occ holds nnz bits)
     __builtin_amdgcn_wave_barrier();
@@ -832,6 +852,7 @@ __device__ inline void emit_flush(const int32_t* lr, const int32_t* lc, const in
             if (i < n) {
                 rows[out0 + i] = lr[i];
                 cols[out0 + i] = lc[i];
+                if (cols16) cols16[out0 + i] = (uint16_t)lc[i];
                 vals[out0 + i] = src[q] >= 0 ? v[q] : 0.0f;
             }
         }
@@ -844,7 +865,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, const uint32_t* __restrict__ old_bm,
     int64_t words, int64_t units, const int32_t* __restrict__ occ_cnt, const int32_t* __restrict__ old_cnt,
     const float* __restrict__ vold, int64_t nnz, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
-    float* __restrict__ vals, int32_t* __restrict__ wpre)
+    float* __restrict__ vals, int32_t* __restrict__ wpre, uint16_t* __restrict__ cols16)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
@@ -927,7 +948,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         // the list takes this sweep if it fits (sweeps of a dense layer may not)
         const bool listed = ta <= kEmitList;
         if (nl > 0 && (!listed || nl + ta > kEmitList)) {
-            emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, lane);
+            emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, cols16, lane);
             nl = 0;
         }
         if (listed && nl == 0) lout0 = sweep0;
@@ -965,12 +986,13 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
             } else {
                 rows[out] = (int32_t)r;
                 cols[out] = (int32_t)c;
+                if (cols16) cols16[out] = (uint16_t)c;
                 vals[out] = src >= 0 ? vold[src] : 0.0f;
             }
             ++out;
         }
     }
-    if (nl > 0) emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, lane);
+    if (nl > 0) emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, cols16, lane);
 }
 
 // ---- the column view from the new bitmap -----------------------------------
@@ -1189,7 +1211,7 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     const uint32_t* __restrict__ occ_bm, uint64_t words, const int32_t* __restrict__ wpre, int32_t M, int32_t K,
     int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ col_ptr,
     const float* __restrict__ vals, int32_t* __restrict__ rows_t, float* __restrict__ vals_t,
-    int32_t* __restrict__ iperm, CvTabs tabs)
+    int32_t* __restrict__ iperm, CvTabs tabs, uint16_t* __restrict__ rows_t16)
 {
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
     __shared__ uint32_t colbits[kCvDim * kCvPad];
@@ -1314,6 +1336,7 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
             const int32_t loc = eloc[e];
             const int32_t kt = colbase[c] + (e - colstart[c]);
             rows_t[kt] = t.r0 + xrow[loc];
+            if (rows_t16) rows_t16[kt] = (uint16_t)(t.r0 + xrow[loc]);
             vals_t[kt] = sval[loc];
             sslot[loc] = kt;
         }
@@ -1340,6 +1363,7 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
         const int ci = c >> 5;
         const int32_t k = rowk[rr] + rwp[rr * kCvWords + ci] + __popc(rowbits[rr * kCvPad + ci] & ((1u << (c & 31)) - 1u));
         rows_t[kt] = t.r0 + rr;
+        if (rows_t16) rows_t16[kt] = (uint16_t)(t.r0 + rr);
         vals_t[kt] = vals[k];
         iperm[k] = kt;
     }
@@ -1462,6 +1486,9 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
 {
     const int64_t nnz = L->nnz;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
+    // with the column view built from the bitmap, the 16-bit index copies are written beside the
+    // indices (only their first nnz slots change: the padding past nnz never does)
+    const bool idx16_here = cv_from_bitmap(L);
     // ---- new canonical arrays: set bits of occ in ascending position ----
     {
         const int64_t nu = ps.units;
@@ -1479,7 +1506,7 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
         auto emit = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm, ps.old_bm,
                                ps.words, nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals,
-                               wpre);
+                               wpre, idx16_here ? L->fwd.idx16 : nullptr);
         };
         if (direct) {
             if (wide) emit(emit_units_kernel<true, true>);
@@ -1511,9 +1538,9 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
         }
         hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm, words,
                            ps.wpre, M, K, nbi, nbj, ps.cvcnt, L->col_ptr, L->vals, L->rows_t, L->vals_t, L->iperm,
-                           tabs);
+                           tabs, L->tr.idx16);
         SNACK_HIP(hipGetLastError());
-        SNACK_CHECK(canon_index_tail(L, s));
+        SNACK_CHECK(canon_index_tail(L, s, /*idx16_done=*/true));
         for (int w = 0; w < kTileWidths; ++w) {
             if (tabs.rtab[w]) L->fwd.split[w].valid = true;
             if (tabs.ctab[w]) L->tr.split[w].valid = true;
@@ -1616,13 +1643,11 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
                            words_total, g.cap, ps.fill, ps.bucket, claimed ? ps.occ_bm : ps.kept_bm, ps.occ_bm,
                            ps.acc8, ps.state);
         hipLaunchKernelGGL(tile_sum_kernel, dim3((unsigned)nsum), dim3(256), 0, s, ps.acc8, T, ps.tsum, ps.state);
-        hipLaunchKernelGGL(cut_kernel, dim3(1), dim3(1024), 0, s, ps.tsum, nsum, ps.acc8, T, need, ps.state);
-        hipLaunchKernelGGL(give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kThreads), 0, s,
-                           L->seed, L->epoch, t0, T, N, ps.acc8, ps.occ_bm, ps.state);
+        // the cut, the give-back and the result words (overflow, taken) written to the host
+        hipLaunchKernelGGL(cut_give_back_kernel, dim3(grid_for(T) < 256u ? grid_for(T) : 256u), dim3(kCutThreads), 0,
+                           s, L->seed, L->epoch, t0, T, N, ps.tsum, nsum, need, ps.acc8, ps.occ_bm, ps.state,
+                           L->host_res_dev);
         SNACK_HIP(hipGetLastError());
-        // overflow flag, taken
-        SNACK_HIP(hipMemcpyAsync(L->host_res, ps.state + kStOverflow, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost,
-                                 s));
         SNACK_HIP(hipEventRecord(L->grow_ev, s));
         const bool queued = speculate;
         if (queued) {
@@ -1633,7 +1658,8 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
             speculate = false;
         }
         SNACK_HIP(hipEventSynchronize(L->grow_ev));
-        const uint32_t res[2] = {L->host_res[0], L->host_res[1]};
+        const volatile uint32_t* hr = L->host_res;
+        const uint32_t res[2] = {hr[0], hr[1]};
         if (++batches > 100000) return SNACK_ERR_UNSUPPORTED;
         if (queued) {
             if (res[0] == 0u && (int64_t)res[1] == need) {

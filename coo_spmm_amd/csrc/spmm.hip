@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(WPB * kWave) seg_kernel(RoleArgs ra, RoleArgs 
     extern __shared__ __align__(16) float xs_dyn[];   // the gathered operand, when staged in LDS
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = (int)(threadIdx.x / kWave);
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // uniform: scalar work below
     int bid = (int)blockIdx.x;
     const bool role_a = bid < grid_a;
     if (!role_a) bid -= grid_a;
@@ -773,7 +773,7 @@ __global__ void __launch_bounds__(kBlock) key_kernel(RoleArgs A, int bp, int B)
     const int bid = (int)blockIdx.x;
     const int vb = (bid % kXcd) * A.per_xcd + bid / kXcd;
     if (vb >= A.nblocks) return;
-    const int c = vb * kWavesPerBlock + (int)(threadIdx.x / kWave);
+    const int c = vb * kWavesPerBlock + uni((int)(threadIdx.x / kWave));   // uniform: scalar loads of the chunk
     if (c >= A.nchunks) return;
     key_chunk<BT, NB, U, DW, SPMM, VAL>(A, c, A.G, bp, B);
 }
