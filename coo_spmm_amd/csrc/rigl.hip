@@ -225,21 +225,67 @@ __global__ void grad_copy_kernel(const uint32_t* __restrict__ src, uint32_t* __r
 }
 
 // the digit of pass `pass` that holds the need-th best key, counting from the
-// largest digit down; need becomes the rank within that digit (one thread:
-// at most 4096 bins)
-__global__ void grad_pick_kernel(uint32_t* __restrict__ state, const uint32_t* __restrict__ hist, int pass)
+// largest digit down; need becomes the rank within that digit.  One
+// workgroup: each thread four consecutive bins from the top, a scan of their
+// sums finds the first digit (from the top, above 0) where the count reaches
+// need; digit 0 takes what is left when none does.
+constexpr int kPickThreads = 1024;
+static_assert(kH2 <= 4 * kPickThreads, "four bins per thread");
+
+__global__ void __launch_bounds__(kPickThreads) grad_pick_kernel(uint32_t* __restrict__ state,
+                                                                 const uint32_t* __restrict__ hist, int pass)
 {
-    if (threadIdx.x != 0) return;
+    __shared__ uint32_t wsum[kPickThreads / kWave];
+    __shared__ uint32_t s_found, s_t, s_rest;
     const int nb = pass == 1 ? kH1 : (pass == 2 ? kH2 : kH3);
     const uint32_t* h = hist + (pass == 1 ? 0 : (pass == 2 ? kH1 : kH1 + kH2));
-    uint32_t need = state[kSNeed];
-    int t = nb - 1;
-    for (; t > 0; --t) {
-        if (h[t] >= need) break;
-        need -= h[t];
+    const uint32_t need = state[kSNeed];
+    const int tid = (int)threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    uint32_t c[4];
+    int t[4];
+    uint32_t sum = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        t[j] = nb - 1 - (4 * tid + j);
+        c[j] = t[j] >= 1 ? h[t[j]] : 0u;
+        sum += c[j];
     }
-    state[pass == 1 ? kST1 : (pass == 2 ? kST2 : kST3)] = (uint32_t)t;
-    state[kSNeed] = need;
+    uint32_t inc = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) wsum[w] = inc;
+    if (tid == 0) s_found = 0u;
+    __syncthreads();
+    uint32_t base = 0u, total = 0u;
+    for (int i = 0; i < kPickThreads / kWave; ++i) {
+        if (i < w) base += wsum[i];
+        total += wsum[i];
+    }
+    inc += base;
+    const uint32_t excl = inc - sum;
+    if (excl < need && inc >= need) {   // exactly one thread
+        uint32_t r = need - excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (c[j] >= r) {
+                s_t = (uint32_t)t[j];
+                s_rest = r;
+                break;
+            }
+            r -= c[j];
+        }
+        s_found = 1u;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t tt = s_found ? s_t : 0u;
+        const uint32_t rest = s_found ? s_rest : need - total;
+        state[pass == 1 ? kST1 : (pass == 2 ? kST2 : kST3)] = tt;
+        state[kSNeed] = rest;
+    }
 }
 
 }  // namespace
@@ -269,11 +315,11 @@ snack_status grow_by_gradient(const snack_layer* L, const GradGrow& g, hipStream
         hipLaunchKernelGGL(grad_copy_kernel, dim3((unsigned)nb), dim3(256), 0, s, g.kept_bm, g.occ_bm, g.words);
     }
     hipLaunchKernelGGL(grad_cells_kernel<kHist1>, grid, block, 0, s, a);
-    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(64), 0, s, g.state, g.hist, 1);
+    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(kPickThreads), 0, s, g.state, g.hist, 1);
     hipLaunchKernelGGL(grad_cells_kernel<kHist2>, grid, block, 0, s, a);
-    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(64), 0, s, g.state, g.hist, 2);
+    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(kPickThreads), 0, s, g.state, g.hist, 2);
     hipLaunchKernelGGL(grad_cells_kernel<kHist3>, grid, block, 0, s, a);
-    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(64), 0, s, g.state, g.hist, 3);
+    hipLaunchKernelGGL(grad_pick_kernel, dim3(1), dim3(kPickThreads), 0, s, g.state, g.hist, 3);
     hipLaunchKernelGGL(grad_cells_kernel<kMark>, grid, block, 0, s, a);
     SNACK_HIP(hipGetLastError());
     SNACK_CHECK(exclusive_scan_i32(g.tie_cnt, g.tie_cnt, (int64_t)L->M * a.nct, nullptr, g.scan, s));
