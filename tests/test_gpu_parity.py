@@ -67,6 +67,27 @@ def test_long_keys_wide_batches(M, K, nnz):
     _check_layer_vs_oracle(M, K, nnz, (1, 2, 3, 4, 5, 8, 9, 16, 24, 32, 40, 64, 65), f"gpu/longkeys/{M}x{K}")
 
 
+def test_wide_batches_over_skewed_short_keys():
+    # more than one 64-column batch tile over views whose keys average few entries (the wide-batch
+    # short-key passes), with a skewed degree: three rows and three columns far longer than the rest,
+    # most rows and columns empty, and batches that end inside a 64-column block
+    from snack_inputs import rng_for
+    M, K = 700, 500
+    g = rng_for("gpu/wide/skew")
+    pos = set()
+    for r in (3, 350, 699):                      # long rows
+        pos.update(r * K + int(c) for c in g.choice(K, 300, replace=False))
+    for c in (0, 250, 499):                      # long columns
+        pos.update(int(r) * K + c for r in g.choice(M, 400, replace=False))
+    for p in g.choice(M * K, 1500, replace=False):   # a sprinkle elsewhere
+        pos.add(int(p))
+    pos = np.array(sorted(pos), np.int64)
+    rows, cols = (pos // K).astype(np.int32), (pos % K).astype(np.int32)
+    vals = normal((pos.shape[0],), "gpu/wide/skew/v")
+    _check_layer_vs_oracle(M, K, pos.shape[0], (65, 100, 128, 191, 257), "gpu/wide/skew",
+                           triple=(rows, cols, vals))
+
+
 def test_slice_tiled_several_batch_tiles():
     # long keys with operands of three and four slices per view; at 449 and 500
     # columns (eight 64-column tiles, the first with a last tile of one column)
