@@ -1148,14 +1148,14 @@ __device__ inline void tile_h(const float* __restrict__ H, int64_t key, int bp, 
     }
 }
 
+// The slice-tiled pass of one workgroup: `bid` of `nwg` workgroups of the role
+// (a multiple of kXcd), over batch tile `tile`.
 template <int BT, int NB, int U, int D, bool DW, bool SPMM, bool VAL = SPMM>
-__global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, TileArgs T, int bp, int B)
+__device__ __forceinline__ void tile_body(RoleArgs A, const TileArgs& T, int bp, int B, int bid, int nwg, int tile)
 {
     constexpr int BTILE = BT * NB;
     using TB = TileBlock<BT, U>;
     extern __shared__ __align__(16) float gs_dyn[];
-    const int nwg = (int)gridDim.x;
-    const int bid = (int)blockIdx.x;
     const int per = nwg / kXcd;   // the grid is a multiple of kXcd
     // workgroups of one XCD take consecutive (slice, key block) pairs: they share slices in L2
     const int lg = (bid % kXcd) * per + bid / kXcd;
@@ -1165,7 +1165,6 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
     const int nkeys = A.nkeys;
     // batch tile (grid dimension y); over several tiles, a dW pass reads the
     // tile's columns of the key's row and writes the tile's own dW slab
-    const int tile = (int)blockIdx.y;
     if constexpr (DW) {
         A.H += (int64_t)tile * BTILE;
         A.dwo += (int64_t)tile * T.dwstride;
@@ -1274,6 +1273,26 @@ __global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, Ti
         }
         if (!d[0].valid()) break;
     }
+}
+
+template <int BT, int NB, int U, int D, bool DW, bool SPMM, bool VAL = SPMM>
+__global__ void __launch_bounds__(kTileWaves * kWave) tile_kernel(RoleArgs A, TileArgs T, int bp, int B)
+{
+    tile_body<BT, NB, U, D, DW, SPMM, VAL>(A, T, bp, B, (int)blockIdx.x, (int)gridDim.x, (int)blockIdx.y);
+}
+
+// The backward's two slice-tiled passes of one batch tile in one launch: the
+// first g0 workgroups the column pass (dX partial sums; the column-ordered
+// values stepped in place from the dW they compute), the rest the row pass
+// (dW in canonical order; the canonical values stepped in place).  Neither
+// reads what the other writes.
+template <int BT, int NB, int U, int D>
+__global__ void __launch_bounds__(kTileWaves * kWave)
+    tile_bwd_kernel(RoleArgs Ac, TileArgs Tc, RoleArgs Ar, TileArgs Tr, int g0, int bp, int B)
+{
+    const int bid = (int)blockIdx.x;
+    if (bid < g0) tile_body<BT, NB, U, D, true, true, true>(Ac, Tc, bp, B, bid, g0, 0);
+    else tile_body<BT, NB, U, D, true, false, true>(Ar, Tr, bp, B, bid - g0, (int)gridDim.x - g0, 0);
 }
 
 // ---- streamed kernel for batch tiles of 1 to 4 columns, operand in LDS ----
@@ -2465,6 +2484,81 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     return SNACK_OK;
 }
 
+// The backward's two slice-tiled passes at one batch tile in one launch (see
+// tile_bwd_kernel), then the column pass's slice reduction into dX.  The
+// column pass steps vals_t and writes no dW; the row pass writes the canonical
+// dW and steps vals.
+snack_status launch_tile_bwd2(const BatchPlan& p, const snack_layer* L, const float* dyt, const float* xt, float* dX,
+                              float* dW, float lr, int B, hipStream_t s)
+{
+    if (p.ntiles != 1) return SNACK_ERR_INVALID_ARG;
+    const int w = tile_index(p.btile);
+    SNACK_CHECK(ensure_split(L->tr, w, s));
+    SNACK_CHECK(ensure_split(L->fwd, w, s));
+    auto setup = [&](const View& v, const float* G, const float* H, float* out, float* dwo, float* apply, bool spmm,
+                     RoleArgs& a, TileArgs& t, int64_t& nwg, size_t& lds) {
+        const SplitTab& st = v.split[w];
+        a = role_for(v, G, H, out, dwo, kWavesPerBlock, L->cap);
+        a.apply = apply;
+        a.lr = lr;
+        t.S = st.S;
+        t.tab = st.S >= 2 ? st.tab : v.ptr;
+        t.tstride = st.S >= 2 ? v.nkeys : 1;
+        t.dwstride = 0;
+        t.part = (st.S >= 2 && spmm) ? ws_part(L, p) : nullptr;
+        t.pstride = (int64_t)t.S * v.nkeys * p.btile;
+        t.KB = tile_key_blocks(L, v, t.S, p.ntiles);
+        t.R = (v.nkeys + t.KB - 1) / t.KB;
+        nwg = (int64_t)t.S * t.KB;
+        nwg = (nwg + kXcd - 1) / kXcd * kXcd;
+        const int32_t rows = (v.nidx + t.S - 1) / t.S + 1;   // the slice and a zero row
+        lds = (size_t)rows * p.btile * sizeof(float);
+    };
+    RoleArgs ac, ar;
+    TileArgs tc, tr;
+    int64_t nc, nr;
+    size_t lc, lr_;
+    setup(L->tr, dyt, xt, dX, nullptr, L->vals_t, true, ac, tc, nc, lc);
+    setup(L->fwd, xt, dyt, nullptr, dW, L->vals, false, ar, tr, nr, lr_);
+    const size_t lds = lc > lr_ ? lc : lr_;
+    const dim3 grid((unsigned)(nc + nr), 1), block(kTileWaves * kWave);
+    constexpr int Dp = kTileDepthDw;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, ac, tc, ar, tr, (int)nc, p.bp, B); };
+    switch (p.btile) {
+    case 8: go(tile_bwd_kernel<2, 4, 2, Dp>); break;
+    case 16: go(tile_bwd_kernel<4, 4, 4, Dp>); break;
+    case 32: go(tile_bwd_kernel<4, 8, 4, Dp>); break;
+    case 64: go(tile_bwd_kernel<16, 4, 4, Dp>); break;
+    default: return SNACK_ERR_INVALID_ARG;
+    }
+    SNACK_HIP(hipGetLastError());
+    if (tc.part) {
+        const MseOut mo{nullptr, nullptr, nullptr, 0.0f};
+        const View& v = L->tr;
+        auto rg = [&](int kpb) { return dim3((unsigned)((v.nkeys + kpb - 1) / kpb), 1u); };
+        switch (p.btile) {
+        case 8:
+            hipLaunchKernelGGL((split_reduce_kernel<8>), rg(kSplitReduceKeys<8>), dim3(256), 0, s, tc.part, tc.S,
+                               v.nkeys, B, dX, mo);
+            break;
+        case 16:
+            hipLaunchKernelGGL((split_reduce_kernel<16>), rg(kSplitReduceKeys<16>), dim3(256), 0, s, tc.part, tc.S,
+                               v.nkeys, B, dX, mo);
+            break;
+        case 32:
+            hipLaunchKernelGGL((split_reduce_kernel<32>), rg(kSplitReduceKeys<32>), dim3(256), 0, s, tc.part, tc.S,
+                               v.nkeys, B, dX, mo);
+            break;
+        default:
+            hipLaunchKernelGGL((split_reduce_kernel<64>), rg(kSplitReduceKeys<64>), dim3(256), 0, s, tc.part, tc.S,
+                               v.nkeys, B, dX, mo);
+            break;
+        }
+        SNACK_HIP(hipGetLastError());
+    }
+    return SNACK_OK;
+}
+
 }  // namespace
 
 int tile_splits(const snack_layer* L, const View& v, int btile)
@@ -2718,6 +2812,14 @@ snack_status spmm_backward_fused(const snack_layer* L, const float* xt, const fl
     }
     if (dW && dW_t && p.ntiles == 1 && use_keyed(L->tr, L->nnz, p)) {
         const bool recompute = recompute_dw(L, p);
+        if (step && recompute && use_tile(L, L->tr, p) && use_tile(L, L->fwd, p)) {
+            // both slice-tiled passes in one launch (counted as the column pass), each stepping its values
+            ProfScope prof(KC_SPMM_DX, s);
+            SNACK_CHECK(launch_tile_bwd2(p, L, dyt, xt, dX, dW, step->lr, B, s));
+            step->done = true;
+            step->canon_done = true;
+            return SNACK_OK;
+        }
         // with the step the column pass steps vals_t in place; where the canonical dW is permuted from the
         // column order, the canonical values then take their step in a separate pass (cheaper than in the
         // permutation, which waits on memory)
