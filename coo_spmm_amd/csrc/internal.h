@@ -41,6 +41,7 @@ enum KernelClass : int {
 // whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
 // change of the index.
 constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
+constexpr int kMaxSplits = 64;   // most slices of one table
 // one SGD step on one value: v - lr * g with a single rounding; every update of
 // either value copy goes through it, so the two copies stay bit-identical
 __device__ inline float sgd_value(float v, float g, float lr) { return fmaf(-lr, g, v); }

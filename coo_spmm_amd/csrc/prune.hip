@@ -57,23 +57,23 @@ __device__ inline uint64_t splitmix64_output(uint64_t z)
 
 __device__ inline uint32_t mag_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
+// inclusive sum over lanes 0 .. lane: shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes (DPP row_shr, zero where the source lies before the row), then the
+// end of row 0 added to row 1 and of row 2 to row 3 (row_bcast:15), then the
+// end of row 1 to rows 2 and 3 (row_bcast:31); no LDS round trips
 __device__ inline int32_t wave_incl(int32_t v)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
     return v;
 }
 
-__device__ inline int32_t wave_sum(int32_t v)
-{
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
+// the wavefront's sum (uniform)
+__device__ inline int32_t wave_sum(int32_t v) { return __builtin_amdgcn_readlane(wave_incl(v), kWave - 1); }
 
 // ---- drop: radix select ---------------------------------------------------
 // Four passes over the magnitude keys, eight bits each, most significant
@@ -221,12 +221,7 @@ __device__ inline int32_t block_excl(int32_t v, int32_t* smem /*[waves]*/, int32
 {
     constexpr int W = kKeepThreads / kWave;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    int32_t inc = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t o = __shfl_up(inc, d, kWave);
-        if (lane >= d) inc += o;
-    }
+    const int32_t inc = wave_incl(v);
     if (lane == kWave - 1) smem[w] = inc;
     __syncthreads();
     int32_t base = 0;
@@ -743,14 +738,6 @@ __global__ void __launch_bounds__(kCutThreads) cut_give_back_kernel(
 // seen the batch's result: when the batch overflowed or fell short, the old
 // cells are put back into occ, so the rebuild sees a complete set of exactly
 // nnz cells (its output is then replaced once the grow is redone).
-__global__ void occ_guard_kernel(const uint32_t* __restrict__ state, uint32_t need,
-                                 const uint32_t* __restrict__ old_bm, uint32_t* __restrict__ occ_bm, int64_t words)
-{
-    if (state[kStOverflow] == 0u && state[kStTaken] == need) return;
-    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x)
-        occ_bm[w] = old_bm[w];
-}
-
 struct GrowPlan {
     int rb, sb;
     int32_t R, cap;
@@ -797,21 +784,37 @@ constexpr int kEmitSweeps = 8;
 constexpr int64_t kEmitUnit = (int64_t)kWave * kEmitSweeps;   // words per wavefront
 constexpr int64_t kEmitDirect = 16384;
 
-__global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint32_t* __restrict__ occ_bm,
+// With `guard` (a rebuild queued behind a grow batch before its result is
+// known): when that batch did not complete the grow (overflow, or fewer than
+// `need` taken), occ is first put back to the cells before the drop, so that
+// it holds exactly nnz cells and the rebuild stays inside the arrays; the grow
+// is then taken again and the layer rebuilt once more.
+__global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(uint32_t* __restrict__ occ_bm,
                                                                       const uint32_t* __restrict__ old_bm,
                                                                       int64_t words, int64_t units,
                                                                       int32_t* __restrict__ occ_cnt,
-                                                                      int32_t* __restrict__ old_cnt)
+                                                                      int32_t* __restrict__ old_cnt,
+                                                                      const uint32_t* __restrict__ guard,
+                                                                      uint32_t need)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
     if (u >= units) return;
+    const bool restore = guard && !(guard[kStOverflow] == 0u && guard[kStTaken] == need);
     int32_t a = 0, b = 0;
     for (int it = 0; it < kEmitSweeps; ++it) {
         const int64_t w = u * kEmitUnit + (int64_t)it * kWave + lane;
         if (w < words) {
-            a += __popc(occ_bm[w]);
-            b += __popc(old_bm[w]);
+            const uint32_t d = old_bm[w];
+            uint32_t o;
+            if (restore) {
+                o = d;
+                occ_bm[w] = d;
+            } else {
+                o = occ_bm[w];
+            }
+            a += __popc(o);
+            b += __popc(d);
         }
     }
     a = wave_sum(a);
@@ -830,12 +833,12 @@ __global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint
 // contiguous runs and the old values are read four at a time per lane.
 constexpr int kEmitList = 512;   // entries per wave
 
-__device__ inline void emit_flush(const int32_t* lr, const int32_t* lc, const int32_t* ls, int32_t n, int64_t out0,
-                                  int64_t nnz, const float* __restrict__ vold, int32_t* __restrict__ rows,
+__device__ inline void emit_flush(const int32_t* lr, const int32_t* lc, const int32_t* ls, int32_t n, int32_t out0,
+                                  int32_t nnz, const float* __restrict__ vold, int32_t* __restrict__ rows,
                                   int32_t* __restrict__ cols, float* __restrict__ vals, uint16_t* __restrict__ cols16,
                                   int lane)
 {
-    if ((int64_t)n > nnz - out0) n = (int32_t)(nnz - out0);   // never past the triple (occ holds nnz bits)
+    if (n > nnz - out0) n = nnz - out0;   // never past the triple (occ holds nnz bits)
     __builtin_amdgcn_wave_barrier();
     for (int32_t i0 = 0; i0 < n; i0 += 4 * kWave) {
         float v[4];
@@ -873,7 +876,9 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     // of the units before the workgroup, each wave then adds its neighbours'
     __shared__ int32_t red[2][kEmitThreads / kWave];
     const int64_t u0 = (int64_t)blockIdx.x * (kEmitThreads / kWave);
-    int64_t run_o, run_d;
+    // slots fit 32 bits (nnz < 2^31)
+    const int32_t nnz32 = (int32_t)nnz;
+    int32_t run_o, run_d;
     if constexpr (DIRECT) {
         // eight loads of each count in flight per thread (clamped indexes, no branch around a load)
         int32_t a = 0, b = 0;
@@ -922,7 +927,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     int32_t* lc = lc_[threadIdx.x / kWave];
     int32_t* ls = ls_[threadIdx.x / kWave];
     int32_t nl = 0;      // entries in the list (wave-uniform)
-    int64_t lout0 = 0;   // output slot of the list's first entry
+    int32_t lout0 = 0;   // output slot of the list's first entry
     uint32_t om_[kEmitSweeps], dm_[kEmitSweeps], km_[kEmitSweeps];
 #pragma unroll
     for (int it = 0; it < kEmitSweeps; ++it) {
@@ -938,37 +943,38 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         const uint32_t om = om_[it], dm = dm_[it], km = km_[it];
         const int32_t a = __popc(om), b = __popc(dm);
         const int32_t ia = wave_incl(a), ib = wave_incl(b);
-        const int32_t ta = __shfl(ia, kWave - 1, kWave);
-        const int64_t sweep0 = run_o;
-        int64_t out = run_o + ia - a;
-        const int64_t oldbase = run_d + ib - b;
+        const int32_t ta = __builtin_amdgcn_readlane(ia, kWave - 1);
+        const int32_t sweep0 = run_o;
+        int32_t out = run_o + ia - a;
+        const int32_t oldbase = run_d + ib - b;
         run_o += ta;
-        run_d += __shfl(ib, kWave - 1, kWave);
-        if (wpre && w < words) wpre[w] = (int32_t)out;
+        run_d += __builtin_amdgcn_readlane(ib, kWave - 1);
+        if (wpre && w < words) wpre[w] = out;
         // the list takes this sweep if it fits (sweeps of a dense layer may not)
         const bool listed = ta <= kEmitList;
         if (nl > 0 && (!listed || nl + ta > kEmitList)) {
-            emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, cols16, lane);
+            emit_flush(lr, lc, ls, nl, lout0, nnz32, vold, rows, cols, vals, cols16, lane);
             nl = 0;
         }
         if (listed && nl == 0) lout0 = sweep0;
-        int32_t lp = (int32_t)(out - lout0);
+        int32_t lp = out - lout0;
         if (listed) nl += ta;
         if (!om) continue;
-        int64_t r, c;
+        int32_t r, c;
         if constexpr (WIDE) {
             const uint64_t p0 = (uint64_t)w << 5;
-            r = (int64_t)(p0 / (uint64_t)K);
-            c = (int64_t)(p0 - (uint64_t)r * (uint64_t)K);
+            const uint64_t rr = p0 / (uint64_t)K;
+            r = (int32_t)rr;
+            c = (int32_t)(p0 - rr * (uint64_t)K);
         } else {
             const uint32_t p0 = (uint32_t)w << 5;
             const uint32_t rr = p0 / (uint32_t)K;
-            r = rr;
-            c = (int64_t)(p0 - rr * (uint32_t)K);
+            r = (int32_t)rr;
+            c = (int32_t)(p0 - rr * (uint32_t)K);
         }
         int last = 0;
         uint32_t m = om;
-        while (m && out < nnz) {
+        while (m && out < nnz32) {
             const int bit = __ffs(m) - 1;
             m &= m - 1u;
             c += bit - last;
@@ -977,22 +983,22 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
                 c -= K;
                 ++r;
             }
-            const int32_t src = ((km >> bit) & 1u) ? (int32_t)(oldbase + __popc(dm & ((1u << bit) - 1u))) : -1;
+            const int32_t src = ((km >> bit) & 1u) ? oldbase + __popc(dm & ((1u << bit) - 1u)) : -1;
             if (listed) {
-                lr[lp] = (int32_t)r;
-                lc[lp] = (int32_t)c;
+                lr[lp] = r;
+                lc[lp] = c;
                 ls[lp] = src;
                 ++lp;
             } else {
-                rows[out] = (int32_t)r;
-                cols[out] = (int32_t)c;
+                rows[out] = r;
+                cols[out] = c;
                 if (cols16) cols16[out] = (uint16_t)c;
                 vals[out] = src >= 0 ? vold[src] : 0.0f;
             }
             ++out;
         }
     }
-    if (nl > 0) emit_flush(lr, lc, ls, nl, lout0, nnz, vold, rows, cols, vals, cols16, lane);
+    if (nl > 0) emit_flush(lr, lc, ls, nl, lout0, nnz32, vold, rows, cols, vals, cols16, lane);
 }
 
 // ---- the column view from the new bitmap -----------------------------------
@@ -1133,24 +1139,36 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __
     if (tid < t.ncols) cnt[(int64_t)bi * K + t.c0 + tid] = c;
 }
 
-// down each column: counts -> exclusive prefix over the row blocks; totals out
-__global__ void cv_column_scan_kernel(int32_t* __restrict__ cnt, int32_t nbi, int32_t K, int32_t* __restrict__ tot)
+// down each column: counts -> exclusive prefix over the row blocks; the
+// column totals out, and per band of kCvDim columns (one workgroup) their sum
+__global__ void __launch_bounds__(kCvDim) cv_column_scan_kernel(int32_t* __restrict__ cnt, int32_t nbi, int32_t K,
+                                                                int32_t* __restrict__ tot, int32_t* __restrict__ band)
 {
     constexpr int kBatch = 16;   // loads in flight per thread
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= K) return;
+    __shared__ int32_t red[kCvDim / kWave];
+    const int64_t c = (int64_t)blockIdx.x * kCvDim + threadIdx.x;
     int32_t run = 0;
-    for (int32_t b0 = 0; b0 < nbi; b0 += kBatch) {
-        int32_t v[kBatch];
+    if (c < K) {
+        for (int32_t b0 = 0; b0 < nbi; b0 += kBatch) {
+            int32_t v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = b0 + u < nbi ? cnt[(int64_t)(b0 + u) * K + c] : 0;
+            for (int u = 0; u < kBatch; ++u) v[u] = b0 + u < nbi ? cnt[(int64_t)(b0 + u) * K + c] : 0;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (b0 + u < nbi) cnt[(int64_t)(b0 + u) * K + c] = run;
-            run += v[u];
+            for (int u = 0; u < kBatch; ++u) {
+                if (b0 + u < nbi) cnt[(int64_t)(b0 + u) * K + c] = run;
+                run += v[u];
+            }
         }
+        tot[c] = run;
     }
-    tot[c] = run;
+    const int32_t ws = wave_sum(run);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ws;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+        for (int i = 0; i < kCvDim / kWave; ++i) t += red[i];
+        band[blockIdx.x] = t;
+    }
 }
 
 // last index i in [0, n) with a[i] <= x (a ascending, a[0] <= x)
@@ -1173,25 +1191,60 @@ struct CvTabs {
     int32_t* ctab[kTileWidths];
 };
 
-// a view's slice-table entries for boundaries inside one tile: keys along the
-// tile's one side (lane a < nkey), boundaries along the other, starting at
-// `o0` with `n` positions; the last tile along the boundary side also writes
-// the end entry (s = S).  Entry = slot of the key's first entry in the tile
-// (`first`) plus the key's entries before the boundary (word prefixes `pre`
-// and the bits of the boundary's word).
-__device__ inline void cv_tab_side(int32_t* tab, int32_t S, int32_t nidx, int32_t nkeys, int32_t o0, int32_t n,
-                                   bool last, int32_t key0, int a, int32_t nkey, int32_t first,
-                                   const uint8_t* pre, const uint32_t* bits, int32_t total)
+// The slice boundaries that fall inside one tile, per side (0: the row
+// view's, along the columns; 1: the column view's, along the rows) and batch
+// width: s = lo .. lo + n - 1, boundary s at tile offset off[s] (the last tile
+// along a side also takes s = S, whose offset is the side's length).  One
+// thread per (side, width, s) computes its boundary once.
+struct CvBounds {
+    int32_t lo[2][kTileWidths], n[2][kTileWidths];
+    int16_t off[2][kTileWidths][kMaxSplits + 1];
+};
+
+__device__ inline void cv_bounds_init(CvBounds& cb)
 {
-    for (int32_t s = (int32_t)(((int64_t)o0 * S + nidx - 1) / nidx); s <= S; ++s) {
-        const int32_t b = split_start(s, S, nidx);
-        if (b >= o0 + n && !(s == S && last)) break;
-        if (a < nkey) {
-            const int32_t lb = b - o0;
-            const int32_t before = lb >= kCvDim ? total
-                                   : pre[a * kCvWords + (lb >> 5)] + __popc(bits[a * kCvPad + (lb >> 5)] & ((1u << (lb & 31)) - 1u));
-            tab[(int64_t)s * nkeys + key0 + a] = first + before;
-        }
+    if (threadIdx.x < 2 * kTileWidths) {
+        (&cb.lo[0][0])[threadIdx.x] = kMaxSplits + 1;
+        (&cb.n[0][0])[threadIdx.x] = 0;
+    }
+}
+
+__device__ inline void cv_bounds_find(CvBounds& cb, const CvTabs& tabs, const CvTileShape& t, int32_t M, int32_t K,
+                                      bool last_r, bool last_c)
+{
+    constexpr int PER = kMaxSplits + 1;
+    const int q = (int)threadIdx.x;
+    if (q >= 2 * kTileWidths * PER) return;
+    const int side = q / (kTileWidths * PER), w = (q / PER) % kTileWidths, s = q % PER;
+    const int32_t S = side == 0 ? tabs.rS[w] : tabs.cS[w];
+    const bool has = side == 0 ? tabs.rtab[w] != nullptr : tabs.ctab[w] != nullptr;
+    if (!has || s > S) return;
+    const int32_t nidx = side == 0 ? K : M;
+    const int32_t o0 = side == 0 ? t.c0 : t.r0, len = side == 0 ? t.ncols : t.nrows;
+    const bool last = side == 0 ? last_r : last_c;
+    const int32_t b = split_start(s, S, nidx);
+    if ((b >= o0 && b < o0 + len) || (s == S && last)) {
+        cb.off[side][w][s] = (int16_t)(b - o0);
+        atomicMin(&cb.lo[side][w], s);
+        atomicAdd(&cb.n[side][w], 1);
+    }
+}
+
+// a view's slice-table entries at one side's boundaries inside the tile, for
+// key a (< nkey) along the other side: slot of the key's first entry in the
+// tile (`first`) plus its entries before the boundary (word prefixes `pre` and
+// the bits of the boundary's word)
+__device__ inline void cv_tab_side(int32_t* tab, const CvBounds& cb, int side, int w, int32_t nkeys, int32_t key0,
+                                   int a, int32_t nkey, int32_t first, const uint8_t* pre, const uint32_t* bits,
+                                   int32_t total)
+{
+    const int32_t lo = cb.lo[side][w], n = cb.n[side][w];
+    if (a >= nkey) return;
+    for (int32_t s = lo; s < lo + n; ++s) {
+        const int32_t lb = cb.off[side][w][s];
+        const int32_t before = lb >= kCvDim ? total
+                               : pre[a * kCvWords + (lb >> 5)] + __popc(bits[a * kCvPad + (lb >> 5)] & ((1u << (lb & 31)) - 1u));
+        tab[(int64_t)s * nkeys + key0 + a] = first + before;
     }
 }
 
@@ -1201,17 +1254,19 @@ constexpr int32_t kCvStage = 4096;   // tile entries handled through LDS lists
 // One tile per workgroup.  Entries are numbered twice inside the tile: x in
 // row order (a row's entries are consecutive canonical slots, starting at
 // rowk) and e in column order (a column's entries are consecutive transposed
-// slots, starting at colbase).  Bit walks over the tile's words fill LDS lists
-// (row of x; row-order index and column of e), after which every pass over
-// the entries is striped across the threads: values are read and iperm
-// written as row runs, rows_t and vals_t written as column runs.  A tile with
-// more than kCvStage entries finds each entry's column by binary search and
-// reads and writes global memory directly.
+// slots, starting at colbase).  A walk over each row word's bits lists the
+// row and column of every x; a pass in x order (striped across the threads)
+// then reads each entry's value as part of a row run, finds its e from the
+// column words, writes iperm as a row run and leaves the value, row and
+// column at e in LDS, from where a pass in e order writes rows_t and vals_t as
+// column runs.  A tile with more than kCvStage entries finds each entry's
+// column by binary search and reads and writes global memory directly.
 __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     const uint32_t* __restrict__ occ_bm, uint64_t words, const int32_t* __restrict__ wpre, int32_t M, int32_t K,
-    int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ col_ptr,
-    const float* __restrict__ vals, int32_t* __restrict__ rows_t, float* __restrict__ vals_t,
-    int32_t* __restrict__ iperm, CvTabs tabs, uint16_t* __restrict__ rows_t16)
+    int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ tot,
+    const int32_t* __restrict__ band, int32_t* __restrict__ col_ptr, const float* __restrict__ vals,
+    int32_t* __restrict__ rows_t, float* __restrict__ vals_t, int32_t* __restrict__ iperm, CvTabs tabs,
+    uint16_t* __restrict__ rows_t16)
 {
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
     __shared__ uint32_t colbits[kCvDim * kCvPad];
@@ -1221,28 +1276,45 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     __shared__ int32_t rowoff[kCvDim + 1];        // x of a row's first entry
     __shared__ int32_t colstart[kCvDim + 1];      // e of a column's first entry
     __shared__ int32_t colbase[kCvDim];           // transposed slot of a column's first entry
-    __shared__ uint8_t xrow[kCvStage];
-    __shared__ uint16_t eloc[kCvStage];
-    __shared__ uint8_t ecol[kCvStage];
-    __shared__ float sval[kCvStage];
-    __shared__ int32_t sslot[kCvStage];
+    __shared__ uint8_t xrow[kCvStage];   // row of x
+    __shared__ uint8_t xcol[kCvStage];   // column of x
+    __shared__ uint8_t erow[kCvStage];   // row of e
+    __shared__ uint8_t ecol[kCvStage];   // column of e
+    __shared__ float sval[kCvStage];     // value of e
     __shared__ int32_t red[2][kCvDim / kWave];
+    __shared__ int32_t cwsum[kCvDim / kWave];
+    __shared__ CvBounds cb;
     int32_t bi, bj;
     if (!cv_tile_of(nbi, nbj, bi, bj)) return;
     const CvTileShape t = cv_shape(bi, bj, M, K);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 
+    cv_bounds_init(cb);
     cv_load_rows<kCvScatterThreads>(occ_bm, words, K, t, rowbits);
+    // the columns' first transposed slots: the bands before this one, then a scan of the band's
+    // column totals (column starts also written to col_ptr by the first row block)
+    int32_t ctot = 0, ccnt = 0, cincl = 0, boff = 0;
     if (tid < kCvDim) {
         const int32_t c = t.c0 + (tid < t.ncols ? tid : t.ncols - 1);
         const int32_t r = t.r0 + (tid < t.nrows ? tid : t.nrows - 1);
-        const int32_t cb = col_ptr[c] + cnt[(int64_t)bi * K + c];
+        ctot = tid < t.ncols ? tot[c] : 0;
+        ccnt = cnt[(int64_t)bi * K + c];
+        for (int32_t b = lane; b < bj; b += kWave) boff += band[b];
         const int32_t k = cv_slot_at(occ_bm, wpre, (uint64_t)r * (uint64_t)K + (uint64_t)t.c0);
-        colbase[tid] = tid < t.ncols ? cb : 0;
         rowk[tid] = tid < t.nrows ? k : 0;
+        boff = wave_sum(boff);
+        cincl = wave_incl(ctot);
+        if (lane == kWave - 1) cwsum[wv] = cincl;
     }
     __syncthreads();
+    if (tid < kCvDim) {
+        int32_t start = boff + cincl - ctot;
+        for (int i = 0; i < wv; ++i) start += cwsum[i];
+        colbase[tid] = tid < t.ncols ? start + ccnt : 0;
+        if (bi == 0 && tid < t.ncols) col_ptr[t.c0 + tid] = start;
+    }
     cv_transpose<kCvScatterThreads>(rowbits, colbits);
+    cv_bounds_find(cb, tabs, t, M, K, bj == nbj - 1, bi == nbi - 1);
     __syncthreads();
     // word prefixes and counts: threads 0..255 rows, 256..511 columns
     int32_t cntv = 0;
@@ -1277,19 +1349,19 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
         for (int w = 0; w < kTileWidths; ++w) {
             if (row && tabs.rtab[w]) {
                 const int32_t total = a < t.nrows ? rowoff[a + 1] - rowoff[a] : 0;
-                cv_tab_side(tabs.rtab[w], tabs.rS[w], K, M, t.c0, t.ncols, bj == nbj - 1, t.r0, a, t.nrows,
-                            a < t.nrows ? rowk[a] : 0, rwp, rowbits, total);
+                cv_tab_side(tabs.rtab[w], cb, 0, w, M, t.r0, a, t.nrows, a < t.nrows ? rowk[a] : 0, rwp, rowbits,
+                            total);
             }
             if (!row && tabs.ctab[w]) {
                 const int32_t total = a < t.ncols ? colstart[a + 1] - colstart[a] : 0;
-                cv_tab_side(tabs.ctab[w], tabs.cS[w], M, K, t.r0, t.nrows, bi == nbi - 1, t.c0, a, t.ncols,
-                            a < t.ncols ? colbase[a] : 0, cwp, colbits, total);
+                cv_tab_side(tabs.ctab[w], cb, 1, w, K, t.c0, a, t.ncols, a < t.ncols ? colbase[a] : 0, cwp, colbits,
+                            total);
             }
         }
     }
     const int32_t E = colstart[kCvDim];
     if (E <= kCvStage) {   // uniform
-        // lists: two row words and two column words per thread
+        // row and column of every x: two row words per thread
 #pragma unroll
         for (int n = 0; n < kCvDim * kCvWords / kCvScatterThreads; ++n) {
             const int q = tid + n * kCvScatterThreads;
@@ -1297,53 +1369,50 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
             uint32_t m = rowbits[a * kCvPad + i];
             int32_t x = rowoff[a] + rwp[a * kCvWords + i];
             while (m) {
+                xrow[x] = (uint8_t)a;
+                xcol[x] = (uint8_t)(32 * i + __ffs(m) - 1);
                 m &= m - 1u;
-                xrow[x++] = (uint8_t)a;
-            }
-            // column a, rows 32i .. 32i+31
-            m = colbits[a * kCvPad + i];
-            int32_t e = colstart[a] + cwp[a * kCvWords + i];
-            const int ci = a >> 5;
-            const uint32_t below = (1u << (a & 31)) - 1u;
-            while (m) {
-                const int rr = 32 * i + __ffs(m) - 1;
-                m &= m - 1u;
-                eloc[e] = (uint16_t)(rowoff[rr] + rwp[rr * kCvWords + ci] + __popc(rowbits[rr * kCvPad + ci] & below));
-                ecol[e] = (uint8_t)a;
-                ++e;
+                ++x;
             }
         }
         __syncthreads();
         {
+            // x order: values read (all R loads in flight first), iperm written, (value, row, column) to e
             constexpr int R = kCvStage / kCvScatterThreads;
             float v[R];
+            int32_t k[R];
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int32_t x = tid + u * kCvScatterThreads;
-                const int32_t xc = x < E ? x : 0;
-                const int rr = xrow[xc];
-                v[u] = vals[x < E ? rowk[rr] + (x - rowoff[rr]) : 0];
+                const int rr = xrow[x < E ? x : 0];
+                k[u] = x < E ? rowk[rr] + (x - rowoff[rr]) : 0;
+                v[u] = vals[k[u]];
             }
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int32_t x = tid + u * kCvScatterThreads;
-                if (x < E) sval[x] = v[u];
+                if (x < E) {
+                    const int rr = xrow[x], c = xcol[x];
+                    const int j = rr >> 5;
+                    const int32_t before =
+                        cwp[c * kCvWords + j] + __popc(colbits[c * kCvPad + j] & ((1u << (rr & 31)) - 1u));
+                    const int32_t e = colstart[c] + before;
+                    iperm[k[u]] = colbase[c] + before;
+                    sval[e] = v[u];
+                    erow[e] = (uint8_t)rr;
+                    ecol[e] = (uint8_t)c;
+                }
             }
         }
         __syncthreads();
+        // e order: the column runs of rows_t and vals_t
         for (int32_t e = tid; e < E; e += kCvScatterThreads) {
             const int c = ecol[e];
-            const int32_t loc = eloc[e];
             const int32_t kt = colbase[c] + (e - colstart[c]);
-            rows_t[kt] = t.r0 + xrow[loc];
-            if (rows_t16) rows_t16[kt] = (uint16_t)(t.r0 + xrow[loc]);
-            vals_t[kt] = sval[loc];
-            sslot[loc] = kt;
-        }
-        __syncthreads();
-        for (int32_t x = tid; x < E; x += kCvScatterThreads) {
-            const int rr = xrow[x];
-            iperm[rowk[rr] + (x - rowoff[rr])] = sslot[x];
+            const int32_t r = t.r0 + erow[e];
+            rows_t[kt] = r;
+            if (rows_t16) rows_t16[kt] = (uint16_t)r;
+            vals_t[kt] = sval[e];
         }
         return;
     }
@@ -1386,6 +1455,7 @@ struct PruneScratch {
     int32_t* wpre;      // [words] first canonical slot of every bitmap word (column view from the bitmap)
     int32_t* cvcnt;     // [row blocks * K] entries per column and row block, then their prefixes
     int32_t* cvtot;     // [K] entries per column
+    int32_t* cvband;    // [column bands] entries per band of kCvDim columns
     uint32_t* gstate;   // [16] gradient grow: thresholds and counts
     uint32_t* ghist;    // [kGradHistWords] gradient grow: digit histograms
     int32_t* tie_cnt;   // [M * grad_col_tiles(K)] gradient grow: threshold ties per row and column tile
@@ -1437,6 +1507,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     size_t o_acc = take((size_t)tm + 8), o_tsum = take((size_t)(tm / kSumTile + 1) * 4);
     size_t o_fill = take((size_t)kMaxRegions * 4), o_bucket = take((size_t)nb * 8);
     size_t o_wpre = take((size_t)words * 4), o_cvcnt = take((size_t)nbi * L->K * 4), o_cvtot = take((size_t)L->K * 4);
+    size_t o_cvband = take((size_t)((L->K + kCvDim - 1) / kCvDim) * 4);
     size_t o_gst = take(16 * 4), o_gh = take((size_t)kGradHistWords * 4), o_tie = take((size_t)nties * 4);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
@@ -1457,6 +1528,7 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         ps->wpre = (int32_t*)(base + o_wpre);
         ps->cvcnt = (int32_t*)(base + o_cvcnt);
         ps->cvtot = (int32_t*)(base + o_cvtot);
+        ps->cvband = (int32_t*)(base + o_cvband);
         ps->gstate = (uint32_t*)(base + o_gst);
         ps->ghist = (uint32_t*)(base + o_gh);
         ps->tie_cnt = (int32_t*)(base + o_tie);
@@ -1482,7 +1554,8 @@ size_t prune_scratch_bytes(const snack_layer* L)
 namespace {
 
 // The canonical arrays and both views from the occupancy bitmap.
-snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
+snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s, const uint32_t* guard = nullptr,
+                     uint32_t need = 0)
 {
     const int64_t nnz = L->nnz;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
@@ -1494,7 +1567,7 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
         const int64_t nu = ps.units;
         const unsigned grid = (unsigned)((nu + (kEmitThreads / kWave) - 1) / (kEmitThreads / kWave));
         hipLaunchKernelGGL(bm_unit_counts_kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.old_bm, ps.words,
-                           nu, ps.occ_cnt, ps.old_cnt);
+                           nu, ps.occ_cnt, ps.old_cnt, guard, need);
         SNACK_HIP(hipGetLastError());
         const bool direct = nu <= kEmitDirect;
         if (!direct) {
@@ -1525,10 +1598,9 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
         const int64_t nslots = (int64_t)kXcds * ((nbj + kXcds - 1) / kXcds) * nbi;
         hipLaunchKernelGGL(cv_count_kernel, dim3((unsigned)nslots), dim3(kCvThreads), 0, s, ps.occ_bm, words, ps.wpre,
                            M, K, nbi, nbj, nnz, ps.cvcnt, L->row_ptr, L->col_ptr);
-        hipLaunchKernelGGL(cv_column_scan_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, ps.cvcnt, nbi, K,
-                           ps.cvtot);
+        hipLaunchKernelGGL(cv_column_scan_kernel, dim3((unsigned)nbj), dim3(kCvDim), 0, s, ps.cvcnt, nbi, K, ps.cvtot,
+                           ps.cvband);
         SNACK_HIP(hipGetLastError());
-        SNACK_CHECK(exclusive_scan_i32(ps.cvtot, L->col_ptr, K, nullptr, ps.scan, s));
         CvTabs tabs;
         for (int w = 0; w < kTileWidths; ++w) {
             tabs.rS[w] = L->fwd.split[w].S;
@@ -1537,8 +1609,8 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s)
             tabs.ctab[w] = L->tr.split[w].S >= 2 ? L->tr.split[w].tab : nullptr;
         }
         hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm, words,
-                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, L->col_ptr, L->vals, L->rows_t, L->vals_t, L->iperm,
-                           tabs, L->tr.idx16);
+                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, ps.cvtot, ps.cvband, L->col_ptr, L->vals, L->rows_t,
+                           L->vals_t, L->iperm, tabs, L->tr.idx16);
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(canon_index_tail(L, s, /*idx16_done=*/true));
         for (int w = 0; w < kTileWidths; ++w) {
@@ -1618,7 +1690,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
     const uint64_t words_total = (uint64_t)ps.words;
     // The first batch nearly always completes the grow, so the rebuild is
     // queued right behind it, before its result is read (the host would
-    // otherwise leave the GPU idle while it waits and relaunches); a guard
+    // otherwise leave the GPU idle while it waits and relaunches); its first
     // kernel keeps that rebuild consistent if the batch did not complete it,
     // and the grow then starts over from the kept cells.  Only the bitmap
     // rebuild qualifies: it uses no scratch that the grow needs.
@@ -1651,10 +1723,7 @@ snack_status prune_regrow(snack_layer* L, int64_t n_drop, hipStream_t s)
         SNACK_HIP(hipEventRecord(L->grow_ev, s));
         const bool queued = speculate;
         if (queued) {
-            hipLaunchKernelGGL(occ_guard_kernel, dim3(grid_for(ps.words) < 1024u ? grid_for(ps.words) : 1024u),
-                               dim3(kThreads), 0, s, ps.state, (uint32_t)need, ps.old_bm, ps.occ_bm, ps.words);
-            SNACK_HIP(hipGetLastError());
-            SNACK_CHECK(rebuild(L, ps, s));
+            SNACK_CHECK(rebuild(L, ps, s, ps.state, (uint32_t)need));
             speculate = false;
         }
         SNACK_HIP(hipEventSynchronize(L->grow_ev));

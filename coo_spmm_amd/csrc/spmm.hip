@@ -798,7 +798,6 @@ constexpr int kLdsKeyWaves = 16;
 constexpr int kTileWaves = 16;
 constexpr int kTileDepth = 8;     // blocks in flight per wavefront
 constexpr int kTileDepthDw = 4;   // with dW: each block also holds its key's operand row
-constexpr int kMaxSplits = 64;
 constexpr int kTileStaticLds = 1024;   // bytes kept back from the slice buffer
 
 struct TileArgs {
