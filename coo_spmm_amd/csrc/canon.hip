@@ -91,12 +91,9 @@ struct PartArgs {
     int32_t* n_empty;
 };
 
-__global__ void build_chunks_kernel(PartArgs va, PartArgs vb, int32_t work)
+__device__ inline void chunks_part(const PartArgs& v, int32_t work, int bx, int nbx)
 {
-    const PartArgs& v = blockIdx.y == 0 ? va : vb;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *v.n_empty = 0;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c <= v.nchunks;
-         c += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t c = (int64_t)bx * blockDim.x + threadIdx.x; c <= v.nchunks; c += (int64_t)nbx * blockDim.x) {
         int32_t key = v.nkeys;
         if (c < v.nchunks) {
             const int64_t target = c * (int64_t)work;
@@ -112,14 +109,20 @@ __global__ void build_chunks_kernel(PartArgs va, PartArgs vb, int32_t work)
     }
 }
 
-// Keys without entries, in no particular order (the SpMM only writes zeros
-// for them, so the order cannot change any result); one atomic per wave.
-__global__ void empty_keys_kernel(PartArgs va, PartArgs vb)
+__global__ void build_chunks_kernel(PartArgs va, PartArgs vb, int32_t work)
 {
     const PartArgs& v = blockIdx.y == 0 ? va : vb;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *v.n_empty = 0;
+    chunks_part(v, work, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Keys without entries, in no particular order (the SpMM only writes zeros
+// for them, so the order cannot change any result); one atomic per wave.
+__device__ inline void empty_part(const PartArgs& v, int bx, int nbx)
+{
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t r0 = (int64_t)blockIdx.x * blockDim.x; r0 < v.nkeys; r0 += stride) {
+    const int64_t stride = (int64_t)nbx * blockDim.x;
+    for (int64_t r0 = (int64_t)bx * blockDim.x; r0 < v.nkeys; r0 += stride) {
         const int64_t r = r0 + threadIdx.x;
         const bool empty = r < v.nkeys && v.ptr[r] == v.ptr[r + 1];
         const uint64_t m = __ballot(empty);
@@ -129,6 +132,21 @@ __global__ void empty_keys_kernel(PartArgs va, PartArgs vb)
         base = __shfl(base, __ffsll((unsigned long long)m) - 1, kWave);
         if (empty) v.empty_keys[base + __popcll(m & ((1ull << lane) - 1ull))] = (int32_t)r;
     }
+}
+
+__global__ void empty_keys_kernel(PartArgs va, PartArgs vb)
+{
+    empty_part(blockIdx.y == 0 ? va : vb, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Both in one launch when the empty-key counters are already zero: of a grid
+// row (one view), the first `nbc` workgroups build the chunk descriptors and
+// the others list the empty keys.
+__global__ void partition_kernel(PartArgs va, PartArgs vb, int32_t work, int32_t nbc)
+{
+    const PartArgs& v = blockIdx.y == 0 ? va : vb;
+    if ((int)blockIdx.x < nbc) chunks_part(v, work, (int)blockIdx.x, nbc);
+    else empty_part(v, (int)blockIdx.x - nbc, (int)gridDim.x - nbc);
 }
 
 __global__ void iota_cols_kernel(const int32_t* __restrict__ cols, int64_t nnz, uint32_t* __restrict__ keys,
@@ -305,7 +323,7 @@ __global__ void invert_iperm_kernel(const int32_t* __restrict__ iperm, int64_t n
         perm[iperm[k]] = (int32_t)k;
 }
 
-snack_status build_view_partitions(snack_layer* L, hipStream_t s)
+snack_status build_view_partitions(snack_layer* L, hipStream_t s, bool empty_cleared)
 {
     auto args = [](const View& v) {
         PartArgs a;
@@ -320,9 +338,15 @@ snack_status build_view_partitions(snack_layer* L, hipStream_t s)
     const PartArgs a = args(L->fwd), b = args(L->tr);
     const int32_t nc = a.nchunks > b.nchunks ? a.nchunks : b.nchunks;
     const int32_t nk = a.nkeys > b.nkeys ? a.nkeys : b.nkeys;
-    hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)nc + 1), 2), dim3(kThreads), 0, s, a, b,
-                       L->chunk_work);
-    hipLaunchKernelGGL(empty_keys_kernel, dim3(grid_for(nk), 2), dim3(kThreads), 0, s, a, b);
+    if (empty_cleared) {
+        const unsigned nbc = grid_for((int64_t)nc + 1), nbe = grid_for(nk);
+        hipLaunchKernelGGL(partition_kernel, dim3(nbc + nbe, 2), dim3(kThreads), 0, s, a, b, L->chunk_work,
+                           (int32_t)nbc);
+    } else {
+        hipLaunchKernelGGL(build_chunks_kernel, dim3(grid_for((int64_t)nc + 1), 2), dim3(kThreads), 0, s, a, b,
+                           L->chunk_work);
+        hipLaunchKernelGGL(empty_keys_kernel, dim3(grid_for(nk), 2), dim3(kThreads), 0, s, a, b);
+    }
     SNACK_HIP(hipGetLastError());
     return SNACK_OK;
 }
@@ -470,7 +494,7 @@ snack_status build_idx16(snack_layer* L, hipStream_t s)
     return SNACK_OK;
 }
 
-snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done)
+snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done, bool empty_cleared)
 {
     if (!idx16_done) SNACK_CHECK(build_idx16(L, s));
     L->vals_t_stale = false;
@@ -478,7 +502,7 @@ snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done)
         L->fwd.split[i].valid = false;
         L->tr.split[i].valid = false;
     }
-    SNACK_CHECK(build_view_partitions(L, s));
+    SNACK_CHECK(build_view_partitions(L, s, empty_cleared));
     return SNACK_OK;
 }
 

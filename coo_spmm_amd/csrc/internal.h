@@ -208,7 +208,7 @@ snack_status canon_build_index(snack_layer* L, hipStream_t s);
 // The part of canon_build_index after row_ptr and the transposed view exist
 // (for callers that build those themselves): partitions of both views, flags,
 // and the 16-bit index copies unless the caller wrote them (idx16_done).
-snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done = false);
+snack_status canon_index_tail(snack_layer* L, hipStream_t s, bool idx16_done = false, bool empty_cleared = false);
 // vals_t[iperm[k]] = vals[k]
 snack_status refresh_vals_t(snack_layer* L, hipStream_t s);
 // the views' 16-bit index copies from their 32-bit indices (where allocated)

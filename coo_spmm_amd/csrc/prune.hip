@@ -1112,7 +1112,9 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __
                                                               const int32_t* __restrict__ wpre, int32_t M, int32_t K,
                                                               int32_t nbi, int32_t nbj, int64_t nnz, int32_t* __restrict__ cnt,
                                                               int32_t* __restrict__ row_ptr,
-                                                              int32_t* __restrict__ col_ptr)
+                                                              int32_t* __restrict__ col_ptr,
+                                                              int32_t* __restrict__ n_empty_r,
+                                                              int32_t* __restrict__ n_empty_c)
 {
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
     __shared__ uint32_t colbits[kCvDim * kCvPad];
@@ -1128,6 +1130,8 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __
     if (bi == 0 && bj == 0 && tid == 0) {
         row_ptr[M] = (int32_t)nnz;
         col_ptr[K] = (int32_t)nnz;
+        *n_empty_r = 0;   // the views' empty-key lists are rebuilt at the end
+        *n_empty_c = 0;
     }
     cv_load_rows<kCvThreads>(occ_bm, words, K, t, rowbits);
     __syncthreads();
@@ -1597,7 +1601,7 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s, cons
         const uint64_t words = (uint64_t)ps.words;
         const int64_t nslots = (int64_t)kXcds * ((nbj + kXcds - 1) / kXcds) * nbi;
         hipLaunchKernelGGL(cv_count_kernel, dim3((unsigned)nslots), dim3(kCvThreads), 0, s, ps.occ_bm, words, ps.wpre,
-                           M, K, nbi, nbj, nnz, ps.cvcnt, L->row_ptr, L->col_ptr);
+                           M, K, nbi, nbj, nnz, ps.cvcnt, L->row_ptr, L->col_ptr, L->fwd.n_empty, L->tr.n_empty);
         hipLaunchKernelGGL(cv_column_scan_kernel, dim3((unsigned)nbj), dim3(kCvDim), 0, s, ps.cvcnt, nbi, K, ps.cvtot,
                            ps.cvband);
         SNACK_HIP(hipGetLastError());
@@ -1612,7 +1616,7 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s, cons
                            ps.wpre, M, K, nbi, nbj, ps.cvcnt, ps.cvtot, ps.cvband, L->col_ptr, L->vals, L->rows_t,
                            L->vals_t, L->iperm, tabs, L->tr.idx16);
         SNACK_HIP(hipGetLastError());
-        SNACK_CHECK(canon_index_tail(L, s, /*idx16_done=*/true));
+        SNACK_CHECK(canon_index_tail(L, s, /*idx16_done=*/true, /*empty_cleared=*/true));
         for (int w = 0; w < kTileWidths; ++w) {
             if (tabs.rtab[w]) L->fwd.split[w].valid = true;
             if (tabs.ctab[w]) L->tr.split[w].valid = true;
