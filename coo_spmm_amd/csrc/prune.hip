@@ -777,44 +777,27 @@ int64_t bucket_bound(uint64_t N, int64_t tmax)
 // prefix -- summed from the unit counts before it when there are few units,
 // else read from their scans -- and, per sweep, turns the lanes' counts into
 // slots with a wavefront scan: an occupied cell goes to the next slot; a kept
-// cell takes the value the old entry at its old rank had.  With `wpre` it also
-// stores every word's first slot (the set bits of `occ` before the word).
+// cell takes the value the old entry at its old rank had.
 constexpr int kEmitThreads = 256;
 constexpr int kEmitSweeps = 8;
 constexpr int64_t kEmitUnit = (int64_t)kWave * kEmitSweeps;   // words per wavefront
 constexpr int64_t kEmitDirect = 16384;
 
-// With `guard` (a rebuild queued behind a grow batch before its result is
-// known): when that batch did not complete the grow (overflow, or fewer than
-// `need` taken), occ is first put back to the cells before the drop, so that
-// it holds exactly nnz cells and the rebuild stays inside the arrays; the grow
-// is then taken again and the layer rebuilt once more.
-__global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(uint32_t* __restrict__ occ_bm,
+__global__ void __launch_bounds__(kEmitThreads) bm_unit_counts_kernel(const uint32_t* __restrict__ occ_bm,
                                                                       const uint32_t* __restrict__ old_bm,
                                                                       int64_t words, int64_t units,
                                                                       int32_t* __restrict__ occ_cnt,
-                                                                      int32_t* __restrict__ old_cnt,
-                                                                      const uint32_t* __restrict__ guard,
-                                                                      uint32_t need)
+                                                                      int32_t* __restrict__ old_cnt)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
     if (u >= units) return;
-    const bool restore = guard && !(guard[kStOverflow] == 0u && guard[kStTaken] == need);
     int32_t a = 0, b = 0;
     for (int it = 0; it < kEmitSweeps; ++it) {
         const int64_t w = u * kEmitUnit + (int64_t)it * kWave + lane;
         if (w < words) {
-            const uint32_t d = old_bm[w];
-            uint32_t o;
-            if (restore) {
-                o = d;
-                occ_bm[w] = d;
-            } else {
-                o = occ_bm[w];
-            }
-            a += __popc(o);
-            b += __popc(d);
+            a += __popc(occ_bm[w]);
+            b += __popc(old_bm[w]);
         }
     }
     a = wave_sum(a);
@@ -868,7 +851,7 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
     const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ kept_bm, const uint32_t* __restrict__ old_bm,
     int64_t words, int64_t units, const int32_t* __restrict__ occ_cnt, const int32_t* __restrict__ old_cnt,
     const float* __restrict__ vold, int64_t nnz, int32_t K, int32_t* __restrict__ rows, int32_t* __restrict__ cols,
-    float* __restrict__ vals, int32_t* __restrict__ wpre, uint16_t* __restrict__ cols16)
+    float* __restrict__ vals, uint16_t* __restrict__ cols16)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t u = (int64_t)blockIdx.x * (kEmitThreads / kWave) + threadIdx.x / kWave;
@@ -949,7 +932,6 @@ __global__ void __launch_bounds__(kEmitThreads) emit_units_kernel(
         const int32_t oldbase = run_d + ib - b;
         run_o += ta;
         run_d += __builtin_amdgcn_readlane(ib, kWave - 1);
-        if (wpre && w < words) wpre[w] = out;
         // the list takes this sweep if it fits (sweeps of a dense layer may not)
         const bool listed = ta <= kEmitList;
         if (nl > 0 && (!listed || nl + ta > kEmitList)) {
@@ -1100,41 +1082,56 @@ __device__ inline void cv_transpose(const uint32_t* rowbits, uint32_t* colbits)
     }
 }
 
-// the first canonical slot at or after `cell`: word prefix plus the bits before it
-__device__ inline int32_t cv_slot_at(const uint32_t* __restrict__ occ_bm, const int32_t* __restrict__ wpre,
-                                     uint64_t cell)
-{
-    const uint64_t w = cell >> 5;
-    return wpre[w] + __popc(occ_bm[w] & ((1u << (cell & 31)) - 1u));
-}
-
-__global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __restrict__ occ_bm, uint64_t words,
-                                                              const int32_t* __restrict__ wpre, int32_t M, int32_t K,
-                                                              int32_t nbi, int32_t nbj, int64_t nnz, int32_t* __restrict__ cnt,
-                                                              int32_t* __restrict__ row_ptr,
-                                                              int32_t* __restrict__ col_ptr,
-                                                              int32_t* __restrict__ n_empty_r,
-                                                              int32_t* __restrict__ n_empty_c)
+// ---- count and scan passes of the rebuild ---------------------------------
+// Pass 1 (one workgroup per tile): each column's entries in the tile (cnt,
+// [row block][K]), and each row's entries in the tile, new and old (rcnt and
+// ocnt, [column block][M]).  With `guard` (a rebuild queued behind a grow batch
+// before its result is known): when that batch did not complete the grow
+// (overflow, or fewer than `need` taken), occ is first put back to the cells
+// before the drop, so that it holds exactly nnz cells and the rebuild stays
+// inside the arrays; the grow is then taken again and the layer rebuilt once
+// more.
+__global__ void __launch_bounds__(kCvThreads) cv_count_kernel(
+    uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ old_bm, uint64_t words, int32_t M, int32_t K,
+    int32_t nbi, int32_t nbj, int64_t nnz, int32_t* __restrict__ cnt, int32_t* __restrict__ rcnt,
+    int32_t* __restrict__ ocnt, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_ptr,
+    int32_t* __restrict__ n_empty_r, int32_t* __restrict__ n_empty_c, const uint32_t* __restrict__ guard,
+    uint32_t need)
 {
     __shared__ uint32_t rowbits[kCvDim * kCvPad];
     __shared__ uint32_t colbits[kCvDim * kCvPad];
+    __shared__ uint32_t oldbits[kCvDim * kCvPad];
+    const bool restore = guard && !(guard[kStOverflow] == 0u && guard[kStTaken] == need);
+    if (restore) {   // every workgroup reads the old cells below, so the copy races with no read
+        const int64_t step = (int64_t)gridDim.x * kCvThreads;
+        for (int64_t w = (int64_t)blockIdx.x * kCvThreads + threadIdx.x; w < (int64_t)words; w += step)
+            occ_bm[w] = old_bm[w];
+    }
     int32_t bi, bj;
     if (!cv_tile_of(nbi, nbj, bi, bj)) return;
     const CvTileShape t = cv_shape(bi, bj, M, K);
     const int tid = threadIdx.x;
-    if (bj == 0) {
-        const int32_t r = t.r0 + (tid < t.nrows ? tid : t.nrows - 1);
-        const int32_t k = cv_slot_at(occ_bm, wpre, (uint64_t)r * (uint64_t)K);
-        if (tid < t.nrows) row_ptr[r] = k;
-    }
     if (bi == 0 && bj == 0 && tid == 0) {
         row_ptr[M] = (int32_t)nnz;
         col_ptr[K] = (int32_t)nnz;
         *n_empty_r = 0;   // the views' empty-key lists are rebuilt at the end
         *n_empty_c = 0;
     }
-    cv_load_rows<kCvThreads>(occ_bm, words, K, t, rowbits);
+    cv_load_rows<kCvThreads>(restore ? old_bm : occ_bm, words, K, t, rowbits);
+    cv_load_rows<kCvThreads>(old_bm, words, K, t, oldbits);
     __syncthreads();
+    {
+        int32_t rc = 0, oc = 0;
+#pragma unroll
+        for (int i = 0; i < kCvWords; ++i) {
+            rc += __popc(rowbits[tid * kCvPad + i]);
+            oc += __popc(oldbits[tid * kCvPad + i]);
+        }
+        if (tid < t.nrows) {
+            rcnt[(int64_t)bj * M + t.r0 + tid] = rc;
+            ocnt[(int64_t)bj * M + t.r0 + tid] = oc;
+        }
+    }
     cv_transpose<kCvThreads>(rowbits, colbits);
     __syncthreads();
     int32_t c = 0;
@@ -1143,35 +1140,73 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(const uint32_t* __
     if (tid < t.ncols) cnt[(int64_t)bi * K + t.c0 + tid] = c;
 }
 
-// down each column: counts -> exclusive prefix over the row blocks; the
-// column totals out, and per band of kCvDim columns (one workgroup) their sum
-__global__ void __launch_bounds__(kCvDim) cv_column_scan_kernel(int32_t* __restrict__ cnt, int32_t nbi, int32_t K,
-                                                                int32_t* __restrict__ tot, int32_t* __restrict__ band)
+// counts a[0], a[stride], ... (n of them) -> their exclusive prefix, in place; returns the total
+__device__ inline int32_t cv_scan_down(int32_t* __restrict__ a, int64_t stride, int32_t n)
 {
     constexpr int kBatch = 16;   // loads in flight per thread
-    __shared__ int32_t red[kCvDim / kWave];
-    const int64_t c = (int64_t)blockIdx.x * kCvDim + threadIdx.x;
     int32_t run = 0;
-    if (c < K) {
-        for (int32_t b0 = 0; b0 < nbi; b0 += kBatch) {
-            int32_t v[kBatch];
+    for (int32_t b0 = 0; b0 < n; b0 += kBatch) {
+        int32_t v[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) v[u] = b0 + u < nbi ? cnt[(int64_t)(b0 + u) * K + c] : 0;
+        for (int u = 0; u < kBatch; ++u) v[u] = b0 + u < n ? a[(int64_t)(b0 + u) * stride] : 0;
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                if (b0 + u < nbi) cnt[(int64_t)(b0 + u) * K + c] = run;
-                run += v[u];
-            }
+        for (int u = 0; u < kBatch; ++u) {
+            if (b0 + u < n) a[(int64_t)(b0 + u) * stride] = run;
+            run += v[u];
         }
-        tot[c] = run;
     }
-    const int32_t ws = wave_sum(run);
+    return run;
+}
+
+// a workgroup's sum of one value per thread (kCvDim threads)
+__device__ inline int32_t cv_block_sum(int32_t v, int32_t* red /*[kCvDim / kWave]*/)
+{
+    const int32_t ws = wave_sum(v);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ws;
     __syncthreads();
+    int32_t t = 0;
+    for (int i = 0; i < kCvDim / kWave; ++i) t += red[i];
+    return t;
+}
+
+// Pass 2: workgroups [0, nbj) take a band of kCvDim columns each: the counts
+// down each column become prefixes over the row blocks, the column totals and
+// the band's sum go out.  Workgroups [nbj, nbj + nbi) do the same for a band of
+// kCvDim rows, across the column blocks, for the new and the old cells.
+__global__ void __launch_bounds__(kCvDim) cv_scan_kernel(int32_t* __restrict__ cnt, int32_t* __restrict__ rcnt,
+                                                         int32_t* __restrict__ ocnt, int32_t nbi, int32_t nbj,
+                                                         int32_t M, int32_t K, int32_t* __restrict__ tot,
+                                                         int32_t* __restrict__ band, int32_t* __restrict__ rtot,
+                                                         int32_t* __restrict__ rband, int32_t* __restrict__ otot,
+                                                         int32_t* __restrict__ oband)
+{
+    __shared__ int32_t red[kCvDim / kWave];
+    if ((int32_t)blockIdx.x < nbj) {
+        const int64_t c = (int64_t)blockIdx.x * kCvDim + threadIdx.x;
+        int32_t run = 0;
+        if (c < K) {
+            run = cv_scan_down(cnt + c, K, nbi);
+            tot[c] = run;
+        }
+        const int32_t s = cv_block_sum(run, red);
+        if (threadIdx.x == 0) band[blockIdx.x] = s;
+        return;
+    }
+    const int32_t b = (int32_t)blockIdx.x - nbj;
+    const int64_t r = (int64_t)b * kCvDim + threadIdx.x;
+    int32_t rn = 0, ro = 0;
+    if (r < M) {
+        rn = cv_scan_down(rcnt + r, M, nbj);
+        ro = cv_scan_down(ocnt + r, M, nbj);
+        rtot[r] = rn;
+        otot[r] = ro;
+    }
+    const int32_t sn = cv_block_sum(rn, red);
+    __syncthreads();
+    const int32_t so = cv_block_sum(ro, red);
     if (threadIdx.x == 0) {
-        int32_t t = 0;
-        for (int i = 0; i < kCvDim / kWave; ++i) t += red[i];
-        band[blockIdx.x] = t;
+        rband[b] = sn;
+        oband[b] = so;
     }
 }
 
@@ -1255,39 +1290,89 @@ __device__ inline void cv_tab_side(int32_t* tab, const CvBounds& cb, int side, i
 constexpr int kCvScatterThreads = 1024;
 constexpr int32_t kCvStage = 4096;   // tile entries handled through LDS lists
 
-// One tile per workgroup.  Entries are numbered twice inside the tile: x in
-// row order (a row's entries are consecutive canonical slots, starting at
-// rowk) and e in column order (a column's entries are consecutive transposed
-// slots, starting at colbase).  A walk over each row word's bits lists the
-// row and column of every x; a pass in x order (striped across the threads)
-// then reads each entry's value as part of a row run, finds its e from the
-// column words, writes iperm as a row run and leaves the value, row and
+// Pass 3, one tile per workgroup: both index views and the canonical triple.
+// Entries are numbered twice inside the tile: x in row order (a row's entries
+// are consecutive canonical slots, starting at rowk) and e in column order (a
+// column's entries are consecutive transposed slots, starting at colbase).  A
+// walk over each row word's bits lists the row and column of every x; a pass
+// in x order (striped across the threads) finds each entry's e from the
+// column words and, for a kept cell, its old slot from the old cells' words,
+// reads its value from the copy taken before the drop (a grown cell is +0),
+// writes the canonical triple and iperm as row runs and leaves value, row and
 // column at e in LDS, from where a pass in e order writes rows_t and vals_t as
 // column runs.  A tile with more than kCvStage entries finds each entry's
 // column by binary search and reads and writes global memory directly.
-__global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
-    const uint32_t* __restrict__ occ_bm, uint64_t words, const int32_t* __restrict__ wpre, int32_t M, int32_t K,
-    int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt, const int32_t* __restrict__ tot,
-    const int32_t* __restrict__ band, int32_t* __restrict__ col_ptr, const float* __restrict__ vals,
-    int32_t* __restrict__ rows_t, float* __restrict__ vals_t, int32_t* __restrict__ iperm, CvTabs tabs,
-    uint16_t* __restrict__ rows_t16)
+struct CvScatterOut {
+    int32_t* row_ptr;
+    int32_t* col_ptr;
+    int32_t* rows;
+    int32_t* cols;
+    float* vals;
+    uint16_t* cols16;   // or null
+    int32_t* rows_t;
+    float* vals_t;
+    int32_t* iperm;
+    uint16_t* rows_t16;   // or null
+};
+
+// a band scan's start for the thread's key (one of kCvDim, in waves 4q .. 4q+3
+// of the workgroup): the bands before this one, plus the exclusive prefix of
+// the band's totals; `tot_here` is the thread's own total (0 past the matrix)
+struct CvBandScan {
+    int32_t incl, own, boff;
+};
+
+__device__ inline CvBandScan cv_band_scan_a(const int32_t* __restrict__ band, int32_t nb_before, int32_t tot_here,
+                                            int32_t* wsum /*[kCvDim / kWave]*/)
 {
-    __shared__ uint32_t rowbits[kCvDim * kCvPad];
+    const int lane = threadIdx.x & (kWave - 1);
+    CvBandScan b;
+    b.own = tot_here;
+    int32_t o = 0;
+    for (int32_t i = lane; i < nb_before; i += kWave) o += band[i];
+    b.boff = wave_sum(o);
+    b.incl = wave_incl(tot_here);
+    if (lane == kWave - 1) wsum[(threadIdx.x / kWave) % (kCvDim / kWave)] = b.incl;
+    return b;
+}
+
+__device__ inline int32_t cv_band_scan_b(const CvBandScan& b, const int32_t* wsum)
+{
+    int32_t start = b.boff + b.incl - b.own;
+    const int w = (threadIdx.x / kWave) % (kCvDim / kWave);
+    for (int i = 0; i < w; ++i) start += wsum[i];
+    return start;
+}
+
+__global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
+    const uint32_t* __restrict__ occ_bm, const uint32_t* __restrict__ old_bm, const uint32_t* __restrict__ kept_bm,
+    uint64_t words, int32_t M, int32_t K, int32_t nbi, int32_t nbj, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ tot, const int32_t* __restrict__ band, const int32_t* __restrict__ rcnt,
+    const int32_t* __restrict__ rtot, const int32_t* __restrict__ rband, const int32_t* __restrict__ ocnt,
+    const int32_t* __restrict__ otot, const int32_t* __restrict__ oband, const float* __restrict__ vcopy,
+    CvScatterOut out, CvTabs tabs)
+{
+    __shared__ uint32_t rowbits[kCvDim * kCvPad];    // rows of the new cells; later erow, ecol
     __shared__ uint32_t colbits[kCvDim * kCvPad];
+    __shared__ uint32_t oldbits[kCvDim * kCvPad];
+    __shared__ uint32_t keptbits[kCvDim * kCvPad];
     __shared__ uint8_t rwp[kCvDim * kCvWords];    // entries of a row before each of its words
     __shared__ uint8_t cwp[kCvDim * kCvWords];    // entries of a column before each of its words
+    __shared__ uint8_t owp[kCvDim * kCvWords];    // old cells of a row before each of its words
     __shared__ int32_t rowk[kCvDim];              // canonical slot of a row's first entry in the tile
+    __shared__ int32_t orowk[kCvDim];             // old slot of a row's first old cell in the tile
     __shared__ int32_t rowoff[kCvDim + 1];        // x of a row's first entry
     __shared__ int32_t colstart[kCvDim + 1];      // e of a column's first entry
     __shared__ int32_t colbase[kCvDim];           // transposed slot of a column's first entry
     __shared__ uint8_t xrow[kCvStage];   // row of x
     __shared__ uint8_t xcol[kCvStage];   // column of x
-    __shared__ uint8_t erow[kCvStage];   // row of e
-    __shared__ uint8_t ecol[kCvStage];   // column of e
     __shared__ float sval[kCvStage];     // value of e
     __shared__ int32_t red[2][kCvDim / kWave];
-    __shared__ int32_t cwsum[kCvDim / kWave];
+    __shared__ int32_t wsum[3][kCvDim / kWave];
     __shared__ CvBounds cb;
+    static_assert(2 * kCvStage <= (int)sizeof(rowbits), "erow and ecol fit the new cells' rows");
+    uint8_t* erow = reinterpret_cast<uint8_t*>(rowbits);   // row of e (x pass on)
+    uint8_t* ecol = erow + kCvStage;                        // column of e
     int32_t bi, bj;
     if (!cv_tile_of(nbi, nbj, bi, bj)) return;
     const CvTileShape t = cv_shape(bi, bj, M, K);
@@ -1295,52 +1380,62 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
 
     cv_bounds_init(cb);
     cv_load_rows<kCvScatterThreads>(occ_bm, words, K, t, rowbits);
-    // the columns' first transposed slots: the bands before this one, then a scan of the band's
-    // column totals (column starts also written to col_ptr by the first row block)
-    int32_t ctot = 0, ccnt = 0, cincl = 0, boff = 0;
-    if (tid < kCvDim) {
-        const int32_t c = t.c0 + (tid < t.ncols ? tid : t.ncols - 1);
-        const int32_t r = t.r0 + (tid < t.nrows ? tid : t.nrows - 1);
-        ctot = tid < t.ncols ? tot[c] : 0;
-        ccnt = cnt[(int64_t)bi * K + c];
-        for (int32_t b = lane; b < bj; b += kWave) boff += band[b];
-        const int32_t k = cv_slot_at(occ_bm, wpre, (uint64_t)r * (uint64_t)K + (uint64_t)t.c0);
-        rowk[tid] = tid < t.nrows ? k : 0;
-        boff = wave_sum(boff);
-        cincl = wave_incl(ctot);
-        if (lane == kWave - 1) cwsum[wv] = cincl;
+    cv_load_rows<kCvScatterThreads>(old_bm, words, K, t, oldbits);
+    cv_load_rows<kCvScatterThreads>(kept_bm, words, K, t, keptbits);
+    // first slots: waves 0-3 the columns' transposed ones (column starts also to col_ptr from the
+    // first row block), 4-7 the rows' canonical ones (row starts to row_ptr from the first column
+    // block), 8-11 the rows' old ones: the bands before this one, a scan of the band's totals, and
+    // the key's entries in the blocks before this tile
+    const int role = wv / (kCvDim / kWave);   // uniform per wave
+    const int a = tid % kCvDim;
+    CvBandScan bs{0, 0, 0};
+    int32_t before_tile = 0;
+    if (role == 0) {
+        const int32_t c = t.c0 + (a < t.ncols ? a : t.ncols - 1);
+        before_tile = cnt[(int64_t)bi * K + c];
+        bs = cv_band_scan_a(band, bj, a < t.ncols ? tot[c] : 0, wsum[0]);
+    } else if (role == 1 || role == 2) {
+        const int32_t r = t.r0 + (a < t.nrows ? a : t.nrows - 1);
+        const bool nw = role == 1;
+        before_tile = (nw ? rcnt : ocnt)[(int64_t)bj * M + r];
+        bs = cv_band_scan_a(nw ? rband : oband, bi, a < t.nrows ? (nw ? rtot : otot)[r] : 0, wsum[role]);
     }
     __syncthreads();
-    if (tid < kCvDim) {
-        int32_t start = boff + cincl - ctot;
-        for (int i = 0; i < wv; ++i) start += cwsum[i];
-        colbase[tid] = tid < t.ncols ? start + ccnt : 0;
-        if (bi == 0 && tid < t.ncols) col_ptr[t.c0 + tid] = start;
+    if (role == 0) {
+        const int32_t start = cv_band_scan_b(bs, wsum[0]);
+        colbase[a] = a < t.ncols ? start + before_tile : 0;
+        if (bi == 0 && a < t.ncols) out.col_ptr[t.c0 + a] = start;
+    } else if (role == 1) {
+        const int32_t start = cv_band_scan_b(bs, wsum[1]);
+        rowk[a] = a < t.nrows ? start + before_tile : 0;
+        if (bj == 0 && a < t.nrows) out.row_ptr[t.r0 + a] = start;
+    } else if (role == 2) {
+        const int32_t start = cv_band_scan_b(bs, wsum[2]);
+        orowk[a] = a < t.nrows ? start + before_tile : 0;
     }
     cv_transpose<kCvScatterThreads>(rowbits, colbits);
     cv_bounds_find(cb, tabs, t, M, K, bj == nbj - 1, bi == nbi - 1);
     __syncthreads();
-    // word prefixes and counts: threads 0..255 rows, 256..511 columns
+    // word prefixes and counts: threads 0..255 rows, 256..511 columns, 512..767 the old cells' rows
     int32_t cntv = 0;
-    if (tid < 2 * kCvDim) {
-        const bool row = tid < kCvDim;
-        const int a = row ? tid : tid - kCvDim;
-        const uint32_t* bits = row ? rowbits : colbits;
-        uint8_t* pre = row ? rwp : cwp;
+    if (tid < 3 * kCvDim) {
+        const uint32_t* bits = role == 0 ? rowbits : role == 1 ? colbits : oldbits;
+        uint8_t* pre = role == 0 ? rwp : role == 1 ? cwp : owp;
 #pragma unroll
         for (int i = 0; i < kCvWords; ++i) {
             pre[a * kCvWords + i] = (uint8_t)cntv;
             cntv += __popc(bits[a * kCvPad + i]);
         }
-        const int32_t inc = wave_incl(cntv);
-        if (lane == kWave - 1) red[row ? 0 : 1][(tid % kCvDim) / kWave] = inc;
+        if (role < 2) {
+            const int32_t inc = wave_incl(cntv);
+            if (lane == kWave - 1) red[role][a / kWave] = inc;
+        }
     }
     __syncthreads();
     if (tid < 2 * kCvDim) {
-        const bool row = tid < kCvDim;
-        const int a = row ? tid : tid - kCvDim;
+        const bool row = role == 0;
         int32_t before = 0;
-        for (int i = 0; i < a / kWave; ++i) before += red[row ? 0 : 1][i];
+        for (int i = 0; i < a / kWave; ++i) before += red[role][i];
         const int32_t ex = before + wave_incl(cntv) - cntv;
         (row ? rowoff : colstart)[a] = ex;
         if (a == kCvDim - 1) (row ? rowoff : colstart)[kCvDim] = ex + cntv;
@@ -1348,8 +1443,7 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     __syncthreads();
     // slice tables: threads 0..255 the rows' entries (row view), 256..511 the columns'
     if (tid < 2 * kCvDim) {
-        const bool row = tid < kCvDim;
-        const int a = row ? tid : tid - kCvDim;
+        const bool row = role == 0;
         for (int w = 0; w < kTileWidths; ++w) {
             if (row && tabs.rtab[w]) {
                 const int32_t total = a < t.nrows ? rowoff[a + 1] - rowoff[a] : 0;
@@ -1364,45 +1458,59 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
         }
     }
     const int32_t E = colstart[kCvDim];
+    // a kept cell's value from the copy taken before the drop (its old slot: the row's first old
+    // cell in the tile plus the old cells before it); a grown cell is +0
+    auto old_slot = [&](int rr, int c) -> int32_t {
+        const int ci = c >> 5;
+        const uint32_t below = (1u << (c & 31)) - 1u;
+        if (!((keptbits[rr * kCvPad + ci] >> (c & 31)) & 1u)) return -1;
+        return orowk[rr] + owp[rr * kCvWords + ci] + __popc(oldbits[rr * kCvPad + ci] & below);
+    };
     if (E <= kCvStage) {   // uniform
         // row and column of every x: two row words per thread
 #pragma unroll
         for (int n = 0; n < kCvDim * kCvWords / kCvScatterThreads; ++n) {
             const int q = tid + n * kCvScatterThreads;
-            const int a = q / kCvWords, i = q % kCvWords;
-            uint32_t m = rowbits[a * kCvPad + i];
-            int32_t x = rowoff[a] + rwp[a * kCvWords + i];
+            const int ra = q / kCvWords, i = q % kCvWords;
+            uint32_t m = rowbits[ra * kCvPad + i];
+            int32_t x = rowoff[ra] + rwp[ra * kCvWords + i];
             while (m) {
-                xrow[x] = (uint8_t)a;
+                xrow[x] = (uint8_t)ra;
                 xcol[x] = (uint8_t)(32 * i + __ffs(m) - 1);
                 m &= m - 1u;
                 ++x;
             }
         }
-        __syncthreads();
+        __syncthreads();   // rowbits is dead from here: erow and ecol take its place
         {
-            // x order: values read (all R loads in flight first), iperm written, (value, row, column) to e
+            // x order: the old values read (all R loads in flight first), the canonical triple and
+            // iperm written, (value, row, column) to e
             constexpr int R = kCvStage / kCvScatterThreads;
             float v[R];
-            int32_t k[R];
+            int32_t src[R];
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int32_t x = tid + u * kCvScatterThreads;
-                const int rr = xrow[x < E ? x : 0];
-                k[u] = x < E ? rowk[rr] + (x - rowoff[rr]) : 0;
-                v[u] = vals[k[u]];
+                src[u] = x < E ? old_slot(xrow[x], xcol[x]) : -1;
+                v[u] = vcopy[src[u] >= 0 ? src[u] : 0];
             }
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int32_t x = tid + u * kCvScatterThreads;
                 if (x < E) {
                     const int rr = xrow[x], c = xcol[x];
+                    const float val = src[u] >= 0 ? v[u] : 0.0f;
+                    const int32_t k = rowk[rr] + (x - rowoff[rr]);
                     const int j = rr >> 5;
                     const int32_t before =
                         cwp[c * kCvWords + j] + __popc(colbits[c * kCvPad + j] & ((1u << (rr & 31)) - 1u));
                     const int32_t e = colstart[c] + before;
-                    iperm[k[u]] = colbase[c] + before;
-                    sval[e] = v[u];
+                    out.rows[k] = t.r0 + rr;
+                    out.cols[k] = t.c0 + c;
+                    if (out.cols16) out.cols16[k] = (uint16_t)(t.c0 + c);
+                    out.vals[k] = val;
+                    out.iperm[k] = colbase[c] + before;
+                    sval[e] = val;
                     erow[e] = (uint8_t)rr;
                     ecol[e] = (uint8_t)c;
                 }
@@ -1414,9 +1522,9 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
             const int c = ecol[e];
             const int32_t kt = colbase[c] + (e - colstart[c]);
             const int32_t r = t.r0 + erow[e];
-            rows_t[kt] = r;
-            if (rows_t16) rows_t16[kt] = (uint16_t)r;
-            vals_t[kt] = sval[e];
+            out.rows_t[kt] = r;
+            if (out.rows_t16) out.rows_t16[kt] = (uint16_t)r;
+            out.vals_t[kt] = sval[e];
         }
         return;
     }
@@ -1435,10 +1543,16 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
         const int rr = 32 * j + __ffs(m) - 1;
         const int ci = c >> 5;
         const int32_t k = rowk[rr] + rwp[rr * kCvWords + ci] + __popc(rowbits[rr * kCvPad + ci] & ((1u << (c & 31)) - 1u));
-        rows_t[kt] = t.r0 + rr;
-        if (rows_t16) rows_t16[kt] = (uint16_t)(t.r0 + rr);
-        vals_t[kt] = vals[k];
-        iperm[k] = kt;
+        const int32_t src = old_slot(rr, c);
+        const float val = src >= 0 ? vcopy[src] : 0.0f;
+        out.rows[k] = t.r0 + rr;
+        out.cols[k] = t.c0 + c;
+        if (out.cols16) out.cols16[k] = (uint16_t)(t.c0 + c);
+        out.vals[k] = val;
+        out.rows_t[kt] = t.r0 + rr;
+        if (out.rows_t16) out.rows_t16[kt] = (uint16_t)(t.r0 + rr);
+        out.vals_t[kt] = val;
+        out.iperm[k] = kt;
     }
 }
 
@@ -1456,10 +1570,15 @@ struct PruneScratch {
     int32_t* tsum;      // [tmax / kSumTile] accepted per tile
     int32_t* fill;      // [kMaxRegions] bucket fill per region
     uint64_t* bucket;   // [nbucket] candidates grouped by region
-    int32_t* wpre;      // [words] first canonical slot of every bitmap word (column view from the bitmap)
     int32_t* cvcnt;     // [row blocks * K] entries per column and row block, then their prefixes
     int32_t* cvtot;     // [K] entries per column
-    int32_t* cvband;    // [column bands] entries per band of kCvDim columns
+    int32_t* cvband;    // [column blocks] entries per band of kCvDim columns
+    int32_t* rcnt;      // [column blocks * M] entries per row and column block, then their prefixes
+    int32_t* ocnt;      // [column blocks * M] the same for the cells before the drop
+    int32_t* rtot;      // [M] entries per row
+    int32_t* otot;      // [M] cells before the drop per row
+    int32_t* rband;     // [row blocks] entries per band of kCvDim rows
+    int32_t* oband;     // [row blocks] cells before the drop per band of rows
     uint32_t* gstate;   // [16] gradient grow: thresholds and counts
     uint32_t* ghist;    // [kGradHistWords] gradient grow: digit histograms
     int32_t* tie_cnt;   // [M * grad_col_tiles(K)] gradient grow: threshold ties per row and column tile
@@ -1510,8 +1629,12 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
     size_t o_oc = take((size_t)units * 4), o_dc = take((size_t)units * 4);
     size_t o_acc = take((size_t)tm + 8), o_tsum = take((size_t)(tm / kSumTile + 1) * 4);
     size_t o_fill = take((size_t)kMaxRegions * 4), o_bucket = take((size_t)nb * 8);
-    size_t o_wpre = take((size_t)words * 4), o_cvcnt = take((size_t)nbi * L->K * 4), o_cvtot = take((size_t)L->K * 4);
-    size_t o_cvband = take((size_t)((L->K + kCvDim - 1) / kCvDim) * 4);
+    const int64_t nbj = (L->K + kCvDim - 1) / kCvDim;
+    size_t o_cvcnt = take((size_t)nbi * L->K * 4), o_cvtot = take((size_t)L->K * 4);
+    size_t o_cvband = take((size_t)nbj * 4);
+    size_t o_rcnt = take((size_t)nbj * L->M * 4), o_ocnt = take((size_t)nbj * L->M * 4);
+    size_t o_rtot = take((size_t)L->M * 4), o_otot = take((size_t)L->M * 4);
+    size_t o_rband = take((size_t)nbi * 4), o_oband = take((size_t)nbi * 4);
     size_t o_gst = take(16 * 4), o_gh = take((size_t)kGradHistWords * 4), o_tie = take((size_t)nties * 4);
     size_t o_scan = take(scan_scratch_bytes(sn));
     if (ps) {
@@ -1529,10 +1652,15 @@ size_t layout(const snack_layer* L, PruneScratch* ps)
         ps->tsum = (int32_t*)(base + o_tsum);
         ps->fill = (int32_t*)(base + o_fill);
         ps->bucket = (uint64_t*)(base + o_bucket);
-        ps->wpre = (int32_t*)(base + o_wpre);
         ps->cvcnt = (int32_t*)(base + o_cvcnt);
         ps->cvtot = (int32_t*)(base + o_cvtot);
         ps->cvband = (int32_t*)(base + o_cvband);
+        ps->rcnt = (int32_t*)(base + o_rcnt);
+        ps->ocnt = (int32_t*)(base + o_ocnt);
+        ps->rtot = (int32_t*)(base + o_rtot);
+        ps->otot = (int32_t*)(base + o_otot);
+        ps->rband = (int32_t*)(base + o_rband);
+        ps->oband = (int32_t*)(base + o_oband);
         ps->gstate = (uint32_t*)(base + o_gst);
         ps->ghist = (uint32_t*)(base + o_gh);
         ps->tie_cnt = (int32_t*)(base + o_tie);
@@ -1563,47 +1691,19 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s, cons
 {
     const int64_t nnz = L->nnz;
     const uint64_t N = (uint64_t)L->M * (uint64_t)L->K;
-    // with the column view built from the bitmap, the 16-bit index copies are written beside the
-    // indices (only their first nnz slots change: the padding past nnz never does)
-    const bool idx16_here = cv_from_bitmap(L);
-    // ---- new canonical arrays: set bits of occ in ascending position ----
-    {
-        const int64_t nu = ps.units;
-        const unsigned grid = (unsigned)((nu + (kEmitThreads / kWave) - 1) / (kEmitThreads / kWave));
-        hipLaunchKernelGGL(bm_unit_counts_kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.old_bm, ps.words,
-                           nu, ps.occ_cnt, ps.old_cnt, guard, need);
-        SNACK_HIP(hipGetLastError());
-        const bool direct = nu <= kEmitDirect;
-        if (!direct) {
-            SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, nu, nullptr, ps.scan, s));
-            SNACK_CHECK(exclusive_scan_i32(ps.old_cnt, ps.old_cnt, nu, nullptr, ps.scan, s));
-        }
-        const bool wide = N > 0xFFFFFFFFull;
-        int32_t* wpre = cv_from_bitmap(L) ? ps.wpre : nullptr;
-        auto emit = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm, ps.old_bm,
-                               ps.words, nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals,
-                               wpre, idx16_here ? L->fwd.idx16 : nullptr);
-        };
-        if (direct) {
-            if (wide) emit(emit_units_kernel<true, true>);
-            else emit(emit_units_kernel<true, false>);
-        } else {
-            if (wide) emit(emit_units_kernel<false, true>);
-            else emit(emit_units_kernel<false, false>);
-        }
-        SNACK_HIP(hipGetLastError());
-    }
     if (cv_from_bitmap(L)) {
+        // count, scan, then one pass over the tiles writes the canonical triple (with its 16-bit
+        // column copy), the column view (with its 16-bit row copy) and the slice tables
         ProfScope pc(KC_CANON, s);
         const int32_t M = L->M, K = L->K;
         const int32_t nbi = (M + kCvDim - 1) / kCvDim, nbj = (K + kCvDim - 1) / kCvDim;
         const uint64_t words = (uint64_t)ps.words;
         const int64_t nslots = (int64_t)kXcds * ((nbj + kXcds - 1) / kXcds) * nbi;
-        hipLaunchKernelGGL(cv_count_kernel, dim3((unsigned)nslots), dim3(kCvThreads), 0, s, ps.occ_bm, words, ps.wpre,
-                           M, K, nbi, nbj, nnz, ps.cvcnt, L->row_ptr, L->col_ptr, L->fwd.n_empty, L->tr.n_empty);
-        hipLaunchKernelGGL(cv_column_scan_kernel, dim3((unsigned)nbj), dim3(kCvDim), 0, s, ps.cvcnt, nbi, K, ps.cvtot,
-                           ps.cvband);
+        hipLaunchKernelGGL(cv_count_kernel, dim3((unsigned)nslots), dim3(kCvThreads), 0, s, ps.occ_bm, ps.old_bm, words,
+                           M, K, nbi, nbj, nnz, ps.cvcnt, ps.rcnt, ps.ocnt, L->row_ptr, L->col_ptr, L->fwd.n_empty,
+                           L->tr.n_empty, guard, need);
+        hipLaunchKernelGGL(cv_scan_kernel, dim3((unsigned)(nbj + nbi)), dim3(kCvDim), 0, s, ps.cvcnt, ps.rcnt, ps.ocnt,
+                           nbi, nbj, M, K, ps.cvtot, ps.cvband, ps.rtot, ps.rband, ps.otot, ps.oband);
         SNACK_HIP(hipGetLastError());
         CvTabs tabs;
         for (int w = 0; w < kTileWidths; ++w) {
@@ -1612,19 +1712,56 @@ snack_status rebuild(snack_layer* L, const PruneScratch& ps, hipStream_t s, cons
             tabs.cS[w] = L->tr.split[w].S;
             tabs.ctab[w] = L->tr.split[w].S >= 2 ? L->tr.split[w].tab : nullptr;
         }
-        hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm, words,
-                           ps.wpre, M, K, nbi, nbj, ps.cvcnt, ps.cvtot, ps.cvband, L->col_ptr, L->vals, L->rows_t,
-                           L->vals_t, L->iperm, tabs, L->tr.idx16);
+        CvScatterOut o;
+        o.row_ptr = L->row_ptr;
+        o.col_ptr = L->col_ptr;
+        o.rows = L->rows;
+        o.cols = L->cols;
+        o.vals = L->vals;
+        o.cols16 = L->fwd.idx16;
+        o.rows_t = L->rows_t;
+        o.vals_t = L->vals_t;
+        o.iperm = L->iperm;
+        o.rows_t16 = L->tr.idx16;
+        hipLaunchKernelGGL(cv_scatter_kernel, dim3((unsigned)nslots), dim3(kCvScatterThreads), 0, s, ps.occ_bm,
+                           ps.old_bm, ps.kept_bm, words, M, K, nbi, nbj, ps.cvcnt, ps.cvtot, ps.cvband, ps.rcnt,
+                           ps.rtot, ps.rband, ps.ocnt, ps.otot, ps.oband, ps.vcopy, o, tabs);
         SNACK_HIP(hipGetLastError());
         SNACK_CHECK(canon_index_tail(L, s, /*idx16_done=*/true, /*empty_cleared=*/true));
         for (int w = 0; w < kTileWidths; ++w) {
             if (tabs.rtab[w]) L->fwd.split[w].valid = true;
             if (tabs.ctab[w]) L->tr.split[w].valid = true;
         }
-    } else {
-        SNACK_CHECK(canon_build_index(L, s));
+        return SNACK_OK;
     }
-    return SNACK_OK;
+    // ---- a layer too sparse for the tiles: the canonical arrays from the bitmap in unit order,
+    // then the index build ----
+    if (guard) return SNACK_ERR_INVALID_ARG;   // only the tile rebuild is queued ahead of a grow result
+    const int64_t nu = ps.units;
+    const unsigned grid = (unsigned)((nu + (kEmitThreads / kWave) - 1) / (kEmitThreads / kWave));
+    hipLaunchKernelGGL(bm_unit_counts_kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.old_bm, ps.words,
+                       nu, ps.occ_cnt, ps.old_cnt);
+    SNACK_HIP(hipGetLastError());
+    const bool direct = nu <= kEmitDirect;
+    if (!direct) {
+        SNACK_CHECK(exclusive_scan_i32(ps.occ_cnt, ps.occ_cnt, nu, nullptr, ps.scan, s));
+        SNACK_CHECK(exclusive_scan_i32(ps.old_cnt, ps.old_cnt, nu, nullptr, ps.scan, s));
+    }
+    const bool wide = N > 0xFFFFFFFFull;
+    auto emit = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kEmitThreads), 0, s, ps.occ_bm, ps.kept_bm, ps.old_bm, ps.words,
+                           nu, ps.occ_cnt, ps.old_cnt, ps.vcopy, nnz, L->K, L->rows, L->cols, L->vals,
+                           (uint16_t*)nullptr);
+    };
+    if (direct) {
+        if (wide) emit(emit_units_kernel<true, true>);
+        else emit(emit_units_kernel<true, false>);
+    } else {
+        if (wide) emit(emit_units_kernel<false, true>);
+        else emit(emit_units_kernel<false, false>);
+    }
+    SNACK_HIP(hipGetLastError());
+    return canon_build_index(L, s);
 }
 
 }  // namespace
