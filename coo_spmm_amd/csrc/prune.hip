@@ -1030,33 +1030,49 @@ __device__ inline bool cv_tile_of(int32_t nbi, int32_t nbj, int32_t& bi, int32_t
 // c0+32i .. c0+32i+31 of tile row rr (zero outside the matrix).  Every thread
 // issues all its loads (clamped indexes, both words of each unaligned span)
 // before it writes any of them, so none waits behind another.
-template <int T>
-__device__ inline void cv_load_rows(const uint32_t* __restrict__ occ_bm, uint64_t words, int32_t K,
-                                    const CvTileShape& t, uint32_t* rowbits)
+template <int T, int NB = 1>
+__device__ inline void cv_load_rows(const uint32_t* const (&bm)[NB], uint64_t words, int32_t K, const CvTileShape& t,
+                                    uint32_t* const (&rowbits)[NB])
 {
     constexpr int R = kCvDim * kCvWords / T;
-    uint32_t lo[R], hi[R];
-    uint64_t cell[R];
+    uint32_t lo[NB][R], hi[NB][R];
+    int sh[R];
 #pragma unroll
     for (int n = 0; n < R; ++n) {
         const int q = threadIdx.x + n * T;
         const int rr = q / kCvWords, i = q % kCvWords;
         const bool in = rr < t.nrows && 32 * i < t.ncols;
-        cell[n] = in ? (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + 32 * i) : 0ull;
-        const uint64_t w = cell[n] >> 5;
-        lo[n] = occ_bm[w];
-        hi[n] = occ_bm[w + 1 < words ? w + 1 : w];
+        const uint64_t cell = in ? (uint64_t)(t.r0 + rr) * (uint64_t)K + (uint64_t)(t.c0 + 32 * i) : 0ull;
+        const uint64_t w = cell >> 5, w1 = w + 1 < words ? w + 1 : w;
+        sh[n] = (int)(cell & 31);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            lo[b][n] = bm[b][w];
+            hi[b][n] = bm[b][w1];
+        }
     }
 #pragma unroll
     for (int n = 0; n < R; ++n) {
         const int q = threadIdx.x + n * T;
         const int rr = q / kCvWords, i = q % kCvWords;
-        const int sh = (int)(cell[n] & 31);
-        uint32_t x = sh ? (lo[n] >> sh) | (hi[n] << (32 - sh)) : lo[n];
         const int32_t valid = t.ncols - 32 * i;
-        if (valid < 32) x &= (1u << valid) - 1u;
-        rowbits[rr * kCvPad + i] = (rr < t.nrows && valid > 0) ? x : 0u;
+        const uint32_t keep = valid >= 32 ? ~0u : (1u << (valid > 0 ? valid : 0)) - 1u;
+        const bool live = rr < t.nrows && valid > 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t x = sh[n] ? (lo[b][n] >> sh[n]) | (hi[b][n] << (32 - sh[n])) : lo[b][n];
+            rowbits[b][rr * kCvPad + i] = live ? (x & keep) : 0u;
+        }
     }
+}
+
+template <int T>
+__device__ inline void cv_load_rows(const uint32_t* bm, uint64_t words, int32_t K, const CvTileShape& t,
+                                    uint32_t* rowbits)
+{
+    const uint32_t* const src[1] = {bm};
+    uint32_t* const dst[1] = {rowbits};
+    cv_load_rows<T, 1>(src, words, K, t, dst);
 }
 
 // Column words: colbits[c * kCvPad + j] holds rows 32j .. 32j+31 of column c.
@@ -1117,8 +1133,11 @@ __global__ void __launch_bounds__(kCvThreads) cv_count_kernel(
         *n_empty_r = 0;   // the views' empty-key lists are rebuilt at the end
         *n_empty_c = 0;
     }
-    cv_load_rows<kCvThreads>(restore ? old_bm : occ_bm, words, K, t, rowbits);
-    cv_load_rows<kCvThreads>(old_bm, words, K, t, oldbits);
+    {
+        const uint32_t* const src[2] = {restore ? old_bm : occ_bm, old_bm};
+        uint32_t* const dst[2] = {rowbits, oldbits};
+        cv_load_rows<kCvThreads, 2>(src, words, K, t, dst);
+    }
     __syncthreads();
     {
         int32_t rc = 0, oc = 0;
@@ -1379,9 +1398,11 @@ __global__ void __launch_bounds__(kCvScatterThreads) cv_scatter_kernel(
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 
     cv_bounds_init(cb);
-    cv_load_rows<kCvScatterThreads>(occ_bm, words, K, t, rowbits);
-    cv_load_rows<kCvScatterThreads>(old_bm, words, K, t, oldbits);
-    cv_load_rows<kCvScatterThreads>(kept_bm, words, K, t, keptbits);
+    {
+        const uint32_t* const src[3] = {occ_bm, old_bm, kept_bm};
+        uint32_t* const dst[3] = {rowbits, oldbits, keptbits};
+        cv_load_rows<kCvScatterThreads, 3>(src, words, K, t, dst);
+    }
     // first slots: waves 0-3 the columns' transposed ones (column starts also to col_ptr from the
     // first row block), 4-7 the rows' canonical ones (row starts to row_ptr from the first column
     // block), 8-11 the rows' old ones: the bands before this one, a scan of the band's totals, and
