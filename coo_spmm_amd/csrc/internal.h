@@ -41,6 +41,11 @@ enum KernelClass : int {
 // whose index lies in slice s or later (s = 0..S).  Rebuilt lazily after every
 // change of the index.
 constexpr int kTileWidths = 4;   // batch tiles 8, 16, 32, 64
+// Floats per staged row of the slice-tiled passes: a batch tile's columns,
+// padded by 16 bytes below 64 columns so that consecutive rows start in
+// different LDS banks (a lane group reads part of a row; at 64 columns each
+// group reads whole 256-byte rows and needs no padding).
+__host__ __device__ constexpr int tile_row_floats(int btile) { return btile < 64 ? btile + 4 : btile; }
 constexpr int kMaxSplits = 64;   // most slices of one table
 // one SGD step on one value: v - lr * g with a single rounding; every update of
 // either value copy goes through it, so the two copies stay bit-identical

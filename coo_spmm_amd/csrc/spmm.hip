@@ -1153,6 +1153,7 @@ template <int BT, int NB, int U, int D, bool DW, bool SPMM, bool VAL = SPMM>
 __device__ __forceinline__ void tile_body(RoleArgs A, const TileArgs& T, int bp, int B, int bid, int nwg, int tile)
 {
     constexpr int BTILE = BT * NB;
+    constexpr int ROW = tile_row_floats(BTILE);   // floats per staged row
     using TB = TileBlock<BT, U>;
     extern __shared__ __align__(16) float gs_dyn[];
     const int per = nwg / kXcd;   // the grid is a multiple of kXcd
@@ -1171,9 +1172,9 @@ __device__ __forceinline__ void tile_body(RoleArgs A, const TileArgs& T, int bp,
     const int32_t i0 = split_start(s, T.S, A.nidx);
     const int32_t nrow = split_start(s + 1, T.S, A.nidx) - i0;
     {
-        // the tile's columns of the slice's rows: rows of BTILE floats, bp apart
-        // (contiguous when the batch is a single tile)
-        constexpr int Q = BTILE / 4;
+        // the tile's columns of the slice's rows (BTILE floats, bp apart in global memory;
+        // contiguous when the batch is a single tile) into LDS rows of ROW floats
+        constexpr int Q = BTILE / 4, RQ = ROW / 4;
         const int64_t n4 = (int64_t)nrow * Q;
         const int64_t rs4 = bp / 4;
         const float4* __restrict__ src = reinterpret_cast<const float4*>(A.G + (int64_t)i0 * bp + (int64_t)tile * BTILE);
@@ -1193,10 +1194,11 @@ __device__ __forceinline__ void tile_body(RoleArgs A, const TileArgs& T, int bp,
 #pragma unroll
             for (int k = 0; k < SB; ++k) {
                 const int64_t q = q0 + (int64_t)k * NT;
-                dst[q < n4 ? q : n4 - 1] = v[k];
+                const int64_t qc = q < n4 ? q : n4 - 1;
+                dst[(qc / Q) * RQ + (qc % Q)] = v[k];
             }
         }
-        if (threadIdx.x < BTILE / 4) dst[n4 + threadIdx.x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);   // zero row
+        if (threadIdx.x < BTILE / 4) dst[(int64_t)nrow * RQ + threadIdx.x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);   // zero row
         __syncthreads();
     }
     const int lane = threadIdx.x & (kWave - 1);
@@ -1240,7 +1242,7 @@ __device__ __forceinline__ void tile_body(RoleArgs A, const TileArgs& T, int bp,
     for (;;) {
 #pragma unroll
         for (int q = 0; q < D; ++q) {
-            blk[q].prepare(d[q].base, d[q].lim, lk, i0, BTILE * 4, nrow * BTILE * 4);
+            blk[q].prepare(d[q].base, d[q].lim, lk, i0, ROW * 4, nrow * ROW * 4);
             float y[U][NB];
             tile_gather<U, BT, NB>(blk[q], lane_off, y);
             if constexpr (SPMM) {
@@ -2437,7 +2439,7 @@ snack_status launch_tile(const BatchPlan& p, const snack_layer* L, const View& v
     int64_t nwg = (int64_t)t.S * t.KB;
     nwg = (nwg + kXcd - 1) / kXcd * kXcd;
     const int32_t rows = (v.nidx + t.S - 1) / t.S + 1;   // the slice and a zero row
-    const size_t lds = (size_t)rows * p.btile * sizeof(float);
+    const size_t lds = (size_t)rows * tile_row_floats(p.btile) * sizeof(float);
     const dim3 grid((unsigned)nwg, (unsigned)p.ntiles), block(kTileWaves * kWave);
     // group width x values per lane x entries per group: 2 x 4 x 2, 4 x 4 x 4,
     // 4 x 8 x 4, 16 x 4 x 8 (x 4 with dW: short slice segments waste less)
@@ -2511,7 +2513,7 @@ snack_status launch_tile_bwd2(const BatchPlan& p, const snack_layer* L, const fl
         nwg = (int64_t)t.S * t.KB;
         nwg = (nwg + kXcd - 1) / kXcd * kXcd;
         const int32_t rows = (v.nidx + t.S - 1) / t.S + 1;   // the slice and a zero row
-        lds = (size_t)rows * p.btile * sizeof(float);
+        lds = (size_t)rows * tile_row_floats(p.btile) * sizeof(float);
     };
     RoleArgs ac, ar;
     TileArgs tc, tr;
@@ -2563,7 +2565,7 @@ snack_status launch_tile_bwd2(const BatchPlan& p, const snack_layer* L, const fl
 int tile_splits(const snack_layer* L, const View& v, int btile)
 {
     if (L->lds_bytes <= kTileStaticLds || v.nidx <= 0 || v.nkeys <= 0) return 0;
-    const int64_t rows = (int64_t)(L->lds_bytes - kTileStaticLds) / ((int64_t)btile * 4);
+    const int64_t rows = (int64_t)(L->lds_bytes - kTileStaticLds) / ((int64_t)tile_row_floats(btile) * 4);
     if (rows < 1) return 0;
     const int64_t S = (v.nidx + rows - 1) / rows;
     return S <= kMaxSplits ? (int)S : 0;
