@@ -93,9 +93,6 @@ __device__ inline void load_nb(const float* __restrict__ p, float (&x)[NB])
     }
 }
 
-__device__ inline int comp(const int4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
-__device__ inline float compf(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
-
 // Reduce four per-lane values over the BT lanes of a group (a butterfly whose
 // upper levels exchange half of the remaining values).  On return lane bl
 // holds the full group sum of value (bl / (BT/4)) & 3 for BT >= 4, of values
